@@ -1,0 +1,23 @@
+"""fp64 CPU oracle for the block-sparse attention backward.
+
+TEST INFRASTRUCTURE ONLY: imported by ``tests/``, ``__graft_entry__.smoke()``
+and the ``cpu_baseline`` leg of ``bench.py``; never by the product path.
+
+Parity status of each function (what pins it, in ``tests/test_oracle.py``):
+
+* ``element_mask`` / ``block_lists``: hand-worked example (``tests/golden``),
+  brute-force properties (ascending, row/column lists transpose each other,
+  expansion reproduces the clipped mask).
+* ``forward`` / ``backward`` (and the ``_dense`` twins): central finite
+  differences of sum(dO*O) on tiny inputs (GQA, partial blocks, TND, padded
+  BNSD), equality with torch fp64 autograd for the dense and the element-mask
+  special cases, closed forms (Q = 0; one key per row; the worked sample of the
+  aclnnBlockSparseAttentionGrad page), the dK / dV column-sum invariants, and
+  the GQA / TND / padding identities.
+* ``backward_dq_rows`` / ``backward_dkdv_rows``: equal to the matching rows of
+  ``backward``.
+
+No function here is "parity unpinned".
+"""
+from .ref import *  # noqa: F401,F403
+from .ref import __all__  # noqa: F401
