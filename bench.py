@@ -1,0 +1,286 @@
+#!/usr/bin/env python3
+"""Benchmark: block-sparse attention backward on one MI355X.
+
+One step = one full ``bsa_bwd`` call (sequence table, delta pre-pass, mask
+compaction, dK/dV kernel, dQ kernel) over the workload's inputs, which are
+resident in HBM before timing starts.  Prints one JSON line:
+
+  value    backward TFLOP/s counted over active blocks: 10*bx*by*D FLOPs per
+           selected in-range (batch, query head, Q block, KV block)
+  roofline the dominant kernel (dK/dV) against the dense bf16 MFMA peak,
+           timed with HIP events recorded between the library's stages
+  cpu_baseline  the fp64 CPU oracle's backward on a bounded sample of the
+           same workload, on this host's cores
+
+Inputs are synthetic: Q, K, V, dO ~ N(0, 1) rounded to the dtype; O and LSE
+come from a plain torch fp32 masked-attention forward on the GPU
+(``gpu_forward``), outside the timed region.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+MFMA_PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16/fp16 MFMA (published figure)
+HBM_PEAK_GBS = 8000.0
+
+
+def _torch():
+    import torch
+    return torch
+
+
+# ---------------------------------------------------------------------------
+# input synthesis on the GPU
+# ---------------------------------------------------------------------------
+def to_device(case, device="cuda"):
+    """Upload a synth.Case: returns dict of torch tensors (dtype-exact values)."""
+    torch = _torch()
+    dt = torch.bfloat16 if case.dtype == "bf16" else torch.float16
+    d = {
+        "q": torch.from_numpy(case.q).to(device=device).to(dt),
+        "k": torch.from_numpy(case.k).to(device=device).to(dt),
+        "v": torch.from_numpy(case.v).to(device=device).to(dt),
+        "do": torch.from_numpy(case.do).to(device=device).to(dt),
+        "mask": None if case.mask is None else torch.from_numpy(case.mask).to(device),
+    }
+    return d
+
+
+def _seq_views(x, layout, b, length, off):
+    """[heads, length, D] view of sequence b."""
+    if layout == "BNSD":
+        return x[b, :, :length]
+    return x[off:off + length].transpose(0, 1)
+
+
+def gpu_forward(case, dev, rows_per_chunk=2048):
+    """O (case dtype) and LSE (fp32) of masked attention, computed with plain torch fp32 ops.
+
+    Input synthesis for large workloads: the block mask is expanded to an
+    element mask per chunk of query rows (block i//bx, j//by; only the
+    sequence's valid rows/columns), scores outside it are -inf, and
+    LSE = logsumexp, O = softmax * V.  Rows with no selected key get O = 0,
+    LSE = -inf.
+    """
+    torch = _torch()
+    q, k, v, mask = dev["q"], dev["k"], dev["v"], dev["mask"]
+    o = torch.zeros_like(q)
+    lse = torch.full(q.shape[:-1], float("-inf"), dtype=torch.float32, device=q.device)
+    offq = np.concatenate([[0], np.cumsum(case.len_q)[:-1]]).astype(np.int64)
+    offk = np.concatenate([[0], np.cumsum(case.len_kv)[:-1]]).astype(np.int64)
+    G = case.N // case.Nkv
+    bx, by = case.bx, case.by
+    chunk_blocks = max(1, rows_per_chunk // bx)
+    for b in range(case.B):
+        lq, lk = int(case.len_q[b]), int(case.len_kv[b])
+        if lq == 0:
+            continue
+        qs = _seq_views(q, case.layout, b, lq, offq[b])
+        ks = _seq_views(k, case.layout, b, lk, offk[b])
+        vs = _seq_views(v, case.layout, b, lk, offk[b])
+        os_ = _seq_views(o, case.layout, b, lq, offq[b])
+        ls = lse[b, :, :lq] if case.layout == "BNSD" else lse[offq[b]:offq[b] + lq].transpose(0, 1)
+        nqb_b, nkb_b = -(-lq // bx), -(-lk // by)
+        for n in range(case.N):
+            h = n // G
+            kf = ks[h].float()
+            vf = vs[h].float()
+            for ib0 in range(0, nqb_b, chunk_blocks):
+                ib1 = min(nqb_b, ib0 + chunk_blocks)
+                r0, r1 = ib0 * bx, min(ib1 * bx, lq)
+                s = case.scale * (qs[n, r0:r1].float() @ kf.t().contiguous())
+                if mask is not None and lk > 0:
+                    mb = mask[b, n, ib0:ib1, :nkb_b].bool()
+                    em = mb.repeat_interleave(bx, dim=0)[: r1 - r0].repeat_interleave(by, dim=1)[:, :lk]
+                    s.masked_fill_(~em, float("-inf"))
+                l = torch.logsumexp(s, dim=1)
+                p = torch.exp(s - l[:, None])
+                p = torch.nan_to_num(p, nan=0.0)
+                os_[n, r0:r1] = (p @ vf).to(q.dtype)
+                ls[n, r0:r1] = l
+                del s, p
+    return o, lse
+
+
+# ---------------------------------------------------------------------------
+# running the library
+# ---------------------------------------------------------------------------
+class Runner:
+    """Pre-allocated outputs and workspace for repeated bsa_bwd calls."""
+
+    def __init__(self, case, dev, o, lse):
+        torch = _torch()
+        import block_sparse_attention_bwd_amd as bsa
+        self.bsa = bsa
+        self.dev = dev
+        self.dq = torch.empty_like(dev["q"])
+        self.dk = torch.empty_like(dev["k"])
+        self.dv = torch.empty_like(dev["v"])
+        lengths = case.explicit_lengths or case.layout == "TND"
+        self.kw = dict(
+            block_sparse_mask=dev["mask"], atten_mask=None, block_shape=[case.bx, case.by],
+            actual_seq_lengths=list(map(int, case.len_q)) if lengths else None,
+            actual_seq_lengths_kv=list(map(int, case.len_kv)) if lengths else None,
+            q_input_layout=case.layout, kv_input_layout=case.layout, num_key_value_heads=case.Nkv,
+            mask_type=0, scale_value=case.scale, pre_tokens=bsa.NO_WINDOW, next_tokens=bsa.NO_WINDOW,
+            dq=self.dq, dk=self.dk, dv=self.dv)
+        self.args = (dev["do"], dev["q"], dev["k"], dev["v"], o, lse)
+        self.ws_size = bsa.bsa_bwd_workspace_size(*self.args, **self.kw)
+        self.ws = torch.empty(max(1, self.ws_size), dtype=torch.uint8, device=dev["q"].device)
+
+    def __call__(self, stream=None):
+        self.bsa.bsa_bwd(*self.args, **self.kw, workspace=self.ws, workspace_size=self.ws_size, stream=stream)
+        return self.dq, self.dk, self.dv
+
+
+# ---------------------------------------------------------------------------
+# CPU baseline: the oracle on a bounded sample
+# ---------------------------------------------------------------------------
+def cpu_baseline(case, o_host, lse_host, heads):
+    """Time the fp64 oracle backward on batch 0, the first ``heads`` KV-head groups."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    G = case.N // case.Nkv
+    nq = heads * G
+    sl_q = lambda x: x[0:1, :nq]
+    sl_k = lambda x: x[0:1, :heads]
+    mask = None if case.mask is None else case.mask[0:1, :nq]
+    kw = dict(layout="BNSD", bx=case.bx, by=case.by, scale=case.scale)
+    if case.explicit_lengths:
+        kw.update(len_q=case.len_q[:1], len_kv=case.len_kv[:1])
+    t0 = time.perf_counter()
+    oracle.backward(sl_q(case.q), sl_k(case.k), sl_k(case.v), sl_q(o_host), sl_q(case.do),
+                    sl_q(lse_host), mask, **kw)
+    dt = time.perf_counter() - t0
+    nq_b = -(-int(case.len_q[0]) // case.bx)
+    nk_b = -(-int(case.len_kv[0]) // case.by)
+    blocks = int(np.count_nonzero(mask[0, :, :nq_b, :nk_b])) if mask is not None else nq * nq_b * nk_b
+    flops = 10.0 * case.bx * case.by * case.D * blocks
+    return {
+        "value": flops / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(cores),
+        "kind": "oracle",
+        "sample": f"batch 0, query heads 0..{nq - 1} ({blocks} active blocks), fp64 NumPy, {dt:.1f} s",
+    }
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=2)
+    ap.add_argument("--cpu-heads", type=int, default=2, help="KV-head groups in the CPU oracle sample")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    args = ap.parse_args(argv)
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on exactly one GPU; --gpus must be 1",
+                          "n_gpus": args.gpus}))
+        return 2
+
+    torch = _torch()
+    import synth
+    import block_sparse_attention_bwd_amd as bsa
+
+    torch.backends.cuda.matmul.allow_tf32 = False
+    case = synth.config(args.config)
+    blocks = synth.active_blocks(case)
+    flops = 10.0 * case.bx * case.by * case.D * blocks
+    print(f"# workload {case.name}: {blocks} active blocks, {flops / 1e9:.1f} GFLOP counted", file=sys.stderr, flush=True)
+
+    dev = to_device(case)
+    o, lse = gpu_forward(case, dev)
+    torch.cuda.synchronize()
+    run = Runner(case, dev, o, lse)
+    stream = torch.cuda.current_stream()
+
+    for _ in range(args.warmup):
+        run()
+    torch.cuda.synchronize()
+
+    bsa.bsa_profile_start(args.steps)
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for _ in range(args.steps):
+        run()
+    end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(end)
+    stage_ms, ncalls = bsa.bsa_profile_stop()
+    ms = total_ms / args.steps
+    tflops = flops / (ms * 1e-3) / 1e12
+    print(f"# {ms:.4f} ms/step; stages (avg ms): " +
+          ", ".join(f"{k}={v / max(1, ncalls):.4f}" for k, v in stage_ms.items()), file=sys.stderr, flush=True)
+
+    # dominant kernel: dK/dV, credited with 4 of the 5 counted block GEMMs (S, dP, dV, dK)
+    dkdv_ms = stage_ms["dkdv"] / max(1, ncalls)
+    dkdv_flops = 8.0 * case.bx * case.by * case.D * blocks
+    achieved = dkdv_flops / (dkdv_ms * 1e-3) / 1e12
+    roofline = {
+        "bound": "mfma",
+        "achieved": round(achieved, 2),
+        "peak": MFMA_PEAK_BF16_TFLOPS,
+        "unit": "TFLOP/s",
+        "frac": round(achieved / MFMA_PEAK_BF16_TFLOPS, 4),
+        "traffic": None,
+        "kernel": "dkdv_kernel",
+        "kernel_ms": round(dkdv_ms, 5),
+        "stage_ms": {k: round(v / max(1, ncalls), 5) for k, v in stage_ms.items()},
+    }
+
+    cpu = None
+    if not args.no_cpu:
+        o_h = o.float().cpu().numpy()
+        l_h = lse.cpu().numpy()
+        cpu = cpu_baseline(case, o_h, l_h, args.cpu_heads)
+
+    out = {
+        "metric": "bwd TFLOP/s over active blocks (bf16) + % of MFMA peak, 1xMI355X",
+        "value": round(tflops, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": case.dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": case.name,
+            "layout": case.layout, "B": case.B, "N": case.N, "Nkv": case.Nkv,
+            "Sq": case.Sq, "Skv": case.Skv, "D": case.D, "block": [case.bx, case.by],
+            "active_blocks": blocks, "gflop_counted": round(flops / 1e9, 3),
+            "frac_of_mfma_peak": round(tflops / MFMA_PEAK_BF16_TFLOPS, 4),
+            "parallelism": "single-gpu",
+        },
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,73 @@
+"""Build the HIP shared library ``libbsa_bwd.so`` in-tree for gfx950.
+
+Usage: ``python -m block_sparse_attention_bwd_amd.build`` (or ``build()``).
+Always recompiles; writes the library next to this file atomically.
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+import tempfile
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIB_NAME = "libbsa_bwd.so"
+LIB_PATH = os.path.join(PKG, LIB_NAME)
+ARCH = os.environ.get("BSA_OFFLOAD_ARCH", "gfx950")
+
+SOURCES = ["bsa_api.cpp", "bsa_kernels.hip"]
+
+
+def _hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found (ROCm is required to build the library)")
+
+
+def compile_flags() -> list:
+    return [
+        f"--offload-arch={ARCH}",
+        "-O3",
+        "-std=c++17",
+        "-fPIC",
+        "-Wall",
+        # packed fp32 VALU ops stay off: the compiler would otherwise form them
+        "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        "-I", INCLUDE,
+        "-I", CSRC,
+    ]
+
+
+def build(verbose: bool = False) -> str:
+    hipcc = _hipcc()
+    with tempfile.TemporaryDirectory(prefix="bsa_build_") as tmp:
+        objs = []
+        for src in SOURCES:
+            obj = os.path.join(tmp, os.path.splitext(src)[0] + ".o")
+            cmd = [hipcc, *compile_flags(), "-c", os.path.join(CSRC, src), "-o", obj]
+            if verbose:
+                print(" ".join(cmd), flush=True)
+            r = subprocess.run(cmd, capture_output=True, text=True)
+            err = "\n".join(l for l in r.stderr.splitlines() if "packed-fp32-ops" not in l)
+            if r.returncode != 0:
+                raise RuntimeError(f"compiling {src} failed:\n{err}")
+            if verbose and err.strip():
+                print(err, file=sys.stderr)
+            objs.append(obj)
+        out_tmp = os.path.join(tmp, LIB_NAME)
+        cmd = [hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", out_tmp]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"linking {LIB_NAME} failed:\n{r.stderr}")
+        shutil.copyfile(out_tmp, LIB_PATH + ".tmp")
+        os.replace(LIB_PATH + ".tmp", LIB_PATH)
+    return LIB_PATH
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

@@ -1,0 +1,596 @@
+// Host side of the C ABI declared in include/bsa_bwd.h: argument validation
+// (aclnnBlockSparseAttentionGrad page, 参数说明 / 返回值 / 约束说明), the
+// workspace plan, and the launch sequence on the caller's stream.
+#include <hip/hip_runtime_api.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "bsa_bwd.h"
+#include "bsa_internal.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+constexpr int64_t kInt32Max = 2147483647;
+constexpr int64_t kNoWindow = 2147483647;  // preTokens/nextTokens value meaning "no sliding window"
+constexpr uint64_t kAlign = 256;
+
+uint64_t align_up(uint64_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+struct Args {
+  const bsa_tensor* dout;
+  const bsa_tensor* query;
+  const bsa_tensor* key;
+  const bsa_tensor* value;
+  const bsa_tensor* attention_out;
+  const bsa_tensor* softmax_lse;
+  const bsa_tensor* block_sparse_mask;
+  const bsa_tensor* atten_mask;
+  const int64_t* block_shape;
+  int64_t block_shape_len;
+  const int64_t* actual_seq_lengths;
+  int64_t actual_seq_lengths_len;
+  const int64_t* actual_seq_lengths_kv;
+  int64_t actual_seq_lengths_kv_len;
+  const char* q_input_layout;
+  const char* kv_input_layout;
+  int64_t num_key_value_heads;
+  int64_t mask_type;
+  double scale_value;
+  int64_t pre_tokens;
+  int64_t next_tokens;
+  const bsa_tensor* dq;
+  const bsa_tensor* dk;
+  const bsa_tensor* dv;
+};
+
+struct Plan {
+  bsa::Params p{};
+  std::vector<bsa::SeqInfo> seq;
+  uint64_t off[BSA_WS_NUM] = {};
+  int64_t dims[4] = {};
+};
+
+bool row_major_contiguous(const bsa_tensor* t) {
+  int64_t expect = 1;
+  for (int d = t->ndim - 1; d >= 0; --d) {
+    if (t->shape[d] != 1 && t->stride[d] != expect) return false;
+    expect *= t->shape[d];
+  }
+  return true;
+}
+
+const char* dtype_name(int32_t d) {
+  switch (d) {
+    case BSA_DTYPE_F16: return "float16";
+    case BSA_DTYPE_BF16: return "bfloat16";
+    case BSA_DTYPE_F32: return "float32";
+    case BSA_DTYPE_BOOL: return "bool";
+    default: return "unknown";
+  }
+}
+
+int check_dims(const bsa_tensor* t, const char* name) {
+  if (t->ndim < 1 || t->ndim > 4) return fail(BSA_ERR_PARAM_INVALID, "%s: ndim %d out of range", name, t->ndim);
+  for (int d = 0; d < t->ndim; ++d) {
+    if (t->shape[d] <= 0)
+      return fail(BSA_ERR_PARAM_INVALID, "%s: dimension %d is %lld (empty tensors are not supported)", name, d,
+                  static_cast<long long>(t->shape[d]));
+    if (t->shape[d] > kInt32Max)
+      return fail(BSA_ERR_PARAM_INVALID, "%s: dimension %d exceeds 2^31-1", name, d);
+  }
+  return BSA_OK;
+}
+
+bool same_shape(const bsa_tensor* a, const bsa_tensor* b) {
+  if (a->ndim != b->ndim) return false;
+  for (int d = 0; d < a->ndim; ++d)
+    if (a->shape[d] != b->shape[d]) return false;
+  return true;
+}
+
+int make_plan(const Args& a, Plan* plan) {
+  // ---- null pointers (返回值: 161001) ------------------------------------
+  struct Named {
+    const bsa_tensor* t;
+    const char* name;
+  };
+  const Named required[] = {{a.dout, "dout"},         {a.query, "query"},
+                            {a.key, "key"},           {a.value, "value"},
+                            {a.attention_out, "attentionOut"}, {a.softmax_lse, "softmaxLse"},
+                            {a.dq, "dq"},             {a.dk, "dk"},
+                            {a.dv, "dv"}};
+  for (const Named& n : required) {
+    if (n.t == nullptr) return fail(BSA_ERR_PARAM_NULLPTR, "%s is a null pointer", n.name);
+    if (n.t->data == nullptr) return fail(BSA_ERR_PARAM_NULLPTR, "%s has a null data pointer", n.name);
+  }
+  if (a.block_sparse_mask != nullptr && a.block_sparse_mask->data == nullptr)
+    return fail(BSA_ERR_PARAM_NULLPTR, "blockSparseMask has a null data pointer");
+  if (a.q_input_layout == nullptr || a.kv_input_layout == nullptr)
+    return fail(BSA_ERR_PARAM_NULLPTR, "input layout string is a null pointer");
+
+  // ---- layouts ----------------------------------------------------------
+  const bool q_tnd = std::strcmp(a.q_input_layout, "TND") == 0;
+  const bool q_bnsd = std::strcmp(a.q_input_layout, "BNSD") == 0;
+  const bool kv_tnd = std::strcmp(a.kv_input_layout, "TND") == 0;
+  const bool kv_bnsd = std::strcmp(a.kv_input_layout, "BNSD") == 0;
+  if (!(q_tnd || q_bnsd)) return fail(BSA_ERR_PARAM_INVALID, "qInputLayout '%s' is not BNSD or TND", a.q_input_layout);
+  if (!(kv_tnd || kv_bnsd))
+    return fail(BSA_ERR_PARAM_INVALID, "kvInputLayout '%s' is not BNSD or TND", a.kv_input_layout);
+  if (q_tnd != kv_tnd) return fail(BSA_ERR_PARAM_INVALID, "qInputLayout and kvInputLayout differ");
+  const bool tnd = q_tnd;
+  if (tnd && a.actual_seq_lengths == nullptr)
+    return fail(BSA_ERR_PARAM_NULLPTR, "TND layout needs actualSeqLengths");
+  if (tnd && a.actual_seq_lengths_kv == nullptr)
+    return fail(BSA_ERR_PARAM_NULLPTR, "TND layout needs actualSeqLengthsKv");
+
+  // ---- dtypes -----------------------------------------------------------
+  const int32_t dt = a.query->dtype;
+  if (dt != BSA_DTYPE_F16 && dt != BSA_DTYPE_BF16)
+    return fail(BSA_ERR_PARAM_INVALID, "query dtype %s is not float16/bfloat16", dtype_name(dt));
+  const Named same_dtype[] = {{a.dout, "dout"}, {a.key, "key"}, {a.value, "value"},
+                              {a.attention_out, "attentionOut"}, {a.dq, "dq"},
+                              {a.dk, "dk"}, {a.dv, "dv"}};
+  for (const Named& n : same_dtype)
+    if (n.t->dtype != dt)
+      return fail(BSA_ERR_PARAM_INVALID, "%s dtype %s differs from query dtype %s", n.name,
+                  dtype_name(n.t->dtype), dtype_name(dt));
+  if (a.softmax_lse->dtype != BSA_DTYPE_F32)
+    return fail(BSA_ERR_PARAM_INVALID, "softmaxLse dtype %s is not float32", dtype_name(a.softmax_lse->dtype));
+  if (a.block_sparse_mask && a.block_sparse_mask->dtype != BSA_DTYPE_BOOL)
+    return fail(BSA_ERR_PARAM_INVALID, "blockSparseMask dtype %s is not bool/uint8",
+                dtype_name(a.block_sparse_mask->dtype));
+
+  // ---- reserved attributes ------------------------------------------------
+  if (a.atten_mask != nullptr) return fail(BSA_ERR_PARAM_INVALID, "attenMask is not supported and must be null");
+  if (a.mask_type != 0) return fail(BSA_ERR_PARAM_INVALID, "maskType %lld is not supported (only 0)",
+                                    static_cast<long long>(a.mask_type));
+  if (a.pre_tokens != kNoWindow || a.next_tokens != kNoWindow)
+    return fail(BSA_ERR_PARAM_INVALID, "sliding window is not supported: preTokens/nextTokens must be 2147483647");
+  if (!std::isfinite(a.scale_value)) return fail(BSA_ERR_PARAM_INVALID, "scaleValue is not finite");
+
+  // ---- shapes -----------------------------------------------------------
+  const Named all[] = {{a.dout, "dout"}, {a.query, "query"}, {a.key, "key"}, {a.value, "value"},
+                       {a.attention_out, "attentionOut"}, {a.softmax_lse, "softmaxLse"},
+                       {a.dq, "dq"}, {a.dk, "dk"}, {a.dv, "dv"}};
+  for (const Named& n : all) {
+    int rc = check_dims(n.t, n.name);
+    if (rc) return rc;
+  }
+  const int want_nd = tnd ? 3 : 4;
+  const Named data_t[] = {{a.dout, "dout"}, {a.query, "query"}, {a.key, "key"}, {a.value, "value"},
+                          {a.attention_out, "attentionOut"}, {a.dq, "dq"}, {a.dk, "dk"}, {a.dv, "dv"}};
+  for (const Named& n : data_t)
+    if (n.t->ndim != want_nd)
+      return fail(BSA_ERR_PARAM_INVALID, "%s has %d dims; layout %s needs %d", n.name, n.t->ndim,
+                  a.q_input_layout, want_nd);
+  const Named qlike[] = {{a.dout, "dout"}, {a.attention_out, "attentionOut"}, {a.dq, "dq"}};
+  for (const Named& n : qlike)
+    if (!same_shape(n.t, a.query)) return fail(BSA_ERR_PARAM_INVALID, "%s shape differs from query", n.name);
+  const Named kvlike[] = {{a.value, "value"}, {a.dk, "dk"}, {a.dv, "dv"}};
+  for (const Named& n : kvlike)
+    if (!same_shape(n.t, a.key)) return fail(BSA_ERR_PARAM_INVALID, "%s shape differs from key", n.name);
+
+  const bsa_tensor* q = a.query;
+  const bsa_tensor* k = a.key;
+  int64_t B, N, Nkv, D, Sq = 0, Skv = 0, Tq = 0, Tkv = 0;
+  if (tnd) {
+    Tq = q->shape[0];
+    N = q->shape[1];
+    D = q->shape[2];
+    Tkv = k->shape[0];
+    Nkv = k->shape[1];
+    if (k->shape[2] != D) return fail(BSA_ERR_PARAM_INVALID, "key head dim differs from query");
+    B = a.actual_seq_lengths_len;
+    if (B <= 0) return fail(BSA_ERR_PARAM_INVALID, "actualSeqLengths is empty");
+    if (a.actual_seq_lengths_kv_len != B)
+      return fail(BSA_ERR_PARAM_INVALID, "actualSeqLengths and actualSeqLengthsKv have different lengths");
+  } else {
+    B = q->shape[0];
+    N = q->shape[1];
+    Sq = q->shape[2];
+    D = q->shape[3];
+    if (k->shape[0] != B) return fail(BSA_ERR_PARAM_INVALID, "key batch differs from query");
+    Nkv = k->shape[1];
+    Skv = k->shape[2];
+    if (k->shape[3] != D) return fail(BSA_ERR_PARAM_INVALID, "key head dim differs from query");
+  }
+  if (a.num_key_value_heads != Nkv)
+    return fail(BSA_ERR_PARAM_INVALID, "numKeyValueHeads %lld does not match key's head count %lld",
+                static_cast<long long>(a.num_key_value_heads), static_cast<long long>(Nkv));
+  if (N < Nkv || N % Nkv != 0)
+    return fail(BSA_ERR_PARAM_INVALID, "query heads %lld must be a multiple of KV heads %lld",
+                static_cast<long long>(N), static_cast<long long>(Nkv));
+  if (D != 64 && D != 128)
+    return fail(BSA_ERR_PARAM_INVALID, "head dim %lld is not supported (64 or 128)", static_cast<long long>(D));
+
+  // ---- contiguity: inputs contiguous, outputs unit innermost stride ----------
+  const Named inputs[] = {{a.dout, "dout"}, {a.query, "query"}, {a.key, "key"}, {a.value, "value"},
+                          {a.attention_out, "attentionOut"}, {a.softmax_lse, "softmaxLse"}};
+  for (const Named& n : inputs)
+    if (!row_major_contiguous(n.t)) return fail(BSA_ERR_PARAM_INVALID, "%s is not contiguous", n.name);
+  const Named outputs[] = {{a.dq, "dq"}, {a.dk, "dk"}, {a.dv, "dv"}};
+  for (const Named& n : outputs) {
+    if (n.t->stride[n.t->ndim - 1] != 1)
+      return fail(BSA_ERR_PARAM_INVALID, "%s innermost stride must be 1", n.name);
+    for (int d = 0; d < n.t->ndim - 1; ++d)
+      if (n.t->stride[d] < 0) return fail(BSA_ERR_PARAM_INVALID, "%s has a negative stride", n.name);
+  }
+
+  // ---- sequence lengths (参数说明: actualSeqLengths[Kv]Optional) ----------
+  std::vector<int64_t> lq(B), lk(B);
+  if (tnd) {
+    int64_t sq = 0, sk = 0;
+    for (int64_t b = 0; b < B; ++b) {
+      lq[b] = a.actual_seq_lengths[b];
+      lk[b] = a.actual_seq_lengths_kv[b];
+      if (lq[b] < 0 || lk[b] < 0) return fail(BSA_ERR_PARAM_INVALID, "negative sequence length");
+      sq += lq[b];
+      sk += lk[b];
+    }
+    if (sq != Tq) return fail(BSA_ERR_PARAM_INVALID, "actualSeqLengths sum %lld != query tokens %lld",
+                              static_cast<long long>(sq), static_cast<long long>(Tq));
+    if (sk != Tkv) return fail(BSA_ERR_PARAM_INVALID, "actualSeqLengthsKv sum %lld != key tokens %lld",
+                               static_cast<long long>(sk), static_cast<long long>(Tkv));
+    for (int64_t b = 0; b < B; ++b) {
+      Sq = lq[b] > Sq ? lq[b] : Sq;
+      Skv = lk[b] > Skv ? lk[b] : Skv;
+    }
+  } else {
+    for (int64_t b = 0; b < B; ++b) {
+      lq[b] = Sq;
+      lk[b] = Skv;
+    }
+    if (a.actual_seq_lengths != nullptr) {
+      if (a.actual_seq_lengths_len != B)
+        return fail(BSA_ERR_PARAM_INVALID, "actualSeqLengths has %lld entries, batch is %lld",
+                    static_cast<long long>(a.actual_seq_lengths_len), static_cast<long long>(B));
+      for (int64_t b = 0; b < B; ++b) {
+        lq[b] = a.actual_seq_lengths[b];
+        if (lq[b] < 0 || lq[b] > Sq) return fail(BSA_ERR_PARAM_INVALID, "actualSeqLengths[%lld] out of [0, S]",
+                                                 static_cast<long long>(b));
+      }
+    }
+    if (a.actual_seq_lengths_kv != nullptr) {
+      if (a.actual_seq_lengths_kv_len != B)
+        return fail(BSA_ERR_PARAM_INVALID, "actualSeqLengthsKv has %lld entries, batch is %lld",
+                    static_cast<long long>(a.actual_seq_lengths_kv_len), static_cast<long long>(B));
+      for (int64_t b = 0; b < B; ++b) {
+        lk[b] = a.actual_seq_lengths_kv[b];
+        if (lk[b] < 0 || lk[b] > Skv)
+          return fail(BSA_ERR_PARAM_INVALID, "actualSeqLengthsKv[%lld] out of [0, S]", static_cast<long long>(b));
+      }
+    }
+  }
+  if (Sq <= 0 || Skv <= 0) return fail(BSA_ERR_PARAM_INVALID, "every sequence is empty");
+
+  // ---- softmaxLse shape -----------------------------------------------------
+  {
+    const bsa_tensor* l = a.softmax_lse;
+    const bool trailing1 = (l->ndim == (tnd ? 3 : 4)) && l->shape[l->ndim - 1] == 1;
+    const int core = trailing1 ? l->ndim - 1 : l->ndim;
+    bool ok;
+    if (tnd) ok = (core == 2) && l->shape[0] == Tq && l->shape[1] == N;
+    else ok = (core == 3) && l->shape[0] == B && l->shape[1] == N && l->shape[2] == Sq;
+    if (!ok || (l->ndim != core && !trailing1))
+      return fail(BSA_ERR_PARAM_INVALID, "softmaxLse shape must be %s", tnd ? "[T, N] or [T, N, 1]" : "[B, N, S] or [B, N, S, 1]");
+  }
+
+  // ---- block shape and mask (参数说明: blockShapeOptional, blockSparseMaskOptional) ----
+  int64_t bx = 128, by = 128;
+  if (a.block_sparse_mask != nullptr && a.block_shape != nullptr) {
+    if (a.block_shape_len < 2) return fail(BSA_ERR_PARAM_INVALID, "blockShape needs at least two elements");
+    bx = a.block_shape[0];
+    by = a.block_shape[1];
+    if (bx <= 0 || by <= 0) return fail(BSA_ERR_PARAM_INVALID, "blockShape elements must be > 0");
+    if (bx > (int64_t(1) << 30) || by > (int64_t(1) << 30))
+      return fail(BSA_ERR_PARAM_INVALID, "blockShape elements must be <= 2^30");
+  }
+  const int64_t nqb = ceil_div(Sq, bx), nkb = ceil_div(Skv, by);
+  if (a.block_sparse_mask != nullptr) {
+    const bsa_tensor* m = a.block_sparse_mask;
+    int rc = check_dims(m, "blockSparseMask");
+    if (rc) return rc;
+    if (m->ndim != 4 || m->shape[0] != B || m->shape[1] != N || m->shape[2] != nqb || m->shape[3] != nkb)
+      return fail(BSA_ERR_PARAM_INVALID,
+                  "blockSparseMask shape must be [B, N, ceil(maxSq/bx), ceil(maxSkv/by)] = [%lld, %lld, %lld, %lld]",
+                  static_cast<long long>(B), static_cast<long long>(N), static_cast<long long>(nqb),
+                  static_cast<long long>(nkb));
+    if (!row_major_contiguous(m)) return fail(BSA_ERR_PARAM_INVALID, "blockSparseMask is not contiguous");
+  }
+  if (B * N * nqb * nkb > kInt32Max) return fail(BSA_ERR_PARAM_INVALID, "block grid too large for int32 lists");
+  const int64_t nsub_q = ceil_div(bx, 128), nsub_kv = ceil_div(by, 128);
+  if (B * N * nqb * nsub_q > kInt32Max || B * Nkv * nkb * nsub_kv > kInt32Max)
+    return fail(BSA_ERR_PARAM_INVALID, "launch grid too large");
+
+  // ---- plan -----------------------------------------------------------------
+  bsa::Params& p = plan->p;
+  p = bsa::Params{};
+  p.q = a.query->data;
+  p.k = a.key->data;
+  p.v = a.value->data;
+  p.o = a.attention_out->data;
+  p.dout = a.dout->data;
+  p.lse = static_cast<const float*>(a.softmax_lse->data);
+  p.mask = a.block_sparse_mask ? static_cast<const uint8_t*>(a.block_sparse_mask->data) : nullptr;
+  p.dq = a.dq->data;
+  p.dk = a.dk->data;
+  p.dv = a.dv->data;
+  if (tnd) {
+    p.q_sb = 0, p.q_sr = N * D, p.q_sh = D;
+    p.kv_sb = 0, p.kv_sr = Nkv * D, p.kv_sh = D;
+    p.dq_sb = 0, p.dq_sr = a.dq->stride[0], p.dq_sh = a.dq->stride[1];
+    p.dk_sb = 0, p.dk_sr = a.dk->stride[0], p.dk_sh = a.dk->stride[1];
+    p.dv_sb = 0, p.dv_sr = a.dv->stride[0], p.dv_sh = a.dv->stride[1];
+    p.lse_sb = 0, p.lse_sr = N, p.lse_sh = 1;
+  } else {
+    p.q_sb = N * Sq * D, p.q_sh = Sq * D, p.q_sr = D;
+    p.kv_sb = Nkv * Skv * D, p.kv_sh = Skv * D, p.kv_sr = D;
+    p.dq_sb = a.dq->stride[0], p.dq_sh = a.dq->stride[1], p.dq_sr = a.dq->stride[2];
+    p.dk_sb = a.dk->stride[0], p.dk_sh = a.dk->stride[1], p.dk_sr = a.dk->stride[2];
+    p.dv_sb = a.dv->stride[0], p.dv_sh = a.dv->stride[1], p.dv_sr = a.dv->stride[2];
+    p.lse_sb = N * Sq, p.lse_sh = Sq, p.lse_sr = 1;
+  }
+  p.B = static_cast<int32_t>(B);
+  p.N = static_cast<int32_t>(N);
+  p.Nkv = static_cast<int32_t>(Nkv);
+  p.G = static_cast<int32_t>(N / Nkv);
+  p.D = static_cast<int32_t>(D);
+  p.bx = static_cast<int32_t>(bx);
+  p.by = static_cast<int32_t>(by);
+  p.nqb = static_cast<int32_t>(nqb);
+  p.nkb = static_cast<int32_t>(nkb);
+  p.sq_max = static_cast<int32_t>(Sq);
+  p.dtype = dt;
+  p.scale = static_cast<float>(a.scale_value);
+  p.scale_log2e = static_cast<float>(a.scale_value * 1.4426950408889634);
+
+  plan->seq.resize(B);
+  int64_t oq = 0, ok = 0;
+  for (int64_t b = 0; b < B; ++b) {
+    bsa::SeqInfo& s = plan->seq[b];
+    s.off_q = tnd ? oq : 0;
+    s.off_kv = tnd ? ok : 0;
+    s.len_q = static_cast<int32_t>(lq[b]);
+    s.len_kv = static_cast<int32_t>(lk[b]);
+    s.wlim_q = static_cast<int32_t>(tnd ? lq[b] : Sq);
+    s.wlim_kv = static_cast<int32_t>(tnd ? lk[b] : Skv);
+    oq += lq[b];
+    ok += lk[b];
+  }
+
+  // workspace regions (sizes from shapes, block shape and lengths only)
+  uint64_t off = 0;
+  auto take = [&](int region, uint64_t bytes) {
+    plan->off[region] = off;
+    off = align_up(off + bytes);
+  };
+  const uint64_t rows = static_cast<uint64_t>(B) * N * Sq;
+  take(BSA_WS_SEQ, sizeof(bsa::SeqInfo) * static_cast<uint64_t>(B));
+  take(BSA_WS_DELTA, 4 * rows);
+  take(BSA_WS_LSE2, 4 * rows);
+  take(BSA_WS_ROW_CNT, 4ull * B * N * nqb);
+  take(BSA_WS_ROW_LIST, 4ull * B * N * nqb * nkb);
+  take(BSA_WS_COL_CNT, 4ull * B * N * nkb);
+  take(BSA_WS_COL_LIST, 4ull * B * N * nkb * nqb);
+  plan->off[BSA_WS_TOTAL] = off;
+  plan->dims[0] = bx;
+  plan->dims[1] = by;
+  plan->dims[2] = nqb;
+  plan->dims[3] = nkb;
+  return BSA_OK;
+}
+
+// ---- profiling -----------------------------------------------------------
+constexpr int kStages = 3;
+const char* const kStageNames[kStages] = {"prologue", "dkdv", "dq"};
+struct Profile {
+  bool on = false;
+  int max_calls = 0;
+  std::vector<hipEvent_t> ev;  // (kStages + 1) per call
+} g_prof;
+
+void free_profile_events() {
+  for (hipEvent_t e : g_prof.ev) (void)hipEventDestroy(e);
+  g_prof.ev.clear();
+}
+
+int record_stage(hipStream_t s) {
+  hipEvent_t e;
+  if (hipEventCreate(&e) != hipSuccess) return fail(BSA_ERR_RUNTIME, "hipEventCreate failed");
+  g_prof.ev.push_back(e);
+  if (hipEventRecord(e, s) != hipSuccess) return fail(BSA_ERR_RUNTIME, "hipEventRecord failed");
+  return BSA_OK;
+}
+
+int check_device_pointer(const void* ptr, int device, const char* name) {
+  hipPointerAttribute_t attr;
+  hipError_t e = hipPointerGetAttributes(&attr, ptr);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(BSA_ERR_PARAM_INVALID, "%s is not device memory (%s)", name, hipGetErrorString(e));
+  }
+  if (attr.type != hipMemoryTypeDevice && attr.type != hipMemoryTypeManaged && attr.type != hipMemoryTypeUnified)
+    return fail(BSA_ERR_PARAM_INVALID, "%s is not device memory", name);
+  if (attr.type == hipMemoryTypeDevice && attr.device != device)
+    return fail(BSA_ERR_PARAM_INVALID, "%s lives on device %d, the current device is %d", name, attr.device, device);
+  return BSA_OK;
+}
+
+}  // namespace
+
+#define BSA_ARGS_DECL                                                                               \
+  const bsa_tensor *dout, const bsa_tensor *query, const bsa_tensor *key, const bsa_tensor *value,  \
+      const bsa_tensor *attention_out, const bsa_tensor *softmax_lse,                               \
+      const bsa_tensor *block_sparse_mask, const bsa_tensor *atten_mask, const int64_t *block_shape, \
+      int64_t block_shape_len, const int64_t *actual_seq_lengths, int64_t actual_seq_lengths_len,   \
+      const int64_t *actual_seq_lengths_kv, int64_t actual_seq_lengths_kv_len,                      \
+      const char *q_input_layout, const char *kv_input_layout, int64_t num_key_value_heads,         \
+      int64_t mask_type, double scale_value, int64_t pre_tokens, int64_t next_tokens,               \
+      const bsa_tensor *dq, const bsa_tensor *dk, const bsa_tensor *dv
+
+#define BSA_ARGS_PACK                                                                              \
+  Args {                                                                                           \
+    dout, query, key, value, attention_out, softmax_lse, block_sparse_mask, atten_mask,            \
+        block_shape, block_shape_len, actual_seq_lengths, actual_seq_lengths_len,                  \
+        actual_seq_lengths_kv, actual_seq_lengths_kv_len, q_input_layout, kv_input_layout,         \
+        num_key_value_heads, mask_type, scale_value, pre_tokens, next_tokens, dq, dk, dv           \
+  }
+
+extern "C" {
+
+int bsa_bwd_workspace_size(BSA_ARGS_DECL, uint64_t* workspace_size) {
+  g_err.clear();
+  if (workspace_size == nullptr) return fail(BSA_ERR_PARAM_NULLPTR, "workspaceSize is a null pointer");
+  Plan plan;
+  int rc = make_plan(BSA_ARGS_PACK, &plan);
+  if (rc) return rc;
+  *workspace_size = plan.off[BSA_WS_TOTAL];
+  return BSA_OK;
+}
+
+int bsa_bwd_workspace_layout(BSA_ARGS_DECL, uint64_t* offsets, int64_t* dims) {
+  g_err.clear();
+  if (offsets == nullptr) return fail(BSA_ERR_PARAM_NULLPTR, "offsets is a null pointer");
+  Plan plan;
+  int rc = make_plan(BSA_ARGS_PACK, &plan);
+  if (rc) return rc;
+  for (int i = 0; i < BSA_WS_NUM; ++i) offsets[i] = plan.off[i];
+  if (dims)
+    for (int i = 0; i < 4; ++i) dims[i] = plan.dims[i];
+  return BSA_OK;
+}
+
+int bsa_bwd(BSA_ARGS_DECL, void* workspace, uint64_t workspace_size, void* stream) {
+  g_err.clear();
+  Plan plan;
+  int rc = make_plan(BSA_ARGS_PACK, &plan);
+  if (rc) return rc;
+  const uint64_t need = plan.off[BSA_WS_TOTAL];
+  if (workspace_size < need)
+    return fail(BSA_ERR_PARAM_INVALID, "workspace of %llu bytes is smaller than the %llu needed",
+                static_cast<unsigned long long>(workspace_size), static_cast<unsigned long long>(need));
+  if (need > 0 && workspace == nullptr) return fail(BSA_ERR_PARAM_NULLPTR, "workspace is a null pointer");
+  if (reinterpret_cast<uintptr_t>(workspace) % kAlign != 0)
+    return fail(BSA_ERR_PARAM_INVALID, "workspace must be %llu-byte aligned", static_cast<unsigned long long>(kAlign));
+
+  int device = -1;
+  if (hipGetDevice(&device) != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(BSA_ERR_RUNTIME, "hipGetDevice failed (no usable GPU?)");
+  }
+  struct Ptr {
+    const void* ptr;
+    const char* name;
+  };
+  const Ptr ptrs[] = {{dout->data, "dout"}, {query->data, "query"}, {key->data, "key"},
+                      {value->data, "value"}, {attention_out->data, "attentionOut"},
+                      {softmax_lse->data, "softmaxLse"},
+                      {block_sparse_mask ? block_sparse_mask->data : nullptr, "blockSparseMask"},
+                      {dq->data, "dq"}, {dk->data, "dk"}, {dv->data, "dv"}, {workspace, "workspace"}};
+  for (const Ptr& q : ptrs) {
+    if (q.ptr == nullptr) continue;
+    rc = check_device_pointer(q.ptr, device, q.name);
+    if (rc) return rc;
+  }
+
+  bsa::Params& p = plan.p;
+  char* ws = static_cast<char*>(workspace);
+  p.seq = reinterpret_cast<bsa::SeqInfo*>(ws + plan.off[BSA_WS_SEQ]);
+  p.delta = reinterpret_cast<float*>(ws + plan.off[BSA_WS_DELTA]);
+  p.lse2 = reinterpret_cast<float*>(ws + plan.off[BSA_WS_LSE2]);
+  p.row_cnt = reinterpret_cast<int32_t*>(ws + plan.off[BSA_WS_ROW_CNT]);
+  p.row_list = reinterpret_cast<int32_t*>(ws + plan.off[BSA_WS_ROW_LIST]);
+  p.col_cnt = reinterpret_cast<int32_t*>(ws + plan.off[BSA_WS_COL_CNT]);
+  p.col_list = reinterpret_cast<int32_t*>(ws + plan.off[BSA_WS_COL_LIST]);
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool prof = g_prof.on && g_prof.max_calls > 0;
+  if (prof) {
+    --g_prof.max_calls;
+    if ((rc = record_stage(s))) return rc;
+  }
+  int herr = 0;
+  for (size_t first = 0; first < plan.seq.size() && herr == 0; first += bsa::kMaxInlineSeq) {
+    bsa::SeqChunk chunk{};
+    chunk.first = static_cast<int32_t>(first);
+    chunk.count = static_cast<int32_t>(std::min<size_t>(bsa::kMaxInlineSeq, plan.seq.size() - first));
+    for (int i = 0; i < chunk.count; ++i) chunk.s[i] = plan.seq[first + i];
+    herr = bsa::launch_stage_seq(chunk, p.seq, stream);
+  }
+  if (herr == 0) herr = bsa::launch_prologue(p, stream);
+  if (herr) return fail(BSA_ERR_RUNTIME, "prologue launch failed: %s", hipGetErrorString(static_cast<hipError_t>(herr)));
+  if (prof && (rc = record_stage(s))) return rc;
+  herr = bsa::launch_dkdv(p, stream);
+  if (herr) return fail(BSA_ERR_RUNTIME, "dK/dV launch failed: %s", hipGetErrorString(static_cast<hipError_t>(herr)));
+  if (prof && (rc = record_stage(s))) return rc;
+  herr = bsa::launch_dq(p, stream);
+  if (herr) return fail(BSA_ERR_RUNTIME, "dQ launch failed: %s", hipGetErrorString(static_cast<hipError_t>(herr)));
+  if (prof && (rc = record_stage(s))) return rc;
+  return BSA_OK;
+}
+
+const char* bsa_last_error(void) { return g_err.c_str(); }
+
+int bsa_profile_start(int32_t max_calls) {
+  g_err.clear();
+  if (max_calls <= 0) return fail(BSA_ERR_PARAM_INVALID, "max_calls must be > 0");
+  free_profile_events();
+  g_prof.on = true;
+  g_prof.max_calls = max_calls;
+  g_prof.ev.reserve(static_cast<size_t>(max_calls) * (kStages + 1));
+  return BSA_OK;
+}
+
+int bsa_profile_stop(double* stage_ms, int32_t n_stages, int32_t* n_calls) {
+  g_err.clear();
+  const size_t per = kStages + 1;
+  const size_t calls = g_prof.ev.size() / per;
+  int rc = BSA_OK;
+  if (stage_ms)
+    for (int i = 0; i < n_stages; ++i) stage_ms[i] = 0.0;
+  for (size_t c = 0; c < calls && rc == BSA_OK; ++c) {
+    if (hipEventSynchronize(g_prof.ev[c * per + kStages]) != hipSuccess) {
+      rc = fail(BSA_ERR_RUNTIME, "hipEventSynchronize failed");
+      break;
+    }
+    for (int st = 0; st < kStages && st < n_stages; ++st) {
+      float ms = 0.f;
+      if (hipEventElapsedTime(&ms, g_prof.ev[c * per + st], g_prof.ev[c * per + st + 1]) != hipSuccess) {
+        rc = fail(BSA_ERR_RUNTIME, "hipEventElapsedTime failed");
+        break;
+      }
+      if (stage_ms) stage_ms[st] += ms;
+    }
+  }
+  if (n_calls) *n_calls = static_cast<int32_t>(calls);
+  free_profile_events();
+  g_prof.on = false;
+  g_prof.max_calls = 0;
+  return rc;
+}
+
+const char* bsa_stage_name(int32_t stage) {
+  if (stage < 0 || stage >= kStages) return nullptr;
+  return kStageNames[stage];
+}
+
+}  // extern "C"

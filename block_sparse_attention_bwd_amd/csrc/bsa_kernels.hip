@@ -1,0 +1,542 @@
+// HIP kernels of the block-sparse attention backward for gfx950 (CDNA4).
+//
+// Stages, all enqueued on the caller's stream (aclnnBlockSparseAttentionGrad
+// page, 功能说明 / 计算公式 for the equations):
+//
+//   stage_seq   copy the per-sequence table (offsets, lengths) into the workspace
+//   prologue    one launch, three block ranges:
+//                 - softmax_grad: delta = rowsum(dOut o Out) in fp32, and
+//                   lse2 = softmaxLse * log2(e), both [B, N, maxSq]
+//                 - per-Q-block lists of selected in-range KV blocks
+//                 - per-KV-block lists of selected in-range Q blocks
+//   dkdv        one workgroup per (batch, KV head, KV block [, 128-row part]);
+//               K/V rows stay in registers; walks the Q blocks that select it
+//               for every query head of its group:  S, P, dV += P^T dO,
+//               dP, dS, dK += dS^T Q  (four MFMA GEMMs per step)
+//   dq          one workgroup per (batch, query head, Q block [, part]);
+//               Q/dO rows in registers; walks its KV blocks: S, P, dP, dS,
+//               dQ += dS K (three MFMA GEMMs per step).  No atomics anywhere,
+//               so every output is written exactly once, in a fixed order.
+//
+// MFMA used: v_mfma_f32_32x32x16_{bf16,f16}.  Operand layout (wave64, lane l,
+// g = l / 32):  A[m][k]: lane holds row m = l % 32, k = 8g .. 8g+7;
+// B[k][n]: lane holds column n = l % 32, k = 8g .. 8g+7;  C[m][n] (16 fp32):
+// register i holds row 8*(i/4) + 4g + (i%4), column l % 32.
+// A C tile's registers 8h..8h+7 therefore hold, per lane, the rows
+// 16h + {4g..4g+3, 8+4g..8+4g+3}: the same (g, t) -> index map is used for
+// the K dimension of the next product, so a score tile feeds the next MFMA
+// straight from registers and only the other operand is gathered from LDS in
+// that order.
+#include <hip/hip_runtime.h>
+
+#include "bsa_internal.h"
+
+namespace bsa {
+namespace {
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kTileRows = 128;  // rows per LDS tile and per workgroup part
+
+struct EBf16 {
+  static __device__ __forceinline__ f32x16 mma(u16x8 a, u16x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                    __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ unsigned short from_f32(float x) {
+    return __builtin_bit_cast(unsigned short, static_cast<__bf16>(x));
+  }
+  static __device__ __forceinline__ float to_f32(unsigned short u) {
+    return __uint_as_float(static_cast<unsigned>(u) << 16);
+  }
+};
+
+struct EF16 {
+  static __device__ __forceinline__ f32x16 mma(u16x8 a, u16x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                   __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ unsigned short from_f32(float x) {
+    return __builtin_bit_cast(unsigned short, static_cast<_Float16>(x));
+  }
+  static __device__ __forceinline__ float to_f32(unsigned short u) {
+    return static_cast<float>(__builtin_bit_cast(_Float16, u));
+  }
+};
+
+template <class E>
+__device__ __forceinline__ u16x8 pack8(const float* x) {
+  u16x8 r;
+#pragma unroll
+  for (int t = 0; t < 8; ++t) r[t] = E::from_f32(x[t]);
+  return r;
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// ---------------------------------------------------------------------------
+// per-sequence table
+// ---------------------------------------------------------------------------
+__global__ void stage_seq_kernel(SeqChunk c, SeqInfo* dst) {
+  const int t = threadIdx.x;
+  if (t < c.count) dst[c.first + t] = c.s[t];
+}
+
+// ---------------------------------------------------------------------------
+// prologue: softmax_grad + lse2, block lists
+// ---------------------------------------------------------------------------
+constexpr int kDeltaRowsPerBlock = 64;
+
+template <class E, int D>
+__device__ void delta_part(const Params& p, int blk) {
+  constexpr int LPR = D / 8;        // lanes per row, 8 elements (16 bytes) each
+  constexpr int RPP = 256 / LPR;    // rows per pass of the 256-thread block
+  const int tid = threadIdx.x;
+  const int sub = tid % LPR, rloc = tid / LPR;
+  const int64_t total = static_cast<int64_t>(p.B) * p.N * p.sq_max;
+  const unsigned short* op = static_cast<const unsigned short*>(p.o);
+  const unsigned short* dp = static_cast<const unsigned short*>(p.dout);
+#pragma unroll 1
+  for (int pass = 0; pass < kDeltaRowsPerBlock / RPP; ++pass) {
+    const int64_t r = static_cast<int64_t>(blk) * kDeltaRowsPerBlock + pass * RPP + rloc;
+    float acc = 0.f, l2 = 0.f;
+    bool valid = false;
+    if (r < total) {
+      const int i = static_cast<int>(r % p.sq_max);
+      const int64_t bn = r / p.sq_max;
+      const int n = static_cast<int>(bn % p.N);
+      const int b = static_cast<int>(bn / p.N);
+      const SeqInfo si = p.seq[b];
+      if (i < si.len_q) {
+        valid = true;
+        const int64_t off = b * p.q_sb + (si.off_q + i) * p.q_sr + n * p.q_sh + sub * 8;
+        const u16x8 ov = *reinterpret_cast<const u16x8*>(op + off);
+        const u16x8 dv = *reinterpret_cast<const u16x8*>(dp + off);
+#pragma unroll
+        for (int t = 0; t < 8; ++t) acc += E::to_f32(dv[t]) * E::to_f32(ov[t]);
+        if (sub == 0) l2 = p.lse[b * p.lse_sb + (si.off_q + i) * p.lse_sr + n * p.lse_sh] * kLog2e;
+      }
+    }
+#pragma unroll
+    for (int m = LPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m);
+    if (r < total && sub == 0) {
+      p.delta[r] = valid ? acc : 0.f;
+      p.lse2[r] = valid ? l2 : 0.f;
+    }
+  }
+}
+
+// One wave per (b, n, Q block): ascending list of selected in-range KV blocks.
+__device__ void row_list_part(const Params& p, int blk) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int64_t R = static_cast<int64_t>(blk) * 4 + w;
+  if (R >= static_cast<int64_t>(p.B) * p.N * p.nqb) return;  // wave-uniform
+  const int ib = static_cast<int>(R % p.nqb);
+  const int b = static_cast<int>(R / p.nqb / p.N);
+  const SeqInfo si = p.seq[b];
+  const int nq_b = (si.len_q + p.bx - 1) / p.bx;
+  const int nk_b = (si.len_kv + p.by - 1) / p.by;
+  int base = 0;
+  if (ib < nq_b) {
+    int32_t* out = p.row_list + R * p.nkb;
+    const uint8_t* mrow = p.mask ? p.mask + R * p.nkb : nullptr;
+    for (int j0 = 0; j0 < nk_b; j0 += 64) {
+      const int j = j0 + lane;
+      const bool on = j < nk_b && (mrow == nullptr || mrow[j] != 0);
+      const uint64_t bal = __ballot(on);
+      const int pre = __popcll(bal & ((1ull << lane) - 1ull));
+      if (on) out[base + pre] = j;
+      base += __popcll(bal);
+    }
+  }
+  if (lane == 0) p.row_cnt[R] = base;
+}
+
+// One lane per (b, n, KV block): ascending list of selected in-range Q blocks.
+// A wave covers 64 consecutive KV blocks, so each mask row read is coalesced.
+__device__ void col_list_part(const Params& p, int blk) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int ncw = (p.nkb + 63) / 64;
+  const int64_t W = static_cast<int64_t>(blk) * 4 + w;
+  if (W >= static_cast<int64_t>(p.B) * p.N * ncw) return;  // wave-uniform
+  const int cw = static_cast<int>(W % ncw);
+  const int64_t bn = W / ncw;
+  const int b = static_cast<int>(bn / p.N);
+  const int j = cw * 64 + lane;
+  if (j >= p.nkb) return;
+  const SeqInfo si = p.seq[b];
+  const int nq_b = (si.len_q + p.bx - 1) / p.bx;
+  const int nk_b = (si.len_kv + p.by - 1) / p.by;
+  int cnt = 0;
+  if (j < nk_b) {
+    int32_t* out = p.col_list + (bn * p.nkb + j) * p.nqb;
+    const uint8_t* mcol = p.mask ? p.mask + bn * p.nqb * p.nkb + j : nullptr;
+    for (int i = 0; i < nq_b; ++i) {
+      const bool on = mcol == nullptr || mcol[static_cast<int64_t>(i) * p.nkb] != 0;
+      if (on) out[cnt++] = i;
+    }
+  }
+  p.col_cnt[bn * p.nkb + j] = cnt;
+}
+
+template <class E, int D>
+__global__ __launch_bounds__(256) void prologue_kernel(Params p, int nb_delta, int nb_rows) {
+  const int bid = blockIdx.x;
+  if (bid < nb_delta) {
+    delta_part<E, D>(p, bid);
+  } else if (bid < nb_delta + nb_rows) {
+    row_list_part(p, bid - nb_delta);
+  } else {
+    col_list_part(p, bid - nb_delta - nb_rows);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dK / dV: KV-block-outer
+// ---------------------------------------------------------------------------
+template <class E, int D>
+__global__ __launch_bounds__(256) void dkdv_kernel(Params p) {
+  constexpr int KS = D / 16;  // K=16 steps over the head dim
+  constexpr int NT = D / 32;  // 32-wide column tiles of the head dim
+  constexpr int PITCH = D + 8;
+  constexpr int CPR = D / 8;  // 16-byte chunks per row
+  __shared__ __align__(16) unsigned short sQ[kTileRows * PITCH];
+  __shared__ __align__(16) unsigned short sO[kTileRows * PITCH];  // dOut rows
+  __shared__ float sL[kTileRows];
+  __shared__ float sDl[kTileRows];
+
+  const int tid = threadIdx.x, nthr = blockDim.x;
+  const int lane = tid & 63, w = tid >> 6, l32 = lane & 31, g = lane >> 5;
+
+  int wid = blockIdx.x;
+  const int nsub = (p.by + kTileRows - 1) / kTileRows;
+  const int sub = wid % nsub;
+  wid /= nsub;
+  const int jb = wid % p.nkb;
+  wid /= p.nkb;
+  const int h = wid % p.Nkv;
+  const int b = wid / p.Nkv;
+  const SeqInfo si = p.seq[b];
+  const int kv0 = jb * p.by + sub * kTileRows;
+  const int part_end = min(jb * p.by + p.by, kv0 + kTileRows);
+  const int kv_end = min(part_end, si.len_kv);  // rows that take part
+  const int w_end = min(part_end, si.wlim_kv);  // rows this workgroup writes
+  if (kv0 >= w_end) return;                     // uniform over the workgroup
+
+  const int my_kv = kv0 + 32 * w + l32;  // B-operand column == score column of this lane
+  const bool kv_ok = my_kv < kv_end;
+  const int64_t kv_base = b * p.kv_sb + si.off_kv * p.kv_sr + h * p.kv_sh;
+  const unsigned short* kp = static_cast<const unsigned short*>(p.k) + kv_base;
+  const unsigned short* vp = static_cast<const unsigned short*>(p.v) + kv_base;
+
+  u16x8 kreg[KS], vreg[KS];
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {
+    u16x8 zk = {0, 0, 0, 0, 0, 0, 0, 0};
+    u16x8 zv = zk;
+    if (kv_ok) {
+      zk = *reinterpret_cast<const u16x8*>(kp + my_kv * p.kv_sr + 16 * s + 8 * g);
+      zv = *reinterpret_cast<const u16x8*>(vp + my_kv * p.kv_sr + 16 * s + 8 * g);
+    }
+    kreg[s] = zk;
+    vreg[s] = zv;
+  }
+
+  f32x16 adv[NT], adk[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    adv[nt] = f32x16{};
+    adk[nt] = f32x16{};
+  }
+
+  const float c2 = p.scale_log2e;
+  for (int n = h * p.G; n < (h + 1) * p.G; ++n) {
+    const int64_t bn = static_cast<int64_t>(b) * p.N + n;
+    const int cnt = p.col_cnt[bn * p.nkb + jb];
+    const int32_t* lst = p.col_list + (bn * p.nkb + jb) * p.nqb;
+    const int64_t q_base = b * p.q_sb + si.off_q * p.q_sr + n * p.q_sh;
+    const unsigned short* qp = static_cast<const unsigned short*>(p.q) + q_base;
+    const unsigned short* dop = static_cast<const unsigned short*>(p.dout) + q_base;
+    const float* l2p = p.lse2 + bn * p.sq_max;
+    const float* dlp = p.delta + bn * p.sq_max;
+    for (int e = 0; e < cnt; ++e) {
+      const int ib = lst[e];
+      const int qb_end = min(ib * p.bx + p.bx, si.len_q);
+      for (int q0 = ib * p.bx; q0 < qb_end; q0 += kTileRows) {
+        const int rows = min(kTileRows, qb_end - q0);
+        const int rows32 = (rows + 31) & ~31;
+        __syncthreads();  // the previous tile is no longer read
+        for (int idx = tid; idx < rows32 * CPR; idx += nthr) {
+          const int r = idx / CPR, c = idx % CPR;
+          u16x8 a = {0, 0, 0, 0, 0, 0, 0, 0};
+          u16x8 d = a;
+          if (r < rows) {
+            a = *reinterpret_cast<const u16x8*>(qp + (q0 + r) * p.q_sr + 8 * c);
+            d = *reinterpret_cast<const u16x8*>(dop + (q0 + r) * p.q_sr + 8 * c);
+          }
+          *reinterpret_cast<u16x8*>(sQ + r * PITCH + 8 * c) = a;
+          *reinterpret_cast<u16x8*>(sO + r * PITCH + 8 * c) = d;
+        }
+        for (int r = tid; r < rows32; r += nthr) {
+          sL[r] = r < rows ? l2p[q0 + r] : 0.f;
+          sDl[r] = r < rows ? dlp[q0 + r] : 0.f;
+        }
+        __syncthreads();
+
+        for (int c0 = 0; c0 < rows; c0 += 32) {
+          f32x16 s = {}, dpv = {};
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks) {
+            const u16x8 aq = *reinterpret_cast<const u16x8*>(sQ + (c0 + l32) * PITCH + 16 * ks + 8 * g);
+            const u16x8 ao = *reinterpret_cast<const u16x8*>(sO + (c0 + l32) * PITCH + 16 * ks + 8 * g);
+            s = E::mma(aq, kreg[ks], s);      // S[q][kv] (unscaled); this lane's column is my_kv
+            dpv = E::mma(ao, vreg[ks], dpv);  // dP[q][kv] = dOut * V^T
+          }
+          float pv[16], dsv[16];
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int qr = c0 + 8 * (i >> 2) + 4 * g + (i & 3);
+            const bool ok = kv_ok && qr < rows;
+            const float x = fast_exp2(s[i] * c2 - sL[qr]);  // P = exp(scale*S - LSE)
+            pv[i] = ok ? x : 0.f;
+            dsv[i] = ok ? x * (dpv[i] - sDl[qr]) : 0.f;      // dS = P o (dP - softmax_grad)
+          }
+          const u16x8 pa[2] = {pack8<E>(pv), pack8<E>(pv + 8)};
+          const u16x8 da[2] = {pack8<E>(dsv), pack8<E>(dsv + 8)};
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) {
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+              u16x8 bo, bq;
+#pragma unroll
+              for (int t = 0; t < 8; ++t) {
+                const int r = c0 + 16 * hh + 4 * g + (t & 3) + 8 * (t >> 2);
+                bo[t] = sO[r * PITCH + 32 * nt + l32];
+                bq[t] = sQ[r * PITCH + 32 * nt + l32];
+              }
+              adv[nt] = E::mma(pa[hh], bo, adv[nt]);  // dV += P^T * dOut
+              adk[nt] = E::mma(da[hh], bq, adk[nt]);  // dK += dS^T * Q
+            }
+          }
+        }
+      }
+    }
+  }
+
+  unsigned short* dkp = static_cast<unsigned short*>(p.dk) + b * p.dk_sb + si.off_kv * p.dk_sr + h * p.dk_sh;
+  unsigned short* dvp = static_cast<unsigned short*>(p.dv) + b * p.dv_sb + si.off_kv * p.dv_sr + h * p.dv_sh;
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int r = kv0 + 32 * w + 8 * (i >> 2) + 4 * g + (i & 3);
+      if (r < w_end) {
+        dkp[r * p.dk_sr + 32 * nt + l32] = E::from_f32(adk[nt][i] * p.scale);
+        dvp[r * p.dv_sr + 32 * nt + l32] = E::from_f32(adv[nt][i]);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dQ: Q-block-outer
+// ---------------------------------------------------------------------------
+template <class E, int D>
+__global__ __launch_bounds__(256) void dq_kernel(Params p) {
+  constexpr int KS = D / 16;
+  constexpr int NT = D / 32;
+  constexpr int PITCH = D + 8;
+  constexpr int CPR = D / 8;
+  __shared__ __align__(16) unsigned short sK[kTileRows * PITCH];
+  __shared__ __align__(16) unsigned short sV[kTileRows * PITCH];
+
+  const int tid = threadIdx.x, nthr = blockDim.x;
+  const int lane = tid & 63, w = tid >> 6, l32 = lane & 31, g = lane >> 5;
+
+  int wid = blockIdx.x;
+  const int nsub = (p.bx + kTileRows - 1) / kTileRows;
+  const int sub = wid % nsub;
+  wid /= nsub;
+  const int ib = wid % p.nqb;
+  wid /= p.nqb;
+  const int n = wid % p.N;
+  const int b = wid / p.N;
+  const SeqInfo si = p.seq[b];
+  const int q0 = ib * p.bx + sub * kTileRows;
+  const int part_end = min(ib * p.bx + p.bx, q0 + kTileRows);
+  const int q_end = min(part_end, si.len_q);
+  const int w_end = min(part_end, si.wlim_q);
+  if (q0 >= w_end) return;
+
+  const int h = n / p.G;
+  const int64_t bn = static_cast<int64_t>(b) * p.N + n;
+  const int my_q = q0 + 32 * w + l32;  // B-operand column == score column of this lane
+  const bool q_ok = my_q < q_end;
+  const int64_t q_base = b * p.q_sb + si.off_q * p.q_sr + n * p.q_sh;
+  const unsigned short* qp = static_cast<const unsigned short*>(p.q) + q_base;
+  const unsigned short* dop = static_cast<const unsigned short*>(p.dout) + q_base;
+
+  u16x8 qreg[KS], oreg[KS];
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {
+    u16x8 zq = {0, 0, 0, 0, 0, 0, 0, 0};
+    u16x8 zo = zq;
+    if (q_ok) {
+      zq = *reinterpret_cast<const u16x8*>(qp + my_q * p.q_sr + 16 * s + 8 * g);
+      zo = *reinterpret_cast<const u16x8*>(dop + my_q * p.q_sr + 16 * s + 8 * g);
+    }
+    qreg[s] = zq;
+    oreg[s] = zo;
+  }
+  const float l2 = q_ok ? p.lse2[bn * p.sq_max + my_q] : 0.f;
+  const float dl = q_ok ? p.delta[bn * p.sq_max + my_q] : 0.f;
+
+  f32x16 adq[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) adq[nt] = f32x16{};
+
+  const int64_t kv_base = b * p.kv_sb + si.off_kv * p.kv_sr + h * p.kv_sh;
+  const unsigned short* kp = static_cast<const unsigned short*>(p.k) + kv_base;
+  const unsigned short* vp = static_cast<const unsigned short*>(p.v) + kv_base;
+  const int cnt = p.row_cnt[bn * p.nqb + ib];
+  const int32_t* lst = p.row_list + (bn * p.nqb + ib) * p.nkb;
+  const float c2 = p.scale_log2e;
+
+  for (int e = 0; e < cnt; ++e) {
+    const int jb = lst[e];
+    const int kb_end = min(jb * p.by + p.by, si.len_kv);
+    for (int k0 = jb * p.by; k0 < kb_end; k0 += kTileRows) {
+      const int rows = min(kTileRows, kb_end - k0);
+      const int rows32 = (rows + 31) & ~31;
+      __syncthreads();
+      for (int idx = tid; idx < rows32 * CPR; idx += nthr) {
+        const int r = idx / CPR, c = idx % CPR;
+        u16x8 a = {0, 0, 0, 0, 0, 0, 0, 0};
+        u16x8 d = a;
+        if (r < rows) {
+          a = *reinterpret_cast<const u16x8*>(kp + (k0 + r) * p.kv_sr + 8 * c);
+          d = *reinterpret_cast<const u16x8*>(vp + (k0 + r) * p.kv_sr + 8 * c);
+        }
+        *reinterpret_cast<u16x8*>(sK + r * PITCH + 8 * c) = a;
+        *reinterpret_cast<u16x8*>(sV + r * PITCH + 8 * c) = d;
+      }
+      __syncthreads();
+
+      for (int c0 = 0; c0 < rows; c0 += 32) {
+        f32x16 st = {}, dpt = {};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          const u16x8 ak = *reinterpret_cast<const u16x8*>(sK + (c0 + l32) * PITCH + 16 * ks + 8 * g);
+          const u16x8 av = *reinterpret_cast<const u16x8*>(sV + (c0 + l32) * PITCH + 16 * ks + 8 * g);
+          st = E::mma(ak, qreg[ks], st);   // S^T[kv][q]
+          dpt = E::mma(av, oreg[ks], dpt); // dP^T[kv][q]
+        }
+        float dsv[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int kr = c0 + 8 * (i >> 2) + 4 * g + (i & 3);
+          const bool ok = q_ok && kr < rows;
+          const float x = fast_exp2(st[i] * c2 - l2);
+          dsv[i] = ok ? x * (dpt[i] - dl) : 0.f;
+        }
+        const u16x8 da[2] = {pack8<E>(dsv), pack8<E>(dsv + 8)};
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh) {
+            u16x8 bk;
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+              const int r = c0 + 16 * hh + 4 * g + (t & 3) + 8 * (t >> 2);
+              bk[t] = sK[r * PITCH + 32 * nt + l32];
+            }
+            adq[nt] = E::mma(da[hh], bk, adq[nt]);  // dQ += dS * K
+          }
+        }
+      }
+    }
+  }
+
+  unsigned short* dqp = static_cast<unsigned short*>(p.dq) + b * p.dq_sb + si.off_q * p.dq_sr + n * p.dq_sh;
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int r = q0 + 32 * w + 8 * (i >> 2) + 4 * g + (i & 3);
+      if (r < w_end) dqp[r * p.dq_sr + 32 * nt + l32] = E::from_f32(adq[nt][i] * p.scale);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dispatch
+// ---------------------------------------------------------------------------
+inline int waves_for(int rows) {
+  const int r = rows < kTileRows ? rows : kTileRows;
+  return (r + 31) / 32;
+}
+
+}  // namespace
+
+int launch_stage_seq(const SeqChunk& chunk, SeqInfo* dst, void* stream) {
+  hipLaunchKernelGGL(stage_seq_kernel, dim3(1), dim3(kMaxInlineSeq), 0,
+                     static_cast<hipStream_t>(stream), chunk, dst);
+  return static_cast<int>(hipGetLastError());
+}
+
+int launch_prologue(const Params& p, void* stream) {
+  const int64_t rows = static_cast<int64_t>(p.B) * p.N * p.sq_max;
+  const int nb_delta = static_cast<int>((rows + kDeltaRowsPerBlock - 1) / kDeltaRowsPerBlock);
+  const int nb_rows = static_cast<int>((static_cast<int64_t>(p.B) * p.N * p.nqb + 3) / 4);
+  const int ncw = (p.nkb + 63) / 64;
+  const int nb_cols = static_cast<int>((static_cast<int64_t>(p.B) * p.N * ncw + 3) / 4);
+  const dim3 grid(nb_delta + nb_rows + nb_cols), block(256);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool bf = p.dtype == 2;
+  if (p.D == 128) {
+    if (bf) hipLaunchKernelGGL((prologue_kernel<EBf16, 128>), grid, block, 0, s, p, nb_delta, nb_rows);
+    else hipLaunchKernelGGL((prologue_kernel<EF16, 128>), grid, block, 0, s, p, nb_delta, nb_rows);
+  } else {
+    if (bf) hipLaunchKernelGGL((prologue_kernel<EBf16, 64>), grid, block, 0, s, p, nb_delta, nb_rows);
+    else hipLaunchKernelGGL((prologue_kernel<EF16, 64>), grid, block, 0, s, p, nb_delta, nb_rows);
+  }
+  return static_cast<int>(hipGetLastError());
+}
+
+int launch_dkdv(const Params& p, void* stream) {
+  const int nsub = (p.by + kTileRows - 1) / kTileRows;
+  const dim3 grid(static_cast<unsigned>(static_cast<int64_t>(p.B) * p.Nkv * p.nkb * nsub));
+  const dim3 block(64 * waves_for(p.by));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool bf = p.dtype == 2;
+  if (p.D == 128) {
+    if (bf) hipLaunchKernelGGL((dkdv_kernel<EBf16, 128>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((dkdv_kernel<EF16, 128>), grid, block, 0, s, p);
+  } else {
+    if (bf) hipLaunchKernelGGL((dkdv_kernel<EBf16, 64>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((dkdv_kernel<EF16, 64>), grid, block, 0, s, p);
+  }
+  return static_cast<int>(hipGetLastError());
+}
+
+int launch_dq(const Params& p, void* stream) {
+  const int nsub = (p.bx + kTileRows - 1) / kTileRows;
+  const dim3 grid(static_cast<unsigned>(static_cast<int64_t>(p.B) * p.N * p.nqb * nsub));
+  const dim3 block(64 * waves_for(p.bx));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool bf = p.dtype == 2;
+  if (p.D == 128) {
+    if (bf) hipLaunchKernelGGL((dq_kernel<EBf16, 128>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((dq_kernel<EF16, 128>), grid, block, 0, s, p);
+  } else {
+    if (bf) hipLaunchKernelGGL((dq_kernel<EBf16, 64>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((dq_kernel<EF16, 64>), grid, block, 0, s, p);
+  }
+  return static_cast<int>(hipGetLastError());
+}
+
+}  // namespace bsa

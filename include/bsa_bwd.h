@@ -1,0 +1,191 @@
+/*
+ * bsa_bwd.h -- C ABI of the block-sparse attention backward for AMD MI355X (gfx950).
+ *
+ * Operation (aclnnBlockSparseAttentionGrad page, 功能说明 / 计算公式): given the
+ * forward S = Mask(scale * Q * K_sparse^T), P = Softmax(S), Out = P * V_sparse,
+ * compute
+ *     softmax_grad_i = sum_d dOut[i,d] * Out[i,d]          (row sum of dOut o Out)
+ *     P              = exp(scale * Q * K^T - softmaxLse)    on selected blocks only
+ *     dP             = dOut * V^T
+ *     dS             = P o (dP - softmax_grad)              (element-wise)
+ *     dV             = P^T * dOut
+ *     dQ             = (dS * K) * scale
+ *     dK             = (dS^T * Q) * scale
+ * where the block mask picks, for every Q block of blockShape[0] rows, the KV
+ * blocks of blockShape[1] rows that take part; everything outside the selected
+ * blocks is excluded from the softmax and contributes nothing.  With GQA, query
+ * head n reads KV head n / (N / Nkv) and dK/dV sum over the query heads of a
+ * group (in ascending head order, so results are run-to-run bitwise identical).
+ *
+ * Two-phase use, mirroring the page's prototypes (函数原型):
+ *   1. bsa_bwd_workspace_size(...)  -- host only: validates every argument and
+ *      returns the device workspace size the call needs (a function of the
+ *      shapes, block shape and sequence lengths only; never of the mask values).
+ *   2. bsa_bwd(..., workspace, workspace_size, stream) -- re-validates, then
+ *      enqueues the kernels on `stream` and returns without synchronising.
+ *
+ * Ownership: the caller owns every device buffer (inputs, dq/dk/dv, workspace)
+ * and the stream.  The library allocates no device memory, frees nothing and
+ * never synchronises the stream.  Host arrays (block_shape, actual_seq_*) and
+ * strings are read only during the call.  All tensors passed to bsa_bwd must
+ * live in device memory of the current HIP device.  Every element of dq/dk/dv
+ * is written (zeros where nothing contributes: padded BNSD rows, query rows
+ * that select no key, keys no row selects), so outputs need no pre-zeroing.
+ * Calls on different streams that share a workspace race; give each in-flight
+ * call its own workspace.
+ *
+ * Error behaviour: every entry point returns BSA_OK or one of the bsa_status
+ * codes below; on a non-zero status nothing has been enqueued and
+ * bsa_last_error() (thread-local) describes the first failed check.
+ */
+#ifndef BSA_BWD_H
+#define BSA_BWD_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element types (参数说明 table: FLOAT16/BFLOAT16 data, FLOAT LSE, BOOL mask). */
+enum bsa_dtype {
+  BSA_DTYPE_F16 = 1,
+  BSA_DTYPE_BF16 = 2,
+  BSA_DTYPE_F32 = 3,
+  BSA_DTYPE_BOOL = 4 /* one byte per element, nonzero = selected (UINT8 accepted) */
+};
+
+/* Status codes (返回值 table of the page; runtime/inner codes of the same family). */
+enum bsa_status {
+  BSA_OK = 0,
+  BSA_ERR_PARAM_NULLPTR = 161001, /* a required tensor/pointer is NULL; TND without lengths */
+  BSA_ERR_PARAM_INVALID = 161002, /* dtype, layout, shape, stride, attribute or size invalid */
+  BSA_ERR_RUNTIME = 361001,       /* a HIP call failed (launch, pointer query, event) */
+  BSA_ERR_INNER = 561002          /* internal planning failure */
+};
+
+/* Non-owning tensor descriptor.  `data` is a device pointer; shape and stride
+ * are in elements, outermost first; only the first `ndim` entries are read. */
+typedef struct bsa_tensor {
+  void* data;
+  int32_t dtype; /* enum bsa_dtype */
+  int32_t ndim;  /* 1..4 */
+  int64_t shape[4];
+  int64_t stride[4];
+} bsa_tensor;
+
+/*
+ * Phase 1: validate and size the workspace.  Arguments in the page's order
+ * (参数说明 of aclnnBlockSparseAttentionGradGetWorkspaceSize):
+ *
+ *  dout, query, attention_out  [B, N, Sq, D] (BNSD) or [Tq, N, D] (TND); fp16/bf16,
+ *                              contiguous.  All eight data tensors share one dtype.
+ *  key, value                  [B, Nkv, Skv, D] or [Tkv, Nkv, D]; contiguous.
+ *  softmax_lse                 fp32 [B, N, Sq] or [B, N, Sq, 1] (BNSD),
+ *                              [Tq, N] or [Tq, N, 1] (TND); natural-log
+ *                              log-sum-exp of the scaled scores; contiguous.
+ *  block_sparse_mask           bool/uint8 [B, N, ceil(maxSq/bx), ceil(maxSkv/by)],
+ *                              contiguous; NULL = every block selected.
+ *  atten_mask                  reserved: must be NULL.
+ *  block_shape, _len           {bx, by} (first two entries used, each > 0);
+ *                              NULL = {128, 128}.  Ignored without a mask.
+ *  actual_seq_lengths(_kv), _len
+ *                              per-sequence token counts, length B.  Required
+ *                              for TND (sums must equal Tq / Tkv); optional for
+ *                              BNSD (each in [0, S]; padding past it is ignored
+ *                              and its outputs are zero).
+ *  q_input_layout, kv_input_layout   "BNSD" or "TND", equal.
+ *  num_key_value_heads         Nkv; N >= Nkv and N % Nkv == 0 (约束说明).
+ *  mask_type                   reserved: must be 0.
+ *  scale_value                 the scale (typically D^-0.5); finite.
+ *  pre_tokens, next_tokens     reserved: must be 2147483647.
+ *  dq, dk, dv                  outputs, same dtype/shape as query/key/value;
+ *                              any outer strides, innermost stride 1.
+ *  workspace_size              out: bytes of device workspace needed.
+ *
+ * Head dim D must be 64 or 128 (the tile set built into this library).
+ */
+int bsa_bwd_workspace_size(const bsa_tensor* dout, const bsa_tensor* query, const bsa_tensor* key,
+                           const bsa_tensor* value, const bsa_tensor* attention_out,
+                           const bsa_tensor* softmax_lse, const bsa_tensor* block_sparse_mask,
+                           const bsa_tensor* atten_mask, const int64_t* block_shape,
+                           int64_t block_shape_len, const int64_t* actual_seq_lengths,
+                           int64_t actual_seq_lengths_len, const int64_t* actual_seq_lengths_kv,
+                           int64_t actual_seq_lengths_kv_len, const char* q_input_layout,
+                           const char* kv_input_layout, int64_t num_key_value_heads,
+                           int64_t mask_type, double scale_value, int64_t pre_tokens,
+                           int64_t next_tokens, const bsa_tensor* dq, const bsa_tensor* dk,
+                           const bsa_tensor* dv, uint64_t* workspace_size);
+
+/*
+ * Phase 2 (aclnnBlockSparseAttentionGrad): same arguments, then the device
+ * workspace (at least the size phase 1 returned, 256-byte aligned; may be NULL
+ * only if that size is 0) and the hipStream_t to enqueue on (NULL = the null
+ * stream).  Returns after enqueueing; completion is observed through the stream.
+ */
+int bsa_bwd(const bsa_tensor* dout, const bsa_tensor* query, const bsa_tensor* key,
+            const bsa_tensor* value, const bsa_tensor* attention_out, const bsa_tensor* softmax_lse,
+            const bsa_tensor* block_sparse_mask, const bsa_tensor* atten_mask,
+            const int64_t* block_shape, int64_t block_shape_len, const int64_t* actual_seq_lengths,
+            int64_t actual_seq_lengths_len, const int64_t* actual_seq_lengths_kv,
+            int64_t actual_seq_lengths_kv_len, const char* q_input_layout,
+            const char* kv_input_layout, int64_t num_key_value_heads, int64_t mask_type,
+            double scale_value, int64_t pre_tokens, int64_t next_tokens, const bsa_tensor* dq,
+            const bsa_tensor* dk, const bsa_tensor* dv, void* workspace, uint64_t workspace_size,
+            void* stream);
+
+/* Workspace regions, as byte offsets filled in by bsa_bwd_workspace_layout. */
+enum bsa_ws_region {
+  BSA_WS_SEQ = 0,      /* per-sequence table: {int64 q_offset, int64 kv_offset, int32 len_q, int32 len_kv, pad} x B */
+  BSA_WS_DELTA = 1,    /* fp32 [B, N, maxSq]: softmax_grad (row sums of dOut o Out); 0 past len_q */
+  BSA_WS_LSE2 = 2,     /* fp32 [B, N, maxSq]: softmaxLse * log2(e) */
+  BSA_WS_ROW_CNT = 3,  /* int32 [B, N, nQB]: number of selected in-range KV blocks per Q block */
+  BSA_WS_ROW_LIST = 4, /* int32 [B, N, nQB, nKB]: ascending KV-block lists, first ROW_CNT entries valid */
+  BSA_WS_COL_CNT = 5,  /* int32 [B, N, nKB]: number of selected in-range Q blocks per KV block */
+  BSA_WS_COL_LIST = 6, /* int32 [B, N, nKB, nQB]: ascending Q-block lists, first COL_CNT entries valid */
+  BSA_WS_TOTAL = 7,    /* total bytes (== the phase-1 size) */
+  BSA_WS_NUM = 8
+};
+
+/*
+ * Test and tooling hook: the same validation as phase 1, then the byte offset
+ * of every workspace region (offsets[BSA_WS_NUM]) and the plan's block grid
+ * (dims[4] = {bx, by, nQB, nKB}; may be NULL).  After a bsa_bwd call has
+ * completed, these regions hold the delta pre-pass and the mask compaction.
+ */
+int bsa_bwd_workspace_layout(const bsa_tensor* dout, const bsa_tensor* query,
+                             const bsa_tensor* key, const bsa_tensor* value,
+                             const bsa_tensor* attention_out, const bsa_tensor* softmax_lse,
+                             const bsa_tensor* block_sparse_mask, const bsa_tensor* atten_mask,
+                             const int64_t* block_shape, int64_t block_shape_len,
+                             const int64_t* actual_seq_lengths, int64_t actual_seq_lengths_len,
+                             const int64_t* actual_seq_lengths_kv,
+                             int64_t actual_seq_lengths_kv_len, const char* q_input_layout,
+                             const char* kv_input_layout, int64_t num_key_value_heads,
+                             int64_t mask_type, double scale_value, int64_t pre_tokens,
+                             int64_t next_tokens, const bsa_tensor* dq, const bsa_tensor* dk,
+                             const bsa_tensor* dv, uint64_t* offsets, int64_t* dims);
+
+/* Message for the last non-zero status returned on this thread ("" if none). */
+const char* bsa_last_error(void);
+
+/*
+ * Per-stage timing for benchmarks.  bsa_profile_start(max_calls) makes the
+ * next max_calls bsa_bwd calls on this process record HIP events between
+ * their kernel stages (on the call's stream).  bsa_profile_stop waits for the
+ * recorded events, writes the summed milliseconds of each stage into
+ * stage_ms[0..n_stages) (stage order: 0 = sequence table + delta + mask
+ * compaction, 1 = dK/dV, 2 = dQ), writes the number of profiled calls to
+ * *n_calls, frees the events and turns recording off.  Not thread-safe.
+ */
+int bsa_profile_start(int32_t max_calls);
+int bsa_profile_stop(double* stage_ms, int32_t n_stages, int32_t* n_calls);
+
+/* Name of a profiling stage, or NULL past the last one. */
+const char* bsa_stage_name(int32_t stage);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BSA_BWD_H */

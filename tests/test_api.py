@@ -1,0 +1,220 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports
+every function the header declares, and phase 1 returns the documented status
+for every invalid argument (aclnnBlockSparseAttentionGrad page, 返回值 table:
+161001 for null inputs and TND without lengths, 161002 for invalid dtypes,
+layouts and other parameters)."""
+import ctypes
+import os
+
+import pytest
+import torch
+
+import block_sparse_attention_bwd_amd as bsa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    if not os.path.exists(bsa.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+    bsa.load_library()
+
+
+def test_exports_every_header_function():
+    lib = bsa.load_library()
+    names = bsa.header_functions()
+    assert {"bsa_bwd_workspace_size", "bsa_bwd", "bsa_last_error"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def _bnsd(B=2, N=4, Nkv=2, Sq=300, Skv=270, D=128, dt=torch.bfloat16, bx=128, by=128):
+    q = torch.zeros(B, N, Sq, D, dtype=dt)
+    k = torch.zeros(B, Nkv, Skv, D, dtype=dt)
+    lse = torch.zeros(B, N, Sq, dtype=torch.float32)
+    mask = torch.ones(B, N, -(-Sq // bx), -(-Skv // by), dtype=torch.bool)
+    return dict(dout=q, query=q, key=k, value=k, attention_out=q, softmax_lse=lse, block_sparse_mask=mask,
+                atten_mask=None, block_shape=[bx, by], actual_seq_lengths=None, actual_seq_lengths_kv=None,
+                q_input_layout="BNSD", kv_input_layout="BNSD", num_key_value_heads=Nkv, mask_type=0,
+                scale_value=D ** -0.5, pre_tokens=bsa.NO_WINDOW, next_tokens=bsa.NO_WINDOW,
+                dq=q.clone(), dk=k.clone(), dv=k.clone())
+
+
+def _tnd(lq=(100, 37, 250), lk=(80, 90, 5), N=4, Nkv=1, D=64, dt=torch.float16, bx=64, by=128):
+    q = torch.zeros(sum(lq), N, D, dtype=dt)
+    k = torch.zeros(sum(lk), Nkv, D, dtype=dt)
+    lse = torch.zeros(sum(lq), N, 1, dtype=torch.float32)
+    mask = torch.ones(len(lq), N, -(-max(lq) // bx), -(-max(lk) // by), dtype=torch.uint8)
+    return dict(dout=q, query=q, key=k, value=k, attention_out=q, softmax_lse=lse, block_sparse_mask=mask,
+                atten_mask=None, block_shape=[bx, by], actual_seq_lengths=list(lq),
+                actual_seq_lengths_kv=list(lk), q_input_layout="TND", kv_input_layout="TND",
+                num_key_value_heads=Nkv, mask_type=0, scale_value=D ** -0.5, pre_tokens=bsa.NO_WINDOW,
+                next_tokens=bsa.NO_WINDOW, dq=q.clone(), dk=k.clone(), dv=k.clone())
+
+
+def _code(args):
+    try:
+        bsa.bsa_bwd_workspace_size(**args)
+    except bsa.BsaError as e:
+        assert bsa.bsa_last_error() == e.message
+        return e.code
+    return bsa.BSA_OK
+
+
+def test_valid_arguments_are_accepted():
+    assert bsa.bsa_bwd_workspace_size(**_bnsd()) > 0
+    assert bsa.bsa_bwd_workspace_size(**_tnd()) > 0
+    a = _bnsd()
+    a["softmax_lse"] = a["softmax_lse"][..., None]  # trailing 1 accepted
+    assert _code(a) == bsa.BSA_OK
+    a = _bnsd()
+    a["block_sparse_mask"] = None  # no mask = dense; block shape ignored
+    a["block_shape"] = [0, 0]
+    assert _code(a) == bsa.BSA_OK
+    a = _bnsd(bx=64, by=128)
+    a["block_shape"] = [64, 128, 999]  # at least two elements; the first two are used
+    assert _code(a) == bsa.BSA_OK
+    a = _bnsd(bx=128, by=128)
+    a["block_shape"] = None  # default [128, 128]
+    assert _code(a) == bsa.BSA_OK
+    a = _bnsd()
+    a["actual_seq_lengths"] = [300, 17]
+    a["actual_seq_lengths_kv"] = [0, 270]
+    assert _code(a) == bsa.BSA_OK
+
+
+def test_workspace_size_depends_on_shapes_only():
+    a = _bnsd()
+    s1 = bsa.bsa_bwd_workspace_size(**a)
+    a["block_sparse_mask"] = torch.zeros_like(a["block_sparse_mask"])
+    assert bsa.bsa_bwd_workspace_size(**a) == s1
+    a["block_sparse_mask"] = torch.rand(a["block_sparse_mask"].shape) < 0.3
+    assert bsa.bsa_bwd_workspace_size(**a) == s1
+    b = _bnsd(Sq=600)
+    assert bsa.bsa_bwd_workspace_size(**b) > s1
+
+
+def test_layout_regions_are_ordered_and_aligned():
+    offs, dims = bsa.bsa_bwd_workspace_layout(**_tnd())
+    vals = [offs[k] for k in bsa.WS_REGIONS]
+    assert vals == sorted(vals)
+    assert all(v % 256 == 0 for v in vals)
+    assert offs["total"] == bsa.bsa_bwd_workspace_size(**_tnd())
+    assert dims == (64, 128, 4, 1)
+
+
+NULLPTR = bsa.BSA_ERR_PARAM_NULLPTR
+INVALID = bsa.BSA_ERR_PARAM_INVALID
+
+
+def _mut(base, **kv):
+    a = base()
+    a.update(kv)
+    return a
+
+
+def _tr(x):
+    return x.transpose(-1, -2).contiguous().transpose(-1, -2)
+
+
+CASES = [
+    # null inputs (161001)
+    ("dout null", lambda: _mut(_bnsd, dout=None), NULLPTR),
+    ("query null", lambda: _mut(_bnsd, query=None), NULLPTR),
+    ("key null", lambda: _mut(_bnsd, key=None), NULLPTR),
+    ("value null", lambda: _mut(_bnsd, value=None), NULLPTR),
+    ("attentionOut null", lambda: _mut(_bnsd, attention_out=None), NULLPTR),
+    ("softmaxLse null", lambda: _mut(_bnsd, softmax_lse=None), NULLPTR),
+    ("dq null", lambda: _mut(_bnsd, dq=None), NULLPTR),
+    ("dk null", lambda: _mut(_bnsd, dk=None), NULLPTR),
+    ("dv null", lambda: _mut(_bnsd, dv=None), NULLPTR),
+    ("TND without q lengths", lambda: _mut(_tnd, actual_seq_lengths=None), NULLPTR),
+    ("TND without kv lengths", lambda: _mut(_tnd, actual_seq_lengths_kv=None), NULLPTR),
+    ("layout string null", lambda: _mut(_bnsd, q_input_layout=None), NULLPTR),
+    # invalid dtypes (161002)
+    ("fp32 data", lambda: _mut(_bnsd, query=torch.zeros(2, 4, 300, 128)), INVALID),
+    ("mixed dtypes", lambda: _mut(_bnsd, key=torch.zeros(2, 2, 270, 128, dtype=torch.float16),
+                                  value=torch.zeros(2, 2, 270, 128, dtype=torch.float16)), INVALID),
+    ("fp16 lse", lambda: _mut(_bnsd, softmax_lse=torch.zeros(2, 4, 300, dtype=torch.float16)), INVALID),
+    ("float mask", lambda: _mut(_bnsd, block_sparse_mask=torch.ones(2, 4, 3, 3)), INVALID),
+    ("fp16 dq with bf16 inputs", lambda: _mut(_bnsd, dq=torch.zeros(2, 4, 300, 128, dtype=torch.float16)), INVALID),
+    # invalid layouts
+    ("layout BSND", lambda: _mut(_bnsd, q_input_layout="BSND", kv_input_layout="BSND"), INVALID),
+    ("layouts differ", lambda: _mut(_bnsd, kv_input_layout="TND"), INVALID),
+    ("ndim mismatch", lambda: _mut(_bnsd, q_input_layout="TND", kv_input_layout="TND",
+                                   actual_seq_lengths=[300, 300], actual_seq_lengths_kv=[270, 270]), INVALID),
+    # heads and dims
+    ("N % Nkv != 0", lambda: _mut(lambda: _bnsd(N=3, Nkv=2)), INVALID),
+    ("N < Nkv", lambda: _mut(lambda: _bnsd(N=2, Nkv=4)), INVALID),
+    ("numKeyValueHeads mismatch", lambda: _mut(_bnsd, num_key_value_heads=1), INVALID),
+    ("head dim 96", lambda: _mut(lambda: _bnsd(D=96)), INVALID),
+    ("query/key batch differ", lambda: _mut(_bnsd, key=torch.zeros(1, 2, 270, 128, dtype=torch.bfloat16)), INVALID),
+    ("dout shape differs", lambda: _mut(_bnsd, dout=torch.zeros(2, 4, 299, 128, dtype=torch.bfloat16)), INVALID),
+    ("dk shape differs", lambda: _mut(_bnsd, dk=torch.zeros(2, 2, 271, 128, dtype=torch.bfloat16)), INVALID),
+    ("lse shape", lambda: _mut(_bnsd, softmax_lse=torch.zeros(2, 4, 299)), INVALID),
+    ("lse trailing 2", lambda: _mut(_bnsd, softmax_lse=torch.zeros(2, 4, 300, 2)), INVALID),
+    ("empty dim", lambda: _mut(_bnsd, query=torch.zeros(2, 4, 0, 128, dtype=torch.bfloat16)), NULLPTR),
+    # mask and block shape
+    ("mask shape", lambda: _mut(_bnsd, block_sparse_mask=torch.ones(2, 4, 3, 2, dtype=torch.bool)), INVALID),
+    ("mask on KV heads", lambda: _mut(_bnsd, block_sparse_mask=torch.ones(2, 2, 3, 3, dtype=torch.bool)), INVALID),
+    ("blockShape one element", lambda: _mut(_bnsd, block_shape=[128]), INVALID),
+    ("blockShape zero", lambda: _mut(_bnsd, block_shape=[0, 128]), INVALID),
+    ("blockShape negative", lambda: _mut(_bnsd, block_shape=[128, -1]), INVALID),
+    ("blockShape mismatches mask", lambda: _mut(_bnsd, block_shape=[64, 128]), INVALID),
+    # reserved attributes
+    ("attenMask given", lambda: _mut(_bnsd, atten_mask=torch.zeros(300, 270, dtype=torch.bool)), INVALID),
+    ("maskType 1", lambda: _mut(_bnsd, mask_type=1), INVALID),
+    ("preTokens", lambda: _mut(_bnsd, pre_tokens=1024), INVALID),
+    ("nextTokens", lambda: _mut(_bnsd, next_tokens=0), INVALID),
+    ("scale NaN", lambda: _mut(_bnsd, scale_value=float("nan")), INVALID),
+    # strides
+    ("non-contiguous query", lambda: _mut(_bnsd, query=_tr(torch.zeros(2, 4, 300, 128, dtype=torch.bfloat16))), INVALID),
+    ("non-contiguous key", lambda: _mut(_bnsd, key=torch.zeros(2, 270, 2, 128, dtype=torch.bfloat16).transpose(1, 2)), INVALID),
+    ("dq inner stride", lambda: _mut(_bnsd, dq=_tr(torch.zeros(2, 4, 300, 128, dtype=torch.bfloat16))), INVALID),
+    # sequence lengths
+    ("BNSD length > S", lambda: _mut(_bnsd, actual_seq_lengths=[301, 3]), INVALID),
+    ("BNSD length count", lambda: _mut(_bnsd, actual_seq_lengths=[300]), INVALID),
+    ("BNSD negative length", lambda: _mut(_bnsd, actual_seq_lengths_kv=[-1, 3]), INVALID),
+    ("TND q sum", lambda: _mut(_tnd, actual_seq_lengths=[100, 37, 249]), INVALID),
+    ("TND kv sum", lambda: _mut(_tnd, actual_seq_lengths_kv=[80, 90, 6]), INVALID),
+    ("TND count mismatch", lambda: _mut(_tnd, actual_seq_lengths_kv=[170, 5]), INVALID),
+    ("TND prefix sums", lambda: _mut(_tnd, actual_seq_lengths=[100, 137, 387]), INVALID),
+]
+
+
+@pytest.mark.parametrize("name,make,code", CASES, ids=[c[0] for c in CASES])
+def test_phase1_status(name, make, code):
+    assert _code(make()) == code
+
+
+def test_null_workspace_size_pointer():
+    lib = bsa.load_library()
+    from block_sparse_attention_bwd_amd._binding import _marshal
+    a = _bnsd()
+    args = _marshal(**a)
+    assert lib.bsa_bwd_workspace_size(*args, None) == NULLPTR
+
+
+def test_phase2_rejects_before_touching_the_device():
+    """bsa_bwd re-validates; a short or null workspace fails before any HIP call."""
+    lib = bsa.load_library()
+    from block_sparse_attention_bwd_amd._binding import _marshal
+    a = _bnsd()
+    need = bsa.bsa_bwd_workspace_size(**a)
+    args = _marshal(**a)
+    assert lib.bsa_bwd(*args, ctypes.c_void_p(4096), need - 1, None) == INVALID
+    assert lib.bsa_bwd(*args, None, need, None) == NULLPTR
+    assert lib.bsa_bwd(*args, ctypes.c_void_p(4096 + 8), need, None) == INVALID  # misaligned
+    bad = _marshal(**_mut(_bnsd, mask_type=3))
+    assert lib.bsa_bwd(*bad, ctypes.c_void_p(4096), need, None) == INVALID
+
+
+def test_binding_refuses_cpu_tensors_for_phase2():
+    with pytest.raises(ValueError):
+        bsa.bsa_bwd(**_bnsd(), workspace=None, workspace_size=0)
+
+
+def test_stage_names():
+    assert [bsa.bsa_stage_name(i) for i in range(4)] == ["prologue", "dkdv", "dq", None]

@@ -1,0 +1,285 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 oracle.
+
+Bars: block lists bit-exact; dQ, dK, dV per tensor within
+max|gpu - ref| <= tol * max|ref| (tol 5e-3 fp16, 2e-2 bf16); bitwise
+run-to-run determinism.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from gpu_common import TOL, assert_close, oracle_fwd_inputs, oracle_kw, run_bsa, to_np, upload
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import block_sparse_attention_bwd_amd as bsa
+    bsa.load_library()
+    torch.backends.cuda.matmul.allow_tf32 = False
+    yield
+
+
+def _case(name):
+    mk = synth.make_case
+    cases = {
+        "config1": lambda: synth.config(1),
+        # several 128x128 tiles with ragged tails on both axes, GQA 4/2
+        "bnsd_bf16_d128_b128x128_ragged": lambda: mk(layout="BNSD", dtype="bf16", B=2, N=4, Nkv=2, D=128,
+                                                     Sq=300, Skv=270, bx=128, by=128, p=0.5, seed=101),
+        # padded BNSD (actual lengths), D=64, 64x128 blocks
+        "bnsd_fp16_d64_b64x128_padded": lambda: mk(layout="BNSD", dtype="fp16", B=2, N=2, Nkv=1, D=64,
+                                                   Sq=256, Skv=320, bx=64, by=128, p=0.5,
+                                                   lengths_q=[256, 150], lengths_kv=[320, 97], seed=102),
+        # varlen TND, GQA 4/1
+        "tnd_fp16_d128_b64x128_gqa": lambda: mk(layout="TND", dtype="fp16", B=3, N=4, Nkv=1, D=128,
+                                                bx=64, by=128, p=0.4, lengths_q=[200, 77, 333],
+                                                lengths_kv=[260, 129, 190], seed=103),
+        "bnsd_bf16_d128_b128x64": lambda: mk(layout="BNSD", dtype="bf16", B=1, N=2, Nkv=2, D=128,
+                                             Sq=256, Skv=520, bx=128, by=64, p=0.3, seed=104),
+        # block sizes that are not multiples of the 32-row MFMA tile
+        "bnsd_bf16_d64_b48x80": lambda: mk(layout="BNSD", dtype="bf16", B=1, N=2, Nkv=1, D=64,
+                                           Sq=200, Skv=230, bx=48, by=80, p=0.5, seed=105),
+        # blocks larger than the 128-row workgroup part
+        "bnsd_fp16_d128_b256x256": lambda: mk(layout="BNSD", dtype="fp16", B=1, N=2, Nkv=2, D=128,
+                                              Sq=600, Skv=530, bx=256, by=256, p=0.6, seed=106),
+        # element-level mask (1x1 blocks), some rows select nothing
+        "bnsd_bf16_d64_b1x1": lambda: mk(layout="BNSD", dtype="bf16", B=1, N=2, Nkv=1, D=64,
+                                         Sq=40, Skv=37, bx=1, by=1, mask_rule="bernoulli", p=0.3, seed=107),
+        # null mask = dense
+        "bnsd_bf16_d128_nullmask": lambda: mk(layout="BNSD", dtype="bf16", B=1, N=2, Nkv=1, D=128,
+                                              Sq=200, Skv=300, mask_rule="dense", seed=108),
+        # a sequence with no queries and one with no keys
+        "tnd_bf16_d64_empty_seqs": lambda: mk(layout="TND", dtype="bf16", B=3, N=2, Nkv=2, D=64,
+                                              bx=64, by=64, p=0.5, lengths_q=[100, 0, 60],
+                                              lengths_kv=[50, 70, 0], seed=109),
+        # rows without the diagonal: empty Q-block rows and unselected KV blocks
+        "bnsd_fp16_d128_sparse_rows": lambda: mk(layout="BNSD", dtype="fp16", B=1, N=2, Nkv=1, D=128,
+                                                 Sq=512, Skv=512, bx=64, by=64, mask_rule="bernoulli",
+                                                 p=0.15, seed=110),
+    }
+    return cases[name]()
+
+
+SMALL = ["config1", "bnsd_bf16_d128_b128x128_ragged", "bnsd_fp16_d64_b64x128_padded",
+         "tnd_fp16_d128_b64x128_gqa", "bnsd_bf16_d128_b128x64", "bnsd_bf16_d64_b48x80",
+         "bnsd_fp16_d128_b256x256", "bnsd_bf16_d64_b1x1", "bnsd_bf16_d128_nullmask",
+         "tnd_bf16_d64_empty_seqs", "bnsd_fp16_d128_sparse_rows"]
+
+_cache = {}
+
+
+def _prepared(name):
+    if name not in _cache:
+        c = _case(name)
+        o, lse = oracle_fwd_inputs(c)
+        ref = oracle.backward(c.q, c.k, c.v, o, c.do, lse, c.mask, **oracle_kw(c))
+        _cache[name] = (c, o, lse, ref)
+    return _cache[name]
+
+
+@pytest.mark.parametrize("name", SMALL)
+def test_small_case_parity(name):
+    c, o, lse, ref = _prepared(name)
+    print(f"[parity] {name}", flush=True)
+    dev = upload(c, o, lse)
+    (dq, dk, dv), _ = run_bsa(c, dev)
+    torch.cuda.synchronize()
+    floor = float(np.abs(ref[2]).max())
+    for nm, got, want in (("dq", dq, ref[0]), ("dk", dk, ref[1]), ("dv", dv, ref[2])):
+        assert_close(f"{name}/{nm}", to_np(got), want, c.dtype, floor_ref=floor)
+
+
+def _read_ws(runner, offs, name, count, dtype=np.int32):
+    import block_sparse_attention_bwd_amd  # noqa: F401
+    start = offs[name]
+    nbytes = count * np.dtype(dtype).itemsize
+    return runner.ws[start:start + nbytes].cpu().numpy().view(dtype)
+
+
+@pytest.mark.parametrize("name", SMALL)
+def test_block_lists_bit_exact(name):
+    import block_sparse_attention_bwd_amd as bsa
+    c, o, lse, _ = _prepared(name)
+    dev = upload(c, o, lse)
+    _, r = run_bsa(c, dev)
+    torch.cuda.synchronize()
+    offs, (bx, by, nqb, nkb) = bsa.bsa_bwd_workspace_layout(*r.args, **r.kw)
+    rows, cols = oracle.block_lists(c.mask, c.B, c.N, nqb, nkb, bx, by, c.len_q, c.len_kv)
+    rc = _read_ws(r, offs, "row_cnt", c.B * c.N * nqb).reshape(c.B, c.N, nqb)
+    rl = _read_ws(r, offs, "row_list", c.B * c.N * nqb * nkb).reshape(c.B, c.N, nqb, nkb)
+    cc = _read_ws(r, offs, "col_cnt", c.B * c.N * nkb).reshape(c.B, c.N, nkb)
+    cl = _read_ws(r, offs, "col_list", c.B * c.N * nkb * nqb).reshape(c.B, c.N, nkb, nqb)
+    for b in range(c.B):
+        for n in range(c.N):
+            for i in range(nqb):
+                assert rc[b, n, i] == len(rows[b][n][i]), (b, n, i)
+                assert list(rl[b, n, i, :rc[b, n, i]]) == rows[b][n][i], (b, n, i)
+            for j in range(nkb):
+                assert cc[b, n, j] == len(cols[b][n][j]), (b, n, j)
+                assert list(cl[b, n, j, :cc[b, n, j]]) == cols[b][n][j], (b, n, j)
+
+
+@pytest.mark.parametrize("name", ["config1", "tnd_fp16_d128_b64x128_gqa", "bnsd_fp16_d64_b64x128_padded"])
+def test_delta_and_lse2(name):
+    import block_sparse_attention_bwd_amd as bsa
+    c, o, lse, _ = _prepared(name)
+    dev = upload(c, o, lse)
+    _, r = run_bsa(c, dev)
+    torch.cuda.synchronize()
+    offs, _ = bsa.bsa_bwd_workspace_layout(*r.args, **r.kw)
+    sq = c.Sq
+    delta = _read_ws(r, offs, "delta", c.B * c.N * sq, np.float32).reshape(c.B, c.N, sq)
+    lse2 = _read_ws(r, offs, "lse2", c.B * c.N * sq, np.float32).reshape(c.B, c.N, sq)
+    offq = oracle.sequence_offsets(c.len_q)
+    for b in range(c.B):
+        L = int(c.len_q[b])
+        if c.layout == "BNSD":
+            dob, ob, lb = c.do[b, :, :L], o[b, :, :L], lse[b, :, :L]
+        else:
+            dob = c.do[offq[b]:offq[b] + L].transpose(1, 0, 2)
+            ob = o[offq[b]:offq[b] + L].transpose(1, 0, 2)
+            lb = lse[offq[b]:offq[b] + L].T
+        want = oracle.softmax_grad(dob, ob)
+        mag = np.sum(np.abs(dob.astype(np.float64) * ob), axis=-1)
+        assert np.all(np.abs(delta[b, :, :L] - want) <= 1e-5 * mag + 1e-30)
+        assert np.all(delta[b, :, L:] == 0)
+        fin = np.isfinite(lb)
+        np.testing.assert_allclose(lse2[b, :, :L][fin], lb[fin].astype(np.float64) * math.log2(math.e), rtol=1e-6)
+
+
+@pytest.mark.parametrize("name", ["bnsd_bf16_d128_b128x128_ragged", "tnd_fp16_d128_b64x128_gqa"])
+def test_bitwise_deterministic(name):
+    c, o, lse, _ = _prepared(name)
+    dev = upload(c, o, lse)
+    (dq, dk, dv), r = run_bsa(c, dev)
+    a = [t.clone() for t in (dq, dk, dv)]
+    for _ in range(3):
+        r()
+    torch.cuda.synchronize()
+    for x, y in zip(a, (r.dq, r.dk, r.dv)):
+        assert torch.equal(x.view(torch.int16), y.view(torch.int16))
+
+
+def test_noncontiguous_outputs_match():
+    c, o, lse, ref = _prepared("bnsd_bf16_d128_b128x128_ragged")
+    dev = upload(c, o, lse)
+    (dq, dk, dv), r = run_bsa(c, dev)
+    torch.cuda.synchronize()
+    base = [t.clone() for t in (dq, dk, dv)]
+    bigq = torch.full((c.B, c.N, c.Sq, 2 * c.D), 7.0, dtype=dq.dtype, device="cuda")
+    bigk = torch.full((c.B, c.Nkv, c.Skv, 2 * c.D), 7.0, dtype=dq.dtype, device="cuda")
+    bigv = torch.full((c.B, c.Nkv, c.Skv, 2 * c.D), 7.0, dtype=dq.dtype, device="cuda")
+    r.kw.update(dq=bigq[..., c.D:], dk=bigk[..., :c.D], dv=bigv[..., c.D:])
+    r()
+    torch.cuda.synchronize()
+    assert torch.equal(bigq[..., c.D:], base[0])
+    assert torch.equal(bigk[..., :c.D], base[1])
+    assert torch.equal(bigv[..., c.D:], base[2])
+    assert torch.all(bigq[..., :c.D] == 7.0) and torch.all(bigk[..., c.D:] == 7.0)
+
+
+def test_page_worked_sample():
+    """The page's sample: constant fp16 inputs; dQ = dK = 0 and dV = 128 exp(S - 5) dout."""
+    import block_sparse_attention_bwd_amd as bsa
+    B, N, S, D = 1, 1, 128, 128
+    full = lambda val: torch.full((B, N, S, D), val, dtype=torch.float16, device="cuda")
+    q, k, v, o, do = full(0.1), full(0.1), full(0.1), full(0.1), full(0.01)
+    lse = torch.full((B, N, S), 5.0, dtype=torch.float32, device="cuda")
+    mask = torch.ones((B, N, 2, 2), dtype=torch.uint8, device="cuda")
+    dq, dk, dv = bsa.block_sparse_attention_grad(do, q, k, v, o, lse, mask, block_shape=[64, 64],
+                                                 actual_seq_lengths=[S], actual_seq_lengths_kv=[S],
+                                                 scale_value=1 / math.sqrt(D))
+    torch.cuda.synchronize()
+    q16, d16 = 0.0999755859375, 0.01000213623046875
+    want_dv = S * math.exp(D * q16 * q16 / math.sqrt(D) - 5.0) * d16
+    assert_close("page/dq", to_np(dq), np.zeros((B, N, S, D)), "fp16", floor_ref=want_dv)
+    assert_close("page/dk", to_np(dk), np.zeros((B, N, S, D)), "fp16", floor_ref=want_dv)
+    assert_close("page/dv", to_np(dv), np.full((B, N, S, D), want_dv), "fp16")
+
+
+def test_too_small_workspace_launches_nothing():
+    import block_sparse_attention_bwd_amd as bsa
+    c, o, lse, _ = _prepared("config1")
+    dev = upload(c, o, lse)
+    (dq, dk, dv), r = run_bsa(c, dev)
+    torch.cuda.synchronize()
+    for t in (r.dq, r.dk, r.dv):
+        t.fill_(3.0)
+    with pytest.raises(bsa.BsaError) as e:
+        bsa.bsa_bwd(*r.args, **r.kw, workspace=r.ws, workspace_size=r.ws_size - 1)
+    assert e.value.code == bsa.BSA_ERR_PARAM_INVALID
+    with pytest.raises(ValueError):
+        bsa.bsa_bwd(*r.args, **r.kw, workspace=r.ws.cpu(), workspace_size=r.ws_size)
+    torch.cuda.synchronize()
+    for t in (r.dq, r.dk, r.dv):
+        assert torch.all(t == 3.0)
+
+
+# ---------------------------------------------------------------------------
+# full-size workloads, checked on sampled output rows
+# ---------------------------------------------------------------------------
+def _sample_rows(c, rng, nq=48, nk=48):
+    qrows, krows = [], []
+    for _ in range(nq):
+        b = int(rng.integers(c.B))
+        L = int(c.len_q[b])
+        if L == 0:
+            continue
+        qrows.append((b, int(rng.integers(c.N)), int(rng.integers(L))))
+    for _ in range(nk):
+        b = int(rng.integers(c.B))
+        L = int(c.len_kv[b])
+        if L == 0:
+            continue
+        krows.append((b, int(rng.integers(c.Nkv)), int(rng.integers(L))))
+    # tile edges: first and last rows of a sequence
+    qrows += [(0, 0, 0), (c.B - 1, c.N - 1, int(c.len_q[c.B - 1]) - 1)]
+    krows += [(0, 0, 0), (c.B - 1, c.Nkv - 1, int(c.len_kv[c.B - 1]) - 1)]
+    return qrows, krows
+
+
+def _row(x, layout, b, n, r, off):
+    return x[b, n, r] if layout == "BNSD" else x[off[b] + r, n]
+
+
+@pytest.mark.parametrize("k", [2, 3, 4, 5])
+def test_full_config_sampled_rows(k):
+    from bench import gpu_forward, to_device, Runner
+    c = synth.config(k)
+    print(f"[full] config {k}: {c.name}", flush=True)
+    dev = to_device(c)
+    o, lse = gpu_forward(c, dev)
+    torch.cuda.synchronize()
+    r = Runner(c, dev, o, lse)
+    dq, dk, dv = r()
+    torch.cuda.synchronize()
+    o_h = o.float().cpu().numpy()
+    lse_h = lse.cpu().numpy()
+    rng = np.random.default_rng(5000 + k)
+    qrows, krows = _sample_rows(c, rng)
+    kw = oracle_kw(c)
+    ref_q = oracle.backward_dq_rows(c.q, c.k, c.v, o_h, c.do, lse_h, c.mask, rows=qrows, **kw)
+    ref_k, ref_v = oracle.backward_dkdv_rows(c.q, c.k, c.v, o_h, c.do, lse_h, c.mask, rows=krows, **kw)
+    offq, offk = oracle.sequence_offsets(c.len_q), oracle.sequence_offsets(c.len_kv)
+    dq_h, dk_h, dv_h = to_np(dq), to_np(dk), to_np(dv)
+    got_q = np.stack([_row(dq_h, c.layout, *key, offq) for key in qrows])
+    got_k = np.stack([_row(dk_h, c.layout, *key, offk) for key in krows])
+    got_v = np.stack([_row(dv_h, c.layout, *key, offk) for key in krows])
+    want_q = np.stack([ref_q[key] for key in qrows])
+    want_k = np.stack([ref_k[key] for key in krows])
+    want_v = np.stack([ref_v[key] for key in krows])
+    assert_close(f"config{k}/dq", got_q, want_q, c.dtype)
+    assert_close(f"config{k}/dk", got_k, want_k, c.dtype)
+    assert_close(f"config{k}/dv", got_v, want_v, c.dtype)
+    # properties that hold at any size: finite everywhere; padding/unused rows zero
+    for t in (dq, dk, dv):
+        assert torch.isfinite(t.float()).all()
