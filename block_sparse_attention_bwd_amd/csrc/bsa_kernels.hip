@@ -196,21 +196,113 @@ __global__ __launch_bounds__(256) void prologue_kernel(Params p, int nb_delta, i
 }
 
 // ---------------------------------------------------------------------------
+// shared pieces of the two MFMA kernels
+// ---------------------------------------------------------------------------
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef unsigned short u16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __attribute__((address_space(3))) unsigned short lds_u16;
+
+// ds_read_b64_tr_b16: within each 16-lane block, lanes 4t..4t+3 address four
+// consecutive 16-bit elements of row t (t = 0..3); lane j of the block then
+// holds column j of those four rows, one row per element.
+__device__ __forceinline__ u16x4 lds_read_tr(const unsigned short* tile, int elem) {
+  // C-style casts: generic -> LDS address-space conversion of a pointer into __shared__ memory
+  lds_u16* base = (lds_u16*)(tile);
+  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + elem));
+  return __builtin_bit_cast(u16x4, v);
+}
+
+// MFMA B fragment of a row-major [rows][PITCH] LDS tile read along its rows:
+// lane (column n = l % 32, g = l / 32) gets rows r0 + 4g + {0,1,2,3} and
+// r0 + 8 + 4g + {0,1,2,3} of column col0 + n, the k order a C tile's
+// registers 8h..8h+7 use (see the layout note at the top of this file).
+template <int PITCH>
+__device__ __forceinline__ u16x8 frag_down_rows(const unsigned short* tile, int r0, int col0, int lane) {
+  const int row = r0 + 4 * (lane >> 5) + ((lane & 15) >> 2);
+  const int col = col0 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  const u16x4 a = lds_read_tr(tile, row * PITCH + col);
+  const u16x4 b = lds_read_tr(tile, (row + 8) * PITCH + col);
+  return u16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+}
+
+// Register prefetch of one staged tile: rows [r0, r0 + rows) of two row-major
+// tensors (row stride sr elements, D columns), 16 bytes per chunk, chunk
+// c = it * nthr + tid.  Rows past `rows` are zero.  With H = 32 * waves rows
+// per stage every thread holds exactly D / 16 chunks of each tensor.
+template <int D>
+struct TilePrefetch {
+  static constexpr int CPR = D / 8;
+  static constexpr int CPT = D / 16;
+  u16x8 a[CPT], b[CPT];
+
+  __device__ __forceinline__ void load(const unsigned short* pa, const unsigned short* pb, int64_t sr,
+                                       int r0, int rows, int tid, int nthr) {
+#pragma unroll
+    for (int it = 0; it < CPT; ++it) {
+      const int c = it * nthr + tid;
+      const int r = c / CPR, k = c % CPR;
+      u16x8 x = {0, 0, 0, 0, 0, 0, 0, 0};
+      u16x8 y = x;
+      if (r < rows) {
+        x = *reinterpret_cast<const u16x8*>(pa + (r0 + r) * sr + 8 * k);
+        y = *reinterpret_cast<const u16x8*>(pb + (r0 + r) * sr + 8 * k);
+      }
+      a[it] = x;
+      b[it] = y;
+    }
+  }
+
+  template <int PITCH>
+  __device__ __forceinline__ void store(unsigned short* ta, unsigned short* tb, int tid, int nthr) const {
+#pragma unroll
+    for (int it = 0; it < CPT; ++it) {
+      const int c = it * nthr + tid;
+      const int r = c / CPR, k = c % CPR;
+      *reinterpret_cast<u16x8*>(ta + r * PITCH + 8 * k) = a[it];
+      *reinterpret_cast<u16x8*>(tb + r * PITCH + 8 * k) = b[it];
+    }
+  }
+};
+
+// ---------------------------------------------------------------------------
 // dK / dV: KV-block-outer
 // ---------------------------------------------------------------------------
+// Walk state over (query head n of the group, position e in its list of
+// Q blocks selecting this KV block, first row q0 of the stage in that block).
+struct QTile {
+  int n, e, q0, qend;
+};
+
+__device__ __forceinline__ bool dkdv_seek(const Params& p, int64_t bn0, int jb, int n_end, int len_q, QTile& t) {
+  // advance (t.n, t.e) to the next existing list entry; set q0/qend
+  while (t.n < n_end) {
+    const int64_t col = (bn0 + t.n) * p.nkb + jb;
+    if (t.e < p.col_cnt[col]) {
+      const int ib = p.col_list[col * p.nqb + t.e];
+      t.q0 = ib * p.bx;
+      t.qend = min(t.q0 + p.bx, len_q);
+      return true;
+    }
+    ++t.n;
+    t.e = 0;
+  }
+  return false;
+}
+
 template <class E, int D>
 __global__ __launch_bounds__(256) void dkdv_kernel(Params p) {
   constexpr int KS = D / 16;  // K=16 steps over the head dim
   constexpr int NT = D / 32;  // 32-wide column tiles of the head dim
   constexpr int PITCH = D + 8;
-  constexpr int CPR = D / 8;  // 16-byte chunks per row
   __shared__ __align__(16) unsigned short sQ[kTileRows * PITCH];
   __shared__ __align__(16) unsigned short sO[kTileRows * PITCH];  // dOut rows
-  __shared__ float sL[kTileRows];
-  __shared__ float sDl[kTileRows];
+  __shared__ __align__(16) float sL[kTileRows];
+  __shared__ __align__(16) float sDl[kTileRows];
 
   const int tid = threadIdx.x, nthr = blockDim.x;
   const int lane = tid & 63, w = tid >> 6, l32 = lane & 31, g = lane >> 5;
+  const int H = nthr / 2;  // staged Q rows: 32 per wave
 
   int wid = blockIdx.x;
   const int nsub = (p.by + kTileRows - 1) / kTileRows;
@@ -254,77 +346,82 @@ __global__ __launch_bounds__(256) void dkdv_kernel(Params p) {
   }
 
   const float c2 = p.scale_log2e;
-  for (int n = h * p.G; n < (h + 1) * p.G; ++n) {
-    const int64_t bn = static_cast<int64_t>(b) * p.N + n;
-    const int cnt = p.col_cnt[bn * p.nkb + jb];
-    const int32_t* lst = p.col_list + (bn * p.nkb + jb) * p.nqb;
-    const int64_t q_base = b * p.q_sb + si.off_q * p.q_sr + n * p.q_sh;
-    const unsigned short* qp = static_cast<const unsigned short*>(p.q) + q_base;
-    const unsigned short* dop = static_cast<const unsigned short*>(p.dout) + q_base;
-    const float* l2p = p.lse2 + bn * p.sq_max;
-    const float* dlp = p.delta + bn * p.sq_max;
-    for (int e = 0; e < cnt; ++e) {
-      const int ib = lst[e];
-      const int qb_end = min(ib * p.bx + p.bx, si.len_q);
-      for (int q0 = ib * p.bx; q0 < qb_end; q0 += kTileRows) {
-        const int rows = min(kTileRows, qb_end - q0);
-        const int rows32 = (rows + 31) & ~31;
-        __syncthreads();  // the previous tile is no longer read
-        for (int idx = tid; idx < rows32 * CPR; idx += nthr) {
-          const int r = idx / CPR, c = idx % CPR;
-          u16x8 a = {0, 0, 0, 0, 0, 0, 0, 0};
-          u16x8 d = a;
-          if (r < rows) {
-            a = *reinterpret_cast<const u16x8*>(qp + (q0 + r) * p.q_sr + 8 * c);
-            d = *reinterpret_cast<const u16x8*>(dop + (q0 + r) * p.q_sr + 8 * c);
-          }
-          *reinterpret_cast<u16x8*>(sQ + r * PITCH + 8 * c) = a;
-          *reinterpret_cast<u16x8*>(sO + r * PITCH + 8 * c) = d;
-        }
-        for (int r = tid; r < rows32; r += nthr) {
-          sL[r] = r < rows ? l2p[q0 + r] : 0.f;
-          sDl[r] = r < rows ? dlp[q0 + r] : 0.f;
-        }
-        __syncthreads();
+  const int64_t bn0 = static_cast<int64_t>(b) * p.N;
+  const int n_end = (h + 1) * p.G;
+  const unsigned short* qbase = static_cast<const unsigned short*>(p.q) + b * p.q_sb + si.off_q * p.q_sr;
+  const unsigned short* obase = static_cast<const unsigned short*>(p.dout) + b * p.q_sb + si.off_q * p.q_sr;
 
-        for (int c0 = 0; c0 < rows; c0 += 32) {
-          f32x16 s = {}, dpv = {};
+  TilePrefetch<D> pf;
+  float pl = 0.f, pd = 0.f;
+  auto prefetch = [&](const QTile& t) {
+    const int rows = min(H, t.qend - t.q0);
+    pf.load(qbase + t.n * p.q_sh, obase + t.n * p.q_sh, p.q_sr, t.q0, rows, tid, nthr);
+    const int64_t li = (bn0 + t.n) * p.sq_max + t.q0 + tid;
+    // rows past the block get LSE = +inf, so their P is exactly 0 with no per-element test
+    pl = tid < rows ? p.lse2[li] : __builtin_inff();
+    pd = tid < rows ? p.delta[li] : 0.f;
+  };
+
+  QTile cur{h * p.G, 0, 0, 0};
+  bool have = dkdv_seek(p, bn0, jb, n_end, si.len_q, cur);
+  if (have) prefetch(cur);
+  while (have) {
+    const int rows = min(H, cur.qend - cur.q0);
+    __syncthreads();  // every wave is done with the previous tile
+    pf.template store<PITCH>(sQ, sO, tid, nthr);
+    if (tid < H) {
+      sL[tid] = pl;
+      sDl[tid] = pd;
+    }
+    __syncthreads();
+    QTile nxt = cur;
+    nxt.q0 += H;
+    bool more = nxt.q0 < nxt.qend;
+    if (!more) {
+      ++nxt.e;
+      more = dkdv_seek(p, bn0, jb, n_end, si.len_q, nxt);
+    }
+    if (more) prefetch(nxt);  // global loads stay in flight during the MFMA work below
+
+    for (int c0 = 0; c0 < rows; c0 += 32) {
+      f32x16 s = {}, dpv = {};
 #pragma unroll
-          for (int ks = 0; ks < KS; ++ks) {
-            const u16x8 aq = *reinterpret_cast<const u16x8*>(sQ + (c0 + l32) * PITCH + 16 * ks + 8 * g);
-            const u16x8 ao = *reinterpret_cast<const u16x8*>(sO + (c0 + l32) * PITCH + 16 * ks + 8 * g);
-            s = E::mma(aq, kreg[ks], s);      // S[q][kv] (unscaled); this lane's column is my_kv
-            dpv = E::mma(ao, vreg[ks], dpv);  // dP[q][kv] = dOut * V^T
-          }
-          float pv[16], dsv[16];
+      for (int ks = 0; ks < KS; ++ks) {
+        const u16x8 aq = *reinterpret_cast<const u16x8*>(sQ + (c0 + l32) * PITCH + 16 * ks + 8 * g);
+        const u16x8 ao = *reinterpret_cast<const u16x8*>(sO + (c0 + l32) * PITCH + 16 * ks + 8 * g);
+        s = E::mma(aq, kreg[ks], s);      // S[q][kv] (unscaled); this lane's column is my_kv
+        dpv = E::mma(ao, vreg[ks], dpv);  // dP[q][kv] = dOut * V^T
+      }
+      // this lane's 16 score rows are c0 + 8a + 4g + {0..3}: four float4 reads each
+      float4 l4[4], d4[4];
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int qr = c0 + 8 * (i >> 2) + 4 * g + (i & 3);
-            const bool ok = kv_ok && qr < rows;
-            const float x = fast_exp2(s[i] * c2 - sL[qr]);  // P = exp(scale*S - LSE)
-            pv[i] = ok ? x : 0.f;
-            dsv[i] = ok ? x * (dpv[i] - sDl[qr]) : 0.f;      // dS = P o (dP - softmax_grad)
-          }
-          const u16x8 pa[2] = {pack8<E>(pv), pack8<E>(pv + 8)};
-          const u16x8 da[2] = {pack8<E>(dsv), pack8<E>(dsv + 8)};
+      for (int a = 0; a < 4; ++a) {
+        l4[a] = *reinterpret_cast<const float4*>(sL + c0 + 8 * a + 4 * g);
+        d4[a] = *reinterpret_cast<const float4*>(sDl + c0 + 8 * a + 4 * g);
+      }
+      float pv[16], dsv[16];
 #pragma unroll
-          for (int nt = 0; nt < NT; ++nt) {
+      for (int i = 0; i < 16; ++i) {
+        const float li = l4[i >> 2][i & 3], di = d4[i >> 2][i & 3];
+        const float x = fast_exp2(s[i] * c2 - li);  // P = exp(scale*S - LSE)
+        pv[i] = kv_ok ? x : 0.f;
+        dsv[i] = pv[i] * (dpv[i] - di);              // dS = P o (dP - softmax_grad)
+      }
+      const u16x8 pa[2] = {pack8<E>(pv), pack8<E>(pv + 8)};
+      const u16x8 da[2] = {pack8<E>(dsv), pack8<E>(dsv + 8)};
 #pragma unroll
-            for (int hh = 0; hh < 2; ++hh) {
-              u16x8 bo, bq;
+      for (int nt = 0; nt < NT; ++nt) {
 #pragma unroll
-              for (int t = 0; t < 8; ++t) {
-                const int r = c0 + 16 * hh + 4 * g + (t & 3) + 8 * (t >> 2);
-                bo[t] = sO[r * PITCH + 32 * nt + l32];
-                bq[t] = sQ[r * PITCH + 32 * nt + l32];
-              }
-              adv[nt] = E::mma(pa[hh], bo, adv[nt]);  // dV += P^T * dOut
-              adk[nt] = E::mma(da[hh], bq, adk[nt]);  // dK += dS^T * Q
-            }
-          }
+        for (int hh = 0; hh < 2; ++hh) {
+          const u16x8 bo = frag_down_rows<PITCH>(sO, c0 + 16 * hh, 32 * nt, lane);
+          const u16x8 bq = frag_down_rows<PITCH>(sQ, c0 + 16 * hh, 32 * nt, lane);
+          adv[nt] = E::mma(pa[hh], bo, adv[nt]);  // dV += P^T * dOut
+          adk[nt] = E::mma(da[hh], bq, adk[nt]);  // dK += dS^T * Q
         }
       }
     }
+    cur = nxt;
+    have = more;
   }
 
   unsigned short* dkp = static_cast<unsigned short*>(p.dk) + b * p.dk_sb + si.off_kv * p.dk_sr + h * p.dk_sh;
@@ -350,12 +447,12 @@ __global__ __launch_bounds__(256) void dq_kernel(Params p) {
   constexpr int KS = D / 16;
   constexpr int NT = D / 32;
   constexpr int PITCH = D + 8;
-  constexpr int CPR = D / 8;
   __shared__ __align__(16) unsigned short sK[kTileRows * PITCH];
   __shared__ __align__(16) unsigned short sV[kTileRows * PITCH];
 
   const int tid = threadIdx.x, nthr = blockDim.x;
   const int lane = tid & 63, w = tid >> 6, l32 = lane & 31, g = lane >> 5;
+  const int H = nthr / 2;  // staged K/V rows: 32 per wave
 
   int wid = blockIdx.x;
   const int nsub = (p.bx + kTileRows - 1) / kTileRows;
@@ -406,59 +503,59 @@ __global__ __launch_bounds__(256) void dq_kernel(Params p) {
   const int32_t* lst = p.row_list + (bn * p.nqb + ib) * p.nkb;
   const float c2 = p.scale_log2e;
 
-  for (int e = 0; e < cnt; ++e) {
-    const int jb = lst[e];
-    const int kb_end = min(jb * p.by + p.by, si.len_kv);
-    for (int k0 = jb * p.by; k0 < kb_end; k0 += kTileRows) {
-      const int rows = min(kTileRows, kb_end - k0);
-      const int rows32 = (rows + 31) & ~31;
-      __syncthreads();
-      for (int idx = tid; idx < rows32 * CPR; idx += nthr) {
-        const int r = idx / CPR, c = idx % CPR;
-        u16x8 a = {0, 0, 0, 0, 0, 0, 0, 0};
-        u16x8 d = a;
-        if (r < rows) {
-          a = *reinterpret_cast<const u16x8*>(kp + (k0 + r) * p.kv_sr + 8 * c);
-          d = *reinterpret_cast<const u16x8*>(vp + (k0 + r) * p.kv_sr + 8 * c);
-        }
-        *reinterpret_cast<u16x8*>(sK + r * PITCH + 8 * c) = a;
-        *reinterpret_cast<u16x8*>(sV + r * PITCH + 8 * c) = d;
+  // walk state: (position e in the KV-block list, first row k0 of the stage)
+  TilePrefetch<D> pf;
+  int e = 0, k0 = 0, kend = 0;
+  if (cnt > 0) {
+    k0 = lst[0] * p.by;
+    kend = min(k0 + p.by, si.len_kv);
+    pf.load(kp, vp, p.kv_sr, k0, min(H, kend - k0), tid, nthr);
+  }
+  while (e < cnt) {
+    const int rows = min(H, kend - k0);
+    __syncthreads();
+    pf.template store<PITCH>(sK, sV, tid, nthr);
+    __syncthreads();
+    int ne = e, nk0 = k0 + H, nkend = kend;
+    if (nk0 >= kend) {
+      ++ne;
+      if (ne < cnt) {
+        nk0 = lst[ne] * p.by;
+        nkend = min(nk0 + p.by, si.len_kv);
       }
-      __syncthreads();
+    }
+    if (ne < cnt) pf.load(kp, vp, p.kv_sr, nk0, min(H, nkend - nk0), tid, nthr);
 
-      for (int c0 = 0; c0 < rows; c0 += 32) {
-        f32x16 st = {}, dpt = {};
+    for (int c0 = 0; c0 < rows; c0 += 32) {
+      f32x16 st = {}, dpt = {};
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          const u16x8 ak = *reinterpret_cast<const u16x8*>(sK + (c0 + l32) * PITCH + 16 * ks + 8 * g);
-          const u16x8 av = *reinterpret_cast<const u16x8*>(sV + (c0 + l32) * PITCH + 16 * ks + 8 * g);
-          st = E::mma(ak, qreg[ks], st);   // S^T[kv][q]
-          dpt = E::mma(av, oreg[ks], dpt); // dP^T[kv][q]
-        }
-        float dsv[16];
+      for (int ks = 0; ks < KS; ++ks) {
+        const u16x8 ak = *reinterpret_cast<const u16x8*>(sK + (c0 + l32) * PITCH + 16 * ks + 8 * g);
+        const u16x8 av = *reinterpret_cast<const u16x8*>(sV + (c0 + l32) * PITCH + 16 * ks + 8 * g);
+        st = E::mma(ak, qreg[ks], st);   // S^T[kv][q]
+        dpt = E::mma(av, oreg[ks], dpt); // dP^T[kv][q]
+      }
+      float dsv[16];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int kr = c0 + 8 * (i >> 2) + 4 * g + (i & 3);
-          const bool ok = q_ok && kr < rows;
-          const float x = fast_exp2(st[i] * c2 - l2);
-          dsv[i] = ok ? x * (dpt[i] - dl) : 0.f;
-        }
-        const u16x8 da[2] = {pack8<E>(dsv), pack8<E>(dsv + 8)};
+      for (int i = 0; i < 16; ++i) {
+        const int kr = c0 + 8 * (i >> 2) + 4 * g + (i & 3);
+        const bool ok = q_ok && kr < rows;
+        const float x = fast_exp2(st[i] * c2 - l2);
+        dsv[i] = ok ? x * (dpt[i] - dl) : 0.f;
+      }
+      const u16x8 da[2] = {pack8<E>(dsv), pack8<E>(dsv + 8)};
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
+      for (int nt = 0; nt < NT; ++nt) {
 #pragma unroll
-          for (int hh = 0; hh < 2; ++hh) {
-            u16x8 bk;
-#pragma unroll
-            for (int t = 0; t < 8; ++t) {
-              const int r = c0 + 16 * hh + 4 * g + (t & 3) + 8 * (t >> 2);
-              bk[t] = sK[r * PITCH + 32 * nt + l32];
-            }
-            adq[nt] = E::mma(da[hh], bk, adq[nt]);  // dQ += dS * K
-          }
+        for (int hh = 0; hh < 2; ++hh) {
+          const u16x8 bk = frag_down_rows<PITCH>(sK, c0 + 16 * hh, 32 * nt, lane);
+          adq[nt] = E::mma(da[hh], bk, adq[nt]);  // dQ += dS * K
         }
       }
     }
+    e = ne;
+    k0 = nk0;
+    kend = nkend;
   }
 
   unsigned short* dqp = static_cast<unsigned short*>(p.dq) + b * p.dq_sb + si.off_q * p.dq_sr + n * p.dq_sh;
