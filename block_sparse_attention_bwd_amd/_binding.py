@@ -14,7 +14,8 @@ import re
 from typing import Optional, Sequence
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG, "libbsa_bwd.so")
+# BSA_LIBRARY may name another build of the same library (same ABI)
+LIB_PATH = os.environ.get("BSA_LIBRARY") or os.path.join(PKG, "libbsa_bwd.so")
 HEADER = os.path.join(os.path.dirname(PKG), "include", "bsa_bwd.h")
 
 BSA_OK = 0

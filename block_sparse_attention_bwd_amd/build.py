@@ -43,13 +43,14 @@ def compile_flags() -> list:
     ]
 
 
-def build(verbose: bool = False) -> str:
+def build(verbose: bool = False, out: str = LIB_PATH, csrc: str = CSRC, defines=()) -> str:
     hipcc = _hipcc()
     with tempfile.TemporaryDirectory(prefix="bsa_build_") as tmp:
         objs = []
         for src in SOURCES:
             obj = os.path.join(tmp, os.path.splitext(src)[0] + ".o")
-            cmd = [hipcc, *compile_flags(), "-c", os.path.join(CSRC, src), "-o", obj]
+            cmd = [hipcc, *compile_flags(), *[f"-D{d}" for d in defines], "-I", csrc, "-c",
+                   os.path.join(csrc, src), "-o", obj]
             if verbose:
                 print(" ".join(cmd), flush=True)
             r = subprocess.run(cmd, capture_output=True, text=True)
@@ -64,9 +65,9 @@ def build(verbose: bool = False) -> str:
         r = subprocess.run(cmd, capture_output=True, text=True)
         if r.returncode != 0:
             raise RuntimeError(f"linking {LIB_NAME} failed:\n{r.stderr}")
-        shutil.copyfile(out_tmp, LIB_PATH + ".tmp")
-        os.replace(LIB_PATH + ".tmp", LIB_PATH)
-    return LIB_PATH
+        shutil.copyfile(out_tmp, out + ".tmp")
+        os.replace(out + ".tmp", out)
+    return out
 
 
 if __name__ == "__main__":

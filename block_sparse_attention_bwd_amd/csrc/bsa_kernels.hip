@@ -203,6 +203,19 @@ typedef unsigned short u16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 typedef __attribute__((address_space(3))) unsigned short lds_u16;
 
+// LDS tiles are row-major and padded.  A tile read along its rows by 16-byte
+// reads (MFMA A/B fragments of 8 consecutive columns) uses a pitch of D + 8
+// elements; a tile read down its rows by transposing 8-byte reads uses D + 16.
+// Measured on gfx950, each pitch keeps its own access pattern free of bank
+// conflicts (16-byte reads of 16 consecutive rows; transposing reads of 4
+// consecutive rows x 32 bytes per 16 lanes) and halves the throughput of the
+// other, so a tile that is read both ways is staged twice.
+template <int D>
+struct Pitch {
+  static constexpr int A = D + 8;   // along rows
+  static constexpr int T = D + 16;  // down rows
+};
+
 // ds_read_b64_tr_b16: within each 16-lane block, lanes 4t..4t+3 address four
 // consecutive 16-bit elements of row t (t = 0..3); lane j of the block then
 // holds column j of those four rows, one row per element.
@@ -213,54 +226,93 @@ __device__ __forceinline__ u16x4 lds_read_tr(const unsigned short* tile, int ele
   return __builtin_bit_cast(u16x4, v);
 }
 
-// MFMA B fragment of a row-major [rows][PITCH] LDS tile read along its rows:
-// lane (column n = l % 32, g = l / 32) gets rows r0 + 4g + {0,1,2,3} and
-// r0 + 8 + 4g + {0,1,2,3} of column col0 + n, the k order a C tile's
-// registers 8h..8h+7 use (see the layout note at the top of this file).
-template <int PITCH>
+// MFMA B fragment read down the rows of a tile: lane (column n = l % 32,
+// g = l / 32) gets rows r0 + 4g + {0..3} and r0 + 8 + 4g + {0..3} of column
+// col0 + n -- the k order of a C tile's registers 8h..8h+7 (see the layout
+// note at the top of this file).
+template <int D>
 __device__ __forceinline__ u16x8 frag_down_rows(const unsigned short* tile, int r0, int col0, int lane) {
+  constexpr int P = Pitch<D>::T;
   const int row = r0 + 4 * (lane >> 5) + ((lane & 15) >> 2);
   const int col = col0 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-  const u16x4 a = lds_read_tr(tile, row * PITCH + col);
-  const u16x4 b = lds_read_tr(tile, (row + 8) * PITCH + col);
+  const u16x4 a = lds_read_tr(tile, row * P + col);
+  const u16x4 b = lds_read_tr(tile, (row + 8) * P + col);
   return u16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
 }
 
-// Register prefetch of one staged tile: rows [r0, r0 + rows) of two row-major
-// tensors (row stride sr elements, D columns), 16 bytes per chunk, chunk
-// c = it * nthr + tid.  Rows past `rows` are zero.  With H = 32 * waves rows
-// per stage every thread holds exactly D / 16 chunks of each tensor.
+// MFMA A fragment read along a row: lane (row m = l % 32, g) gets columns
+// col0 + 8g .. col0 + 8g + 7 of row r0 + m.
 template <int D>
-struct TilePrefetch {
+__device__ __forceinline__ u16x8 frag_along_row(const unsigned short* tile, int r0, int col0, int lane) {
+  constexpr int P = Pitch<D>::A;
+  return *reinterpret_cast<const u16x8*>(tile + (r0 + (lane & 31)) * P + col0 + 8 * (lane >> 5));
+}
+
+// The work of a workgroup is a stream of 32-row slices (of Q blocks for the
+// dK/dV kernel, of KV blocks for the dQ kernel); a stage stages W slices, one
+// per wave of rows, into a 32*W-row tile.  nrows == 0 marks an empty slice.
+struct Slice {
+  int head;   // query head (dK/dV kernel); unused by the dQ kernel
+  int row0;   // first sequence-local row
+  int nrows;  // valid rows, 0..32
+};
+
+// sl[j] for a per-lane j, by selects (no dynamic register indexing).
+template <int W>
+__device__ __forceinline__ Slice pick_slice(const Slice* sl, int j) {
+  Slice r = sl[0];
+#pragma unroll
+  for (int k = 1; k < W; ++k)
+    if (j == k) r = sl[k];
+  return r;
+}
+
+// Register prefetch of one stage: for each of the two tensors, thread tid
+// holds chunks c = it * 64W + tid (16 bytes, it < D/16) of the 32W x D tile;
+// chunk c is row c / (D/8), and row r belongs to slice r / 32, which is a
+// compile-time function of `it` for every (D, W) used.
+template <int D, int W>
+struct StagePrefetch {
   static constexpr int CPR = D / 8;
   static constexpr int CPT = D / 16;
+  static constexpr int NTHR = 64 * W;
   u16x8 a[CPT], b[CPT];
 
-  __device__ __forceinline__ void load(const unsigned short* pa, const unsigned short* pb, int64_t sr,
-                                       int r0, int rows, int tid, int nthr) {
+  // pa/pb(slice, row) give the row's address in the two source tensors
+  template <class Addr>
+  __device__ __forceinline__ void load(const Slice* sl, Addr addr, int tid) {
 #pragma unroll
     for (int it = 0; it < CPT; ++it) {
-      const int c = it * nthr + tid;
+      const int c = it * NTHR + tid;
       const int r = c / CPR, k = c % CPR;
+      const int j = (it * NTHR) / (32 * CPR);  // slice of this chunk (uniform per it)
+      const int rr = r & 31;
       u16x8 x = {0, 0, 0, 0, 0, 0, 0, 0};
       u16x8 y = x;
-      if (r < rows) {
-        x = *reinterpret_cast<const u16x8*>(pa + (r0 + r) * sr + 8 * k);
-        y = *reinterpret_cast<const u16x8*>(pb + (r0 + r) * sr + 8 * k);
+      if (rr < sl[j].nrows) {
+        const unsigned short* pa;
+        const unsigned short* pb;
+        addr(sl[j], sl[j].row0 + rr, pa, pb);
+        x = *reinterpret_cast<const u16x8*>(pa + 8 * k);
+        y = *reinterpret_cast<const u16x8*>(pb + 8 * k);
       }
       a[it] = x;
       b[it] = y;
     }
   }
 
-  template <int PITCH>
-  __device__ __forceinline__ void store(unsigned short* ta, unsigned short* tb, int tid, int nthr) const {
+  // Tensor a goes to tiles ta (pitch A) and, if given, ta_t (pitch T); tensor b
+  // to tb (pitch A) and, if given, tb_t (pitch T).
+  __device__ __forceinline__ void store(unsigned short* ta, unsigned short* ta_t, unsigned short* tb,
+                                        unsigned short* tb_t, int tid) const {
 #pragma unroll
     for (int it = 0; it < CPT; ++it) {
-      const int c = it * nthr + tid;
+      const int c = it * NTHR + tid;
       const int r = c / CPR, k = c % CPR;
-      *reinterpret_cast<u16x8*>(ta + r * PITCH + 8 * k) = a[it];
-      *reinterpret_cast<u16x8*>(tb + r * PITCH + 8 * k) = b[it];
+      *reinterpret_cast<u16x8*>(ta + r * Pitch<D>::A + 8 * k) = a[it];
+      *reinterpret_cast<u16x8*>(tb + r * Pitch<D>::A + 8 * k) = b[it];
+      if (ta_t) *reinterpret_cast<u16x8*>(ta_t + r * Pitch<D>::T + 8 * k) = a[it];
+      if (tb_t) *reinterpret_cast<u16x8*>(tb_t + r * Pitch<D>::T + 8 * k) = b[it];
     }
   }
 };
@@ -268,41 +320,44 @@ struct TilePrefetch {
 // ---------------------------------------------------------------------------
 // dK / dV: KV-block-outer
 // ---------------------------------------------------------------------------
-// Walk state over (query head n of the group, position e in its list of
-// Q blocks selecting this KV block, first row q0 of the stage in that block).
-struct QTile {
-  int n, e, q0, qend;
+// Slices of the Q blocks that select this KV block, for the query heads of
+// the group in ascending order, each head's blocks in ascending order.
+struct QSliceWalk {
+  int n, n_end, e, cnt, q, qend;
+
+  __device__ __forceinline__ bool next(const Params& p, int64_t bn0, int jb, int len_q, Slice& s) {
+    while (q >= qend) {
+      ++e;
+      while (e >= cnt) {
+        if (++n >= n_end) return false;
+        e = 0;
+        cnt = p.col_cnt[(bn0 + n) * p.nkb + jb];
+      }
+      q = p.col_list[((bn0 + n) * p.nkb + jb) * p.nqb + e] * p.bx;
+      qend = min(q + p.bx, len_q);
+    }
+    s.head = n;
+    s.row0 = q;
+    s.nrows = min(32, qend - q);
+    q += 32;
+    return true;
+  }
 };
 
-__device__ __forceinline__ bool dkdv_seek(const Params& p, int64_t bn0, int jb, int n_end, int len_q, QTile& t) {
-  // advance (t.n, t.e) to the next existing list entry; set q0/qend
-  while (t.n < n_end) {
-    const int64_t col = (bn0 + t.n) * p.nkb + jb;
-    if (t.e < p.col_cnt[col]) {
-      const int ib = p.col_list[col * p.nqb + t.e];
-      t.q0 = ib * p.bx;
-      t.qend = min(t.q0 + p.bx, len_q);
-      return true;
-    }
-    ++t.n;
-    t.e = 0;
-  }
-  return false;
-}
-
-template <class E, int D>
-__global__ __launch_bounds__(256) void dkdv_kernel(Params p) {
+template <class E, int D, int W>
+__global__ __launch_bounds__(64 * W) void dkdv_kernel(Params p) {
   constexpr int KS = D / 16;  // K=16 steps over the head dim
   constexpr int NT = D / 32;  // 32-wide column tiles of the head dim
-  constexpr int PITCH = D + 8;
-  __shared__ __align__(16) unsigned short sQ[kTileRows * PITCH];
-  __shared__ __align__(16) unsigned short sO[kTileRows * PITCH];  // dOut rows
-  __shared__ __align__(16) float sL[kTileRows];
-  __shared__ __align__(16) float sDl[kTileRows];
+  constexpr int H = 32 * W;   // staged Q rows
+  __shared__ __align__(16) unsigned short sQ[H * Pitch<D>::A];   // Q rows, read along
+  __shared__ __align__(16) unsigned short sO[H * Pitch<D>::A];   // dOut rows, read along
+  __shared__ __align__(16) unsigned short sQt[H * Pitch<D>::T];  // the same rows, read down
+  __shared__ __align__(16) unsigned short sOt[H * Pitch<D>::T];
+  __shared__ __align__(16) float sL[H];
+  __shared__ __align__(16) float sDl[H];
 
-  const int tid = threadIdx.x, nthr = blockDim.x;
+  const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6, l32 = lane & 31, g = lane >> 5;
-  const int H = nthr / 2;  // staged Q rows: 32 per wave
 
   int wid = blockIdx.x;
   const int nsub = (p.by + kTileRows - 1) / kTileRows;
@@ -347,65 +402,81 @@ __global__ __launch_bounds__(256) void dkdv_kernel(Params p) {
 
   const float c2 = p.scale_log2e;
   const int64_t bn0 = static_cast<int64_t>(b) * p.N;
-  const int n_end = (h + 1) * p.G;
   const unsigned short* qbase = static_cast<const unsigned short*>(p.q) + b * p.q_sb + si.off_q * p.q_sr;
   const unsigned short* obase = static_cast<const unsigned short*>(p.dout) + b * p.q_sb + si.off_q * p.q_sr;
-
-  TilePrefetch<D> pf;
-  float pl = 0.f, pd = 0.f;
-  auto prefetch = [&](const QTile& t) {
-    const int rows = min(H, t.qend - t.q0);
-    pf.load(qbase + t.n * p.q_sh, obase + t.n * p.q_sh, p.q_sr, t.q0, rows, tid, nthr);
-    const int64_t li = (bn0 + t.n) * p.sq_max + t.q0 + tid;
-    // rows past the block get LSE = +inf, so their P is exactly 0 with no per-element test
-    pl = tid < rows ? p.lse2[li] : __builtin_inff();
-    pd = tid < rows ? p.delta[li] : 0.f;
+  auto addr = [&](const Slice& s, int row, const unsigned short*& pa, const unsigned short*& pb) {
+    const int64_t off = s.head * p.q_sh + row * p.q_sr;
+    pa = qbase + off;
+    pb = obase + off;
   };
 
-  QTile cur{h * p.G, 0, 0, 0};
-  bool have = dkdv_seek(p, bn0, jb, n_end, si.len_q, cur);
-  if (have) prefetch(cur);
+  QSliceWalk walk{h * p.G, (h + 1) * p.G, -1, 0, 0, 0};
+  walk.cnt = p.col_cnt[(bn0 + walk.n) * p.nkb + jb];
+  Slice sl[W];
+  auto gather = [&]() {
+    bool any = false;
+#pragma unroll
+    for (int j = 0; j < W; ++j) {
+      if (!walk.next(p, bn0, jb, si.len_q, sl[j])) sl[j] = Slice{h * p.G, 0, 0};
+      any |= sl[j].nrows > 0;
+    }
+    return any;
+  };
+
+  StagePrefetch<D, W> pf;
+  float pl = 0.f, pd = 0.f;
+  auto prefetch = [&]() {
+    pf.load(sl, addr, tid);
+    if (tid < H) {  // row tid of the stage belongs to slice tid / 32
+      const Slice s = pick_slice<W>(sl, tid >> 5);
+      const int rr = tid & 31;
+      const int64_t li = (bn0 + s.head) * p.sq_max + s.row0 + rr;
+      // rows past a slice's end get LSE = +inf, so their P is exactly 0
+      pl = rr < s.nrows ? p.lse2[li] : __builtin_inff();
+      pd = rr < s.nrows ? p.delta[li] : 0.f;
+    }
+  };
+
+  bool have = gather();
+  if (have) prefetch();
   while (have) {
-    const int rows = min(H, cur.qend - cur.q0);
-    __syncthreads();  // every wave is done with the previous tile
-    pf.template store<PITCH>(sQ, sO, tid, nthr);
+    __syncthreads();  // every wave is done with the previous stage
+    pf.store(sQ, sQt, sO, sOt, tid);
     if (tid < H) {
       sL[tid] = pl;
       sDl[tid] = pd;
     }
     __syncthreads();
-    QTile nxt = cur;
-    nxt.q0 += H;
-    bool more = nxt.q0 < nxt.qend;
-    if (!more) {
-      ++nxt.e;
-      more = dkdv_seek(p, bn0, jb, n_end, si.len_q, nxt);
-    }
-    if (more) prefetch(nxt);  // global loads stay in flight during the MFMA work below
+    const bool more = gather();
+    if (more) prefetch();  // global loads stay in flight during the MFMA work below
 
-    for (int c0 = 0; c0 < rows; c0 += 32) {
-      f32x16 s = {}, dpv = {};
+    // S and dP of chunk j (32 Q rows x this wave's 32 KV rows)
+    auto sdp = [&](int j, f32x16& s, f32x16& dpv) {
+      s = f32x16{};
+      dpv = f32x16{};
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const u16x8 aq = *reinterpret_cast<const u16x8*>(sQ + (c0 + l32) * PITCH + 16 * ks + 8 * g);
-        const u16x8 ao = *reinterpret_cast<const u16x8*>(sO + (c0 + l32) * PITCH + 16 * ks + 8 * g);
-        s = E::mma(aq, kreg[ks], s);      // S[q][kv] (unscaled); this lane's column is my_kv
-        dpv = E::mma(ao, vreg[ks], dpv);  // dP[q][kv] = dOut * V^T
+        s = E::mma(frag_along_row<D>(sQ, 32 * j, 16 * ks, lane), kreg[ks], s);    // S[q][kv]
+        dpv = E::mma(frag_along_row<D>(sO, 32 * j, 16 * ks, lane), vreg[ks], dpv); // dP = dOut * V^T
       }
-      // this lane's 16 score rows are c0 + 8a + 4g + {0..3}: four float4 reads each
+    };
+#pragma unroll
+    for (int j = 0; j < W; ++j) {
+      f32x16 s, dpv;
+      sdp(j, s, dpv);
+      // this lane's 16 score rows are 32j + 8a + 4g + {0..3}: four float4 reads each
       float4 l4[4], d4[4];
 #pragma unroll
       for (int a = 0; a < 4; ++a) {
-        l4[a] = *reinterpret_cast<const float4*>(sL + c0 + 8 * a + 4 * g);
-        d4[a] = *reinterpret_cast<const float4*>(sDl + c0 + 8 * a + 4 * g);
+        l4[a] = *reinterpret_cast<const float4*>(sL + 32 * j + 8 * a + 4 * g);
+        d4[a] = *reinterpret_cast<const float4*>(sDl + 32 * j + 8 * a + 4 * g);
       }
       float pv[16], dsv[16];
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const float li = l4[i >> 2][i & 3], di = d4[i >> 2][i & 3];
-        const float x = fast_exp2(s[i] * c2 - li);  // P = exp(scale*S - LSE)
+        const float x = fast_exp2(s[i] * c2 - l4[i >> 2][i & 3]);  // P = exp(scale*S - LSE)
         pv[i] = kv_ok ? x : 0.f;
-        dsv[i] = pv[i] * (dpv[i] - di);              // dS = P o (dP - softmax_grad)
+        dsv[i] = pv[i] * (dpv[i] - d4[i >> 2][i & 3]);           // dS = P o (dP - softmax_grad)
       }
       const u16x8 pa[2] = {pack8<E>(pv), pack8<E>(pv + 8)};
       const u16x8 da[2] = {pack8<E>(dsv), pack8<E>(dsv + 8)};
@@ -413,14 +484,11 @@ __global__ __launch_bounds__(256) void dkdv_kernel(Params p) {
       for (int nt = 0; nt < NT; ++nt) {
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
-          const u16x8 bo = frag_down_rows<PITCH>(sO, c0 + 16 * hh, 32 * nt, lane);
-          const u16x8 bq = frag_down_rows<PITCH>(sQ, c0 + 16 * hh, 32 * nt, lane);
-          adv[nt] = E::mma(pa[hh], bo, adv[nt]);  // dV += P^T * dOut
-          adk[nt] = E::mma(da[hh], bq, adk[nt]);  // dK += dS^T * Q
+          adv[nt] = E::mma(pa[hh], frag_down_rows<D>(sOt, 32 * j + 16 * hh, 32 * nt, lane), adv[nt]);  // dV += P^T dOut
+          adk[nt] = E::mma(da[hh], frag_down_rows<D>(sQt, 32 * j + 16 * hh, 32 * nt, lane), adk[nt]);  // dK += dS^T Q
         }
       }
     }
-    cur = nxt;
     have = more;
   }
 
@@ -442,17 +510,37 @@ __global__ __launch_bounds__(256) void dkdv_kernel(Params p) {
 // ---------------------------------------------------------------------------
 // dQ: Q-block-outer
 // ---------------------------------------------------------------------------
-template <class E, int D>
-__global__ __launch_bounds__(256) void dq_kernel(Params p) {
+// Slices of the KV blocks this Q block selects, in list (ascending) order.
+struct KVSliceWalk {
+  int e, cnt, k, kend;
+  const int32_t* lst;
+
+  __device__ __forceinline__ bool next(const Params& p, int len_kv, Slice& s) {
+    while (k >= kend) {
+      if (++e >= cnt) return false;
+      k = lst[e] * p.by;
+      kend = min(k + p.by, len_kv);
+    }
+    s.head = 0;
+    s.row0 = k;
+    s.nrows = min(32, kend - k);
+    k += 32;
+    return true;
+  }
+};
+
+template <class E, int D, int W>
+__global__ __launch_bounds__(64 * W) void dq_kernel(Params p) {
   constexpr int KS = D / 16;
   constexpr int NT = D / 32;
-  constexpr int PITCH = D + 8;
-  __shared__ __align__(16) unsigned short sK[kTileRows * PITCH];
-  __shared__ __align__(16) unsigned short sV[kTileRows * PITCH];
+  constexpr int H = 32 * W;  // staged K/V rows
+  __shared__ __align__(16) unsigned short sK[H * Pitch<D>::A];   // K rows, read along
+  __shared__ __align__(16) unsigned short sKt[H * Pitch<D>::T];  // the same rows, read down
+  __shared__ __align__(16) unsigned short sV[H * Pitch<D>::A];
+  __shared__ __align__(16) float sB[H];  // 0 for rows that take part, -inf for padding rows
 
-  const int tid = threadIdx.x, nthr = blockDim.x;
+  const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6, l32 = lane & 31, g = lane >> 5;
-  const int H = nthr / 2;  // staged K/V rows: 32 per wave
 
   int wid = blockIdx.x;
   const int nsub = (p.bx + kTileRows - 1) / kTileRows;
@@ -477,6 +565,8 @@ __global__ __launch_bounds__(256) void dq_kernel(Params p) {
   const unsigned short* qp = static_cast<const unsigned short*>(p.q) + q_base;
   const unsigned short* dop = static_cast<const unsigned short*>(p.dout) + q_base;
 
+  // Invalid query lanes hold zero Q/dO rows and LSE = softmax_grad = 0, so
+  // their dP is 0 and so is every dS they produce.
   u16x8 qreg[KS], oreg[KS];
 #pragma unroll
   for (int s = 0; s < KS; ++s) {
@@ -499,63 +589,72 @@ __global__ __launch_bounds__(256) void dq_kernel(Params p) {
   const int64_t kv_base = b * p.kv_sb + si.off_kv * p.kv_sr + h * p.kv_sh;
   const unsigned short* kp = static_cast<const unsigned short*>(p.k) + kv_base;
   const unsigned short* vp = static_cast<const unsigned short*>(p.v) + kv_base;
-  const int cnt = p.row_cnt[bn * p.nqb + ib];
-  const int32_t* lst = p.row_list + (bn * p.nqb + ib) * p.nkb;
+  auto addr = [&](const Slice& s, int row, const unsigned short*& pa, const unsigned short*& pb) {
+    pa = kp + row * p.kv_sr;
+    pb = vp + row * p.kv_sr;
+  };
   const float c2 = p.scale_log2e;
 
-  // walk state: (position e in the KV-block list, first row k0 of the stage)
-  TilePrefetch<D> pf;
-  int e = 0, k0 = 0, kend = 0;
-  if (cnt > 0) {
-    k0 = lst[0] * p.by;
-    kend = min(k0 + p.by, si.len_kv);
-    pf.load(kp, vp, p.kv_sr, k0, min(H, kend - k0), tid, nthr);
-  }
-  while (e < cnt) {
-    const int rows = min(H, kend - k0);
-    __syncthreads();
-    pf.template store<PITCH>(sK, sV, tid, nthr);
-    __syncthreads();
-    int ne = e, nk0 = k0 + H, nkend = kend;
-    if (nk0 >= kend) {
-      ++ne;
-      if (ne < cnt) {
-        nk0 = lst[ne] * p.by;
-        nkend = min(nk0 + p.by, si.len_kv);
-      }
+  KVSliceWalk walk{-1, p.row_cnt[bn * p.nqb + ib], 0, 0, p.row_list + (bn * p.nqb + ib) * p.nkb};
+  Slice sl[W];
+  auto gather = [&]() {
+    bool any = false;
+#pragma unroll
+    for (int j = 0; j < W; ++j) {
+      if (!walk.next(p, si.len_kv, sl[j])) sl[j] = Slice{0, 0, 0};
+      any |= sl[j].nrows > 0;
     }
-    if (ne < cnt) pf.load(kp, vp, p.kv_sr, nk0, min(H, nkend - nk0), tid, nthr);
+    return any;
+  };
 
-    for (int c0 = 0; c0 < rows; c0 += 32) {
-      f32x16 st = {}, dpt = {};
+  StagePrefetch<D, W> pf;
+  float pb = 0.f;
+  auto prefetch = [&]() {
+    pf.load(sl, addr, tid);
+    if (tid < H) pb = (tid & 31) < pick_slice<W>(sl, tid >> 5).nrows ? 0.f : -__builtin_inff();
+  };
+
+  bool have = gather();
+  if (have) prefetch();
+  while (have) {
+    __syncthreads();
+    pf.store(sK, sKt, sV, nullptr, tid);
+    if (tid < H) sB[tid] = pb;
+    __syncthreads();
+    const bool more = gather();
+    if (more) prefetch();
+
+    auto sdp = [&](int j, f32x16& st, f32x16& dpt) {
+      st = f32x16{};
+      dpt = f32x16{};
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const u16x8 ak = *reinterpret_cast<const u16x8*>(sK + (c0 + l32) * PITCH + 16 * ks + 8 * g);
-        const u16x8 av = *reinterpret_cast<const u16x8*>(sV + (c0 + l32) * PITCH + 16 * ks + 8 * g);
-        st = E::mma(ak, qreg[ks], st);   // S^T[kv][q]
-        dpt = E::mma(av, oreg[ks], dpt); // dP^T[kv][q]
+        st = E::mma(frag_along_row<D>(sK, 32 * j, 16 * ks, lane), qreg[ks], st);   // S^T[kv][q]
+        dpt = E::mma(frag_along_row<D>(sV, 32 * j, 16 * ks, lane), oreg[ks], dpt); // dP^T[kv][q]
       }
+    };
+#pragma unroll
+    for (int j = 0; j < W; ++j) {
+      f32x16 st, dpt;
+      sdp(j, st, dpt);
+      float4 b4[4];
+#pragma unroll
+      for (int a = 0; a < 4; ++a) b4[a] = *reinterpret_cast<const float4*>(sB + 32 * j + 8 * a + 4 * g);
       float dsv[16];
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const int kr = c0 + 8 * (i >> 2) + 4 * g + (i & 3);
-        const bool ok = q_ok && kr < rows;
-        const float x = fast_exp2(st[i] * c2 - l2);
-        dsv[i] = ok ? x * (dpt[i] - dl) : 0.f;
+        const float x = fast_exp2(st[i] * c2 + (b4[i >> 2][i & 3] - l2));
+        dsv[i] = x * (dpt[i] - dl);
       }
       const u16x8 da[2] = {pack8<E>(dsv), pack8<E>(dsv + 8)};
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
 #pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-          const u16x8 bk = frag_down_rows<PITCH>(sK, c0 + 16 * hh, 32 * nt, lane);
-          adq[nt] = E::mma(da[hh], bk, adq[nt]);  // dQ += dS * K
-        }
+        for (int hh = 0; hh < 2; ++hh)
+          adq[nt] = E::mma(da[hh], frag_down_rows<D>(sKt, 32 * j + 16 * hh, 32 * nt, lane), adq[nt]);  // dQ += dS K
       }
     }
-    e = ne;
-    k0 = nk0;
-    kend = nkend;
+    have = more;
   }
 
   unsigned short* dqp = static_cast<unsigned short*>(p.dq) + b * p.dq_sb + si.off_q * p.dq_sr + n * p.dq_sh;
@@ -574,7 +673,8 @@ __global__ __launch_bounds__(256) void dq_kernel(Params p) {
 // ---------------------------------------------------------------------------
 inline int waves_for(int rows) {
   const int r = rows < kTileRows ? rows : kTileRows;
-  return (r + 31) / 32;
+  const int w = (r + 31) / 32;
+  return w == 3 ? 4 : w;  // kernels are built for 1, 2 and 4 waves
 }
 
 }  // namespace
@@ -604,35 +704,36 @@ int launch_prologue(const Params& p, void* stream) {
   return static_cast<int>(hipGetLastError());
 }
 
+#define BSA_DISPATCH_W(KERNEL, E, D, W, GRID, S, P)                                    \
+  do {                                                                                  \
+    if ((W) == 4) hipLaunchKernelGGL((KERNEL<E, D, 4>), GRID, dim3(256), 0, S, P);      \
+    else if ((W) == 2) hipLaunchKernelGGL((KERNEL<E, D, 2>), GRID, dim3(128), 0, S, P); \
+    else hipLaunchKernelGGL((KERNEL<E, D, 1>), GRID, dim3(64), 0, S, P);                \
+  } while (0)
+
+#define BSA_DISPATCH(KERNEL, W, GRID, S, P)                                     \
+  do {                                                                          \
+    const bool bf_ = (P).dtype == 2;                                            \
+    if ((P).D == 128) {                                                         \
+      if (bf_) BSA_DISPATCH_W(KERNEL, EBf16, 128, W, GRID, S, P);               \
+      else BSA_DISPATCH_W(KERNEL, EF16, 128, W, GRID, S, P);                    \
+    } else {                                                                    \
+      if (bf_) BSA_DISPATCH_W(KERNEL, EBf16, 64, W, GRID, S, P);                \
+      else BSA_DISPATCH_W(KERNEL, EF16, 64, W, GRID, S, P);                     \
+    }                                                                           \
+  } while (0)
+
 int launch_dkdv(const Params& p, void* stream) {
   const int nsub = (p.by + kTileRows - 1) / kTileRows;
   const dim3 grid(static_cast<unsigned>(static_cast<int64_t>(p.B) * p.Nkv * p.nkb * nsub));
-  const dim3 block(64 * waves_for(p.by));
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  const bool bf = p.dtype == 2;
-  if (p.D == 128) {
-    if (bf) hipLaunchKernelGGL((dkdv_kernel<EBf16, 128>), grid, block, 0, s, p);
-    else hipLaunchKernelGGL((dkdv_kernel<EF16, 128>), grid, block, 0, s, p);
-  } else {
-    if (bf) hipLaunchKernelGGL((dkdv_kernel<EBf16, 64>), grid, block, 0, s, p);
-    else hipLaunchKernelGGL((dkdv_kernel<EF16, 64>), grid, block, 0, s, p);
-  }
+  BSA_DISPATCH(dkdv_kernel, waves_for(p.by), grid, static_cast<hipStream_t>(stream), p);
   return static_cast<int>(hipGetLastError());
 }
 
 int launch_dq(const Params& p, void* stream) {
   const int nsub = (p.bx + kTileRows - 1) / kTileRows;
   const dim3 grid(static_cast<unsigned>(static_cast<int64_t>(p.B) * p.N * p.nqb * nsub));
-  const dim3 block(64 * waves_for(p.bx));
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  const bool bf = p.dtype == 2;
-  if (p.D == 128) {
-    if (bf) hipLaunchKernelGGL((dq_kernel<EBf16, 128>), grid, block, 0, s, p);
-    else hipLaunchKernelGGL((dq_kernel<EF16, 128>), grid, block, 0, s, p);
-  } else {
-    if (bf) hipLaunchKernelGGL((dq_kernel<EBf16, 64>), grid, block, 0, s, p);
-    else hipLaunchKernelGGL((dq_kernel<EF16, 64>), grid, block, 0, s, p);
-  }
+  BSA_DISPATCH(dq_kernel, waves_for(p.bx), grid, static_cast<hipStream_t>(stream), p);
   return static_cast<int>(hipGetLastError());
 }
 
