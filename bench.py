@@ -149,37 +149,69 @@ class Runner:
 # ---------------------------------------------------------------------------
 # CPU baseline: the oracle on a bounded sample
 # ---------------------------------------------------------------------------
-def cpu_baseline(case, o_host, lse_host, heads):
-    """Time the fp64 oracle backward on batch 0, the first ``heads`` KV-head groups."""
+def cpu_baseline(case, o_host, lse_host, min_seconds=10.0, max_runs=5):
+    """Time the fp64 oracle backward on the whole workload (median of repeated runs)."""
     import oracle
     try:
         from threadpoolctl import threadpool_info
         cores = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
     except Exception:  # pragma: no cover
         cores = os.cpu_count() or 1
-    G = case.N // case.Nkv
-    nq = heads * G
-    sl_q = lambda x: x[0:1, :nq]
-    sl_k = lambda x: x[0:1, :heads]
-    mask = None if case.mask is None else case.mask[0:1, :nq]
-    kw = dict(layout="BNSD", bx=case.bx, by=case.by, scale=case.scale)
-    if case.explicit_lengths:
-        kw.update(len_q=case.len_q[:1], len_kv=case.len_kv[:1])
-    t0 = time.perf_counter()
-    oracle.backward(sl_q(case.q), sl_k(case.k), sl_k(case.v), sl_q(o_host), sl_q(case.do),
-                    sl_q(lse_host), mask, **kw)
-    dt = time.perf_counter() - t0
-    nq_b = -(-int(case.len_q[0]) // case.bx)
-    nk_b = -(-int(case.len_kv[0]) // case.by)
-    blocks = int(np.count_nonzero(mask[0, :, :nq_b, :nk_b])) if mask is not None else nq * nq_b * nk_b
-    flops = 10.0 * case.bx * case.by * case.D * blocks
+    kw = dict(layout=case.layout, bx=case.bx, by=case.by, scale=case.scale)
+    if case.explicit_lengths or case.layout == "TND":
+        kw.update(len_q=case.len_q, len_kv=case.len_kv)
+    times = []
+    t_start = time.perf_counter()
+    while not times or (time.perf_counter() - t_start < min_seconds and len(times) < max_runs):
+        t0 = time.perf_counter()
+        oracle.backward(case.q, case.k, case.v, o_host, case.do, lse_host, case.mask, **kw)
+        times.append(time.perf_counter() - t0)
+    dt = float(np.median(times))
+    flops = 10.0 * case.bx * case.by * case.D * synth_blocks(case)
     return {
-        "value": flops / dt / 1e12,
+        "value": round(flops / dt / 1e12, 5),
         "unit": "TFLOP/s",
         "cores": int(cores),
         "kind": "oracle",
-        "sample": f"batch 0, query heads 0..{nq - 1} ({blocks} active blocks), fp64 NumPy, {dt:.1f} s",
+        "sample": f"the whole workload (all batches and heads), fp64 NumPy backward only, "
+                  f"median of {len(times)} runs: {dt:.2f} s",
     }
+
+
+def synth_blocks(case):
+    import synth
+    return synth.active_blocks(case)
+
+
+def kernel_source_hash():
+    import hashlib
+    path = os.path.join(ROOT, "block_sparse_attention_bwd_amd", "csrc", "bsa_kernels.hip")
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def traffic_from_profile(workload, kernel, launches_per_step=1):
+    """HBM bytes per launch of `kernel` from a committed rocprofv3 counter summary.
+
+    The summary records FETCH_SIZE and WRITE_SIZE (KiB per dispatch), the scale
+    factors measured on a plain copy kernel, and the sha256 of the kernel source
+    it was taken on; if the source has changed since, the figure is stale and
+    None is returned.
+    """
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_hbm_counters.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                vals[k.strip()] = v.strip()
+    if vals.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    fetch = float(vals["FETCH_SIZE_KiB_per_dispatch"]) * float(vals["fetch_scale"])
+    write = float(vals["WRITE_SIZE_KiB_per_dispatch"]) * float(vals["write_scale"])
+    return round((fetch + write) * 1024.0 * launches_per_step)
 
 
 def main(argv=None):
@@ -188,7 +220,6 @@ def main(argv=None):
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=2)
-    ap.add_argument("--cpu-heads", type=int, default=2, help="KV-head groups in the CPU oracle sample")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     args = ap.parse_args(argv)
     if args.gpus != 1:
@@ -242,7 +273,7 @@ def main(argv=None):
         "peak": MFMA_PEAK_BF16_TFLOPS,
         "unit": "TFLOP/s",
         "frac": round(achieved / MFMA_PEAK_BF16_TFLOPS, 4),
-        "traffic": None,
+        "traffic": traffic_from_profile(case.name, "dkdv_kernel"),
         "kernel": "dkdv_kernel",
         "kernel_ms": round(dkdv_ms, 5),
         "stage_ms": {k: round(v / max(1, ncalls), 5) for k, v in stage_ms.items()},
@@ -252,7 +283,7 @@ def main(argv=None):
     if not args.no_cpu:
         o_h = o.float().cpu().numpy()
         l_h = lse.cpu().numpy()
-        cpu = cpu_baseline(case, o_h, l_h, args.cpu_heads)
+        cpu = cpu_baseline(case, o_h, l_h)
 
     out = {
         "metric": "bwd TFLOP/s over active blocks (bf16) + % of MFMA peak, 1xMI355X",
