@@ -384,7 +384,7 @@ int make_plan(const Args& a, Plan* plan) {
     off = align_up(off + bytes);
   };
   const uint64_t rows = static_cast<uint64_t>(B) * N * Sq;
-  take(BSA_WS_SEQ, sizeof(bsa::SeqInfo) * static_cast<uint64_t>(B));
+  take(BSA_WS_SEQ, sizeof(bsa::SeqInfo) * static_cast<uint64_t>(B) + 4 * bsa::kConstFloats);
   take(BSA_WS_DELTA, 4 * rows);
   take(BSA_WS_LSE2, 4 * rows);
   take(BSA_WS_ROW_CNT, 4ull * B * N * nqb);
@@ -515,6 +515,8 @@ int bsa_bwd(BSA_ARGS_DECL, void* workspace, uint64_t workspace_size, void* strea
   bsa::Params& p = plan.p;
   char* ws = static_cast<char*>(workspace);
   p.seq = reinterpret_cast<bsa::SeqInfo*>(ws + plan.off[BSA_WS_SEQ]);
+  float* consts = reinterpret_cast<float*>(ws + plan.off[BSA_WS_SEQ] + sizeof(bsa::SeqInfo) * plan.seq.size());
+  p.consts = consts;
   p.delta = reinterpret_cast<float*>(ws + plan.off[BSA_WS_DELTA]);
   p.lse2 = reinterpret_cast<float*>(ws + plan.off[BSA_WS_LSE2]);
   p.row_cnt = reinterpret_cast<int32_t*>(ws + plan.off[BSA_WS_ROW_CNT]);
@@ -534,7 +536,7 @@ int bsa_bwd(BSA_ARGS_DECL, void* workspace, uint64_t workspace_size, void* strea
     chunk.first = static_cast<int32_t>(first);
     chunk.count = static_cast<int32_t>(std::min<size_t>(bsa::kMaxInlineSeq, plan.seq.size() - first));
     for (int i = 0; i < chunk.count; ++i) chunk.s[i] = plan.seq[first + i];
-    herr = bsa::launch_stage_seq(chunk, p.seq, stream);
+    herr = bsa::launch_stage_seq(chunk, p.seq, consts, stream);
   }
   if (herr == 0) herr = bsa::launch_prologue(p, stream);
   if (herr) return fail(BSA_ERR_RUNTIME, "prologue launch failed: %s", hipGetErrorString(static_cast<hipError_t>(herr)));

@@ -49,6 +49,7 @@ struct Params {
 
   // workspace regions
   SeqInfo* seq;
+  const float* consts;  // kConstFloats floats after the sequence table: zeros, then +inf, -inf
   float* delta;
   float* lse2;
   int32_t* row_cnt;
@@ -56,6 +57,13 @@ struct Params {
   int32_t* col_cnt;
   int32_t* col_list;
 };
+
+// Constant block staged with the sequence table: kZeroFloats zeros (rows past a
+// slice's end are loaded from here), then +inf and -inf.
+constexpr int kZeroFloats = 64;
+constexpr int kConstFloats = kZeroFloats + 64;
+constexpr int kConstPosInf = kZeroFloats;
+constexpr int kConstNegInf = kZeroFloats + 1;
 
 // Host-side description of the sequences (at most kMaxInlineSeq per staging launch).
 constexpr int kMaxInlineSeq = 64;
@@ -66,7 +74,7 @@ struct SeqChunk {
 };
 
 // Launch helpers (bsa_kernels.hip).  Return a hipError_t value (0 = success).
-int launch_stage_seq(const SeqChunk& chunk, SeqInfo* dst, void* stream);
+int launch_stage_seq(const SeqChunk& chunk, SeqInfo* dst, float* consts, void* stream);
 int launch_prologue(const Params& p, void* stream);
 int launch_dkdv(const Params& p, void* stream);
 int launch_dq(const Params& p, void* stream);

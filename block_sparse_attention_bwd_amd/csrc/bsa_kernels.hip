@@ -12,11 +12,16 @@
 //   dkdv        one workgroup per (batch, KV head, KV block [, 128-row part]);
 //               K/V rows stay in registers; walks the Q blocks that select it
 //               for every query head of its group:  S, P, dV += P^T dO,
-//               dP, dS, dK += dS^T Q  (four MFMA GEMMs per step)
+//               dP, dS, dK += dS^T Q  (four MFMA GEMMs per step).  Staged Q/dO
+//               tiles use a padded pitch; the next tile is prefetched into
+//               registers during the current one.
 //   dq          one workgroup per (batch, query head, Q block [, part]);
-//               Q/dO rows in registers; walks its KV blocks: S, P, dP, dS,
-//               dQ += dS K (three MFMA GEMMs per step).  No atomics anywhere,
+//               Q/dO rows in registers; streams 32-row slices of its KV blocks
+//               through double-buffered, XOR-swizzled LDS tiles: S, P, dP, dS,
+//               dQ += dS K (three MFMA GEMMs per slice).  No atomics anywhere,
 //               so every output is written exactly once, in a fixed order.
+// Both MFMA kernels number their workgroups so that each XCD gets a
+// contiguous range (the workgroups sharing a head's tiles share one L2).
 //
 // MFMA used: v_mfma_f32_32x32x16_{bf16,f16}.  Operand layout (wave64, lane l,
 // g = l / 32):  A[m][k]: lane holds row m = l % 32, k = 8g .. 8g+7;
@@ -40,7 +45,11 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr int kTileRows = 128;  // rows per LDS tile and per workgroup part
+constexpr int kTileRows = 128;  // rows per workgroup part (32 per wave, at most 4 waves)
+#ifndef BSA_STAGE_SLICES
+#define BSA_STAGE_SLICES 1
+#endif
+constexpr int kStageSlices = BSA_STAGE_SLICES;  // 32-row slices staged per pipeline stage
 
 struct EBf16 {
   static __device__ __forceinline__ f32x16 mma(u16x8 a, u16x8 b, f32x16 c) {
@@ -81,9 +90,13 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // ---------------------------------------------------------------------------
 // per-sequence table
 // ---------------------------------------------------------------------------
-__global__ void stage_seq_kernel(SeqChunk c, SeqInfo* dst) {
+__global__ void stage_seq_kernel(SeqChunk c, SeqInfo* dst, float* consts) {
   const int t = threadIdx.x;
   if (t < c.count) dst[c.first + t] = c.s[t];
+  if (c.first == 0) {
+    for (int i = t; i < kConstFloats; i += blockDim.x)
+      consts[i] = i == kConstPosInf ? __builtin_inff() : i == kConstNegInf ? -__builtin_inff() : 0.f;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -202,19 +215,21 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef unsigned short u16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 typedef __attribute__((address_space(3))) unsigned short lds_u16;
+typedef __attribute__((address_space(3))) void lds_void;
 
-// LDS tiles are row-major and padded.  A tile read along its rows by 16-byte
-// reads (MFMA A/B fragments of 8 consecutive columns) uses a pitch of D + 8
-// elements; a tile read down its rows by transposing 8-byte reads uses D + 16.
-// Measured on gfx950, each pitch keeps its own access pattern free of bank
-// conflicts (16-byte reads of 16 consecutive rows; transposing reads of 4
-// consecutive rows x 32 bytes per 16 lanes) and halves the throughput of the
-// other, so a tile that is read both ways is staged twice.
+// LDS tiles: row-major, D elements per row, no padding; the 16-byte chunks of
+// row r are XOR-permuted by swz(r) so that 16-byte reads of one chunk column
+// by 16 consecutive rows and transposing reads of 4 consecutive rows spread
+// over the banks (the best single layout for both patterns measured on gfx950).
 template <int D>
-struct Pitch {
-  static constexpr int A = D + 8;   // along rows
-  static constexpr int T = D + 16;  // down rows
-};
+__device__ __forceinline__ int swz(int r) {
+  if constexpr (D == 128) return 2 * (r & 3) + ((r >> 2) & 1) + 8 * ((r >> 3) & 1);
+  else return 2 * (r & 3) + ((r >> 2) & 1);
+}
+template <int D>
+__device__ __forceinline__ int tile_off(int r, int col) {
+  return r * D + ((((col >> 3) ^ swz<D>(r))) << 3) + (col & 7);
+}
 
 // ds_read_b64_tr_b16: within each 16-lane block, lanes 4t..4t+3 address four
 // consecutive 16-bit elements of row t (t = 0..3); lane j of the block then
@@ -232,11 +247,10 @@ __device__ __forceinline__ u16x4 lds_read_tr(const unsigned short* tile, int ele
 // note at the top of this file).
 template <int D>
 __device__ __forceinline__ u16x8 frag_down_rows(const unsigned short* tile, int r0, int col0, int lane) {
-  constexpr int P = Pitch<D>::T;
   const int row = r0 + 4 * (lane >> 5) + ((lane & 15) >> 2);
   const int col = col0 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-  const u16x4 a = lds_read_tr(tile, row * P + col);
-  const u16x4 b = lds_read_tr(tile, (row + 8) * P + col);
+  const u16x4 a = lds_read_tr(tile, tile_off<D>(row, col));
+  const u16x4 b = lds_read_tr(tile, tile_off<D>(row + 8, col));
   return u16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
 }
 
@@ -244,13 +258,12 @@ __device__ __forceinline__ u16x8 frag_down_rows(const unsigned short* tile, int 
 // col0 + 8g .. col0 + 8g + 7 of row r0 + m.
 template <int D>
 __device__ __forceinline__ u16x8 frag_along_row(const unsigned short* tile, int r0, int col0, int lane) {
-  constexpr int P = Pitch<D>::A;
-  return *reinterpret_cast<const u16x8*>(tile + (r0 + (lane & 31)) * P + col0 + 8 * (lane >> 5));
+  return *reinterpret_cast<const u16x8*>(tile + tile_off<D>(r0 + (lane & 31), col0 + 8 * (lane >> 5)));
 }
 
 // The work of a workgroup is a stream of 32-row slices (of Q blocks for the
-// dK/dV kernel, of KV blocks for the dQ kernel); a stage stages W slices, one
-// per wave of rows, into a 32*W-row tile.  nrows == 0 marks an empty slice.
+// dK/dV kernel, of KV blocks for the dQ kernel), staged CH at a time; every
+// wave computes on every slice of a stage.  nrows == 0 marks an empty slice.
 struct Slice {
   int head;   // query head (dK/dV kernel); unused by the dQ kernel
   int row0;   // first sequence-local row
@@ -258,27 +271,28 @@ struct Slice {
 };
 
 // sl[j] for a per-lane j, by selects (no dynamic register indexing).
-template <int W>
+template <int CH>
 __device__ __forceinline__ Slice pick_slice(const Slice* sl, int j) {
   Slice r = sl[0];
 #pragma unroll
-  for (int k = 1; k < W; ++k)
+  for (int k = 1; k < CH; ++k)
     if (j == k) r = sl[k];
   return r;
 }
 
-// Register prefetch of one stage: for each of the two tensors, thread tid
-// holds chunks c = it * 64W + tid (16 bytes, it < D/16) of the 32W x D tile;
-// chunk c is row c / (D/8), and row r belongs to slice r / 32, which is a
-// compile-time function of `it` for every (D, W) used.
-template <int D, int W>
+// Register prefetch of one stage of CH slices (32*CH rows): for each of the
+// two tensors, thread tid holds chunks c = it * NTHR + tid (16 bytes) of the
+// 32CH x D tile; chunk c is row c / (D/8), and row r belongs to slice r / 32,
+// a compile-time function of `it` (NTHR and 32 * D/8 divide one another).
+// Rows past a slice's end hold zeros.
+template <int D, int CH, int NTHR>
 struct StagePrefetch {
   static constexpr int CPR = D / 8;
-  static constexpr int CPT = D / 16;
-  static constexpr int NTHR = 64 * W;
+  static constexpr int CPT = 32 * CH * CPR / NTHR;
+  static_assert(CPT * NTHR == 32 * CH * CPR, "stage must split evenly over the threads");
   u16x8 a[CPT], b[CPT];
 
-  // pa/pb(slice, row) give the row's address in the two source tensors
+  // addr(slice, row, pa, pb) gives the row's address in the two source tensors
   template <class Addr>
   __device__ __forceinline__ void load(const Slice* sl, Addr addr, int tid) {
 #pragma unroll
@@ -301,18 +315,78 @@ struct StagePrefetch {
     }
   }
 
-  // Tensor a goes to tiles ta (pitch A) and, if given, ta_t (pitch T); tensor b
-  // to tb (pitch A) and, if given, tb_t (pitch T).
-  __device__ __forceinline__ void store(unsigned short* ta, unsigned short* ta_t, unsigned short* tb,
-                                        unsigned short* tb_t, int tid) const {
+  __device__ __forceinline__ void store(unsigned short* ta, unsigned short* tb, int tid) const {
 #pragma unroll
     for (int it = 0; it < CPT; ++it) {
       const int c = it * NTHR + tid;
       const int r = c / CPR, k = c % CPR;
-      *reinterpret_cast<u16x8*>(ta + r * Pitch<D>::A + 8 * k) = a[it];
-      *reinterpret_cast<u16x8*>(tb + r * Pitch<D>::A + 8 * k) = b[it];
-      if (ta_t) *reinterpret_cast<u16x8*>(ta_t + r * Pitch<D>::T + 8 * k) = a[it];
-      if (tb_t) *reinterpret_cast<u16x8*>(tb_t + r * Pitch<D>::T + 8 * k) = b[it];
+      *reinterpret_cast<u16x8*>(ta + tile_off<D>(r, 8 * k)) = a[it];
+      *reinterpret_cast<u16x8*>(tb + tile_off<D>(r, 8 * k)) = b[it];
+    }
+  }
+};
+
+// Logical workgroup id: hardware hands consecutive workgroup ids to the eight
+// XCDs in turn; this bijection gives each XCD a contiguous range of logical
+// ids, so workgroups that share a head's tiles share one L2.
+__device__ __forceinline__ int xcd_local_id() {
+  const int nb = gridDim.x, bid = blockIdx.x;
+  const int xcd = bid & 7, slot = bid >> 3;
+  const int per = nb >> 3, rem = nb & 7;
+  return xcd * per + min(xcd, rem) + slot;
+}
+
+// ---------------------------------------------------------------------------
+// dK / dV: KV-block-outer
+// ---------------------------------------------------------------------------
+// MFMA B fragment of a row-major [rows][PITCH] LDS tile read along its rows:
+// lane (column n = l % 32, g = l / 32) gets rows r0 + 4g + {0,1,2,3} and
+// r0 + 8 + 4g + {0,1,2,3} of column col0 + n, the k order a C tile's
+// registers 8h..8h+7 use (see the layout note at the top of this file).
+template <int PITCH>
+__device__ __forceinline__ u16x8 frag_down_rows_padded(const unsigned short* tile, int r0, int col0, int lane) {
+  const int row = r0 + 4 * (lane >> 5) + ((lane & 15) >> 2);
+  const int col = col0 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  const u16x4 a = lds_read_tr(tile, row * PITCH + col);
+  const u16x4 b = lds_read_tr(tile, (row + 8) * PITCH + col);
+  return u16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+}
+
+// Register prefetch of one staged tile: rows [r0, r0 + rows) of two row-major
+// tensors (row stride sr elements, D columns), 16 bytes per chunk, chunk
+// c = it * nthr + tid.  Rows past `rows` are zero.  With H = 32 * waves rows
+// per stage every thread holds exactly D / 16 chunks of each tensor.
+template <int D>
+struct PaddedTilePrefetch {
+  static constexpr int CPR = D / 8;
+  static constexpr int CPT = D / 16;
+  u16x8 a[CPT], b[CPT];
+
+  __device__ __forceinline__ void load(const unsigned short* pa, const unsigned short* pb, int64_t sr,
+                                       int r0, int rows, int tid, int nthr) {
+#pragma unroll
+    for (int it = 0; it < CPT; ++it) {
+      const int c = it * nthr + tid;
+      const int r = c / CPR, k = c % CPR;
+      u16x8 x = {0, 0, 0, 0, 0, 0, 0, 0};
+      u16x8 y = x;
+      if (r < rows) {
+        x = *reinterpret_cast<const u16x8*>(pa + (r0 + r) * sr + 8 * k);
+        y = *reinterpret_cast<const u16x8*>(pb + (r0 + r) * sr + 8 * k);
+      }
+      a[it] = x;
+      b[it] = y;
+    }
+  }
+
+  template <int PITCH>
+  __device__ __forceinline__ void store(unsigned short* ta, unsigned short* tb, int tid, int nthr) const {
+#pragma unroll
+    for (int it = 0; it < CPT; ++it) {
+      const int c = it * nthr + tid;
+      const int r = c / CPR, k = c % CPR;
+      *reinterpret_cast<u16x8*>(ta + r * PITCH + 8 * k) = a[it];
+      *reinterpret_cast<u16x8*>(tb + r * PITCH + 8 * k) = b[it];
     }
   }
 };
@@ -320,46 +394,43 @@ struct StagePrefetch {
 // ---------------------------------------------------------------------------
 // dK / dV: KV-block-outer
 // ---------------------------------------------------------------------------
-// Slices of the Q blocks that select this KV block, for the query heads of
-// the group in ascending order, each head's blocks in ascending order.
-struct QSliceWalk {
-  int n, n_end, e, cnt, q, qend;
-
-  __device__ __forceinline__ bool next(const Params& p, int64_t bn0, int jb, int len_q, Slice& s) {
-    while (q >= qend) {
-      ++e;
-      while (e >= cnt) {
-        if (++n >= n_end) return false;
-        e = 0;
-        cnt = p.col_cnt[(bn0 + n) * p.nkb + jb];
-      }
-      q = p.col_list[((bn0 + n) * p.nkb + jb) * p.nqb + e] * p.bx;
-      qend = min(q + p.bx, len_q);
-    }
-    s.head = n;
-    s.row0 = q;
-    s.nrows = min(32, qend - q);
-    q += 32;
-    return true;
-  }
+// Walk state over (query head n of the group, position e in its list of
+// Q blocks selecting this KV block, first row q0 of the stage in that block).
+struct QTile {
+  int n, e, q0, qend;
 };
 
+__device__ __forceinline__ bool dkdv_seek(const Params& p, int64_t bn0, int jb, int n_end, int len_q, QTile& t) {
+  // advance (t.n, t.e) to the next existing list entry; set q0/qend
+  while (t.n < n_end) {
+    const int64_t col = (bn0 + t.n) * p.nkb + jb;
+    if (t.e < p.col_cnt[col]) {
+      const int ib = p.col_list[col * p.nqb + t.e];
+      t.q0 = ib * p.bx;
+      t.qend = min(t.q0 + p.bx, len_q);
+      return true;
+    }
+    ++t.n;
+    t.e = 0;
+  }
+  return false;
+}
+
 template <class E, int D, int W>
-__global__ __launch_bounds__(64 * W) void dkdv_kernel(Params p) {
+__global__ __launch_bounds__(256) void dkdv_kernel(Params p) {
   constexpr int KS = D / 16;  // K=16 steps over the head dim
   constexpr int NT = D / 32;  // 32-wide column tiles of the head dim
-  constexpr int H = 32 * W;   // staged Q rows
-  __shared__ __align__(16) unsigned short sQ[H * Pitch<D>::A];   // Q rows, read along
-  __shared__ __align__(16) unsigned short sO[H * Pitch<D>::A];   // dOut rows, read along
-  __shared__ __align__(16) unsigned short sQt[H * Pitch<D>::T];  // the same rows, read down
-  __shared__ __align__(16) unsigned short sOt[H * Pitch<D>::T];
-  __shared__ __align__(16) float sL[H];
-  __shared__ __align__(16) float sDl[H];
+  constexpr int PITCH = D + 8;
+  __shared__ __align__(16) unsigned short sQ[kTileRows * PITCH];
+  __shared__ __align__(16) unsigned short sO[kTileRows * PITCH];  // dOut rows
+  __shared__ __align__(16) float sL[kTileRows];
+  __shared__ __align__(16) float sDl[kTileRows];
 
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, nthr = blockDim.x;
   const int lane = tid & 63, w = tid >> 6, l32 = lane & 31, g = lane >> 5;
+  const int H = nthr / 2;  // staged Q rows: 32 per wave
 
-  int wid = blockIdx.x;
+  int wid = xcd_local_id();
   const int nsub = (p.by + kTileRows - 1) / kTileRows;
   const int sub = wid % nsub;
   wid /= nsub;
@@ -402,81 +473,65 @@ __global__ __launch_bounds__(64 * W) void dkdv_kernel(Params p) {
 
   const float c2 = p.scale_log2e;
   const int64_t bn0 = static_cast<int64_t>(b) * p.N;
+  const int n_end = (h + 1) * p.G;
   const unsigned short* qbase = static_cast<const unsigned short*>(p.q) + b * p.q_sb + si.off_q * p.q_sr;
   const unsigned short* obase = static_cast<const unsigned short*>(p.dout) + b * p.q_sb + si.off_q * p.q_sr;
-  auto addr = [&](const Slice& s, int row, const unsigned short*& pa, const unsigned short*& pb) {
-    const int64_t off = s.head * p.q_sh + row * p.q_sr;
-    pa = qbase + off;
-    pb = obase + off;
-  };
 
-  QSliceWalk walk{h * p.G, (h + 1) * p.G, -1, 0, 0, 0};
-  walk.cnt = p.col_cnt[(bn0 + walk.n) * p.nkb + jb];
-  Slice sl[W];
-  auto gather = [&]() {
-    bool any = false;
-#pragma unroll
-    for (int j = 0; j < W; ++j) {
-      if (!walk.next(p, bn0, jb, si.len_q, sl[j])) sl[j] = Slice{h * p.G, 0, 0};
-      any |= sl[j].nrows > 0;
-    }
-    return any;
-  };
-
-  StagePrefetch<D, W> pf;
+  PaddedTilePrefetch<D> pf;
   float pl = 0.f, pd = 0.f;
-  auto prefetch = [&]() {
-    pf.load(sl, addr, tid);
-    if (tid < H) {  // row tid of the stage belongs to slice tid / 32
-      const Slice s = pick_slice<W>(sl, tid >> 5);
-      const int rr = tid & 31;
-      const int64_t li = (bn0 + s.head) * p.sq_max + s.row0 + rr;
-      // rows past a slice's end get LSE = +inf, so their P is exactly 0
-      pl = rr < s.nrows ? p.lse2[li] : __builtin_inff();
-      pd = rr < s.nrows ? p.delta[li] : 0.f;
-    }
+  auto prefetch = [&](const QTile& t) {
+    const int rows = min(H, t.qend - t.q0);
+    pf.load(qbase + t.n * p.q_sh, obase + t.n * p.q_sh, p.q_sr, t.q0, rows, tid, nthr);
+    const int64_t li = (bn0 + t.n) * p.sq_max + t.q0 + tid;
+    // rows past the block get LSE = +inf, so their P is exactly 0 with no per-element test
+    pl = tid < rows ? p.lse2[li] : __builtin_inff();
+    pd = tid < rows ? p.delta[li] : 0.f;
   };
 
-  bool have = gather();
-  if (have) prefetch();
+  QTile cur{h * p.G, 0, 0, 0};
+  bool have = dkdv_seek(p, bn0, jb, n_end, si.len_q, cur);
+  if (have) prefetch(cur);
   while (have) {
-    __syncthreads();  // every wave is done with the previous stage
-    pf.store(sQ, sQt, sO, sOt, tid);
+    const int rows = min(H, cur.qend - cur.q0);
+    __syncthreads();  // every wave is done with the previous tile
+    pf.template store<PITCH>(sQ, sO, tid, nthr);
     if (tid < H) {
       sL[tid] = pl;
       sDl[tid] = pd;
     }
     __syncthreads();
-    const bool more = gather();
-    if (more) prefetch();  // global loads stay in flight during the MFMA work below
+    QTile nxt = cur;
+    nxt.q0 += H;
+    bool more = nxt.q0 < nxt.qend;
+    if (!more) {
+      ++nxt.e;
+      more = dkdv_seek(p, bn0, jb, n_end, si.len_q, nxt);
+    }
+    if (more) prefetch(nxt);  // global loads stay in flight during the MFMA work below
 
-    // S and dP of chunk j (32 Q rows x this wave's 32 KV rows)
-    auto sdp = [&](int j, f32x16& s, f32x16& dpv) {
-      s = f32x16{};
-      dpv = f32x16{};
+    for (int c0 = 0; c0 < rows; c0 += 32) {
+      f32x16 s = {}, dpv = {};
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        s = E::mma(frag_along_row<D>(sQ, 32 * j, 16 * ks, lane), kreg[ks], s);    // S[q][kv]
-        dpv = E::mma(frag_along_row<D>(sO, 32 * j, 16 * ks, lane), vreg[ks], dpv); // dP = dOut * V^T
+        const u16x8 aq = *reinterpret_cast<const u16x8*>(sQ + (c0 + l32) * PITCH + 16 * ks + 8 * g);
+        const u16x8 ao = *reinterpret_cast<const u16x8*>(sO + (c0 + l32) * PITCH + 16 * ks + 8 * g);
+        s = E::mma(aq, kreg[ks], s);      // S[q][kv] (unscaled); this lane's column is my_kv
+        dpv = E::mma(ao, vreg[ks], dpv);  // dP[q][kv] = dOut * V^T
       }
-    };
-#pragma unroll
-    for (int j = 0; j < W; ++j) {
-      f32x16 s, dpv;
-      sdp(j, s, dpv);
-      // this lane's 16 score rows are 32j + 8a + 4g + {0..3}: four float4 reads each
+      // this lane's 16 score rows are c0 + 8a + 4g + {0..3}: four float4 reads each
       float4 l4[4], d4[4];
 #pragma unroll
       for (int a = 0; a < 4; ++a) {
-        l4[a] = *reinterpret_cast<const float4*>(sL + 32 * j + 8 * a + 4 * g);
-        d4[a] = *reinterpret_cast<const float4*>(sDl + 32 * j + 8 * a + 4 * g);
+        l4[a] = *reinterpret_cast<const float4*>(sL + c0 + 8 * a + 4 * g);
+        d4[a] = *reinterpret_cast<const float4*>(sDl + c0 + 8 * a + 4 * g);
       }
       float pv[16], dsv[16];
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const float x = fast_exp2(s[i] * c2 - l4[i >> 2][i & 3]);  // P = exp(scale*S - LSE)
+        const float li = l4[i >> 2][i & 3], di = d4[i >> 2][i & 3];
+        const float x = fast_exp2(s[i] * c2 - li);  // P = exp(scale*S - LSE)
         pv[i] = kv_ok ? x : 0.f;
-        dsv[i] = pv[i] * (dpv[i] - d4[i >> 2][i & 3]);           // dS = P o (dP - softmax_grad)
+        dsv[i] = pv[i] * (dpv[i] - di);              // dS = P o (dP - softmax_grad)
       }
       const u16x8 pa[2] = {pack8<E>(pv), pack8<E>(pv + 8)};
       const u16x8 da[2] = {pack8<E>(dsv), pack8<E>(dsv + 8)};
@@ -484,11 +539,14 @@ __global__ __launch_bounds__(64 * W) void dkdv_kernel(Params p) {
       for (int nt = 0; nt < NT; ++nt) {
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
-          adv[nt] = E::mma(pa[hh], frag_down_rows<D>(sOt, 32 * j + 16 * hh, 32 * nt, lane), adv[nt]);  // dV += P^T dOut
-          adk[nt] = E::mma(da[hh], frag_down_rows<D>(sQt, 32 * j + 16 * hh, 32 * nt, lane), adk[nt]);  // dK += dS^T Q
+          const u16x8 bo = frag_down_rows_padded<PITCH>(sO, c0 + 16 * hh, 32 * nt, lane);
+          const u16x8 bq = frag_down_rows_padded<PITCH>(sQ, c0 + 16 * hh, 32 * nt, lane);
+          adv[nt] = E::mma(pa[hh], bo, adv[nt]);  // dV += P^T * dOut
+          adk[nt] = E::mma(da[hh], bq, adk[nt]);  // dK += dS^T * Q
         }
       }
     }
+    cur = nxt;
     have = more;
   }
 
@@ -533,16 +591,16 @@ template <class E, int D, int W>
 __global__ __launch_bounds__(64 * W) void dq_kernel(Params p) {
   constexpr int KS = D / 16;
   constexpr int NT = D / 32;
-  constexpr int H = 32 * W;  // staged K/V rows
-  __shared__ __align__(16) unsigned short sK[H * Pitch<D>::A];   // K rows, read along
-  __shared__ __align__(16) unsigned short sKt[H * Pitch<D>::T];  // the same rows, read down
-  __shared__ __align__(16) unsigned short sV[H * Pitch<D>::A];
-  __shared__ __align__(16) float sB[H];  // 0 for rows that take part, -inf for padding rows
+  constexpr int CH = kStageSlices;
+  constexpr int H = 32 * CH;  // staged K/V rows
+  constexpr int NTHR = 64 * W;
+  __shared__ __align__(16) unsigned short sK[2][H * D], sV[2][H * D];
+  __shared__ __align__(16) float sB[2][CH * 64];  // per slice: 32 row biases (0 / -inf), 32 unused
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6, l32 = lane & 31, g = lane >> 5;
 
-  int wid = blockIdx.x;
+  int wid = xcd_local_id();
   const int nsub = (p.bx + kTileRows - 1) / kTileRows;
   const int sub = wid % nsub;
   wid /= nsub;
@@ -589,57 +647,55 @@ __global__ __launch_bounds__(64 * W) void dq_kernel(Params p) {
   const int64_t kv_base = b * p.kv_sb + si.off_kv * p.kv_sr + h * p.kv_sh;
   const unsigned short* kp = static_cast<const unsigned short*>(p.k) + kv_base;
   const unsigned short* vp = static_cast<const unsigned short*>(p.v) + kv_base;
-  auto addr = [&](const Slice& s, int row, const unsigned short*& pa, const unsigned short*& pb) {
-    pa = kp + row * p.kv_sr;
-    pb = vp + row * p.kv_sr;
-  };
   const float c2 = p.scale_log2e;
 
   KVSliceWalk walk{-1, p.row_cnt[bn * p.nqb + ib], 0, 0, p.row_list + (bn * p.nqb + ib) * p.nkb};
-  Slice sl[W];
+  Slice sl[CH];
   auto gather = [&]() {
     bool any = false;
 #pragma unroll
-    for (int j = 0; j < W; ++j) {
+    for (int j = 0; j < CH; ++j) {
       if (!walk.next(p, si.len_kv, sl[j])) sl[j] = Slice{0, 0, 0};
       any |= sl[j].nrows > 0;
     }
     return any;
   };
-
-  StagePrefetch<D, W> pf;
-  float pb = 0.f;
+  auto addr = [&](const Slice& s, int row, const unsigned short*& pa, const unsigned short*& pb) {
+    pa = kp + row * p.kv_sr;
+    pb = vp + row * p.kv_sr;
+  };
+  StagePrefetch<D, CH, NTHR> pf;
+  constexpr int BPT = (H + NTHR - 1) / NTHR;
+  float pb[BPT];
   auto prefetch = [&]() {
     pf.load(sl, addr, tid);
-    if (tid < H) pb = (tid & 31) < pick_slice<W>(sl, tid >> 5).nrows ? 0.f : -__builtin_inff();
+#pragma unroll
+    for (int k = 0; k < BPT; ++k) {
+      const int r = tid + k * NTHR;
+      if (r < H) pb[k] = (r & 31) < pick_slice<CH>(sl, r >> 5).nrows ? 0.f : -__builtin_inff();
+    }
+  };
+  auto commit = [&](unsigned short* tk, unsigned short* tv, float* tb) {
+    pf.store(tk, tv, tid);
+#pragma unroll
+    for (int k = 0; k < BPT; ++k) {
+      const int r = tid + k * NTHR;
+      if (r < H) tb[64 * (r >> 5) + (r & 31)] = pb[k];
+    }
   };
 
-  bool have = gather();
-  if (have) prefetch();
-  while (have) {
-    __syncthreads();
-    pf.store(sK, sKt, sV, nullptr, tid);
-    if (tid < H) sB[tid] = pb;
-    __syncthreads();
-    const bool more = gather();
-    if (more) prefetch();
-
-    auto sdp = [&](int j, f32x16& st, f32x16& dpt) {
-      st = f32x16{};
-      dpt = f32x16{};
+  auto compute = [&](const unsigned short* tk, const unsigned short* tv, const float* tb) {
+#pragma unroll
+    for (int j = 0; j < CH; ++j) {
+      f32x16 st = {}, dpt = {};
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        st = E::mma(frag_along_row<D>(sK, 32 * j, 16 * ks, lane), qreg[ks], st);   // S^T[kv][q]
-        dpt = E::mma(frag_along_row<D>(sV, 32 * j, 16 * ks, lane), oreg[ks], dpt); // dP^T[kv][q]
+        st = E::mma(frag_along_row<D>(tk, 32 * j, 16 * ks, lane), qreg[ks], st);   // S^T[kv][q]
+        dpt = E::mma(frag_along_row<D>(tv, 32 * j, 16 * ks, lane), oreg[ks], dpt); // dP^T[kv][q]
       }
-    };
-#pragma unroll
-    for (int j = 0; j < W; ++j) {
-      f32x16 st, dpt;
-      sdp(j, st, dpt);
       float4 b4[4];
 #pragma unroll
-      for (int a = 0; a < 4; ++a) b4[a] = *reinterpret_cast<const float4*>(sB + 32 * j + 8 * a + 4 * g);
+      for (int a = 0; a < 4; ++a) b4[a] = *reinterpret_cast<const float4*>(tb + 64 * j + 8 * a + 4 * g);
       float dsv[16];
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
@@ -651,10 +707,27 @@ __global__ __launch_bounds__(64 * W) void dq_kernel(Params p) {
       for (int nt = 0; nt < NT; ++nt) {
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh)
-          adq[nt] = E::mma(da[hh], frag_down_rows<D>(sKt, 32 * j + 16 * hh, 32 * nt, lane), adq[nt]);  // dQ += dS K
+          adq[nt] = E::mma(da[hh], frag_down_rows<D>(tk, 32 * j + 16 * hh, 32 * nt, lane), adq[nt]);  // dQ += dS K
       }
     }
-    have = more;
+  };
+
+  bool have = gather();
+  if (have) {
+    prefetch();
+    commit(sK[0], sV[0], sB[0]);
+  }
+  bool more = have && gather();
+  if (more) prefetch();
+  __syncthreads();
+  for (int cur = 0; have; cur ^= 1) {
+    if (more) commit(sK[cur ^ 1], sV[cur ^ 1], sB[cur ^ 1]);
+    const bool next = more;
+    more = more && gather();
+    if (more) prefetch();
+    compute(sK[cur], sV[cur], sB[cur]);
+    __syncthreads();
+    have = next;
   }
 
   unsigned short* dqp = static_cast<unsigned short*>(p.dq) + b * p.dq_sb + si.off_q * p.dq_sr + n * p.dq_sh;
@@ -679,9 +752,9 @@ inline int waves_for(int rows) {
 
 }  // namespace
 
-int launch_stage_seq(const SeqChunk& chunk, SeqInfo* dst, void* stream) {
+int launch_stage_seq(const SeqChunk& chunk, SeqInfo* dst, float* consts, void* stream) {
   hipLaunchKernelGGL(stage_seq_kernel, dim3(1), dim3(kMaxInlineSeq), 0,
-                     static_cast<hipStream_t>(stream), chunk, dst);
+                     static_cast<hipStream_t>(stream), chunk, dst, consts);
   return static_cast<int>(hipGetLastError());
 }
 
