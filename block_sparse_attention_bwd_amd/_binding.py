@@ -30,7 +30,8 @@ BSA_DTYPE_F32 = 3
 BSA_DTYPE_BOOL = 4
 
 NO_WINDOW = 2147483647
-WS_REGIONS = ("seq", "delta", "lse2", "row_cnt", "row_list", "col_cnt", "col_list", "total")
+WS_REGIONS = ("seq", "delta", "lse2", "row_cnt", "row_list", "col_cnt", "col_list", "plan", "partial",
+              "total")
 
 
 class bsa_tensor(ctypes.Structure):

@@ -318,8 +318,11 @@ int make_plan(const Args& a, Plan* plan) {
   }
   if (B * N * nqb * nkb > kInt32Max) return fail(BSA_ERR_PARAM_INVALID, "block grid too large for int32 lists");
   const int64_t nsub_q = ceil_div(bx, 128), nsub_kv = ceil_div(by, 128);
-  if (B * N * nqb * nsub_q > kInt32Max || B * Nkv * nkb * nsub_kv > kInt32Max)
-    return fail(BSA_ERR_PARAM_INVALID, "launch grid too large");
+  if (B * N * nqb * nsub_q + bsa::kMaxSlots > bsa::kMaxGridGroups ||
+      B * Nkv * nkb * nsub_kv + bsa::kMaxSlots > bsa::kMaxGridGroups ||
+      bsa::prologue_grid(B, N, Sq, nqb, nkb).total() > bsa::kMaxGridGroups)
+    return fail(BSA_ERR_PARAM_INVALID, "launch grid too large (more than %lld workgroups)",
+                static_cast<long long>(bsa::kMaxGridGroups));
 
   // ---- plan -----------------------------------------------------------------
   bsa::Params& p = plan->p;
@@ -391,7 +394,15 @@ int make_plan(const Args& a, Plan* plan) {
   take(BSA_WS_ROW_LIST, 4ull * B * N * nqb * nkb);
   take(BSA_WS_COL_CNT, 4ull * B * N * nkb);
   take(BSA_WS_COL_LIST, 4ull * B * N * nkb * nqb);
+  const int64_t n_units = B * Nkv * nkb * nsub_kv;
+  const int64_t max_pieces = n_units * (N / Nkv) * nqb;  // a piece holds at least one Q block
+  const int64_t slots = max_pieces < bsa::kMaxSlots ? max_pieces : bsa::kMaxSlots;
+  take(BSA_WS_PLAN, 4ull * bsa::plan_words(n_units, slots));
+  take(BSA_WS_PARTIAL, 4ull * slots * 2 * bsa::kTileRowsMax * D);
   plan->off[BSA_WS_TOTAL] = off;
+  p.n_units = static_cast<int32_t>(n_units);
+  p.n_dq_units = static_cast<int32_t>(B * N * nqb * nsub_q);
+  p.slots_cap = static_cast<int32_t>(slots);
   plan->dims[0] = bx;
   plan->dims[1] = by;
   plan->dims[2] = nqb;
@@ -523,6 +534,8 @@ int bsa_bwd(BSA_ARGS_DECL, void* workspace, uint64_t workspace_size, void* strea
   p.row_list = reinterpret_cast<int32_t*>(ws + plan.off[BSA_WS_ROW_LIST]);
   p.col_cnt = reinterpret_cast<int32_t*>(ws + plan.off[BSA_WS_COL_CNT]);
   p.col_list = reinterpret_cast<int32_t*>(ws + plan.off[BSA_WS_COL_LIST]);
+  p.plan = reinterpret_cast<int32_t*>(ws + plan.off[BSA_WS_PLAN]);
+  p.partial = reinterpret_cast<float*>(ws + plan.off[BSA_WS_PARTIAL]);
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool prof = g_prof.on && g_prof.max_calls > 0;
@@ -539,6 +552,7 @@ int bsa_bwd(BSA_ARGS_DECL, void* workspace, uint64_t workspace_size, void* strea
     herr = bsa::launch_stage_seq(chunk, p.seq, consts, stream);
   }
   if (herr == 0) herr = bsa::launch_prologue(p, stream);
+  if (herr == 0) herr = bsa::launch_plan(p, stream);
   if (herr) return fail(BSA_ERR_RUNTIME, "prologue launch failed: %s", hipGetErrorString(static_cast<hipError_t>(herr)));
   if (prof && (rc = record_stage(s))) return rc;
   herr = bsa::launch_dkdv(p, stream);

@@ -56,7 +56,49 @@ struct Params {
   int32_t* row_list;
   int32_t* col_cnt;
   int32_t* col_list;
+
+  // load balance of the dK/dV kernel (see plan_kernel)
+  int32_t n_units;     // dK/dV work units: B * Nkv * nKB * ceil(by / 128)
+  int32_t n_dq_units;  // dQ workgroups: B * N * nQB * ceil(bx / 128)
+  int32_t slots_cap;   // partial-result slots for units split over several workgroups
+  int32_t* plan;       // [0] chunk size, [1] work items, [2] dQ order, [3] unused, unit_k[n_units],
+                       // unit_base[n_units], slot_unit[slots_cap], slot_chunk[slots_cap],
+                       // order_unit[n_units + slots_cap], order_piece[n_units + slots_cap]
+  float* partial;      // [slots_cap][2][kTileRowsMax][D] fp32 (dK unscaled, dV)
 };
+
+// Work-split parameters: a unit with more than `chunk` selecting Q blocks is
+// split into ceil(T / chunk) pieces, chunk = max(kMinChunk, ceil(total /
+// kBalanceGroups)); at most kMaxSlots pieces exist in total, which that
+// choice of chunk guarantees (pieces <= total / chunk + split units <= 2 x kBalanceGroups).
+constexpr int kTileRowsMax = 128;
+
+// Words (int32) of the plan region: 4 header words, then per unit its piece
+// count and first slot, per slot its unit and piece, and the launch order as
+// two arrays (unit, piece) of n_units + slots entries.
+inline constexpr int64_t plan_words(int64_t n_units, int64_t slots) { return 4 + 4 * (n_units + slots); }
+constexpr int kBalanceGroups = 256;
+constexpr int kMinChunk = 4;
+constexpr int kMaxSlots = 2 * kBalanceGroups;
+
+// Launch-grid limits.  A dispatch counts work-items in 32 bits, so a grid of
+// 256-thread workgroups holds at most kMaxGridGroups of them.
+constexpr int64_t kMaxGridGroups = ((int64_t(1) << 32) - 1) / 256;
+constexpr int kDeltaRowsPerBlock = 64;  // prologue: softmax_grad rows per workgroup
+
+// Workgroups of the prologue launch: softmax_grad, row lists (4 Q-block rows per
+// workgroup), column lists (4 x 64 KV blocks per workgroup).
+struct PrologueGrid {
+  int64_t delta, rows, cols;
+  int64_t total() const { return delta + rows + cols; }
+};
+inline PrologueGrid prologue_grid(int64_t B, int64_t N, int64_t sq_max, int64_t nqb, int64_t nkb) {
+  PrologueGrid g;
+  g.delta = (B * N * sq_max + kDeltaRowsPerBlock - 1) / kDeltaRowsPerBlock;
+  g.rows = (B * N * nqb + 3) / 4;
+  g.cols = (B * N * ((nkb + 63) / 64) + 3) / 4;
+  return g;
+}
 
 // Constant block staged with the sequence table: kZeroFloats zeros (rows past a
 // slice's end are loaded from here), then +inf and -inf.
@@ -76,6 +118,7 @@ struct SeqChunk {
 // Launch helpers (bsa_kernels.hip).  Return a hipError_t value (0 = success).
 int launch_stage_seq(const SeqChunk& chunk, SeqInfo* dst, float* consts, void* stream);
 int launch_prologue(const Params& p, void* stream);
+int launch_plan(const Params& p, void* stream);
 int launch_dkdv(const Params& p, void* stream);
 int launch_dq(const Params& p, void* stream);
 

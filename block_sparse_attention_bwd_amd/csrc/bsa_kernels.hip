@@ -102,8 +102,6 @@ __global__ void stage_seq_kernel(SeqChunk c, SeqInfo* dst, float* consts) {
 // ---------------------------------------------------------------------------
 // prologue: softmax_grad + lse2, block lists
 // ---------------------------------------------------------------------------
-constexpr int kDeltaRowsPerBlock = 64;
-
 template <class E, int D>
 __device__ void delta_part(const Params& p, int blk) {
   constexpr int LPR = D / 8;        // lanes per row, 8 elements (16 bytes) each
@@ -205,6 +203,192 @@ __global__ __launch_bounds__(256) void prologue_kernel(Params p, int nb_delta, i
     row_list_part(p, bid - nb_delta);
   } else {
     col_list_part(p, bid - nb_delta - nb_rows);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// work split of the dK/dV kernel
+// ---------------------------------------------------------------------------
+// One dK/dV unit (batch, KV head, KV block, 128-row part) walks every Q block
+// that selects it, for every query head of its group: T_u entries.  Units with
+// far more entries than the rest (a KV block every Q block selects) would keep
+// one workgroup busy long after the others finish, so a unit with
+// T_u > chunk is cut into ceil(T_u / chunk) pieces of consecutive entries;
+// each piece writes an fp32 partial dK/dV and the pieces are summed in order
+// afterwards, so the result is the same on every run.  Pieces get slots by an
+// exclusive scan over units in unit order; units that would overflow the slot
+// capacity stay whole.  One workgroup of 1024 threads.
+__device__ __forceinline__ int unit_entries(const Params& p, int u) {
+  const int nsub = (p.by + kTileRows - 1) / kTileRows;
+  int w = u / nsub;
+  const int jb = w % p.nkb;
+  w /= p.nkb;
+  const int h = w % p.Nkv;
+  const int b = w / p.Nkv;
+  int t = 0;
+  for (int n = h * p.G; n < (h + 1) * p.G; ++n) t += p.col_cnt[(static_cast<int64_t>(b) * p.N + n) * p.nkb + jb];
+  return t;
+}
+
+// dQ workgroup order.  Hardware hands workgroup i to XCD i % 8.  In XCD-range
+// order XCD x runs the x-th of eight contiguous ranges of units, so the Q
+// blocks of a head group, which read the same K/V rows, share one L2; the plan
+// kernel picks it only when the eight ranges hold nearly equal work, since one
+// heavy range (a long sequence among short ones) would leave seven XCDs idle.
+// Otherwise workgroup i runs unit i, spreading every range over all XCDs.
+__device__ __forceinline__ int xcd_range_id(int bid, int n) {
+  const int x = bid & 7, per = n >> 3, rem = n & 7;
+  return x * per + min(x, rem) + (bid >> 3);
+}
+// The XCD whose range holds unit u under xcd_range_id.
+__device__ __forceinline__ int xcd_of_unit(int u, int n) {
+  const int per = n >> 3, rem = n & 7;
+  const int big = (per + 1) * rem;  // the first rem ranges hold per + 1 units
+  return u < big ? u / (per + 1) : rem + (u - big) / max(per, 1);
+}
+constexpr int kDqOrderPlain = 0, kDqOrderXcdRange = 1;
+
+// The plan region, in order: [0] chunk, [1] number of work items, [2] dQ order, [3]
+// unused, then per unit its piece count and first slot, per slot its unit
+// (-1 = unused) and piece, and the work items (unit, piece) in launch order.
+struct PlanView {
+  int32_t* unit_k;
+  int32_t* unit_base;
+  int32_t* slot_unit;
+  int32_t* slot_chunk;
+  int32_t* order_unit;
+  int32_t* order_piece;
+  __device__ explicit PlanView(const Params& p) {
+    unit_k = p.plan + 4;
+    unit_base = unit_k + p.n_units;
+    slot_unit = unit_base + p.n_units;
+    slot_chunk = slot_unit + p.slots_cap;
+    order_unit = slot_chunk + p.slots_cap;
+    order_piece = order_unit + p.n_units + p.slots_cap;
+  }
+};
+
+// Launch order of the work items: longest first, so that the last workgroups
+// to start are short ones.  Costs (Q-block entries of the piece) are binned
+// into kOrderBins classes, class kOrderBins-1 holding pieces of about `chunk`
+// entries and class 0 the units with nothing to do (they only write zeros).
+// The order inside a class depends on scheduling; the results do not, since
+// every piece sums its entries in list order and pieces are reduced in order.
+constexpr int kOrderBins = 64;
+__device__ __forceinline__ int order_bin(int cost, int chunk) {
+  if (cost <= 0) return 0;
+  return min(kOrderBins - 1, 1 + static_cast<int>((static_cast<long long>(cost - 1) * (kOrderBins - 1)) / chunk));
+}
+
+__global__ __launch_bounds__(1024) void plan_kernel(Params p) {
+  __shared__ long long s_red[1024];
+  __shared__ int s_scan[1024];
+  __shared__ int s_hist[kOrderBins], s_cursor[kOrderBins];
+  __shared__ unsigned long long s_xcd[8];
+  const int tid = threadIdx.x;
+  const PlanView pv(p);
+  const int per = (p.n_units + 1023) / 1024;
+  const int u0 = min(p.n_units, tid * per), u1 = min(p.n_units, u0 + per);
+  if (tid < kOrderBins) s_hist[tid] = 0;
+  if (tid < 8) s_xcd[tid] = 0;
+
+  long long tot = 0;
+  for (int u = u0; u < u1; ++u) tot += unit_entries(p, u);
+  s_red[tid] = tot;
+  __syncthreads();
+  for (int st = 512; st > 0; st >>= 1) {
+    if (tid < st) s_red[tid] += s_red[tid + st];
+    __syncthreads();
+  }
+  const long long total = s_red[0];
+  const int chunk = static_cast<int>(max(static_cast<long long>(kMinChunk),
+                                         (total + kBalanceGroups - 1) / kBalanceGroups));
+
+  int mine = 0;
+  for (int u = u0; u < u1; ++u) {
+    const int t = unit_entries(p, u);
+    if (t > chunk) mine += (t + chunk - 1) / chunk;
+  }
+  s_scan[tid] = mine;
+  for (int i = tid; i < p.slots_cap; i += 1024) pv.slot_unit[i] = -1;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {  // inclusive scan
+    const int v = tid >= off ? s_scan[tid - off] : 0;
+    __syncthreads();
+    s_scan[tid] += v;
+    __syncthreads();
+  }
+  int run = s_scan[tid] - mine;  // exclusive prefix
+  int extra = 0;                 // pieces >= 1 this thread creates
+  for (int u = u0; u < u1; ++u) {
+    const int t = unit_entries(p, u);
+    const int k = t > chunk ? (t + chunk - 1) / chunk : 1;
+    if (k > 1 && run + k <= p.slots_cap) {
+      pv.unit_k[u] = k;
+      pv.unit_base[u] = run;
+      for (int c = 0; c < k; ++c) {
+        pv.slot_unit[run + c] = u;
+        pv.slot_chunk[run + c] = c;
+        atomicAdd(&s_hist[order_bin(min(chunk, t - c * chunk), chunk)], 1);
+      }
+      run += k;
+      extra += k - 1;
+    } else {
+      pv.unit_k[u] = 1;
+      pv.unit_base[u] = 0;
+      atomicAdd(&s_hist[order_bin(t, chunk)], 1);
+    }
+  }
+  s_scan[tid] = extra;
+  __syncthreads();
+  for (int st = 512; st > 0; st >>= 1) {
+    if (tid < st) s_scan[tid] += s_scan[tid + st];
+    __syncthreads();
+  }
+  // dQ order: work of each XCD range, a unit costing its selected KV blocks + 1
+  {
+    const int nd = p.n_dq_units, nsub_q = (p.bx + kTileRows - 1) / kTileRows;
+    const int dper = (nd + 1023) / 1024;
+    const int d0 = min(nd, tid * dper), d1 = min(nd, d0 + dper);
+    unsigned long long acc = 0;
+    int cur = d0 < d1 ? xcd_of_unit(d0, nd) : 0;
+    for (int u = d0; u < d1; ++u) {
+      const int x = xcd_of_unit(u, nd);
+      if (x != cur) {
+        atomicAdd(&s_xcd[cur], acc);
+        acc = 0;
+        cur = x;
+      }
+      acc += 1ull + static_cast<unsigned>(p.row_cnt[u / nsub_q]);
+    }
+    if (acc) atomicAdd(&s_xcd[cur], acc);
+  }
+  __syncthreads();
+  if (tid == 0) {
+    unsigned long long tot = 0, mx = 0;
+    for (int x = 0; x < 8; ++x) {
+      tot += s_xcd[x];
+      mx = max(mx, s_xcd[x]);
+    }
+    // contiguous ranges only if the heaviest holds at most 1/32 more than the mean
+    p.plan[2] = 8 * mx * 32 <= tot * 33 ? kDqOrderXcdRange : kDqOrderPlain;
+    int base = 0;  // classes in descending order
+    for (int c = kOrderBins - 1; c >= 0; --c) {
+      s_cursor[c] = base;
+      base += s_hist[c];
+    }
+    p.plan[0] = chunk;
+    p.plan[1] = p.n_units + s_scan[0];
+  }
+  __syncthreads();
+  for (int u = u0; u < u1; ++u) {
+    const int t = unit_entries(p, u);
+    const int k = pv.unit_k[u];
+    for (int c = 0; c < k; ++c) {
+      const int at = atomicAdd(&s_cursor[order_bin(k > 1 ? min(chunk, t - c * chunk) : t, chunk)], 1);
+      pv.order_unit[at] = u;
+      pv.order_piece[at] = c;
+    }
   }
 }
 
@@ -326,15 +510,6 @@ struct StagePrefetch {
   }
 };
 
-// Logical workgroup id: hardware hands consecutive workgroup ids to the eight
-// XCDs in turn; this bijection gives each XCD a contiguous range of logical
-// ids, so workgroups that share a head's tiles share one L2.
-__device__ __forceinline__ int xcd_local_id() {
-  const int nb = gridDim.x, bid = blockIdx.x;
-  const int xcd = bid & 7, slot = bid >> 3;
-  const int per = nb >> 3, rem = nb & 7;
-  return xcd * per + min(xcd, rem) + slot;
-}
 
 // ---------------------------------------------------------------------------
 // dK / dV: KV-block-outer
@@ -400,18 +575,20 @@ struct QTile {
   int n, e, q0, qend;
 };
 
+// Move (t.n, t.e) to entry t.e of the group's merged list (head t.n's entries,
+// then the next head's, ...), i.e. past the heads whose lists it overruns.
 __device__ __forceinline__ bool dkdv_seek(const Params& p, int64_t bn0, int jb, int n_end, int len_q, QTile& t) {
-  // advance (t.n, t.e) to the next existing list entry; set q0/qend
   while (t.n < n_end) {
     const int64_t col = (bn0 + t.n) * p.nkb + jb;
-    if (t.e < p.col_cnt[col]) {
+    const int cnt = p.col_cnt[col];
+    if (t.e < cnt) {
       const int ib = p.col_list[col * p.nqb + t.e];
       t.q0 = ib * p.bx;
       t.qend = min(t.q0 + p.bx, len_q);
       return true;
     }
+    t.e -= cnt;
     ++t.n;
-    t.e = 0;
   }
   return false;
 }
@@ -430,7 +607,18 @@ __global__ __launch_bounds__(256) void dkdv_kernel(Params p) {
   const int lane = tid & 63, w = tid >> 6, l32 = lane & 31, g = lane >> 5;
   const int H = nthr / 2;  // staged Q rows: 32 per wave
 
-  int wid = xcd_local_id();
+  // Workgroup i takes work item i of the plan's launch order: piece `piece`
+  // of unit u (the whole unit unless it is split).
+  const PlanView pv(p);
+  if (static_cast<int>(blockIdx.x) >= p.plan[1]) return;
+  const int u = pv.order_unit[blockIdx.x];
+  const int piece = pv.order_piece[blockIdx.x];
+  const int32_t* unit_k = pv.unit_k;
+  const int32_t* unit_base = pv.unit_base;
+  const int pieces = unit_k[u];
+  const int chunk = p.plan[0];
+
+  int wid = u;
   const int nsub = (p.by + kTileRows - 1) / kTileRows;
   const int sub = wid % nsub;
   wid /= nsub;
@@ -488,7 +676,9 @@ __global__ __launch_bounds__(256) void dkdv_kernel(Params p) {
     pd = tid < rows ? p.delta[li] : 0.f;
   };
 
-  QTile cur{h * p.G, 0, 0, 0};
+  // entries [piece * chunk, piece * chunk + chunk) of the merged list, or all of them
+  int left = pieces > 1 ? chunk : 0x7fffffff;
+  QTile cur{h * p.G, pieces > 1 ? piece * chunk : 0, 0, 0};
   bool have = dkdv_seek(p, bn0, jb, n_end, si.len_q, cur);
   if (have) prefetch(cur);
   while (have) {
@@ -503,7 +693,7 @@ __global__ __launch_bounds__(256) void dkdv_kernel(Params p) {
     QTile nxt = cur;
     nxt.q0 += H;
     bool more = nxt.q0 < nxt.qend;
-    if (!more) {
+    if (!more && --left > 0) {
       ++nxt.e;
       more = dkdv_seek(p, bn0, jb, n_end, si.len_q, nxt);
     }
@@ -550,6 +740,21 @@ __global__ __launch_bounds__(256) void dkdv_kernel(Params p) {
     have = more;
   }
 
+  if (pieces > 1) {  // fp32 partial of this piece; the reduction applies the scale
+    float* dst = p.partial + static_cast<int64_t>(unit_base[u] + piece) * 2 * kTileRowsMax * D;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int rl = 32 * w + 8 * (i >> 2) + 4 * g + (i & 3);
+        if (kv0 + rl < w_end) {
+          dst[rl * D + 32 * nt + l32] = adk[nt][i];
+          dst[(kTileRowsMax + rl) * D + 32 * nt + l32] = adv[nt][i];
+        }
+      }
+    }
+    return;
+  }
   unsigned short* dkp = static_cast<unsigned short*>(p.dk) + b * p.dk_sb + si.off_kv * p.dk_sr + h * p.dk_sh;
   unsigned short* dvp = static_cast<unsigned short*>(p.dv) + b * p.dv_sb + si.off_kv * p.dv_sr + h * p.dv_sh;
 #pragma unroll
@@ -562,6 +767,52 @@ __global__ __launch_bounds__(256) void dkdv_kernel(Params p) {
         dvp[r * p.dv_sr + 32 * nt + l32] = E::from_f32(adv[nt][i]);
       }
     }
+  }
+}
+
+// Sum the pieces of split dK/dV unit slot_unit[s] (for the slot holding its
+// piece 0) in piece order, scale dK, round and store both.  Runs as extra
+// workgroups of the dQ launch, which starts after the dK/dV kernel finished.
+template <class E, int D>
+__device__ void reduce_pieces(const Params& p, int s) {
+  const PlanView pv(p);
+  const int u = pv.slot_unit[s];
+  if (u < 0 || pv.slot_chunk[s] != 0) return;
+  const int pieces = pv.unit_k[u];
+  const float* src = p.partial + static_cast<int64_t>(pv.unit_base[u]) * 2 * kTileRowsMax * D;
+  int wid = u;
+  const int nsub = (p.by + kTileRows - 1) / kTileRows;
+  const int sub = wid % nsub;
+  wid /= nsub;
+  const int jb = wid % p.nkb;
+  wid /= p.nkb;
+  const int h = wid % p.Nkv;
+  const int b = wid / p.Nkv;
+  const SeqInfo si = p.seq[b];
+  const int kv0 = jb * p.by + sub * kTileRows;
+  const int w_end = min(min(jb * p.by + p.by, kv0 + kTileRows), si.wlim_kv);
+  if (kv0 >= w_end) return;
+  unsigned short* dkp = static_cast<unsigned short*>(p.dk) + b * p.dk_sb + si.off_kv * p.dk_sr + h * p.dk_sh;
+  unsigned short* dvp = static_cast<unsigned short*>(p.dv) + b * p.dv_sb + si.off_kv * p.dv_sr + h * p.dv_sh;
+  const int n4 = 2 * (w_end - kv0) * D / 4;  // float4 groups over [dK rows, dV rows]
+  for (int q = threadIdx.x; q < n4; q += blockDim.x) {
+    const int t = q / ((w_end - kv0) * D / 4);  // 0: dK, 1: dV
+    const int rem = q % ((w_end - kv0) * D / 4);
+    const int rl = rem / (D / 4), d = 4 * (rem % (D / 4));
+    float4 acc = *reinterpret_cast<const float4*>(src + (t * kTileRowsMax + rl) * D + d);
+    for (int c = 1; c < pieces; ++c) {
+      const float4 x = *reinterpret_cast<const float4*>(src + (static_cast<int64_t>(c) * 2 * kTileRowsMax + t * kTileRowsMax + rl) * D + d);
+      acc.x += x.x;
+      acc.y += x.y;
+      acc.z += x.z;
+      acc.w += x.w;
+    }
+    const float sc = t == 0 ? p.scale : 1.f;
+    unsigned short* dst = (t == 0 ? dkp + (kv0 + rl) * p.dk_sr : dvp + (kv0 + rl) * p.dv_sr) + d;
+    dst[0] = E::from_f32(acc.x * sc);
+    dst[1] = E::from_f32(acc.y * sc);
+    dst[2] = E::from_f32(acc.z * sc);
+    dst[3] = E::from_f32(acc.w * sc);
   }
 }
 
@@ -600,7 +851,11 @@ __global__ __launch_bounds__(64 * W) void dq_kernel(Params p) {
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6, l32 = lane & 31, g = lane >> 5;
 
-  int wid = xcd_local_id();
+  if (static_cast<int>(blockIdx.x) >= p.n_dq_units) {  // the workgroups after the dQ ones reduce split dK/dV units
+    reduce_pieces<E, D>(p, blockIdx.x - p.n_dq_units);
+    return;
+  }
+  int wid = p.plan[2] == kDqOrderXcdRange ? xcd_range_id(blockIdx.x, p.n_dq_units) : static_cast<int>(blockIdx.x);
   const int nsub = (p.bx + kTileRows - 1) / kTileRows;
   const int sub = wid % nsub;
   wid /= nsub;
@@ -759,12 +1014,9 @@ int launch_stage_seq(const SeqChunk& chunk, SeqInfo* dst, float* consts, void* s
 }
 
 int launch_prologue(const Params& p, void* stream) {
-  const int64_t rows = static_cast<int64_t>(p.B) * p.N * p.sq_max;
-  const int nb_delta = static_cast<int>((rows + kDeltaRowsPerBlock - 1) / kDeltaRowsPerBlock);
-  const int nb_rows = static_cast<int>((static_cast<int64_t>(p.B) * p.N * p.nqb + 3) / 4);
-  const int ncw = (p.nkb + 63) / 64;
-  const int nb_cols = static_cast<int>((static_cast<int64_t>(p.B) * p.N * ncw + 3) / 4);
-  const dim3 grid(nb_delta + nb_rows + nb_cols), block(256);
+  const PrologueGrid pg = prologue_grid(p.B, p.N, p.sq_max, p.nqb, p.nkb);
+  const int nb_delta = static_cast<int>(pg.delta), nb_rows = static_cast<int>(pg.rows);
+  const dim3 grid(static_cast<unsigned>(pg.total())), block(256);
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool bf = p.dtype == 2;
   if (p.D == 128) {
@@ -796,16 +1048,19 @@ int launch_prologue(const Params& p, void* stream) {
     }                                                                           \
   } while (0)
 
+int launch_plan(const Params& p, void* stream) {
+  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(1024), 0, static_cast<hipStream_t>(stream), p);
+  return static_cast<int>(hipGetLastError());
+}
+
 int launch_dkdv(const Params& p, void* stream) {
-  const int nsub = (p.by + kTileRows - 1) / kTileRows;
-  const dim3 grid(static_cast<unsigned>(static_cast<int64_t>(p.B) * p.Nkv * p.nkb * nsub));
+  const dim3 grid(static_cast<unsigned>(p.n_units + p.slots_cap));
   BSA_DISPATCH(dkdv_kernel, waves_for(p.by), grid, static_cast<hipStream_t>(stream), p);
   return static_cast<int>(hipGetLastError());
 }
 
 int launch_dq(const Params& p, void* stream) {
-  const int nsub = (p.bx + kTileRows - 1) / kTileRows;
-  const dim3 grid(static_cast<unsigned>(static_cast<int64_t>(p.B) * p.N * p.nqb * nsub));
+  const dim3 grid(static_cast<unsigned>(p.n_dq_units + p.slots_cap));
   BSA_DISPATCH(dq_kernel, waves_for(p.bx), grid, static_cast<hipStream_t>(stream), p);
   return static_cast<int>(hipGetLastError());
 }

@@ -143,8 +143,10 @@ enum bsa_ws_region {
   BSA_WS_ROW_LIST = 4, /* int32 [B, N, nQB, nKB]: ascending KV-block lists, first ROW_CNT entries valid */
   BSA_WS_COL_CNT = 5,  /* int32 [B, N, nKB]: number of selected in-range Q blocks per KV block */
   BSA_WS_COL_LIST = 6, /* int32 [B, N, nKB, nQB]: ascending Q-block lists, first COL_CNT entries valid */
-  BSA_WS_TOTAL = 7,    /* total bytes (== the phase-1 size) */
-  BSA_WS_NUM = 8
+  BSA_WS_PLAN = 7,     /* int32: dK/dV work split (chunk size, per-unit piece counts and slots, slot table) */
+  BSA_WS_PARTIAL = 8,  /* fp32 per-piece dK/dV partial sums of split units, reduced in piece order */
+  BSA_WS_TOTAL = 9,    /* total bytes (== the phase-1 size) */
+  BSA_WS_NUM = 10
 };
 
 /*

@@ -105,6 +105,22 @@ def test_layout_regions_are_ordered_and_aligned():
     assert dims == (64, 128, 4, 1)
 
 
+def test_layout_region_sizes():
+    """Every region holds what the header says it holds (BNSD, B=2, N=4, Nkv=2,
+    Sq=300, Skv=270, 128 x 128 blocks: nQB = nKB = 3, 12 dK/dV units of one
+    128-row part, 72 possible pieces)."""
+    offs, dims = bsa.bsa_bwd_workspace_layout(**_bnsd())
+    B, N, Nkv, Sq, D, nqb, nkb = 2, 4, 2, 300, 128, 3, 3
+    n_units, slots = B * Nkv * nkb, min(B * Nkv * nkb * (N // Nkv) * nqb, 512)
+    size = {k: offs[b] - offs[a] for k, a, b in zip(bsa.WS_REGIONS, bsa.WS_REGIONS, bsa.WS_REGIONS[1:])}
+    assert size["seq"] >= B * 32 + 128 * 4
+    assert size["delta"] >= B * N * Sq * 4 and size["lse2"] >= B * N * Sq * 4
+    assert size["row_cnt"] >= B * N * nqb * 4 and size["row_list"] >= B * N * nqb * nkb * 4
+    assert size["col_cnt"] >= B * N * nkb * 4 and size["col_list"] >= B * N * nkb * nqb * 4
+    assert size["plan"] >= 4 * (4 + 4 * (n_units + slots))
+    assert size["partial"] >= slots * 2 * 128 * D * 4
+
+
 NULLPTR = bsa.BSA_ERR_PARAM_NULLPTR
 INVALID = bsa.BSA_ERR_PARAM_INVALID
 
@@ -218,3 +234,49 @@ def test_binding_refuses_cpu_tensors_for_phase2():
 
 def test_stage_names():
     assert [bsa.bsa_stage_name(i) for i in range(4)] == ["prologue", "dkdv", "dq", None]
+
+
+def _fake(t):
+    """Descriptor of a meta tensor with a non-null address: phase 1 never reads data."""
+    d = bsa.bsa_tensor()
+    d.data = 0x1000
+    d.dtype = bsa._binding._dtype_code(t)
+    d.ndim = t.dim()
+    for i in range(t.dim()):
+        d.shape[i] = t.shape[i]
+        d.stride[i] = t.stride(i)
+    return d
+
+
+def _huge(B, N, Sq, Skv, bx, by, D=64):
+    meta = dict(device="meta")
+    q = torch.empty(B, N, Sq, D, dtype=torch.bfloat16, **meta)
+    k = torch.empty(B, 1, Skv, D, dtype=torch.bfloat16, **meta)
+    lse = torch.empty(B, N, Sq, dtype=torch.float32, **meta)
+    mask = torch.empty(B, N, -(-Sq // bx), -(-Skv // by), dtype=torch.bool, **meta)
+    return dict(dout=_fake(q), query=_fake(q), key=_fake(k), value=_fake(k), attention_out=_fake(q),
+                softmax_lse=_fake(lse), block_sparse_mask=_fake(mask), atten_mask=None, block_shape=[bx, by],
+                actual_seq_lengths=None, actual_seq_lengths_kv=None, q_input_layout="BNSD",
+                kv_input_layout="BNSD", num_key_value_heads=1, mask_type=0, scale_value=D ** -0.5,
+                pre_tokens=bsa.NO_WINDOW, next_tokens=bsa.NO_WINDOW, dq=_fake(q), dk=_fake(k), dv=_fake(k))
+
+
+# Prologue workgroups at Sq = 131072, Skv = 128: N*Sq/64 (softmax_grad) + N*Sq/512
+# (row lists) + ceil(N/4) (column lists) = 16,774,940 for N = 7280 and
+# 16,777,245 for N = 7281, against a limit of (2^32 - 1) / 256 = 16,777,215.
+@pytest.mark.parametrize("what,shape", [
+    ("prologue", (1, 7281, 131072, 128, 128, 128)),
+    # 2^24 dQ workgroups of 128 query rows
+    ("dq", (1, 16384, 131072, 128, 128, 128)),
+    # 2^24 dK/dV units of 128 key rows (a 1 x 2^24 block grid per head)
+    ("dkdv", (1, 1, 128, (1 << 31) - 1, 128, 128)),
+])
+def test_launch_grid_limit(what, shape):
+    args = _huge(*shape)
+    assert _code(args) == INVALID, what
+    assert "launch grid too large" in bsa.bsa_last_error()
+
+
+def test_launch_grid_just_below_limit():
+    args = _huge(1, 7280, 131072, 128, 128, 128)
+    assert _code(args) == bsa.BSA_OK, bsa.bsa_last_error()

@@ -65,6 +65,17 @@ def _case(name):
         "bnsd_fp16_d128_sparse_rows": lambda: mk(layout="BNSD", dtype="fp16", B=1, N=2, Nkv=1, D=128,
                                                  Sq=512, Skv=512, bx=64, by=64, mask_rule="bernoulli",
                                                  p=0.15, seed=110),
+        # local window + 2 sink blocks: sink columns are selected by every Q block of every head,
+        # so the dK/dV work of most units is split into pieces and reduced in piece order
+        "bnsd_bf16_d128_local_sink_split": lambda: mk(layout="BNSD", dtype="bf16", B=1, N=4, Nkv=1,
+                                                      D=128, Sq=1024, Skv=1024, bx=64, by=64,
+                                                      mask_rule="local8_sink2", seed=111),
+        # the same with 256-row KV blocks (two 128-row parts per unit) and ragged lengths
+        "bnsd_fp16_d64_sink_split_parts": lambda: mk(layout="BNSD", dtype="fp16", B=2, N=4, Nkv=2,
+                                                     D=64, Sq=1000, Skv=1000, bx=32, by=256,
+                                                     mask_rule="local8_sink2",
+                                                     lengths_q=[1000, 700], lengths_kv=[1000, 650],
+                                                     seed=112),
     }
     return cases[name]()
 
@@ -72,7 +83,8 @@ def _case(name):
 SMALL = ["config1", "bnsd_bf16_d128_b128x128_ragged", "bnsd_fp16_d64_b64x128_padded",
          "tnd_fp16_d128_b64x128_gqa", "bnsd_bf16_d128_b128x64", "bnsd_bf16_d64_b48x80",
          "bnsd_fp16_d128_b256x256", "bnsd_bf16_d64_b1x1", "bnsd_bf16_d128_nullmask",
-         "tnd_bf16_d64_empty_seqs", "bnsd_fp16_d128_sparse_rows"]
+         "tnd_bf16_d64_empty_seqs", "bnsd_fp16_d128_sparse_rows", "bnsd_bf16_d128_local_sink_split",
+         "bnsd_fp16_d64_sink_split_parts"]
 
 _cache = {}
 
@@ -156,7 +168,8 @@ def test_delta_and_lse2(name):
         np.testing.assert_allclose(lse2[b, :, :L][fin], lb[fin].astype(np.float64) * math.log2(math.e), rtol=1e-6)
 
 
-@pytest.mark.parametrize("name", ["bnsd_bf16_d128_b128x128_ragged", "tnd_fp16_d128_b64x128_gqa"])
+@pytest.mark.parametrize("name", ["bnsd_bf16_d128_b128x128_ragged", "tnd_fp16_d128_b64x128_gqa",
+                                  "bnsd_bf16_d128_local_sink_split"])
 def test_bitwise_deterministic(name):
     c, o, lse, _ = _prepared(name)
     dev = upload(c, o, lse)
@@ -167,6 +180,63 @@ def test_bitwise_deterministic(name):
     torch.cuda.synchronize()
     for x, y in zip(a, (r.dq, r.dk, r.dv)):
         assert torch.equal(x.view(torch.int16), y.view(torch.int16))
+
+
+def test_split_units_are_planned():
+    """The sink-column case really takes the split path: read the plan back.
+
+    Checks the chunk rule, the piece count of every unit, and that the launch
+    order lists every (unit, piece) once, longest first by cost class."""
+    import block_sparse_attention_bwd_amd as bsa
+    c, o, lse, _ = _prepared("bnsd_bf16_d128_local_sink_split")
+    dev = upload(c, o, lse)
+    _, r = run_bsa(c, dev)
+    torch.cuda.synchronize()
+    offs, (bx, by, nqb, nkb) = bsa.bsa_bwd_workspace_layout(*r.args, **r.kw)
+    n_units = c.B * c.Nkv * nkb
+    G = c.N // c.Nkv
+    slots = min(n_units * G * nqb, 512)
+    assert offs["partial"] - offs["plan"] >= 4 * (4 + 4 * (n_units + slots))
+    plan = _read_ws(r, offs, "plan", 4 + 4 * (n_units + slots))
+    chunk, n_items = int(plan[0]), int(plan[1])
+    pieces = [int(k) for k in plan[4:4 + n_units]]
+    _, cols = oracle.block_lists(c.mask, c.B, c.N, nqb, nkb, bx, by, c.len_q, c.len_kv)
+    totals = [sum(len(cols[0][n][j]) for n in range(c.N)) for j in range(nkb)]
+    assert chunk == max(4, -(-sum(totals) // 256))
+    assert pieces == [(-(-t // chunk) if t > chunk else 1) for t in totals]
+    assert max(pieces) > 1
+    assert n_items == sum(pieces)
+    ou = plan[4 + 2 * (n_units + slots):][:n_items]
+    op = plan[4 + 3 * (n_units + slots):][:n_items]
+    assert sorted(zip(ou.tolist(), op.tolist())) == [(u, k) for u in range(n_units) for k in range(pieces[u])]
+
+    def cls(u, k):
+        cost = min(chunk, totals[u] - k * chunk) if pieces[u] > 1 else totals[u]
+        return 0 if cost <= 0 else min(63, 1 + (cost - 1) * 63 // chunk)
+    classes = [cls(u, k) for u, k in zip(ou.tolist(), op.tolist())]
+    assert classes == sorted(classes, reverse=True)
+
+
+@pytest.mark.parametrize("name", ["config1", "tnd_fp16_d128_b64x128_gqa", "bnsd_bf16_d128_local_sink_split",
+                                  "bnsd_fp16_d128_b256x256"])
+def test_dq_order_choice(name):
+    """plan[2]: XCD-range order for dQ iff the eight contiguous ranges of dQ
+    units carry work within 1/32 of each other (unit cost = selected KV blocks + 1)."""
+    import block_sparse_attention_bwd_amd as bsa
+    c, o, lse, _ = _prepared(name)
+    dev = upload(c, o, lse)
+    _, r = run_bsa(c, dev)
+    torch.cuda.synchronize()
+    offs, (bx, by, nqb, nkb) = bsa.bsa_bwd_workspace_layout(*r.args, **r.kw)
+    rows, _ = oracle.block_lists(c.mask, c.B, c.N, nqb, nkb, bx, by, c.len_q, c.len_kv)
+    nsub = -(-bx // 128)
+    cost = [1 + len(rows[b][n][i]) for b in range(c.B) for n in range(c.N) for i in range(nqb) for _ in range(nsub)]
+    nd = len(cost)
+    per, rem = nd // 8, nd % 8
+    bounds = [x * per + min(x, rem) for x in range(9)]
+    work = [sum(cost[bounds[x]:bounds[x + 1]]) for x in range(8)]
+    want = 1 if 8 * max(work) * 32 <= sum(work) * 33 else 0
+    assert int(_read_ws(r, offs, "plan", 4)[2]) == want
 
 
 def test_noncontiguous_outputs_match():
