@@ -8,7 +8,8 @@ resident in HBM before timing starts.  Prints one JSON line:
   value    backward TFLOP/s counted over active blocks: 10*bx*by*D FLOPs per
            selected in-range (batch, query head, Q block, KV block)
   roofline the dominant kernel (dK/dV) against the dense bf16 MFMA peak,
-           timed with HIP events recorded between the library's stages
+           timed with HIP events recorded between the library's stages on
+           the launch stream, over a second run of the same K steps
   cpu_baseline  the fp64 CPU oracle's backward on a bounded sample of the
            same workload, on this host's cores
 
@@ -16,7 +17,12 @@ Inputs are synthetic: Q, K, V, dO ~ N(0, 1) rounded to the dtype; O and LSE
 come from a plain torch fp32 masked-attention forward on the GPU
 (``gpu_forward``), outside the timed region.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2]
+With ``--op fwd`` a step is one ``bsa_fwd`` call (sequence table, row lists,
+forward kernel) producing O and LSE, counted at 4*bx*by*D FLOPs per active
+block (the S and PV products), with the forward kernel as the roofline and the
+oracle's forward as the CPU baseline.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2] [--op bwd|fwd]
 """
 from __future__ import annotations
 
@@ -146,11 +152,37 @@ class Runner:
         return self.dq, self.dk, self.dv
 
 
+class FwdRunner:
+    """Pre-allocated O, LSE and workspace for repeated bsa_fwd calls."""
+
+    def __init__(self, case, dev):
+        torch = _torch()
+        import block_sparse_attention_bwd_amd as bsa
+        self.bsa = bsa
+        self.o = torch.empty_like(dev["q"])
+        self.lse = torch.empty(dev["q"].shape[:-1], dtype=torch.float32, device=dev["q"].device)
+        lengths = case.explicit_lengths or case.layout == "TND"
+        self.kw = dict(
+            block_sparse_mask=dev["mask"], atten_mask=None, block_shape=[case.bx, case.by],
+            actual_seq_lengths=list(map(int, case.len_q)) if lengths else None,
+            actual_seq_lengths_kv=list(map(int, case.len_kv)) if lengths else None,
+            q_input_layout=case.layout, kv_input_layout=case.layout, num_key_value_heads=case.Nkv,
+            mask_type=0, scale_value=case.scale, pre_tokens=bsa.NO_WINDOW, next_tokens=bsa.NO_WINDOW,
+            attention_out=self.o, softmax_lse=self.lse)
+        self.args = (dev["q"], dev["k"], dev["v"])
+        self.ws_size = bsa.bsa_fwd_workspace_size(*self.args, **self.kw)
+        self.ws = torch.empty(max(1, self.ws_size), dtype=torch.uint8, device=dev["q"].device)
+
+    def __call__(self, stream=None):
+        self.bsa.bsa_fwd(*self.args, **self.kw, workspace=self.ws, workspace_size=self.ws_size, stream=stream)
+        return self.o, self.lse
+
+
 # ---------------------------------------------------------------------------
 # CPU baseline: the oracle on a bounded sample
 # ---------------------------------------------------------------------------
-def cpu_baseline(case, o_host, lse_host, min_seconds=10.0, max_runs=5):
-    """Time the fp64 oracle backward on the whole workload (median of repeated runs)."""
+def cpu_baseline(case, o_host, lse_host, min_seconds=10.0, max_runs=5, op="bwd"):
+    """Time the fp64 oracle backward (or forward) on the whole workload (median of repeated runs)."""
     import oracle
     try:
         from threadpoolctl import threadpool_info
@@ -164,16 +196,19 @@ def cpu_baseline(case, o_host, lse_host, min_seconds=10.0, max_runs=5):
     t_start = time.perf_counter()
     while not times or (time.perf_counter() - t_start < min_seconds and len(times) < max_runs):
         t0 = time.perf_counter()
-        oracle.backward(case.q, case.k, case.v, o_host, case.do, lse_host, case.mask, **kw)
+        if op == "fwd":
+            oracle.forward(case.q, case.k, case.v, case.mask, **kw)
+        else:
+            oracle.backward(case.q, case.k, case.v, o_host, case.do, lse_host, case.mask, **kw)
         times.append(time.perf_counter() - t0)
     dt = float(np.median(times))
-    flops = 10.0 * case.bx * case.by * case.D * synth_blocks(case)
+    flops = (4.0 if op == "fwd" else 10.0) * case.bx * case.by * case.D * synth_blocks(case)
     return {
         "value": round(flops / dt / 1e12, 5),
         "unit": "TFLOP/s",
         "cores": int(cores),
         "kind": "oracle",
-        "sample": f"the whole workload (all batches and heads), fp64 NumPy backward only, "
+        "sample": f"the whole workload (all batches and heads), fp64 NumPy {'forward' if op == 'fwd' else 'backward'} only, "
                   f"median of {len(times)} runs: {dt:.2f} s",
     }
 
@@ -221,6 +256,8 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=2)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--op", choices=["bwd", "fwd"], default="bwd",
+                    help="bwd: the backward (default); fwd: the forward that produces O and LSE")
     args = ap.parse_args(argv)
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on exactly one GPU; --gpus must be 1",
@@ -234,20 +271,25 @@ def main(argv=None):
     torch.backends.cuda.matmul.allow_tf32 = False
     case = synth.config(args.config)
     blocks = synth.active_blocks(case)
-    flops = 10.0 * case.bx * case.by * case.D * blocks
+    fwd = args.op == "fwd"
+    flops = (4.0 if fwd else 10.0) * case.bx * case.by * case.D * blocks
     print(f"# workload {case.name}: {blocks} active blocks, {flops / 1e9:.1f} GFLOP counted", file=sys.stderr, flush=True)
 
     dev = to_device(case)
-    o, lse = gpu_forward(case, dev)
-    torch.cuda.synchronize()
-    run = Runner(case, dev, o, lse)
+    if fwd:
+        o = lse = None
+        run = FwdRunner(case, dev)
+    else:
+        o, lse = gpu_forward(case, dev)
+        torch.cuda.synchronize()
+        run = Runner(case, dev, o, lse)
     stream = torch.cuda.current_stream()
 
     for _ in range(args.warmup):
         run()
     torch.cuda.synchronize()
 
-    bsa.bsa_profile_start(args.steps)
+    # timed region: K whole calls with nothing else on the stream
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -257,15 +299,24 @@ def main(argv=None):
     end.record(stream)
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(end)
+    # per-kernel durations: K more calls with the library's HIP events between
+    # its stages, on the launch stream (kept out of the timed region above,
+    # since each event adds a few microseconds to the stream)
+    bsa.bsa_profile_start(args.steps)
+    for _ in range(args.steps):
+        run()
+    torch.cuda.synchronize()
     stage_ms, ncalls = bsa.bsa_profile_stop()
     ms = total_ms / args.steps
     tflops = flops / (ms * 1e-3) / 1e12
     print(f"# {ms:.4f} ms/step; stages (avg ms): " +
           ", ".join(f"{k}={v / max(1, ncalls):.4f}" for k, v in stage_ms.items()), file=sys.stderr, flush=True)
 
-    # dominant kernel: dK/dV, credited with 4 of the 5 counted block GEMMs (S, dP, dV, dK)
-    dkdv_ms = stage_ms["dkdv"] / max(1, ncalls)
-    dkdv_flops = 8.0 * case.bx * case.by * case.D * blocks
+    # dominant kernel: dK/dV, credited with 4 of the 5 counted block GEMMs (S, dP, dV, dK);
+    # the forward kernel for --op fwd, credited with both of its GEMMs (S, PV)
+    kname, kstage, kflop = ("fwd_kernel", "fwd", 4.0) if fwd else ("dkdv_kernel", "dkdv", 8.0)
+    dkdv_ms = stage_ms[kstage] / max(1, ncalls)
+    dkdv_flops = kflop * case.bx * case.by * case.D * blocks
     achieved = dkdv_flops / (dkdv_ms * 1e-3) / 1e12
     roofline = {
         "bound": "mfma",
@@ -273,20 +324,24 @@ def main(argv=None):
         "peak": MFMA_PEAK_BF16_TFLOPS,
         "unit": "TFLOP/s",
         "frac": round(achieved / MFMA_PEAK_BF16_TFLOPS, 4),
-        "traffic": traffic_from_profile(case.name, "dkdv_kernel"),
-        "kernel": "dkdv_kernel",
+        "traffic": traffic_from_profile(case.name, kname),
+        "kernel": kname,
         "kernel_ms": round(dkdv_ms, 5),
         "stage_ms": {k: round(v / max(1, ncalls), 5) for k, v in stage_ms.items()},
     }
 
     cpu = None
     if not args.no_cpu:
-        o_h = o.float().cpu().numpy()
-        l_h = lse.cpu().numpy()
-        cpu = cpu_baseline(case, o_h, l_h)
+        if fwd:
+            cpu = cpu_baseline(case, None, None, op="fwd")
+        else:
+            o_h = o.float().cpu().numpy()
+            l_h = lse.cpu().numpy()
+            cpu = cpu_baseline(case, o_h, l_h)
 
     out = {
-        "metric": "bwd TFLOP/s over active blocks (bf16) + % of MFMA peak, 1xMI355X",
+        "metric": ("fwd TFLOP/s over active blocks (4*bx*by*D per block) + % of MFMA peak, 1xMI355X" if fwd
+                   else "bwd TFLOP/s over active blocks (bf16) + % of MFMA peak, 1xMI355X"),
         "value": round(tflops, 3),
         "unit": "TFLOP/s",
         "n_gpus": 1,

@@ -1,4 +1,4 @@
-"""Block-sparse attention backward for AMD MI355X (gfx950).
+"""Block-sparse attention backward (and the forward it differentiates) for AMD MI355X (gfx950).
 
 The compute lives in ``libbsa_bwd.so`` (hand-written HIP kernels behind the C
 ABI of ``include/bsa_bwd.h``); this package only marshals torch tensors into
@@ -18,10 +18,13 @@ from ._binding import (  # noqa: F401
     NO_WINDOW,
     WS_REGIONS,
     BsaError,
+    block_sparse_attention,
     block_sparse_attention_grad,
     bsa_bwd,
     bsa_bwd_workspace_layout,
     bsa_bwd_workspace_size,
+    bsa_fwd,
+    bsa_fwd_workspace_size,
     bsa_last_error,
     bsa_profile_start,
     bsa_profile_stop,

@@ -64,6 +64,9 @@ _COMMON = [_PT] * 8 + [
     _PT, _PT, _PT,
 ]
 
+# forward: query, key, value, mask, atten_mask, ... (the common scalars) ..., attention_out, softmax_lse
+_FWD = [_PT] * 5 + _COMMON[8:-3] + [_PT, _PT]
+
 _lib = None
 
 
@@ -82,6 +85,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.bsa_bwd.restype = ctypes.c_int
     lib.bsa_bwd_workspace_layout.argtypes = _COMMON + [ctypes.POINTER(ctypes.c_uint64), _PI64]
     lib.bsa_bwd_workspace_layout.restype = ctypes.c_int
+    lib.bsa_fwd_workspace_size.argtypes = _FWD + [ctypes.POINTER(ctypes.c_uint64)]
+    lib.bsa_fwd_workspace_size.restype = ctypes.c_int
+    lib.bsa_fwd.argtypes = _FWD + [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p]
+    lib.bsa_fwd.restype = ctypes.c_int
     lib.bsa_last_error.argtypes = []
     lib.bsa_last_error.restype = ctypes.c_char_p
     lib.bsa_profile_start.argtypes = [ctypes.c_int32]
@@ -155,6 +162,16 @@ def _marshal(dout, query, key, value, attention_out, softmax_lse, block_sparse_m
     ]
 
 
+def _marshal_fwd(query, key, value, block_sparse_mask, atten_mask, block_shape, actual_seq_lengths,
+                 actual_seq_lengths_kv, q_input_layout, kv_input_layout, num_key_value_heads, mask_type,
+                 scale_value, pre_tokens, next_tokens, attention_out, softmax_lse):
+    a = _marshal(None, query, key, value, attention_out, softmax_lse, block_sparse_mask, atten_mask,
+                 block_shape, actual_seq_lengths, actual_seq_lengths_kv, q_input_layout, kv_input_layout,
+                 num_key_value_heads, mask_type, scale_value, pre_tokens, next_tokens, None, None, None)
+    # reorder to the forward's argument list
+    return [a[1], a[2], a[3], a[6], a[7]] + a[8:21] + [a[4], a[5]]
+
+
 def _check(rc: int):
     if rc != BSA_OK:
         msg = load_library().bsa_last_error()
@@ -225,6 +242,75 @@ def bsa_bwd(dout, query, key, value, attention_out, softmax_lse, block_sparse_ma
     _check(lib.bsa_bwd(*args, ws_ptr, int(workspace_size), ctypes.c_void_p(handle)))
 
 
+def bsa_fwd_workspace_size(query, key, value, block_sparse_mask=None, atten_mask=None, block_shape=None,
+                           actual_seq_lengths=None, actual_seq_lengths_kv=None, q_input_layout="BNSD",
+                           kv_input_layout="BNSD", num_key_value_heads=1, mask_type=0, scale_value=1.0,
+                           pre_tokens=NO_WINDOW, next_tokens=NO_WINDOW, attention_out=None,
+                           softmax_lse=None) -> int:
+    """Forward phase 1: validate and return the workspace size in bytes (host only)."""
+    lib = load_library()
+    args = _marshal_fwd(query, key, value, block_sparse_mask, atten_mask, block_shape, actual_seq_lengths,
+                        actual_seq_lengths_kv, q_input_layout, kv_input_layout, num_key_value_heads,
+                        mask_type, scale_value, pre_tokens, next_tokens, attention_out, softmax_lse)
+    size = ctypes.c_uint64(0)
+    _check(lib.bsa_fwd_workspace_size(*args, ctypes.byref(size)))
+    return size.value
+
+
+def bsa_fwd(query, key, value, block_sparse_mask=None, atten_mask=None, block_shape=None,
+            actual_seq_lengths=None, actual_seq_lengths_kv=None, q_input_layout="BNSD",
+            kv_input_layout="BNSD", num_key_value_heads=1, mask_type=0, scale_value=1.0,
+            pre_tokens=NO_WINDOW, next_tokens=NO_WINDOW, attention_out=None, softmax_lse=None,
+            workspace=None, workspace_size=None, stream=None) -> None:
+    """Forward phase 2: enqueue O and LSE on ``stream`` (default: torch's current stream)."""
+    import torch
+    lib = load_library()
+    for name, t in (("query", query), ("key", key), ("value", value), ("block_sparse_mask", block_sparse_mask),
+                    ("attention_out", attention_out), ("softmax_lse", softmax_lse), ("workspace", workspace)):
+        if t is not None and not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor")
+    args = _marshal_fwd(query, key, value, block_sparse_mask, atten_mask, block_shape, actual_seq_lengths,
+                        actual_seq_lengths_kv, q_input_layout, kv_input_layout, num_key_value_heads,
+                        mask_type, scale_value, pre_tokens, next_tokens, attention_out, softmax_lse)
+    if workspace_size is None:
+        workspace_size = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    ws_ptr = None if workspace is None or workspace.numel() == 0 else workspace.data_ptr()
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    handle = stream if isinstance(stream, int) else stream.cuda_stream
+    _check(lib.bsa_fwd(*args, ws_ptr, int(workspace_size), ctypes.c_void_p(handle)))
+
+
+def block_sparse_attention(query, key, value, block_sparse_mask=None,
+                           block_shape: Optional[Sequence[int]] = None, actual_seq_lengths=None,
+                           actual_seq_lengths_kv=None, layout="BNSD",
+                           num_key_value_heads: Optional[int] = None, scale_value: Optional[float] = None,
+                           stream=None):
+    """Allocate O, LSE and the workspace with torch, then run the forward.
+
+    Returns ``(attention_out, softmax_lse)`` with LSE shaped [B, N, S] (BNSD)
+    or [T, N] (TND); the work is enqueued on ``stream`` and not synchronised.
+    """
+    import torch
+    if num_key_value_heads is None:
+        num_key_value_heads = key.shape[1]
+    if scale_value is None:
+        scale_value = query.shape[-1] ** -0.5
+    out = torch.empty_like(query)
+    lse = torch.empty(query.shape[:-1], dtype=torch.float32, device=query.device)
+    kw = dict(block_sparse_mask=block_sparse_mask, atten_mask=None, block_shape=block_shape,
+              actual_seq_lengths=actual_seq_lengths, actual_seq_lengths_kv=actual_seq_lengths_kv,
+              q_input_layout=layout, kv_input_layout=layout, num_key_value_heads=num_key_value_heads,
+              mask_type=0, scale_value=scale_value, pre_tokens=NO_WINDOW, next_tokens=NO_WINDOW,
+              attention_out=out, softmax_lse=lse)
+    ws = bsa_fwd_workspace_size(query, key, value, **kw)
+    workspace = torch.empty(max(ws, 1), dtype=torch.uint8, device=query.device)
+    bsa_fwd(query, key, value, **kw, workspace=workspace, workspace_size=ws, stream=stream)
+    if stream is not None and not isinstance(stream, int):
+        workspace.record_stream(stream)
+    return out, lse
+
+
 def bsa_last_error() -> str:
     msg = load_library().bsa_last_error()
     return msg.decode() if msg else ""
@@ -234,9 +320,13 @@ def bsa_profile_start(max_calls: int) -> None:
     _check(load_library().bsa_profile_start(int(max_calls)))
 
 
-def bsa_profile_stop(n_stages: int = 3):
-    """Returns ({stage name: summed ms}, number of profiled calls)."""
+def bsa_profile_stop(n_stages: Optional[int] = None):
+    """Returns ({stage name: summed ms}, number of profiled calls) for every stage."""
     lib = load_library()
+    if n_stages is None:
+        n_stages = 0
+        while bsa_stage_name(n_stages) is not None:
+            n_stages += 1
     ms = (ctypes.c_double * n_stages)()
     calls = ctypes.c_int32(0)
     _check(lib.bsa_profile_stop(ms, n_stages, ctypes.byref(calls)))

@@ -1,6 +1,7 @@
 // Host side of the C ABI declared in include/bsa_bwd.h: argument validation
 // (aclnnBlockSparseAttentionGrad page, 参数说明 / 返回值 / 约束说明), the
-// workspace plan, and the launch sequence on the caller's stream.
+// workspace plan, and the launch sequences of the backward and of the forward
+// it differentiates, on the caller's stream.
 #include <hip/hip_runtime_api.h>
 
 #include <algorithm>
@@ -60,6 +61,7 @@ struct Args {
   const bsa_tensor* dq;
   const bsa_tensor* dk;
   const bsa_tensor* dv;
+  bool fwd;  // forward: dout/dq/dk/dv absent; attention_out and softmax_lse are outputs
 };
 
 struct Plan {
@@ -113,11 +115,15 @@ int make_plan(const Args& a, Plan* plan) {
     const bsa_tensor* t;
     const char* name;
   };
-  const Named required[] = {{a.dout, "dout"},         {a.query, "query"},
-                            {a.key, "key"},           {a.value, "value"},
-                            {a.attention_out, "attentionOut"}, {a.softmax_lse, "softmaxLse"},
-                            {a.dq, "dq"},             {a.dk, "dk"},
-                            {a.dv, "dv"}};
+  const Named required_bwd[] = {{a.dout, "dout"},         {a.query, "query"},
+                                {a.key, "key"},           {a.value, "value"},
+                                {a.attention_out, "attentionOut"}, {a.softmax_lse, "softmaxLse"},
+                                {a.dq, "dq"},             {a.dk, "dk"},
+                                {a.dv, "dv"}};
+  const Named required_fwd[] = {{a.query, "query"}, {a.key, "key"}, {a.value, "value"},
+                                {a.attention_out, "attentionOut"}, {a.softmax_lse, "softmaxLse"}};
+  const std::vector<Named> required = a.fwd ? std::vector<Named>(std::begin(required_fwd), std::end(required_fwd))
+                                            : std::vector<Named>(std::begin(required_bwd), std::end(required_bwd));
   for (const Named& n : required) {
     if (n.t == nullptr) return fail(BSA_ERR_PARAM_NULLPTR, "%s is a null pointer", n.name);
     if (n.t->data == nullptr) return fail(BSA_ERR_PARAM_NULLPTR, "%s has a null data pointer", n.name);
@@ -150,7 +156,7 @@ int make_plan(const Args& a, Plan* plan) {
                               {a.attention_out, "attentionOut"}, {a.dq, "dq"},
                               {a.dk, "dk"}, {a.dv, "dv"}};
   for (const Named& n : same_dtype)
-    if (n.t->dtype != dt)
+    if (n.t != nullptr && n.t->dtype != dt)
       return fail(BSA_ERR_PARAM_INVALID, "%s dtype %s differs from query dtype %s", n.name,
                   dtype_name(n.t->dtype), dtype_name(dt));
   if (a.softmax_lse->dtype != BSA_DTYPE_F32)
@@ -172,6 +178,7 @@ int make_plan(const Args& a, Plan* plan) {
                        {a.attention_out, "attentionOut"}, {a.softmax_lse, "softmaxLse"},
                        {a.dq, "dq"}, {a.dk, "dk"}, {a.dv, "dv"}};
   for (const Named& n : all) {
+    if (n.t == nullptr) continue;
     int rc = check_dims(n.t, n.name);
     if (rc) return rc;
   }
@@ -179,15 +186,15 @@ int make_plan(const Args& a, Plan* plan) {
   const Named data_t[] = {{a.dout, "dout"}, {a.query, "query"}, {a.key, "key"}, {a.value, "value"},
                           {a.attention_out, "attentionOut"}, {a.dq, "dq"}, {a.dk, "dk"}, {a.dv, "dv"}};
   for (const Named& n : data_t)
-    if (n.t->ndim != want_nd)
+    if (n.t != nullptr && n.t->ndim != want_nd)
       return fail(BSA_ERR_PARAM_INVALID, "%s has %d dims; layout %s needs %d", n.name, n.t->ndim,
                   a.q_input_layout, want_nd);
   const Named qlike[] = {{a.dout, "dout"}, {a.attention_out, "attentionOut"}, {a.dq, "dq"}};
   for (const Named& n : qlike)
-    if (!same_shape(n.t, a.query)) return fail(BSA_ERR_PARAM_INVALID, "%s shape differs from query", n.name);
+    if (n.t != nullptr && !same_shape(n.t, a.query)) return fail(BSA_ERR_PARAM_INVALID, "%s shape differs from query", n.name);
   const Named kvlike[] = {{a.value, "value"}, {a.dk, "dk"}, {a.dv, "dv"}};
   for (const Named& n : kvlike)
-    if (!same_shape(n.t, a.key)) return fail(BSA_ERR_PARAM_INVALID, "%s shape differs from key", n.name);
+    if (n.t != nullptr && !same_shape(n.t, a.key)) return fail(BSA_ERR_PARAM_INVALID, "%s shape differs from key", n.name);
 
   const bsa_tensor* q = a.query;
   const bsa_tensor* k = a.key;
@@ -223,12 +230,16 @@ int make_plan(const Args& a, Plan* plan) {
     return fail(BSA_ERR_PARAM_INVALID, "head dim %lld is not supported (64 or 128)", static_cast<long long>(D));
 
   // ---- contiguity: inputs contiguous, outputs unit innermost stride ----------
+  // (forward: attentionOut is an output with free outer strides; softmaxLse
+  // is written densely, so it must be contiguous either way)
   const Named inputs[] = {{a.dout, "dout"}, {a.query, "query"}, {a.key, "key"}, {a.value, "value"},
-                          {a.attention_out, "attentionOut"}, {a.softmax_lse, "softmaxLse"}};
+                          {a.fwd ? nullptr : a.attention_out, "attentionOut"}, {a.softmax_lse, "softmaxLse"}};
   for (const Named& n : inputs)
-    if (!row_major_contiguous(n.t)) return fail(BSA_ERR_PARAM_INVALID, "%s is not contiguous", n.name);
-  const Named outputs[] = {{a.dq, "dq"}, {a.dk, "dk"}, {a.dv, "dv"}};
+    if (n.t != nullptr && !row_major_contiguous(n.t))
+      return fail(BSA_ERR_PARAM_INVALID, "%s is not contiguous", n.name);
+  const Named outputs[] = {{a.dq, "dq"}, {a.dk, "dk"}, {a.dv, "dv"}, {a.fwd ? a.attention_out : nullptr, "attentionOut"}};
   for (const Named& n : outputs) {
+    if (n.t == nullptr) continue;
     if (n.t->stride[n.t->ndim - 1] != 1)
       return fail(BSA_ERR_PARAM_INVALID, "%s innermost stride must be 1", n.name);
     for (int d = 0; d < n.t->ndim - 1; ++d)
@@ -330,28 +341,38 @@ int make_plan(const Args& a, Plan* plan) {
   p.q = a.query->data;
   p.k = a.key->data;
   p.v = a.value->data;
-  p.o = a.attention_out->data;
-  p.dout = a.dout->data;
-  p.lse = static_cast<const float*>(a.softmax_lse->data);
   p.mask = a.block_sparse_mask ? static_cast<const uint8_t*>(a.block_sparse_mask->data) : nullptr;
-  p.dq = a.dq->data;
-  p.dk = a.dk->data;
-  p.dv = a.dv->data;
+  if (a.fwd) {
+    p.out_o = a.attention_out->data;
+    p.out_lse = static_cast<float*>(a.softmax_lse->data);
+  } else {
+    p.o = a.attention_out->data;
+    p.dout = a.dout->data;
+    p.lse = static_cast<const float*>(a.softmax_lse->data);
+    p.dq = a.dq->data;
+    p.dk = a.dk->data;
+    p.dv = a.dv->data;
+  }
+  // strides of a q-like output: dq, or the forward's attention_out
+  const bsa_tensor* qout = a.fwd ? a.attention_out : a.dq;
+  const bsa_tensor* kout = a.fwd ? a.key : a.dk;  // dk/dv strides (unused by the forward)
+  const bsa_tensor* vout = a.fwd ? a.value : a.dv;
   if (tnd) {
     p.q_sb = 0, p.q_sr = N * D, p.q_sh = D;
     p.kv_sb = 0, p.kv_sr = Nkv * D, p.kv_sh = D;
-    p.dq_sb = 0, p.dq_sr = a.dq->stride[0], p.dq_sh = a.dq->stride[1];
-    p.dk_sb = 0, p.dk_sr = a.dk->stride[0], p.dk_sh = a.dk->stride[1];
-    p.dv_sb = 0, p.dv_sr = a.dv->stride[0], p.dv_sh = a.dv->stride[1];
+    p.dq_sb = 0, p.dq_sr = qout->stride[0], p.dq_sh = qout->stride[1];
+    p.dk_sb = 0, p.dk_sr = kout->stride[0], p.dk_sh = kout->stride[1];
+    p.dv_sb = 0, p.dv_sr = vout->stride[0], p.dv_sh = vout->stride[1];
     p.lse_sb = 0, p.lse_sr = N, p.lse_sh = 1;
   } else {
     p.q_sb = N * Sq * D, p.q_sh = Sq * D, p.q_sr = D;
     p.kv_sb = Nkv * Skv * D, p.kv_sh = Skv * D, p.kv_sr = D;
-    p.dq_sb = a.dq->stride[0], p.dq_sh = a.dq->stride[1], p.dq_sr = a.dq->stride[2];
-    p.dk_sb = a.dk->stride[0], p.dk_sh = a.dk->stride[1], p.dk_sr = a.dk->stride[2];
-    p.dv_sb = a.dv->stride[0], p.dv_sh = a.dv->stride[1], p.dv_sr = a.dv->stride[2];
+    p.dq_sb = qout->stride[0], p.dq_sh = qout->stride[1], p.dq_sr = qout->stride[2];
+    p.dk_sb = kout->stride[0], p.dk_sh = kout->stride[1], p.dk_sr = kout->stride[2];
+    p.dv_sb = vout->stride[0], p.dv_sh = vout->stride[1], p.dv_sr = vout->stride[2];
     p.lse_sb = N * Sq, p.lse_sh = Sq, p.lse_sr = 1;
   }
+  p.o_sb = p.dq_sb, p.o_sh = p.dq_sh, p.o_sr = p.dq_sr;
   p.B = static_cast<int32_t>(B);
   p.N = static_cast<int32_t>(N);
   p.Nkv = static_cast<int32_t>(Nkv);
@@ -386,19 +407,22 @@ int make_plan(const Args& a, Plan* plan) {
     plan->off[region] = off;
     off = align_up(off + bytes);
   };
+  // (the forward needs only the sequence table and the row lists: the other
+  // regions are empty)
+  const uint64_t bwd = a.fwd ? 0 : 1;
   const uint64_t rows = static_cast<uint64_t>(B) * N * Sq;
   take(BSA_WS_SEQ, sizeof(bsa::SeqInfo) * static_cast<uint64_t>(B) + 4 * bsa::kConstFloats);
-  take(BSA_WS_DELTA, 4 * rows);
-  take(BSA_WS_LSE2, 4 * rows);
+  take(BSA_WS_DELTA, bwd * 4 * rows);
+  take(BSA_WS_LSE2, bwd * 4 * rows);
   take(BSA_WS_ROW_CNT, 4ull * B * N * nqb);
   take(BSA_WS_ROW_LIST, 4ull * B * N * nqb * nkb);
-  take(BSA_WS_COL_CNT, 4ull * B * N * nkb);
-  take(BSA_WS_COL_LIST, 4ull * B * N * nkb * nqb);
+  take(BSA_WS_COL_CNT, bwd * 4ull * B * N * nkb);
+  take(BSA_WS_COL_LIST, bwd * 4ull * B * N * nkb * nqb);
   const int64_t n_units = B * Nkv * nkb * nsub_kv;
   const int64_t max_pieces = n_units * (N / Nkv) * nqb;  // a piece holds at least one Q block
   const int64_t slots = max_pieces < bsa::kMaxSlots ? max_pieces : bsa::kMaxSlots;
-  take(BSA_WS_PLAN, 4ull * bsa::plan_words(n_units, slots));
-  take(BSA_WS_PARTIAL, 4ull * slots * 2 * bsa::kTileRowsMax * D);
+  take(BSA_WS_PLAN, bwd * 4ull * bsa::plan_words(n_units, slots));
+  take(BSA_WS_PARTIAL, bwd * 4ull * slots * 2 * bsa::kTileRowsMax * D);
   plan->off[BSA_WS_TOTAL] = off;
   p.n_units = static_cast<int32_t>(n_units);
   p.n_dq_units = static_cast<int32_t>(B * N * nqb * nsub_q);
@@ -411,23 +435,27 @@ int make_plan(const Args& a, Plan* plan) {
 }
 
 // ---- profiling -----------------------------------------------------------
-constexpr int kStages = 3;
-const char* const kStageNames[kStages] = {"prologue", "dkdv", "dq"};
+constexpr int kStages = 4;
+const char* const kStageNames[kStages] = {"prologue", "dkdv", "dq", "fwd"};
+enum { kStagePrologue = 0, kStageDkdv, kStageDq, kStageFwd };
 struct Profile {
   bool on = false;
   int max_calls = 0;
-  std::vector<hipEvent_t> ev;  // (kStages + 1) per call
+  std::vector<hipEvent_t> ev;  // per call: a start event, then one event after each stage run
+  std::vector<int> tag;        // -1 for a call's start event, else the stage that event ends
 } g_prof;
 
 void free_profile_events() {
   for (hipEvent_t e : g_prof.ev) (void)hipEventDestroy(e);
   g_prof.ev.clear();
+  g_prof.tag.clear();
 }
 
-int record_stage(hipStream_t s) {
+int record_stage(hipStream_t s, int tag) {
   hipEvent_t e;
   if (hipEventCreate(&e) != hipSuccess) return fail(BSA_ERR_RUNTIME, "hipEventCreate failed");
   g_prof.ev.push_back(e);
+  g_prof.tag.push_back(tag);
   if (hipEventRecord(e, s) != hipSuccess) return fail(BSA_ERR_RUNTIME, "hipEventRecord failed");
   return BSA_OK;
 }
@@ -446,7 +474,108 @@ int check_device_pointer(const void* ptr, int device, const char* name) {
   return BSA_OK;
 }
 
+// Validate, carve the workspace and enqueue the kernels of one call.
+int run(const Args& a, void* workspace, uint64_t workspace_size, void* stream) {
+  Plan plan;
+  int rc = make_plan(a, &plan);
+  if (rc) return rc;
+  const uint64_t need = plan.off[BSA_WS_TOTAL];
+  if (workspace_size < need)
+    return fail(BSA_ERR_PARAM_INVALID, "workspace of %llu bytes is smaller than the %llu needed",
+                static_cast<unsigned long long>(workspace_size), static_cast<unsigned long long>(need));
+  if (need > 0 && workspace == nullptr) return fail(BSA_ERR_PARAM_NULLPTR, "workspace is a null pointer");
+  if (reinterpret_cast<uintptr_t>(workspace) % kAlign != 0)
+    return fail(BSA_ERR_PARAM_INVALID, "workspace must be %llu-byte aligned", static_cast<unsigned long long>(kAlign));
+
+  int device = -1;
+  if (hipGetDevice(&device) != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(BSA_ERR_RUNTIME, "hipGetDevice failed (no usable GPU?)");
+  }
+  struct Ptr {
+    const bsa_tensor* t;
+    const char* name;
+  };
+  const Ptr ptrs[] = {{a.dout, "dout"}, {a.query, "query"}, {a.key, "key"},
+                      {a.value, "value"}, {a.attention_out, "attentionOut"},
+                      {a.softmax_lse, "softmaxLse"}, {a.block_sparse_mask, "blockSparseMask"},
+                      {a.dq, "dq"}, {a.dk, "dk"}, {a.dv, "dv"}};
+  for (const Ptr& q : ptrs) {
+    if (q.t == nullptr || q.t->data == nullptr) continue;
+    rc = check_device_pointer(q.t->data, device, q.name);
+    if (rc) return rc;
+  }
+  if (workspace != nullptr && (rc = check_device_pointer(workspace, device, "workspace"))) return rc;
+
+  bsa::Params& p = plan.p;
+  char* ws = static_cast<char*>(workspace);
+  p.seq = reinterpret_cast<bsa::SeqInfo*>(ws + plan.off[BSA_WS_SEQ]);
+  float* consts = reinterpret_cast<float*>(ws + plan.off[BSA_WS_SEQ] + sizeof(bsa::SeqInfo) * plan.seq.size());
+  p.consts = consts;
+  p.row_cnt = reinterpret_cast<int32_t*>(ws + plan.off[BSA_WS_ROW_CNT]);
+  p.row_list = reinterpret_cast<int32_t*>(ws + plan.off[BSA_WS_ROW_LIST]);
+  if (!a.fwd) {
+    p.delta = reinterpret_cast<float*>(ws + plan.off[BSA_WS_DELTA]);
+    p.lse2 = reinterpret_cast<float*>(ws + plan.off[BSA_WS_LSE2]);
+    p.col_cnt = reinterpret_cast<int32_t*>(ws + plan.off[BSA_WS_COL_CNT]);
+    p.col_list = reinterpret_cast<int32_t*>(ws + plan.off[BSA_WS_COL_LIST]);
+    p.plan = reinterpret_cast<int32_t*>(ws + plan.off[BSA_WS_PLAN]);
+    p.partial = reinterpret_cast<float*>(ws + plan.off[BSA_WS_PARTIAL]);
+  }
+
+  // Profiling: one event before the first stage and one after each stage run.
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool prof = g_prof.on && g_prof.max_calls > 0;
+  if (prof) --g_prof.max_calls;
+  auto mark = [&](int tag) { return prof ? record_stage(s, tag) : static_cast<int>(BSA_OK); };
+  auto launch_failed = [&](int herr, const char* what) {
+    return fail(BSA_ERR_RUNTIME, "%s launch failed: %s", what, hipGetErrorString(static_cast<hipError_t>(herr)));
+  };
+  if ((rc = mark(-1))) return rc;
+  int herr = 0;
+  for (size_t first = 0; first < plan.seq.size() && herr == 0; first += bsa::kMaxInlineSeq) {
+    bsa::SeqChunk chunk{};
+    chunk.first = static_cast<int32_t>(first);
+    chunk.count = static_cast<int32_t>(std::min<size_t>(bsa::kMaxInlineSeq, plan.seq.size() - first));
+    for (int i = 0; i < chunk.count; ++i) chunk.s[i] = plan.seq[first + i];
+    herr = bsa::launch_stage_seq(chunk, p.seq, consts, stream);
+  }
+  if (a.fwd) {
+    if (herr == 0) herr = bsa::launch_prologue_rows(p, stream);
+    if (herr) return launch_failed(herr, "prologue");
+    if ((rc = mark(kStagePrologue))) return rc;
+    if ((herr = bsa::launch_fwd(p, stream))) return launch_failed(herr, "forward");
+    return mark(kStageFwd);
+  }
+  if (herr == 0) herr = bsa::launch_prologue(p, stream);
+  if (herr == 0) herr = bsa::launch_plan(p, stream);
+  if (herr) return launch_failed(herr, "prologue");
+  if ((rc = mark(kStagePrologue))) return rc;
+  if ((herr = bsa::launch_dkdv(p, stream))) return launch_failed(herr, "dK/dV");
+  if ((rc = mark(kStageDkdv))) return rc;
+  if ((herr = bsa::launch_dq(p, stream))) return launch_failed(herr, "dQ");
+  return mark(kStageDq);
+}
+
 }  // namespace
+
+#define BSA_FWD_ARGS_DECL                                                                           \
+  const bsa_tensor *query, const bsa_tensor *key, const bsa_tensor *value,                          \
+      const bsa_tensor *block_sparse_mask, const bsa_tensor *atten_mask, const int64_t *block_shape, \
+      int64_t block_shape_len, const int64_t *actual_seq_lengths, int64_t actual_seq_lengths_len,   \
+      const int64_t *actual_seq_lengths_kv, int64_t actual_seq_lengths_kv_len,                      \
+      const char *q_input_layout, const char *kv_input_layout, int64_t num_key_value_heads,         \
+      int64_t mask_type, double scale_value, int64_t pre_tokens, int64_t next_tokens,               \
+      const bsa_tensor *attention_out, const bsa_tensor *softmax_lse
+
+#define BSA_FWD_ARGS_PACK                                                                          \
+  Args {                                                                                           \
+    nullptr, query, key, value, attention_out, softmax_lse, block_sparse_mask, atten_mask,         \
+        block_shape, block_shape_len, actual_seq_lengths, actual_seq_lengths_len,                  \
+        actual_seq_lengths_kv, actual_seq_lengths_kv_len, q_input_layout, kv_input_layout,         \
+        num_key_value_heads, mask_type, scale_value, pre_tokens, next_tokens, nullptr, nullptr,    \
+        nullptr, true                                                                              \
+  }
 
 #define BSA_ARGS_DECL                                                                               \
   const bsa_tensor *dout, const bsa_tensor *query, const bsa_tensor *key, const bsa_tensor *value,  \
@@ -463,7 +592,7 @@ int check_device_pointer(const void* ptr, int device, const char* name) {
     dout, query, key, value, attention_out, softmax_lse, block_sparse_mask, atten_mask,            \
         block_shape, block_shape_len, actual_seq_lengths, actual_seq_lengths_len,                  \
         actual_seq_lengths_kv, actual_seq_lengths_kv_len, q_input_layout, kv_input_layout,         \
-        num_key_value_heads, mask_type, scale_value, pre_tokens, next_tokens, dq, dk, dv           \
+        num_key_value_heads, mask_type, scale_value, pre_tokens, next_tokens, dq, dk, dv, false    \
   }
 
 extern "C" {
@@ -492,76 +621,22 @@ int bsa_bwd_workspace_layout(BSA_ARGS_DECL, uint64_t* offsets, int64_t* dims) {
 
 int bsa_bwd(BSA_ARGS_DECL, void* workspace, uint64_t workspace_size, void* stream) {
   g_err.clear();
+  return run(BSA_ARGS_PACK, workspace, workspace_size, stream);
+}
+
+int bsa_fwd_workspace_size(BSA_FWD_ARGS_DECL, uint64_t* workspace_size) {
+  g_err.clear();
+  if (workspace_size == nullptr) return fail(BSA_ERR_PARAM_NULLPTR, "workspaceSize is a null pointer");
   Plan plan;
-  int rc = make_plan(BSA_ARGS_PACK, &plan);
+  int rc = make_plan(BSA_FWD_ARGS_PACK, &plan);
   if (rc) return rc;
-  const uint64_t need = plan.off[BSA_WS_TOTAL];
-  if (workspace_size < need)
-    return fail(BSA_ERR_PARAM_INVALID, "workspace of %llu bytes is smaller than the %llu needed",
-                static_cast<unsigned long long>(workspace_size), static_cast<unsigned long long>(need));
-  if (need > 0 && workspace == nullptr) return fail(BSA_ERR_PARAM_NULLPTR, "workspace is a null pointer");
-  if (reinterpret_cast<uintptr_t>(workspace) % kAlign != 0)
-    return fail(BSA_ERR_PARAM_INVALID, "workspace must be %llu-byte aligned", static_cast<unsigned long long>(kAlign));
-
-  int device = -1;
-  if (hipGetDevice(&device) != hipSuccess) {
-    (void)hipGetLastError();
-    return fail(BSA_ERR_RUNTIME, "hipGetDevice failed (no usable GPU?)");
-  }
-  struct Ptr {
-    const void* ptr;
-    const char* name;
-  };
-  const Ptr ptrs[] = {{dout->data, "dout"}, {query->data, "query"}, {key->data, "key"},
-                      {value->data, "value"}, {attention_out->data, "attentionOut"},
-                      {softmax_lse->data, "softmaxLse"},
-                      {block_sparse_mask ? block_sparse_mask->data : nullptr, "blockSparseMask"},
-                      {dq->data, "dq"}, {dk->data, "dk"}, {dv->data, "dv"}, {workspace, "workspace"}};
-  for (const Ptr& q : ptrs) {
-    if (q.ptr == nullptr) continue;
-    rc = check_device_pointer(q.ptr, device, q.name);
-    if (rc) return rc;
-  }
-
-  bsa::Params& p = plan.p;
-  char* ws = static_cast<char*>(workspace);
-  p.seq = reinterpret_cast<bsa::SeqInfo*>(ws + plan.off[BSA_WS_SEQ]);
-  float* consts = reinterpret_cast<float*>(ws + plan.off[BSA_WS_SEQ] + sizeof(bsa::SeqInfo) * plan.seq.size());
-  p.consts = consts;
-  p.delta = reinterpret_cast<float*>(ws + plan.off[BSA_WS_DELTA]);
-  p.lse2 = reinterpret_cast<float*>(ws + plan.off[BSA_WS_LSE2]);
-  p.row_cnt = reinterpret_cast<int32_t*>(ws + plan.off[BSA_WS_ROW_CNT]);
-  p.row_list = reinterpret_cast<int32_t*>(ws + plan.off[BSA_WS_ROW_LIST]);
-  p.col_cnt = reinterpret_cast<int32_t*>(ws + plan.off[BSA_WS_COL_CNT]);
-  p.col_list = reinterpret_cast<int32_t*>(ws + plan.off[BSA_WS_COL_LIST]);
-  p.plan = reinterpret_cast<int32_t*>(ws + plan.off[BSA_WS_PLAN]);
-  p.partial = reinterpret_cast<float*>(ws + plan.off[BSA_WS_PARTIAL]);
-
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  const bool prof = g_prof.on && g_prof.max_calls > 0;
-  if (prof) {
-    --g_prof.max_calls;
-    if ((rc = record_stage(s))) return rc;
-  }
-  int herr = 0;
-  for (size_t first = 0; first < plan.seq.size() && herr == 0; first += bsa::kMaxInlineSeq) {
-    bsa::SeqChunk chunk{};
-    chunk.first = static_cast<int32_t>(first);
-    chunk.count = static_cast<int32_t>(std::min<size_t>(bsa::kMaxInlineSeq, plan.seq.size() - first));
-    for (int i = 0; i < chunk.count; ++i) chunk.s[i] = plan.seq[first + i];
-    herr = bsa::launch_stage_seq(chunk, p.seq, consts, stream);
-  }
-  if (herr == 0) herr = bsa::launch_prologue(p, stream);
-  if (herr == 0) herr = bsa::launch_plan(p, stream);
-  if (herr) return fail(BSA_ERR_RUNTIME, "prologue launch failed: %s", hipGetErrorString(static_cast<hipError_t>(herr)));
-  if (prof && (rc = record_stage(s))) return rc;
-  herr = bsa::launch_dkdv(p, stream);
-  if (herr) return fail(BSA_ERR_RUNTIME, "dK/dV launch failed: %s", hipGetErrorString(static_cast<hipError_t>(herr)));
-  if (prof && (rc = record_stage(s))) return rc;
-  herr = bsa::launch_dq(p, stream);
-  if (herr) return fail(BSA_ERR_RUNTIME, "dQ launch failed: %s", hipGetErrorString(static_cast<hipError_t>(herr)));
-  if (prof && (rc = record_stage(s))) return rc;
+  *workspace_size = plan.off[BSA_WS_TOTAL];
   return BSA_OK;
+}
+
+int bsa_fwd(BSA_FWD_ARGS_DECL, void* workspace, uint64_t workspace_size, void* stream) {
+  g_err.clear();
+  return run(BSA_FWD_ARGS_PACK, workspace, workspace_size, stream);
 }
 
 const char* bsa_last_error(void) { return g_err.c_str(); }
@@ -573,31 +648,32 @@ int bsa_profile_start(int32_t max_calls) {
   g_prof.on = true;
   g_prof.max_calls = max_calls;
   g_prof.ev.reserve(static_cast<size_t>(max_calls) * (kStages + 1));
+  g_prof.tag.reserve(static_cast<size_t>(max_calls) * (kStages + 1));
   return BSA_OK;
 }
 
 int bsa_profile_stop(double* stage_ms, int32_t n_stages, int32_t* n_calls) {
   g_err.clear();
-  const size_t per = kStages + 1;
-  const size_t calls = g_prof.ev.size() / per;
   int rc = BSA_OK;
+  int calls = 0;
   if (stage_ms)
     for (int i = 0; i < n_stages; ++i) stage_ms[i] = 0.0;
-  for (size_t c = 0; c < calls && rc == BSA_OK; ++c) {
-    if (hipEventSynchronize(g_prof.ev[c * per + kStages]) != hipSuccess) {
-      rc = fail(BSA_ERR_RUNTIME, "hipEventSynchronize failed");
+  if (!g_prof.ev.empty() && hipEventSynchronize(g_prof.ev.back()) != hipSuccess)
+    rc = fail(BSA_ERR_RUNTIME, "hipEventSynchronize failed");
+  for (size_t i = 0; i < g_prof.ev.size() && rc == BSA_OK; ++i) {
+    const int st = g_prof.tag[i];
+    if (st < 0) {
+      ++calls;
+      continue;
+    }
+    float ms = 0.f;
+    if (hipEventElapsedTime(&ms, g_prof.ev[i - 1], g_prof.ev[i]) != hipSuccess) {
+      rc = fail(BSA_ERR_RUNTIME, "hipEventElapsedTime failed");
       break;
     }
-    for (int st = 0; st < kStages && st < n_stages; ++st) {
-      float ms = 0.f;
-      if (hipEventElapsedTime(&ms, g_prof.ev[c * per + st], g_prof.ev[c * per + st + 1]) != hipSuccess) {
-        rc = fail(BSA_ERR_RUNTIME, "hipEventElapsedTime failed");
-        break;
-      }
-      if (stage_ms) stage_ms[st] += ms;
-    }
+    if (stage_ms && st < n_stages) stage_ms[st] += ms;
   }
-  if (n_calls) *n_calls = static_cast<int32_t>(calls);
+  if (n_calls) *n_calls = calls;
   free_profile_events();
   g_prof.on = false;
   g_prof.max_calls = 0;

@@ -31,6 +31,8 @@ struct Params {
   void* dq;
   void* dk;
   void* dv;
+  void* out_o;      // forward outputs: attention_out, softmax_lse (natural log)
+  float* out_lse;
 
   int64_t q_sb, q_sh, q_sr;    // query, attention_out, dout (identical, contiguous)
   int64_t kv_sb, kv_sh, kv_sr; // key, value
@@ -38,6 +40,7 @@ struct Params {
   int64_t dk_sb, dk_sh, dk_sr;
   int64_t dv_sb, dv_sh, dv_sr;
   int64_t lse_sb, lse_sh, lse_sr;
+  int64_t o_sb, o_sh, o_sr;    // forward output O (any outer strides)
 
   int32_t B, N, Nkv, G, D;
   int32_t bx, by;      // block shape (Q rows, KV rows)
@@ -119,6 +122,8 @@ struct SeqChunk {
 int launch_stage_seq(const SeqChunk& chunk, SeqInfo* dst, float* consts, void* stream);
 int launch_prologue(const Params& p, void* stream);
 int launch_plan(const Params& p, void* stream);
+int launch_prologue_rows(const Params& p, void* stream);  // row lists only (the forward's)
+int launch_fwd(const Params& p, void* stream);
 int launch_dkdv(const Params& p, void* stream);
 int launch_dq(const Params& p, void* stream);
 

@@ -997,6 +997,200 @@ __global__ __launch_bounds__(64 * W) void dq_kernel(Params p) {
 }
 
 // ---------------------------------------------------------------------------
+// forward: O and LSE, Q-block outer
+// ---------------------------------------------------------------------------
+// The forward the backward differentiates (aclnnBlockSparseAttentionGrad page,
+// 功能说明 / 计算公式: S = Mask(scale * Q K^T), P = Softmax(S), Out = P V),
+// evaluated over the selected blocks only with a running maximum and sum per
+// query row (the FlashSoftmax rescaling of the FlashAttentionScore page,
+// 实现原理).  One workgroup per (batch, query head, Q block, 128-row part),
+// 32 query rows per wave held in registers as MFMA B operands; K/V slices of
+// the selected KV blocks stream through the same double-buffered LDS tiles as
+// the dQ kernel.  S^T = K Q^T leaves each lane one query row's scores, so the
+// running maximum needs one exchange with the partner lane (+-32), and the
+// output is accumulated transposed, O^T += V^T P^T, so that each lane also
+// holds its own row of O and rescales it in place.  Rows that select nothing
+// (and BNSD padding rows) get O = 0 and LSE = -inf.
+template <class E>
+__device__ __forceinline__ u16x4 pack4(const float* x) {
+  u16x4 r;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) r[t] = E::from_f32(x[t]);
+  return r;
+}
+
+template <class E, int D, int W>
+__global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) void fwd_kernel(Params p) {
+  constexpr int KS = D / 16;
+  constexpr int NT = D / 32;
+  constexpr int CH = kStageSlices;
+  constexpr int H = 32 * CH;
+  constexpr int NTHR = 64 * W;
+  __shared__ __align__(16) unsigned short sK[2][H * D], sV[2][H * D];
+  __shared__ __align__(16) float sB[2][CH * 64];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, w = tid >> 6, l32 = lane & 31, g = lane >> 5;
+
+  int wid = blockIdx.x;
+  const int nsub = (p.bx + kTileRows - 1) / kTileRows;
+  const int sub = wid % nsub;
+  wid /= nsub;
+  const int ib = wid % p.nqb;
+  wid /= p.nqb;
+  const int n = wid % p.N;
+  const int b = wid / p.N;
+  const SeqInfo si = p.seq[b];
+  const int q0 = ib * p.bx + sub * kTileRows;
+  const int part_end = min(ib * p.bx + p.bx, q0 + kTileRows);
+  const int q_end = min(part_end, si.len_q);
+  const int w_end = min(part_end, si.wlim_q);
+  if (q0 >= w_end) return;
+
+  const int h = n / p.G;
+  const int64_t bn = static_cast<int64_t>(b) * p.N + n;
+  const int my_q = q0 + 32 * w + l32;
+  const bool q_ok = my_q < q_end;
+  const unsigned short* qp = static_cast<const unsigned short*>(p.q) + b * p.q_sb + si.off_q * p.q_sr + n * p.q_sh;
+  u16x8 qreg[KS];
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {
+    u16x8 zq = {0, 0, 0, 0, 0, 0, 0, 0};
+    if (q_ok) zq = *reinterpret_cast<const u16x8*>(qp + my_q * p.q_sr + 16 * s + 8 * g);
+    qreg[s] = zq;
+  }
+
+  f32x16 aot[NT];  // O^T[d][q]: this lane's column is query row my_q
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) aot[nt] = f32x16{};
+  float m_run = -__builtin_inff(), l_run = 0.f;
+
+  const int64_t kv_base = b * p.kv_sb + si.off_kv * p.kv_sr + h * p.kv_sh;
+  const unsigned short* kp = static_cast<const unsigned short*>(p.k) + kv_base;
+  const unsigned short* vp = static_cast<const unsigned short*>(p.v) + kv_base;
+  const float c2 = p.scale_log2e;
+
+  KVSliceWalk walk{-1, p.row_cnt[bn * p.nqb + ib], 0, 0, p.row_list + (bn * p.nqb + ib) * p.nkb};
+  Slice sl[CH];
+  auto gather = [&]() {
+    bool any = false;
+#pragma unroll
+    for (int j = 0; j < CH; ++j) {
+      if (!walk.next(p, si.len_kv, sl[j])) sl[j] = Slice{0, 0, 0};
+      any |= sl[j].nrows > 0;
+    }
+    return any;
+  };
+  auto addr = [&](const Slice& s, int row, const unsigned short*& pa, const unsigned short*& pb) {
+    pa = kp + row * p.kv_sr;
+    pb = vp + row * p.kv_sr;
+  };
+  StagePrefetch<D, CH, NTHR> pf;
+  constexpr int BPT = (H + NTHR - 1) / NTHR;
+  float pb[BPT];
+  auto prefetch = [&]() {
+    pf.load(sl, addr, tid);
+#pragma unroll
+    for (int k = 0; k < BPT; ++k) {
+      const int r = tid + k * NTHR;
+      if (r < H) pb[k] = (r & 31) < pick_slice<CH>(sl, r >> 5).nrows ? 0.f : -__builtin_inff();
+    }
+  };
+  auto commit = [&](unsigned short* tk, unsigned short* tv, float* tb) {
+    pf.store(tk, tv, tid);
+#pragma unroll
+    for (int k = 0; k < BPT; ++k) {
+      const int r = tid + k * NTHR;
+      if (r < H) tb[64 * (r >> 5) + (r & 31)] = pb[k];
+    }
+  };
+
+  auto compute = [&](const unsigned short* tk, const unsigned short* tv, const float* tb) {
+#pragma unroll
+    for (int j = 0; j < CH; ++j) {
+      f32x16 st = {};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        st = E::mma(frag_along_row<D>(tk, 32 * j, 16 * ks, lane), qreg[ks], st);  // S^T[kv][q]
+      float4 b4[4];
+#pragma unroll
+      for (int a = 0; a < 4; ++a) b4[a] = *reinterpret_cast<const float4*>(tb + 64 * j + 8 * a + 4 * g);
+      float x[16];
+      float mx = -__builtin_inff();
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        x[i] = st[i] * c2 + b4[i >> 2][i & 3];  // scaled score in log2 units; -inf off the slice
+        mx = fmaxf(mx, x[i]);
+      }
+      mx = fmaxf(mx, __shfl_xor(mx, 32));  // the partner lane holds the row's other 16 keys
+      const float m_new = fmaxf(m_run, mx);
+      const float m_use = m_new == -__builtin_inff() ? 0.f : m_new;
+      const float alpha = fast_exp2(m_run - m_use);
+      float pv[16], ls = 0.f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        pv[i] = fast_exp2(x[i] - m_use);
+        ls += pv[i];
+      }
+      l_run = l_run * alpha + ls;
+      // alpha is exactly 1 where the running maximum did not move; once the
+      // maxima settle most slices skip the rescale (wave-uniform test)
+      if (__any(m_new != m_run)) {
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) aot[nt] *= alpha;
+      }
+      m_run = m_new;
+      const u16x8 pa[2] = {pack8<E>(pv), pack8<E>(pv + 8)};
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+          aot[nt] = E::mma(frag_down_rows<D>(tv, 32 * j + 16 * hh, 32 * nt, lane), pa[hh], aot[nt]);  // O^T += V^T P^T
+      }
+    }
+  };
+
+  bool have = gather();
+  if (have) {
+    prefetch();
+    commit(sK[0], sV[0], sB[0]);
+  }
+  bool more = have && gather();
+  if (more) prefetch();
+  __syncthreads();
+  for (int cur = 0; have; cur ^= 1) {
+    if (more) commit(sK[cur ^ 1], sV[cur ^ 1], sB[cur ^ 1]);
+    const bool next = more;
+    more = more && gather();
+    if (more) prefetch();
+    compute(sK[cur], sV[cur], sB[cur]);
+    __syncthreads();
+    have = next;
+  }
+
+  float l_tot = l_run + __shfl_xor(l_run, 32);
+  if (!q_ok) l_tot = 0.f;  // padding rows: nothing selected by definition
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  if (my_q < w_end) {
+    unsigned short* op = static_cast<unsigned short*>(p.out_o) + b * p.o_sb + si.off_q * p.o_sr + n * p.o_sh +
+                         static_cast<int64_t>(my_q) * p.o_sr;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        float v4[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) v4[c] = aot[nt][4 * a + c] * inv;
+        *reinterpret_cast<u16x4*>(op + 32 * nt + 8 * a + 4 * g) = pack4<E>(v4);
+      }
+    }
+    if (g == 0)
+      p.out_lse[b * p.lse_sb + (si.off_q + my_q) * p.lse_sr + n * p.lse_sh] =
+          l_tot > 0.f ? (m_run + __builtin_amdgcn_logf(l_tot)) * 0.6931471805599453f : -__builtin_inff();
+  }
+}
+
+// ---------------------------------------------------------------------------
 // dispatch
 // ---------------------------------------------------------------------------
 inline int waves_for(int rows) {
@@ -1047,6 +1241,28 @@ int launch_prologue(const Params& p, void* stream) {
       else BSA_DISPATCH_W(KERNEL, EF16, 64, W, GRID, S, P);                     \
     }                                                                           \
   } while (0)
+
+int launch_prologue_rows(const Params& p, void* stream) {
+  const PrologueGrid pg = prologue_grid(p.B, p.N, p.sq_max, p.nqb, p.nkb);
+  const dim3 grid(static_cast<unsigned>(pg.rows)), block(256);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool bf = p.dtype == 2;
+  const int nb_rows = static_cast<int>(pg.rows);
+  if (p.D == 128) {
+    if (bf) hipLaunchKernelGGL((prologue_kernel<EBf16, 128>), grid, block, 0, s, p, 0, nb_rows);
+    else hipLaunchKernelGGL((prologue_kernel<EF16, 128>), grid, block, 0, s, p, 0, nb_rows);
+  } else {
+    if (bf) hipLaunchKernelGGL((prologue_kernel<EBf16, 64>), grid, block, 0, s, p, 0, nb_rows);
+    else hipLaunchKernelGGL((prologue_kernel<EF16, 64>), grid, block, 0, s, p, 0, nb_rows);
+  }
+  return static_cast<int>(hipGetLastError());
+}
+
+int launch_fwd(const Params& p, void* stream) {
+  const dim3 grid(static_cast<unsigned>(p.n_dq_units));
+  BSA_DISPATCH(fwd_kernel, waves_for(p.bx), grid, static_cast<hipStream_t>(stream), p);
+  return static_cast<int>(hipGetLastError());
+}
 
 int launch_plan(const Params& p, void* stream) {
   hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(1024), 0, static_cast<hipStream_t>(stream), p);

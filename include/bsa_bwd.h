@@ -134,6 +134,47 @@ int bsa_bwd(const bsa_tensor* dout, const bsa_tensor* query, const bsa_tensor* k
             const bsa_tensor* dk, const bsa_tensor* dv, void* workspace, uint64_t workspace_size,
             void* stream);
 
+/*
+ * Forward (the operation the backward differentiates; aclnnBlockSparseAttentionGrad
+ * page, 计算公式: S = Mask(scale * Q * K^T), P = Softmax(S), Out = P * V, with the
+ * softmax taken over the selected blocks only, as the FlashAttentionScore page's
+ * 实现原理 describes for the dense case).  Produces the attentionOut and softmaxLse
+ * inputs of bsa_bwd:
+ *     attention_out[i] = sum_j P_ij * V[j]
+ *     softmax_lse[i]   = ln sum_j exp(scale * Q[i] . K[j])     (natural log)
+ * over the selected in-range keys j of query row i.  A row that selects no key
+ * (and every BNSD row past its actual length) gets attention_out = 0 and
+ * softmax_lse = -inf.
+ *
+ * Arguments are those of bsa_bwd_workspace_size without dout, dq, dk and dv, in
+ * the same order and with the same rules, except:
+ *  attention_out   output, dtype of query, shape of query; any outer strides,
+ *                  innermost stride 1.  Every element is written.
+ *  softmax_lse     output, fp32, [B, N, S] / [B, N, S, 1] (BNSD) or
+ *                  [T, N] / [T, N, 1] (TND), contiguous.  Every element is written.
+ * Ownership, stream, workspace and error behaviour are as for bsa_bwd; the
+ * forward's workspace (sequence table and row lists) is smaller than the
+ * backward's.
+ */
+int bsa_fwd_workspace_size(const bsa_tensor* query, const bsa_tensor* key, const bsa_tensor* value,
+                           const bsa_tensor* block_sparse_mask, const bsa_tensor* atten_mask,
+                           const int64_t* block_shape, int64_t block_shape_len,
+                           const int64_t* actual_seq_lengths, int64_t actual_seq_lengths_len,
+                           const int64_t* actual_seq_lengths_kv, int64_t actual_seq_lengths_kv_len,
+                           const char* q_input_layout, const char* kv_input_layout,
+                           int64_t num_key_value_heads, int64_t mask_type, double scale_value,
+                           int64_t pre_tokens, int64_t next_tokens, const bsa_tensor* attention_out,
+                           const bsa_tensor* softmax_lse, uint64_t* workspace_size);
+
+int bsa_fwd(const bsa_tensor* query, const bsa_tensor* key, const bsa_tensor* value,
+            const bsa_tensor* block_sparse_mask, const bsa_tensor* atten_mask, const int64_t* block_shape,
+            int64_t block_shape_len, const int64_t* actual_seq_lengths, int64_t actual_seq_lengths_len,
+            const int64_t* actual_seq_lengths_kv, int64_t actual_seq_lengths_kv_len,
+            const char* q_input_layout, const char* kv_input_layout, int64_t num_key_value_heads,
+            int64_t mask_type, double scale_value, int64_t pre_tokens, int64_t next_tokens,
+            const bsa_tensor* attention_out, const bsa_tensor* softmax_lse, void* workspace,
+            uint64_t workspace_size, void* stream);
+
 /* Workspace regions, as byte offsets filled in by bsa_bwd_workspace_layout. */
 enum bsa_ws_region {
   BSA_WS_SEQ = 0,      /* per-sequence table {int64 q_offset, kv_offset; int32 len_q, len_kv, wlim_q, wlim_kv} x B, then 128 fp32 constants */
@@ -173,12 +214,13 @@ const char* bsa_last_error(void);
 
 /*
  * Per-stage timing for benchmarks.  bsa_profile_start(max_calls) makes the
- * next max_calls bsa_bwd calls on this process record HIP events between
- * their kernel stages (on the call's stream).  bsa_profile_stop waits for the
- * recorded events, writes the summed milliseconds of each stage into
+ * next max_calls bsa_bwd / bsa_fwd calls on this process record HIP events
+ * between their kernel stages (on the call's stream).  bsa_profile_stop waits
+ * for the recorded events, writes the summed milliseconds of each stage into
  * stage_ms[0..n_stages) (stage order: 0 = sequence table + delta + mask
- * compaction, 1 = dK/dV, 2 = dQ), writes the number of profiled calls to
- * *n_calls, frees the events and turns recording off.  Not thread-safe.
+ * compaction + work plan, 1 = dK/dV, 2 = dQ, 3 = forward; a stage a call does
+ * not run adds 0), writes the number of profiled calls to *n_calls, frees the
+ * events and turns recording off.  Not thread-safe.
  */
 int bsa_profile_start(int32_t max_calls);
 int bsa_profile_stop(double* stage_ms, int32_t n_stages, int32_t* n_calls);

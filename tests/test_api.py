@@ -233,7 +233,7 @@ def test_binding_refuses_cpu_tensors_for_phase2():
 
 
 def test_stage_names():
-    assert [bsa.bsa_stage_name(i) for i in range(4)] == ["prologue", "dkdv", "dq", None]
+    assert [bsa.bsa_stage_name(i) for i in range(5)] == ["prologue", "dkdv", "dq", "fwd", None]
 
 
 def _fake(t):
@@ -280,3 +280,61 @@ def test_launch_grid_limit(what, shape):
 def test_launch_grid_just_below_limit():
     args = _huge(1, 7280, 131072, 128, 128, 128)
     assert _code(args) == bsa.BSA_OK, bsa.bsa_last_error()
+
+
+# ---- forward (bsa_fwd_workspace_size): same validation, O and LSE are outputs ----
+def _fwd(base=_bnsd, **kv):
+    a = base()
+    for k in ("dout", "dq", "dk", "dv"):
+        a.pop(k)
+    a.update(kv)
+    return a
+
+
+def _fcode(args):
+    try:
+        bsa.bsa_fwd_workspace_size(**args)
+    except bsa.BsaError as e:
+        assert bsa.bsa_last_error() == e.message
+        return e.code
+    return bsa.BSA_OK
+
+
+FWD_CASES = [
+    ("valid BNSD", lambda: _fwd(), bsa.BSA_OK),
+    ("valid TND", lambda: _fwd(_tnd), bsa.BSA_OK),
+    ("valid LSE [B,N,S,1]", lambda: _fwd(softmax_lse=torch.zeros(2, 4, 300, 1)), bsa.BSA_OK),
+    ("O with outer strides", lambda: _fwd(attention_out=torch.zeros(2, 300, 4, 128, dtype=torch.bfloat16).transpose(1, 2)),
+     bsa.BSA_OK),
+    ("O null", lambda: _fwd(attention_out=None), NULLPTR),
+    ("LSE null", lambda: _fwd(softmax_lse=None), NULLPTR),
+    ("query null", lambda: _fwd(query=None), NULLPTR),
+    ("O dtype", lambda: _fwd(attention_out=torch.zeros(2, 4, 300, 128, dtype=torch.float16)), INVALID),
+    ("O shape", lambda: _fwd(attention_out=torch.zeros(2, 4, 299, 128, dtype=torch.bfloat16)), INVALID),
+    ("O inner stride", lambda: _fwd(attention_out=_tr(torch.zeros(2, 4, 300, 128, dtype=torch.bfloat16))), INVALID),
+    ("LSE fp16", lambda: _fwd(softmax_lse=torch.zeros(2, 4, 300, dtype=torch.float16)), INVALID),
+    ("LSE non-contiguous", lambda: _fwd(softmax_lse=torch.zeros(2, 300, 4).transpose(1, 2)), INVALID),
+    ("LSE shape", lambda: _fwd(softmax_lse=torch.zeros(2, 4, 299)), INVALID),
+    ("sliding window", lambda: _fwd(pre_tokens=64), INVALID),
+    ("TND without lengths", lambda: _fwd(_tnd, actual_seq_lengths=None), NULLPTR),
+]
+
+
+@pytest.mark.parametrize("name,make,code", FWD_CASES, ids=[c[0] for c in FWD_CASES])
+def test_forward_phase1_status(name, make, code):
+    assert _fcode(make()) == code
+
+
+def test_forward_workspace_is_sequence_table_and_row_lists():
+    """The forward needs the sequence table, 128 constants and the row lists only."""
+    fwd = bsa.bsa_fwd_workspace_size(**_fwd())
+    B, N, nqb, nkb = 2, 4, 3, 3
+    al = lambda x: -(-x // 256) * 256
+    assert fwd == al(B * 32 + 128 * 4) + al(B * N * nqb * 4) + al(B * N * nqb * nkb * 4)
+    assert fwd < bsa.bsa_bwd_workspace_size(**_bnsd())
+
+
+def test_forward_binding_refuses_cpu_tensors():
+    a = _fwd()
+    with pytest.raises(ValueError):
+        bsa.bsa_fwd(**a, workspace=None)

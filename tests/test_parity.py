@@ -28,63 +28,7 @@ def _gpu():
     yield
 
 
-def _case(name):
-    mk = synth.make_case
-    cases = {
-        "config1": lambda: synth.config(1),
-        # several 128x128 tiles with ragged tails on both axes, GQA 4/2
-        "bnsd_bf16_d128_b128x128_ragged": lambda: mk(layout="BNSD", dtype="bf16", B=2, N=4, Nkv=2, D=128,
-                                                     Sq=300, Skv=270, bx=128, by=128, p=0.5, seed=101),
-        # padded BNSD (actual lengths), D=64, 64x128 blocks
-        "bnsd_fp16_d64_b64x128_padded": lambda: mk(layout="BNSD", dtype="fp16", B=2, N=2, Nkv=1, D=64,
-                                                   Sq=256, Skv=320, bx=64, by=128, p=0.5,
-                                                   lengths_q=[256, 150], lengths_kv=[320, 97], seed=102),
-        # varlen TND, GQA 4/1
-        "tnd_fp16_d128_b64x128_gqa": lambda: mk(layout="TND", dtype="fp16", B=3, N=4, Nkv=1, D=128,
-                                                bx=64, by=128, p=0.4, lengths_q=[200, 77, 333],
-                                                lengths_kv=[260, 129, 190], seed=103),
-        "bnsd_bf16_d128_b128x64": lambda: mk(layout="BNSD", dtype="bf16", B=1, N=2, Nkv=2, D=128,
-                                             Sq=256, Skv=520, bx=128, by=64, p=0.3, seed=104),
-        # block sizes that are not multiples of the 32-row MFMA tile
-        "bnsd_bf16_d64_b48x80": lambda: mk(layout="BNSD", dtype="bf16", B=1, N=2, Nkv=1, D=64,
-                                           Sq=200, Skv=230, bx=48, by=80, p=0.5, seed=105),
-        # blocks larger than the 128-row workgroup part
-        "bnsd_fp16_d128_b256x256": lambda: mk(layout="BNSD", dtype="fp16", B=1, N=2, Nkv=2, D=128,
-                                              Sq=600, Skv=530, bx=256, by=256, p=0.6, seed=106),
-        # element-level mask (1x1 blocks), some rows select nothing
-        "bnsd_bf16_d64_b1x1": lambda: mk(layout="BNSD", dtype="bf16", B=1, N=2, Nkv=1, D=64,
-                                         Sq=40, Skv=37, bx=1, by=1, mask_rule="bernoulli", p=0.3, seed=107),
-        # null mask = dense
-        "bnsd_bf16_d128_nullmask": lambda: mk(layout="BNSD", dtype="bf16", B=1, N=2, Nkv=1, D=128,
-                                              Sq=200, Skv=300, mask_rule="dense", seed=108),
-        # a sequence with no queries and one with no keys
-        "tnd_bf16_d64_empty_seqs": lambda: mk(layout="TND", dtype="bf16", B=3, N=2, Nkv=2, D=64,
-                                              bx=64, by=64, p=0.5, lengths_q=[100, 0, 60],
-                                              lengths_kv=[50, 70, 0], seed=109),
-        # rows without the diagonal: empty Q-block rows and unselected KV blocks
-        "bnsd_fp16_d128_sparse_rows": lambda: mk(layout="BNSD", dtype="fp16", B=1, N=2, Nkv=1, D=128,
-                                                 Sq=512, Skv=512, bx=64, by=64, mask_rule="bernoulli",
-                                                 p=0.15, seed=110),
-        # local window + 2 sink blocks: sink columns are selected by every Q block of every head,
-        # so the dK/dV work of most units is split into pieces and reduced in piece order
-        "bnsd_bf16_d128_local_sink_split": lambda: mk(layout="BNSD", dtype="bf16", B=1, N=4, Nkv=1,
-                                                      D=128, Sq=1024, Skv=1024, bx=64, by=64,
-                                                      mask_rule="local8_sink2", seed=111),
-        # the same with 256-row KV blocks (two 128-row parts per unit) and ragged lengths
-        "bnsd_fp16_d64_sink_split_parts": lambda: mk(layout="BNSD", dtype="fp16", B=2, N=4, Nkv=2,
-                                                     D=64, Sq=1000, Skv=1000, bx=32, by=256,
-                                                     mask_rule="local8_sink2",
-                                                     lengths_q=[1000, 700], lengths_kv=[1000, 650],
-                                                     seed=112),
-    }
-    return cases[name]()
-
-
-SMALL = ["config1", "bnsd_bf16_d128_b128x128_ragged", "bnsd_fp16_d64_b64x128_padded",
-         "tnd_fp16_d128_b64x128_gqa", "bnsd_bf16_d128_b128x64", "bnsd_bf16_d64_b48x80",
-         "bnsd_fp16_d128_b256x256", "bnsd_bf16_d64_b1x1", "bnsd_bf16_d128_nullmask",
-         "tnd_bf16_d64_empty_seqs", "bnsd_fp16_d128_sparse_rows", "bnsd_bf16_d128_local_sink_split",
-         "bnsd_fp16_d64_sink_split_parts"]
+from cases import SMALL, case as _case  # noqa: E402
 
 _cache = {}
 
