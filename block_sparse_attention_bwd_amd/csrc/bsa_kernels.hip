@@ -511,6 +511,105 @@ struct StagePrefetch {
 };
 
 
+// Direct global -> LDS copy (global_load_lds_dwordx4): lane L's 16 bytes land
+// at LDS byte address m0 + 16 L, with no register staging.  Issued from inline
+// assembly so that the compiler adds no waits of its own around it: the
+// caller waits on vmcnt for its own copies, then a barrier publishes the
+// buffer to the workgroup.  (Compiler-issued vector loads are counted by the
+// same vmcnt; loads complete in issue order, so either side's waits may only
+// wait longer than needed, never shorter.)
+__device__ __forceinline__ unsigned lds_addr(const void* p) {
+  return static_cast<unsigned>(reinterpret_cast<uintptr_t>((lds_void*)(p)));
+}
+__device__ __forceinline__ void dma16(const void* src, unsigned lds) {
+  const unsigned m = __builtin_amdgcn_readfirstlane(lds);  // wave-uniform by construction
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "s"(m) : "memory", "m0");
+}
+// s_waitcnt vmcnt(N) with the other counters left alone (gfx9 encoding: vmcnt
+// bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// A ring of NB LDS buffers, each holding one 32-row slice of K and of V in the
+// swizzled tile layout, filled by DMA NB - 1 slices ahead of the compute.  One
+// wave instruction fills 1 KB (512 / D rows): lane L writes physical chunk
+// L % (D/8) of row L / (D/8) and so fetches the logical chunk that the swizzle
+// puts there.  Rows past a slice's end (and every row of an empty slice) are
+// fetched from a zero block, so every stage issues the same number of copies
+// and the wait before a stage is a constant.
+template <int D, int W, int NB>
+struct KVRing {
+  static constexpr int RPI = 512 / D;       // rows per wave instruction
+  static constexpr int IPT = 32 / RPI;      // wave instructions per tensor and slice
+  static constexpr int IPW = IPT / W;       // ... per wave
+  static constexpr int NI = 2 * IPW;        // copies per wave and stage (K and V)
+  static constexpr int WAIT = (NB - 2) * NI;  // copies of the two later stages still in flight
+  static_assert(IPW >= 1 && IPW * W == IPT, "slice must split evenly over the waves");
+
+  __device__ __forceinline__ static void issue(unsigned short* tk, unsigned short* tv, const Slice& s,
+                                               const unsigned short* kp, const unsigned short* vp,
+                                               int64_t sr, const void* zeros, int w, int lane) {
+    const unsigned kb = lds_addr(tk), vb = lds_addr(tv);
+#pragma unroll
+    for (int i = 0; i < IPW; ++i) {
+      const int ins = w * IPW + i;
+      const int r = ins * RPI + lane / (D / 8);
+      const int c = (lane % (D / 8)) ^ swz<D>(r);
+      const bool ok = r < s.nrows;
+      const int64_t off = static_cast<int64_t>(s.row0 + r) * sr + 8 * c;
+      dma16(ok ? static_cast<const void*>(kp + off) : zeros, kb + 1024u * ins);
+      dma16(ok ? static_cast<const void*>(vp + off) : zeros, vb + 1024u * ins);
+    }
+  }
+};
+// Buffers per ring: 4 (three slices in flight) for 4-wave workgroups; with
+// fewer waves a workgroup has less work per slice, and 64 KB of LDS would cap
+// a CU at two of them, so they use 2 (one slice in flight, 32 KB).
+__host__ __device__ constexpr int ring_buffers(int waves) { return waves >= 4 ? 4 : 2; }
+
+// Make the compiler complete the loads of x here: a use it cannot see through.
+// Called on values loaded before the first copy, so that its waits for them
+// are not left inside the stage loop (where, loads completing in order, they
+// would wait for every copy in flight).
+template <class T>
+__device__ __forceinline__ void settle(const T& x) {
+  asm volatile("" : : "v"(x));
+}
+
+// The KV-slice walk of a Q block over its list of selected KV blocks, with
+// the list read from an LDS copy (kListChunk entries at a time): the stage
+// loop then issues no vector loads of its own.  Every thread walks the same
+// list, so the refill branch is uniform over the workgroup.
+constexpr int kListChunk = 1024;
+struct LdsListWalk {
+  int e, cnt, k, kend, base;
+  const int32_t* lst;
+  int* sl;  // kListChunk entries in LDS: lst[base .. base + kListChunk)
+
+  __device__ __forceinline__ void fill(int from, int tid, int nthr) {
+    __syncthreads();  // everyone is done reading the previous chunk
+    base = from;
+    for (int i = tid; i < kListChunk && from + i < cnt; i += nthr) sl[i] = lst[from + i];
+    __syncthreads();
+  }
+  __device__ __forceinline__ bool next(const Params& p, int len_kv, Slice& s, int tid, int nthr) {
+    while (k >= kend) {
+      if (++e >= cnt) return false;
+      if (e >= base + kListChunk) fill(e, tid, nthr);
+      k = sl[e - base] * p.by;
+      kend = min(k + p.by, len_kv);
+    }
+    s.head = 0;
+    s.row0 = k;
+    s.nrows = min(32, kend - k);
+    k += 32;
+    return true;
+  }
+};
+
 // ---------------------------------------------------------------------------
 // dK / dV: KV-block-outer
 // ---------------------------------------------------------------------------
@@ -839,14 +938,14 @@ struct KVSliceWalk {
 };
 
 template <class E, int D, int W>
-__global__ __launch_bounds__(64 * W) void dq_kernel(Params p) {
+__global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) void dq_kernel(Params p) {
   constexpr int KS = D / 16;
   constexpr int NT = D / 32;
-  constexpr int CH = kStageSlices;
-  constexpr int H = 32 * CH;  // staged K/V rows
-  constexpr int NTHR = 64 * W;
-  __shared__ __align__(16) unsigned short sK[2][H * D], sV[2][H * D];
-  __shared__ __align__(16) float sB[2][CH * 64];  // per slice: 32 row biases (0 / -inf), 32 unused
+  constexpr int NB = ring_buffers(W);
+  using Ring = KVRing<D, W, NB>;
+  __shared__ __align__(1024) unsigned short sK[NB][32 * D], sV[NB][32 * D];
+  __shared__ int sN[NB];  // valid rows of the slice in each buffer (0 = past the end)
+  __shared__ int sList[kListChunk];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6, l32 = lane & 31, g = lane >> 5;
@@ -894,6 +993,13 @@ __global__ __launch_bounds__(64 * W) void dq_kernel(Params p) {
   }
   const float l2 = q_ok ? p.lse2[bn * p.sq_max + my_q] : 0.f;
   const float dl = q_ok ? p.delta[bn * p.sq_max + my_q] : 0.f;
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {
+    settle(qreg[s]);
+    settle(oreg[s]);
+  }
+  settle(l2);
+  settle(dl);
 
   f32x16 adq[NT];
 #pragma unroll
@@ -904,86 +1010,61 @@ __global__ __launch_bounds__(64 * W) void dq_kernel(Params p) {
   const unsigned short* vp = static_cast<const unsigned short*>(p.v) + kv_base;
   const float c2 = p.scale_log2e;
 
-  KVSliceWalk walk{-1, p.row_cnt[bn * p.nqb + ib], 0, 0, p.row_list + (bn * p.nqb + ib) * p.nkb};
-  Slice sl[CH];
-  auto gather = [&]() {
-    bool any = false;
-#pragma unroll
-    for (int j = 0; j < CH; ++j) {
-      if (!walk.next(p, si.len_kv, sl[j])) sl[j] = Slice{0, 0, 0};
-      any |= sl[j].nrows > 0;
-    }
-    return any;
-  };
-  auto addr = [&](const Slice& s, int row, const unsigned short*& pa, const unsigned short*& pb) {
-    pa = kp + row * p.kv_sr;
-    pb = vp + row * p.kv_sr;
-  };
-  StagePrefetch<D, CH, NTHR> pf;
-  constexpr int BPT = (H + NTHR - 1) / NTHR;
-  float pb[BPT];
-  auto prefetch = [&]() {
-    pf.load(sl, addr, tid);
-#pragma unroll
-    for (int k = 0; k < BPT; ++k) {
-      const int r = tid + k * NTHR;
-      if (r < H) pb[k] = (r & 31) < pick_slice<CH>(sl, r >> 5).nrows ? 0.f : -__builtin_inff();
-    }
-  };
-  auto commit = [&](unsigned short* tk, unsigned short* tv, float* tb) {
-    pf.store(tk, tv, tid);
-#pragma unroll
-    for (int k = 0; k < BPT; ++k) {
-      const int r = tid + k * NTHR;
-      if (r < H) tb[64 * (r >> 5) + (r & 31)] = pb[k];
-    }
+  LdsListWalk walk{-1, p.row_cnt[bn * p.nqb + ib], 0, 0, 0, p.row_list + (bn * p.nqb + ib) * p.nkb, sList};
+  walk.fill(0, tid, 64 * W);
+  auto issue = [&](int slot) {
+    Slice sl;
+    if (!walk.next(p, si.len_kv, sl, tid, 64 * W)) sl = Slice{0, 0, 0};
+    Ring::issue(sK[slot], sV[slot], sl, kp, vp, p.kv_sr, p.consts, w, lane);
+    if (tid == 0) sN[slot] = sl.nrows;
   };
 
-  auto compute = [&](const unsigned short* tk, const unsigned short* tv, const float* tb) {
+  auto compute = [&](const unsigned short* tk, const unsigned short* tv, int nrows) {
+    f32x16 st = {}, dpt = {};
 #pragma unroll
-    for (int j = 0; j < CH; ++j) {
-      f32x16 st = {}, dpt = {};
+    for (int ks = 0; ks < KS; ++ks) {
+      st = E::mma(frag_along_row<D>(tk, 0, 16 * ks, lane), qreg[ks], st);   // S^T[kv][q]
+      dpt = E::mma(frag_along_row<D>(tv, 0, 16 * ks, lane), oreg[ks], dpt); // dP^T[kv][q]
+    }
+    float dsv[16];
+    if (nrows == 32) {  // uniform: full slices need no row mask
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        st = E::mma(frag_along_row<D>(tk, 32 * j, 16 * ks, lane), qreg[ks], st);   // S^T[kv][q]
-        dpt = E::mma(frag_along_row<D>(tv, 32 * j, 16 * ks, lane), oreg[ks], dpt); // dP^T[kv][q]
-      }
-      float4 b4[4];
-#pragma unroll
-      for (int a = 0; a < 4; ++a) b4[a] = *reinterpret_cast<const float4*>(tb + 64 * j + 8 * a + 4 * g);
-      float dsv[16];
+      for (int i = 0; i < 16; ++i) dsv[i] = fast_exp2(st[i] * c2 - l2) * (dpt[i] - dl);
+    } else {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const float x = fast_exp2(st[i] * c2 + (b4[i >> 2][i & 3] - l2));
+        const int kv = 8 * (i >> 2) + 4 * g + (i & 3);  // this register's key row in the slice
+        const float x = kv < nrows ? fast_exp2(st[i] * c2 - l2) : 0.f;
         dsv[i] = x * (dpt[i] - dl);
       }
-      const u16x8 da[2] = {pack8<E>(dsv), pack8<E>(dsv + 8)};
+    }
+    const u16x8 da[2] = {pack8<E>(dsv), pack8<E>(dsv + 8)};
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
+    for (int nt = 0; nt < NT; ++nt) {
 #pragma unroll
-        for (int hh = 0; hh < 2; ++hh)
-          adq[nt] = E::mma(da[hh], frag_down_rows<D>(tk, 32 * j + 16 * hh, 32 * nt, lane), adq[nt]);  // dQ += dS K
-      }
+      for (int hh = 0; hh < 2; ++hh)
+        adq[nt] = E::mma(da[hh], frag_down_rows<D>(tk, 16 * hh, 32 * nt, lane), adq[nt]);  // dQ += dS K
     }
   };
 
-  bool have = gather();
-  if (have) {
-    prefetch();
-    commit(sK[0], sV[0], sB[0]);
-  }
-  bool more = have && gather();
-  if (more) prefetch();
+  // slices 0 .. NB-2 in flight, then per stage: wait for this wave's copies of
+  // slice t, barrier (all copies landed; everyone is done with slice t - 1),
+  // refill the freed buffer with slice t + NB - 1, compute slice t
+#pragma unroll
+  for (int t = 0; t < NB - 1; ++t) issue(t);
+  wait_vmcnt<Ring::WAIT>();
   __syncthreads();
-  for (int cur = 0; have; cur ^= 1) {
-    if (more) commit(sK[cur ^ 1], sV[cur ^ 1], sB[cur ^ 1]);
-    const bool next = more;
-    more = more && gather();
-    if (more) prefetch();
-    compute(sK[cur], sV[cur], sB[cur]);
+  int nrows = sN[0];
+  for (int t = 0; nrows > 0;) {  // nrows is uniform; 0 once the walk is over
+    const int cur = t % NB;
+    issue((t + NB - 1) % NB);
+    compute(sK[cur], sV[cur], nrows);
+    ++t;
+    wait_vmcnt<Ring::WAIT>();
     __syncthreads();
-    have = next;
+    nrows = sN[t % NB];
   }
+  wait_vmcnt<0>();  // copies of the empty slices past the end
 
   unsigned short* dqp = static_cast<unsigned short*>(p.dq) + b * p.dq_sb + si.off_q * p.dq_sr + n * p.dq_sh;
 #pragma unroll
