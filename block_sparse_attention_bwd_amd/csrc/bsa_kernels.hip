@@ -46,10 +46,6 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kTileRows = 128;  // rows per workgroup part (32 per wave, at most 4 waves)
-#ifndef BSA_STAGE_SLICES
-#define BSA_STAGE_SLICES 1
-#endif
-constexpr int kStageSlices = BSA_STAGE_SLICES;  // 32-row slices staged per pipeline stage
 
 struct EBf16 {
   static __device__ __forceinline__ f32x16 mma(u16x8 a, u16x8 b, f32x16 c) {
@@ -446,70 +442,13 @@ __device__ __forceinline__ u16x8 frag_along_row(const unsigned short* tile, int 
 }
 
 // The work of a workgroup is a stream of 32-row slices (of Q blocks for the
-// dK/dV kernel, of KV blocks for the dQ kernel), staged CH at a time; every
-// wave computes on every slice of a stage.  nrows == 0 marks an empty slice.
+// dK/dV kernel, of KV blocks for the dQ and forward kernels); every wave
+// computes on every slice.  nrows == 0 marks an empty slice.
 struct Slice {
   int head;   // query head (dK/dV kernel); unused by the dQ kernel
   int row0;   // first sequence-local row
   int nrows;  // valid rows, 0..32
 };
-
-// sl[j] for a per-lane j, by selects (no dynamic register indexing).
-template <int CH>
-__device__ __forceinline__ Slice pick_slice(const Slice* sl, int j) {
-  Slice r = sl[0];
-#pragma unroll
-  for (int k = 1; k < CH; ++k)
-    if (j == k) r = sl[k];
-  return r;
-}
-
-// Register prefetch of one stage of CH slices (32*CH rows): for each of the
-// two tensors, thread tid holds chunks c = it * NTHR + tid (16 bytes) of the
-// 32CH x D tile; chunk c is row c / (D/8), and row r belongs to slice r / 32,
-// a compile-time function of `it` (NTHR and 32 * D/8 divide one another).
-// Rows past a slice's end hold zeros.
-template <int D, int CH, int NTHR>
-struct StagePrefetch {
-  static constexpr int CPR = D / 8;
-  static constexpr int CPT = 32 * CH * CPR / NTHR;
-  static_assert(CPT * NTHR == 32 * CH * CPR, "stage must split evenly over the threads");
-  u16x8 a[CPT], b[CPT];
-
-  // addr(slice, row, pa, pb) gives the row's address in the two source tensors
-  template <class Addr>
-  __device__ __forceinline__ void load(const Slice* sl, Addr addr, int tid) {
-#pragma unroll
-    for (int it = 0; it < CPT; ++it) {
-      const int c = it * NTHR + tid;
-      const int r = c / CPR, k = c % CPR;
-      const int j = (it * NTHR) / (32 * CPR);  // slice of this chunk (uniform per it)
-      const int rr = r & 31;
-      u16x8 x = {0, 0, 0, 0, 0, 0, 0, 0};
-      u16x8 y = x;
-      if (rr < sl[j].nrows) {
-        const unsigned short* pa;
-        const unsigned short* pb;
-        addr(sl[j], sl[j].row0 + rr, pa, pb);
-        x = *reinterpret_cast<const u16x8*>(pa + 8 * k);
-        y = *reinterpret_cast<const u16x8*>(pb + 8 * k);
-      }
-      a[it] = x;
-      b[it] = y;
-    }
-  }
-
-  __device__ __forceinline__ void store(unsigned short* ta, unsigned short* tb, int tid) const {
-#pragma unroll
-    for (int it = 0; it < CPT; ++it) {
-      const int c = it * NTHR + tid;
-      const int r = c / CPR, k = c % CPR;
-      *reinterpret_cast<u16x8*>(ta + tile_off<D>(r, 8 * k)) = a[it];
-      *reinterpret_cast<u16x8*>(tb + tile_off<D>(r, 8 * k)) = b[it];
-    }
-  }
-};
-
 
 // Direct global -> LDS copy (global_load_lds_dwordx4): lane L's 16 bytes land
 // at LDS byte address m0 + 16 L, with no register staging.  Issued from inline
@@ -918,25 +857,8 @@ __device__ void reduce_pieces(const Params& p, int s) {
 // ---------------------------------------------------------------------------
 // dQ: Q-block-outer
 // ---------------------------------------------------------------------------
-// Slices of the KV blocks this Q block selects, in list (ascending) order.
-struct KVSliceWalk {
-  int e, cnt, k, kend;
-  const int32_t* lst;
-
-  __device__ __forceinline__ bool next(const Params& p, int len_kv, Slice& s) {
-    while (k >= kend) {
-      if (++e >= cnt) return false;
-      k = lst[e] * p.by;
-      kend = min(k + p.by, len_kv);
-    }
-    s.head = 0;
-    s.row0 = k;
-    s.nrows = min(32, kend - k);
-    k += 32;
-    return true;
-  }
-};
-
+// One workgroup per (batch, query head, Q block, 128-row part); it walks the
+// slices of the KV blocks its Q block selects, in list (ascending) order.
 template <class E, int D, int W>
 __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) void dq_kernel(Params p) {
   constexpr int KS = D / 16;
@@ -1104,11 +1026,11 @@ template <class E, int D, int W>
 __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) void fwd_kernel(Params p) {
   constexpr int KS = D / 16;
   constexpr int NT = D / 32;
-  constexpr int CH = kStageSlices;
-  constexpr int H = 32 * CH;
-  constexpr int NTHR = 64 * W;
-  __shared__ __align__(16) unsigned short sK[2][H * D], sV[2][H * D];
-  __shared__ __align__(16) float sB[2][CH * 64];
+  constexpr int NB = ring_buffers(W);
+  using Ring = KVRing<D, W, NB>;
+  __shared__ __align__(1024) unsigned short sK[NB][32 * D], sV[NB][32 * D];
+  __shared__ int sN[NB];  // valid rows of the slice in each buffer (0 = past the end)
+  __shared__ int sList[kListChunk];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6, l32 = lane & 31, g = lane >> 5;
@@ -1140,6 +1062,8 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
     if (q_ok) zq = *reinterpret_cast<const u16x8*>(qp + my_q * p.q_sr + 16 * s + 8 * g);
     qreg[s] = zq;
   }
+#pragma unroll
+  for (int s = 0; s < KS; ++s) settle(qreg[s]);
 
   f32x16 aot[NT];  // O^T[d][q]: this lane's column is query row my_q
 #pragma unroll
@@ -1151,103 +1075,79 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
   const unsigned short* vp = static_cast<const unsigned short*>(p.v) + kv_base;
   const float c2 = p.scale_log2e;
 
-  KVSliceWalk walk{-1, p.row_cnt[bn * p.nqb + ib], 0, 0, p.row_list + (bn * p.nqb + ib) * p.nkb};
-  Slice sl[CH];
-  auto gather = [&]() {
-    bool any = false;
-#pragma unroll
-    for (int j = 0; j < CH; ++j) {
-      if (!walk.next(p, si.len_kv, sl[j])) sl[j] = Slice{0, 0, 0};
-      any |= sl[j].nrows > 0;
-    }
-    return any;
-  };
-  auto addr = [&](const Slice& s, int row, const unsigned short*& pa, const unsigned short*& pb) {
-    pa = kp + row * p.kv_sr;
-    pb = vp + row * p.kv_sr;
-  };
-  StagePrefetch<D, CH, NTHR> pf;
-  constexpr int BPT = (H + NTHR - 1) / NTHR;
-  float pb[BPT];
-  auto prefetch = [&]() {
-    pf.load(sl, addr, tid);
-#pragma unroll
-    for (int k = 0; k < BPT; ++k) {
-      const int r = tid + k * NTHR;
-      if (r < H) pb[k] = (r & 31) < pick_slice<CH>(sl, r >> 5).nrows ? 0.f : -__builtin_inff();
-    }
-  };
-  auto commit = [&](unsigned short* tk, unsigned short* tv, float* tb) {
-    pf.store(tk, tv, tid);
-#pragma unroll
-    for (int k = 0; k < BPT; ++k) {
-      const int r = tid + k * NTHR;
-      if (r < H) tb[64 * (r >> 5) + (r & 31)] = pb[k];
-    }
+  LdsListWalk walk{-1, p.row_cnt[bn * p.nqb + ib], 0, 0, 0, p.row_list + (bn * p.nqb + ib) * p.nkb, sList};
+  walk.fill(0, tid, 64 * W);
+  auto issue = [&](int slot) {
+    Slice sl;
+    if (!walk.next(p, si.len_kv, sl, tid, 64 * W)) sl = Slice{0, 0, 0};
+    Ring::issue(sK[slot], sV[slot], sl, kp, vp, p.kv_sr, p.consts, w, lane);
+    if (tid == 0) sN[slot] = sl.nrows;
   };
 
-  auto compute = [&](const unsigned short* tk, const unsigned short* tv, const float* tb) {
+  auto compute = [&](const unsigned short* tk, const unsigned short* tv, int nrows) {
+    f32x16 st = {};
 #pragma unroll
-    for (int j = 0; j < CH; ++j) {
-      f32x16 st = {};
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-        st = E::mma(frag_along_row<D>(tk, 32 * j, 16 * ks, lane), qreg[ks], st);  // S^T[kv][q]
-      float4 b4[4];
-#pragma unroll
-      for (int a = 0; a < 4; ++a) b4[a] = *reinterpret_cast<const float4*>(tb + 64 * j + 8 * a + 4 * g);
-      float x[16];
-      float mx = -__builtin_inff();
+    for (int ks = 0; ks < KS; ++ks)
+      st = E::mma(frag_along_row<D>(tk, 0, 16 * ks, lane), qreg[ks], st);  // S^T[kv][q]
+    float x[16];
+    float mx = -__builtin_inff();
+    if (nrows == 32) {  // uniform: full slices need no row mask
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        x[i] = st[i] * c2 + b4[i >> 2][i & 3];  // scaled score in log2 units; -inf off the slice
+        x[i] = st[i] * c2;  // scaled score in log2 units
         mx = fmaxf(mx, x[i]);
       }
-      mx = fmaxf(mx, __shfl_xor(mx, 32));  // the partner lane holds the row's other 16 keys
-      const float m_new = fmaxf(m_run, mx);
-      const float m_use = m_new == -__builtin_inff() ? 0.f : m_new;
-      const float alpha = fast_exp2(m_run - m_use);
-      float pv[16], ls = 0.f;
+    } else {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        pv[i] = fast_exp2(x[i] - m_use);
-        ls += pv[i];
+        const int kv = 8 * (i >> 2) + 4 * g + (i & 3);  // this register's key row in the slice
+        x[i] = kv < nrows ? st[i] * c2 : -__builtin_inff();
+        mx = fmaxf(mx, x[i]);
       }
-      l_run = l_run * alpha + ls;
-      // alpha is exactly 1 where the running maximum did not move; once the
-      // maxima settle most slices skip the rescale (wave-uniform test)
-      if (__any(m_new != m_run)) {
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 32));  // the partner lane holds the row's other 16 keys
+    const float m_new = fmaxf(m_run, mx);
+    const float m_use = m_new == -__builtin_inff() ? 0.f : m_new;
+    const float alpha = fast_exp2(m_run - m_use);
+    float pv[16], ls = 0.f;
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) aot[nt] *= alpha;
-      }
-      m_run = m_new;
-      const u16x8 pa[2] = {pack8<E>(pv), pack8<E>(pv + 8)};
+    for (int i = 0; i < 16; ++i) {
+      pv[i] = fast_exp2(x[i] - m_use);
+      ls += pv[i];
+    }
+    l_run = l_run * alpha + ls;
+    // alpha is exactly 1 where the running maximum did not move; once the
+    // maxima settle most slices skip the rescale (wave-uniform test)
+    if (__any(m_new != m_run)) {
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
+      for (int nt = 0; nt < NT; ++nt) aot[nt] *= alpha;
+    }
+    m_run = m_new;
+    const u16x8 pa[2] = {pack8<E>(pv), pack8<E>(pv + 8)};
 #pragma unroll
-        for (int hh = 0; hh < 2; ++hh)
-          aot[nt] = E::mma(frag_down_rows<D>(tv, 32 * j + 16 * hh, 32 * nt, lane), pa[hh], aot[nt]);  // O^T += V^T P^T
-      }
+    for (int nt = 0; nt < NT; ++nt) {
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh)
+        aot[nt] = E::mma(frag_down_rows<D>(tv, 16 * hh, 32 * nt, lane), pa[hh], aot[nt]);  // O^T += V^T P^T
     }
   };
 
-  bool have = gather();
-  if (have) {
-    prefetch();
-    commit(sK[0], sV[0], sB[0]);
-  }
-  bool more = have && gather();
-  if (more) prefetch();
+  // the dQ kernel's stage loop: NB - 1 slices in flight ahead of the compute
+#pragma unroll
+  for (int t = 0; t < NB - 1; ++t) issue(t);
+  wait_vmcnt<Ring::WAIT>();
   __syncthreads();
-  for (int cur = 0; have; cur ^= 1) {
-    if (more) commit(sK[cur ^ 1], sV[cur ^ 1], sB[cur ^ 1]);
-    const bool next = more;
-    more = more && gather();
-    if (more) prefetch();
-    compute(sK[cur], sV[cur], sB[cur]);
+  int nrows = sN[0];
+  for (int t = 0; nrows > 0;) {
+    const int cur = t % NB;
+    issue((t + NB - 1) % NB);
+    compute(sK[cur], sV[cur], nrows);
+    ++t;
+    wait_vmcnt<Ring::WAIT>();
     __syncthreads();
-    have = next;
+    nrows = sN[t % NB];
   }
+  wait_vmcnt<0>();
 
   float l_tot = l_run + __shfl_xor(l_run, 32);
   if (!q_ok) l_tot = 0.f;  // padding rows: nothing selected by definition
