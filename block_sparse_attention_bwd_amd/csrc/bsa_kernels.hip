@@ -464,6 +464,10 @@ __device__ __forceinline__ void dma16(const void* src, unsigned lds) {
   const unsigned m = __builtin_amdgcn_readfirstlane(lds);  // wave-uniform by construction
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "s"(m) : "memory", "m0");
 }
+__device__ __forceinline__ void dma4(const void* src, unsigned lds) {  // lane L's 4 bytes -> m0 + 4 L
+  const unsigned m = __builtin_amdgcn_readfirstlane(lds);
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" : : "v"(src), "s"(m) : "memory", "m0");
+}
 // s_waitcnt vmcnt(N) with the other counters left alone (gfx9 encoding: vmcnt
 // bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
 template <int N>
@@ -552,58 +556,6 @@ struct LdsListWalk {
 // ---------------------------------------------------------------------------
 // dK / dV: KV-block-outer
 // ---------------------------------------------------------------------------
-// MFMA B fragment of a row-major [rows][PITCH] LDS tile read along its rows:
-// lane (column n = l % 32, g = l / 32) gets rows r0 + 4g + {0,1,2,3} and
-// r0 + 8 + 4g + {0,1,2,3} of column col0 + n, the k order a C tile's
-// registers 8h..8h+7 use (see the layout note at the top of this file).
-template <int PITCH>
-__device__ __forceinline__ u16x8 frag_down_rows_padded(const unsigned short* tile, int r0, int col0, int lane) {
-  const int row = r0 + 4 * (lane >> 5) + ((lane & 15) >> 2);
-  const int col = col0 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-  const u16x4 a = lds_read_tr(tile, row * PITCH + col);
-  const u16x4 b = lds_read_tr(tile, (row + 8) * PITCH + col);
-  return u16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-}
-
-// Register prefetch of one staged tile: rows [r0, r0 + rows) of two row-major
-// tensors (row stride sr elements, D columns), 16 bytes per chunk, chunk
-// c = it * nthr + tid.  Rows past `rows` are zero.  With H = 32 * waves rows
-// per stage every thread holds exactly D / 16 chunks of each tensor.
-template <int D>
-struct PaddedTilePrefetch {
-  static constexpr int CPR = D / 8;
-  static constexpr int CPT = D / 16;
-  u16x8 a[CPT], b[CPT];
-
-  __device__ __forceinline__ void load(const unsigned short* pa, const unsigned short* pb, int64_t sr,
-                                       int r0, int rows, int tid, int nthr) {
-#pragma unroll
-    for (int it = 0; it < CPT; ++it) {
-      const int c = it * nthr + tid;
-      const int r = c / CPR, k = c % CPR;
-      u16x8 x = {0, 0, 0, 0, 0, 0, 0, 0};
-      u16x8 y = x;
-      if (r < rows) {
-        x = *reinterpret_cast<const u16x8*>(pa + (r0 + r) * sr + 8 * k);
-        y = *reinterpret_cast<const u16x8*>(pb + (r0 + r) * sr + 8 * k);
-      }
-      a[it] = x;
-      b[it] = y;
-    }
-  }
-
-  template <int PITCH>
-  __device__ __forceinline__ void store(unsigned short* ta, unsigned short* tb, int tid, int nthr) const {
-#pragma unroll
-    for (int it = 0; it < CPT; ++it) {
-      const int c = it * nthr + tid;
-      const int r = c / CPR, k = c % CPR;
-      *reinterpret_cast<u16x8*>(ta + r * PITCH + 8 * k) = a[it];
-      *reinterpret_cast<u16x8*>(tb + r * PITCH + 8 * k) = b[it];
-    }
-  }
-};
-
 // ---------------------------------------------------------------------------
 // dK / dV: KV-block-outer
 // ---------------------------------------------------------------------------
@@ -635,15 +587,16 @@ template <class E, int D, int W>
 __global__ __launch_bounds__(256) void dkdv_kernel(Params p) {
   constexpr int KS = D / 16;  // K=16 steps over the head dim
   constexpr int NT = D / 32;  // 32-wide column tiles of the head dim
-  constexpr int PITCH = D + 8;
-  __shared__ __align__(16) unsigned short sQ[kTileRows * PITCH];
-  __shared__ __align__(16) unsigned short sO[kTileRows * PITCH];  // dOut rows
-  __shared__ __align__(16) float sL[kTileRows];
-  __shared__ __align__(16) float sDl[kTileRows];
+  constexpr int H = 32 * W;   // Q rows per tile: 32 per wave
+  // Q and dOut tiles (swizzled layout) and their LSE*log2(e) / softmax_grad
+  // rows, double-buffered: tile t + 1 is copied in by DMA during tile t
+  __shared__ __align__(1024) unsigned short sQ[2][H * D];
+  __shared__ __align__(1024) unsigned short sO[2][H * D];  // dOut rows
+  __shared__ __align__(16) float sL[2][H];
+  __shared__ __align__(16) float sDl[2][H];
 
-  const int tid = threadIdx.x, nthr = blockDim.x;
+  const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6, l32 = lane & 31, g = lane >> 5;
-  const int H = nthr / 2;  // staged Q rows: 32 per wave
 
   // Workgroup i takes work item i of the plan's launch order: piece `piece`
   // of unit u (the whole unit unless it is split).
@@ -703,31 +656,49 @@ __global__ __launch_bounds__(256) void dkdv_kernel(Params p) {
   const unsigned short* qbase = static_cast<const unsigned short*>(p.q) + b * p.q_sb + si.off_q * p.q_sr;
   const unsigned short* obase = static_cast<const unsigned short*>(p.dout) + b * p.q_sb + si.off_q * p.q_sr;
 
-  PaddedTilePrefetch<D> pf;
-  float pl = 0.f, pd = 0.f;
-  auto prefetch = [&](const QTile& t) {
+  // DMA of one tile into buffer `buf`: wave w copies rows 32w .. 32w + 31 of
+  // Q and dOut (one 1 KB wave instruction per 512 / D rows, lanes fetching
+  // the swizzled chunk they land on) and their LSE / softmax_grad values;
+  // rows past the tile's valid rows read zeros and LSE = +inf, so their P is
+  // exactly 0 with no per-element test.
+  constexpr int RPI = 512 / D;
+  auto issue = [&](const QTile& t, int buf) {
     const int rows = min(H, t.qend - t.q0);
-    pf.load(qbase + t.n * p.q_sh, obase + t.n * p.q_sh, p.q_sr, t.q0, rows, tid, nthr);
-    const int64_t li = (bn0 + t.n) * p.sq_max + t.q0 + tid;
-    // rows past the block get LSE = +inf, so their P is exactly 0 with no per-element test
-    pl = tid < rows ? p.lse2[li] : __builtin_inff();
-    pd = tid < rows ? p.delta[li] : 0.f;
+    const unsigned short* qa = qbase + t.n * p.q_sh;
+    const unsigned short* oa = obase + t.n * p.q_sh;
+    const unsigned qb = lds_addr(sQ[buf]), ob = lds_addr(sO[buf]);
+#pragma unroll
+    for (int i = 0; i < 32 / RPI; ++i) {
+      const int ins = w * (32 / RPI) + i;
+      const int r = ins * RPI + lane / (D / 8);
+      const int c = (lane % (D / 8)) ^ swz<D>(r);
+      const bool ok = r < rows;
+      const int64_t off = static_cast<int64_t>(t.q0 + r) * p.q_sr + 8 * c;
+      dma16(ok ? static_cast<const void*>(qa + off) : p.consts, qb + 1024u * ins);
+      dma16(ok ? static_cast<const void*>(oa + off) : p.consts, ob + 1024u * ins);
+    }
+    if (lane < 32) {
+      const int r = 32 * w + lane;
+      const int64_t li = (bn0 + t.n) * p.sq_max + t.q0 + r;
+      dma4(r < rows ? static_cast<const void*>(p.lse2 + li) : p.consts + kConstPosInf, lds_addr(&sL[buf][32 * w]));
+      dma4(r < rows ? static_cast<const void*>(p.delta + li) : p.consts, lds_addr(&sDl[buf][32 * w]));
+    }
   };
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {  // complete the K/V loads before the first copy
+    settle(kreg[s]);
+    settle(vreg[s]);
+  }
 
   // entries [piece * chunk, piece * chunk + chunk) of the merged list, or all of them
   int left = pieces > 1 ? chunk : 0x7fffffff;
   QTile cur{h * p.G, pieces > 1 ? piece * chunk : 0, 0, 0};
   bool have = dkdv_seek(p, bn0, jb, n_end, si.len_q, cur);
-  if (have) prefetch(cur);
-  while (have) {
+  if (have) issue(cur, 0);
+  wait_vmcnt<0>();
+  __syncthreads();
+  for (int buf = 0; have; buf ^= 1) {
     const int rows = min(H, cur.qend - cur.q0);
-    __syncthreads();  // every wave is done with the previous tile
-    pf.template store<PITCH>(sQ, sO, tid, nthr);
-    if (tid < H) {
-      sL[tid] = pl;
-      sDl[tid] = pd;
-    }
-    __syncthreads();
     QTile nxt = cur;
     nxt.q0 += H;
     bool more = nxt.q0 < nxt.qend;
@@ -735,14 +706,18 @@ __global__ __launch_bounds__(256) void dkdv_kernel(Params p) {
       ++nxt.e;
       more = dkdv_seek(p, bn0, jb, n_end, si.len_q, nxt);
     }
-    if (more) prefetch(nxt);  // global loads stay in flight during the MFMA work below
+    if (more) issue(nxt, buf ^ 1);  // the other buffer: everyone finished with it at the last barrier
+    const unsigned short* tQ = sQ[buf];
+    const unsigned short* tO = sO[buf];
+    const float* tL = sL[buf];
+    const float* tD = sDl[buf];
 
     for (int c0 = 0; c0 < rows; c0 += 32) {
       f32x16 s = {}, dpv = {};
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const u16x8 aq = *reinterpret_cast<const u16x8*>(sQ + (c0 + l32) * PITCH + 16 * ks + 8 * g);
-        const u16x8 ao = *reinterpret_cast<const u16x8*>(sO + (c0 + l32) * PITCH + 16 * ks + 8 * g);
+        const u16x8 aq = frag_along_row<D>(tQ, c0, 16 * ks, lane);
+        const u16x8 ao = frag_along_row<D>(tO, c0, 16 * ks, lane);
         s = E::mma(aq, kreg[ks], s);      // S[q][kv] (unscaled); this lane's column is my_kv
         dpv = E::mma(ao, vreg[ks], dpv);  // dP[q][kv] = dOut * V^T
       }
@@ -750,8 +725,8 @@ __global__ __launch_bounds__(256) void dkdv_kernel(Params p) {
       float4 l4[4], d4[4];
 #pragma unroll
       for (int a = 0; a < 4; ++a) {
-        l4[a] = *reinterpret_cast<const float4*>(sL + c0 + 8 * a + 4 * g);
-        d4[a] = *reinterpret_cast<const float4*>(sDl + c0 + 8 * a + 4 * g);
+        l4[a] = *reinterpret_cast<const float4*>(tL + c0 + 8 * a + 4 * g);
+        d4[a] = *reinterpret_cast<const float4*>(tD + c0 + 8 * a + 4 * g);
       }
       float pv[16], dsv[16];
 #pragma unroll
@@ -767,13 +742,15 @@ __global__ __launch_bounds__(256) void dkdv_kernel(Params p) {
       for (int nt = 0; nt < NT; ++nt) {
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
-          const u16x8 bo = frag_down_rows_padded<PITCH>(sO, c0 + 16 * hh, 32 * nt, lane);
-          const u16x8 bq = frag_down_rows_padded<PITCH>(sQ, c0 + 16 * hh, 32 * nt, lane);
+          const u16x8 bo = frag_down_rows<D>(tO, c0 + 16 * hh, 32 * nt, lane);
+          const u16x8 bq = frag_down_rows<D>(tQ, c0 + 16 * hh, 32 * nt, lane);
           adv[nt] = E::mma(pa[hh], bo, adv[nt]);  // dV += P^T * dOut
           adk[nt] = E::mma(da[hh], bq, adk[nt]);  // dK += dS^T * Q
         }
       }
     }
+    wait_vmcnt<0>();  // this wave's copies of the next tile
+    __syncthreads();  // everyone's copies landed; everyone is done with this tile
     cur = nxt;
     have = more;
   }
