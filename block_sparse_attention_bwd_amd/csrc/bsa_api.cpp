@@ -331,7 +331,8 @@ int make_plan(const Args& a, Plan* plan) {
   const int64_t nsub_q = ceil_div(bx, 128), nsub_kv = ceil_div(by, 128);
   if (B * N * nqb * nsub_q + bsa::kMaxSlots > bsa::kMaxGridGroups ||
       B * Nkv * nkb * nsub_kv + bsa::kMaxSlots > bsa::kMaxGridGroups ||
-      bsa::prologue_grid(B, N, Sq, nqb, nkb).total() > bsa::kMaxGridGroups)
+      bsa::prologue_grid(B, N, Sq, nqb, nkb, tnd).total() > bsa::kMaxGridGroups ||
+      (tnd ? Sq * N : Sq) > kInt32Max)
     return fail(BSA_ERR_PARAM_INVALID, "launch grid too large (more than %lld workgroups)",
                 static_cast<long long>(bsa::kMaxGridGroups));
 
@@ -384,6 +385,7 @@ int make_plan(const Args& a, Plan* plan) {
   p.nkb = static_cast<int32_t>(nkb);
   p.sq_max = static_cast<int32_t>(Sq);
   p.dtype = dt;
+  p.tnd = tnd ? 1 : 0;
   p.scale = static_cast<float>(a.scale_value);
   p.scale_log2e = static_cast<float>(a.scale_value * 1.4426950408889634);
 

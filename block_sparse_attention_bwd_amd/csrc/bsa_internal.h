@@ -47,6 +47,7 @@ struct Params {
   int32_t nqb, nkb;    // mask block grid: ceil(maxSq/bx), ceil(maxSkv/by)
   int32_t sq_max;      // row extent of the delta/lse2 arrays
   int32_t dtype;       // bsa_dtype of the data tensors
+  int32_t tnd;         // 1 for the TND layout (rows of one token's heads are adjacent)
   float scale;         // scale_value rounded to fp32
   float scale_log2e;   // scale * log2(e)
 
@@ -87,19 +88,21 @@ constexpr int kMaxSlots = 2 * kBalanceGroups;
 // Launch-grid limits.  A dispatch counts work-items in 32 bits, so a grid of
 // 256-thread workgroups holds at most kMaxGridGroups of them.
 constexpr int64_t kMaxGridGroups = ((int64_t(1) << 32) - 1) / 256;
-constexpr int kDeltaRowsPerBlock = 64;  // prologue: softmax_grad rows per workgroup
 
-// Workgroups of the prologue launch: softmax_grad, row lists (4 Q-block rows per
-// workgroup), column lists (4 x 64 KV blocks per workgroup).
+// Workgroups of the prologue launch: softmax_grad (kDeltaRowsPerBlock rows
+// each, runs of one (b, n) for BNSD or of one sequence for TND), row lists
+// (4 Q-block rows each), column lists (64 KV blocks each).
+constexpr int kDeltaRowsPerBlock = 64;
 struct PrologueGrid {
   int64_t delta, rows, cols;
   int64_t total() const { return delta + rows + cols; }
 };
-inline PrologueGrid prologue_grid(int64_t B, int64_t N, int64_t sq_max, int64_t nqb, int64_t nkb) {
+inline PrologueGrid prologue_grid(int64_t B, int64_t N, int64_t sq_max, int64_t nqb, int64_t nkb, bool tnd) {
   PrologueGrid g;
-  g.delta = (B * N * sq_max + kDeltaRowsPerBlock - 1) / kDeltaRowsPerBlock;
+  g.delta = tnd ? B * ((sq_max * N + kDeltaRowsPerBlock - 1) / kDeltaRowsPerBlock)
+                : B * N * ((sq_max + kDeltaRowsPerBlock - 1) / kDeltaRowsPerBlock);
   g.rows = (B * N * nqb + 3) / 4;
-  g.cols = (B * N * ((nkb + 63) / 64) + 3) / 4;
+  g.cols = B * N * ((nkb + 63) / 64);
   return g;
 }
 
@@ -125,6 +128,6 @@ int launch_plan(const Params& p, void* stream);
 int launch_prologue_rows(const Params& p, void* stream);  // row lists only (the forward's)
 int launch_fwd(const Params& p, void* stream);
 int launch_dkdv(const Params& p, void* stream);
-int launch_dq(const Params& p, void* stream);
+int launch_dq(const Params& p, void* stream);  // also sums the pieces of split dK/dV units
 
 }  // namespace bsa

@@ -98,41 +98,62 @@ __global__ void stage_seq_kernel(SeqChunk c, SeqInfo* dst, float* consts) {
 // ---------------------------------------------------------------------------
 // prologue: softmax_grad + lse2, block lists
 // ---------------------------------------------------------------------------
+// softmax_grad = row sums of dOut o Out, and lse2 = LSE * log2(e), for every
+// row of the [B, N, maxSq] grid (0 past a sequence's length).  A workgroup
+// takes 64 rows adjacent in memory: BNSD, 64 consecutive positions of one
+// (b, n); TND, 64 consecutive (position, head) rows of one sequence, whose
+// heads are adjacent.  LPR lanes read a row's D elements 16 bytes each, and
+// every pass's loads are issued together.
 template <class E, int D>
 __device__ void delta_part(const Params& p, int blk) {
   constexpr int LPR = D / 8;        // lanes per row, 8 elements (16 bytes) each
   constexpr int RPP = 256 / LPR;    // rows per pass of the 256-thread block
+  constexpr int NP = kDeltaRowsPerBlock / RPP;
   const int tid = threadIdx.x;
   const int sub = tid % LPR, rloc = tid / LPR;
-  const int64_t total = static_cast<int64_t>(p.B) * p.N * p.sq_max;
   const unsigned short* op = static_cast<const unsigned short*>(p.o);
   const unsigned short* dp = static_cast<const unsigned short*>(p.dout);
-#pragma unroll 1
-  for (int pass = 0; pass < kDeltaRowsPerBlock / RPP; ++pass) {
-    const int64_t r = static_cast<int64_t>(blk) * kDeltaRowsPerBlock + pass * RPP + rloc;
-    float acc = 0.f, l2 = 0.f;
-    bool valid = false;
-    if (r < total) {
-      const int i = static_cast<int>(r % p.sq_max);
-      const int64_t bn = r / p.sq_max;
-      const int n = static_cast<int>(bn % p.N);
-      const int b = static_cast<int>(bn / p.N);
-      const SeqInfo si = p.seq[b];
-      if (i < si.len_q) {
-        valid = true;
-        const int64_t off = b * p.q_sb + (si.off_q + i) * p.q_sr + n * p.q_sh + sub * 8;
-        const u16x8 ov = *reinterpret_cast<const u16x8*>(op + off);
-        const u16x8 dv = *reinterpret_cast<const u16x8*>(dp + off);
+  const int per_seq = p.tnd ? (p.sq_max * p.N + kDeltaRowsPerBlock - 1) / kDeltaRowsPerBlock
+                            : (p.sq_max + kDeltaRowsPerBlock - 1) / kDeltaRowsPerBlock;
+  const int outer = blk / per_seq;  // TND: sequence b; BNSD: b * N + n
+  const int f0 = (blk % per_seq) * kDeltaRowsPerBlock;
+  float acc[NP], l2[NP];
+  int64_t out[NP];
+  bool valid[NP];
 #pragma unroll
-        for (int t = 0; t < 8; ++t) acc += E::to_f32(dv[t]) * E::to_f32(ov[t]);
-        if (sub == 0) l2 = p.lse[b * p.lse_sb + (si.off_q + i) * p.lse_sr + n * p.lse_sh] * kLog2e;
-      }
+  for (int k = 0; k < NP; ++k) {
+    const int f = f0 + k * RPP + rloc;  // row within the (sequence | (b, n)) run
+    int b, n, i;
+    if (p.tnd) {
+      b = outer;
+      i = f / p.N;
+      n = f - i * p.N;
+    } else {
+      b = outer / p.N;
+      n = outer - b * p.N;
+      i = f;
     }
+    const SeqInfo si = p.seq[b];
+    out[k] = i < p.sq_max ? (static_cast<int64_t>(b) * p.N + n) * p.sq_max + i : -1;
+    valid[k] = i < si.len_q;
+    acc[k] = 0.f;
+    l2[k] = 0.f;
+    if (valid[k]) {
+      const int64_t off = b * p.q_sb + (si.off_q + i) * p.q_sr + n * p.q_sh + sub * 8;
+      const u16x8 ov = *reinterpret_cast<const u16x8*>(op + off);
+      const u16x8 dv = *reinterpret_cast<const u16x8*>(dp + off);
 #pragma unroll
-    for (int m = LPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m);
-    if (r < total && sub == 0) {
-      p.delta[r] = valid ? acc : 0.f;
-      p.lse2[r] = valid ? l2 : 0.f;
+      for (int t = 0; t < 8; ++t) acc[k] += E::to_f32(dv[t]) * E::to_f32(ov[t]);
+      if (sub == 0) l2[k] = p.lse[b * p.lse_sb + (si.off_q + i) * p.lse_sr + n * p.lse_sh] * kLog2e;
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < NP; ++k) {
+#pragma unroll
+    for (int m = LPR / 2; m >= 1; m >>= 1) acc[k] += __shfl_xor(acc[k], m);
+    if (sub == 0 && out[k] >= 0) {
+      p.delta[out[k]] = acc[k];
+      p.lse2[out[k]] = l2[k];
     }
   }
 }
@@ -163,44 +184,67 @@ __device__ void row_list_part(const Params& p, int blk) {
   if (lane == 0) p.row_cnt[R] = base;
 }
 
-// One lane per (b, n, KV block): ascending list of selected in-range Q blocks.
-// A wave covers 64 consecutive KV blocks, so each mask row read is coalesced.
+// One workgroup per (b, n, group of 64 KV blocks): ascending lists of the
+// selected in-range Q blocks of those 64 columns.  The mask is taken 64 Q-block
+// rows at a time through an LDS tile (byte rows at a pitch of 68, so that a
+// column read down the 64 rows hits 64 distinct banks); wave w then compacts
+// columns 16w .. 16w + 15 of the tile with one ballot per column.
+constexpr int kColTilePitch = 68;
 __device__ void col_list_part(const Params& p, int blk) {
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  __shared__ uint8_t tile[64 * kColTilePitch];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int ncw = (p.nkb + 63) / 64;
-  const int64_t W = static_cast<int64_t>(blk) * 4 + w;
-  if (W >= static_cast<int64_t>(p.B) * p.N * ncw) return;  // wave-uniform
-  const int cw = static_cast<int>(W % ncw);
-  const int64_t bn = W / ncw;
+  const int cw = blk % ncw;
+  const int64_t bn = blk / ncw;
   const int b = static_cast<int>(bn / p.N);
-  const int j = cw * 64 + lane;
-  if (j >= p.nkb) return;
   const SeqInfo si = p.seq[b];
   const int nq_b = (si.len_q + p.bx - 1) / p.bx;
   const int nk_b = (si.len_kv + p.by - 1) / p.by;
-  int cnt = 0;
-  if (j < nk_b) {
-    int32_t* out = p.col_list + (bn * p.nkb + j) * p.nqb;
-    const uint8_t* mcol = p.mask ? p.mask + bn * p.nqb * p.nkb + j : nullptr;
-    for (int i = 0; i < nq_b; ++i) {
-      const bool on = mcol == nullptr || mcol[static_cast<int64_t>(i) * p.nkb] != 0;
-      if (on) out[cnt++] = i;
+  const int j0 = cw * 64;
+  int cnt[16];
+#pragma unroll
+  for (int k = 0; k < 16; ++k) cnt[k] = 0;
+  for (int i0 = 0; i0 < nq_b; i0 += 64) {  // uniform over the workgroup
+    __syncthreads();  // the previous tile is consumed
+    {
+      const int r = tid >> 2, c0 = 16 * (tid & 3);
+      const int i = i0 + r;
+#pragma unroll
+      for (int c = 0; c < 16; ++c) {
+        const int j = j0 + c0 + c;
+        uint8_t v = 0;
+        if (i < nq_b && j < nk_b) v = p.mask ? p.mask[(bn * p.nqb + i) * p.nkb + j] : 1;
+        tile[r * kColTilePitch + c0 + c] = v;
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const int c = 16 * w + k;
+      const bool on = tile[lane * kColTilePitch + c] != 0;  // 0 outside the in-range rows/columns
+      const uint64_t bal = __ballot(on);
+      const int j = j0 + c;
+      if (on) p.col_list[(bn * p.nkb + j) * p.nqb + cnt[k] + __popcll(bal & ((1ull << lane) - 1ull))] = i0 + lane;
+      cnt[k] += __popcll(bal);
     }
   }
-  p.col_cnt[bn * p.nkb + j] = cnt;
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    const int j = j0 + 16 * w + k;
+    if (lane == 0 && j < p.nkb) p.col_cnt[bn * p.nkb + j] = cnt[k];
+  }
 }
 
+// softmax_grad workgroups, then row lists, then column lists (the forward
+// launches the row lists only).
 template <class E, int D>
 __global__ __launch_bounds__(256) void prologue_kernel(Params p, int nb_delta, int nb_rows) {
   const int bid = blockIdx.x;
-  if (bid < nb_delta) {
-    delta_part<E, D>(p, bid);
-  } else if (bid < nb_delta + nb_rows) {
-    row_list_part(p, bid - nb_delta);
-  } else {
-    col_list_part(p, bid - nb_delta - nb_rows);
-  }
+  if (bid < nb_delta) delta_part<E, D>(p, bid);
+  else if (bid < nb_delta + nb_rows) row_list_part(p, bid - nb_delta);
+  else col_list_part(p, bid - nb_delta - nb_rows);
 }
+
 
 // ---------------------------------------------------------------------------
 // work split of the dK/dV kernel
@@ -276,20 +320,30 @@ __device__ __forceinline__ int order_bin(int cost, int chunk) {
   return min(kOrderBins - 1, 1 + static_cast<int>((static_cast<long long>(cost - 1) * (kOrderBins - 1)) / chunk));
 }
 
+constexpr int kPlanCachedUnits = 8192;  // units whose T_u the plan kernel keeps in LDS
+
 __global__ __launch_bounds__(1024) void plan_kernel(Params p) {
   __shared__ long long s_red[1024];
   __shared__ int s_scan[1024];
   __shared__ int s_hist[kOrderBins], s_cursor[kOrderBins];
   __shared__ unsigned long long s_xcd[8];
+  __shared__ int s_T[kPlanCachedUnits];
   const int tid = threadIdx.x;
   const PlanView pv(p);
   const int per = (p.n_units + 1023) / 1024;
   const int u0 = min(p.n_units, tid * per), u1 = min(p.n_units, u0 + per);
   if (tid < kOrderBins) s_hist[tid] = 0;
   if (tid < 8) s_xcd[tid] = 0;
+  // T_u, read from the column counts once (each thread reads back only its own units)
+  const bool cached = p.n_units <= kPlanCachedUnits;
+  auto T = [&](int u) { return cached ? s_T[u] : unit_entries(p, u); };
 
   long long tot = 0;
-  for (int u = u0; u < u1; ++u) tot += unit_entries(p, u);
+  for (int u = u0; u < u1; ++u) {
+    const int t = unit_entries(p, u);
+    if (cached) s_T[u] = t;
+    tot += t;
+  }
   s_red[tid] = tot;
   __syncthreads();
   for (int st = 512; st > 0; st >>= 1) {
@@ -302,7 +356,7 @@ __global__ __launch_bounds__(1024) void plan_kernel(Params p) {
 
   int mine = 0;
   for (int u = u0; u < u1; ++u) {
-    const int t = unit_entries(p, u);
+    const int t = T(u);
     if (t > chunk) mine += (t + chunk - 1) / chunk;
   }
   s_scan[tid] = mine;
@@ -317,7 +371,7 @@ __global__ __launch_bounds__(1024) void plan_kernel(Params p) {
   int run = s_scan[tid] - mine;  // exclusive prefix
   int extra = 0;                 // pieces >= 1 this thread creates
   for (int u = u0; u < u1; ++u) {
-    const int t = unit_entries(p, u);
+    const int t = T(u);
     const int k = t > chunk ? (t + chunk - 1) / chunk : 1;
     if (k > 1 && run + k <= p.slots_cap) {
       pv.unit_k[u] = k;
@@ -343,19 +397,21 @@ __global__ __launch_bounds__(1024) void plan_kernel(Params p) {
   }
   // dQ order: work of each XCD range, a unit costing its selected KV blocks + 1
   {
+    // strided over the units (coalesced, several loads in flight per thread);
+    // a thread's units change XCD range only every nd / 8 units
     const int nd = p.n_dq_units, nsub_q = (p.bx + kTileRows - 1) / kTileRows;
-    const int dper = (nd + 1023) / 1024;
-    const int d0 = min(nd, tid * dper), d1 = min(nd, d0 + dper);
     unsigned long long acc = 0;
-    int cur = d0 < d1 ? xcd_of_unit(d0, nd) : 0;
-    for (int u = d0; u < d1; ++u) {
+    int cur = xcd_of_unit(min(tid, max(nd - 1, 0)), max(nd, 1));
+#pragma unroll 4
+    for (int u = tid; u < nd; u += 1024) {
       const int x = xcd_of_unit(u, nd);
+      const unsigned c = 1u + static_cast<unsigned>(p.row_cnt[u / nsub_q]);
       if (x != cur) {
         atomicAdd(&s_xcd[cur], acc);
         acc = 0;
         cur = x;
       }
-      acc += 1ull + static_cast<unsigned>(p.row_cnt[u / nsub_q]);
+      acc += c;
     }
     if (acc) atomicAdd(&s_xcd[cur], acc);
   }
@@ -378,7 +434,7 @@ __global__ __launch_bounds__(1024) void plan_kernel(Params p) {
   }
   __syncthreads();
   for (int u = u0; u < u1; ++u) {
-    const int t = unit_entries(p, u);
+    const int t = T(u);
     const int k = pv.unit_k[u];
     for (int c = 0; c < k; ++c) {
       const int at = atomicAdd(&s_cursor[order_bin(k > 1 ? min(chunk, t - c * chunk) : t, chunk)], 1);
@@ -1165,19 +1221,23 @@ int launch_stage_seq(const SeqChunk& chunk, SeqInfo* dst, float* consts, void* s
   return static_cast<int>(hipGetLastError());
 }
 
-int launch_prologue(const Params& p, void* stream) {
-  const PrologueGrid pg = prologue_grid(p.B, p.N, p.sq_max, p.nqb, p.nkb);
-  const int nb_delta = static_cast<int>(pg.delta), nb_rows = static_cast<int>(pg.rows);
-  const dim3 grid(static_cast<unsigned>(pg.total())), block(256);
-  hipStream_t s = static_cast<hipStream_t>(stream);
+// prologue_kernel<E, D> for the data type and head dim of p
+template <class... A>
+void launch_prologue_kernel(const Params& p, dim3 grid, hipStream_t s, A... a) {
   const bool bf = p.dtype == 2;
   if (p.D == 128) {
-    if (bf) hipLaunchKernelGGL((prologue_kernel<EBf16, 128>), grid, block, 0, s, p, nb_delta, nb_rows);
-    else hipLaunchKernelGGL((prologue_kernel<EF16, 128>), grid, block, 0, s, p, nb_delta, nb_rows);
+    if (bf) hipLaunchKernelGGL((prologue_kernel<EBf16, 128>), grid, dim3(256), 0, s, p, a...);
+    else hipLaunchKernelGGL((prologue_kernel<EF16, 128>), grid, dim3(256), 0, s, p, a...);
   } else {
-    if (bf) hipLaunchKernelGGL((prologue_kernel<EBf16, 64>), grid, block, 0, s, p, nb_delta, nb_rows);
-    else hipLaunchKernelGGL((prologue_kernel<EF16, 64>), grid, block, 0, s, p, nb_delta, nb_rows);
+    if (bf) hipLaunchKernelGGL((prologue_kernel<EBf16, 64>), grid, dim3(256), 0, s, p, a...);
+    else hipLaunchKernelGGL((prologue_kernel<EF16, 64>), grid, dim3(256), 0, s, p, a...);
   }
+}
+
+int launch_prologue(const Params& p, void* stream) {
+  const PrologueGrid pg = prologue_grid(p.B, p.N, p.sq_max, p.nqb, p.nkb, p.tnd != 0);
+  launch_prologue_kernel(p, dim3(static_cast<unsigned>(pg.total())), static_cast<hipStream_t>(stream),
+                         static_cast<int>(pg.delta), static_cast<int>(pg.rows));
   return static_cast<int>(hipGetLastError());
 }
 
@@ -1201,18 +1261,9 @@ int launch_prologue(const Params& p, void* stream) {
   } while (0)
 
 int launch_prologue_rows(const Params& p, void* stream) {
-  const PrologueGrid pg = prologue_grid(p.B, p.N, p.sq_max, p.nqb, p.nkb);
-  const dim3 grid(static_cast<unsigned>(pg.rows)), block(256);
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  const bool bf = p.dtype == 2;
-  const int nb_rows = static_cast<int>(pg.rows);
-  if (p.D == 128) {
-    if (bf) hipLaunchKernelGGL((prologue_kernel<EBf16, 128>), grid, block, 0, s, p, 0, nb_rows);
-    else hipLaunchKernelGGL((prologue_kernel<EF16, 128>), grid, block, 0, s, p, 0, nb_rows);
-  } else {
-    if (bf) hipLaunchKernelGGL((prologue_kernel<EBf16, 64>), grid, block, 0, s, p, 0, nb_rows);
-    else hipLaunchKernelGGL((prologue_kernel<EF16, 64>), grid, block, 0, s, p, 0, nb_rows);
-  }
+  const PrologueGrid pg = prologue_grid(p.B, p.N, p.sq_max, p.nqb, p.nkb, p.tnd != 0);
+  launch_prologue_kernel(p, dim3(static_cast<unsigned>(pg.rows)), static_cast<hipStream_t>(stream), 0,
+                         static_cast<int>(pg.rows));
   return static_cast<int>(hipGetLastError());
 }
 

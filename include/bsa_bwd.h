@@ -217,10 +217,11 @@ const char* bsa_last_error(void);
  * next max_calls bsa_bwd / bsa_fwd calls on this process record HIP events
  * between their kernel stages (on the call's stream).  bsa_profile_stop waits
  * for the recorded events, writes the summed milliseconds of each stage into
- * stage_ms[0..n_stages) (stage order: 0 = sequence table + delta + mask
- * compaction + work plan, 1 = dK/dV, 2 = dQ, 3 = forward; a stage a call does
- * not run adds 0), writes the number of profiled calls to *n_calls, frees the
- * events and turns recording off.  Not thread-safe.
+ * stage_ms[0..n_stages) (stage order: 0 = sequence table + softmax_grad + mask
+ * compaction + work plan, 1 = dK/dV, 2 = dQ + the sum of split dK/dV units,
+ * 3 = forward; a stage a call does not run adds 0), writes the number of
+ * profiled calls to *n_calls, frees the events and turns recording off.
+ * Not thread-safe.
  */
 int bsa_profile_start(int32_t max_calls);
 int bsa_profile_stop(double* stage_ms, int32_t n_stages, int32_t* n_calls);

@@ -261,11 +261,12 @@ def _huge(B, N, Sq, Skv, bx, by, D=64):
                 pre_tokens=bsa.NO_WINDOW, next_tokens=bsa.NO_WINDOW, dq=_fake(q), dk=_fake(k), dv=_fake(k))
 
 
-# Prologue workgroups at Sq = 131072, Skv = 128: N*Sq/64 (softmax_grad) + N*Sq/512
-# (row lists) + ceil(N/4) (column lists) = 16,774,940 for N = 7280 and
-# 16,777,245 for N = 7281, against a limit of (2^32 - 1) / 256 = 16,777,215.
+# Prologue workgroups with one query row, Skv = 16384 and 1 x 1 blocks: N
+# (softmax_grad, one 64-row run per head) + ceil(N / 4) (row lists) + 256 N
+# (column lists, 64 KV blocks each), i.e. 16,777,074 for N = 65217 and
+# 16,777,331 for N = 65218, against a limit of (2^32 - 1) / 256 = 16,777,215.
 @pytest.mark.parametrize("what,shape", [
-    ("prologue", (1, 7281, 131072, 128, 128, 128)),
+    ("prologue", (1, 65218, 1, 16384, 1, 1)),
     # 2^24 dQ workgroups of 128 query rows
     ("dq", (1, 16384, 131072, 128, 128, 128)),
     # 2^24 dK/dV units of 128 key rows (a 1 x 2^24 block grid per head)
@@ -278,7 +279,7 @@ def test_launch_grid_limit(what, shape):
 
 
 def test_launch_grid_just_below_limit():
-    args = _huge(1, 7280, 131072, 128, 128, 128)
+    args = _huge(1, 65217, 1, 16384, 1, 1)
     assert _code(args) == bsa.BSA_OK, bsa.bsa_last_error()
 
 
