@@ -16,6 +16,12 @@ Parity status of each function (what pins it, in ``tests/test_oracle.py``):
   the GQA / TND / padding identities.
 * ``backward_dq_rows`` / ``backward_dkdv_rows``: equal to the matching rows of
   ``backward``.
+* the sliding window (``window=(pre, nxt)``, ``in_window``; in
+  ``tests/test_oracle_window.py``): finite differences with windows that do and
+  do not contain the diagonal, torch fp64 autograd on a hand-built element mask,
+  the zero-width-window closed form, slab path == dense path (with rows the
+  window leaves empty), the block lists against an interval formula, and the
+  row-sampled helpers.
 
 No function here is "parity unpinned".
 """

@@ -38,6 +38,13 @@ design notes):
   b start at the sum of the previous sequences' lengths.
 * outputs at padded BNSD positions, rows with no selected key (dQ) and keys
   no row selects (dK, dV) are zero.
+* sliding window (参数说明 preTokens / nextTokens: how many earlier and later
+  tokens the current token may attend to): with ``window = (pre, nxt)`` key j
+  takes part for query i only if ``i - pre <= j <= i + nxt``, both positions
+  sequence-local and counted from 0; ``None`` (2147483647 for both) means no
+  window.  A block stays in the lists only if the block mask selects it and at
+  least one of its in-range elements lies in the window.  A query row that
+  the window leaves no key has LSE = -inf and zero O and dQ.
 
 Everything is computed in float64 from the exact input values (fp16/bf16
 values upcast, the given fp32 LSE upcast).  The work is organised per
@@ -55,6 +62,7 @@ import numpy as np
 
 __all__ = [
     "sequence_offsets",
+    "in_window",
     "element_mask",
     "block_lists",
     "softmax_grad",
@@ -115,19 +123,34 @@ def _put_lse(out: np.ndarray, val: np.ndarray, layout: str, b: int, length: int,
 # ---------------------------------------------------------------------------
 # mask: block mask -> element mask, and the per-block lists
 # ---------------------------------------------------------------------------
-def element_mask(block_mask_bn: Optional[np.ndarray], bx: int, by: int, lq: int, lkv: int) -> np.ndarray:
-    """Element mask [lq, lkv] of one (batch, head): M[i, j] = mask[i // bx, j // by] != 0.
+def in_window(rows: np.ndarray, cols: np.ndarray, window) -> np.ndarray:
+    """[len(rows), len(cols)] bool: query position i may see key position j,
+    i.e. ``i - pre <= j <= i + nxt`` for ``window = (pre, nxt)``; all true for None."""
+    rows = np.asarray(rows, np.int64)
+    cols = np.asarray(cols, np.int64)
+    if window is None:
+        return np.ones((rows.size, cols.size), dtype=bool)
+    pre, nxt = window
+    d = cols[None, :] - rows[:, None]
+    return (d >= -pre) & (d <= nxt)
+
+
+def element_mask(block_mask_bn: Optional[np.ndarray], bx: int, by: int, lq: int, lkv: int,
+                 window=None) -> np.ndarray:
+    """Element mask [lq, lkv] of one (batch, head): M[i, j] = mask[i // bx, j // by] != 0,
+    and (i, j) in the window.
 
     ``None`` (no block mask) selects every pair.  Rows and columns past the
     sequence's lengths do not exist in the result.
     """
     if block_mask_bn is None:
-        return np.ones((lq, lkv), dtype=bool)
-    m = np.zeros((lq, lkv), dtype=bool)
-    for i in range(lq):
-        for j in range(lkv):
-            m[i, j] = block_mask_bn[i // bx, j // by] != 0
-    return m
+        m = np.ones((lq, lkv), dtype=bool)
+    else:
+        m = np.zeros((lq, lkv), dtype=bool)
+        for i in range(lq):
+            for j in range(lkv):
+                m[i, j] = block_mask_bn[i // bx, j // by] != 0
+    return m & in_window(np.arange(lq), np.arange(lkv), window)
 
 
 def _selected_blocks(block_mask_bn: Optional[np.ndarray], ib: int, nkb_b: int) -> List[int]:
@@ -138,14 +161,15 @@ def _selected_blocks(block_mask_bn: Optional[np.ndarray], ib: int, nkb_b: int) -
 
 
 def block_lists(mask: Optional[np.ndarray], B: int, N: int, nqb: int, nkb: int, bx: int, by: int,
-                len_q: Sequence[int], len_kv: Sequence[int]):
+                len_q: Sequence[int], len_kv: Sequence[int], window=None):
     """Per-Q-block and per-KV-block lists of selected in-range blocks.
 
     Returns ``(row_lists, col_lists)``: ``row_lists[b][n][i]`` is the ascending
     list of KV blocks ``j`` with ``mask[b, n, i, j] != 0``, ``i < ceil(Lq_b/bx)``
-    and ``j < ceil(Lkv_b/by)``; ``col_lists[b][n][j]`` is the ascending list of
+    and ``j < ceil(Lkv_b/by)`` (and, with a window, at least one in-range element
+    of the block inside it); ``col_lists[b][n][j]`` is the ascending list of
     such ``i`` for KV block ``j``.  Lists of out-of-range blocks are empty.
-    Brute force over every mask entry.
+    Brute force over every mask entry (and every element of a block for the window).
     """
     row_lists = [[[[] for _ in range(nqb)] for _ in range(N)] for _ in range(B)]
     col_lists = [[[[] for _ in range(nkb)] for _ in range(N)] for _ in range(B)]
@@ -156,6 +180,10 @@ def block_lists(mask: Optional[np.ndarray], B: int, N: int, nqb: int, nkb: int, 
             for i in range(nqb):
                 for j in range(nkb):
                     on = True if mask is None else bool(mask[b, n, i, j] != 0)
+                    if on and i < nq_b and j < nk_b and window is not None:
+                        rr = np.arange(i * bx, min(i * bx + bx, int(len_q[b])))
+                        cc = np.arange(j * by, min(j * by + by, int(len_kv[b])))
+                        on = bool(in_window(rr, cc, window).any())
                     if on and i < nq_b and j < nk_b:
                         row_lists[b][n][i].append(j)
                         col_lists[b][n][j].append(i)
@@ -179,25 +207,30 @@ def _slab_columns(block_mask_bn, ib, by, lkv):
     return np.concatenate(cols)
 
 
-def _head_forward(q, k, v, bm, bx, by, scale):
+def _head_forward(q, k, v, bm, bx, by, scale, window=None):
     """Forward of one (batch, query head): O [lq, D], LSE [lq] (fp64)."""
     lq, lkv = q.shape[0], k.shape[0]
     o = np.zeros_like(q)
     lse = np.full(lq, -np.inf)
     for ib in range(-(-lq // bx)):
-        rows = slice(ib * bx, min(ib * bx + bx, lq))
+        r = np.arange(ib * bx, min(ib * bx + bx, lq))
         cols = _slab_columns(bm, ib, by, lkv)
         if cols.size == 0:
             continue
-        s = scale * (q[rows] @ k[cols].T)
+        allowed = in_window(r, cols, window)
+        live = allowed.any(axis=1)          # rows the window leaves some key
+        if not live.any():
+            continue
+        rl, al = r[live], allowed[live]
+        s = np.where(al, scale * (q[rl] @ k[cols].T), -np.inf)
         m = s.max(axis=1, keepdims=True)
         l = m[:, 0] + np.log(np.sum(np.exp(s - m), axis=1))
-        lse[rows] = l
-        o[rows] = np.exp(s - l[:, None]) @ v[cols]
+        lse[rl] = l
+        o[rl] = np.exp(s - l[:, None]) @ v[cols]
     return o, lse
 
 
-def _head_backward(q, k, v, o, do, lse, bm, bx, by, scale):
+def _head_backward(q, k, v, o, do, lse, bm, bx, by, scale, window=None):
     """Backward of one (batch, query head): dQ, and this head's dK, dV terms."""
     lq, lkv = q.shape[0], k.shape[0]
     delta = softmax_grad(do, o)
@@ -209,8 +242,10 @@ def _head_backward(q, k, v, o, do, lse, bm, bx, by, scale):
         cols = _slab_columns(bm, ib, by, lkv)
         if cols.size == 0:
             continue
+        allowed = in_window(np.arange(rows.start, rows.stop), cols, window)
         s = scale * (q[rows] @ k[cols].T)          # S
-        p = np.exp(s - lse[rows, None])            # P, recomputed from the LSE
+        with np.errstate(over="ignore", invalid="ignore"):  # P, recomputed from the LSE, 0 off the window
+            p = np.where(allowed, np.exp(np.where(allowed, s - lse[rows, None], 0.0)), 0.0)
         dp = do[rows] @ v[cols].T                  # dP = dOut * V^T
         ds = p * (dp - delta[rows, None])          # dS = P o (dP - softmax_grad)
         dv[cols] += p.T @ do[rows]                 # dV = P^T * dOut
@@ -251,7 +286,7 @@ def _lengths(layout, q, k, len_q, len_kv):
     return lq, lk
 
 
-def forward(q, k, v, mask, *, layout, bx, by, scale, len_q=None, len_kv=None):
+def forward(q, k, v, mask, *, layout, bx, by, scale, len_q=None, len_kv=None, window=None):
     """Masked attention forward: O (q's layout) and LSE ([B,N,S] or [T,N]), fp64."""
     _, N, Nkv, _ = _dims(q, k, layout)
     G = _check_heads(N, Nkv)
@@ -268,13 +303,13 @@ def forward(q, k, v, mask, *, layout, bx, by, scale, len_q=None, len_kv=None):
         lb = np.full((N, Lq), -np.inf)
         for n in range(N):
             bm = None if mask is None else mask[b, n]
-            ob[n], lb[n] = _head_forward(qs[n], ks[n // G], vs[n // G], bm, bx, by, scale)
+            ob[n], lb[n] = _head_forward(qs[n], ks[n // G], vs[n // G], bm, bx, by, scale, window)
         _put(o, ob, layout, b, Lq, offq[b])
         _put_lse(lse, lb, layout, b, Lq, offq[b])
     return o, lse
 
 
-def backward(q, k, v, o, do, lse, mask, *, layout, bx, by, scale, len_q=None, len_kv=None):
+def backward(q, k, v, o, do, lse, mask, *, layout, bx, by, scale, len_q=None, len_kv=None, window=None):
     """dQ, dK, dV (fp64, in the inputs' layouts) of block-sparse attention."""
     _, N, Nkv, _ = _dims(q, k, layout)
     G = _check_heads(N, Nkv)
@@ -297,7 +332,7 @@ def backward(q, k, v, o, do, lse, mask, *, layout, bx, by, scale, len_q=None, le
         for n in range(N):
             h = n // G
             bm = None if mask is None else mask[b, n]
-            dqn, dkn, dvn = _head_backward(qs[n], ks[h], vs[h], os_[n], dos[n], ls[n], bm, bx, by, scale)
+            dqn, dkn, dvn = _head_backward(qs[n], ks[h], vs[h], os_[n], dos[n], ls[n], bm, bx, by, scale, window)
             dqb[n] = dqn
             dkb[h] += dkn
             dvb[h] += dvn
@@ -310,7 +345,7 @@ def backward(q, k, v, o, do, lse, mask, *, layout, bx, by, scale, len_q=None, le
 # ---------------------------------------------------------------------------
 # literal dense versions (tiny shapes): full element mask, full matrices
 # ---------------------------------------------------------------------------
-def forward_dense(q, k, v, mask, *, layout, bx, by, scale, len_q=None, len_kv=None):
+def forward_dense(q, k, v, mask, *, layout, bx, by, scale, len_q=None, len_kv=None, window=None):
     """Same as ``forward`` but on the full [Lq, Lkv] element mask."""
     _, N, Nkv, _ = _dims(q, k, layout)
     G = _check_heads(N, Nkv)
@@ -327,7 +362,7 @@ def forward_dense(q, k, v, mask, *, layout, bx, by, scale, len_q=None, len_kv=No
         lb = np.full((N, Lq), -np.inf)
         for n in range(N):
             h = n // G
-            m = element_mask(None if mask is None else mask[b, n], bx, by, Lq, Lk)
+            m = element_mask(None if mask is None else mask[b, n], bx, by, Lq, Lk, window)
             s = np.where(m, scale * (qs[n] @ ks[h].T), -np.inf)
             for i in range(Lq):
                 if m[i].any():
@@ -340,7 +375,8 @@ def forward_dense(q, k, v, mask, *, layout, bx, by, scale, len_q=None, len_kv=No
     return o, lse
 
 
-def backward_dense(q, k, v, o, do, lse, mask, *, layout, bx, by, scale, len_q=None, len_kv=None):
+def backward_dense(q, k, v, o, do, lse, mask, *, layout, bx, by, scale, len_q=None, len_kv=None,
+                   window=None):
     """Same as ``backward`` but on the full [Lq, Lkv] element mask."""
     _, N, Nkv, _ = _dims(q, k, layout)
     G = _check_heads(N, Nkv)
@@ -362,7 +398,7 @@ def backward_dense(q, k, v, o, do, lse, mask, *, layout, bx, by, scale, len_q=No
         dvb = np.zeros_like(vs)
         for n in range(N):
             h = n // G
-            m = element_mask(None if mask is None else mask[b, n], bx, by, Lq, Lk)
+            m = element_mask(None if mask is None else mask[b, n], bx, by, Lq, Lk, window)
             delta = softmax_grad(dos[n], os_[n])
             s = scale * (qs[n] @ ks[h].T)
             with np.errstate(over="ignore", invalid="ignore"):
@@ -405,7 +441,7 @@ def _lse_rows(lse, layout, b, n, rows, off):
 
 
 def backward_dq_rows(q, k, v, o, do, lse, mask, *, layout, bx, by, scale, len_q=None, len_kv=None,
-                     rows: Iterable[Tuple[int, int, int]] = ()) -> Dict[Tuple[int, int, int], np.ndarray]:
+                     rows: Iterable[Tuple[int, int, int]] = (), window=None) -> Dict[Tuple[int, int, int], np.ndarray]:
     """dQ rows for ``(b, n, i)`` triples (sequence-local i), fp64 [D] each.
 
     Row i of head n sums over the columns of the KV blocks its Q-block selects.
@@ -424,6 +460,7 @@ def backward_dq_rows(q, k, v, o, do, lse, mask, *, layout, bx, by, scale, len_q=
         h = n // G
         bm = None if mask is None else mask[b, n]
         cols = _slab_columns(bm, i // bx, by, Lk)
+        cols = cols[in_window([i], cols, window)[0]]
         if cols.size == 0:
             out[(b, n, i)] = np.zeros(D)
             continue
@@ -442,7 +479,7 @@ def backward_dq_rows(q, k, v, o, do, lse, mask, *, layout, bx, by, scale, len_q=
 
 
 def backward_dkdv_rows(q, k, v, o, do, lse, mask, *, layout, bx, by, scale, len_q=None, len_kv=None,
-                       rows: Iterable[Tuple[int, int, int]] = ()):
+                       rows: Iterable[Tuple[int, int, int]] = (), window=None):
     """dK and dV rows for ``(b, h, j)`` triples (sequence-local j), fp64 [D] each.
 
     Key j of KV head h sums over every query head n of its group and every row
@@ -468,6 +505,9 @@ def backward_dkdv_rows(q, k, v, o, do, lse, mask, *, layout, bx, by, scale, len_
                     if bm is not None and bm[ib, j // by] == 0:
                         continue
                     rr = np.arange(ib * bx, min(ib * bx + bx, Lq))
+                    rr = rr[in_window(rr, [j], window)[:, 0]]
+                    if rr.size == 0:
+                        continue
                     qr = _rows_of(q, layout, b, n, rr, offq[b])
                     orr = _rows_of(o, layout, b, n, rr, offq[b])
                     dor = _rows_of(do, layout, b, n, rr, offq[b])
