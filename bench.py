@@ -112,6 +112,10 @@ def gpu_forward(case, dev, rows_per_chunk=2048):
                     mb = mask[b, n, ib0:ib1, :nkb_b].bool()
                     em = mb.repeat_interleave(bx, dim=0)[: r1 - r0].repeat_interleave(by, dim=1)[:, :lk]
                     s.masked_fill_(~em, float("-inf"))
+                if case.window is not None and lk > 0:  # sliding window: i - pre <= j <= i + next
+                    d = (torch.arange(lk, device=s.device)[None, :]
+                         - torch.arange(r0, r1, device=s.device)[:, None])
+                    s.masked_fill_((d < -case.window[0]) | (d > case.window[1]), float("-inf"))
                 l = torch.logsumexp(s, dim=1)
                 p = torch.exp(s - l[:, None])
                 p = torch.nan_to_num(p, nan=0.0)
@@ -141,7 +145,9 @@ class Runner:
             actual_seq_lengths=list(map(int, case.len_q)) if lengths else None,
             actual_seq_lengths_kv=list(map(int, case.len_kv)) if lengths else None,
             q_input_layout=case.layout, kv_input_layout=case.layout, num_key_value_heads=case.Nkv,
-            mask_type=0, scale_value=case.scale, pre_tokens=bsa.NO_WINDOW, next_tokens=bsa.NO_WINDOW,
+            mask_type=0, scale_value=case.scale,
+            pre_tokens=bsa.NO_WINDOW if case.window is None else int(case.window[0]),
+            next_tokens=bsa.NO_WINDOW if case.window is None else int(case.window[1]),
             dq=self.dq, dk=self.dk, dv=self.dv)
         self.args = (dev["do"], dev["q"], dev["k"], dev["v"], o, lse)
         self.ws_size = bsa.bsa_bwd_workspace_size(*self.args, **self.kw)
@@ -167,7 +173,9 @@ class FwdRunner:
             actual_seq_lengths=list(map(int, case.len_q)) if lengths else None,
             actual_seq_lengths_kv=list(map(int, case.len_kv)) if lengths else None,
             q_input_layout=case.layout, kv_input_layout=case.layout, num_key_value_heads=case.Nkv,
-            mask_type=0, scale_value=case.scale, pre_tokens=bsa.NO_WINDOW, next_tokens=bsa.NO_WINDOW,
+            mask_type=0, scale_value=case.scale,
+            pre_tokens=bsa.NO_WINDOW if case.window is None else int(case.window[0]),
+            next_tokens=bsa.NO_WINDOW if case.window is None else int(case.window[1]),
             attention_out=self.o, softmax_lse=self.lse)
         self.args = (dev["q"], dev["k"], dev["v"])
         self.ws_size = bsa.bsa_fwd_workspace_size(*self.args, **self.kw)
@@ -213,9 +221,29 @@ def cpu_baseline(case, o_host, lse_host, min_seconds=10.0, max_runs=5, op="bwd")
     }
 
 
-def synth_blocks(case):
+def active_blocks(case):
+    """Blocks that take part (the FLOP count's unit): selected, in range and, with a
+    sliding window, meeting it (some element with -pre <= j - i <= next)."""
     import synth
-    return synth.active_blocks(case)
+    if case.window is None:
+        return synth.active_blocks(case)
+    pre, nxt = case.window
+    total = 0
+    for b in range(case.B):
+        lq, lk = int(case.len_q[b]), int(case.len_kv[b])
+        nq_b, nk_b = -(-lq // case.bx), -(-lk // case.by)
+        i = np.arange(nq_b)[:, None]
+        j = np.arange(nk_b)[None, :]
+        r0, r1 = i * case.bx, np.minimum(i * case.bx + case.bx, lq)
+        c0, c1 = j * case.by, np.minimum(j * case.by + case.by, lk)
+        meets = (c0 - (r1 - 1) <= nxt) & ((c1 - 1) - r0 >= -pre)
+        sel = np.ones((case.N, nq_b, nk_b), bool) if case.mask is None else case.mask[b, :, :nq_b, :nk_b] != 0
+        total += int(np.count_nonzero(sel & meets[None]))
+    return total
+
+
+def synth_blocks(case):
+    return active_blocks(case)
 
 
 def kernel_source_hash():
@@ -256,6 +284,8 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=2)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--window", default=None,
+                    help="PRE,NEXT: a sliding window (preTokens, nextTokens) on top of the workload's mask")
     ap.add_argument("--op", choices=["bwd", "fwd"], default="bwd",
                     help="bwd: the backward (default); fwd: the forward that produces O and LSE")
     args = ap.parse_args(argv)
@@ -270,7 +300,11 @@ def main(argv=None):
 
     torch.backends.cuda.matmul.allow_tf32 = False
     case = synth.config(args.config)
-    blocks = synth.active_blocks(case)
+    if args.window:
+        pre, nxt = (int(x) for x in args.window.split(","))
+        case.window = (pre, nxt)
+        case.name += f"_window{pre}_{nxt}"
+    blocks = active_blocks(case)
     fwd = args.op == "fwd"
     flops = (4.0 if fwd else 10.0) * case.bx * case.by * case.D * blocks
     print(f"# workload {case.name}: {blocks} active blocks, {flops / 1e9:.1f} GFLOP counted", file=sys.stderr, flush=True)

@@ -169,8 +169,7 @@ int make_plan(const Args& a, Plan* plan) {
   if (a.atten_mask != nullptr) return fail(BSA_ERR_PARAM_INVALID, "attenMask is not supported and must be null");
   if (a.mask_type != 0) return fail(BSA_ERR_PARAM_INVALID, "maskType %lld is not supported (only 0)",
                                     static_cast<long long>(a.mask_type));
-  if (a.pre_tokens != kNoWindow || a.next_tokens != kNoWindow)
-    return fail(BSA_ERR_PARAM_INVALID, "sliding window is not supported: preTokens/nextTokens must be 2147483647");
+
   if (!std::isfinite(a.scale_value)) return fail(BSA_ERR_PARAM_INVALID, "scaleValue is not finite");
 
   // ---- shapes -----------------------------------------------------------
@@ -386,6 +385,14 @@ int make_plan(const Args& a, Plan* plan) {
   p.sq_max = static_cast<int32_t>(Sq);
   p.dtype = dt;
   p.tnd = tnd ? 1 : 0;
+  // preTokens / nextTokens (参数说明): both 2147483647 = no window; otherwise the
+  // window, clamped to +-(Sq + Skv + 1), which no position difference reaches
+  if (a.pre_tokens != kNoWindow || a.next_tokens != kNoWindow) {
+    const int64_t lim = std::min<int64_t>(Sq + Skv + 1, kInt32Max);
+    p.win = 1;
+    p.win_pre = static_cast<int32_t>(std::max(-lim, std::min(lim, a.pre_tokens)));
+    p.win_next = static_cast<int32_t>(std::max(-lim, std::min(lim, a.next_tokens)));
+  }
   p.scale = static_cast<float>(a.scale_value);
   p.scale_log2e = static_cast<float>(a.scale_value * 1.4426950408889634);
 

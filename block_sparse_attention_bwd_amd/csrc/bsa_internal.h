@@ -48,6 +48,9 @@ struct Params {
   int32_t sq_max;      // row extent of the delta/lse2 arrays
   int32_t dtype;       // bsa_dtype of the data tensors
   int32_t tnd;         // 1 for the TND layout (rows of one token's heads are adjacent)
+  // sliding window: key j takes part for query i only if i - win_pre <= j <= i + win_next
+  // (sequence-local positions); win == 0 means no window
+  int32_t win, win_pre, win_next;
   float scale;         // scale_value rounded to fp32
   float scale_log2e;   // scale * log2(e)
 

@@ -83,6 +83,23 @@ __device__ __forceinline__ u16x8 pack8(const float* x) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// The sliding window (preTokens / nextTokens): key position j takes part for
+// query position i only if i - pre <= j <= i + next.  Positions are below
+// 2^31, so j - i fits in 32 bits; pre and next are clamped on the host.
+__device__ __forceinline__ bool in_band(const Params& p, int i, int j) {
+  const int d = j - i;
+  return d >= -p.win_pre && d <= p.win_next;
+}
+// Every pair of rows [r0, r0 + nr) x columns [c0, c0 + nc) is in the window
+// (true without one): the differences j - i fill [c0 - r0 - nr + 1, c0 + nc - 1 - r0].
+__device__ __forceinline__ bool rect_in_band(const Params& p, int r0, int nr, int c0, int nc) {
+  return !p.win || (c0 - (r0 + nr - 1) >= -p.win_pre && (c0 + nc - 1) - r0 <= p.win_next);
+}
+// Some pair of the rectangle is in the window.
+__device__ __forceinline__ bool rect_meets_band(const Params& p, int r0, int nr, int c0, int nc) {
+  return !p.win || (c0 - (r0 + nr - 1) <= p.win_next && (c0 + nc - 1) - r0 >= -p.win_pre);
+}
+
 // ---------------------------------------------------------------------------
 // per-sequence table
 // ---------------------------------------------------------------------------
@@ -172,9 +189,11 @@ __device__ void row_list_part(const Params& p, int blk) {
   if (ib < nq_b) {
     int32_t* out = p.row_list + R * p.nkb;
     const uint8_t* mrow = p.mask ? p.mask + R * p.nkb : nullptr;
+    const int r0 = ib * p.bx, nr = min(p.bx, si.len_q - r0);
     for (int j0 = 0; j0 < nk_b; j0 += 64) {
       const int j = j0 + lane;
-      const bool on = j < nk_b && (mrow == nullptr || mrow[j] != 0);
+      const bool on = j < nk_b && (mrow == nullptr || mrow[j] != 0) &&
+                      rect_meets_band(p, r0, nr, j * p.by, min(p.by, si.len_kv - j * p.by));
       const uint64_t bal = __ballot(on);
       const int pre = __popcll(bal & ((1ull << lane) - 1ull));
       if (on) out[base + pre] = j;
@@ -213,7 +232,9 @@ __device__ void col_list_part(const Params& p, int blk) {
       for (int c = 0; c < 16; ++c) {
         const int j = j0 + c0 + c;
         uint8_t v = 0;
-        if (i < nq_b && j < nk_b) v = p.mask ? p.mask[(bn * p.nqb + i) * p.nkb + j] : 1;
+        if (i < nq_b && j < nk_b &&
+            rect_meets_band(p, i * p.bx, min(p.bx, si.len_q - i * p.bx), j * p.by, min(p.by, si.len_kv - j * p.by)))
+          v = p.mask ? p.mask[(bn * p.nqb + i) * p.nkb + j] : 1;
         tile[r * kColTilePitch + c0 + c] = v;
       }
     }
@@ -785,12 +806,23 @@ __global__ __launch_bounds__(256) void dkdv_kernel(Params p) {
         d4[a] = *reinterpret_cast<const float4*>(tD + c0 + 8 * a + 4 * g);
       }
       float pv[16], dsv[16];
+      if (rect_in_band(p, cur.q0 + c0, 32, kv0 + 32 * w, 32)) {  // uniform: the window cuts nothing here
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float li = l4[i >> 2][i & 3], di = d4[i >> 2][i & 3];
-        const float x = fast_exp2(s[i] * c2 - li);  // P = exp(scale*S - LSE)
-        pv[i] = kv_ok ? x : 0.f;
-        dsv[i] = pv[i] * (dpv[i] - di);              // dS = P o (dP - softmax_grad)
+        for (int i = 0; i < 16; ++i) {
+          const float li = l4[i >> 2][i & 3], di = d4[i >> 2][i & 3];
+          const float x = fast_exp2(s[i] * c2 - li);  // P = exp(scale*S - LSE)
+          pv[i] = kv_ok ? x : 0.f;
+          dsv[i] = pv[i] * (dpv[i] - di);              // dS = P o (dP - softmax_grad)
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float li = l4[i >> 2][i & 3], di = d4[i >> 2][i & 3];
+          const int q = cur.q0 + c0 + 8 * (i >> 2) + 4 * g + (i & 3);  // this register's query row
+          const float x = fast_exp2(s[i] * c2 - li);
+          pv[i] = kv_ok && in_band(p, q, my_kv) ? x : 0.f;  // a select: li may be -inf off the window
+          dsv[i] = pv[i] * (dpv[i] - di);
+        }
       }
       const u16x8 pa[2] = {pack8<E>(pv), pack8<E>(pv + 8)};
       const u16x8 da[2] = {pack8<E>(dsv), pack8<E>(dsv + 8)};
@@ -900,6 +932,7 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
   using Ring = KVRing<D, W, NB>;
   __shared__ __align__(1024) unsigned short sK[NB][32 * D], sV[NB][32 * D];
   __shared__ int sN[NB];  // valid rows of the slice in each buffer (0 = past the end)
+  __shared__ int sR[NB];  // its first key row (sequence-local)
   __shared__ int sList[kListChunk];
 
   const int tid = threadIdx.x;
@@ -971,10 +1004,13 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
     Slice sl;
     if (!walk.next(p, si.len_kv, sl, tid, 64 * W)) sl = Slice{0, 0, 0};
     Ring::issue(sK[slot], sV[slot], sl, kp, vp, p.kv_sr, p.consts, w, lane);
-    if (tid == 0) sN[slot] = sl.nrows;
+    if (tid == 0) {
+      sN[slot] = sl.nrows;
+      sR[slot] = sl.row0;
+    }
   };
 
-  auto compute = [&](const unsigned short* tk, const unsigned short* tv, int nrows) {
+  auto compute = [&](const unsigned short* tk, const unsigned short* tv, int nrows, int row0) {
     f32x16 st = {}, dpt = {};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
@@ -982,14 +1018,15 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
       dpt = E::mma(frag_along_row<D>(tv, 0, 16 * ks, lane), oreg[ks], dpt); // dP^T[kv][q]
     }
     float dsv[16];
-    if (nrows == 32) {  // uniform: full slices need no row mask
+    if (nrows == 32 && rect_in_band(p, q0 + 32 * w, 32, row0, 32)) {  // uniform: no mask needed
 #pragma unroll
       for (int i = 0; i < 16; ++i) dsv[i] = fast_exp2(st[i] * c2 - l2) * (dpt[i] - dl);
     } else {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int kv = 8 * (i >> 2) + 4 * g + (i & 3);  // this register's key row in the slice
-        const float x = kv < nrows ? fast_exp2(st[i] * c2 - l2) : 0.f;
+        const bool on = kv < nrows && (!p.win || in_band(p, my_q, row0 + kv));
+        const float x = on ? fast_exp2(st[i] * c2 - l2) : 0.f;  // a select: l2 may be -inf off the window
         dsv[i] = x * (dpt[i] - dl);
       }
     }
@@ -1013,7 +1050,7 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
   for (int t = 0; nrows > 0;) {  // nrows is uniform; 0 once the walk is over
     const int cur = t % NB;
     issue((t + NB - 1) % NB);
-    compute(sK[cur], sV[cur], nrows);
+    compute(sK[cur], sV[cur], nrows, sR[cur]);
     ++t;
     wait_vmcnt<Ring::WAIT>();
     __syncthreads();
@@ -1063,6 +1100,7 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
   using Ring = KVRing<D, W, NB>;
   __shared__ __align__(1024) unsigned short sK[NB][32 * D], sV[NB][32 * D];
   __shared__ int sN[NB];  // valid rows of the slice in each buffer (0 = past the end)
+  __shared__ int sR[NB];  // its first key row (sequence-local)
   __shared__ int sList[kListChunk];
 
   const int tid = threadIdx.x;
@@ -1114,17 +1152,20 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
     Slice sl;
     if (!walk.next(p, si.len_kv, sl, tid, 64 * W)) sl = Slice{0, 0, 0};
     Ring::issue(sK[slot], sV[slot], sl, kp, vp, p.kv_sr, p.consts, w, lane);
-    if (tid == 0) sN[slot] = sl.nrows;
+    if (tid == 0) {
+      sN[slot] = sl.nrows;
+      sR[slot] = sl.row0;
+    }
   };
 
-  auto compute = [&](const unsigned short* tk, const unsigned short* tv, int nrows) {
+  auto compute = [&](const unsigned short* tk, const unsigned short* tv, int nrows, int row0) {
     f32x16 st = {};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
       st = E::mma(frag_along_row<D>(tk, 0, 16 * ks, lane), qreg[ks], st);  // S^T[kv][q]
     float x[16];
     float mx = -__builtin_inff();
-    if (nrows == 32) {  // uniform: full slices need no row mask
+    if (nrows == 32 && rect_in_band(p, q0 + 32 * w, 32, row0, 32)) {  // uniform: no mask needed
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         x[i] = st[i] * c2;  // scaled score in log2 units
@@ -1134,7 +1175,8 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int kv = 8 * (i >> 2) + 4 * g + (i & 3);  // this register's key row in the slice
-        x[i] = kv < nrows ? st[i] * c2 : -__builtin_inff();
+        const bool on = kv < nrows && (!p.win || in_band(p, my_q, row0 + kv));
+        x[i] = on ? st[i] * c2 : -__builtin_inff();
         mx = fmaxf(mx, x[i]);
       }
     }
@@ -1174,7 +1216,7 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
   for (int t = 0; nrows > 0;) {
     const int cur = t % NB;
     issue((t + NB - 1) % NB);
-    compute(sK[cur], sV[cur], nrows);
+    compute(sK[cur], sV[cur], nrows, sR[cur]);
     ++t;
     wait_vmcnt<Ring::WAIT>();
     __syncthreads();

@@ -12,8 +12,9 @@
  *     dQ             = (dS * K) * scale
  *     dK             = (dS^T * Q) * scale
  * where the block mask picks, for every Q block of blockShape[0] rows, the KV
- * blocks of blockShape[1] rows that take part; everything outside the selected
- * blocks is excluded from the softmax and contributes nothing.  With GQA, query
+ * blocks of blockShape[1] rows that take part (and an optional sliding window
+ * further restricts each row to a band of keys); everything outside is
+ * excluded from the softmax and contributes nothing.  With GQA, query
  * head n reads KV head n / (N / Nkv) and dK/dV sum over the query heads of a
  * group (in ascending head order, so results are run-to-run bitwise identical).
  *
@@ -98,7 +99,13 @@ typedef struct bsa_tensor {
  *  num_key_value_heads         Nkv; N >= Nkv and N % Nkv == 0 (约束说明).
  *  mask_type                   reserved: must be 0.
  *  scale_value                 the scale (typically D^-0.5); finite.
- *  pre_tokens, next_tokens     reserved: must be 2147483647.
+ *  pre_tokens, next_tokens     sliding window (参数说明 preTokens / nextTokens: how
+ *                              many earlier / later tokens a token may attend to):
+ *                              key j takes part for query i only if
+ *                              i - pre_tokens <= j <= i + next_tokens, positions
+ *                              sequence-local from 0.  Both 2147483647 = no window;
+ *                              any int64 otherwise (a window that leaves a row no
+ *                              key gives that row LSE = -inf and zero outputs).
  *  dq, dk, dv                  outputs, same dtype/shape as query/key/value;
  *                              any outer strides, innermost stride 1.
  *  workspace_size              out: bytes of device workspace needed.

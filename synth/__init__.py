@@ -133,6 +133,9 @@ class Case:
     v: np.ndarray
     do: np.ndarray
     seed: int
+    # (preTokens, nextTokens) of a sliding window, or None for none; a
+    # parameter handed to both sides unchanged
+    window: Optional[tuple] = None
 
     @property
     def G(self) -> int:
@@ -204,6 +207,7 @@ def make_case(
     scale: Optional[float] = None,
     seed: int = 0,
     name: str = "custom",
+    window: Optional[tuple] = None,
 ) -> Case:
     """Draw one case.
 
@@ -256,7 +260,7 @@ def make_case(
     return Case(
         name=name, layout=layout, dtype=dtype, B=B, N=N, Nkv=Nkv, D=D, Sq=Sq, Skv=Skv,
         bx=bx, by=by, scale=float(scale), len_q=lq, len_kv=lk, explicit_lengths=explicit,
-        mask=mask, q=q, k=k, v=v, do=do, seed=seed,
+        mask=mask, q=q, k=k, v=v, do=do, seed=seed, window=window,
     )
 
 

@@ -53,6 +53,22 @@ def case(name):
                                                      mask_rule="local8_sink2",
                                                      lengths_q=[1000, 700], lengths_kv=[1000, 650],
                                                      seed=112),
+        # sliding windows (preTokens, nextTokens): a band wider than a block, GQA, ragged
+        "bnsd_bf16_d128_window": lambda: mk(layout="BNSD", dtype="bf16", B=2, N=4, Nkv=2, D=128, Sq=384,
+                                            Skv=320, bx=64, by=64, p=0.6, window=(100, 20), seed=116),
+        # a band that excludes the diagonal (rows past the last keys are left empty), TND
+        "tnd_fp16_d64_window_ahead": lambda: mk(layout="TND", dtype="fp16", B=2, N=4, Nkv=1, D=64, bx=32,
+                                                by=64, p=0.7, lengths_q=[150, 97], lengths_kv=[130, 200],
+                                                window=(-3, 60), seed=117),
+        # zero-width window (each row sees its own key only), 128-row blocks
+        "bnsd_fp16_d128_window_zero": lambda: mk(layout="BNSD", dtype="fp16", B=1, N=2, Nkv=1, D=128,
+                                                 Sq=256, Skv=256, bx=128, by=128, mask_rule="ones",
+                                                 window=(0, 0), seed=118),
+        # local window on top of the sink pattern: split units and element masks together
+        "bnsd_bf16_d128_window_sink_split": lambda: mk(layout="BNSD", dtype="bf16", B=1, N=4, Nkv=1,
+                                                       D=128, Sq=1024, Skv=1024, bx=64, by=64,
+                                                       mask_rule="local8_sink2", window=(300, 0),
+                                                       seed=119),
     }
     return cases[name]()
 
@@ -61,5 +77,6 @@ SMALL = ["config1", "bnsd_bf16_d128_b128x128_ragged", "bnsd_fp16_d64_b64x128_pad
          "tnd_fp16_d128_b64x128_gqa", "bnsd_bf16_d128_b128x64", "bnsd_bf16_d64_b48x80",
          "bnsd_fp16_d128_b256x256", "bnsd_bf16_d64_b1x1", "bnsd_bf16_d128_nullmask",
          "tnd_bf16_d64_empty_seqs", "bnsd_fp16_d128_sparse_rows", "bnsd_bf16_d128_local_sink_split",
-         "bnsd_fp16_d64_sink_split_parts"]
+         "bnsd_fp16_d64_sink_split_parts", "bnsd_bf16_d128_window", "tnd_fp16_d64_window_ahead",
+         "bnsd_fp16_d128_window_zero", "bnsd_bf16_d128_window_sink_split"]
 

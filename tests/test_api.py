@@ -182,8 +182,10 @@ CASES = [
     # reserved attributes
     ("attenMask given", lambda: _mut(_bnsd, atten_mask=torch.zeros(300, 270, dtype=torch.bool)), INVALID),
     ("maskType 1", lambda: _mut(_bnsd, mask_type=1), INVALID),
-    ("preTokens", lambda: _mut(_bnsd, pre_tokens=1024), INVALID),
-    ("nextTokens", lambda: _mut(_bnsd, next_tokens=0), INVALID),
+    # a sliding window (preTokens / nextTokens other than 2147483647) is accepted
+    ("preTokens window", lambda: _mut(_bnsd, pre_tokens=1024), bsa.BSA_OK),
+    ("nextTokens window", lambda: _mut(_bnsd, next_tokens=0), bsa.BSA_OK),
+    ("negative window", lambda: _mut(_bnsd, pre_tokens=-5, next_tokens=2**40), bsa.BSA_OK),
     ("scale NaN", lambda: _mut(_bnsd, scale_value=float("nan")), INVALID),
     # strides
     ("non-contiguous query", lambda: _mut(_bnsd, query=_tr(torch.zeros(2, 4, 300, 128, dtype=torch.bfloat16))), INVALID),
@@ -316,7 +318,7 @@ FWD_CASES = [
     ("LSE fp16", lambda: _fwd(softmax_lse=torch.zeros(2, 4, 300, dtype=torch.float16)), INVALID),
     ("LSE non-contiguous", lambda: _fwd(softmax_lse=torch.zeros(2, 300, 4).transpose(1, 2)), INVALID),
     ("LSE shape", lambda: _fwd(softmax_lse=torch.zeros(2, 4, 299)), INVALID),
-    ("sliding window", lambda: _fwd(pre_tokens=64), INVALID),
+    ("sliding window", lambda: _fwd(pre_tokens=64, next_tokens=0), bsa.BSA_OK),
     ("TND without lengths", lambda: _fwd(_tnd, actual_seq_lengths=None), NULLPTR),
 ]
 

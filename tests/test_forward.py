@@ -44,7 +44,9 @@ def _run_fwd(c, out=None):
               actual_seq_lengths=list(map(int, c.len_q)) if lengths else None,
               actual_seq_lengths_kv=list(map(int, c.len_kv)) if lengths else None,
               q_input_layout=c.layout, kv_input_layout=c.layout, num_key_value_heads=c.Nkv,
-              mask_type=0, scale_value=c.scale, pre_tokens=bsa.NO_WINDOW, next_tokens=bsa.NO_WINDOW,
+              mask_type=0, scale_value=c.scale,
+              pre_tokens=bsa.NO_WINDOW if c.window is None else c.window[0],
+              next_tokens=bsa.NO_WINDOW if c.window is None else c.window[1],
               attention_out=o, softmax_lse=lse)
     ws = bsa.bsa_fwd_workspace_size(dev["q"], dev["k"], dev["v"], **kw)
     wbuf = torch.empty(max(ws, 1), dtype=torch.uint8, device="cuda")

@@ -69,7 +69,7 @@ def test_block_lists_bit_exact(name):
     _, r = run_bsa(c, dev)
     torch.cuda.synchronize()
     offs, (bx, by, nqb, nkb) = bsa.bsa_bwd_workspace_layout(*r.args, **r.kw)
-    rows, cols = oracle.block_lists(c.mask, c.B, c.N, nqb, nkb, bx, by, c.len_q, c.len_kv)
+    rows, cols = oracle.block_lists(c.mask, c.B, c.N, nqb, nkb, bx, by, c.len_q, c.len_kv, window=c.window)
     rc = _read_ws(r, offs, "row_cnt", c.B * c.N * nqb).reshape(c.B, c.N, nqb)
     rl = _read_ws(r, offs, "row_list", c.B * c.N * nqb * nkb).reshape(c.B, c.N, nqb, nkb)
     cc = _read_ws(r, offs, "col_cnt", c.B * c.N * nkb).reshape(c.B, c.N, nkb)
