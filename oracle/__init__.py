@@ -22,6 +22,10 @@ Parity status of each function (what pins it, in ``tests/test_oracle.py``):
   the zero-width-window closed form, slab path == dense path (with rows the
   window leaves empty), the block lists against an interval formula, and the
   row-sampled helpers.
+* the attenMask (``atten_mask``, ``allowed_pairs``; same file): torch fp64 autograd on
+  a hand-built element mask (alone and with a window), finite differences (TND,
+  with a window), slab path == dense path with a row the mask empties, and the
+  row-sampled helpers.
 
 No function here is "parity unpinned".
 """

@@ -45,6 +45,10 @@ design notes):
   window.  A block stays in the lists only if the block mask selects it and at
   least one of its in-range elements lies in the window.  A query row that
   the window leaves no key has LSE = -inf and zero O and dQ.
+* attenMask (参数说明 attenMaskOptional, BOOL, 2 dims; the FlashAttentionScore
+  page's polarity, 1 = the pair does not take part): ``atten_mask`` is
+  ``[maxSq, maxSkv]``, shared by every batch and head and indexed by
+  sequence-local positions; it removes pairs without changing the block lists.
 
 Everything is computed in float64 from the exact input values (fp16/bf16
 values upcast, the given fp32 LSE upcast).  The work is organised per
@@ -63,6 +67,7 @@ import numpy as np
 __all__ = [
     "sequence_offsets",
     "in_window",
+    "allowed_pairs",
     "element_mask",
     "block_lists",
     "softmax_grad",
@@ -135,10 +140,18 @@ def in_window(rows: np.ndarray, cols: np.ndarray, window) -> np.ndarray:
     return (d >= -pre) & (d <= nxt)
 
 
+def allowed_pairs(rows, cols, window=None, atten_mask=None) -> np.ndarray:
+    """[len(rows), len(cols)] bool: pairs the window and the attenMask leave in."""
+    ok = in_window(rows, cols, window)
+    if atten_mask is not None:
+        ok &= np.asarray(atten_mask)[np.ix_(np.asarray(rows, np.int64), np.asarray(cols, np.int64))] == 0
+    return ok
+
+
 def element_mask(block_mask_bn: Optional[np.ndarray], bx: int, by: int, lq: int, lkv: int,
-                 window=None) -> np.ndarray:
+                 window=None, atten_mask=None) -> np.ndarray:
     """Element mask [lq, lkv] of one (batch, head): M[i, j] = mask[i // bx, j // by] != 0,
-    and (i, j) in the window.
+    (i, j) in the window, and atten_mask[i, j] == 0.
 
     ``None`` (no block mask) selects every pair.  Rows and columns past the
     sequence's lengths do not exist in the result.
@@ -150,7 +163,7 @@ def element_mask(block_mask_bn: Optional[np.ndarray], bx: int, by: int, lq: int,
         for i in range(lq):
             for j in range(lkv):
                 m[i, j] = block_mask_bn[i // bx, j // by] != 0
-    return m & in_window(np.arange(lq), np.arange(lkv), window)
+    return m & allowed_pairs(np.arange(lq), np.arange(lkv), window, atten_mask)
 
 
 def _selected_blocks(block_mask_bn: Optional[np.ndarray], ib: int, nkb_b: int) -> List[int]:
@@ -207,7 +220,7 @@ def _slab_columns(block_mask_bn, ib, by, lkv):
     return np.concatenate(cols)
 
 
-def _head_forward(q, k, v, bm, bx, by, scale, window=None):
+def _head_forward(q, k, v, bm, bx, by, scale, window=None, atten_mask=None):
     """Forward of one (batch, query head): O [lq, D], LSE [lq] (fp64)."""
     lq, lkv = q.shape[0], k.shape[0]
     o = np.zeros_like(q)
@@ -217,8 +230,8 @@ def _head_forward(q, k, v, bm, bx, by, scale, window=None):
         cols = _slab_columns(bm, ib, by, lkv)
         if cols.size == 0:
             continue
-        allowed = in_window(r, cols, window)
-        live = allowed.any(axis=1)          # rows the window leaves some key
+        allowed = allowed_pairs(r, cols, window, atten_mask)
+        live = allowed.any(axis=1)          # rows the window / attenMask leave some key
         if not live.any():
             continue
         rl, al = r[live], allowed[live]
@@ -230,7 +243,7 @@ def _head_forward(q, k, v, bm, bx, by, scale, window=None):
     return o, lse
 
 
-def _head_backward(q, k, v, o, do, lse, bm, bx, by, scale, window=None):
+def _head_backward(q, k, v, o, do, lse, bm, bx, by, scale, window=None, atten_mask=None):
     """Backward of one (batch, query head): dQ, and this head's dK, dV terms."""
     lq, lkv = q.shape[0], k.shape[0]
     delta = softmax_grad(do, o)
@@ -242,7 +255,7 @@ def _head_backward(q, k, v, o, do, lse, bm, bx, by, scale, window=None):
         cols = _slab_columns(bm, ib, by, lkv)
         if cols.size == 0:
             continue
-        allowed = in_window(np.arange(rows.start, rows.stop), cols, window)
+        allowed = allowed_pairs(np.arange(rows.start, rows.stop), cols, window, atten_mask)
         s = scale * (q[rows] @ k[cols].T)          # S
         with np.errstate(over="ignore", invalid="ignore"):  # P, recomputed from the LSE, 0 off the window
             p = np.where(allowed, np.exp(np.where(allowed, s - lse[rows, None], 0.0)), 0.0)
@@ -286,7 +299,7 @@ def _lengths(layout, q, k, len_q, len_kv):
     return lq, lk
 
 
-def forward(q, k, v, mask, *, layout, bx, by, scale, len_q=None, len_kv=None, window=None):
+def forward(q, k, v, mask, *, layout, bx, by, scale, len_q=None, len_kv=None, window=None, atten_mask=None):
     """Masked attention forward: O (q's layout) and LSE ([B,N,S] or [T,N]), fp64."""
     _, N, Nkv, _ = _dims(q, k, layout)
     G = _check_heads(N, Nkv)
@@ -303,13 +316,14 @@ def forward(q, k, v, mask, *, layout, bx, by, scale, len_q=None, len_kv=None, wi
         lb = np.full((N, Lq), -np.inf)
         for n in range(N):
             bm = None if mask is None else mask[b, n]
-            ob[n], lb[n] = _head_forward(qs[n], ks[n // G], vs[n // G], bm, bx, by, scale, window)
+            ob[n], lb[n] = _head_forward(qs[n], ks[n // G], vs[n // G], bm, bx, by, scale, window, atten_mask)
         _put(o, ob, layout, b, Lq, offq[b])
         _put_lse(lse, lb, layout, b, Lq, offq[b])
     return o, lse
 
 
-def backward(q, k, v, o, do, lse, mask, *, layout, bx, by, scale, len_q=None, len_kv=None, window=None):
+def backward(q, k, v, o, do, lse, mask, *, layout, bx, by, scale, len_q=None, len_kv=None, window=None,
+             atten_mask=None):
     """dQ, dK, dV (fp64, in the inputs' layouts) of block-sparse attention."""
     _, N, Nkv, _ = _dims(q, k, layout)
     G = _check_heads(N, Nkv)
@@ -332,7 +346,8 @@ def backward(q, k, v, o, do, lse, mask, *, layout, bx, by, scale, len_q=None, le
         for n in range(N):
             h = n // G
             bm = None if mask is None else mask[b, n]
-            dqn, dkn, dvn = _head_backward(qs[n], ks[h], vs[h], os_[n], dos[n], ls[n], bm, bx, by, scale, window)
+            dqn, dkn, dvn = _head_backward(qs[n], ks[h], vs[h], os_[n], dos[n], ls[n], bm, bx, by, scale, window,
+                                           atten_mask)
             dqb[n] = dqn
             dkb[h] += dkn
             dvb[h] += dvn
@@ -345,7 +360,8 @@ def backward(q, k, v, o, do, lse, mask, *, layout, bx, by, scale, len_q=None, le
 # ---------------------------------------------------------------------------
 # literal dense versions (tiny shapes): full element mask, full matrices
 # ---------------------------------------------------------------------------
-def forward_dense(q, k, v, mask, *, layout, bx, by, scale, len_q=None, len_kv=None, window=None):
+def forward_dense(q, k, v, mask, *, layout, bx, by, scale, len_q=None, len_kv=None, window=None,
+                  atten_mask=None):
     """Same as ``forward`` but on the full [Lq, Lkv] element mask."""
     _, N, Nkv, _ = _dims(q, k, layout)
     G = _check_heads(N, Nkv)
@@ -362,7 +378,7 @@ def forward_dense(q, k, v, mask, *, layout, bx, by, scale, len_q=None, len_kv=No
         lb = np.full((N, Lq), -np.inf)
         for n in range(N):
             h = n // G
-            m = element_mask(None if mask is None else mask[b, n], bx, by, Lq, Lk, window)
+            m = element_mask(None if mask is None else mask[b, n], bx, by, Lq, Lk, window, atten_mask)
             s = np.where(m, scale * (qs[n] @ ks[h].T), -np.inf)
             for i in range(Lq):
                 if m[i].any():
@@ -376,7 +392,7 @@ def forward_dense(q, k, v, mask, *, layout, bx, by, scale, len_q=None, len_kv=No
 
 
 def backward_dense(q, k, v, o, do, lse, mask, *, layout, bx, by, scale, len_q=None, len_kv=None,
-                   window=None):
+                   window=None, atten_mask=None):
     """Same as ``backward`` but on the full [Lq, Lkv] element mask."""
     _, N, Nkv, _ = _dims(q, k, layout)
     G = _check_heads(N, Nkv)
@@ -398,7 +414,7 @@ def backward_dense(q, k, v, o, do, lse, mask, *, layout, bx, by, scale, len_q=No
         dvb = np.zeros_like(vs)
         for n in range(N):
             h = n // G
-            m = element_mask(None if mask is None else mask[b, n], bx, by, Lq, Lk, window)
+            m = element_mask(None if mask is None else mask[b, n], bx, by, Lq, Lk, window, atten_mask)
             delta = softmax_grad(dos[n], os_[n])
             s = scale * (qs[n] @ ks[h].T)
             with np.errstate(over="ignore", invalid="ignore"):
@@ -441,7 +457,8 @@ def _lse_rows(lse, layout, b, n, rows, off):
 
 
 def backward_dq_rows(q, k, v, o, do, lse, mask, *, layout, bx, by, scale, len_q=None, len_kv=None,
-                     rows: Iterable[Tuple[int, int, int]] = (), window=None) -> Dict[Tuple[int, int, int], np.ndarray]:
+                     rows: Iterable[Tuple[int, int, int]] = (), window=None,
+                     atten_mask=None) -> Dict[Tuple[int, int, int], np.ndarray]:
     """dQ rows for ``(b, n, i)`` triples (sequence-local i), fp64 [D] each.
 
     Row i of head n sums over the columns of the KV blocks its Q-block selects.
@@ -460,7 +477,7 @@ def backward_dq_rows(q, k, v, o, do, lse, mask, *, layout, bx, by, scale, len_q=
         h = n // G
         bm = None if mask is None else mask[b, n]
         cols = _slab_columns(bm, i // bx, by, Lk)
-        cols = cols[in_window([i], cols, window)[0]]
+        cols = cols[allowed_pairs([i], cols, window, atten_mask)[0]]
         if cols.size == 0:
             out[(b, n, i)] = np.zeros(D)
             continue
@@ -479,7 +496,7 @@ def backward_dq_rows(q, k, v, o, do, lse, mask, *, layout, bx, by, scale, len_q=
 
 
 def backward_dkdv_rows(q, k, v, o, do, lse, mask, *, layout, bx, by, scale, len_q=None, len_kv=None,
-                       rows: Iterable[Tuple[int, int, int]] = (), window=None):
+                       rows: Iterable[Tuple[int, int, int]] = (), window=None, atten_mask=None):
     """dK and dV rows for ``(b, h, j)`` triples (sequence-local j), fp64 [D] each.
 
     Key j of KV head h sums over every query head n of its group and every row
@@ -505,7 +522,7 @@ def backward_dkdv_rows(q, k, v, o, do, lse, mask, *, layout, bx, by, scale, len_
                     if bm is not None and bm[ib, j // by] == 0:
                         continue
                     rr = np.arange(ib * bx, min(ib * bx + bx, Lq))
-                    rr = rr[in_window(rr, [j], window)[:, 0]]
+                    rr = rr[allowed_pairs(rr, [j], window, atten_mask)[:, 0]]
                     if rr.size == 0:
                         continue
                     qr = _rows_of(q, layout, b, n, rr, offq[b])

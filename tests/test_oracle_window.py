@@ -156,3 +156,84 @@ def test_window_sampled_rows_equal_full_backward(window):
     for (b, h, j) in rk:
         np.testing.assert_allclose(gk[(b, h, j)], dk[b, h, j], rtol=0, atol=1e-13)
         np.testing.assert_allclose(gv[(b, h, j)], dv[b, h, j], rtol=0, atol=1e-13)
+
+
+# ---------------------------------------------------------------------------
+# attenMask (1 = the pair does not take part), alone and with a window
+# ---------------------------------------------------------------------------
+def _atten(rng, sq, sk, p=0.3):
+    return (rng.random((sq, sk)) < p).astype(np.uint8)
+
+
+@pytest.mark.parametrize("window", [None, (4, 3)])
+def test_atten_mask_equals_torch_autograd_with_explicit_mask(window):
+    B, N, Nkv, Sq, Skv, D, bx, by = 1, 2, 1, 17, 21, 8, 4, 8
+    c = synth.make_case(layout="BNSD", dtype="bf16", B=B, N=N, Nkv=Nkv, D=D, Sq=Sq, Skv=Skv, bx=bx, by=by,
+                        mask_rule="ones", seed=121)
+    rng = np.random.default_rng(9)
+    am = _atten(rng, Sq, Skv)
+    am[np.arange(Sq), np.arange(Sq)] = 0  # keep each row's own position, so torch's softmax is defined
+    em = np.ones((B, N, Sq, Skv), dtype=bool) & (am == 0)[None, None]
+    if window is not None:
+        em &= _band(Sq, Skv, *window)[None, None]
+    assert em.any(axis=-1).all()
+    kw = dict(_kw(c), window=window, atten_mask=am)
+    o, lse = oracle.forward(c.q, c.k, c.v, c.mask, **kw)
+    t_o, t_lse, t_dq, t_dk, t_dv = _torch_reference(c.q, c.k, c.v, c.do, c.scale, c.G, elem_mask=em)
+    np.testing.assert_allclose(o, t_o, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse, t_lse, rtol=0, atol=1e-12)
+    dq, dk, dv = oracle.backward(c.q, c.k, c.v, o, c.do, lse, c.mask, **kw)
+    for a, b in ((dq, t_dq), (dk, t_dk), (dv, t_dv)):
+        np.testing.assert_allclose(a, b, rtol=0, atol=1e-11 * max(1.0, np.abs(b).max()))
+
+
+def test_atten_mask_finite_differences():
+    c = synth.make_case(layout="TND", dtype="fp16", B=2, N=2, Nkv=1, D=3, bx=2, by=3, p=0.7,
+                        lengths_q=[5, 4], lengths_kv=[6, 5], scale=0.7, seed=122)
+    am = _atten(np.random.default_rng(4), 5, 6, 0.4)
+    kw = dict(layout=c.layout, bx=c.bx, by=c.by, scale=c.scale, len_q=c.len_q, len_kv=c.len_kv,
+              atten_mask=am, window=(3, 2))
+    o, lse = oracle.forward(c.q, c.k, c.v, c.mask, **kw)
+    dq, dk, dv = oracle.backward(c.q, c.k, c.v, o, c.do, lse, c.mask, **kw)
+    dof = c.do.astype(np.float64)
+    h = 1e-6
+    base = [c.q.astype(np.float64), c.k.astype(np.float64), c.v.astype(np.float64)]
+    for which, grad in enumerate((dq, dk, dv)):
+        x = base[which]
+        fd = np.zeros_like(x)
+        it = np.nditer(x, flags=["multi_index"])
+        for _ in it:
+            idx = it.multi_index
+            ap = [a.copy() for a in base]
+            am_ = [a.copy() for a in base]
+            ap[which][idx] += h
+            am_[which][idx] -= h
+            fd[idx] = (float(np.sum(dof * oracle.forward(*ap, c.mask, **kw)[0]))
+                       - float(np.sum(dof * oracle.forward(*am_, c.mask, **kw)[0]))) / (2 * h)
+        assert np.abs(fd - grad).max() <= 1e-7 * max(1.0, np.abs(fd).max()), which
+
+
+def test_atten_mask_slab_equals_dense_and_rows():
+    """Including rows the attenMask empties (LSE = -inf, zero O and dQ)."""
+    c = synth.make_case(layout="BNSD", dtype="bf16", B=1, N=4, Nkv=2, D=8, Sq=20, Skv=18, bx=4, by=6,
+                        p=0.6, seed=123)
+    am = _atten(np.random.default_rng(5), 20, 18, 0.5)
+    am[3, :] = 1  # row 3 loses every key
+    kw = dict(_kw(c), atten_mask=am)
+    o, lse = oracle.forward(c.q, c.k, c.v, c.mask, **kw)
+    od, lsed = oracle.forward_dense(c.q, c.k, c.v, c.mask, **kw)
+    np.testing.assert_allclose(o, od, rtol=0, atol=1e-13)
+    assert np.all(np.isneginf(lse[:, :, 3])) and np.all(o[:, :, 3] == 0)
+    g = oracle.backward(c.q, c.k, c.v, o, c.do, lse, c.mask, **kw)
+    gd = oracle.backward_dense(c.q, c.k, c.v, o, c.do, lse, c.mask, **kw)
+    for a, b in zip(g, gd):
+        np.testing.assert_allclose(a, b, rtol=0, atol=1e-12 * max(1.0, np.abs(b).max()))
+    rq = [(0, n, i) for n in range(4) for i in range(20)]
+    got = oracle.backward_dq_rows(c.q, c.k, c.v, o, c.do, lse, c.mask, rows=rq, **kw)
+    for (b, n, i), r in got.items():
+        np.testing.assert_allclose(r, g[0][b, n, i], rtol=0, atol=1e-13)
+    rk = [(0, h, j) for h in range(2) for j in range(18)]
+    gk, gv = oracle.backward_dkdv_rows(c.q, c.k, c.v, o, c.do, lse, c.mask, rows=rk, **kw)
+    for (b, h, j) in rk:
+        np.testing.assert_allclose(gk[(b, h, j)], g[1][b, h, j], rtol=0, atol=1e-13)
+        np.testing.assert_allclose(gv[(b, h, j)], g[2][b, h, j], rtol=0, atol=1e-13)
