@@ -61,6 +61,8 @@ def to_device(case, device="cuda"):
         "v": torch.from_numpy(case.v).to(device=device).to(dt),
         "do": torch.from_numpy(case.do).to(device=device).to(dt),
         "mask": None if case.mask is None else torch.from_numpy(case.mask).to(device),
+        "amask": (None if case.atten_mask is None
+                  else torch.from_numpy(np.ascontiguousarray(case.atten_mask, np.uint8)).to(device)),
     }
     return d
 
@@ -112,6 +114,8 @@ def gpu_forward(case, dev, rows_per_chunk=2048):
                     mb = mask[b, n, ib0:ib1, :nkb_b].bool()
                     em = mb.repeat_interleave(bx, dim=0)[: r1 - r0].repeat_interleave(by, dim=1)[:, :lk]
                     s.masked_fill_(~em, float("-inf"))
+                if dev.get("amask") is not None and lk > 0:  # attenMask: 1 = the pair is left out
+                    s.masked_fill_(dev["amask"][r0:r1, :lk].bool(), float("-inf"))
                 if case.window is not None and lk > 0:  # sliding window: i - pre <= j <= i + next
                     d = (torch.arange(lk, device=s.device)[None, :]
                          - torch.arange(r0, r1, device=s.device)[:, None])
@@ -141,7 +145,7 @@ class Runner:
         self.dv = torch.empty_like(dev["v"])
         lengths = case.explicit_lengths or case.layout == "TND"
         self.kw = dict(
-            block_sparse_mask=dev["mask"], atten_mask=None, block_shape=[case.bx, case.by],
+            block_sparse_mask=dev["mask"], atten_mask=dev.get("amask"), block_shape=[case.bx, case.by],
             actual_seq_lengths=list(map(int, case.len_q)) if lengths else None,
             actual_seq_lengths_kv=list(map(int, case.len_kv)) if lengths else None,
             q_input_layout=case.layout, kv_input_layout=case.layout, num_key_value_heads=case.Nkv,
@@ -169,7 +173,7 @@ class FwdRunner:
         self.lse = torch.empty(dev["q"].shape[:-1], dtype=torch.float32, device=dev["q"].device)
         lengths = case.explicit_lengths or case.layout == "TND"
         self.kw = dict(
-            block_sparse_mask=dev["mask"], atten_mask=None, block_shape=[case.bx, case.by],
+            block_sparse_mask=dev["mask"], atten_mask=dev.get("amask"), block_shape=[case.bx, case.by],
             actual_seq_lengths=list(map(int, case.len_q)) if lengths else None,
             actual_seq_lengths_kv=list(map(int, case.len_kv)) if lengths else None,
             q_input_layout=case.layout, kv_input_layout=case.layout, num_key_value_heads=case.Nkv,

@@ -166,7 +166,10 @@ int make_plan(const Args& a, Plan* plan) {
                 dtype_name(a.block_sparse_mask->dtype));
 
   // ---- reserved attributes ------------------------------------------------
-  if (a.atten_mask != nullptr) return fail(BSA_ERR_PARAM_INVALID, "attenMask is not supported and must be null");
+  if (a.atten_mask != nullptr && a.atten_mask->data == nullptr)
+    return fail(BSA_ERR_PARAM_NULLPTR, "attenMask has a null data pointer");
+  if (a.atten_mask != nullptr && a.atten_mask->dtype != BSA_DTYPE_BOOL)
+    return fail(BSA_ERR_PARAM_INVALID, "attenMask dtype %s is not bool/uint8", dtype_name(a.atten_mask->dtype));
   if (a.mask_type != 0) return fail(BSA_ERR_PARAM_INVALID, "maskType %lld is not supported (only 0)",
                                     static_cast<long long>(a.mask_type));
 
@@ -326,6 +329,15 @@ int make_plan(const Args& a, Plan* plan) {
                   static_cast<long long>(nkb));
     if (!row_major_contiguous(m)) return fail(BSA_ERR_PARAM_INVALID, "blockSparseMask is not contiguous");
   }
+  if (a.atten_mask != nullptr) {  // [maxSq, maxSkv], sequence-local positions
+    const bsa_tensor* m = a.atten_mask;
+    int rc = check_dims(m, "attenMask");
+    if (rc) return rc;
+    if (m->ndim != 2 || m->shape[0] != Sq || m->shape[1] != Skv)
+      return fail(BSA_ERR_PARAM_INVALID, "attenMask shape must be [maxSq, maxSkv] = [%lld, %lld]",
+                  static_cast<long long>(Sq), static_cast<long long>(Skv));
+    if (!row_major_contiguous(m)) return fail(BSA_ERR_PARAM_INVALID, "attenMask is not contiguous");
+  }
   if (B * N * nqb * nkb > kInt32Max) return fail(BSA_ERR_PARAM_INVALID, "block grid too large for int32 lists");
   const int64_t nsub_q = ceil_div(bx, 128), nsub_kv = ceil_div(by, 128);
   if (B * N * nqb * nsub_q + bsa::kMaxSlots > bsa::kMaxGridGroups ||
@@ -342,6 +354,8 @@ int make_plan(const Args& a, Plan* plan) {
   p.k = a.key->data;
   p.v = a.value->data;
   p.mask = a.block_sparse_mask ? static_cast<const uint8_t*>(a.block_sparse_mask->data) : nullptr;
+  p.amask = a.atten_mask ? static_cast<const uint8_t*>(a.atten_mask->data) : nullptr;
+  p.amask_ld = Skv;
   if (a.fwd) {
     p.out_o = a.attention_out->data;
     p.out_lse = static_cast<float*>(a.softmax_lse->data);
@@ -508,6 +522,7 @@ int run(const Args& a, void* workspace, uint64_t workspace_size, void* stream) {
   const Ptr ptrs[] = {{a.dout, "dout"}, {a.query, "query"}, {a.key, "key"},
                       {a.value, "value"}, {a.attention_out, "attentionOut"},
                       {a.softmax_lse, "softmaxLse"}, {a.block_sparse_mask, "blockSparseMask"},
+                      {a.atten_mask, "attenMask"},
                       {a.dq, "dq"}, {a.dk, "dk"}, {a.dv, "dv"}};
   for (const Ptr& q : ptrs) {
     if (q.t == nullptr || q.t->data == nullptr) continue;

@@ -51,6 +51,9 @@ struct Params {
   // sliding window: key j takes part for query i only if i - win_pre <= j <= i + win_next
   // (sequence-local positions); win == 0 means no window
   int32_t win, win_pre, win_next;
+  // attenMask [maxSq, maxSkv] bytes, 1 = the pair does not take part (nullptr: none)
+  const uint8_t* amask;
+  int64_t amask_ld;
   float scale;         // scale_value rounded to fp32
   float scale_log2e;   // scale * log2(e)
 

@@ -95,6 +95,10 @@ __device__ __forceinline__ bool in_band(const Params& p, int i, int j) {
 __device__ __forceinline__ bool rect_in_band(const Params& p, int r0, int nr, int c0, int nc) {
   return !p.win || (c0 - (r0 + nr - 1) >= -p.win_pre && (c0 + nc - 1) - r0 <= p.win_next);
 }
+// attenMask: the pair (query i, key j), both in range, is not excluded.
+__device__ __forceinline__ bool amask_keeps(const Params& p, int i, int j) {
+  return p.amask[static_cast<int64_t>(i) * p.amask_ld + j] == 0;
+}
 // Some pair of the rectangle is in the window.
 __device__ __forceinline__ bool rect_meets_band(const Params& p, int r0, int nr, int c0, int nc) {
   return !p.win || (c0 - (r0 + nr - 1) <= p.win_next && (c0 + nc - 1) - r0 >= -p.win_pre);
@@ -806,7 +810,7 @@ __global__ __launch_bounds__(256) void dkdv_kernel(Params p) {
         d4[a] = *reinterpret_cast<const float4*>(tD + c0 + 8 * a + 4 * g);
       }
       float pv[16], dsv[16];
-      if (rect_in_band(p, cur.q0 + c0, 32, kv0 + 32 * w, 32)) {  // uniform: the window cuts nothing here
+      if (!p.amask && rect_in_band(p, cur.q0 + c0, 32, kv0 + 32 * w, 32)) {  // uniform: no mask cuts anything here
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const float li = l4[i >> 2][i & 3], di = d4[i >> 2][i & 3];
@@ -820,7 +824,9 @@ __global__ __launch_bounds__(256) void dkdv_kernel(Params p) {
           const float li = l4[i >> 2][i & 3], di = d4[i >> 2][i & 3];
           const int q = cur.q0 + c0 + 8 * (i >> 2) + 4 * g + (i & 3);  // this register's query row
           const float x = fast_exp2(s[i] * c2 - li);
-          pv[i] = kv_ok && in_band(p, q, my_kv) ? x : 0.f;  // a select: li may be -inf off the window
+          const bool on = kv_ok && q < cur.qend && (!p.win || in_band(p, q, my_kv)) &&
+                          (!p.amask || amask_keeps(p, q, my_kv));
+          pv[i] = on ? x : 0.f;  // a select: li may be -inf where nothing is left
           dsv[i] = pv[i] * (dpv[i] - di);
         }
       }
@@ -1018,14 +1024,15 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
       dpt = E::mma(frag_along_row<D>(tv, 0, 16 * ks, lane), oreg[ks], dpt); // dP^T[kv][q]
     }
     float dsv[16];
-    if (nrows == 32 && rect_in_band(p, q0 + 32 * w, 32, row0, 32)) {  // uniform: no mask needed
+    if (nrows == 32 && !p.amask && rect_in_band(p, q0 + 32 * w, 32, row0, 32)) {  // uniform: no mask needed
 #pragma unroll
       for (int i = 0; i < 16; ++i) dsv[i] = fast_exp2(st[i] * c2 - l2) * (dpt[i] - dl);
     } else {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int kv = 8 * (i >> 2) + 4 * g + (i & 3);  // this register's key row in the slice
-        const bool on = kv < nrows && (!p.win || in_band(p, my_q, row0 + kv));
+        const bool on = kv < nrows && (!p.win || in_band(p, my_q, row0 + kv)) &&
+                        (!p.amask || !q_ok || amask_keeps(p, my_q, row0 + kv));
         const float x = on ? fast_exp2(st[i] * c2 - l2) : 0.f;  // a select: l2 may be -inf off the window
         dsv[i] = x * (dpt[i] - dl);
       }
@@ -1165,7 +1172,7 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
       st = E::mma(frag_along_row<D>(tk, 0, 16 * ks, lane), qreg[ks], st);  // S^T[kv][q]
     float x[16];
     float mx = -__builtin_inff();
-    if (nrows == 32 && rect_in_band(p, q0 + 32 * w, 32, row0, 32)) {  // uniform: no mask needed
+    if (nrows == 32 && !p.amask && rect_in_band(p, q0 + 32 * w, 32, row0, 32)) {  // uniform: no mask needed
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         x[i] = st[i] * c2;  // scaled score in log2 units
@@ -1175,7 +1182,8 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int kv = 8 * (i >> 2) + 4 * g + (i & 3);  // this register's key row in the slice
-        const bool on = kv < nrows && (!p.win || in_band(p, my_q, row0 + kv));
+        const bool on = kv < nrows && (!p.win || in_band(p, my_q, row0 + kv)) &&
+                        (!p.amask || !q_ok || amask_keeps(p, my_q, row0 + kv));
         x[i] = on ? st[i] * c2 : -__builtin_inff();
         mx = fmaxf(mx, x[i]);
       }

@@ -87,7 +87,11 @@ typedef struct bsa_tensor {
  *                              log-sum-exp of the scaled scores; contiguous.
  *  block_sparse_mask           bool/uint8 [B, N, ceil(maxSq/bx), ceil(maxSkv/by)],
  *                              contiguous; NULL = every block selected.
- *  atten_mask                  reserved: must be NULL.
+ *  atten_mask                  optional element mask (参数说明 attenMaskOptional, BOOL,
+ *                              2 dims): bool/uint8 [maxSq, maxSkv], contiguous,
+ *                              1 = the pair does not take part (the FlashAttentionScore
+ *                              page's polarity); shared by every batch and head and
+ *                              indexed by sequence-local positions.  NULL = none.
  *  block_shape, _len           {bx, by} (first two entries used, each > 0);
  *                              NULL = {128, 128}.  Ignored without a mask.
  *  actual_seq_lengths(_kv), _len
@@ -97,7 +101,7 @@ typedef struct bsa_tensor {
  *                              and its outputs are zero).
  *  q_input_layout, kv_input_layout   "BNSD" or "TND", equal.
  *  num_key_value_heads         Nkv; N >= Nkv and N % Nkv == 0 (约束说明).
- *  mask_type                   reserved: must be 0.
+ *  mask_type                   must be 0 (the only mask type the page defines).
  *  scale_value                 the scale (typically D^-0.5); finite.
  *  pre_tokens, next_tokens     sliding window (参数说明 preTokens / nextTokens: how
  *                              many earlier / later tokens a token may attend to):

@@ -136,6 +136,8 @@ class Case:
     # (preTokens, nextTokens) of a sliding window, or None for none; a
     # parameter handed to both sides unchanged
     window: Optional[tuple] = None
+    # attenMask [maxSq, maxSkv] uint8 (1 = the pair does not take part), or None
+    atten_mask: Optional[np.ndarray] = None
 
     @property
     def G(self) -> int:

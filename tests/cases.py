@@ -2,6 +2,8 @@
 
 Sizes span several tiles with ragged tails; each case names what it exercises.
 """
+import numpy as np
+
 import synth
 
 
@@ -64,13 +66,34 @@ def case(name):
         "bnsd_fp16_d128_window_zero": lambda: mk(layout="BNSD", dtype="fp16", B=1, N=2, Nkv=1, D=128,
                                                  Sq=256, Skv=256, bx=128, by=128, mask_rule="ones",
                                                  window=(0, 0), seed=118),
+        # attenMask (30% of pairs removed, one row emptied), GQA, ragged
+        "bnsd_bf16_d128_attenmask": lambda: mk(layout="BNSD", dtype="bf16", B=2, N=4, Nkv=2, D=128, Sq=200,
+                                               Skv=260, bx=64, by=64, p=0.7, seed=124),
+        # attenMask with a window, TND
+        "tnd_fp16_d64_attenmask_window": lambda: mk(layout="TND", dtype="fp16", B=2, N=2, Nkv=1, D=64,
+                                                    bx=32, by=64, p=0.8, lengths_q=[120, 77],
+                                                    lengths_kv=[100, 150], window=(50, 10), seed=125),
         # local window on top of the sink pattern: split units and element masks together
         "bnsd_bf16_d128_window_sink_split": lambda: mk(layout="BNSD", dtype="bf16", B=1, N=4, Nkv=1,
                                                        D=128, Sq=1024, Skv=1024, bx=64, by=64,
                                                        mask_rule="local8_sink2", window=(300, 0),
                                                        seed=119),
     }
-    return cases[name]()
+    c = cases[name]()
+    if name in ATTEN:  # an attenMask over [maxSq, maxSkv], drawn after the case
+        rng = np.random.default_rng(c.seed + 7)
+        sq, sk = int(c.len_q.max()), int(c.len_kv.max())
+        if c.layout == "BNSD":
+            sq, sk = c.Sq, c.Skv
+        am = (rng.random((sq, sk)) < ATTEN[name]).astype(np.uint8)
+        am[:, : min(8, sk)] = 0   # the first keys stay in, so most rows keep some key ...
+        am[min(5, sq - 1), :] = 1  # ... but one row loses all of them
+        c.atten_mask = am
+    return c
+
+
+# fraction of pairs an attenMask removes, for the cases that carry one
+ATTEN = {"bnsd_bf16_d128_attenmask": 0.3, "tnd_fp16_d64_attenmask_window": 0.5}
 
 
 SMALL = ["config1", "bnsd_bf16_d128_b128x128_ragged", "bnsd_fp16_d64_b64x128_padded",
@@ -78,5 +101,6 @@ SMALL = ["config1", "bnsd_bf16_d128_b128x128_ragged", "bnsd_fp16_d64_b64x128_pad
          "bnsd_fp16_d128_b256x256", "bnsd_bf16_d64_b1x1", "bnsd_bf16_d128_nullmask",
          "tnd_bf16_d64_empty_seqs", "bnsd_fp16_d128_sparse_rows", "bnsd_bf16_d128_local_sink_split",
          "bnsd_fp16_d64_sink_split_parts", "bnsd_bf16_d128_window", "tnd_fp16_d64_window_ahead",
-         "bnsd_fp16_d128_window_zero", "bnsd_bf16_d128_window_sink_split"]
+         "bnsd_fp16_d128_window_zero", "bnsd_bf16_d128_window_sink_split", "bnsd_bf16_d128_attenmask",
+         "tnd_fp16_d64_attenmask_window"]
 

@@ -12,7 +12,8 @@ TOL = {"fp16": 5e-3, "bf16": 2e-2}
 
 def oracle_fwd_inputs(case):
     """O rounded to the case dtype and LSE rounded to fp32, from the oracle forward."""
-    kw = dict(layout=case.layout, bx=case.bx, by=case.by, scale=case.scale, window=case.window)
+    kw = dict(layout=case.layout, bx=case.bx, by=case.by, scale=case.scale, window=case.window,
+              atten_mask=case.atten_mask)
     if case.explicit_lengths:
         kw.update(len_q=case.len_q, len_kv=case.len_kv)
     o, lse = oracle.forward(case.q, case.k, case.v, case.mask, **kw)
@@ -20,7 +21,8 @@ def oracle_fwd_inputs(case):
 
 
 def oracle_kw(case):
-    kw = dict(layout=case.layout, bx=case.bx, by=case.by, scale=case.scale, window=case.window)
+    kw = dict(layout=case.layout, bx=case.bx, by=case.by, scale=case.scale, window=case.window,
+              atten_mask=case.atten_mask)
     if case.explicit_lengths or case.layout == "TND":
         kw.update(len_q=case.len_q, len_kv=case.len_kv)
     return kw

@@ -180,7 +180,11 @@ CASES = [
     ("blockShape negative", lambda: _mut(_bnsd, block_shape=[128, -1]), INVALID),
     ("blockShape mismatches mask", lambda: _mut(_bnsd, block_shape=[64, 128]), INVALID),
     # reserved attributes
-    ("attenMask given", lambda: _mut(_bnsd, atten_mask=torch.zeros(300, 270, dtype=torch.bool)), INVALID),
+    ("attenMask [Sq, Skv]", lambda: _mut(_bnsd, atten_mask=torch.zeros(300, 270, dtype=torch.bool)), bsa.BSA_OK),
+    ("attenMask shape", lambda: _mut(_bnsd, atten_mask=torch.zeros(300, 271, dtype=torch.bool)), INVALID),
+    ("attenMask 4-D", lambda: _mut(_bnsd, atten_mask=torch.zeros(1, 1, 300, 270, dtype=torch.bool)), INVALID),
+    ("attenMask float", lambda: _mut(_bnsd, atten_mask=torch.zeros(300, 270)), INVALID),
+    ("attenMask non-contiguous", lambda: _mut(_bnsd, atten_mask=torch.zeros(270, 300, dtype=torch.bool).t()), INVALID),
     ("maskType 1", lambda: _mut(_bnsd, mask_type=1), INVALID),
     # a sliding window (preTokens / nextTokens other than 2147483647) is accepted
     ("preTokens window", lambda: _mut(_bnsd, pre_tokens=1024), bsa.BSA_OK),

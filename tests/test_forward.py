@@ -40,7 +40,7 @@ def _run_fwd(c, out=None):
     lengths = c.explicit_lengths or c.layout == "TND"
     o = torch.empty_like(dev["q"]) if out is None else out(dev["q"])
     lse = torch.empty(dev["q"].shape[:-1], dtype=torch.float32, device="cuda")
-    kw = dict(block_sparse_mask=dev["mask"], atten_mask=None, block_shape=[c.bx, c.by],
+    kw = dict(block_sparse_mask=dev["mask"], atten_mask=dev.get("amask"), block_shape=[c.bx, c.by],
               actual_seq_lengths=list(map(int, c.len_q)) if lengths else None,
               actual_seq_lengths_kv=list(map(int, c.len_kv)) if lengths else None,
               q_input_layout=c.layout, kv_input_layout=c.layout, num_key_value_heads=c.Nkv,
