@@ -290,6 +290,8 @@ def main(argv=None):
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--window", default=None,
                     help="PRE,NEXT: a sliding window (preTokens, nextTokens) on top of the workload's mask")
+    ap.add_argument("--atten-mask", type=float, default=None, metavar="FRACTION",
+                    help="add an attenMask removing this fraction of (query, key) pairs (seeded, uniform)")
     ap.add_argument("--op", choices=["bwd", "fwd"], default="bwd",
                     help="bwd: the backward (default); fwd: the forward that produces O and LSE")
     args = ap.parse_args(argv)
@@ -308,6 +310,11 @@ def main(argv=None):
         pre, nxt = (int(x) for x in args.window.split(","))
         case.window = (pre, nxt)
         case.name += f"_window{pre}_{nxt}"
+    if args.atten_mask is not None:
+        rng = np.random.default_rng(case.seed + 2)
+        sq, sk = (case.Sq, case.Skv) if case.layout == "BNSD" else (int(case.len_q.max()), int(case.len_kv.max()))
+        case.atten_mask = (rng.random((sq, sk), dtype=np.float32) < args.atten_mask).astype(np.uint8)
+        case.name += f"_attenmask{args.atten_mask:g}"
     blocks = active_blocks(case)
     fwd = args.op == "fwd"
     flops = (4.0 if fwd else 10.0) * case.bx * case.by * case.D * blocks
