@@ -23,6 +23,7 @@ block (the S and PV products), with the forward kernel as the roofline and the
 oracle's forward as the CPU baseline.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2] [--op bwd|fwd]
+                      [--head-dim 64|128|256] [--window PRE,NEXT] [--atten-mask FRACTION]
 """
 from __future__ import annotations
 
@@ -292,6 +293,8 @@ def main(argv=None):
                     help="PRE,NEXT: a sliding window (preTokens, nextTokens) on top of the workload's mask")
     ap.add_argument("--atten-mask", type=float, default=None, metavar="FRACTION",
                     help="add an attenMask removing this fraction of (query, key) pairs (seeded, uniform)")
+    ap.add_argument("--head-dim", type=int, default=None, choices=[64, 128, 256],
+                    help="replace the workload's head dim (same lengths and mask, scale D^-0.5)")
     ap.add_argument("--op", choices=["bwd", "fwd"], default="bwd",
                     help="bwd: the backward (default); fwd: the forward that produces O and LSE")
     args = ap.parse_args(argv)
@@ -305,7 +308,7 @@ def main(argv=None):
     import block_sparse_attention_bwd_amd as bsa
 
     torch.backends.cuda.matmul.allow_tf32 = False
-    case = synth.config(args.config)
+    case = synth.config(args.config, head_dim=args.head_dim)
     if args.window:
         pre, nxt = (int(x) for x in args.window.split(","))
         case.window = (pre, nxt)

@@ -228,8 +228,8 @@ int make_plan(const Args& a, Plan* plan) {
   if (N < Nkv || N % Nkv != 0)
     return fail(BSA_ERR_PARAM_INVALID, "query heads %lld must be a multiple of KV heads %lld",
                 static_cast<long long>(N), static_cast<long long>(Nkv));
-  if (D != 64 && D != 128)
-    return fail(BSA_ERR_PARAM_INVALID, "head dim %lld is not supported (64 or 128)", static_cast<long long>(D));
+  if (D != 64 && D != 128 && D != 256)
+    return fail(BSA_ERR_PARAM_INVALID, "head dim %lld is not supported (64, 128 or 256)", static_cast<long long>(D));
 
   // ---- contiguity: inputs contiguous, outputs unit innermost stride ----------
   // (forward: attentionOut is an output with free outer strides; softmaxLse
@@ -341,7 +341,7 @@ int make_plan(const Args& a, Plan* plan) {
   if (B * N * nqb * nkb > kInt32Max) return fail(BSA_ERR_PARAM_INVALID, "block grid too large for int32 lists");
   const int64_t nsub_q = ceil_div(bx, 128), nsub_kv = ceil_div(by, 128);
   if (B * N * nqb * nsub_q + bsa::kMaxSlots > bsa::kMaxGridGroups ||
-      B * Nkv * nkb * nsub_kv + bsa::kMaxSlots > bsa::kMaxGridGroups ||
+      bsa::dkdv_passes(static_cast<int>(D)) * (B * Nkv * nkb * nsub_kv + bsa::kMaxSlots) > bsa::kMaxGridGroups ||
       bsa::prologue_grid(B, N, Sq, nqb, nkb, tnd).total() > bsa::kMaxGridGroups ||
       (tnd ? Sq * N : Sq) > kInt32Max)
     return fail(BSA_ERR_PARAM_INVALID, "launch grid too large (more than %lld workgroups)",

@@ -88,6 +88,10 @@ constexpr int kTileRowsMax = 128;
 // two arrays (unit, piece) of n_units + slots entries.
 inline constexpr int64_t plan_words(int64_t n_units, int64_t slots) { return 4 + 4 * (n_units + slots); }
 constexpr int kBalanceGroups = 256;
+// Workgroups per dK/dV work item: 1, or 2 where dK and dV are accumulated by
+// separate workgroups (head dim 256: K, V and both accumulators do not fit
+// in one wave's registers).
+inline constexpr int dkdv_passes(int D) { return D >= 256 ? 2 : 1; }
 constexpr int kMinChunk = 4;
 constexpr int kMaxSlots = 2 * kBalanceGroups;
 

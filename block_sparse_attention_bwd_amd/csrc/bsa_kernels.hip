@@ -482,9 +482,11 @@ typedef __attribute__((address_space(3))) void lds_void;
 // row r are XOR-permuted by swz(r) so that 16-byte reads of one chunk column
 // by 16 consecutive rows and transposing reads of 4 consecutive rows spread
 // over the banks (the best single layout for both patterns measured on gfx950).
+// Rows of 256 B and of 512 B both start on bank 0, so D = 256 takes D = 128's
+// permutation (of its first 16 chunks).
 template <int D>
 __device__ __forceinline__ int swz(int r) {
-  if constexpr (D == 128) return 2 * (r & 3) + ((r >> 2) & 1) + 8 * ((r >> 3) & 1);
+  if constexpr (D >= 128) return 2 * (r & 3) + ((r >> 2) & 1) + 8 * ((r >> 3) & 1);
   else return 2 * (r & 3) + ((r >> 2) & 1);
 }
 template <int D>
@@ -664,27 +666,37 @@ __device__ __forceinline__ bool dkdv_seek(const Params& p, int64_t bn0, int jb, 
   return false;
 }
 
-template <class E, int D, int W>
-__global__ __launch_bounds__(256) void dkdv_kernel(Params p) {
+// What one dK/dV workgroup accumulates: both gradients (four GEMMs per step),
+// or, where K, V and both accumulators would not fit in registers (D = 256),
+// one of them per workgroup, each work item running twice: the dV pass needs
+// S, P and dV += P^T dO, the dK pass S, dP, dS and dK += dS^T Q.
+enum DkdvMode { kDkdvBoth = 0, kDkdvOnlyV = 1, kDkdvOnlyK = 2 };
+// Q rows per staged tile: 32 per wave (16 at D = 256, so that two buffers of
+// Q and dOut fit in LDS), and at least one 32-row slice.
+template <int D, int W>
+__host__ __device__ constexpr int dkdv_tile_rows() {
+  return (D >= 256 ? 16 : 32) * W < 32 ? 32 : (D >= 256 ? 16 : 32) * W;
+}
+
+template <class E, int D, int W, int MODE>
+__device__ __forceinline__ void dkdv_work(const Params& p, int item, unsigned short (*sQ)[dkdv_tile_rows<D, W>() * D],
+                                          unsigned short (*sO)[dkdv_tile_rows<D, W>() * D],
+                                          float (*sL)[dkdv_tile_rows<D, W>()], float (*sDl)[dkdv_tile_rows<D, W>()]) {
   constexpr int KS = D / 16;  // K=16 steps over the head dim
   constexpr int NT = D / 32;  // 32-wide column tiles of the head dim
-  constexpr int H = 32 * W;   // Q rows per tile: 32 per wave
-  // Q and dOut tiles (swizzled layout) and their LSE*log2(e) / softmax_grad
-  // rows, double-buffered: tile t + 1 is copied in by DMA during tile t
-  __shared__ __align__(1024) unsigned short sQ[2][H * D];
-  __shared__ __align__(1024) unsigned short sO[2][H * D];  // dOut rows
-  __shared__ __align__(16) float sL[2][H];
-  __shared__ __align__(16) float sDl[2][H];
+  constexpr int H = dkdv_tile_rows<D, W>();
+  constexpr int RW = H / W;   // rows copied per wave
+  constexpr bool kDoV = MODE != kDkdvOnlyK, kDoK = MODE != kDkdvOnlyV;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6, l32 = lane & 31, g = lane >> 5;
 
-  // Workgroup i takes work item i of the plan's launch order: piece `piece`
-  // of unit u (the whole unit unless it is split).
+  // Work item `item` of the plan's launch order: piece `piece` of unit u
+  // (the whole unit unless it is split).
   const PlanView pv(p);
-  if (static_cast<int>(blockIdx.x) >= p.plan[1]) return;
-  const int u = pv.order_unit[blockIdx.x];
-  const int piece = pv.order_piece[blockIdx.x];
+  if (item >= p.plan[1]) return;
+  const int u = pv.order_unit[item];
+  const int piece = pv.order_piece[item];
   const int32_t* unit_k = pv.unit_k;
   const int32_t* unit_base = pv.unit_base;
   const int pieces = unit_k[u];
@@ -711,24 +723,24 @@ __global__ __launch_bounds__(256) void dkdv_kernel(Params p) {
   const unsigned short* kp = static_cast<const unsigned short*>(p.k) + kv_base;
   const unsigned short* vp = static_cast<const unsigned short*>(p.v) + kv_base;
 
-  u16x8 kreg[KS], vreg[KS];
+  u16x8 kreg[KS], vreg[kDoK ? KS : 1];
 #pragma unroll
   for (int s = 0; s < KS; ++s) {
     u16x8 zk = {0, 0, 0, 0, 0, 0, 0, 0};
     u16x8 zv = zk;
     if (kv_ok) {
       zk = *reinterpret_cast<const u16x8*>(kp + my_kv * p.kv_sr + 16 * s + 8 * g);
-      zv = *reinterpret_cast<const u16x8*>(vp + my_kv * p.kv_sr + 16 * s + 8 * g);
+      if constexpr (kDoK) zv = *reinterpret_cast<const u16x8*>(vp + my_kv * p.kv_sr + 16 * s + 8 * g);
     }
     kreg[s] = zk;
-    vreg[s] = zv;
+    if constexpr (kDoK) vreg[s] = zv;
   }
 
-  f32x16 adv[NT], adk[NT];
+  f32x16 adv[kDoV ? NT : 1], adk[kDoK ? NT : 1];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
-    adv[nt] = f32x16{};
-    adk[nt] = f32x16{};
+    if constexpr (kDoV) adv[nt] = f32x16{};
+    if constexpr (kDoK) adk[nt] = f32x16{};
   }
 
   const float c2 = p.scale_log2e;
@@ -737,8 +749,8 @@ __global__ __launch_bounds__(256) void dkdv_kernel(Params p) {
   const unsigned short* qbase = static_cast<const unsigned short*>(p.q) + b * p.q_sb + si.off_q * p.q_sr;
   const unsigned short* obase = static_cast<const unsigned short*>(p.dout) + b * p.q_sb + si.off_q * p.q_sr;
 
-  // DMA of one tile into buffer `buf`: wave w copies rows 32w .. 32w + 31 of
-  // Q and dOut (one 1 KB wave instruction per 512 / D rows, lanes fetching
+  // DMA of one tile into buffer `buf`: wave w copies rows RW w .. RW w + RW - 1
+  // of Q and dOut (one 1 KB wave instruction per 512 / D rows, lanes fetching
   // the swizzled chunk they land on) and their LSE / softmax_grad values;
   // rows past the tile's valid rows read zeros and LSE = +inf, so their P is
   // exactly 0 with no per-element test.
@@ -749,8 +761,8 @@ __global__ __launch_bounds__(256) void dkdv_kernel(Params p) {
     const unsigned short* oa = obase + t.n * p.q_sh;
     const unsigned qb = lds_addr(sQ[buf]), ob = lds_addr(sO[buf]);
 #pragma unroll
-    for (int i = 0; i < 32 / RPI; ++i) {
-      const int ins = w * (32 / RPI) + i;
+    for (int i = 0; i < RW / RPI; ++i) {
+      const int ins = w * (RW / RPI) + i;
       const int r = ins * RPI + lane / (D / 8);
       const int c = (lane % (D / 8)) ^ swz<D>(r);
       const bool ok = r < rows;
@@ -758,17 +770,17 @@ __global__ __launch_bounds__(256) void dkdv_kernel(Params p) {
       dma16(ok ? static_cast<const void*>(qa + off) : p.consts, qb + 1024u * ins);
       dma16(ok ? static_cast<const void*>(oa + off) : p.consts, ob + 1024u * ins);
     }
-    if (lane < 32) {
-      const int r = 32 * w + lane;
+    if (lane < RW) {
+      const int r = RW * w + lane;
       const int64_t li = (bn0 + t.n) * p.sq_max + t.q0 + r;
-      dma4(r < rows ? static_cast<const void*>(p.lse2 + li) : p.consts + kConstPosInf, lds_addr(&sL[buf][32 * w]));
-      dma4(r < rows ? static_cast<const void*>(p.delta + li) : p.consts, lds_addr(&sDl[buf][32 * w]));
+      dma4(r < rows ? static_cast<const void*>(p.lse2 + li) : p.consts + kConstPosInf, lds_addr(&sL[buf][RW * w]));
+      dma4(r < rows ? static_cast<const void*>(p.delta + li) : p.consts, lds_addr(&sDl[buf][RW * w]));
     }
   };
 #pragma unroll
   for (int s = 0; s < KS; ++s) {  // complete the K/V loads before the first copy
     settle(kreg[s]);
-    settle(vreg[s]);
+    if constexpr (kDoK) settle(vreg[s]);
   }
 
   // entries [piece * chunk, piece * chunk + chunk) of the merged list, or all of them
@@ -798,9 +810,11 @@ __global__ __launch_bounds__(256) void dkdv_kernel(Params p) {
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         const u16x8 aq = frag_along_row<D>(tQ, c0, 16 * ks, lane);
-        const u16x8 ao = frag_along_row<D>(tO, c0, 16 * ks, lane);
-        s = E::mma(aq, kreg[ks], s);      // S[q][kv] (unscaled); this lane's column is my_kv
-        dpv = E::mma(ao, vreg[ks], dpv);  // dP[q][kv] = dOut * V^T
+        s = E::mma(aq, kreg[ks], s);  // S[q][kv] (unscaled); this lane's column is my_kv
+        if constexpr (kDoK) {
+          const u16x8 ao = frag_along_row<D>(tO, c0, 16 * ks, lane);
+          dpv = E::mma(ao, vreg[ks], dpv);  // dP[q][kv] = dOut * V^T
+        }
       }
       // this lane's 16 score rows are c0 + 8a + 4g + {0..3}: four float4 reads each
       float4 l4[4], d4[4];
@@ -836,10 +850,14 @@ __global__ __launch_bounds__(256) void dkdv_kernel(Params p) {
       for (int nt = 0; nt < NT; ++nt) {
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
-          const u16x8 bo = frag_down_rows<D>(tO, c0 + 16 * hh, 32 * nt, lane);
-          const u16x8 bq = frag_down_rows<D>(tQ, c0 + 16 * hh, 32 * nt, lane);
-          adv[nt] = E::mma(pa[hh], bo, adv[nt]);  // dV += P^T * dOut
-          adk[nt] = E::mma(da[hh], bq, adk[nt]);  // dK += dS^T * Q
+          if constexpr (kDoV) {
+            const u16x8 bo = frag_down_rows<D>(tO, c0 + 16 * hh, 32 * nt, lane);
+            adv[nt] = E::mma(pa[hh], bo, adv[nt]);  // dV += P^T * dOut
+          }
+          if constexpr (kDoK) {
+            const u16x8 bq = frag_down_rows<D>(tQ, c0 + 16 * hh, 32 * nt, lane);
+            adk[nt] = E::mma(da[hh], bq, adk[nt]);  // dK += dS^T * Q
+          }
         }
       }
     }
@@ -857,8 +875,8 @@ __global__ __launch_bounds__(256) void dkdv_kernel(Params p) {
       for (int i = 0; i < 16; ++i) {
         const int rl = 32 * w + 8 * (i >> 2) + 4 * g + (i & 3);
         if (kv0 + rl < w_end) {
-          dst[rl * D + 32 * nt + l32] = adk[nt][i];
-          dst[(kTileRowsMax + rl) * D + 32 * nt + l32] = adv[nt][i];
+          if constexpr (kDoK) dst[rl * D + 32 * nt + l32] = adk[nt][i];
+          if constexpr (kDoV) dst[(kTileRowsMax + rl) * D + 32 * nt + l32] = adv[nt][i];
         }
       }
     }
@@ -872,10 +890,27 @@ __global__ __launch_bounds__(256) void dkdv_kernel(Params p) {
     for (int i = 0; i < 16; ++i) {
       const int r = kv0 + 32 * w + 8 * (i >> 2) + 4 * g + (i & 3);
       if (r < w_end) {
-        dkp[r * p.dk_sr + 32 * nt + l32] = E::from_f32(adk[nt][i] * p.scale);
-        dvp[r * p.dv_sr + 32 * nt + l32] = E::from_f32(adv[nt][i]);
+        if constexpr (kDoK) dkp[r * p.dk_sr + 32 * nt + l32] = E::from_f32(adk[nt][i] * p.scale);
+        if constexpr (kDoV) dvp[r * p.dv_sr + 32 * nt + l32] = E::from_f32(adv[nt][i]);
       }
     }
+  }
+}
+
+template <class E, int D, int W>
+__global__ __launch_bounds__(256) void dkdv_kernel(Params p) {
+  constexpr int H = dkdv_tile_rows<D, W>();
+  // Q and dOut tiles (swizzled layout) and their LSE*log2(e) / softmax_grad
+  // rows, double-buffered: tile t + 1 is copied in by DMA during tile t
+  __shared__ __align__(1024) unsigned short sQ[2][H * D];
+  __shared__ __align__(1024) unsigned short sO[2][H * D];  // dOut rows
+  __shared__ __align__(16) float sL[2][H];
+  __shared__ __align__(16) float sDl[2][H];
+  if constexpr (dkdv_passes(D) == 1) {
+    dkdv_work<E, D, W, kDkdvBoth>(p, blockIdx.x, sQ, sO, sL, sDl);
+  } else {  // workgroups 2i and 2i + 1 run the dV and the dK pass of work item i
+    if (blockIdx.x & 1) dkdv_work<E, D, W, kDkdvOnlyK>(p, blockIdx.x >> 1, sQ, sO, sL, sDl);
+    else dkdv_work<E, D, W, kDkdvOnlyV>(p, blockIdx.x >> 1, sQ, sO, sL, sDl);
   }
 }
 
@@ -931,7 +966,7 @@ __device__ void reduce_pieces(const Params& p, int s) {
 // One workgroup per (batch, query head, Q block, 128-row part); it walks the
 // slices of the KV blocks its Q block selects, in list (ascending) order.
 template <class E, int D, int W>
-__global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) void dq_kernel(Params p) {
+__global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(D >= 256 ? 1 : 2))) void dq_kernel(Params p) {
   constexpr int KS = D / 16;
   constexpr int NT = D / 32;
   constexpr int NB = ring_buffers(W);
@@ -1100,7 +1135,7 @@ __device__ __forceinline__ u16x4 pack4(const float* x) {
 }
 
 template <class E, int D, int W>
-__global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) void fwd_kernel(Params p) {
+__global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(D >= 256 ? 1 : 2))) void fwd_kernel(Params p) {
   constexpr int KS = D / 16;
   constexpr int NT = D / 32;
   constexpr int NB = ring_buffers(W);
@@ -1275,7 +1310,10 @@ int launch_stage_seq(const SeqChunk& chunk, SeqInfo* dst, float* consts, void* s
 template <class... A>
 void launch_prologue_kernel(const Params& p, dim3 grid, hipStream_t s, A... a) {
   const bool bf = p.dtype == 2;
-  if (p.D == 128) {
+  if (p.D == 256) {
+    if (bf) hipLaunchKernelGGL((prologue_kernel<EBf16, 256>), grid, dim3(256), 0, s, p, a...);
+    else hipLaunchKernelGGL((prologue_kernel<EF16, 256>), grid, dim3(256), 0, s, p, a...);
+  } else if (p.D == 128) {
     if (bf) hipLaunchKernelGGL((prologue_kernel<EBf16, 128>), grid, dim3(256), 0, s, p, a...);
     else hipLaunchKernelGGL((prologue_kernel<EF16, 128>), grid, dim3(256), 0, s, p, a...);
   } else {
@@ -1301,7 +1339,10 @@ int launch_prologue(const Params& p, void* stream) {
 #define BSA_DISPATCH(KERNEL, W, GRID, S, P)                                     \
   do {                                                                          \
     const bool bf_ = (P).dtype == 2;                                            \
-    if ((P).D == 128) {                                                         \
+    if ((P).D == 256) {                                                         \
+      if (bf_) BSA_DISPATCH_W(KERNEL, EBf16, 256, W, GRID, S, P);               \
+      else BSA_DISPATCH_W(KERNEL, EF16, 256, W, GRID, S, P);                    \
+    } else if ((P).D == 128) {                                                  \
       if (bf_) BSA_DISPATCH_W(KERNEL, EBf16, 128, W, GRID, S, P);               \
       else BSA_DISPATCH_W(KERNEL, EF16, 128, W, GRID, S, P);                    \
     } else {                                                                    \
@@ -1329,8 +1370,12 @@ int launch_plan(const Params& p, void* stream) {
 }
 
 int launch_dkdv(const Params& p, void* stream) {
-  const dim3 grid(static_cast<unsigned>(p.n_units + p.slots_cap));
-  BSA_DISPATCH(dkdv_kernel, waves_for(p.by), grid, static_cast<hipStream_t>(stream), p);
+  const dim3 grid(static_cast<unsigned>(dkdv_passes(p.D) * (p.n_units + p.slots_cap)));
+  // head dim 256: the 1- and 2-wave builds spill registers, so KV blocks of
+  // up to 64 rows also take the 4-wave one (its waves past the block's rows
+  // compute on zero K/V rows and store nothing)
+  const int w = p.D >= 256 ? 4 : waves_for(p.by);
+  BSA_DISPATCH(dkdv_kernel, w, grid, static_cast<hipStream_t>(stream), p);
   return static_cast<int>(hipGetLastError());
 }
 

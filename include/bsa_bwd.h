@@ -114,7 +114,9 @@ typedef struct bsa_tensor {
  *                              any outer strides, innermost stride 1.
  *  workspace_size              out: bytes of device workspace needed.
  *
- * Head dim D must be 64 or 128 (the tile set built into this library).
+ * Head dim D must be 64, 128 or 256 (the tile set built into this library;
+ * the pages' own implementation takes 128 only, the FlashAttentionScore page
+ * allows up to 512).
  */
 int bsa_bwd_workspace_size(const bsa_tensor* dout, const bsa_tensor* query, const bsa_tensor* key,
                            const bsa_tensor* value, const bsa_tensor* attention_out,

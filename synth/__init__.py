@@ -266,32 +266,38 @@ def make_case(
     )
 
 
-def config(k: int, seed: Optional[int] = None) -> Case:
-    """The five named workloads (seed defaults to 1000 + k)."""
+def config(k: int, seed: Optional[int] = None, head_dim: Optional[int] = None) -> Case:
+    """The five named workloads (seed defaults to 1000 + k).
+
+    ``head_dim`` replaces the workload's head dim (and its scale, D^-0.5)
+    while keeping everything else; lengths and mask are drawn before the
+    tensors, so they stay the same.  The name gets a ``_d<D>`` suffix.
+    """
     if seed is None:
         seed = 1000 + k
     name = CONFIG_NAMES[k]
     if k == 1:
-        return make_case(layout="BNSD", dtype="fp16", B=1, N=2, Nkv=2, D=64, Sq=256, Skv=256,
-                         bx=64, by=64, mask_rule="bernoulli_diag", p=0.5, scale=1.0 / 8,
-                         seed=seed, name=name)
-    if k == 2:
-        return make_case(layout="BNSD", dtype="bf16", B=2, N=16, Nkv=16, D=128, Sq=4096,
-                         Skv=4096, bx=128, by=128, mask_rule="bernoulli_diag", p=0.25,
-                         seed=seed, name=name)
-    if k == 3:
-        return make_case(layout="BNSD", dtype="bf16", B=1, N=32, Nkv=8, D=128, Sq=8192,
-                         Skv=8192, bx=128, by=128, mask_rule="local8_sink2", seed=seed,
-                         name=name)
-    if k == 4:
-        return make_case(layout="TND", dtype="fp16", B=8, N=32, Nkv=4, D=128, bx=64, by=128,
-                         mask_rule="bernoulli_diag", p=0.1, draw_lengths=(512, 8192),
-                         seed=seed, name=name)
-    if k == 5:
-        return make_case(layout="BNSD", dtype="bf16", B=1, N=32, Nkv=8, D=128, Sq=16384,
-                         Skv=65536, bx=128, by=64, mask_rule="bernoulli_rowguard", p=0.05,
-                         seed=seed, name=name)
-    raise KeyError(k)
+        kw = dict(layout="BNSD", dtype="fp16", B=1, N=2, Nkv=2, D=64, Sq=256, Skv=256,
+                  bx=64, by=64, mask_rule="bernoulli_diag", p=0.5, scale=1.0 / 8)
+    elif k == 2:
+        kw = dict(layout="BNSD", dtype="bf16", B=2, N=16, Nkv=16, D=128, Sq=4096,
+                  Skv=4096, bx=128, by=128, mask_rule="bernoulli_diag", p=0.25)
+    elif k == 3:
+        kw = dict(layout="BNSD", dtype="bf16", B=1, N=32, Nkv=8, D=128, Sq=8192,
+                  Skv=8192, bx=128, by=128, mask_rule="local8_sink2")
+    elif k == 4:
+        kw = dict(layout="TND", dtype="fp16", B=8, N=32, Nkv=4, D=128, bx=64, by=128,
+                  mask_rule="bernoulli_diag", p=0.1, draw_lengths=(512, 8192))
+    elif k == 5:
+        kw = dict(layout="BNSD", dtype="bf16", B=1, N=32, Nkv=8, D=128, Sq=16384,
+                  Skv=65536, bx=128, by=64, mask_rule="bernoulli_rowguard", p=0.05)
+    else:
+        raise KeyError(k)
+    if head_dim is not None:
+        kw["D"] = int(head_dim)
+        kw["scale"] = 1.0 / math.sqrt(kw["D"])
+        name = f"{name}_d{kw['D']}"
+    return make_case(seed=seed, name=name, **kw)
 
 
 def active_blocks(case: Case) -> int:

@@ -78,6 +78,21 @@ def case(name):
                                                        D=128, Sq=1024, Skv=1024, bx=64, by=64,
                                                        mask_rule="local8_sink2", window=(300, 0),
                                                        seed=119),
+        # head dim 256 (two dK/dV passes per work item): ragged 128x128 tiles, GQA
+        "bnsd_bf16_d256_b128x128_ragged": lambda: mk(layout="BNSD", dtype="bf16", B=2, N=4, Nkv=2, D=256,
+                                                     Sq=300, Skv=270, bx=128, by=128, p=0.5, seed=130),
+        # head dim 256, varlen TND with 64-row blocks (a 4-wave dK/dV workgroup on 64 KV rows)
+        "tnd_fp16_d256_b64x64_gqa": lambda: mk(layout="TND", dtype="fp16", B=2, N=4, Nkv=1, D=256, bx=64,
+                                               by=64, p=0.5, lengths_q=[190, 77], lengths_kv=[150, 201],
+                                               seed=131),
+        # head dim 256 with split dK/dV units reduced in piece order
+        "bnsd_fp16_d256_sink_split": lambda: mk(layout="BNSD", dtype="fp16", B=1, N=4, Nkv=1, D=256,
+                                                Sq=768, Skv=768, bx=64, by=64, mask_rule="local8_sink2",
+                                                seed=132),
+        # head dim 256 with a window and an attenMask, 32-row Q blocks
+        "bnsd_bf16_d256_window_attenmask": lambda: mk(layout="BNSD", dtype="bf16", B=1, N=2, Nkv=1, D=256,
+                                                      Sq=200, Skv=260, bx=32, by=128, p=0.7,
+                                                      window=(90, 30), seed=133),
     }
     c = cases[name]()
     if name in ATTEN:  # an attenMask over [maxSq, maxSkv], drawn after the case
@@ -93,7 +108,8 @@ def case(name):
 
 
 # fraction of pairs an attenMask removes, for the cases that carry one
-ATTEN = {"bnsd_bf16_d128_attenmask": 0.3, "tnd_fp16_d64_attenmask_window": 0.5}
+ATTEN = {"bnsd_bf16_d128_attenmask": 0.3, "tnd_fp16_d64_attenmask_window": 0.5,
+         "bnsd_bf16_d256_window_attenmask": 0.2}
 
 
 SMALL = ["config1", "bnsd_bf16_d128_b128x128_ragged", "bnsd_fp16_d64_b64x128_padded",
@@ -102,5 +118,6 @@ SMALL = ["config1", "bnsd_bf16_d128_b128x128_ragged", "bnsd_fp16_d64_b64x128_pad
          "tnd_bf16_d64_empty_seqs", "bnsd_fp16_d128_sparse_rows", "bnsd_bf16_d128_local_sink_split",
          "bnsd_fp16_d64_sink_split_parts", "bnsd_bf16_d128_window", "tnd_fp16_d64_window_ahead",
          "bnsd_fp16_d128_window_zero", "bnsd_bf16_d128_window_sink_split", "bnsd_bf16_d128_attenmask",
-         "tnd_fp16_d64_attenmask_window"]
+         "tnd_fp16_d64_attenmask_window", "bnsd_bf16_d256_b128x128_ragged", "tnd_fp16_d256_b64x64_gqa",
+         "bnsd_fp16_d256_sink_split", "bnsd_bf16_d256_window_attenmask"]
 

@@ -121,6 +121,19 @@ def test_layout_region_sizes():
     assert size["partial"] >= slots * 2 * 128 * D * 4
 
 
+def test_layout_partial_region_scales_with_head_dim():
+    """The fp32 partials hold [slots][dK, dV][128 rows][D]: twice as large at D = 256."""
+    sizes = {}
+    for D in (64, 128, 256):
+        offs, _ = bsa.bsa_bwd_workspace_layout(**_bnsd(D=D))
+        i = bsa.WS_REGIONS.index("partial")
+        sizes[D] = offs[bsa.WS_REGIONS[i + 1]] - offs["partial"]
+    slots = min(2 * 2 * 3 * 2 * 3, 512)
+    for D in (64, 128, 256):
+        assert sizes[D] >= slots * 2 * 128 * D * 4
+    assert sizes[256] > sizes[128] > sizes[64]
+
+
 NULLPTR = bsa.BSA_ERR_PARAM_NULLPTR
 INVALID = bsa.BSA_ERR_PARAM_INVALID
 
@@ -166,6 +179,9 @@ CASES = [
     ("N < Nkv", lambda: _mut(lambda: _bnsd(N=2, Nkv=4)), INVALID),
     ("numKeyValueHeads mismatch", lambda: _mut(_bnsd, num_key_value_heads=1), INVALID),
     ("head dim 96", lambda: _mut(lambda: _bnsd(D=96)), INVALID),
+    ("head dim 512", lambda: _mut(lambda: _bnsd(D=512)), INVALID),
+    ("head dim 256", lambda: _mut(lambda: _bnsd(D=256)), bsa.BSA_OK),
+    ("head dim 64", lambda: _mut(lambda: _bnsd(D=64)), bsa.BSA_OK),
     ("query/key batch differ", lambda: _mut(_bnsd, key=torch.zeros(1, 2, 270, 128, dtype=torch.bfloat16)), INVALID),
     ("dout shape differs", lambda: _mut(_bnsd, dout=torch.zeros(2, 4, 299, 128, dtype=torch.bfloat16)), INVALID),
     ("dk shape differs", lambda: _mut(_bnsd, dk=torch.zeros(2, 2, 271, 128, dtype=torch.bfloat16)), INVALID),

@@ -84,7 +84,8 @@ def test_block_lists_bit_exact(name):
                 assert list(cl[b, n, j, :cc[b, n, j]]) == cols[b][n][j], (b, n, j)
 
 
-@pytest.mark.parametrize("name", ["config1", "tnd_fp16_d128_b64x128_gqa", "bnsd_fp16_d64_b64x128_padded"])
+@pytest.mark.parametrize("name", ["config1", "tnd_fp16_d128_b64x128_gqa", "bnsd_fp16_d64_b64x128_padded",
+                                  "tnd_fp16_d256_b64x64_gqa"])
 def test_delta_and_lse2(name):
     import block_sparse_attention_bwd_amd as bsa
     c, o, lse, _ = _prepared(name)
@@ -113,7 +114,7 @@ def test_delta_and_lse2(name):
 
 
 @pytest.mark.parametrize("name", ["bnsd_bf16_d128_b128x128_ragged", "tnd_fp16_d128_b64x128_gqa",
-                                  "bnsd_bf16_d128_local_sink_split"])
+                                  "bnsd_bf16_d128_local_sink_split", "bnsd_fp16_d256_sink_split"])
 def test_bitwise_deterministic(name):
     c, o, lse, _ = _prepared(name)
     dev = upload(c, o, lse)
