@@ -26,6 +26,12 @@ Parity status of each function (what pins it, in ``tests/test_oracle.py``):
   a hand-built element mask (alone and with a window), finite differences (TND,
   with a window), slab path == dense path with a row the mask empties, and the
   row-sampled helpers.
+* fp8 inputs (``oracle/fp8.py``: ``decode``, ``dequantize``, ``backward_fp8``,
+  ``forward_fp8``; in ``tests/test_oracle_fp8.py``): hand-worked code values
+  from the OCP format definitions (``tests/golden/fp8_values.json``), torch's
+  float8 dtypes over all 256 codes, IEEE binary16 for E5M2, monotone positive
+  codes, and the per-tensor factors against hand-scaled plain-oracle calls,
+  scaling identities and a torch fp64 forward.
 
 No function here is "parity unpinned".
 """
