@@ -130,20 +130,44 @@ def gpu_forward(case, dev, rows_per_chunk=2048):
     return o, lse
 
 
+def quantize_inputs(dev, keys):
+    """fp8 copies of dev[k] for k in keys (dout E5M2, the others E4M3FN), each with the
+    per-tensor factor max|x| / the format's largest finite value; returns (dict, factors)."""
+    torch = _torch()
+    out, fac = dict(dev), {}
+    for k in keys:
+        tdt, top = (torch.float8_e5m2, 57344.0) if k == "do" else (torch.float8_e4m3fn, 448.0)
+        x = dev[k].float()
+        amax = float(x.abs().max())
+        f = amax / top if amax > 0 else 1.0
+        out[k] = (x / f).to(tdt)
+        fac[k] = f
+        del x
+    return out, fac
+
+
 # ---------------------------------------------------------------------------
 # running the library
 # ---------------------------------------------------------------------------
 class Runner:
-    """Pre-allocated outputs and workspace for repeated bsa_bwd calls."""
+    """Pre-allocated outputs and workspace for repeated bsa_bwd calls.
 
-    def __init__(self, case, dev, o, lse):
+    With ``descale`` (a list of the five dequantisation factors of dout,
+    query, key, value, attention_out) the tensors are fp8 and the calls go to
+    bsa_bwd_fp8, with bf16 gradients.
+    """
+
+    def __init__(self, case, dev, o, lse, descale=None):
         torch = _torch()
         import block_sparse_attention_bwd_amd as bsa
         self.bsa = bsa
         self.dev = dev
-        self.dq = torch.empty_like(dev["q"])
-        self.dk = torch.empty_like(dev["k"])
-        self.dv = torch.empty_like(dev["v"])
+        self.fp8 = descale is not None
+        self.descale = descale
+        odt = torch.bfloat16 if self.fp8 else dev["q"].dtype
+        self.dq = torch.empty(dev["q"].shape, dtype=odt, device=dev["q"].device)
+        self.dk = torch.empty(dev["k"].shape, dtype=odt, device=dev["k"].device)
+        self.dv = torch.empty(dev["v"].shape, dtype=odt, device=dev["v"].device)
         lengths = case.explicit_lengths or case.layout == "TND"
         self.kw = dict(
             block_sparse_mask=dev["mask"], atten_mask=dev.get("amask"), block_shape=[case.bx, case.by],
@@ -155,22 +179,34 @@ class Runner:
             next_tokens=bsa.NO_WINDOW if case.window is None else int(case.window[1]),
             dq=self.dq, dk=self.dk, dv=self.dv)
         self.args = (dev["do"], dev["q"], dev["k"], dev["v"], o, lse)
-        self.ws_size = bsa.bsa_bwd_workspace_size(*self.args, **self.kw)
+        if self.fp8:
+            self.ws_size = bsa.bsa_bwd_fp8_workspace_size(*self.args, **self.kw, descale=descale)
+        else:
+            self.ws_size = bsa.bsa_bwd_workspace_size(*self.args, **self.kw)
         self.ws = torch.empty(max(1, self.ws_size), dtype=torch.uint8, device=dev["q"].device)
 
     def __call__(self, stream=None):
-        self.bsa.bsa_bwd(*self.args, **self.kw, workspace=self.ws, workspace_size=self.ws_size, stream=stream)
+        if self.fp8:
+            self.bsa.bsa_bwd_fp8(*self.args, **self.kw, descale=self.descale, workspace=self.ws,
+                                 workspace_size=self.ws_size, stream=stream)
+        else:
+            self.bsa.bsa_bwd(*self.args, **self.kw, workspace=self.ws, workspace_size=self.ws_size,
+                             stream=stream)
         return self.dq, self.dk, self.dv
 
 
 class FwdRunner:
-    """Pre-allocated O, LSE and workspace for repeated bsa_fwd calls."""
+    """Pre-allocated O, LSE and workspace for repeated bsa_fwd calls (fp8
+    query/key/value through bsa_fwd_fp8, with a bf16 O, when ``descale`` gives
+    their three factors)."""
 
-    def __init__(self, case, dev):
+    def __init__(self, case, dev, descale=None):
         torch = _torch()
         import block_sparse_attention_bwd_amd as bsa
         self.bsa = bsa
-        self.o = torch.empty_like(dev["q"])
+        self.descale = descale
+        odt = torch.bfloat16 if descale is not None else dev["q"].dtype
+        self.o = torch.empty(dev["q"].shape, dtype=odt, device=dev["q"].device)
         self.lse = torch.empty(dev["q"].shape[:-1], dtype=torch.float32, device=dev["q"].device)
         lengths = case.explicit_lengths or case.layout == "TND"
         self.kw = dict(
@@ -183,11 +219,19 @@ class FwdRunner:
             next_tokens=bsa.NO_WINDOW if case.window is None else int(case.window[1]),
             attention_out=self.o, softmax_lse=self.lse)
         self.args = (dev["q"], dev["k"], dev["v"])
-        self.ws_size = bsa.bsa_fwd_workspace_size(*self.args, **self.kw)
+        if descale is not None:
+            self.ws_size = bsa.bsa_fwd_fp8_workspace_size(*self.args, **self.kw, descale=descale)
+        else:
+            self.ws_size = bsa.bsa_fwd_workspace_size(*self.args, **self.kw)
         self.ws = torch.empty(max(1, self.ws_size), dtype=torch.uint8, device=dev["q"].device)
 
     def __call__(self, stream=None):
-        self.bsa.bsa_fwd(*self.args, **self.kw, workspace=self.ws, workspace_size=self.ws_size, stream=stream)
+        if self.descale is not None:
+            self.bsa.bsa_fwd_fp8(*self.args, **self.kw, descale=self.descale, workspace=self.ws,
+                                 workspace_size=self.ws_size, stream=stream)
+        else:
+            self.bsa.bsa_fwd(*self.args, **self.kw, workspace=self.ws, workspace_size=self.ws_size,
+                             stream=stream)
         return self.o, self.lse
 
 
@@ -295,6 +339,9 @@ def main(argv=None):
                     help="add an attenMask removing this fraction of (query, key) pairs (seeded, uniform)")
     ap.add_argument("--head-dim", type=int, default=None, choices=[64, 128, 256],
                     help="replace the workload's head dim (same lengths and mask, scale D^-0.5)")
+    ap.add_argument("--fp8", action="store_true",
+                    help="fp8 inputs (E4M3FN query/key/value/attentionOut, E5M2 dout, per-tensor factors) "
+                         "through the fp8 entry points; bf16 compute and outputs")
     ap.add_argument("--op", choices=["bwd", "fwd"], default="bwd",
                     help="bwd: the backward (default); fwd: the forward that produces O and LSE")
     args = ap.parse_args(argv)
@@ -324,13 +371,24 @@ def main(argv=None):
     print(f"# workload {case.name}: {blocks} active blocks, {flops / 1e9:.1f} GFLOP counted", file=sys.stderr, flush=True)
 
     dev = to_device(case)
+    if args.fp8:
+        case.name += "_fp8"
     if fwd:
         o = lse = None
-        run = FwdRunner(case, dev)
+        if args.fp8:
+            dev8, fac = quantize_inputs(dev, ("q", "k", "v"))
+            run = FwdRunner(case, dev8, descale=[fac["q"], fac["k"], fac["v"]])
+        else:
+            run = FwdRunner(case, dev)
     else:
         o, lse = gpu_forward(case, dev)
         torch.cuda.synchronize()
-        run = Runner(case, dev, o, lse)
+        if args.fp8:
+            dev["o"] = o
+            dev8, fac = quantize_inputs(dev, ("do", "q", "k", "v", "o"))
+            run = Runner(case, dev8, dev8["o"], lse, descale=[fac[k] for k in ("do", "q", "k", "v", "o")])
+        else:
+            run = Runner(case, dev, o, lse)
     stream = torch.cuda.current_stream()
 
     for _ in range(args.warmup):
@@ -399,7 +457,7 @@ def main(argv=None):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": case.dtype,
+        "dtype": "bf16" if args.fp8 else case.dtype,
         "data": "synthetic",
         "config": {
             "workload": case.name,
@@ -408,6 +466,8 @@ def main(argv=None):
             "active_blocks": blocks, "gflop_counted": round(flops / 1e9, 3),
             "frac_of_mfma_peak": round(tflops / MFMA_PEAK_BF16_TFLOPS, 4),
             "parallelism": "single-gpu",
+            "inputs": ("fp8: e4m3fn query/key/value/attentionOut, e5m2 dout, per-tensor factors"
+                       if args.fp8 else case.dtype),
         },
         "roofline": roofline,
         "cpu_baseline": cpu,

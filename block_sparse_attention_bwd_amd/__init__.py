@@ -9,6 +9,8 @@ from ._binding import (  # noqa: F401
     BSA_DTYPE_BOOL,
     BSA_DTYPE_F16,
     BSA_DTYPE_F32,
+    BSA_DTYPE_FP8_E4M3FN,
+    BSA_DTYPE_FP8_E5M2,
     BSA_ERR_INNER,
     BSA_ERR_PARAM_INVALID,
     BSA_ERR_PARAM_NULLPTR,
@@ -21,9 +23,13 @@ from ._binding import (  # noqa: F401
     block_sparse_attention,
     block_sparse_attention_grad,
     bsa_bwd,
+    bsa_bwd_fp8,
+    bsa_bwd_fp8_workspace_size,
     bsa_bwd_workspace_layout,
     bsa_bwd_workspace_size,
     bsa_fwd,
+    bsa_fwd_fp8,
+    bsa_fwd_fp8_workspace_size,
     bsa_fwd_workspace_size,
     bsa_last_error,
     bsa_profile_start,

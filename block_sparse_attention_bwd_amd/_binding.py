@@ -28,10 +28,12 @@ BSA_DTYPE_F16 = 1
 BSA_DTYPE_BF16 = 2
 BSA_DTYPE_F32 = 3
 BSA_DTYPE_BOOL = 4
+BSA_DTYPE_FP8_E4M3FN = 5
+BSA_DTYPE_FP8_E5M2 = 6
 
 NO_WINDOW = 2147483647
 WS_REGIONS = ("seq", "delta", "lse2", "row_cnt", "row_list", "col_cnt", "col_list", "plan", "partial",
-              "total")
+              "stage", "total")
 
 
 class bsa_tensor(ctypes.Structure):
@@ -89,6 +91,15 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.bsa_fwd_workspace_size.restype = ctypes.c_int
     lib.bsa_fwd.argtypes = _FWD + [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p]
     lib.bsa_fwd.restype = ctypes.c_int
+    _pd = ctypes.POINTER(ctypes.c_double)
+    lib.bsa_bwd_fp8_workspace_size.argtypes = _COMMON + [_pd, ctypes.POINTER(ctypes.c_uint64)]
+    lib.bsa_bwd_fp8_workspace_size.restype = ctypes.c_int
+    lib.bsa_bwd_fp8.argtypes = _COMMON + [_pd, ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p]
+    lib.bsa_bwd_fp8.restype = ctypes.c_int
+    lib.bsa_fwd_fp8_workspace_size.argtypes = _FWD + [_pd, ctypes.POINTER(ctypes.c_uint64)]
+    lib.bsa_fwd_fp8_workspace_size.restype = ctypes.c_int
+    lib.bsa_fwd_fp8.argtypes = _FWD + [_pd, ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p]
+    lib.bsa_fwd_fp8.restype = ctypes.c_int
     lib.bsa_last_error.argtypes = []
     lib.bsa_last_error.restype = ctypes.c_char_p
     lib.bsa_profile_start.argtypes = [ctypes.c_int32]
@@ -118,6 +129,8 @@ def _dtype_code(t) -> int:
         torch.float32: BSA_DTYPE_F32,
         torch.bool: BSA_DTYPE_BOOL,
         torch.uint8: BSA_DTYPE_BOOL,
+        torch.float8_e4m3fn: BSA_DTYPE_FP8_E4M3FN,
+        torch.float8_e5m2: BSA_DTYPE_FP8_E5M2,
     }.get(t.dtype, 0)
 
 
@@ -279,6 +292,96 @@ def bsa_fwd(query, key, value, block_sparse_mask=None, atten_mask=None, block_sh
         stream = torch.cuda.current_stream()
     handle = stream if isinstance(stream, int) else stream.cuda_stream
     _check(lib.bsa_fwd(*args, ws_ptr, int(workspace_size), ctypes.c_void_p(handle)))
+
+
+def _descale(descale, n):
+    """Host array of n dequantisation factors for the fp8 entry points (None -> NULL = all 1)."""
+    if descale is None:
+        return None
+    vals = [float(x) for x in descale]
+    if len(vals) != n:
+        raise ValueError(f"descale needs {n} factors, got {len(vals)}")
+    return (ctypes.c_double * n)(*vals)
+
+
+def _launch_args(workspace, workspace_size, stream):
+    import torch
+    if workspace_size is None:
+        workspace_size = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    ws_ptr = None if workspace is None or workspace.numel() == 0 else workspace.data_ptr()
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    handle = stream if isinstance(stream, int) else stream.cuda_stream
+    return ws_ptr, int(workspace_size), ctypes.c_void_p(handle)
+
+
+def _need_gpu(**tensors):
+    for name, t in tensors.items():
+        if t is not None and not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor")
+
+
+def bsa_bwd_fp8_workspace_size(dout, query, key, value, attention_out, softmax_lse, block_sparse_mask=None,
+                               atten_mask=None, block_shape=None, actual_seq_lengths=None,
+                               actual_seq_lengths_kv=None, q_input_layout="BNSD", kv_input_layout="BNSD",
+                               num_key_value_heads=1, mask_type=0, scale_value=1.0, pre_tokens=NO_WINDOW,
+                               next_tokens=NO_WINDOW, dq=None, dk=None, dv=None, descale=None) -> int:
+    """fp8 backward, phase 1.  ``descale``: factors of (dout, query, key, value, attention_out)."""
+    lib = load_library()
+    args = _marshal(dout, query, key, value, attention_out, softmax_lse, block_sparse_mask, atten_mask,
+                    block_shape, actual_seq_lengths, actual_seq_lengths_kv, q_input_layout,
+                    kv_input_layout, num_key_value_heads, mask_type, scale_value, pre_tokens,
+                    next_tokens, dq, dk, dv)
+    size = ctypes.c_uint64(0)
+    _check(lib.bsa_bwd_fp8_workspace_size(*args, _descale(descale, 5), ctypes.byref(size)))
+    return size.value
+
+
+def bsa_bwd_fp8(dout, query, key, value, attention_out, softmax_lse, block_sparse_mask=None, atten_mask=None,
+                block_shape=None, actual_seq_lengths=None, actual_seq_lengths_kv=None, q_input_layout="BNSD",
+                kv_input_layout="BNSD", num_key_value_heads=1, mask_type=0, scale_value=1.0,
+                pre_tokens=NO_WINDOW, next_tokens=NO_WINDOW, dq=None, dk=None, dv=None, descale=None,
+                workspace=None, workspace_size=None, stream=None) -> None:
+    """fp8 backward, phase 2: fp8 dout/query/key/value/attention_out, bf16 dq/dk/dv."""
+    lib = load_library()
+    _need_gpu(dout=dout, query=query, key=key, value=value, attention_out=attention_out,
+              softmax_lse=softmax_lse, block_sparse_mask=block_sparse_mask, dq=dq, dk=dk, dv=dv,
+              workspace=workspace)
+    args = _marshal(dout, query, key, value, attention_out, softmax_lse, block_sparse_mask, atten_mask,
+                    block_shape, actual_seq_lengths, actual_seq_lengths_kv, q_input_layout,
+                    kv_input_layout, num_key_value_heads, mask_type, scale_value, pre_tokens,
+                    next_tokens, dq, dk, dv)
+    _check(lib.bsa_bwd_fp8(*args, _descale(descale, 5), *_launch_args(workspace, workspace_size, stream)))
+
+
+def bsa_fwd_fp8_workspace_size(query, key, value, block_sparse_mask=None, atten_mask=None, block_shape=None,
+                               actual_seq_lengths=None, actual_seq_lengths_kv=None, q_input_layout="BNSD",
+                               kv_input_layout="BNSD", num_key_value_heads=1, mask_type=0, scale_value=1.0,
+                               pre_tokens=NO_WINDOW, next_tokens=NO_WINDOW, attention_out=None,
+                               softmax_lse=None, descale=None) -> int:
+    """fp8 forward, phase 1.  ``descale``: factors of (query, key, value)."""
+    lib = load_library()
+    args = _marshal_fwd(query, key, value, block_sparse_mask, atten_mask, block_shape, actual_seq_lengths,
+                        actual_seq_lengths_kv, q_input_layout, kv_input_layout, num_key_value_heads,
+                        mask_type, scale_value, pre_tokens, next_tokens, attention_out, softmax_lse)
+    size = ctypes.c_uint64(0)
+    _check(lib.bsa_fwd_fp8_workspace_size(*args, _descale(descale, 3), ctypes.byref(size)))
+    return size.value
+
+
+def bsa_fwd_fp8(query, key, value, block_sparse_mask=None, atten_mask=None, block_shape=None,
+                actual_seq_lengths=None, actual_seq_lengths_kv=None, q_input_layout="BNSD",
+                kv_input_layout="BNSD", num_key_value_heads=1, mask_type=0, scale_value=1.0,
+                pre_tokens=NO_WINDOW, next_tokens=NO_WINDOW, attention_out=None, softmax_lse=None,
+                descale=None, workspace=None, workspace_size=None, stream=None) -> None:
+    """fp8 forward, phase 2: fp8 query/key/value, bf16 attention_out, fp32 softmax_lse."""
+    lib = load_library()
+    _need_gpu(query=query, key=key, value=value, block_sparse_mask=block_sparse_mask,
+              attention_out=attention_out, softmax_lse=softmax_lse, workspace=workspace)
+    args = _marshal_fwd(query, key, value, block_sparse_mask, atten_mask, block_shape, actual_seq_lengths,
+                        actual_seq_lengths_kv, q_input_layout, kv_input_layout, num_key_value_heads,
+                        mask_type, scale_value, pre_tokens, next_tokens, attention_out, softmax_lse)
+    _check(lib.bsa_fwd_fp8(*args, _descale(descale, 3), *_launch_args(workspace, workspace_size, stream)))
 
 
 def block_sparse_attention(query, key, value, block_sparse_mask=None,

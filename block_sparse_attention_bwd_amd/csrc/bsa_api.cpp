@@ -62,13 +62,20 @@ struct Args {
   const bsa_tensor* dk;
   const bsa_tensor* dv;
   bool fwd;  // forward: dout/dq/dk/dv absent; attention_out and softmax_lse are outputs
+  bool fp8;                // fp8 entry points: fp8 data inputs, bf16 outputs
+  const double* descale;   // fp8: {dout, query, key, value, attention_out} or {query, key, value}; NULL = 1
 };
+
+enum Fp8Role { kRoleDout = 0, kRoleQuery, kRoleKey, kRoleValue, kRoleOut };
 
 struct Plan {
   bsa::Params p{};
   std::vector<bsa::SeqInfo> seq;
   uint64_t off[BSA_WS_NUM] = {};
   int64_t dims[4] = {};
+  bsa::Fp8Stage stage{};             // fp8: sources, formats and sizes (dst filled in at launch)
+  uint64_t stage_off[bsa::kMaxStaged] = {};  // fp8: offset of each bf16 copy within BSA_WS_STAGE
+  int stage_role[bsa::kMaxStaged] = {};  // which input each copy stands for (an Fp8Role)
 };
 
 bool row_major_contiguous(const bsa_tensor* t) {
@@ -86,6 +93,8 @@ const char* dtype_name(int32_t d) {
     case BSA_DTYPE_BF16: return "bfloat16";
     case BSA_DTYPE_F32: return "float32";
     case BSA_DTYPE_BOOL: return "bool";
+    case BSA_DTYPE_FP8_E4M3FN: return "float8_e4m3fn";
+    case BSA_DTYPE_FP8_E5M2: return "float8_e5m2";
     default: return "unknown";
   }
 }
@@ -149,16 +158,53 @@ int make_plan(const Args& a, Plan* plan) {
     return fail(BSA_ERR_PARAM_NULLPTR, "TND layout needs actualSeqLengthsKv");
 
   // ---- dtypes -----------------------------------------------------------
-  const int32_t dt = a.query->dtype;
-  if (dt != BSA_DTYPE_F16 && dt != BSA_DTYPE_BF16)
-    return fail(BSA_ERR_PARAM_INVALID, "query dtype %s is not float16/bfloat16", dtype_name(dt));
-  const Named same_dtype[] = {{a.dout, "dout"}, {a.key, "key"}, {a.value, "value"},
-                              {a.attention_out, "attentionOut"}, {a.dq, "dq"},
+  // (the kernels' element type: the data dtype, or bf16 for the fp8 entry
+  // points, whose inputs are decoded to bf16 copies first)
+  int32_t dt = a.query->dtype;
+  double fac[5] = {1, 1, 1, 1, 1};  // fp8 dequantisation factors: dout, query, key, value, attentionOut
+  if (a.fp8) {
+    const Named fp8_in[] = {{a.fwd ? nullptr : a.dout, "dout"}, {a.query, "query"}, {a.key, "key"},
+                            {a.value, "value"}, {a.fwd ? nullptr : a.attention_out, "attentionOut"}};
+    for (const Named& n : fp8_in)
+      if (n.t != nullptr && n.t->dtype != BSA_DTYPE_FP8_E4M3FN && n.t->dtype != BSA_DTYPE_FP8_E5M2)
+        return fail(BSA_ERR_PARAM_INVALID, "%s dtype %s is not float8_e4m3fn/float8_e5m2", n.name,
+                    dtype_name(n.t->dtype));
+    const Named bf16_out[] = {{a.fwd ? a.attention_out : nullptr, "attentionOut"}, {a.dq, "dq"},
                               {a.dk, "dk"}, {a.dv, "dv"}};
-  for (const Named& n : same_dtype)
-    if (n.t != nullptr && n.t->dtype != dt)
-      return fail(BSA_ERR_PARAM_INVALID, "%s dtype %s differs from query dtype %s", n.name,
-                  dtype_name(n.t->dtype), dtype_name(dt));
+    for (const Named& n : bf16_out)
+      if (n.t != nullptr && n.t->dtype != BSA_DTYPE_BF16)
+        return fail(BSA_ERR_PARAM_INVALID, "%s dtype %s is not bfloat16 (fp8 inputs give bf16 outputs)", n.name,
+                    dtype_name(n.t->dtype));
+    if (a.descale != nullptr) {
+      const int n = a.fwd ? 3 : 5;
+      for (int i = 0; i < n; ++i) {
+        const double f = a.descale[i];
+        if (!(std::isfinite(f) && f > 0))
+          return fail(BSA_ERR_PARAM_INVALID, "descale[%d] must be finite and > 0", i);
+        fac[a.fwd ? i + 1 : i] = f;
+      }
+    }
+    dt = BSA_DTYPE_BF16;
+  } else {
+    if (dt != BSA_DTYPE_F16 && dt != BSA_DTYPE_BF16)
+      return fail(BSA_ERR_PARAM_INVALID, "query dtype %s is not float16/bfloat16%s", dtype_name(dt),
+                  dt == BSA_DTYPE_FP8_E4M3FN || dt == BSA_DTYPE_FP8_E5M2 ? " (fp8 inputs: the bsa_*_fp8 entry points)"
+                                                                       : "");
+    const Named same_dtype[] = {{a.dout, "dout"}, {a.key, "key"}, {a.value, "value"},
+                                {a.attention_out, "attentionOut"}, {a.dq, "dq"},
+                                {a.dk, "dk"}, {a.dv, "dv"}};
+    for (const Named& n : same_dtype)
+      if (n.t != nullptr && n.t->dtype != dt)
+        return fail(BSA_ERR_PARAM_INVALID, "%s dtype %s differs from query dtype %s", n.name,
+                    dtype_name(n.t->dtype), dtype_name(dt));
+  }
+  {  // inputs are read with 16-byte vector loads and copies
+    const Named in16[] = {{a.fwd ? nullptr : a.dout, "dout"}, {a.query, "query"}, {a.key, "key"},
+                          {a.value, "value"}, {a.fwd ? nullptr : a.attention_out, "attentionOut"}};
+    for (const Named& n : in16)
+      if (n.t != nullptr && reinterpret_cast<uintptr_t>(n.t->data) % 16 != 0)
+        return fail(BSA_ERR_PARAM_INVALID, "%s data pointer is not 16-byte aligned", n.name);
+  }
   if (a.softmax_lse->dtype != BSA_DTYPE_F32)
     return fail(BSA_ERR_PARAM_INVALID, "softmaxLse dtype %s is not float32", dtype_name(a.softmax_lse->dtype));
   if (a.block_sparse_mask && a.block_sparse_mask->dtype != BSA_DTYPE_BOOL)
@@ -408,7 +454,19 @@ int make_plan(const Args& a, Plan* plan) {
     p.win_next = static_cast<int32_t>(std::max(-lim, std::min(lim, a.next_tokens)));
   }
   p.scale = static_cast<float>(a.scale_value);
-  p.scale_log2e = static_cast<float>(a.scale_value * 1.4426950408889634);
+  {
+    // fac: dout, query, key, value, attentionOut (all 1 without fp8 inputs)
+    const double sc = a.scale_value;
+    const double f[6] = {sc * fac[1] * fac[2] * 1.4426950408889634, sc * fac[0] * fac[3] * fac[2],
+                         sc * fac[0] * fac[3] * fac[1], fac[0], fac[4] / fac[3], fac[3]};
+    float* dst[6] = {&p.scale_log2e, &p.dq_scale, &p.dk_scale, &p.dv_scale, &p.delta_scale, &p.o_scale};
+    for (int i = 0; i < 6; ++i) {
+      *dst[i] = static_cast<float>(f[i]);
+      if (a.fp8 && !(std::isfinite(*dst[i]) && std::fabs(*dst[i]) >= 1.1754944e-38f))
+        return fail(BSA_ERR_PARAM_INVALID, "scaleValue and descale give a factor outside the fp32 normal range");
+    }
+    if (!a.fp8) p.o_scale = 1.f, p.delta_scale = 1.f, p.dv_scale = 1.f;  // exactly 1, not value / value
+  }
 
   plan->seq.resize(B);
   int64_t oq = 0, ok = 0;
@@ -446,6 +504,33 @@ int make_plan(const Args& a, Plan* plan) {
   const int64_t slots = max_pieces < bsa::kMaxSlots ? max_pieces : bsa::kMaxSlots;
   take(BSA_WS_PLAN, bwd * 4ull * bsa::plan_words(n_units, slots));
   take(BSA_WS_PARTIAL, bwd * 4ull * slots * 2 * bsa::kTileRowsMax * D);
+  // fp8: bf16 copies of the data inputs, each 256-byte aligned
+  uint64_t stage_bytes = 0;
+  if (a.fp8) {
+    struct In {
+      const bsa_tensor* t;
+      int role;
+    } ins[bsa::kMaxStaged] = {{a.fwd ? nullptr : a.dout, kRoleDout}, {a.query, kRoleQuery}, {a.key, kRoleKey},
+                              {a.value, kRoleValue}, {a.fwd ? nullptr : a.attention_out, kRoleOut}};
+    bsa::Fp8Stage& st = plan->stage;
+    for (const In& in : ins) {
+      if (in.t == nullptr) continue;
+      uint64_t numel = 1;
+      for (int d = 0; d < in.t->ndim; ++d) numel *= static_cast<uint64_t>(in.t->shape[d]);
+      const int i = st.count++;
+      st.src[i] = static_cast<const uint8_t*>(in.t->data);
+      st.n16[i] = static_cast<int64_t>(numel / 16);  // numel is a multiple of D, hence of 16
+      st.fmt[i] = in.t->dtype == BSA_DTYPE_FP8_E5M2 ? 1 : 0;
+      plan->stage_off[i] = stage_bytes;
+      plan->stage_role[i] = in.role;
+      stage_bytes = align_up(stage_bytes + 2 * numel);
+    }
+    int64_t groups = 0;
+    for (int i = 0; i < st.count; ++i) groups += st.n16[i];
+    if ((groups + 255) / 256 > bsa::kMaxGridGroups)
+      return fail(BSA_ERR_PARAM_INVALID, "fp8 inputs too large for one decode launch");
+  }
+  take(BSA_WS_STAGE, stage_bytes);
   plan->off[BSA_WS_TOTAL] = off;
   p.n_units = static_cast<int32_t>(n_units);
   p.n_dq_units = static_cast<int32_t>(B * N * nqb * nsub_q);
@@ -557,6 +642,21 @@ int run(const Args& a, void* workspace, uint64_t workspace_size, void* stream) {
   };
   if ((rc = mark(-1))) return rc;
   int herr = 0;
+  if (a.fp8) {  // decode the fp8 inputs into their bf16 copies; the kernels read those
+    bsa::Fp8Stage st = plan.stage;
+    for (int i = 0; i < st.count; ++i) {
+      st.dst[i] = reinterpret_cast<uint16_t*>(ws + plan.off[BSA_WS_STAGE] + plan.stage_off[i]);
+      const void* copy = st.dst[i];
+      switch (plan.stage_role[i]) {
+        case kRoleDout: p.dout = copy; break;
+        case kRoleQuery: p.q = copy; break;
+        case kRoleKey: p.k = copy; break;
+        case kRoleValue: p.v = copy; break;
+        default: p.o = copy; break;
+      }
+    }
+    if ((herr = bsa::launch_stage_fp8(st, stream))) return launch_failed(herr, "fp8 decode");
+  }
   for (size_t first = 0; first < plan.seq.size() && herr == 0; first += bsa::kMaxInlineSeq) {
     bsa::SeqChunk chunk{};
     chunk.first = static_cast<int32_t>(first);
@@ -661,6 +761,49 @@ int bsa_fwd_workspace_size(BSA_FWD_ARGS_DECL, uint64_t* workspace_size) {
 int bsa_fwd(BSA_FWD_ARGS_DECL, void* workspace, uint64_t workspace_size, void* stream) {
   g_err.clear();
   return run(BSA_FWD_ARGS_PACK, workspace, workspace_size, stream);
+}
+
+int bsa_bwd_fp8_workspace_size(BSA_ARGS_DECL, const double* descale, uint64_t* workspace_size) {
+  g_err.clear();
+  if (workspace_size == nullptr) return fail(BSA_ERR_PARAM_NULLPTR, "workspaceSize is a null pointer");
+  Args a = BSA_ARGS_PACK;
+  a.fp8 = true;
+  a.descale = descale;
+  Plan plan;
+  int rc = make_plan(a, &plan);
+  if (rc) return rc;
+  *workspace_size = plan.off[BSA_WS_TOTAL];
+  return BSA_OK;
+}
+
+int bsa_bwd_fp8(BSA_ARGS_DECL, const double* descale, void* workspace, uint64_t workspace_size, void* stream) {
+  g_err.clear();
+  Args a = BSA_ARGS_PACK;
+  a.fp8 = true;
+  a.descale = descale;
+  return run(a, workspace, workspace_size, stream);
+}
+
+int bsa_fwd_fp8_workspace_size(BSA_FWD_ARGS_DECL, const double* descale, uint64_t* workspace_size) {
+  g_err.clear();
+  if (workspace_size == nullptr) return fail(BSA_ERR_PARAM_NULLPTR, "workspaceSize is a null pointer");
+  Args a = BSA_FWD_ARGS_PACK;
+  a.fp8 = true;
+  a.descale = descale;
+  Plan plan;
+  int rc = make_plan(a, &plan);
+  if (rc) return rc;
+  *workspace_size = plan.off[BSA_WS_TOTAL];
+  return BSA_OK;
+}
+
+int bsa_fwd_fp8(BSA_FWD_ARGS_DECL, const double* descale, void* workspace, uint64_t workspace_size,
+                void* stream) {
+  g_err.clear();
+  Args a = BSA_FWD_ARGS_PACK;
+  a.fp8 = true;
+  a.descale = descale;
+  return run(a, workspace, workspace_size, stream);
 }
 
 const char* bsa_last_error(void) { return g_err.c_str(); }

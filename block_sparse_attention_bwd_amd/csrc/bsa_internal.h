@@ -55,7 +55,13 @@ struct Params {
   const uint8_t* amask;
   int64_t amask_ld;
   float scale;         // scale_value rounded to fp32
-  float scale_log2e;   // scale * log2(e)
+  float scale_log2e;   // factor from a raw score (row dot product) to log2 units: scale * log2(e)
+                       // (fp8 inputs: times query's and key's dequantisation factors)
+  // Factors applied to the fp32 accumulators on the way out, and to the row
+  // sums of dOut o Out; for fp16/bf16 inputs: scale, scale, 1, 1, 1.  With fp8
+  // inputs the kernels run on the codes' values (factor 1) and these restore
+  // the dequantised result (see the fp8 entry points).
+  float dq_scale, dk_scale, dv_scale, delta_scale, o_scale;
 
   // workspace regions
   SeqInfo* seq;
@@ -131,7 +137,20 @@ struct SeqChunk {
   int32_t count;
 };
 
+// fp8 -> bf16 staging: up to five tensors, each `n16` groups of 16 bytes,
+// decoded element by element into bf16 copies (exact: every E4M3FN and E5M2
+// value is a bf16 value).  fmt: 0 = E4M3FN, 1 = E5M2.
+constexpr int kMaxStaged = 5;
+struct Fp8Stage {
+  const uint8_t* src[kMaxStaged];
+  uint16_t* dst[kMaxStaged];
+  int64_t n16[kMaxStaged];
+  int32_t fmt[kMaxStaged];
+  int32_t count;
+};
+
 // Launch helpers (bsa_kernels.hip).  Return a hipError_t value (0 = success).
+int launch_stage_fp8(const Fp8Stage& st, void* stream);
 int launch_stage_seq(const SeqChunk& chunk, SeqInfo* dst, float* consts, void* stream);
 int launch_prologue(const Params& p, void* stream);
 int launch_plan(const Params& p, void* stream);

@@ -117,6 +117,56 @@ __global__ void stage_seq_kernel(SeqChunk c, SeqInfo* dst, float* consts) {
 }
 
 // ---------------------------------------------------------------------------
+// fp8 inputs: decode to bf16 copies
+// ---------------------------------------------------------------------------
+// OCP 8-bit floats -> bf16 bit patterns, exactly.  E4M3FN: sign, 4 exponent
+// bits (bias 7), 3 mantissa bits, NaN only at exponent 15 / mantissa 7, no
+// infinities; E5M2: sign, 5 exponent bits (bias 15), 2 mantissa bits, IEEE
+// infinities and NaNs.  A normal code keeps its mantissa bits at the top of
+// bf16's 7 and moves its exponent to bias 127; a subnormal one (exponent 0) is
+// m * 2^(1 - bias - man), formed in fp32 (exact) and cut to bf16 (exact: at
+// most 3 significant bits).
+__device__ __forceinline__ unsigned short fp8_to_bf16(unsigned c, bool e5m2) {
+  const unsigned sgn = (c & 0x80u) << 8;
+  const unsigned man_bits = e5m2 ? 2u : 3u;
+  const unsigned e = (c & 0x7fu) >> man_bits;
+  const unsigned m = c & ((1u << man_bits) - 1u);
+  const unsigned emax = e5m2 ? 31u : 15u;
+  const int bias = e5m2 ? 15 : 7;
+  unsigned bits;
+  if (e == 0) {
+    const float v = static_cast<float>(m) * __builtin_ldexpf(1.f, 1 - bias - static_cast<int>(man_bits));
+    bits = __float_as_uint(v) >> 16;
+  } else {
+    bits = ((e + 127u - bias) << 7) | (m << (7u - man_bits));
+  }
+  if (e5m2 && e == emax) bits = m == 0 ? 0x7f80u : 0x7fc0u;  // infinity, NaN
+  if (!e5m2 && e == emax && m == 7u) bits = 0x7fc0u;          // NaN
+  return static_cast<unsigned short>(sgn | bits);
+}
+
+// One thread per 16-byte group: 16 codes in, two 16-byte stores of bf16 out.
+// Groups are numbered over the tensors in order; a workgroup may straddle two.
+__global__ __launch_bounds__(256) void stage_fp8_kernel(Fp8Stage st) {
+  int64_t gid = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  int t = 0;
+  while (t < st.count && gid >= st.n16[t]) gid -= st.n16[t++];
+  if (t >= st.count) return;
+  const bool e5 = st.fmt[t] == 1;
+  const uint4 in = reinterpret_cast<const uint4*>(st.src[t])[gid];
+  const unsigned w[4] = {in.x, in.y, in.z, in.w};
+  u16x8 lo, hi;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    lo[i] = fp8_to_bf16((w[i >> 2] >> (8 * (i & 3))) & 0xffu, e5);
+    hi[i] = fp8_to_bf16((w[2 + (i >> 2)] >> (8 * (i & 3))) & 0xffu, e5);
+  }
+  u16x8* out = reinterpret_cast<u16x8*>(st.dst[t]) + 2 * gid;
+  out[0] = lo;
+  out[1] = hi;
+}
+
+// ---------------------------------------------------------------------------
 // prologue: softmax_grad + lse2, block lists
 // ---------------------------------------------------------------------------
 // softmax_grad = row sums of dOut o Out, and lse2 = LSE * log2(e), for every
@@ -173,7 +223,7 @@ __device__ void delta_part(const Params& p, int blk) {
 #pragma unroll
     for (int m = LPR / 2; m >= 1; m >>= 1) acc[k] += __shfl_xor(acc[k], m);
     if (sub == 0 && out[k] >= 0) {
-      p.delta[out[k]] = acc[k];
+      p.delta[out[k]] = acc[k] * p.delta_scale;
       p.lse2[out[k]] = l2[k];
     }
   }
@@ -867,7 +917,7 @@ __device__ __forceinline__ void dkdv_work(const Params& p, int item, unsigned sh
     have = more;
   }
 
-  if (pieces > 1) {  // fp32 partial of this piece; the reduction applies the scale
+  if (pieces > 1) {  // fp32 partial of this piece; the reduction applies the output factors
     float* dst = p.partial + static_cast<int64_t>(unit_base[u] + piece) * 2 * kTileRowsMax * D;
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
@@ -890,8 +940,8 @@ __device__ __forceinline__ void dkdv_work(const Params& p, int item, unsigned sh
     for (int i = 0; i < 16; ++i) {
       const int r = kv0 + 32 * w + 8 * (i >> 2) + 4 * g + (i & 3);
       if (r < w_end) {
-        if constexpr (kDoK) dkp[r * p.dk_sr + 32 * nt + l32] = E::from_f32(adk[nt][i] * p.scale);
-        if constexpr (kDoV) dvp[r * p.dv_sr + 32 * nt + l32] = E::from_f32(adv[nt][i]);
+        if constexpr (kDoK) dkp[r * p.dk_sr + 32 * nt + l32] = E::from_f32(adk[nt][i] * p.dk_scale);
+        if constexpr (kDoV) dvp[r * p.dv_sr + 32 * nt + l32] = E::from_f32(adv[nt][i] * p.dv_scale);
       }
     }
   }
@@ -951,7 +1001,7 @@ __device__ void reduce_pieces(const Params& p, int s) {
       acc.z += x.z;
       acc.w += x.w;
     }
-    const float sc = t == 0 ? p.scale : 1.f;
+    const float sc = t == 0 ? p.dk_scale : p.dv_scale;
     unsigned short* dst = (t == 0 ? dkp + (kv0 + rl) * p.dk_sr : dvp + (kv0 + rl) * p.dv_sr) + d;
     dst[0] = E::from_f32(acc.x * sc);
     dst[1] = E::from_f32(acc.y * sc);
@@ -1106,7 +1156,7 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(D >= 256
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int r = q0 + 32 * w + 8 * (i >> 2) + 4 * g + (i & 3);
-      if (r < w_end) dqp[r * p.dq_sr + 32 * nt + l32] = E::from_f32(adq[nt][i] * p.scale);
+      if (r < w_end) dqp[r * p.dq_sr + 32 * nt + l32] = E::from_f32(adq[nt][i] * p.dq_scale);
     }
   }
 }
@@ -1269,7 +1319,7 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(D >= 256
 
   float l_tot = l_run + __shfl_xor(l_run, 32);
   if (!q_ok) l_tot = 0.f;  // padding rows: nothing selected by definition
-  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  const float inv = (l_tot > 0.f ? 1.f / l_tot : 0.f) * p.o_scale;
   if (my_q < w_end) {
     unsigned short* op = static_cast<unsigned short*>(p.out_o) + b * p.o_sb + si.off_q * p.o_sr + n * p.o_sh +
                          static_cast<int64_t>(my_q) * p.o_sr;
@@ -1299,6 +1349,15 @@ inline int waves_for(int rows) {
 }
 
 }  // namespace
+
+int launch_stage_fp8(const Fp8Stage& st, void* stream) {
+  int64_t groups = 0;
+  for (int t = 0; t < st.count; ++t) groups += st.n16[t];
+  if (groups == 0) return 0;
+  hipLaunchKernelGGL(stage_fp8_kernel, dim3(static_cast<unsigned>((groups + 255) / 256)), dim3(256), 0,
+                     static_cast<hipStream_t>(stream), st);
+  return static_cast<int>(hipGetLastError());
+}
 
 int launch_stage_seq(const SeqChunk& chunk, SeqInfo* dst, float* consts, void* stream) {
   hipLaunchKernelGGL(stage_seq_kernel, dim3(1), dim3(kMaxInlineSeq), 0,

@@ -29,7 +29,9 @@
  * and the stream.  The library allocates no device memory, frees nothing and
  * never synchronises the stream.  Host arrays (block_shape, actual_seq_*) and
  * strings are read only during the call.  All tensors passed to bsa_bwd must
- * live in device memory of the current HIP device.  Every element of dq/dk/dv
+ * live in device memory of the current HIP device, and the data pointers of the
+ * input tensors (dout, query, key, value, attention_out) must be 16-byte
+ * aligned (161002 otherwise).  Every element of dq/dk/dv
  * is written (zeros where nothing contributes: padded BNSD rows, query rows
  * that select no key, keys no row selects), so outputs need no pre-zeroing.
  * Calls on different streams that share a workspace race; give each in-flight
@@ -53,7 +55,11 @@ enum bsa_dtype {
   BSA_DTYPE_F16 = 1,
   BSA_DTYPE_BF16 = 2,
   BSA_DTYPE_F32 = 3,
-  BSA_DTYPE_BOOL = 4 /* one byte per element, nonzero = selected (UINT8 accepted) */
+  BSA_DTYPE_BOOL = 4, /* one byte per element, nonzero = selected (UINT8 accepted) */
+  /* 8-bit floats (the page's FLOAT8_E4M3FN / FLOAT8_E5M2, OCP encodings);
+   * taken only by the bsa_*_fp8 entry points */
+  BSA_DTYPE_FP8_E4M3FN = 5, /* sign, 4 exponent bits (bias 7), 3 mantissa bits; no inf, NaN = 0x7f/0xff */
+  BSA_DTYPE_FP8_E5M2 = 6    /* sign, 5 exponent bits (bias 15), 2 mantissa bits; IEEE inf/NaN */
 };
 
 /* Status codes (返回值 table of the page; runtime/inner codes of the same family). */
@@ -188,6 +194,77 @@ int bsa_fwd(const bsa_tensor* query, const bsa_tensor* key, const bsa_tensor* va
             const bsa_tensor* attention_out, const bsa_tensor* softmax_lse, void* workspace,
             uint64_t workspace_size, void* stream);
 
+/*
+ * fp8 inputs with per-tensor scaling.  The page lists FLOAT8_E4M3FN and
+ * FLOAT8_E5M2 as types some products do not take (产品支持情况 note under 参数说明)
+ * and fixes no scaling rule; here each fp8 input tensor carries one
+ * dequantisation factor: the value of an element is its decoded code times
+ * the factor, and the operation is the one above on those values.
+ *
+ * Arguments are those of bsa_bwd_workspace_size / bsa_bwd (resp. the
+ * forward's), in the same order and with the same rules, except:
+ *  dout, query, key, value, attention_out
+ *                  BSA_DTYPE_FP8_E4M3FN or BSA_DTYPE_FP8_E5M2, chosen per
+ *                  tensor (e.g. E5M2 for dout, E4M3FN for the others);
+ *                  contiguous, 16-byte aligned.  In the forward,
+ *                  attention_out is the output and must be bf16.
+ *  dq, dk, dv      outputs, BSA_DTYPE_BF16 (an fp8 gradient with no output
+ *                  factor would lose most of its range).
+ *  descale         host array: factors of {dout, query, key, value,
+ *                  attention_out} (backward) or {query, key, value}
+ *                  (forward), each finite and > 0; NULL = all 1.  Read only
+ *                  during the call.
+ * The inputs are decoded exactly into bf16 copies in the workspace (region
+ * BSA_WS_STAGE, 2 bytes per input element) and the bf16 kernels run on the
+ * codes' values; the factors are applied in fp32 where the scores are formed
+ * (scale * f_query * f_key), to softmax_grad (f_attention_out / f_value) and to
+ * the outputs (dQ: scale * f_dout * f_value * f_key, dK: scale * f_dout *
+ * f_value * f_query, dV: f_dout; forward O: f_value).  Ownership, stream,
+ * workspace and error behaviour are those of bsa_bwd / bsa_fwd; the
+ * fp16/bf16 entry points reject fp8 dtypes and these reject fp16/bf16 inputs.
+ */
+int bsa_bwd_fp8_workspace_size(const bsa_tensor* dout, const bsa_tensor* query, const bsa_tensor* key,
+                               const bsa_tensor* value, const bsa_tensor* attention_out,
+                               const bsa_tensor* softmax_lse, const bsa_tensor* block_sparse_mask,
+                               const bsa_tensor* atten_mask, const int64_t* block_shape,
+                               int64_t block_shape_len, const int64_t* actual_seq_lengths,
+                               int64_t actual_seq_lengths_len, const int64_t* actual_seq_lengths_kv,
+                               int64_t actual_seq_lengths_kv_len, const char* q_input_layout,
+                               const char* kv_input_layout, int64_t num_key_value_heads, int64_t mask_type,
+                               double scale_value, int64_t pre_tokens, int64_t next_tokens,
+                               const bsa_tensor* dq, const bsa_tensor* dk, const bsa_tensor* dv,
+                               const double* descale, uint64_t* workspace_size);
+
+int bsa_bwd_fp8(const bsa_tensor* dout, const bsa_tensor* query, const bsa_tensor* key,
+                const bsa_tensor* value, const bsa_tensor* attention_out, const bsa_tensor* softmax_lse,
+                const bsa_tensor* block_sparse_mask, const bsa_tensor* atten_mask,
+                const int64_t* block_shape, int64_t block_shape_len, const int64_t* actual_seq_lengths,
+                int64_t actual_seq_lengths_len, const int64_t* actual_seq_lengths_kv,
+                int64_t actual_seq_lengths_kv_len, const char* q_input_layout,
+                const char* kv_input_layout, int64_t num_key_value_heads, int64_t mask_type,
+                double scale_value, int64_t pre_tokens, int64_t next_tokens, const bsa_tensor* dq,
+                const bsa_tensor* dk, const bsa_tensor* dv, const double* descale, void* workspace,
+                uint64_t workspace_size, void* stream);
+
+int bsa_fwd_fp8_workspace_size(const bsa_tensor* query, const bsa_tensor* key, const bsa_tensor* value,
+                               const bsa_tensor* block_sparse_mask, const bsa_tensor* atten_mask,
+                               const int64_t* block_shape, int64_t block_shape_len,
+                               const int64_t* actual_seq_lengths, int64_t actual_seq_lengths_len,
+                               const int64_t* actual_seq_lengths_kv, int64_t actual_seq_lengths_kv_len,
+                               const char* q_input_layout, const char* kv_input_layout,
+                               int64_t num_key_value_heads, int64_t mask_type, double scale_value,
+                               int64_t pre_tokens, int64_t next_tokens, const bsa_tensor* attention_out,
+                               const bsa_tensor* softmax_lse, const double* descale, uint64_t* workspace_size);
+
+int bsa_fwd_fp8(const bsa_tensor* query, const bsa_tensor* key, const bsa_tensor* value,
+                const bsa_tensor* block_sparse_mask, const bsa_tensor* atten_mask, const int64_t* block_shape,
+                int64_t block_shape_len, const int64_t* actual_seq_lengths, int64_t actual_seq_lengths_len,
+                const int64_t* actual_seq_lengths_kv, int64_t actual_seq_lengths_kv_len,
+                const char* q_input_layout, const char* kv_input_layout, int64_t num_key_value_heads,
+                int64_t mask_type, double scale_value, int64_t pre_tokens, int64_t next_tokens,
+                const bsa_tensor* attention_out, const bsa_tensor* softmax_lse, const double* descale,
+                void* workspace, uint64_t workspace_size, void* stream);
+
 /* Workspace regions, as byte offsets filled in by bsa_bwd_workspace_layout. */
 enum bsa_ws_region {
   BSA_WS_SEQ = 0,      /* per-sequence table {int64 q_offset, kv_offset; int32 len_q, len_kv, wlim_q, wlim_kv} x B, then 128 fp32 constants */
@@ -199,8 +276,9 @@ enum bsa_ws_region {
   BSA_WS_COL_LIST = 6, /* int32 [B, N, nKB, nQB]: ascending Q-block lists, first COL_CNT entries valid */
   BSA_WS_PLAN = 7,     /* int32: dK/dV work split (chunk size, per-unit piece counts and slots, slot table) */
   BSA_WS_PARTIAL = 8,  /* fp32 per-piece dK/dV partial sums of split units, reduced in piece order */
-  BSA_WS_TOTAL = 9,    /* total bytes (== the phase-1 size) */
-  BSA_WS_NUM = 10
+  BSA_WS_STAGE = 9,    /* fp8 entry points only (else empty): bf16 copies of the fp8 inputs, each 256-byte aligned */
+  BSA_WS_TOTAL = 10,   /* total bytes (== the phase-1 size) */
+  BSA_WS_NUM = 11
 };
 
 /*
@@ -231,7 +309,8 @@ const char* bsa_last_error(void);
  * between their kernel stages (on the call's stream).  bsa_profile_stop waits
  * for the recorded events, writes the summed milliseconds of each stage into
  * stage_ms[0..n_stages) (stage order: 0 = sequence table + softmax_grad + mask
- * compaction + work plan, 1 = dK/dV, 2 = dQ + the sum of split dK/dV units,
+ * compaction + work plan (+ the fp8 decode of the fp8 entry points),
+ * 1 = dK/dV, 2 = dQ + the sum of split dK/dV units,
  * 3 = forward; a stage a call does not run adds 0), writes the number of
  * profiled calls to *n_calls, frees the events and turns recording off.
  * Not thread-safe.

@@ -48,6 +48,8 @@ __all__ = [
     "round_to_dtype",
     "dtype_bits",
     "CONFIG_NAMES",
+    "FP8_MAX",
+    "quantize_fp8",
 ]
 
 CONFIG_NAMES = {
@@ -298,6 +300,24 @@ def config(k: int, seed: Optional[int] = None, head_dim: Optional[int] = None) -
         kw["scale"] = 1.0 / math.sqrt(kw["D"])
         name = f"{name}_d{kw['D']}"
     return make_case(seed=seed, name=name, **kw)
+
+
+FP8_MAX = {"e4m3fn": 448.0, "e5m2": 57344.0}
+
+
+def quantize_fp8(x: np.ndarray, fmt: str, factor: Optional[float] = None):
+    """Input synthesis for fp8 runs: per-tensor factor (default max|x| / the
+    format's largest finite value, so nothing saturates) and the codes of
+    x / factor rounded to nearest-even by torch's float8 conversion.
+    Returns (uint8 codes, factor)."""
+    import torch
+    tdt = {"e4m3fn": torch.float8_e4m3fn, "e5m2": torch.float8_e5m2}[fmt]
+    x = np.asarray(x, dtype=np.float64)
+    if factor is None:
+        amax = float(np.abs(x).max()) if x.size else 0.0
+        factor = amax / FP8_MAX[fmt] if amax > 0 else 1.0
+    codes = torch.from_numpy(np.ascontiguousarray(x / factor, dtype=np.float32)).to(tdt).view(torch.uint8)
+    return codes.numpy(), float(factor)
 
 
 def active_blocks(case: Case) -> int:
