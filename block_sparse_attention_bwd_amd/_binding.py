@@ -33,7 +33,7 @@ BSA_DTYPE_FP8_E5M2 = 6
 
 NO_WINDOW = 2147483647
 WS_REGIONS = ("seq", "delta", "lse2", "row_cnt", "row_list", "col_cnt", "col_list", "plan", "partial",
-              "stage", "total")
+              "amask", "stage", "total")
 
 
 class bsa_tensor(ctypes.Structure):

@@ -504,6 +504,12 @@ int make_plan(const Args& a, Plan* plan) {
   const int64_t slots = max_pieces < bsa::kMaxSlots ? max_pieces : bsa::kMaxSlots;
   take(BSA_WS_PLAN, bwd * 4ull * bsa::plan_words(n_units, slots));
   take(BSA_WS_PARTIAL, bwd * 4ull * slots * 2 * bsa::kTileRowsMax * D);
+  // attenMask as bits: by query row (all) and by key (the backward's dK/dV kernel)
+  const bool am = a.atten_mask != nullptr;
+  const uint64_t wk = static_cast<uint64_t>(ceil_div(Skv, 32)), wq = static_cast<uint64_t>(ceil_div(Sq, 32));
+  take(BSA_WS_AMASK, am ? 4 * (static_cast<uint64_t>(Sq) * wk + bwd * static_cast<uint64_t>(Skv) * wq) : 0);
+  p.am_wk = static_cast<int32_t>(wk);
+  p.am_wq = static_cast<int32_t>(wq);
   // fp8: bf16 copies of the data inputs, each 256-byte aligned
   uint64_t stage_bytes = 0;
   if (a.fp8) {
@@ -631,6 +637,10 @@ int run(const Args& a, void* workspace, uint64_t workspace_size, void* stream) {
     p.plan = reinterpret_cast<int32_t*>(ws + plan.off[BSA_WS_PLAN]);
     p.partial = reinterpret_cast<float*>(ws + plan.off[BSA_WS_PARTIAL]);
   }
+  if (p.amask) {
+    p.am_rows = reinterpret_cast<uint32_t*>(ws + plan.off[BSA_WS_AMASK]);
+    p.am_cols = a.fwd ? nullptr : p.am_rows + static_cast<uint64_t>(p.sq_max) * p.am_wk;
+  }
 
   // Profiling: one event before the first stage and one after each stage run.
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -664,6 +674,7 @@ int run(const Args& a, void* workspace, uint64_t workspace_size, void* stream) {
     for (int i = 0; i < chunk.count; ++i) chunk.s[i] = plan.seq[first + i];
     herr = bsa::launch_stage_seq(chunk, p.seq, consts, stream);
   }
+  if (herr == 0 && p.amask) herr = bsa::launch_pack_amask(p, stream);
   if (a.fwd) {
     if (herr == 0) herr = bsa::launch_prologue_rows(p, stream);
     if (herr) return launch_failed(herr, "prologue");

@@ -54,6 +54,12 @@ struct Params {
   // attenMask [maxSq, maxSkv] bytes, 1 = the pair does not take part (nullptr: none)
   const uint8_t* amask;
   int64_t amask_ld;
+  // the attenMask packed to bits (1 = excluded) by pack_amask_kernel:
+  // am_rows[i * am_wk + w] bit b <-> (query i, key 32 w + b);
+  // am_cols[j * am_wq + w] bit b <-> (query 32 w + b, key j); zero past the edges
+  uint32_t* am_rows;
+  uint32_t* am_cols;    // nullptr in the forward (only the row form is read there)
+  int32_t am_wk, am_wq; // ceil(maxSkv / 32), ceil(maxSq / 32)
   float scale;         // scale_value rounded to fp32
   float scale_log2e;   // factor from a raw score (row dot product) to log2 units: scale * log2(e)
                        // (fp8 inputs: times query's and key's dequantisation factors)
@@ -151,6 +157,7 @@ struct Fp8Stage {
 
 // Launch helpers (bsa_kernels.hip).  Return a hipError_t value (0 = success).
 int launch_stage_fp8(const Fp8Stage& st, void* stream);
+int launch_pack_amask(const Params& p, void* stream);  // attenMask -> am_rows / am_cols
 int launch_stage_seq(const SeqChunk& chunk, SeqInfo* dst, float* consts, void* stream);
 int launch_prologue(const Params& p, void* stream);
 int launch_plan(const Params& p, void* stream);

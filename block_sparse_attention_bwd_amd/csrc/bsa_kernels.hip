@@ -95,9 +95,11 @@ __device__ __forceinline__ bool in_band(const Params& p, int i, int j) {
 __device__ __forceinline__ bool rect_in_band(const Params& p, int r0, int nr, int c0, int nc) {
   return !p.win || (c0 - (r0 + nr - 1) >= -p.win_pre && (c0 + nc - 1) - r0 <= p.win_next);
 }
-// attenMask: the pair (query i, key j), both in range, is not excluded.
-__device__ __forceinline__ bool amask_keeps(const Params& p, int i, int j) {
-  return p.amask[static_cast<int64_t>(i) * p.amask_ld + j] == 0;
+// attenMask bits of a 32-key slice starting at key row0, for the query of
+// lane l32, from the two words staged for it (bit k: key row0 + k excluded).
+__device__ __forceinline__ uint32_t mask_word(const uint32_t* staged, int row0, int l32) {
+  const uint64_t two = (static_cast<uint64_t>(staged[32 + l32]) << 32) | staged[l32];
+  return static_cast<uint32_t>(two >> (row0 & 31));
 }
 // Some pair of the rectangle is in the window.
 __device__ __forceinline__ bool rect_meets_band(const Params& p, int r0, int nr, int c0, int nc) {
@@ -164,6 +166,40 @@ __global__ __launch_bounds__(256) void stage_fp8_kernel(Fp8Stage st) {
   u16x8* out = reinterpret_cast<u16x8*>(st.dst[t]) + 2 * gid;
   out[0] = lo;
   out[1] = hi;
+}
+
+// ---------------------------------------------------------------------------
+// attenMask: bytes -> bits
+// ---------------------------------------------------------------------------
+// One wave per 64 x 64 tile of the [maxSq, maxSkv] byte mask: lane l reads
+// column j0 + l of each of the 64 rows (64 contiguous bytes per row); a
+// ballot over the lanes gives the row's two 32-key words, and each lane
+// gathers its column's two 32-query words in registers.  Bits past the
+// mask's edges are 0.
+__global__ __launch_bounds__(256) void pack_amask_kernel(Params p, int tiles_i, int tiles_j) {
+  const int lane = threadIdx.x & 63;
+  const int64_t tile = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (tile >= static_cast<int64_t>(tiles_i) * tiles_j) return;  // uniform over the wave
+  const int ti = static_cast<int>(tile / tiles_j), tj = static_cast<int>(tile % tiles_j);
+  const int i0 = 64 * ti, j = 64 * tj + lane;
+  const int sq = p.sq_max;
+  const int64_t skv = p.amask_ld;
+  uint32_t col[2] = {0u, 0u};
+#pragma unroll 8
+  for (int r = 0; r < 64; ++r) {
+    const int i = i0 + r;
+    const bool x = i < sq && j < skv && p.amask[static_cast<int64_t>(i) * skv + j] != 0;
+    const uint64_t row = __ballot(x);
+    const int w = 2 * tj + lane;
+    if (i < sq && lane < 2 && w < p.am_wk)
+      p.am_rows[static_cast<int64_t>(i) * p.am_wk + w] = static_cast<uint32_t>(lane ? row >> 32 : row);
+    col[r >> 5] |= static_cast<uint32_t>(x) << (r & 31);
+  }
+  if (p.am_cols != nullptr && j < skv) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      if (2 * ti + h < p.am_wq) p.am_cols[static_cast<int64_t>(j) * p.am_wq + 2 * ti + h] = col[h];
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -728,10 +764,17 @@ __host__ __device__ constexpr int dkdv_tile_rows() {
   return (D >= 256 ? 16 : 32) * W < 32 ? 32 : (D >= 256 ? 16 : 32) * W;
 }
 
-template <class E, int D, int W, int MODE>
+// attenMask words staged with a Q tile: for each of the workgroup's KV
+// columns, the 32-query words covering the tile's rows (one more than H / 32,
+// as the tile need not start on a word boundary).
+template <int D, int W>
+__host__ __device__ constexpr int dkdv_mask_words() { return dkdv_tile_rows<D, W>() / 32 + 1; }
+
+template <class E, int D, int W, int MODE, bool AM>
 __device__ __forceinline__ void dkdv_work(const Params& p, int item, unsigned short (*sQ)[dkdv_tile_rows<D, W>() * D],
                                           unsigned short (*sO)[dkdv_tile_rows<D, W>() * D],
-                                          float (*sL)[dkdv_tile_rows<D, W>()], float (*sDl)[dkdv_tile_rows<D, W>()]) {
+                                          float (*sL)[dkdv_tile_rows<D, W>()], float (*sDl)[dkdv_tile_rows<D, W>()],
+                                          uint32_t (*sB)[AM ? dkdv_mask_words<D, W>() : 1][32 * W]) {
   constexpr int KS = D / 16;  // K=16 steps over the head dim
   constexpr int NT = D / 32;  // 32-wide column tiles of the head dim
   constexpr int H = dkdv_tile_rows<D, W>();
@@ -826,6 +869,17 @@ __device__ __forceinline__ void dkdv_work(const Params& p, int item, unsigned sh
       dma4(r < rows ? static_cast<const void*>(p.lse2 + li) : p.consts + kConstPosInf, lds_addr(&sL[buf][RW * w]));
       dma4(r < rows ? static_cast<const void*>(p.delta + li) : p.consts, lds_addr(&sDl[buf][RW * w]));
     }
+    if constexpr (AM) {  // attenMask bits of this wave's 32 KV columns over the tile's rows
+      if (lane < 32) {
+        const int wb = t.q0 >> 5;
+#pragma unroll
+        for (int m = 0; m < dkdv_mask_words<D, W>(); ++m) {
+          const bool ok = my_kv < kv_end && wb + m < p.am_wq;
+          dma4(ok ? static_cast<const void*>(p.am_cols + static_cast<int64_t>(my_kv) * p.am_wq + wb + m) : p.consts,
+               lds_addr(&sB[buf][m][32 * w]));
+        }
+      }
+    }
   };
 #pragma unroll
   for (int s = 0; s < KS; ++s) {  // complete the K/V loads before the first copy
@@ -874,7 +928,7 @@ __device__ __forceinline__ void dkdv_work(const Params& p, int item, unsigned sh
         d4[a] = *reinterpret_cast<const float4*>(tD + c0 + 8 * a + 4 * g);
       }
       float pv[16], dsv[16];
-      if (!p.amask && rect_in_band(p, cur.q0 + c0, 32, kv0 + 32 * w, 32)) {  // uniform: no mask cuts anything here
+      if (!AM && rect_in_band(p, cur.q0 + c0, 32, kv0 + 32 * w, 32)) {  // uniform: no mask cuts anything here
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const float li = l4[i >> 2][i & 3], di = d4[i >> 2][i & 3];
@@ -883,13 +937,20 @@ __device__ __forceinline__ void dkdv_work(const Params& p, int item, unsigned sh
           dsv[i] = pv[i] * (dpv[i] - di);              // dS = P o (dP - softmax_grad)
         }
       } else {
+        // attenMask bits of this lane's 32 query rows (bit r: row cur.q0 + c0 + r excluded)
+        uint32_t ex = 0;
+        if constexpr (AM) {
+          const int qs = cur.q0 + c0, m0 = (qs >> 5) - (cur.q0 >> 5);
+          const uint64_t two = (static_cast<uint64_t>(sB[buf][m0 + 1][32 * w + l32]) << 32) | sB[buf][m0][32 * w + l32];
+          ex = static_cast<uint32_t>(two >> (qs & 31));
+        }
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const float li = l4[i >> 2][i & 3], di = d4[i >> 2][i & 3];
-          const int q = cur.q0 + c0 + 8 * (i >> 2) + 4 * g + (i & 3);  // this register's query row
+          const int r = 8 * (i >> 2) + 4 * g + (i & 3);
+          const int q = cur.q0 + c0 + r;  // this register's query row
           const float x = fast_exp2(s[i] * c2 - li);
-          const bool on = kv_ok && q < cur.qend && (!p.win || in_band(p, q, my_kv)) &&
-                          (!p.amask || amask_keeps(p, q, my_kv));
+          const bool on = kv_ok && q < cur.qend && (!p.win || in_band(p, q, my_kv)) && !((ex >> r) & 1u);
           pv[i] = on ? x : 0.f;  // a select: li may be -inf where nothing is left
           dsv[i] = pv[i] * (dpv[i] - di);
         }
@@ -947,7 +1008,9 @@ __device__ __forceinline__ void dkdv_work(const Params& p, int item, unsigned sh
   }
 }
 
-template <class E, int D, int W>
+// AM: built for calls with an attenMask (its bits staged with the Q tiles);
+// the builds without one carry none of that code.
+template <class E, int D, int W, bool AM>
 __global__ __launch_bounds__(256) void dkdv_kernel(Params p) {
   constexpr int H = dkdv_tile_rows<D, W>();
   // Q and dOut tiles (swizzled layout) and their LSE*log2(e) / softmax_grad
@@ -956,11 +1019,12 @@ __global__ __launch_bounds__(256) void dkdv_kernel(Params p) {
   __shared__ __align__(1024) unsigned short sO[2][H * D];  // dOut rows
   __shared__ __align__(16) float sL[2][H];
   __shared__ __align__(16) float sDl[2][H];
+  __shared__ __align__(16) uint32_t sB[2][AM ? dkdv_mask_words<D, W>() : 1][32 * W];  // attenMask bits
   if constexpr (dkdv_passes(D) == 1) {
-    dkdv_work<E, D, W, kDkdvBoth>(p, blockIdx.x, sQ, sO, sL, sDl);
+    dkdv_work<E, D, W, kDkdvBoth, AM>(p, blockIdx.x, sQ, sO, sL, sDl, sB);
   } else {  // workgroups 2i and 2i + 1 run the dV and the dK pass of work item i
-    if (blockIdx.x & 1) dkdv_work<E, D, W, kDkdvOnlyK>(p, blockIdx.x >> 1, sQ, sO, sL, sDl);
-    else dkdv_work<E, D, W, kDkdvOnlyV>(p, blockIdx.x >> 1, sQ, sO, sL, sDl);
+    if (blockIdx.x & 1) dkdv_work<E, D, W, kDkdvOnlyK, AM>(p, blockIdx.x >> 1, sQ, sO, sL, sDl, sB);
+    else dkdv_work<E, D, W, kDkdvOnlyV, AM>(p, blockIdx.x >> 1, sQ, sO, sL, sDl, sB);
   }
 }
 
@@ -1015,7 +1079,7 @@ __device__ void reduce_pieces(const Params& p, int s) {
 // ---------------------------------------------------------------------------
 // One workgroup per (batch, query head, Q block, 128-row part); it walks the
 // slices of the KV blocks its Q block selects, in list (ascending) order.
-template <class E, int D, int W>
+template <class E, int D, int W, bool AM>
 __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(D >= 256 ? 1 : 2))) void dq_kernel(Params p) {
   constexpr int KS = D / 16;
   constexpr int NT = D / 32;
@@ -1025,6 +1089,10 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(D >= 256
   __shared__ int sN[NB];  // valid rows of the slice in each buffer (0 = past the end)
   __shared__ int sR[NB];  // its first key row (sequence-local)
   __shared__ int sList[kListChunk];
+  // per buffer and wave: attenMask words of the slice's keys for the wave's 32
+  // queries ([0, 32): word row0 / 32, [32, 64): the next word; zeros without a mask)
+  __shared__ __align__(16) uint32_t sAB[NB][AM ? W : 1][64];
+  constexpr int kWait = Ring::WAIT + (AM ? NB - 2 : 0);  // the ring's copies (+ one mask-word copy per stage)
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6, l32 = lane & 31, g = lane >> 5;
@@ -1095,13 +1163,19 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(D >= 256
     Slice sl;
     if (!walk.next(p, si.len_kv, sl, tid, 64 * W)) sl = Slice{0, 0, 0};
     Ring::issue(sK[slot], sV[slot], sl, kp, vp, p.kv_sr, p.consts, w, lane);
+    if constexpr (AM) {  // one copy per wave and stage, so the waits stay constants
+      const int wi = (sl.row0 >> 5) + g;
+      const bool ok = sl.nrows > 0 && my_q < p.sq_max && wi < p.am_wk;
+      dma4(ok ? static_cast<const void*>(p.am_rows + static_cast<int64_t>(my_q) * p.am_wk + wi) : p.consts,
+           lds_addr(&sAB[slot][w][0]));
+    }
     if (tid == 0) {
       sN[slot] = sl.nrows;
       sR[slot] = sl.row0;
     }
   };
 
-  auto compute = [&](const unsigned short* tk, const unsigned short* tv, int nrows, int row0) {
+  auto compute = [&](const unsigned short* tk, const unsigned short* tv, int nrows, int row0, int slot) {
     f32x16 st = {}, dpt = {};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
@@ -1109,15 +1183,15 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(D >= 256
       dpt = E::mma(frag_along_row<D>(tv, 0, 16 * ks, lane), oreg[ks], dpt); // dP^T[kv][q]
     }
     float dsv[16];
-    if (nrows == 32 && !p.amask && rect_in_band(p, q0 + 32 * w, 32, row0, 32)) {  // uniform: no mask needed
+    if (nrows == 32 && !AM && rect_in_band(p, q0 + 32 * w, 32, row0, 32)) {  // uniform: no mask needed
 #pragma unroll
       for (int i = 0; i < 16; ++i) dsv[i] = fast_exp2(st[i] * c2 - l2) * (dpt[i] - dl);
     } else {
+      const uint32_t ex = AM ? mask_word(sAB[slot][AM ? w : 0], row0, l32) : 0u;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int kv = 8 * (i >> 2) + 4 * g + (i & 3);  // this register's key row in the slice
-        const bool on = kv < nrows && (!p.win || in_band(p, my_q, row0 + kv)) &&
-                        (!p.amask || !q_ok || amask_keeps(p, my_q, row0 + kv));
+        const bool on = kv < nrows && (!p.win || in_band(p, my_q, row0 + kv)) && !((ex >> kv) & 1u);
         const float x = on ? fast_exp2(st[i] * c2 - l2) : 0.f;  // a select: l2 may be -inf off the window
         dsv[i] = x * (dpt[i] - dl);
       }
@@ -1136,15 +1210,15 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(D >= 256
   // refill the freed buffer with slice t + NB - 1, compute slice t
 #pragma unroll
   for (int t = 0; t < NB - 1; ++t) issue(t);
-  wait_vmcnt<Ring::WAIT>();
+  wait_vmcnt<kWait>();
   __syncthreads();
   int nrows = sN[0];
   for (int t = 0; nrows > 0;) {  // nrows is uniform; 0 once the walk is over
     const int cur = t % NB;
     issue((t + NB - 1) % NB);
-    compute(sK[cur], sV[cur], nrows, sR[cur]);
+    compute(sK[cur], sV[cur], nrows, sR[cur], cur);
     ++t;
-    wait_vmcnt<Ring::WAIT>();
+    wait_vmcnt<kWait>();
     __syncthreads();
     nrows = sN[t % NB];
   }
@@ -1184,7 +1258,7 @@ __device__ __forceinline__ u16x4 pack4(const float* x) {
   return r;
 }
 
-template <class E, int D, int W>
+template <class E, int D, int W, bool AM>
 __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(D >= 256 ? 1 : 2))) void fwd_kernel(Params p) {
   constexpr int KS = D / 16;
   constexpr int NT = D / 32;
@@ -1194,6 +1268,10 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(D >= 256
   __shared__ int sN[NB];  // valid rows of the slice in each buffer (0 = past the end)
   __shared__ int sR[NB];  // its first key row (sequence-local)
   __shared__ int sList[kListChunk];
+  // per buffer and wave: attenMask words of the slice's keys for the wave's 32
+  // queries ([0, 32): word row0 / 32, [32, 64): the next word; zeros without a mask)
+  __shared__ __align__(16) uint32_t sAB[NB][AM ? W : 1][64];
+  constexpr int kWait = Ring::WAIT + (AM ? NB - 2 : 0);  // the ring's copies (+ one mask-word copy per stage)
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6, l32 = lane & 31, g = lane >> 5;
@@ -1244,31 +1322,37 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(D >= 256
     Slice sl;
     if (!walk.next(p, si.len_kv, sl, tid, 64 * W)) sl = Slice{0, 0, 0};
     Ring::issue(sK[slot], sV[slot], sl, kp, vp, p.kv_sr, p.consts, w, lane);
+    if constexpr (AM) {  // one copy per wave and stage, so the waits stay constants
+      const int wi = (sl.row0 >> 5) + g;
+      const bool ok = sl.nrows > 0 && my_q < p.sq_max && wi < p.am_wk;
+      dma4(ok ? static_cast<const void*>(p.am_rows + static_cast<int64_t>(my_q) * p.am_wk + wi) : p.consts,
+           lds_addr(&sAB[slot][w][0]));
+    }
     if (tid == 0) {
       sN[slot] = sl.nrows;
       sR[slot] = sl.row0;
     }
   };
 
-  auto compute = [&](const unsigned short* tk, const unsigned short* tv, int nrows, int row0) {
+  auto compute = [&](const unsigned short* tk, const unsigned short* tv, int nrows, int row0, int slot) {
     f32x16 st = {};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
       st = E::mma(frag_along_row<D>(tk, 0, 16 * ks, lane), qreg[ks], st);  // S^T[kv][q]
     float x[16];
     float mx = -__builtin_inff();
-    if (nrows == 32 && !p.amask && rect_in_band(p, q0 + 32 * w, 32, row0, 32)) {  // uniform: no mask needed
+    if (nrows == 32 && !AM && rect_in_band(p, q0 + 32 * w, 32, row0, 32)) {  // uniform: no mask needed
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         x[i] = st[i] * c2;  // scaled score in log2 units
         mx = fmaxf(mx, x[i]);
       }
     } else {
+      const uint32_t ex = AM ? mask_word(sAB[slot][AM ? w : 0], row0, l32) : 0u;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int kv = 8 * (i >> 2) + 4 * g + (i & 3);  // this register's key row in the slice
-        const bool on = kv < nrows && (!p.win || in_band(p, my_q, row0 + kv)) &&
-                        (!p.amask || !q_ok || amask_keeps(p, my_q, row0 + kv));
+        const bool on = kv < nrows && (!p.win || in_band(p, my_q, row0 + kv)) && !((ex >> kv) & 1u);
         x[i] = on ? st[i] * c2 : -__builtin_inff();
         mx = fmaxf(mx, x[i]);
       }
@@ -1303,15 +1387,15 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(D >= 256
   // the dQ kernel's stage loop: NB - 1 slices in flight ahead of the compute
 #pragma unroll
   for (int t = 0; t < NB - 1; ++t) issue(t);
-  wait_vmcnt<Ring::WAIT>();
+  wait_vmcnt<kWait>();
   __syncthreads();
   int nrows = sN[0];
   for (int t = 0; nrows > 0;) {
     const int cur = t % NB;
     issue((t + NB - 1) % NB);
-    compute(sK[cur], sV[cur], nrows, sR[cur]);
+    compute(sK[cur], sV[cur], nrows, sR[cur], cur);
     ++t;
-    wait_vmcnt<Ring::WAIT>();
+    wait_vmcnt<kWait>();
     __syncthreads();
     nrows = sN[t % NB];
   }
@@ -1359,6 +1443,15 @@ int launch_stage_fp8(const Fp8Stage& st, void* stream) {
   return static_cast<int>(hipGetLastError());
 }
 
+int launch_pack_amask(const Params& p, void* stream) {
+  const int tiles_i = (p.sq_max + 63) / 64;
+  const int tiles_j = static_cast<int>((p.amask_ld + 63) / 64);
+  const int64_t tiles = static_cast<int64_t>(tiles_i) * tiles_j;
+  hipLaunchKernelGGL(pack_amask_kernel, dim3(static_cast<unsigned>((tiles + 3) / 4)), dim3(256), 0,
+                     static_cast<hipStream_t>(stream), p, tiles_i, tiles_j);
+  return static_cast<int>(hipGetLastError());
+}
+
 int launch_stage_seq(const SeqChunk& chunk, SeqInfo* dst, float* consts, void* stream) {
   hipLaunchKernelGGL(stage_seq_kernel, dim3(1), dim3(kMaxInlineSeq), 0,
                      static_cast<hipStream_t>(stream), chunk, dst, consts);
@@ -1388,11 +1481,16 @@ int launch_prologue(const Params& p, void* stream) {
   return static_cast<int>(hipGetLastError());
 }
 
-#define BSA_DISPATCH_W(KERNEL, E, D, W, GRID, S, P)                                    \
-  do {                                                                                  \
-    if ((W) == 4) hipLaunchKernelGGL((KERNEL<E, D, 4>), GRID, dim3(256), 0, S, P);      \
-    else if ((W) == 2) hipLaunchKernelGGL((KERNEL<E, D, 2>), GRID, dim3(128), 0, S, P); \
-    else hipLaunchKernelGGL((KERNEL<E, D, 1>), GRID, dim3(64), 0, S, P);                \
+#define BSA_DISPATCH_AM(KERNEL, E, D, W, AM, GRID, S, P)                                    \
+  do {                                                                                       \
+    if ((W) == 4) hipLaunchKernelGGL((KERNEL<E, D, 4, AM>), GRID, dim3(256), 0, S, P);       \
+    else if ((W) == 2) hipLaunchKernelGGL((KERNEL<E, D, 2, AM>), GRID, dim3(128), 0, S, P);  \
+    else hipLaunchKernelGGL((KERNEL<E, D, 1, AM>), GRID, dim3(64), 0, S, P);                 \
+  } while (0)
+#define BSA_DISPATCH_W(KERNEL, E, D, W, GRID, S, P)                 \
+  do {                                                             \
+    if ((P).amask) BSA_DISPATCH_AM(KERNEL, E, D, W, true, GRID, S, P); \
+    else BSA_DISPATCH_AM(KERNEL, E, D, W, false, GRID, S, P);          \
   } while (0)
 
 #define BSA_DISPATCH(KERNEL, W, GRID, S, P)                                     \

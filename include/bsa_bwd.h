@@ -276,9 +276,11 @@ enum bsa_ws_region {
   BSA_WS_COL_LIST = 6, /* int32 [B, N, nKB, nQB]: ascending Q-block lists, first COL_CNT entries valid */
   BSA_WS_PLAN = 7,     /* int32: dK/dV work split (chunk size, per-unit piece counts and slots, slot table) */
   BSA_WS_PARTIAL = 8,  /* fp32 per-piece dK/dV partial sums of split units, reduced in piece order */
-  BSA_WS_STAGE = 9,    /* fp8 entry points only (else empty): bf16 copies of the fp8 inputs, each 256-byte aligned */
-  BSA_WS_TOTAL = 10,   /* total bytes (== the phase-1 size) */
-  BSA_WS_NUM = 11
+  BSA_WS_AMASK = 9,    /* with an attenMask (else empty): uint32 [maxSq][ceil(maxSkv/32)] bits by query row,
+                          then (backward) uint32 [maxSkv][ceil(maxSq/32)] bits by key; 1 = excluded */
+  BSA_WS_STAGE = 10,   /* fp8 entry points only (else empty): bf16 copies of the fp8 inputs, each 256-byte aligned */
+  BSA_WS_TOTAL = 11,   /* total bytes (== the phase-1 size) */
+  BSA_WS_NUM = 12
 };
 
 /*
@@ -309,7 +311,8 @@ const char* bsa_last_error(void);
  * between their kernel stages (on the call's stream).  bsa_profile_stop waits
  * for the recorded events, writes the summed milliseconds of each stage into
  * stage_ms[0..n_stages) (stage order: 0 = sequence table + softmax_grad + mask
- * compaction + work plan (+ the fp8 decode of the fp8 entry points),
+ * compaction + work plan (+ the attenMask packing, + the fp8 decode of the
+ * fp8 entry points),
  * 1 = dK/dV, 2 = dQ + the sum of split dK/dV units,
  * 3 = forward; a stage a call does not run adds 0), writes the number of
  * profiled calls to *n_calls, frees the events and turns recording off.
