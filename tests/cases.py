@@ -93,6 +93,14 @@ def case(name):
         "bnsd_bf16_d256_window_attenmask": lambda: mk(layout="BNSD", dtype="bf16", B=1, N=2, Nkv=1, D=256,
                                                       Sq=200, Skv=260, bx=32, by=128, p=0.7,
                                                       window=(90, 30), seed=133),
+        # 128-row KV blocks at head dim 128 (the 16-rows-per-wave dK/dV kernel) with an attenMask and a window
+        "bnsd_fp16_d128_b64x128_attenmask_window": lambda: mk(layout="BNSD", dtype="fp16", B=2, N=4, Nkv=2,
+                                                              D=128, Sq=300, Skv=270, bx=64, by=128, p=0.7,
+                                                              window=(150, 40), seed=134),
+        # the same kernel on split units (sink columns), ragged
+        "bnsd_bf16_d128_b64x128_sink_split": lambda: mk(layout="BNSD", dtype="bf16", B=1, N=4, Nkv=1, D=128,
+                                                        Sq=2000, Skv=2000, bx=64, by=128,
+                                                        mask_rule="local8_sink2", seed=135),
     }
     c = cases[name]()
     if name in ATTEN:  # an attenMask over [maxSq, maxSkv], drawn after the case
@@ -109,7 +117,7 @@ def case(name):
 
 # fraction of pairs an attenMask removes, for the cases that carry one
 ATTEN = {"bnsd_bf16_d128_attenmask": 0.3, "tnd_fp16_d64_attenmask_window": 0.5,
-         "bnsd_bf16_d256_window_attenmask": 0.2}
+         "bnsd_bf16_d256_window_attenmask": 0.2, "bnsd_fp16_d128_b64x128_attenmask_window": 0.25}
 
 
 SMALL = ["config1", "bnsd_bf16_d128_b128x128_ragged", "bnsd_fp16_d64_b64x128_padded",
@@ -119,5 +127,6 @@ SMALL = ["config1", "bnsd_bf16_d128_b128x128_ragged", "bnsd_fp16_d64_b64x128_pad
          "bnsd_fp16_d64_sink_split_parts", "bnsd_bf16_d128_window", "tnd_fp16_d64_window_ahead",
          "bnsd_fp16_d128_window_zero", "bnsd_bf16_d128_window_sink_split", "bnsd_bf16_d128_attenmask",
          "tnd_fp16_d64_attenmask_window", "bnsd_bf16_d256_b128x128_ragged", "tnd_fp16_d256_b64x64_gqa",
-         "bnsd_fp16_d256_sink_split", "bnsd_bf16_d256_window_attenmask"]
+         "bnsd_fp16_d256_sink_split", "bnsd_bf16_d256_window_attenmask", "bnsd_fp16_d128_b64x128_attenmask_window",
+         "bnsd_bf16_d128_b64x128_sink_split"]
 
