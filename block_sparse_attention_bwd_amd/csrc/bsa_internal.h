@@ -144,8 +144,8 @@ struct SeqChunk {
 };
 
 // fp8 -> bf16 staging: up to five tensors, each `n16` groups of 16 bytes,
-// decoded element by element into bf16 copies (exact: every E4M3FN and E5M2
-// value is a bf16 value).  fmt: 0 = E4M3FN, 1 = E5M2.
+// decoded into bf16 copies (exact: every E4M3FN and E5M2 value is a bf16
+// value).  fmt: 0 = E4M3FN, 1 = E5M2.
 constexpr int kMaxStaged = 5;
 struct Fp8Stage {
   const uint8_t* src[kMaxStaged];

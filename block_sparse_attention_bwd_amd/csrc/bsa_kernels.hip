@@ -121,30 +121,12 @@ __global__ void stage_seq_kernel(SeqChunk c, SeqInfo* dst, float* consts) {
 // ---------------------------------------------------------------------------
 // fp8 inputs: decode to bf16 copies
 // ---------------------------------------------------------------------------
-// OCP 8-bit floats -> bf16 bit patterns, exactly.  E4M3FN: sign, 4 exponent
-// bits (bias 7), 3 mantissa bits, NaN only at exponent 15 / mantissa 7, no
-// infinities; E5M2: sign, 5 exponent bits (bias 15), 2 mantissa bits, IEEE
-// infinities and NaNs.  A normal code keeps its mantissa bits at the top of
-// bf16's 7 and moves its exponent to bias 127; a subnormal one (exponent 0) is
-// m * 2^(1 - bias - man), formed in fp32 (exact) and cut to bf16 (exact: at
-// most 3 significant bits).
-__device__ __forceinline__ unsigned short fp8_to_bf16(unsigned c, bool e5m2) {
-  const unsigned sgn = (c & 0x80u) << 8;
-  const unsigned man_bits = e5m2 ? 2u : 3u;
-  const unsigned e = (c & 0x7fu) >> man_bits;
-  const unsigned m = c & ((1u << man_bits) - 1u);
-  const unsigned emax = e5m2 ? 31u : 15u;
-  const int bias = e5m2 ? 15 : 7;
-  unsigned bits;
-  if (e == 0) {
-    const float v = static_cast<float>(m) * __builtin_ldexpf(1.f, 1 - bias - static_cast<int>(man_bits));
-    bits = __float_as_uint(v) >> 16;
-  } else {
-    bits = ((e + 127u - bias) << 7) | (m << (7u - man_bits));
-  }
-  if (e5m2 && e == emax) bits = m == 0 ? 0x7f80u : 0x7fc0u;  // infinity, NaN
-  if (!e5m2 && e == emax && m == 7u) bits = 0x7fc0u;          // NaN
-  return static_cast<unsigned short>(sgn | bits);
+// OCP 8-bit floats -> bf16, exactly: v_cvt_pk_f32_fp8 / _bf8 decode two
+// E4M3FN / E5M2 codes (gfx950 takes the OCP encodings) to fp32, whose upper
+// 16 bits are the bf16 value (an fp8 value has at most 4 significant bits).
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ unsigned pack_bf16x2(f32x2 v) {
+  return (__float_as_uint(v[0]) >> 16) | (__float_as_uint(v[1]) & 0xffff0000u);
 }
 
 // One thread per 16-byte group: 16 codes in, two 16-byte stores of bf16 out.
@@ -157,15 +139,23 @@ __global__ __launch_bounds__(256) void stage_fp8_kernel(Fp8Stage st) {
   const bool e5 = st.fmt[t] == 1;
   const uint4 in = reinterpret_cast<const uint4*>(st.src[t])[gid];
   const unsigned w[4] = {in.x, in.y, in.z, in.w};
-  u16x8 lo, hi;
+  unsigned o[8];  // bf16 pairs: codes 2k, 2k + 1
+  if (e5) {
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    lo[i] = fp8_to_bf16((w[i >> 2] >> (8 * (i & 3))) & 0xffu, e5);
-    hi[i] = fp8_to_bf16((w[2 + (i >> 2)] >> (8 * (i & 3))) & 0xffu, e5);
+    for (int i = 0; i < 4; ++i) {
+      o[2 * i] = pack_bf16x2(__builtin_amdgcn_cvt_pk_f32_bf8(w[i], false));
+      o[2 * i + 1] = pack_bf16x2(__builtin_amdgcn_cvt_pk_f32_bf8(w[i], true));
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      o[2 * i] = pack_bf16x2(__builtin_amdgcn_cvt_pk_f32_fp8(w[i], false));
+      o[2 * i + 1] = pack_bf16x2(__builtin_amdgcn_cvt_pk_f32_fp8(w[i], true));
+    }
   }
-  u16x8* out = reinterpret_cast<u16x8*>(st.dst[t]) + 2 * gid;
-  out[0] = lo;
-  out[1] = hi;
+  uint4* out = reinterpret_cast<uint4*>(st.dst[t]) + 2 * gid;
+  out[0] = uint4{o[0], o[1], o[2], o[3]};
+  out[1] = uint4{o[4], o[5], o[6], o[7]};
 }
 
 // ---------------------------------------------------------------------------
