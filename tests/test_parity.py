@@ -298,3 +298,63 @@ def test_full_config_sampled_rows(k):
     # properties that hold at any size: finite everywhere; padding/unused rows zero
     for t in (dq, dk, dv):
         assert torch.isfinite(t.float()).all()
+
+
+# The measured variants of the full workloads (head dim 256, a sliding window,
+# an attenMask, fp8 inputs), in the launch configuration the benchmark times,
+# checked on sampled rows like the plain workloads.
+VARIANTS = ["config2_d256", "config3_window1024_0", "config2_attenmask0.1", "config2_fp8"]
+
+
+def _variant(name):
+    import oracle.fp8 as fp8
+    from bench import gpu_forward, to_device, Runner
+    k = int(name[6])
+    c = synth.config(k, head_dim=256 if name.endswith("_d256") else None)
+    if "window" in name:
+        c.window = (1024, 0)
+    if "attenmask" in name:  # drawn as bench.py --atten-mask draws it
+        rng = np.random.default_rng(c.seed + 2)
+        c.atten_mask = (rng.random((c.Sq, c.Skv), dtype=np.float32) < 0.1).astype(np.uint8)
+    dev = to_device(c)
+    o, lse = gpu_forward(c, dev)
+    torch.cuda.synchronize()
+    o_h = o.float().cpu().numpy()
+    lse_h = lse.cpu().numpy()
+    vals = dict(q=c.q, k=c.k, v=c.v, do=c.do, o=o_h)
+    if not name.endswith("_fp8"):
+        return c, Runner(c, dev, o, lse), vals, lse_h, c.dtype
+    # fp8: E4M3FN query/key/value/attentionOut, E5M2 dout, per-tensor factors; the oracle
+    # takes the dequantised values of the same codes
+    fmts = dict(q=fp8.E4M3, k=fp8.E4M3, v=fp8.E4M3, o=fp8.E4M3, do=fp8.E5M2)
+    tdt = {fp8.E4M3: torch.float8_e4m3fn, fp8.E5M2: torch.float8_e5m2}
+    dev8, fac = dict(dev), {}
+    for key in ("do", "q", "k", "v", "o"):
+        codes, fac[key] = synth.quantize_fp8(vals[key], fmts[key])
+        dev8[key] = torch.from_numpy(codes).cuda().view(tdt[fmts[key]])
+        vals[key] = fp8.dequantize(codes, fmts[key], fac[key])
+    r = Runner(c, dev8, dev8["o"], lse, descale=[fac[key] for key in ("do", "q", "k", "v", "o")])
+    return c, r, vals, lse_h, "bf16"
+
+
+@pytest.mark.parametrize("name", VARIANTS)
+def test_full_variant_sampled_rows(name):
+    print(f"[full variant] {name}", flush=True)
+    c, r, vals, lse_h, tol_dtype = _variant(name)
+    dq, dk, dv = r()
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(5100 + VARIANTS.index(name))
+    qrows, krows = _sample_rows(c, rng, nq=32, nk=32)
+    kw = oracle_kw(c)
+    args = (vals["q"], vals["k"], vals["v"], vals["o"], vals["do"], lse_h, c.mask)
+    ref_q = oracle.backward_dq_rows(*args, rows=qrows, **kw)
+    ref_k, ref_v = oracle.backward_dkdv_rows(*args, rows=krows, **kw)
+    offq, offk = oracle.sequence_offsets(c.len_q), oracle.sequence_offsets(c.len_kv)
+    dq_h, dk_h, dv_h = to_np(dq), to_np(dk), to_np(dv)
+    for nm, got_t, ref, rows, off in (("dq", dq_h, ref_q, qrows, offq), ("dk", dk_h, ref_k, krows, offk),
+                                      ("dv", dv_h, ref_v, krows, offk)):
+        got = np.stack([_row(got_t, c.layout, *key, off) for key in rows])
+        want = np.stack([ref[key] for key in rows])
+        assert_close(f"{name}/{nm}", got, want, tol_dtype)
+    for t in (dq, dk, dv):
+        assert torch.isfinite(t.float()).all()
