@@ -101,6 +101,10 @@ def case(name):
         "bnsd_bf16_d128_b64x128_sink_split": lambda: mk(layout="BNSD", dtype="bf16", B=1, N=4, Nkv=1, D=128,
                                                         Sq=2000, Skv=2000, bx=64, by=128,
                                                         mask_rule="local8_sink2", seed=135),
+        # more sequences than one copy launch of the sequence table takes (two launches)
+        "tnd_bf16_d64_70_seqs": lambda: mk(layout="TND", dtype="bf16", B=70, N=2, Nkv=1, D=64, bx=16, by=16,
+                                           p=0.6, lengths_q=[(7 * b) % 41 for b in range(70)],
+                                           lengths_kv=[(11 * b + 3) % 37 for b in range(70)], seed=136),
     }
     c = cases[name]()
     if name in ATTEN:  # an attenMask over [maxSq, maxSkv], drawn after the case
@@ -128,5 +132,5 @@ SMALL = ["config1", "bnsd_bf16_d128_b128x128_ragged", "bnsd_fp16_d64_b64x128_pad
          "bnsd_fp16_d128_window_zero", "bnsd_bf16_d128_window_sink_split", "bnsd_bf16_d128_attenmask",
          "tnd_fp16_d64_attenmask_window", "bnsd_bf16_d256_b128x128_ragged", "tnd_fp16_d256_b64x64_gqa",
          "bnsd_fp16_d256_sink_split", "bnsd_bf16_d256_window_attenmask", "bnsd_fp16_d128_b64x128_attenmask_window",
-         "bnsd_bf16_d128_b64x128_sink_split"]
+         "bnsd_bf16_d128_b64x128_sink_split", "tnd_bf16_d64_70_seqs"]
 
