@@ -111,8 +111,8 @@ constexpr int kMaxSlots = 2 * kBalanceGroups;
 // 256-thread workgroups holds at most kMaxGridGroups of them.
 constexpr int64_t kMaxGridGroups = ((int64_t(1) << 32) - 1) / 256;
 
-// Workgroups of the prologue launch: softmax_grad (kDeltaRowsPerBlock rows
-// each, runs of one (b, n) for BNSD or of one sequence for TND), row lists
+// Workgroups of the prologue launch: softmax_grad (kDeltaRowsPerBlock
+// consecutive positions of one (b, n) each), row lists
 // (4 Q-block rows each), column lists (64 KV blocks each).
 constexpr int kDeltaRowsPerBlock = 64;
 struct PrologueGrid {
@@ -121,8 +121,8 @@ struct PrologueGrid {
 };
 inline PrologueGrid prologue_grid(int64_t B, int64_t N, int64_t sq_max, int64_t nqb, int64_t nkb, bool tnd) {
   PrologueGrid g;
-  g.delta = tnd ? B * ((sq_max * N + kDeltaRowsPerBlock - 1) / kDeltaRowsPerBlock)
-                : B * N * ((sq_max + kDeltaRowsPerBlock - 1) / kDeltaRowsPerBlock);
+  (void)tnd;  // the same 64-position runs of one (b, n) for both layouts
+  g.delta = B * N * ((sq_max + kDeltaRowsPerBlock - 1) / kDeltaRowsPerBlock);
   g.rows = (B * N * nqb + 3) / 4;
   g.cols = B * N * ((nkb + 63) / 64);
   return g;

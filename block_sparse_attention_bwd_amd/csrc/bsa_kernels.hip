@@ -197,10 +197,10 @@ __global__ __launch_bounds__(256) void pack_amask_kernel(Params p, int tiles_i, 
 // ---------------------------------------------------------------------------
 // softmax_grad = row sums of dOut o Out, and lse2 = LSE * log2(e), for every
 // row of the [B, N, maxSq] grid (0 past a sequence's length).  A workgroup
-// takes 64 rows adjacent in memory: BNSD, 64 consecutive positions of one
-// (b, n); TND, 64 consecutive (position, head) rows of one sequence, whose
-// heads are adjacent.  LPR lanes read a row's D elements 16 bytes each, and
-// every pass's loads are issued together.
+// takes 64 consecutive positions of one (b, n), for either layout: its loads
+// are whole rows (D contiguous elements each) and its stores one contiguous
+// run of the [B, N, maxSq] arrays.  LPR lanes read a row's D elements 16
+// bytes each, and every pass's loads are issued together.
 template <class E, int D>
 __device__ void delta_part(const Params& p, int blk) {
   constexpr int LPR = D / 8;        // lanes per row, 8 elements (16 bytes) each
@@ -210,26 +210,17 @@ __device__ void delta_part(const Params& p, int blk) {
   const int sub = tid % LPR, rloc = tid / LPR;
   const unsigned short* op = static_cast<const unsigned short*>(p.o);
   const unsigned short* dp = static_cast<const unsigned short*>(p.dout);
-  const int per_seq = p.tnd ? (p.sq_max * p.N + kDeltaRowsPerBlock - 1) / kDeltaRowsPerBlock
-                            : (p.sq_max + kDeltaRowsPerBlock - 1) / kDeltaRowsPerBlock;
-  const int outer = blk / per_seq;  // TND: sequence b; BNSD: b * N + n
-  const int f0 = (blk % per_seq) * kDeltaRowsPerBlock;
+  const int per_run = (p.sq_max + kDeltaRowsPerBlock - 1) / kDeltaRowsPerBlock;
+  const int outer = blk / per_run;  // b * N + n
+  const int f0 = (blk % per_run) * kDeltaRowsPerBlock;
   float acc[NP], l2[NP];
   int64_t out[NP];
   bool valid[NP];
 #pragma unroll
   for (int k = 0; k < NP; ++k) {
-    const int f = f0 + k * RPP + rloc;  // row within the (sequence | (b, n)) run
-    int b, n, i;
-    if (p.tnd) {
-      b = outer;
-      i = f / p.N;
-      n = f - i * p.N;
-    } else {
-      b = outer / p.N;
-      n = outer - b * p.N;
-      i = f;
-    }
+    const int i = f0 + k * RPP + rloc;  // position within the (b, n) run
+    const int b = outer / p.N;
+    const int n = outer - b * p.N;
     const SeqInfo si = p.seq[b];
     out[k] = i < p.sq_max ? (static_cast<int64_t>(b) * p.N + n) * p.sq_max + i : -1;
     valid[k] = i < si.len_q;
