@@ -94,3 +94,35 @@ def test_random_case_forward(seed):
     fin = np.isfinite(ref_l)
     assert np.array_equal(np.isneginf(got_l), ~fin), f"random{seed}/LSE: -inf pattern differs"
     assert np.all(np.abs(got_l[fin] - ref_l[fin]) <= 1e-3 * np.maximum(1.0, np.abs(ref_l[fin])))
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_random_case_fp8_backward(seed):
+    """The same draws with fp8 inputs (each tensor E4M3FN or E5M2 at random, per-tensor factors)
+    through bsa_bwd_fp8, against the oracle on the dequantised values (the bf16 bar)."""
+    import oracle.fp8 as fp8
+    from bench import Runner, to_device
+    c = draw(seed)
+    rng = np.random.default_rng(9000 + seed)
+    fmts = {n: [fp8.E4M3, fp8.E5M2][int(rng.integers(2))] for n in ("dout", "query", "key", "value", "attention_out")}
+    print("[random fp8 bwd]", _describe(c), fmts, flush=True)
+    qz = {n: synth.quantize_fp8(x, fmts[n]) for n, x in (("query", c.q), ("key", c.k), ("value", c.v),
+                                                        ("dout", c.do))}
+    deq = {n: fp8.dequantize(codes, fmts[n], f) for n, (codes, f) in qz.items()}
+    o, lse = oracle.forward(deq["query"], deq["key"], deq["value"], c.mask, **oracle_kw(c))
+    qz["attention_out"] = synth.quantize_fp8(o, fmts["attention_out"])
+    lse = lse.astype(np.float32)
+    tdt = {fp8.E4M3: torch.float8_e4m3fn, fp8.E5M2: torch.float8_e5m2}
+    dev = to_device(c)
+    for key, n in (("q", "query"), ("k", "key"), ("v", "value"), ("do", "dout")):
+        dev[key] = torch.from_numpy(np.ascontiguousarray(qz[n][0])).cuda().view(tdt[fmts[n]])
+    o_dev = torch.from_numpy(np.ascontiguousarray(qz["attention_out"][0])).cuda().view(tdt[fmts["attention_out"]])
+    order = ("dout", "query", "key", "value", "attention_out")
+    r = Runner(c, dev, o_dev, torch.from_numpy(lse).cuda(), descale=[qz[n][1] for n in order])
+    dq, dk, dv = r()
+    torch.cuda.synchronize()
+    ref = fp8.backward_fp8(*(qz[n][0] for n in ("query", "key", "value", "attention_out", "dout")), lse, c.mask,
+                           formats=fmts, descale=[qz[n][1] for n in order], **oracle_kw(c))
+    floor = float(np.abs(ref[2]).max()) if ref[2].size else 1.0
+    for nm, got, want in zip(("dQ", "dK", "dV"), (dq, dk, dv), ref):
+        assert_close(f"random{seed}/fp8/{nm}", to_np(got), want, "bf16", floor_ref=floor)
