@@ -16,6 +16,10 @@ Parity status of each function (what pins it, in ``tests/test_oracle.py``):
   the GQA / TND / padding identities.
 * ``backward_dq_rows`` / ``backward_dkdv_rows``: equal to the matching rows of
   ``backward``.
+* ``head_probs_and_ds`` (the P and dS the backward contracts, one head): every
+  row of dS sums to zero with the exact forward's O and LSE, and every row of
+  P sums to one within 4 * 2^-24 * max(1, |LSE|) with the LSE rounded to fp32
+  (``tests/test_oracle.py``, with windows and attenMasks).
 * the sliding window (``window=(pre, nxt)``, ``in_window``; in
   ``tests/test_oracle_window.py``): finite differences with windows that do and
   do not contain the diagonal, torch fp64 autograd on a hand-built element mask,

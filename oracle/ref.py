@@ -71,6 +71,7 @@ __all__ = [
     "element_mask",
     "block_lists",
     "softmax_grad",
+    "head_probs_and_ds",
     "forward",
     "backward",
     "forward_dense",
@@ -243,13 +244,11 @@ def _head_forward(q, k, v, bm, bx, by, scale, window=None, atten_mask=None):
     return o, lse
 
 
-def _head_backward(q, k, v, o, do, lse, bm, bx, by, scale, window=None, atten_mask=None):
-    """Backward of one (batch, query head): dQ, and this head's dK, dV terms."""
+def _head_slabs(q, k, v, o, do, lse, bm, bx, by, scale, window=None, atten_mask=None):
+    """P and dS of one (batch, query head), one Q-block slab at a time:
+    yields (rows, cols, P, dS) over the slab's rows and its selected columns."""
     lq, lkv = q.shape[0], k.shape[0]
     delta = softmax_grad(do, o)
-    dq = np.zeros_like(q)
-    dk = np.zeros_like(k)
-    dv = np.zeros_like(v)
     for ib in range(-(-lq // bx)):
         rows = slice(ib * bx, min(ib * bx + bx, lq))
         cols = _slab_columns(bm, ib, by, lkv)
@@ -261,10 +260,34 @@ def _head_backward(q, k, v, o, do, lse, bm, bx, by, scale, window=None, atten_ma
             p = np.where(allowed, np.exp(np.where(allowed, s - lse[rows, None], 0.0)), 0.0)
         dp = do[rows] @ v[cols].T                  # dP = dOut * V^T
         ds = p * (dp - delta[rows, None])          # dS = P o (dP - softmax_grad)
+        yield rows, cols, p, ds
+
+
+def _head_backward(q, k, v, o, do, lse, bm, bx, by, scale, window=None, atten_mask=None):
+    """Backward of one (batch, query head): dQ, and this head's dK, dV terms."""
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    for rows, cols, p, ds in _head_slabs(q, k, v, o, do, lse, bm, bx, by, scale, window, atten_mask):
         dv[cols] += p.T @ do[rows]                 # dV = P^T * dOut
         dq[rows] = scale * (ds @ k[cols])          # dQ = (dS * K) * scale
         dk[cols] += scale * (ds.T @ q[rows])       # dK = (dS^T * Q) * scale
     return dq, dk, dv
+
+
+def head_probs_and_ds(q, k, v, o, do, lse, block_mask_bn, *, bx, by, scale, window=None, atten_mask=None):
+    """P and dS of one (batch, query head) as dense [lq, lkv] fp64 arrays, 0
+    outside the selected pairs (the values the backward contracts; for the
+    pins that every row of P sums to one and every row of dS to zero).
+    q, o, do: [lq, D] of the head; k, v: [lkv, D] of its KV head; lse [lq]."""
+    q, k, v, o, do = (np.asarray(x, np.float64) for x in (q, k, v, o, do))
+    lse = np.asarray(lse, np.float64)
+    P = np.zeros((q.shape[0], k.shape[0]))
+    dS = np.zeros_like(P)
+    for rows, cols, p, ds in _head_slabs(q, k, v, o, do, lse, block_mask_bn, bx, by, scale, window, atten_mask):
+        P[rows, cols] = p
+        dS[rows, cols] = ds
+    return P, dS
 
 
 def _check_heads(N, Nkv):

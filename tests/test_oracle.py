@@ -427,3 +427,78 @@ def test_null_mask_is_dense():
     g2 = oracle.backward(c.q, c.k, c.v, o, c.do, lse, ones, **_kw(c))
     for a, b in zip(g1, g2):
         np.testing.assert_array_equal(a, b)
+
+
+# ---------------------------------------------------------------------------
+# rows of P sum to one and rows of dS to zero (the P and dS the backward contracts)
+# ---------------------------------------------------------------------------
+ROW_CASES = [
+    dict(layout="BNSD", dtype="bf16", B=2, N=4, Nkv=2, D=16, Sq=70, Skv=90, bx=16, by=32, p=0.5, seed=21),
+    dict(layout="TND", dtype="fp16", B=2, N=2, Nkv=1, D=8, bx=8, by=16, p=0.6, lengths_q=[40, 23],
+         lengths_kv=[50, 31], seed=22),
+    dict(layout="BNSD", dtype="bf16", B=1, N=2, Nkv=1, D=8, Sq=60, Skv=60, bx=16, by=16, p=0.8,
+         window=(10, 3), seed=23),
+]
+
+
+def _heads(c, o, lse):
+    """Per (b, n): the head's q, o, do, lse rows and its KV head's k, v (sequence-local)."""
+    offq, offk = oracle.sequence_offsets(c.len_q), oracle.sequence_offsets(c.len_kv)
+    G = c.N // c.Nkv
+    for b in range(c.B):
+        lq, lk = int(c.len_q[b]), int(c.len_kv[b])
+        for n in range(c.N):
+            h = n // G
+            if c.layout == "BNSD":
+                qs, os_, dos, ls = c.q[b, n, :lq], o[b, n, :lq], c.do[b, n, :lq], lse[b, n, :lq]
+                ks, vs = c.k[b, h, :lk], c.v[b, h, :lk]
+            else:
+                sl = slice(offq[b], offq[b] + lq)
+                qs, os_, dos, ls = c.q[sl, n], o[sl, n], c.do[sl, n], lse[sl, n]
+                ks, vs = c.k[offk[b]:offk[b] + lk, h], c.v[offk[b]:offk[b] + lk, h]
+            yield b, n, qs, ks, vs, os_, dos, ls
+
+
+@pytest.mark.parametrize("spec", ROW_CASES, ids=["bnsd_gqa", "tnd", "window"])
+@pytest.mark.parametrize("with_amask", [False, True])
+def test_ds_rows_sum_to_zero(spec, with_amask):
+    """sum_j dS_ij = delta_i - delta_i * sum_j P_ij = 0 when O and LSE are the exact forward
+    (sum_j P_ij dP_ij = dO_i . O_i = delta_i): a wrong delta, P or dS fails it."""
+    c = synth.make_case(**spec)
+    amask = None
+    if with_amask:
+        rng = np.random.default_rng(spec["seed"])
+        sq, sk = int(c.len_q.max()), int(c.len_kv.max())
+        amask = (rng.random((sq, sk)) < 0.3).astype(np.uint8)
+    kw = dict(_kw(c), window=c.window, atten_mask=amask)
+    if c.layout == "TND":
+        kw.update(len_q=c.len_q, len_kv=c.len_kv)
+    o, lse = oracle.forward(c.q, c.k, c.v, c.mask, **kw)
+    n_rows = 0
+    for b, n, qs, ks, vs, os_, dos, ls in _heads(c, o, lse):
+        P, dS = oracle.head_probs_and_ds(qs, ks, vs, os_, dos, ls, c.mask[b, n], bx=c.bx, by=c.by, scale=c.scale,
+                                         window=c.window, atten_mask=amask)
+        mag = np.abs(dS).sum(axis=1)
+        assert np.all(np.abs(dS.sum(axis=1)) <= 1e-12 * mag + 1e-300), (b, n)
+        n_rows += int((mag > 0).sum())
+    assert n_rows > 0
+
+
+@pytest.mark.parametrize("spec", ROW_CASES, ids=["bnsd_gqa", "tnd", "window"])
+def test_p_rows_sum_to_one_with_fp32_lse(spec):
+    """With the LSE of the oracle forward rounded to fp32 (as the kernels receive it),
+    every row that selects a key has sum_j P_ij = exp(LSE_exact - LSE_fp32) = 1 within
+    4 * 2^-24 * max(1, |LSE_i|); rows that select none (LSE = -inf) have P = 0."""
+    c = synth.make_case(**spec)
+    kw = dict(_kw(c), window=c.window)
+    if c.layout == "TND":
+        kw.update(len_q=c.len_q, len_kv=c.len_kv)
+    o, lse = oracle.forward(c.q, c.k, c.v, c.mask, **kw)
+    lse32 = lse.astype(np.float32).astype(np.float64)
+    for b, n, qs, ks, vs, os_, dos, ls in _heads(c, o, lse32):
+        P, _ = oracle.head_probs_and_ds(qs, ks, vs, os_, dos, ls, c.mask[b, n], bx=c.bx, by=c.by, scale=c.scale,
+                                        window=c.window)
+        fin = np.isfinite(ls)
+        rs = P.sum(axis=1)
+        assert np.all(np.abs(rs[fin] - 1.0) <= 4 * 2.0 ** -24 * np.maximum(1.0, np.abs(ls[fin]))), (b, n)
+        assert np.all(rs[~fin] == 0.0)
