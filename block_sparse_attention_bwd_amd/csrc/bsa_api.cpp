@@ -508,6 +508,8 @@ int make_plan(const Args& a, Plan* plan) {
   const bool am = a.atten_mask != nullptr;
   const uint64_t wk = static_cast<uint64_t>(ceil_div(Skv, 32)), wq = static_cast<uint64_t>(ceil_div(Sq, 32));
   take(BSA_WS_AMASK, am ? 4 * (static_cast<uint64_t>(Sq) * wk + bwd * static_cast<uint64_t>(Skv) * wq) : 0);
+  if (am && (ceil_div(Sq, 64) * ceil_div(Skv, 64) + 3) / 4 > bsa::kMaxGridGroups)  // pack_amask: a 64 x 64 tile per wave
+    return fail(BSA_ERR_PARAM_INVALID, "attenMask too large for one packing launch");
   p.am_wk = static_cast<int32_t>(wk);
   p.am_wq = static_cast<int32_t>(wq);
   // fp8: bf16 copies of the data inputs, each 256-byte aligned

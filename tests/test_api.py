@@ -300,6 +300,19 @@ def test_launch_grid_limit(what, shape):
     assert "launch grid too large" in bsa.bsa_last_error()
 
 
+def test_attenmask_packing_launch_limit():
+    """The attenMask is packed by one wave per 64 x 64 tile, 4 per workgroup: with
+    Sq = Skv = 2^19 that is 2^26 / 4 = 2^24 workgroups, above (2^32 - 1) / 256."""
+    S = 1 << 19
+    args = _huge(1, 1, S, S, S, S)  # one block: the lists stay tiny
+    args["atten_mask"] = _fake(torch.empty(S, S, dtype=torch.bool, device="meta"))
+    assert _code(args) == INVALID
+    assert "attenMask too large" in bsa.bsa_last_error()
+    args = _huge(1, 1, 1 << 16, 1 << 16, 1 << 16, 1 << 16)
+    args["atten_mask"] = _fake(torch.empty(1 << 16, 1 << 16, dtype=torch.bool, device="meta"))
+    assert _code(args) == bsa.BSA_OK
+
+
 def test_launch_grid_just_below_limit():
     args = _huge(1, 65217, 1, 16384, 1, 1)
     assert _code(args) == bsa.BSA_OK, bsa.bsa_last_error()
