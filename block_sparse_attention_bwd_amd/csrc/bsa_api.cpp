@@ -433,6 +433,11 @@ int make_plan(const Args& a, Plan* plan) {
     p.lse_sb = N * Sq, p.lse_sh = Sq, p.lse_sr = 1;
   }
   p.o_sb = p.dq_sb, p.o_sh = p.dq_sh, p.o_sr = p.dq_sr;
+  // the MFMA kernels address the rows of a tile (at most 128) from its first
+  // row by 32-bit byte offsets
+  if (2 * (128 * std::max(p.q_sr, p.kv_sr) + D) > 0xffffffffLL)
+    return fail(BSA_ERR_PARAM_INVALID, "row stride of %lld elements too large for 32-bit tile offsets",
+                static_cast<long long>(std::max(p.q_sr, p.kv_sr)));
   p.B = static_cast<int32_t>(B);
   p.N = static_cast<int32_t>(N);
   p.Nkv = static_cast<int32_t>(Nkv);

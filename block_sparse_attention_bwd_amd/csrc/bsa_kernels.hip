@@ -600,19 +600,21 @@ struct Slice {
   int nrows;  // valid rows, 0..32
 };
 
-// Direct global -> LDS copy (global_load_lds_dwordx4): lane L's 16 bytes land
-// at LDS byte address m0 + 16 L, with no register staging.  Issued from inline
-// assembly so that the compiler adds no waits of its own around it: the
-// caller waits on vmcnt for its own copies, then a barrier publishes the
-// buffer to the workgroup.  (Compiler-issued vector loads are counted by the
-// same vmcnt; loads complete in issue order, so either side's waits may only
-// wait longer than needed, never shorter.)
+// Direct global -> LDS copy (global_load_lds_dwordx4): lane L's 16 bytes,
+// read from a wave-uniform base (held in an SGPR pair) plus a per-lane 32-bit
+// byte offset, land at LDS byte address m0 + 16 L, with no register staging
+// and no per-lane 64-bit address arithmetic.  Issued from inline assembly so
+// that the compiler adds no waits of its own around it: the caller waits on
+// vmcnt for its own copies, then a barrier publishes the buffer to the
+// workgroup.  (Compiler-issued vector loads are counted by the same vmcnt;
+// loads complete in issue order, so either side's waits may only wait longer
+// than needed, never shorter.)
 __device__ __forceinline__ unsigned lds_addr(const void* p) {
   return static_cast<unsigned>(reinterpret_cast<uintptr_t>((lds_void*)(p)));
 }
-__device__ __forceinline__ void dma16(const void* src, unsigned lds) {
+__device__ __forceinline__ void dma16s(const void* base, unsigned voff, unsigned lds) {
   const unsigned m = __builtin_amdgcn_readfirstlane(lds);  // wave-uniform by construction
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "s"(m) : "memory", "m0");
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(voff), "s"(base), "s"(m) : "memory", "m0");
 }
 __device__ __forceinline__ void dma4(const void* src, unsigned lds) {  // lane L's 4 bytes -> m0 + 4 L
   const unsigned m = __builtin_amdgcn_readfirstlane(lds);
@@ -630,9 +632,11 @@ __device__ __forceinline__ void wait_vmcnt() {
 // swizzled tile layout, filled by DMA NB - 1 slices ahead of the compute.  One
 // wave instruction fills 1 KB (512 / D rows): lane L writes physical chunk
 // L % (D/8) of row L / (D/8) and so fetches the logical chunk that the swizzle
-// puts there.  Rows past a slice's end (and every row of an empty slice) are
-// fetched from a zero block, so every stage issues the same number of copies
-// and the wait before a stage is a constant.
+// puts there, at a per-lane byte offset from the slice's first row that is the
+// same for every slice (computed once).  Lanes of rows past a slice's end read
+// a chunk of its first row instead (finite data that the kernels mask to a
+// zero weight); an empty slice reads a zero block.  Every stage issues the
+// same number of copies, so the wait before a stage is a constant.
 template <int D, int W, int NB>
 struct KVRing {
   static constexpr int RPI = 512 / D;       // rows per wave instruction
@@ -642,19 +646,35 @@ struct KVRing {
   static constexpr int WAIT = (NB - 2) * NI;  // copies of the two later stages still in flight
   static_assert(IPW >= 1 && IPW * W == IPT, "slice must split evenly over the waves");
 
-  __device__ __forceinline__ static void issue(unsigned short* tk, unsigned short* tv, const Slice& s,
-                                               const unsigned short* kp, const unsigned short* vp,
-                                               int64_t sr, const void* zeros, int w, int lane) {
+  unsigned voff[IPW];  // byte offset of this lane's chunk from the slice's first row
+  unsigned vz;         // a chunk of the first row (rows past the end)
+  int lrow;            // this lane's row within an instruction's RPI rows
+  int w;
+
+  __device__ __forceinline__ KVRing(int64_t sr, int w_, int lane) : w(w_) {
+    lrow = lane / (D / 8);
+    vz = 16u * static_cast<unsigned>(lane % (D / 8 < 16 ? D / 8 : 16));  // inside the zero block too
+#pragma unroll
+    for (int i = 0; i < IPW; ++i) {
+      const int r = (w * IPW + i) * RPI + lrow;
+      const int c = (lane % (D / 8)) ^ swz<D>(r);
+      voff[i] = static_cast<unsigned>(2 * (r * sr + 8 * c));
+    }
+  }
+
+  __device__ __forceinline__ void issue(unsigned short* tk, unsigned short* tv, const Slice& s,
+                                        const unsigned short* kp, const unsigned short* vp, int64_t sr,
+                                        const void* zeros) const {
     const unsigned kb = lds_addr(tk), vb = lds_addr(tv);
+    const bool any = s.nrows > 0;
+    const void* kbase = any ? static_cast<const void*>(kp + static_cast<int64_t>(s.row0) * sr) : zeros;
+    const void* vbase = any ? static_cast<const void*>(vp + static_cast<int64_t>(s.row0) * sr) : zeros;
 #pragma unroll
     for (int i = 0; i < IPW; ++i) {
       const int ins = w * IPW + i;
-      const int r = ins * RPI + lane / (D / 8);
-      const int c = (lane % (D / 8)) ^ swz<D>(r);
-      const bool ok = r < s.nrows;
-      const int64_t off = static_cast<int64_t>(s.row0 + r) * sr + 8 * c;
-      dma16(ok ? static_cast<const void*>(kp + off) : zeros, kb + 1024u * ins);
-      dma16(ok ? static_cast<const void*>(vp + off) : zeros, vb + 1024u * ins);
+      const unsigned v = ins * RPI + lrow < s.nrows ? voff[i] : vz;
+      dma16s(kbase, v, kb + 1024u * ins);
+      dma16s(vbase, v, vb + 1024u * ins);
     }
   }
 };
@@ -825,24 +845,34 @@ __device__ __forceinline__ void dkdv_work(const Params& p, int item, unsigned sh
 
   // DMA of one tile into buffer `buf`: wave w copies rows RW w .. RW w + RW - 1
   // of Q and dOut (one 1 KB wave instruction per 512 / D rows, lanes fetching
-  // the swizzled chunk they land on) and their LSE / softmax_grad values;
-  // rows past the tile's valid rows read zeros and LSE = +inf, so their P is
-  // exactly 0 with no per-element test.
+  // the swizzled chunk they land on, at a byte offset from the tile's first
+  // row that is the same for every tile) and their LSE / softmax_grad values.
+  // Lanes of rows past the tile's valid rows fetch a chunk of its first row
+  // (finite data) and those rows get LSE = +inf and softmax_grad = 0, so their
+  // P and dS are exactly 0 with no per-element test.
   constexpr int RPI = 512 / D;
+  constexpr int NCP = RW / RPI;  // copies per wave and tensor
+  const int lrow = lane / (D / 8);
+  const unsigned vz = 16u * static_cast<unsigned>(lane % (D / 8));
+  unsigned voff[NCP];
+#pragma unroll
+  for (int i = 0; i < NCP; ++i) {
+    const int r = (w * NCP + i) * RPI + lrow;
+    const int c = (lane % (D / 8)) ^ swz<D>(r);
+    voff[i] = static_cast<unsigned>(2 * (r * p.q_sr + 8 * c));
+  }
   auto issue = [&](const QTile& t, int buf) {
     const int rows = min(H, t.qend - t.q0);
-    const unsigned short* qa = qbase + t.n * p.q_sh;
-    const unsigned short* oa = obase + t.n * p.q_sh;
+    const int64_t first = static_cast<int64_t>(t.q0) * p.q_sr + t.n * p.q_sh;
+    const unsigned short* qa = qbase + first;
+    const unsigned short* oa = obase + first;
     const unsigned qb = lds_addr(sQ[buf]), ob = lds_addr(sO[buf]);
 #pragma unroll
-    for (int i = 0; i < RW / RPI; ++i) {
-      const int ins = w * (RW / RPI) + i;
-      const int r = ins * RPI + lane / (D / 8);
-      const int c = (lane % (D / 8)) ^ swz<D>(r);
-      const bool ok = r < rows;
-      const int64_t off = static_cast<int64_t>(t.q0 + r) * p.q_sr + 8 * c;
-      dma16(ok ? static_cast<const void*>(qa + off) : p.consts, qb + 1024u * ins);
-      dma16(ok ? static_cast<const void*>(oa + off) : p.consts, ob + 1024u * ins);
+    for (int i = 0; i < NCP; ++i) {
+      const int ins = w * NCP + i;
+      const unsigned v = ins * RPI + lrow < rows ? voff[i] : vz;
+      dma16s(qa, v, qb + 1024u * ins);
+      dma16s(oa, v, ob + 1024u * ins);
     }
     if (lane < RW) {
       const int r = RW * w + lane;
@@ -1138,12 +1168,13 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(D >= 256
   const unsigned short* vp = static_cast<const unsigned short*>(p.v) + kv_base;
   const float c2 = p.scale_log2e;
 
+  const Ring ring(p.kv_sr, w, lane);
   LdsListWalk walk{-1, p.row_cnt[bn * p.nqb + ib], 0, 0, 0, p.row_list + (bn * p.nqb + ib) * p.nkb, sList};
   walk.fill(0, tid, 64 * W);
   auto issue = [&](int slot) {
     Slice sl;
     if (!walk.next(p, si.len_kv, sl, tid, 64 * W)) sl = Slice{0, 0, 0};
-    Ring::issue(sK[slot], sV[slot], sl, kp, vp, p.kv_sr, p.consts, w, lane);
+    ring.issue(sK[slot], sV[slot], sl, kp, vp, p.kv_sr, p.consts);
     if constexpr (AM) {  // one copy per wave and stage, so the waits stay constants
       const int wi = (sl.row0 >> 5) + g;
       const bool ok = sl.nrows > 0 && my_q < p.sq_max && wi < p.am_wk;
@@ -1297,12 +1328,13 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(D >= 256
   const unsigned short* vp = static_cast<const unsigned short*>(p.v) + kv_base;
   const float c2 = p.scale_log2e;
 
+  const Ring ring(p.kv_sr, w, lane);
   LdsListWalk walk{-1, p.row_cnt[bn * p.nqb + ib], 0, 0, 0, p.row_list + (bn * p.nqb + ib) * p.nkb, sList};
   walk.fill(0, tid, 64 * W);
   auto issue = [&](int slot) {
     Slice sl;
     if (!walk.next(p, si.len_kv, sl, tid, 64 * W)) sl = Slice{0, 0, 0};
-    Ring::issue(sK[slot], sV[slot], sl, kp, vp, p.kv_sr, p.consts, w, lane);
+    ring.issue(sK[slot], sV[slot], sl, kp, vp, p.kv_sr, p.consts);
     if constexpr (AM) {  // one copy per wave and stage, so the waits stay constants
       const int wi = (sl.row0 >> 5) + g;
       const bool ok = sl.nrows > 0 && my_q < p.sq_max && wi < p.am_wk;
