@@ -111,9 +111,9 @@ constexpr int kMaxSlots = 2 * kBalanceGroups;
 // 256-thread workgroups holds at most kMaxGridGroups of them.
 constexpr int64_t kMaxGridGroups = ((int64_t(1) << 32) - 1) / 256;
 
-// Workgroups of the prologue launch: softmax_grad (kDeltaRowsPerBlock
-// consecutive positions of one (b, n) each), row lists
-// (4 Q-block rows each), column lists (64 KV blocks each).
+// Workgroups of the prologue launch: row lists (4 Q-block rows each), column
+// lists (64 KV blocks each), softmax_grad (kDeltaRowsPerBlock consecutive
+// positions of one (b, n) each).
 constexpr int kDeltaRowsPerBlock = 64;
 struct PrologueGrid {
   int64_t delta, rows, cols;

@@ -261,14 +261,26 @@ __device__ void row_list_part(const Params& p, int blk) {
     int32_t* out = p.row_list + R * p.nkb;
     const uint8_t* mrow = p.mask ? p.mask + R * p.nkb : nullptr;
     const int r0 = ib * p.bx, nr = min(p.bx, si.len_q - r0);
-    for (int j0 = 0; j0 < nk_b; j0 += 64) {
-      const int j = j0 + lane;
-      const bool on = j < nk_b && (mrow == nullptr || mrow[j] != 0) &&
-                      rect_meets_band(p, r0, nr, j * p.by, min(p.by, si.len_kv - j * p.by));
-      const uint64_t bal = __ballot(on);
-      const int pre = __popcll(bal & ((1ull << lane) - 1ull));
-      if (on) out[base + pre] = j;
-      base += __popcll(bal);
+    // the mask bytes of kRowSteps steps of 64 blocks are loaded before any
+    // list entry is stored (the int32 stores could otherwise alias the byte
+    // loads, which would then wait for each other step by step)
+    constexpr int kRowSteps = 8;
+    for (int j00 = 0; j00 < nk_b; j00 += 64 * kRowSteps) {
+      uint8_t sel[kRowSteps];
+#pragma unroll
+      for (int u = 0; u < kRowSteps; ++u) {
+        const int j = j00 + 64 * u + lane;
+        sel[u] = j < nk_b ? (mrow ? mrow[j] : 1) : 0;
+      }
+#pragma unroll
+      for (int u = 0; u < kRowSteps; ++u) {
+        const int j = j00 + 64 * u + lane;
+        const bool on = sel[u] != 0 && rect_meets_band(p, r0, nr, j * p.by, min(p.by, si.len_kv - j * p.by));
+        const uint64_t bal = __ballot(on);
+        const int pre = __popcll(bal & ((1ull << lane) - 1ull));
+        if (on) out[base + pre] = j;
+        base += __popcll(bal);
+      }
     }
   }
   if (lane == 0) p.row_cnt[R] = base;
@@ -327,14 +339,17 @@ __device__ void col_list_part(const Params& p, int blk) {
   }
 }
 
-// softmax_grad workgroups, then row lists, then column lists (the forward
-// launches the row lists only).
+// Row lists, then column lists, then softmax_grad workgroups (the forward
+// launches the row lists only).  The list workgroups are latency-bound (a
+// row-list wave walks its mask row 64 blocks per dependent load); dispatched
+// first, they overlap the bandwidth-bound softmax_grad pass instead of
+// trailing it.
 template <class E, int D>
-__global__ __launch_bounds__(256) void prologue_kernel(Params p, int nb_delta, int nb_rows) {
+__global__ __launch_bounds__(256) void prologue_kernel(Params p, int nb_rows, int nb_cols) {
   const int bid = blockIdx.x;
-  if (bid < nb_delta) delta_part<E, D>(p, bid);
-  else if (bid < nb_delta + nb_rows) row_list_part(p, bid - nb_delta);
-  else col_list_part(p, bid - nb_delta - nb_rows);
+  if (bid < nb_rows) row_list_part(p, bid);
+  else if (bid < nb_rows + nb_cols) col_list_part(p, bid - nb_rows);
+  else delta_part<E, D>(p, bid - nb_rows - nb_cols);
 }
 
 
@@ -1497,7 +1512,7 @@ void launch_prologue_kernel(const Params& p, dim3 grid, hipStream_t s, A... a) {
 int launch_prologue(const Params& p, void* stream) {
   const PrologueGrid pg = prologue_grid(p.B, p.N, p.sq_max, p.nqb, p.nkb, p.tnd != 0);
   launch_prologue_kernel(p, dim3(static_cast<unsigned>(pg.total())), static_cast<hipStream_t>(stream),
-                         static_cast<int>(pg.delta), static_cast<int>(pg.rows));
+                         static_cast<int>(pg.rows), static_cast<int>(pg.cols));
   return static_cast<int>(hipGetLastError());
 }
 
@@ -1530,8 +1545,8 @@ int launch_prologue(const Params& p, void* stream) {
 
 int launch_prologue_rows(const Params& p, void* stream) {
   const PrologueGrid pg = prologue_grid(p.B, p.N, p.sq_max, p.nqb, p.nkb, p.tnd != 0);
-  launch_prologue_kernel(p, dim3(static_cast<unsigned>(pg.rows)), static_cast<hipStream_t>(stream), 0,
-                         static_cast<int>(pg.rows));
+  launch_prologue_kernel(p, dim3(static_cast<unsigned>(pg.rows)), static_cast<hipStream_t>(stream),
+                         static_cast<int>(pg.rows), 0);
   return static_cast<int>(hipGetLastError());
 }
 
