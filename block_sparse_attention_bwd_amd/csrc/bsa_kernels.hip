@@ -4,25 +4,31 @@
 // page, 功能说明 / 计算公式 for the equations):
 //
 //   stage_seq   copy the per-sequence table (offsets, lengths) into the workspace
+//   (pack_amask / stage_fp8: only with an attenMask / fp8 inputs)
 //   prologue    one launch, three block ranges:
-//                 - softmax_grad: delta = rowsum(dOut o Out) in fp32, and
-//                   lse2 = softmaxLse * log2(e), both [B, N, maxSq]
 //                 - per-Q-block lists of selected in-range KV blocks
 //                 - per-KV-block lists of selected in-range Q blocks
-//   dkdv        one workgroup per (batch, KV head, KV block [, 128-row part]);
-//               K/V rows stay in registers; walks the Q blocks that select it
-//               for every query head of its group:  S, P, dV += P^T dO,
-//               dP, dS, dK += dS^T Q  (four MFMA GEMMs per step).  Staged Q/dO
-//               tiles use a padded pitch; the next tile is prefetched into
-//               registers during the current one.
+//                 - softmax_grad: delta = rowsum(dOut o Out) in fp32, and
+//                   lse2 = softmaxLse * log2(e), both [B, N, maxSq]
+//   plan        one workgroup: splits KV blocks that many Q blocks select
+//               into pieces and orders the dK/dV work longest first; picks
+//               the dQ workgroup order
+//   dkdv        one workgroup per work item (batch, KV head, KV block
+//               [, 128-row part] [, piece]); K/V rows stay in registers;
+//               walks the Q blocks that select it for every query head of
+//               its group:  S, P, dV += P^T dO, dP, dS, dK += dS^T Q  (four
+//               MFMA GEMMs per step).  Q/dO tiles (XOR-swizzled) are
+//               double-buffered in LDS, the next one copied in by DMA during
+//               the current one.
 //   dq          one workgroup per (batch, query head, Q block [, part]);
 //               Q/dO rows in registers; streams 32-row slices of its KV blocks
-//               through double-buffered, XOR-swizzled LDS tiles: S, P, dP, dS,
-//               dQ += dS K (three MFMA GEMMs per slice).  No atomics anywhere,
-//               so every output is written exactly once, in a fixed order.
-// Both MFMA kernels number their workgroups so that each XCD gets a
-// contiguous range (the workgroups sharing a head's tiles share one L2).
-//
+//               through a ring of XOR-swizzled LDS buffers filled by DMA:
+//               S, P, dP, dS, dQ += dS K (three MFMA GEMMs per slice).  Extra
+//               workgroups of the same launch sum the pieces of split dK/dV
+//               work items in piece order.  No atomics on outputs anywhere,
+//               so every output is written in a fixed order.
+//   fwd         (the forward entry point) the dq kernel's structure with an
+//               online softmax: O and LSE.
 // MFMA used: v_mfma_f32_32x32x16_{bf16,f16}.  Operand layout (wave64, lane l,
 // g = l / 32):  A[m][k]: lane holds row m = l % 32, k = 8g .. 8g+7;
 // B[k][n]: lane holds column n = l % 32, k = 8g .. 8g+7;  C[m][n] (16 fp32):

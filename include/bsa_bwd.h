@@ -122,7 +122,9 @@ typedef struct bsa_tensor {
  *
  * Head dim D must be 64, 128 or 256 (the tile set built into this library;
  * the pages' own implementation takes 128 only, the FlashAttentionScore page
- * allows up to 512).
+ * allows up to 512).  The kernels address the rows of a tile from its first
+ * row by 32-bit byte offsets: a row stride (D for BNSD, N * D or Nkv * D for
+ * TND) above (2^31 - D) / 128 elements is rejected with 161002.
  */
 int bsa_bwd_workspace_size(const bsa_tensor* dout, const bsa_tensor* query, const bsa_tensor* key,
                            const bsa_tensor* value, const bsa_tensor* attention_out,

@@ -121,6 +121,16 @@ def test_layout_region_sizes():
     assert size["partial"] >= slots * 2 * 128 * D * 4
 
 
+def test_row_stride_beyond_32bit_tile_offsets_is_rejected():
+    """The kernels address a tile's rows (at most 128) from its first row by 32-bit byte
+    offsets, so a TND row of N * D elements may not exceed (2**32 / 2 - D) / 128 elements."""
+    ok = _tnd(lq=(1,), lk=(1,), N=128, Nkv=1, D=128)  # row stride 16384 elements
+    assert bsa.bsa_bwd_workspace_size(**ok) > 0
+    bad = _tnd(lq=(1,), lk=(1,), N=131072, Nkv=1, D=128)  # 16 Mi elements per token row
+    assert _code(bad) == INVALID
+    assert "row stride" in bsa.bsa_last_error()
+
+
 def test_layout_partial_region_scales_with_head_dim():
     """The fp32 partials hold [slots][dK, dV][128 rows][D]: twice as large at D = 256."""
     sizes = {}
