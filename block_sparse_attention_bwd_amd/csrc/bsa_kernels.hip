@@ -1290,6 +1290,8 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(D >= 256
 // output is accumulated transposed, O^T += V^T P^T, so that each lane also
 // holds its own row of O and rescales it in place.  Rows that select nothing
 // (and BNSD padding rows) get O = 0 and LSE = -inf.
+constexpr float kLazyRescale = 8.f;  // forward: how far (log2 units) a row maximum may pass its reference
+
 template <class E>
 __device__ __forceinline__ u16x4 pack4(const float* x) {
   u16x4 r;
@@ -1399,9 +1401,15 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(D >= 256
       }
     }
     mx = fmaxf(mx, __shfl_xor(mx, 32));  // the partner lane holds the row's other 16 keys
-    const float m_new = fmaxf(m_run, mx);
+    // Lazy rescale: the reference maximum m_run moves only once the row's
+    // maximum exceeds it by more than kLazyRescale (log2 units).  P is then
+    // at most 2^kLazyRescale, harmless in the fp32 sums and as a 16-bit MFMA
+    // operand, and O = acc / l and LSE = m_run + log2(l) hold for any
+    // reference, so the result is the same; most slices skip the O rescale.
+    const bool grow = mx > m_run + kLazyRescale;  // always once m_run is -inf and a key is valid
+    const float m_new = grow ? mx : m_run;
     const float m_use = m_new == -__builtin_inff() ? 0.f : m_new;
-    const float alpha = fast_exp2(m_run - m_use);
+    const float alpha = fast_exp2(m_run - m_use);  // exactly 1 where the reference stays
     float pv[16], ls = 0.f;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
@@ -1409,9 +1417,7 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(D >= 256
       ls += pv[i];
     }
     l_run = l_run * alpha + ls;
-    // alpha is exactly 1 where the running maximum did not move; once the
-    // maxima settle most slices skip the rescale (wave-uniform test)
-    if (__any(m_new != m_run)) {
+    if (__any(grow)) {  // wave-uniform test
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) aot[nt] *= alpha;
     }

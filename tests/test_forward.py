@@ -85,6 +85,28 @@ def test_forward_full_config_parity(k):
     _check(f"config{k}", c, o, lse)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+def test_forward_rising_scores_rescale(dtype):
+    """Scores that climb along the keys (head 0: S_ij = q_i . k_j grows by about 6 log2 units
+    per 32-key slice, 50 in all) make each row's maximum pass the kernel's running reference
+    many times in the middle of the walk, so the output is rescaled there; in head 1 the
+    scores fall instead (the maximum is the first key's and never moves).  Random inputs
+    almost never exercise the first path after the first slice."""
+    print(f"[forward] rising scores {dtype}", flush=True)
+    c = synth.make_case(layout="BNSD", dtype=dtype, B=1, N=2, Nkv=1, D=64, Sq=160, Skv=300,
+                        bx=64, by=64, mask_rule="dense", seed=131)
+    rng = np.random.default_rng(131)
+    sign = np.array([1.0, -1.0], np.float32)[None, :, None, None]
+    q = sign * (0.25 + 0.05 * rng.standard_normal(c.q.shape).astype(np.float32))
+    k = np.broadcast_to((np.arange(c.k.shape[2], dtype=np.float32) / 16.0)[None, None, :, None], c.k.shape)
+    c.q = synth.round_to_dtype(np.ascontiguousarray(q, np.float32), dtype)
+    c.k = synth.round_to_dtype(np.ascontiguousarray(k, np.float32), dtype)
+    o, lse = _run_fwd(c)
+    _check(f"rising_{dtype}", c, o, lse)
+    ref_l = oracle.forward(c.q, c.k, c.v, c.mask, **oracle_kw(c))[1]
+    assert ref_l[0, 0].min() > 25.0 and ref_l[0, 1].max() < 10.0  # the two regimes are the intended ones
+
+
 def test_forward_noncontiguous_output():
     c = _case("bnsd_bf16_d128_b128x128_ragged")
     o_ref, l_ref = _run_fwd(c)
