@@ -621,6 +621,11 @@ struct Slice {
   int nrows;  // valid rows, 0..32
 };
 
+// The LDS-DMA loads read m0 for their destination, and an SALU write of m0
+// needs one wait state before such a load reads it (a gfx9 hazard the
+// compiler observes for its own code but cannot see inside inline assembly):
+// hence the s_nop between the two.
+//
 // Direct global -> LDS copy (global_load_lds_dwordx4): lane L's 16 bytes,
 // read from a wave-uniform base (held in an SGPR pair) plus a per-lane 32-bit
 // byte offset, land at LDS byte address m0 + 16 L, with no register staging
@@ -635,11 +640,12 @@ __device__ __forceinline__ unsigned lds_addr(const void* p) {
 }
 __device__ __forceinline__ void dma16s(const void* base, unsigned voff, unsigned lds) {
   const unsigned m = __builtin_amdgcn_readfirstlane(lds);  // wave-uniform by construction
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(voff), "s"(base), "s"(m) : "memory", "m0");
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(voff), "s"(base), "s"(m)
+               : "memory", "m0");
 }
 __device__ __forceinline__ void dma4(const void* src, unsigned lds) {  // lane L's 4 bytes -> m0 + 4 L
   const unsigned m = __builtin_amdgcn_readfirstlane(lds);
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" : : "v"(src), "s"(m) : "memory", "m0");
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" : : "v"(src), "s"(m) : "memory", "m0");
 }
 // s_waitcnt vmcnt(N) with the other counters left alone (gfx9 encoding: vmcnt
 // bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
