@@ -982,15 +982,31 @@ __device__ __forceinline__ void dkdv_work(const Params& p, int item, unsigned sh
           const uint64_t two = (static_cast<uint64_t>(sB[buf][m0 + 1][32 * w + l32]) << 32) | sB[buf][m0][32 * w + l32];
           ex = static_cast<uint32_t>(two >> (qs & 31));
         }
+        if (!p.win) {  // uniform: only the tile's valid rows and the attenMask cut
+          // bit r of keep: slice row r takes part (this lane's key valid, row in
+          // range, not excluded); shifted so that register i tests bit
+          // 8 (i / 4) + i % 4, its row minus 4g
+          const int nv = cur.qend - (cur.q0 + c0);  // >= 1
+          const uint32_t rows_ok = nv >= 32 ? 0xffffffffu : ((1u << nv) - 1u);
+          const uint32_t keep = (kv_ok ? rows_ok & ~ex : 0u) >> (4 * g);
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float li = l4[i >> 2][i & 3], di = d4[i >> 2][i & 3];
-          const int r = 8 * (i >> 2) + 4 * g + (i & 3);
-          const int q = cur.q0 + c0 + r;  // this register's query row
-          const float x = fast_exp2(s[i] * c2 - li);
-          const bool on = kv_ok && q < cur.qend && (!p.win || in_band(p, q, my_kv)) && !((ex >> r) & 1u);
-          pv[i] = on ? x : 0.f;  // a select: li may be -inf where nothing is left
-          dsv[i] = pv[i] * (dpv[i] - di);
+          for (int i = 0; i < 16; ++i) {
+            const float li = l4[i >> 2][i & 3], di = d4[i >> 2][i & 3];
+            const float x = fast_exp2(s[i] * c2 - li);
+            pv[i] = ((keep >> (8 * (i >> 2) + (i & 3))) & 1u) ? x : 0.f;  // a select: li may be -inf
+            dsv[i] = pv[i] * (dpv[i] - di);
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const float li = l4[i >> 2][i & 3], di = d4[i >> 2][i & 3];
+            const int r = 8 * (i >> 2) + 4 * g + (i & 3);
+            const int q = cur.q0 + c0 + r;  // this register's query row
+            const float x = fast_exp2(s[i] * c2 - li);
+            const bool on = kv_ok && q < cur.qend && in_band(p, q, my_kv) && !((ex >> r) & 1u);
+            pv[i] = on ? x : 0.f;  // a select: li may be -inf where nothing is left
+            dsv[i] = pv[i] * (dpv[i] - di);
+          }
         }
       }
       const u16x8 pa[2] = {pack8<E>(pv), pack8<E>(pv + 8)};
@@ -1232,12 +1248,23 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(D >= 256
       for (int i = 0; i < 16; ++i) dsv[i] = fast_exp2(st[i] * c2 - l2) * (dpt[i] - dl);
     } else {
       const uint32_t ex = AM ? mask_word(sAB[slot][AM ? w : 0], row0, l32) : 0u;
+      if (!p.win) {  // uniform: only the slice's valid keys and the attenMask cut
+        // bit kv of keep: slice key kv takes part; shifted as in the dK/dV kernel
+        const uint32_t keys_ok = nrows >= 32 ? 0xffffffffu : ((1u << nrows) - 1u);
+        const uint32_t keep = (keys_ok & ~ex) >> (4 * g);
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int kv = 8 * (i >> 2) + 4 * g + (i & 3);  // this register's key row in the slice
-        const bool on = kv < nrows && (!p.win || in_band(p, my_q, row0 + kv)) && !((ex >> kv) & 1u);
-        const float x = on ? fast_exp2(st[i] * c2 - l2) : 0.f;  // a select: l2 may be -inf off the window
-        dsv[i] = x * (dpt[i] - dl);
+        for (int i = 0; i < 16; ++i) {
+          const float x = ((keep >> (8 * (i >> 2) + (i & 3))) & 1u) ? fast_exp2(st[i] * c2 - l2) : 0.f;
+          dsv[i] = x * (dpt[i] - dl);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int kv = 8 * (i >> 2) + 4 * g + (i & 3);  // this register's key row in the slice
+          const bool on = kv < nrows && in_band(p, my_q, row0 + kv) && !((ex >> kv) & 1u);
+          const float x = on ? fast_exp2(st[i] * c2 - l2) : 0.f;  // a select: l2 may be -inf off the window
+          dsv[i] = x * (dpt[i] - dl);
+        }
       }
     }
     const u16x8 da[2] = {pack8<E>(dsv), pack8<E>(dsv + 8)};
@@ -1398,12 +1425,22 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(D >= 256
       }
     } else {
       const uint32_t ex = AM ? mask_word(sAB[slot][AM ? w : 0], row0, l32) : 0u;
+      if (!p.win) {  // uniform: only the slice's valid keys and the attenMask cut
+        const uint32_t keys_ok = nrows >= 32 ? 0xffffffffu : ((1u << nrows) - 1u);
+        const uint32_t keep = (keys_ok & ~ex) >> (4 * g);
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int kv = 8 * (i >> 2) + 4 * g + (i & 3);  // this register's key row in the slice
-        const bool on = kv < nrows && (!p.win || in_band(p, my_q, row0 + kv)) && !((ex >> kv) & 1u);
-        x[i] = on ? st[i] * c2 : -__builtin_inff();
-        mx = fmaxf(mx, x[i]);
+        for (int i = 0; i < 16; ++i) {
+          x[i] = ((keep >> (8 * (i >> 2) + (i & 3))) & 1u) ? st[i] * c2 : -__builtin_inff();
+          mx = fmaxf(mx, x[i]);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int kv = 8 * (i >> 2) + 4 * g + (i & 3);  // this register's key row in the slice
+          const bool on = kv < nrows && in_band(p, my_q, row0 + kv) && !((ex >> kv) & 1u);
+          x[i] = on ? st[i] * c2 : -__builtin_inff();
+          mx = fmaxf(mx, x[i]);
+        }
       }
     }
     mx = fmaxf(mx, __shfl_xor(mx, 32));  // the partner lane holds the row's other 16 keys
