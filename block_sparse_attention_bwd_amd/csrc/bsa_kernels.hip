@@ -92,14 +92,29 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // The sliding window (preTokens / nextTokens): key position j takes part for
 // query position i only if i - pre <= j <= i + next.  Positions are below
 // 2^31, so j - i fits in 32 bits; pre and next are clamped on the host.
-__device__ __forceinline__ bool in_band(const Params& p, int i, int j) {
-  const int d = j - i;
-  return d >= -p.win_pre && d <= p.win_next;
-}
 // Every pair of rows [r0, r0 + nr) x columns [c0, c0 + nc) is in the window
 // (true without one): the differences j - i fill [c0 - r0 - nr + 1, c0 + nc - 1 - r0].
 __device__ __forceinline__ bool rect_in_band(const Params& p, int r0, int nr, int c0, int nc) {
   return !p.win || (c0 - (r0 + nr - 1) >= -p.win_pre && (c0 + nc - 1) - r0 <= p.win_next);
+}
+// Bits lo..hi (clipped to 0..31) of a 32-bit word: the contiguous run of a
+// slice's 32 rows or keys that a lane's window admits (0 if none).
+__device__ __forceinline__ uint32_t bit_run(int64_t lo, int64_t hi) {
+  if (lo < 0) lo = 0;
+  if (hi > 31) hi = 31;
+  if (lo > hi) return 0u;
+  return (0xffffffffu >> (31 - static_cast<int>(hi))) & (0xffffffffu << static_cast<int>(lo));
+}
+// The rows r of a slice whose query qs + r has key j in the window
+// (i - pre <= j <= i + next, i.e. j - next <= i <= j + pre); all without one.
+__device__ __forceinline__ uint32_t band_rows(const Params& p, int qs, int j) {
+  if (!p.win) return 0xffffffffu;
+  return bit_run(static_cast<int64_t>(j) - p.win_next - qs, static_cast<int64_t>(j) + p.win_pre - qs);
+}
+// The keys k of a slice starting at key row0 in the window of query i.
+__device__ __forceinline__ uint32_t band_keys(const Params& p, int i, int row0) {
+  if (!p.win) return 0xffffffffu;
+  return bit_run(static_cast<int64_t>(i) - p.win_pre - row0, static_cast<int64_t>(i) + p.win_next - row0);
 }
 // attenMask bits of a 32-key slice starting at key row0, for the query of
 // lane l32, from the two words staged for it (bit k: key row0 + k excluded).
@@ -982,31 +997,19 @@ __device__ __forceinline__ void dkdv_work(const Params& p, int item, unsigned sh
           const uint64_t two = (static_cast<uint64_t>(sB[buf][m0 + 1][32 * w + l32]) << 32) | sB[buf][m0][32 * w + l32];
           ex = static_cast<uint32_t>(two >> (qs & 31));
         }
-        if (!p.win) {  // uniform: only the tile's valid rows and the attenMask cut
-          // bit r of keep: slice row r takes part (this lane's key valid, row in
-          // range, not excluded); shifted so that register i tests bit
-          // 8 (i / 4) + i % 4, its row minus 4g
-          const int nv = cur.qend - (cur.q0 + c0);  // >= 1
-          const uint32_t rows_ok = nv >= 32 ? 0xffffffffu : ((1u << nv) - 1u);
-          const uint32_t keep = (kv_ok ? rows_ok & ~ex : 0u) >> (4 * g);
+        // bit r of keep: slice row r takes part (this lane's key valid, row in
+        // range, in the window, not excluded); shifted so that register i
+        // tests bit 8 (i / 4) + i % 4, its row minus 4g
+        const int qs = cur.q0 + c0;
+        const int nv = cur.qend - qs;  // >= 1
+        const uint32_t rows_ok = nv >= 32 ? 0xffffffffu : ((1u << nv) - 1u);
+        const uint32_t keep = (kv_ok ? rows_ok & ~ex & band_rows(p, qs, my_kv) : 0u) >> (4 * g);
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const float li = l4[i >> 2][i & 3], di = d4[i >> 2][i & 3];
-            const float x = fast_exp2(s[i] * c2 - li);
-            pv[i] = ((keep >> (8 * (i >> 2) + (i & 3))) & 1u) ? x : 0.f;  // a select: li may be -inf
-            dsv[i] = pv[i] * (dpv[i] - di);
-          }
-        } else {
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const float li = l4[i >> 2][i & 3], di = d4[i >> 2][i & 3];
-            const int r = 8 * (i >> 2) + 4 * g + (i & 3);
-            const int q = cur.q0 + c0 + r;  // this register's query row
-            const float x = fast_exp2(s[i] * c2 - li);
-            const bool on = kv_ok && q < cur.qend && in_band(p, q, my_kv) && !((ex >> r) & 1u);
-            pv[i] = on ? x : 0.f;  // a select: li may be -inf where nothing is left
-            dsv[i] = pv[i] * (dpv[i] - di);
-          }
+        for (int i = 0; i < 16; ++i) {
+          const float li = l4[i >> 2][i & 3], di = d4[i >> 2][i & 3];
+          const float x = fast_exp2(s[i] * c2 - li);
+          pv[i] = ((keep >> (8 * (i >> 2) + (i & 3))) & 1u) ? x : 0.f;  // a select: li may be -inf
+          dsv[i] = pv[i] * (dpv[i] - di);
         }
       }
       const u16x8 pa[2] = {pack8<E>(pv), pack8<E>(pv + 8)};
@@ -1248,23 +1251,14 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(D >= 256
       for (int i = 0; i < 16; ++i) dsv[i] = fast_exp2(st[i] * c2 - l2) * (dpt[i] - dl);
     } else {
       const uint32_t ex = AM ? mask_word(sAB[slot][AM ? w : 0], row0, l32) : 0u;
-      if (!p.win) {  // uniform: only the slice's valid keys and the attenMask cut
-        // bit kv of keep: slice key kv takes part; shifted as in the dK/dV kernel
-        const uint32_t keys_ok = nrows >= 32 ? 0xffffffffu : ((1u << nrows) - 1u);
-        const uint32_t keep = (keys_ok & ~ex) >> (4 * g);
+      // bit kv of keep: slice key kv takes part (valid, in the window, not
+      // excluded); shifted as in the dK/dV kernel
+      const uint32_t keys_ok = nrows >= 32 ? 0xffffffffu : ((1u << nrows) - 1u);
+      const uint32_t keep = (keys_ok & ~ex & band_keys(p, my_q, row0)) >> (4 * g);
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float x = ((keep >> (8 * (i >> 2) + (i & 3))) & 1u) ? fast_exp2(st[i] * c2 - l2) : 0.f;
-          dsv[i] = x * (dpt[i] - dl);
-        }
-      } else {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int kv = 8 * (i >> 2) + 4 * g + (i & 3);  // this register's key row in the slice
-          const bool on = kv < nrows && in_band(p, my_q, row0 + kv) && !((ex >> kv) & 1u);
-          const float x = on ? fast_exp2(st[i] * c2 - l2) : 0.f;  // a select: l2 may be -inf off the window
-          dsv[i] = x * (dpt[i] - dl);
-        }
+      for (int i = 0; i < 16; ++i) {
+        const float x = ((keep >> (8 * (i >> 2) + (i & 3))) & 1u) ? fast_exp2(st[i] * c2 - l2) : 0.f;
+        dsv[i] = x * (dpt[i] - dl);
       }
     }
     const u16x8 da[2] = {pack8<E>(dsv), pack8<E>(dsv + 8)};
@@ -1425,22 +1419,11 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(D >= 256
       }
     } else {
       const uint32_t ex = AM ? mask_word(sAB[slot][AM ? w : 0], row0, l32) : 0u;
-      if (!p.win) {  // uniform: only the slice's valid keys and the attenMask cut
-        const uint32_t keys_ok = nrows >= 32 ? 0xffffffffu : ((1u << nrows) - 1u);
-        const uint32_t keep = (keys_ok & ~ex) >> (4 * g);
+      const uint32_t keep = ((nrows >= 32 ? 0xffffffffu : ((1u << nrows) - 1u)) & ~ex & band_keys(p, my_q, row0)) >> (4 * g);
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          x[i] = ((keep >> (8 * (i >> 2) + (i & 3))) & 1u) ? st[i] * c2 : -__builtin_inff();
-          mx = fmaxf(mx, x[i]);
-        }
-      } else {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int kv = 8 * (i >> 2) + 4 * g + (i & 3);  // this register's key row in the slice
-          const bool on = kv < nrows && in_band(p, my_q, row0 + kv) && !((ex >> kv) & 1u);
-          x[i] = on ? st[i] * c2 : -__builtin_inff();
-          mx = fmaxf(mx, x[i]);
-        }
+      for (int i = 0; i < 16; ++i) {
+        x[i] = ((keep >> (8 * (i >> 2) + (i & 3))) & 1u) ? st[i] * c2 : -__builtin_inff();
+        mx = fmaxf(mx, x[i]);
       }
     }
     mx = fmaxf(mx, __shfl_xor(mx, 32));  // the partner lane holds the row's other 16 keys
