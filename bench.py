@@ -238,35 +238,91 @@ class FwdRunner:
 # ---------------------------------------------------------------------------
 # CPU baseline: the oracle on a bounded sample
 # ---------------------------------------------------------------------------
-def cpu_baseline(case, o_host, lse_host, min_seconds=10.0, max_runs=5, op="bwd"):
-    """Time the fp64 oracle backward (or forward) on the whole workload (median of repeated runs)."""
-    import oracle
+def _cpu_model():
     try:
-        from threadpoolctl import threadpool_info
-        cores = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
-    except Exception:  # pragma: no cover
-        cores = os.cpu_count() or 1
-    kw = dict(layout=case.layout, bx=case.bx, by=case.by, scale=case.scale)
-    if case.explicit_lengths or case.layout == "TND":
-        kw.update(len_q=case.len_q, len_kv=case.len_kv)
-    times = []
-    t_start = time.perf_counter()
-    while not times or (time.perf_counter() - t_start < min_seconds and len(times) < max_runs):
-        t0 = time.perf_counter()
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _sub_problems(case, q, k, v, o, do, lse):
+    """The workload cut into independent (sequence, KV head) pieces: each holds one
+    sequence and the query heads of one KV head's group, with their mask rows, so
+    the oracle's results on the pieces are disjoint slices of the whole result.
+    Yields (query-side index, key-side index, oracle arguments, oracle keywords);
+    the indices place a piece's dq (resp. dk, dv) in the whole tensor."""
+    G = case.N // case.Nkv
+    offq = np.concatenate([[0], np.cumsum(case.len_q)[:-1]]).astype(np.int64)
+    offk = np.concatenate([[0], np.cumsum(case.len_kv)[:-1]]).astype(np.int64)
+    lengths = case.explicit_lengths or case.layout == "TND"
+    for b in range(case.B):
+        for h in range(case.Nkv):
+            hs = slice(h * G, (h + 1) * G)
+            if case.layout == "BNSD":
+                iq, ik = (slice(b, b + 1), hs), (slice(b, b + 1), slice(h, h + 1))
+            else:
+                iq = (slice(int(offq[b]), int(offq[b] + case.len_q[b])), hs)
+                ik = (slice(int(offk[b]), int(offk[b] + case.len_kv[b])), slice(h, h + 1))
+            kw = dict(layout=case.layout, bx=case.bx, by=case.by, scale=case.scale, window=case.window,
+                      atten_mask=case.atten_mask)
+            if lengths:
+                kw.update(len_q=case.len_q[b:b + 1], len_kv=case.len_kv[b:b + 1])
+            mask = None if case.mask is None else case.mask[b:b + 1, hs]
+            sub = lambda x, i: None if x is None else x[i]
+            yield iq, ik, (q[iq], k[ik], v[ik], sub(o, iq), do[iq], sub(lse, iq), mask), kw
+
+
+def cpu_baseline(case, o_host, lse_host, min_seconds=10.0, max_runs=5, op="bwd", max_workers=16):
+    """Time the fp64 oracle backward (or forward) on the whole workload.
+
+    The oracle runs unchanged on independent (sequence, KV head) pieces of the
+    workload, spread over a pool of threads (NumPy's BLAS calls and large array
+    operations release the interpreter lock), with BLAS held to one thread per
+    worker so that ``cores`` is the number of threads actually used.  The
+    median of repeated runs (at least one, until ``min_seconds`` have passed)."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    import oracle
+    from threadpoolctl import threadpool_info, threadpool_limits
+    pieces = [(a, kw) for _, _, a, kw in _sub_problems(case, case.q, case.k, case.v, o_host, case.do, lse_host)]
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        avail = os.cpu_count() or 1
+    workers = max(1, min(avail, max_workers, len(pieces)))
+    blas = [f"{i.get('internal_api')} {i.get('version')}" for i in threadpool_info() if i.get("user_api") == "blas"]
+
+    def one(piece):
+        (q, k, v, o, do, lse, mask), kw = piece
         if op == "fwd":
-            oracle.forward(case.q, case.k, case.v, case.mask, **kw)
+            oracle.forward(q, k, v, mask, **kw)
         else:
-            oracle.backward(case.q, case.k, case.v, o_host, case.do, lse_host, case.mask, **kw)
-        times.append(time.perf_counter() - t0)
+            oracle.backward(q, k, v, o, do, lse, mask, **kw)
+
+    times = []
+    with threadpool_limits(limits=1, user_api="blas"), ThreadPoolExecutor(max_workers=workers) as pool:
+        t_start = time.perf_counter()
+        while not times or (time.perf_counter() - t_start < min_seconds and len(times) < max_runs):
+            t0 = time.perf_counter()
+            list(pool.map(one, pieces))
+            times.append(time.perf_counter() - t0)
     dt = float(np.median(times))
     flops = (4.0 if op == "fwd" else 10.0) * case.bx * case.by * case.D * synth_blocks(case)
     return {
         "value": round(flops / dt / 1e12, 5),
         "unit": "TFLOP/s",
-        "cores": int(cores),
+        "cores": int(workers),
         "kind": "oracle",
         "sample": f"the whole workload (all batches and heads), fp64 NumPy {'forward' if op == 'fwd' else 'backward'} only, "
+                  f"as {len(pieces)} (sequence, KV head) pieces on {workers} threads with 1 BLAS thread each; "
                   f"median of {len(times)} runs: {dt:.2f} s",
+        "cpu_model": _cpu_model(),
+        "cpus_available": int(avail),
+        "blas": ", ".join(blas) or "unknown",
     }
 
 
@@ -285,7 +341,7 @@ def active_blocks(case):
         j = np.arange(nk_b)[None, :]
         r0, r1 = i * case.bx, np.minimum(i * case.bx + case.bx, lq)
         c0, c1 = j * case.by, np.minimum(j * case.by + case.by, lk)
-        meets = (c0 - (r1 - 1) <= nxt) & ((c1 - 1) - r0 >= -pre)
+        meets = (c0 - (r1 - 1) <= nxt) & ((c1 - 1) - r0 >= -pre) & (-pre <= nxt)
         sel = np.ones((case.N, nq_b, nk_b), bool) if case.mask is None else case.mask[b, :, :nq_b, :nk_b] != 0
         total += int(np.count_nonzero(sel & meets[None]))
     return total
@@ -293,6 +349,48 @@ def active_blocks(case):
 
 def synth_blocks(case):
     return active_blocks(case)
+
+
+PEAK_CLOCK_MHZ = 2400.0  # the clock the published MFMA peak is quoted at
+
+
+def sustained_clock_mhz(run, torch, seconds=1.0, chunk=20):
+    """Median shader clock (MHz) sampled from the driver while the calls run back to
+    back for about ``seconds``; None where the driver gives no reading."""
+    import threading
+    samples, done = [], threading.Event()
+
+    def poll():
+        while not done.is_set():
+            try:
+                mhz = float(torch.cuda.clock_rate())
+            except Exception:  # no reading on this machine
+                return
+            if mhz > 0:
+                samples.append(mhz)
+            done.wait(0.005)
+
+    for _ in range(chunk):  # the GPU is busy before the first sample
+        run()
+    t = threading.Thread(target=poll, daemon=True)
+    t.start()
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(chunk):
+            run()
+        torch.cuda.synchronize()
+    done.set()
+    t.join()
+    return float(np.median(samples)) if samples else None
+
+
+def clock_report(clock_mhz, tflops):
+    """The value as a fraction of the MFMA peak scaled to the sustained clock."""
+    if clock_mhz is None:
+        return {"sustained_mhz": None, "frac_of_peak_at_sustained_clock": None}
+    peak = MFMA_PEAK_BF16_TFLOPS * clock_mhz / PEAK_CLOCK_MHZ
+    return {"sustained_mhz": round(clock_mhz, 1), "peak_at_sustained_clock": round(peak, 1),
+            "frac_of_peak_at_sustained_clock": round(tflops / peak, 4)}
 
 
 def kernel_source_hash():
@@ -405,6 +503,17 @@ def main(argv=None):
     end.record(stream)
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(end)
+    # per-call durations: K more calls, each between its own pair of events
+    # (outside the timed region: events between calls add to the stream's time)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for a, b in evs:
+        a.record(stream)
+        run()
+        b.record(stream)
+    torch.cuda.synchronize()
+    per_call = np.array([a.elapsed_time(b) for a, b in evs])
+    p10, p50, p90 = (float(x) for x in np.percentile(per_call, [10, 50, 90]))
+    clock_mhz = sustained_clock_mhz(run, torch)
     # per-kernel durations: K more calls with the library's HIP events between
     # its stages, on the launch stream (kept out of the timed region above,
     # since each event adds a few microseconds to the stream)
@@ -415,6 +524,8 @@ def main(argv=None):
     stage_ms, ncalls = bsa.bsa_profile_stop()
     ms = total_ms / args.steps
     tflops = flops / (ms * 1e-3) / 1e12
+    print(f"# per call: median {p50:.4f} ms (p10 {p10:.4f}, p90 {p90:.4f}); clock {clock_mhz} MHz", file=sys.stderr,
+          flush=True)
     print(f"# {ms:.4f} ms/step; stages (avg ms): " +
           ", ".join(f"{k}={v / max(1, ncalls):.4f}" for k, v in stage_ms.items()), file=sys.stderr, flush=True)
 
@@ -471,6 +582,9 @@ def main(argv=None):
         },
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "call_ms": {"median": round(p50, 5), "p10": round(p10, 5), "p90": round(p90, 5), "calls": args.steps,
+                    "tflops_at_median": round(flops / (p50 * 1e-3) / 1e12, 3)},
+        "clock": clock_report(clock_mhz, tflops),
     }
     print(json.dumps(out), flush=True)
     return 0

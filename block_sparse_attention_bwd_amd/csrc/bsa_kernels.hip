@@ -122,9 +122,12 @@ __device__ __forceinline__ uint32_t mask_word(const uint32_t* staged, int row0, 
   const uint64_t two = (static_cast<uint64_t>(staged[32 + l32]) << 32) | staged[l32];
   return static_cast<uint32_t>(two >> (row0 & 31));
 }
-// Some pair of the rectangle is in the window.
+// Some pair of the rectangle is in the window: the differences j - i over it
+// fill [c0 - (r0 + nr - 1), c0 + nc - 1 - r0], which must meet [-pre, next]
+// (empty when pre + next < 0: such a window admits no pair at all).
 __device__ __forceinline__ bool rect_meets_band(const Params& p, int r0, int nr, int c0, int nc) {
-  return !p.win || (c0 - (r0 + nr - 1) <= p.win_next && (c0 + nc - 1) - r0 >= -p.win_pre);
+  return !p.win || (c0 - (r0 + nr - 1) <= p.win_next && (c0 + nc - 1) - r0 >= -p.win_pre &&
+                    static_cast<int64_t>(p.win_pre) + p.win_next >= 0);
 }
 
 // ---------------------------------------------------------------------------

@@ -70,6 +70,7 @@ __all__ = [
     "allowed_pairs",
     "element_mask",
     "block_lists",
+    "block_list_arrays",
     "softmax_grad",
     "head_probs_and_ds",
     "forward",
@@ -202,6 +203,40 @@ def block_lists(mask: Optional[np.ndarray], B: int, N: int, nqb: int, nkb: int, 
                         row_lists[b][n][i].append(j)
                         col_lists[b][n][j].append(i)
     return row_lists, col_lists
+
+
+def block_list_arrays(mask: Optional[np.ndarray], B: int, N: int, nqb: int, nkb: int, bx: int, by: int,
+                      len_q: Sequence[int], len_kv: Sequence[int], window=None):
+    """``block_lists``' rule evaluated on whole arrays, for full-size problems.
+
+    Returns ``(row_cnt [B,N,nqb], row_idx [B,N,nqb,nkb], col_cnt [B,N,nkb],
+    col_idx [B,N,nkb,nqb])`` (int64): row (b, n, i) lists its ``row_cnt``
+    selected KV blocks ascending in ``row_idx[b, n, i, :row_cnt]``; the entries
+    after them are not part of the result.  A block (i, j) is listed when the
+    mask selects it, ``i < ceil(Lq_b/bx)``, ``j < ceil(Lkv_b/by)`` and, with a
+    window ``(pre, nxt)``, some in-range pair of it has ``-pre <= j' - i' <= nxt``:
+    over the block's in-range rows [r0, r1) and keys [c0, c1) the differences
+    j' - i' fill the interval [c0 - (r1 - 1), (c1 - 1) - r0], which must meet
+    [-pre, nxt] (an empty window, ``pre + nxt < 0``, meets no block).
+    """
+    sel = np.ones((B, N, nqb, nkb), bool) if mask is None else np.asarray(mask).reshape(B, N, nqb, nkb) != 0
+    sel = sel.copy()
+    i = np.arange(nqb, dtype=np.int64)[:, None]
+    j = np.arange(nkb, dtype=np.int64)[None, :]
+    for b in range(B):
+        lq, lk = int(len_q[b]), int(len_kv[b])
+        ok = (i < -(-lq // bx)) & (j < -(-lk // by))
+        if window is not None:
+            pre, nxt = window
+            r0, r1 = i * bx, np.minimum(i * bx + bx, lq)
+            c0, c1 = j * by, np.minimum(j * by + by, lk)
+            ok &= (c0 - (r1 - 1) <= nxt) & ((c1 - 1) - r0 >= -pre) & (-pre <= nxt)
+        sel[b] &= ok[None]
+    # a stable sort of "not selected" puts the selected indices first, ascending
+    row_idx = np.argsort(~sel, axis=3, kind="stable")
+    col_sel = np.ascontiguousarray(sel.transpose(0, 1, 3, 2))
+    col_idx = np.argsort(~col_sel, axis=3, kind="stable")
+    return sel.sum(axis=3), row_idx, col_sel.sum(axis=3), col_idx
 
 
 # ---------------------------------------------------------------------------

@@ -66,6 +66,10 @@ def case(name):
         "bnsd_fp16_d128_window_zero": lambda: mk(layout="BNSD", dtype="fp16", B=1, N=2, Nkv=1, D=128,
                                                  Sq=256, Skv=256, bx=128, by=128, mask_rule="ones",
                                                  window=(0, 0), seed=118),
+        # an empty window (pre + next < 0 admits no pair): no block is listed, every output is 0
+        "bnsd_bf16_d64_window_empty": lambda: mk(layout="BNSD", dtype="bf16", B=1, N=2, Nkv=1, D=64, Sq=160,
+                                                 Skv=96, bx=32, by=32, mask_rule="ones", window=(2, -4),
+                                                 seed=119),
         # attenMask (30% of pairs removed, one row emptied), GQA, ragged
         "bnsd_bf16_d128_attenmask": lambda: mk(layout="BNSD", dtype="bf16", B=2, N=4, Nkv=2, D=128, Sq=200,
                                                Skv=260, bx=64, by=64, p=0.7, seed=124),
@@ -129,7 +133,7 @@ SMALL = ["config1", "bnsd_bf16_d128_b128x128_ragged", "bnsd_fp16_d64_b64x128_pad
          "bnsd_fp16_d128_b256x256", "bnsd_bf16_d64_b1x1", "bnsd_bf16_d128_nullmask",
          "tnd_bf16_d64_empty_seqs", "bnsd_fp16_d128_sparse_rows", "bnsd_bf16_d128_local_sink_split",
          "bnsd_fp16_d64_sink_split_parts", "bnsd_bf16_d128_window", "tnd_fp16_d64_window_ahead",
-         "bnsd_fp16_d128_window_zero", "bnsd_bf16_d128_window_sink_split", "bnsd_bf16_d128_attenmask",
+         "bnsd_fp16_d128_window_zero", "bnsd_bf16_d64_window_empty", "bnsd_bf16_d128_window_sink_split", "bnsd_bf16_d128_attenmask",
          "tnd_fp16_d64_attenmask_window", "bnsd_bf16_d256_b128x128_ragged", "tnd_fp16_d256_b64x64_gqa",
          "bnsd_fp16_d256_sink_split", "bnsd_bf16_d256_window_attenmask", "bnsd_fp16_d128_b64x128_attenmask_window",
          "bnsd_bf16_d128_b64x128_sink_split", "tnd_bf16_d64_70_seqs"]

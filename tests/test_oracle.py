@@ -502,3 +502,60 @@ def test_p_rows_sum_to_one_with_fp32_lse(spec):
         rs = P.sum(axis=1)
         assert np.all(np.abs(rs[fin] - 1.0) <= 4 * 2.0 ** -24 * np.maximum(1.0, np.abs(ls[fin]))), (b, n)
         assert np.all(rs[~fin] == 0.0)
+
+
+@pytest.mark.parametrize("seed,window", [(0, None), (1, None), (2, (5, 0)), (3, (-2, 7)), (4, (0, -3))])
+def test_block_list_arrays_match_brute_force(seed, window):
+    """The whole-array form of the list rule (used on full-size problems) gives
+    exactly the brute-force lists: counts, and the first `count` entries of each row."""
+    rng = np.random.default_rng(100 + seed)
+    B, N, bx, by = 3, 2, int(rng.integers(1, 6)), int(rng.integers(1, 6))
+    lq = rng.integers(0, 40, size=B)
+    lk = rng.integers(0, 40, size=B)
+    lq[0], lk[0] = 37, 39  # at least one long sequence
+    nqb, nkb = -(-int(lq.max()) // bx), -(-int(lk.max()) // by)
+    mask = (rng.random((B, N, nqb, nkb)) < 0.45).astype(np.uint8)
+    rows, cols = oracle.block_lists(mask, B, N, nqb, nkb, bx, by, lq, lk, window=window)
+    rc, ri, cc, ci = oracle.block_list_arrays(mask, B, N, nqb, nkb, bx, by, lq, lk, window=window)
+    for b in range(B):
+        for n in range(N):
+            for i in range(nqb):
+                assert rc[b, n, i] == len(rows[b][n][i])
+                assert ri[b, n, i, :rc[b, n, i]].tolist() == rows[b][n][i]
+            for j in range(nkb):
+                assert cc[b, n, j] == len(cols[b][n][j])
+                assert ci[b, n, j, :cc[b, n, j]].tolist() == cols[b][n][j]
+
+
+def test_block_list_arrays_null_mask_and_long_rows():
+    """No mask selects every in-range block; rows longer than 512 blocks (by = 1)."""
+    B, N, bx, by = 2, 1, 64, 1
+    lq, lk = np.array([130, 64]), np.array([600, 517])
+    nqb, nkb = 3, 600
+    rows, cols = oracle.block_lists(None, B, N, nqb, nkb, bx, by, lq, lk)
+    rc, ri, cc, ci = oracle.block_list_arrays(None, B, N, nqb, nkb, bx, by, lq, lk)
+    assert rc[0, 0].tolist() == [600, 600, 600] and rc[1, 0].tolist() == [517, 0, 0]
+    assert ri[0, 0, 2, :600].tolist() == list(range(600)) == rows[0][0][2]
+    assert cc[1, 0, :517].tolist() == [1] * 517 and cc[1, 0, 517:].tolist() == [0] * 83
+    assert all(ci[1, 0, j, :1].tolist() == cols[1][0][j] for j in range(517))
+
+
+@pytest.mark.parametrize("layout", ["BNSD", "TND"])
+def test_piecewise_threaded_backward_equals_whole(layout):
+    """The full-size parity tests and the CPU baseline run the oracle on
+    (sequence, KV head) pieces in threads; put back together the pieces are
+    bitwise the whole-problem result (same arithmetic, same order per head)."""
+    from gpu_common import oracle_backward_threaded
+    kw = dict(layout=layout, dtype="bf16", B=3, N=4, Nkv=2, D=16, bx=8, by=16, p=0.5, seed=77)
+    if layout == "TND":
+        kw.update(lengths_q=[40, 0, 23], lengths_kv=[30, 17, 50])
+    else:
+        kw.update(Sq=40, Skv=50, lengths_q=[40, 11, 30], lengths_kv=[50, 20, 1])
+    c = synth.make_case(**kw)
+    c.window = (20, 3)
+    okw = dict(layout=c.layout, bx=c.bx, by=c.by, scale=c.scale, window=c.window, len_q=c.len_q, len_kv=c.len_kv)
+    o, lse = oracle.forward(c.q, c.k, c.v, c.mask, **okw)
+    whole = oracle.backward(c.q, c.k, c.v, o, c.do, lse, c.mask, **okw)
+    parts = oracle_backward_threaded(c, c.q, c.k, c.v, o, c.do, lse, workers=4)
+    for a, b in zip(whole, parts):
+        assert np.array_equal(a, b)

@@ -89,7 +89,7 @@ def test_zero_width_window_closed_form():
     np.testing.assert_allclose(dv, do, rtol=0, atol=1e-14)
 
 
-WINDOWS = [(0, 0), (2, 1), (-2, 4), (5, -3), (40, 40), (3, 0)]
+WINDOWS = [(0, 0), (2, 1), (-2, 4), (5, -3), (40, 40), (3, 0), (2, -4)]
 
 
 @pytest.mark.parametrize("window", WINDOWS)
@@ -116,7 +116,8 @@ def test_window_slab_path_equals_dense_path(window):
 @pytest.mark.parametrize("window", WINDOWS)
 def test_window_block_lists_follow_the_interval_rule(window):
     """A selected in-range block is listed iff the differences j - i over its clipped
-    rectangle, the integer range [c0 - (r1 - 1), (c1 - 1) - r0], meet [-pre, nxt]."""
+    rectangle, the integer range [c0 - (r1 - 1), (c1 - 1) - r0], meet [-pre, nxt]
+    (which is empty when pre + nxt < 0: then nothing is listed)."""
     rng = np.random.default_rng(7)
     B, N, bx, by = 2, 2, 3, 4
     lq, lk = np.array([17, 9]), np.array([13, 21])
@@ -133,7 +134,7 @@ def test_window_block_lists_follow_the_interval_rule(window):
                         continue
                     r0, r1 = i * bx, min(i * bx + bx, int(lq[b]))
                     c0, c1 = j * by, min(j * by + by, int(lk[b]))
-                    if c0 - (r1 - 1) <= nxt and (c1 - 1) - r0 >= -pre:
+                    if c0 - (r1 - 1) <= nxt and (c1 - 1) - r0 >= -pre and -pre <= nxt:
                         want.append(j)
                 assert rows[b][n][i] == want, (b, n, i)
             for j in range(nkb):
