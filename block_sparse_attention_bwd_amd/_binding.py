@@ -409,9 +409,21 @@ def block_sparse_attention(query, key, value, block_sparse_mask=None,
     ws = bsa_fwd_workspace_size(query, key, value, **kw)
     workspace = torch.empty(max(ws, 1), dtype=torch.uint8, device=query.device)
     bsa_fwd(query, key, value, **kw, workspace=workspace, workspace_size=ws, stream=stream)
-    if stream is not None and not isinstance(stream, int):
-        workspace.record_stream(stream)
+    _hold_until_done(workspace, stream)
     return out, lse
+
+
+def _hold_until_done(t, stream) -> None:
+    """Keep torch's caching allocator from handing out ``t`` (freed when the caller
+    returns) before the work enqueued on ``stream`` has finished with it.  With the
+    default stream (torch's current one) frees are already ordered on it; a raw
+    stream handle is wrapped so that the same bookkeeping applies."""
+    import torch
+    if stream is None:
+        return
+    if isinstance(stream, int):
+        stream = torch.cuda.ExternalStream(stream, device=t.device)
+    t.record_stream(stream)
 
 
 def bsa_last_error() -> str:
@@ -469,6 +481,5 @@ def block_sparse_attention_grad(dout, query, key, value, attention_out, softmax_
     workspace = torch.empty(max(ws, 1), dtype=torch.uint8, device=query.device)
     bsa_bwd(dout, query, key, value, attention_out, softmax_lse, **kw, workspace=workspace,
             workspace_size=ws, stream=stream)
-    if stream is not None and not isinstance(stream, int):
-        workspace.record_stream(stream)  # keep the caching allocator from reusing it early
+    _hold_until_done(workspace, stream)
     return dq, dk, dv

@@ -8,6 +8,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <string>
 #include <vector>
@@ -83,6 +84,25 @@ bool row_major_contiguous(const bsa_tensor* t) {
   for (int d = t->ndim - 1; d >= 0; --d) {
     if (t->shape[d] != 1 && t->stride[d] != expect) return false;
     expect *= t->shape[d];
+  }
+  return true;
+}
+
+// No two index tuples of t map to one element: taking the dimensions of
+// extent > 1 by ascending stride, each stride is at least the span of the
+// dimensions before it.  (A zero stride on such a dimension fails.)  This
+// accepts every layout torch makes by slicing, transposing or padding a
+// contiguous tensor.
+bool non_overlapping(const bsa_tensor* t) {
+  int idx[4], m = 0;
+  for (int d = 0; d < t->ndim; ++d)
+    if (t->shape[d] > 1) idx[m++] = d;
+  std::sort(idx, idx + m, [&](int x, int y) { return t->stride[x] < t->stride[y]; });
+  int64_t span = 1;  // elements covered by the dimensions taken so far
+  for (int i = 0; i < m; ++i) {
+    const int d = idx[i];
+    if (t->stride[d] < span) return false;
+    span = t->stride[d] * (t->shape[d] - 1) + span;
   }
   return true;
 }
@@ -292,6 +312,17 @@ int make_plan(const Args& a, Plan* plan) {
       return fail(BSA_ERR_PARAM_INVALID, "%s innermost stride must be 1", n.name);
     for (int d = 0; d < n.t->ndim - 1; ++d)
       if (n.t->stride[d] < 0) return fail(BSA_ERR_PARAM_INVALID, "%s has a negative stride", n.name);
+    if (!non_overlapping(n.t))
+      return fail(BSA_ERR_PARAM_INVALID,
+                  "%s strides let two elements share an address (each output element is written once)", n.name);
+  }
+  if (a.fwd) {  // attention_out is stored four elements (8 bytes) at a time
+    const bsa_tensor* o = a.attention_out;
+    bool ok = reinterpret_cast<uintptr_t>(o->data) % 8 == 0;
+    for (int d = 0; d < o->ndim - 1; ++d) ok = ok && o->stride[d] % 4 == 0;
+    if (!ok)
+      return fail(BSA_ERR_PARAM_INVALID,
+                  "attentionOut: data pointer must be 8-byte aligned and outer strides multiples of 4 elements");
   }
 
   // ---- sequence lengths (参数说明: actualSeqLengths[Kv]Optional) ----------
@@ -555,6 +586,45 @@ int make_plan(const Args& a, Plan* plan) {
   return BSA_OK;
 }
 
+// ---- plan dump (environment variable BSA_LOG=1) ---------------------------
+// One block of text on stderr per validated call: what was decided from the
+// arguments (sizes, block grid, work units, workspace regions, kernel shapes).
+// Read on every call, so it can be switched on and off while a process runs.
+bool plan_log_on() {
+  const char* v = std::getenv("BSA_LOG");
+  return v != nullptr && v[0] == '1';
+}
+
+void log_plan(const char* entry, const Args& a, const Plan& plan) {
+  static const char* const kRegion[BSA_WS_NUM] = {"seq", "delta", "lse2", "row_cnt", "row_list", "col_cnt",
+                                                  "col_list", "plan", "partial", "amask", "stage", "total"};
+  const bsa::Params& p = plan.p;
+  std::fprintf(stderr, "[bsa] %s: %s B=%d N=%d Nkv=%d G=%d D=%d dtype=%s maxSq=%d block=%dx%d nQB=%d nKB=%d\n",
+               entry, p.tnd ? "TND" : "BNSD", p.B, p.N, p.Nkv, p.G, p.D, a.fp8 ? "fp8->bf16" : dtype_name(p.dtype),
+               p.sq_max, p.bx, p.by, p.nqb, p.nkb);
+  std::fprintf(stderr, "[bsa]   mask=%s attenMask=%s window=%s", p.mask ? "given" : "null (dense)",
+               p.amask ? "given" : "none", p.win ? "" : "none");
+  if (p.win) std::fprintf(stderr, "[-%d, +%d]", p.win_pre, p.win_next);
+  std::fprintf(stderr, " scale=%.9g (scale*log2e=%.9g)\n", a.scale_value, static_cast<double>(p.scale_log2e));
+  for (size_t b = 0; b < plan.seq.size() && b < 8; ++b)
+    std::fprintf(stderr, "[bsa]   seq %zu: q[%lld +%d] kv[%lld +%d] writes %d / %d rows\n", b,
+                 static_cast<long long>(plan.seq[b].off_q), plan.seq[b].len_q,
+                 static_cast<long long>(plan.seq[b].off_kv), plan.seq[b].len_kv, plan.seq[b].wlim_q,
+                 plan.seq[b].wlim_kv);
+  if (plan.seq.size() > 8) std::fprintf(stderr, "[bsa]   ... %zu sequences in all\n", plan.seq.size());
+  if (!a.fwd)
+    std::fprintf(stderr, "[bsa]   dK/dV units=%d (+%d split slots, %d workgroup(s) per item)  dQ workgroups=%d\n",
+                 p.n_units, p.slots_cap, bsa::dkdv_passes(p.D), p.n_dq_units);
+  else
+    std::fprintf(stderr, "[bsa]   forward workgroups=%d\n", p.n_dq_units);
+  for (int r = 0; r < BSA_WS_TOTAL; ++r) {
+    const uint64_t sz = plan.off[r + 1] - plan.off[r];
+    if (sz) std::fprintf(stderr, "[bsa]   ws %-8s @%-12llu %llu bytes\n", kRegion[r],
+                         static_cast<unsigned long long>(plan.off[r]), static_cast<unsigned long long>(sz));
+  }
+  std::fprintf(stderr, "[bsa]   workspace total %llu bytes\n", static_cast<unsigned long long>(plan.off[BSA_WS_TOTAL]));
+}
+
 // ---- profiling -----------------------------------------------------------
 constexpr int kStages = 4;
 const char* const kStageNames[kStages] = {"prologue", "dkdv", "dq", "fwd"};
@@ -600,6 +670,7 @@ int run(const Args& a, void* workspace, uint64_t workspace_size, void* stream) {
   Plan plan;
   int rc = make_plan(a, &plan);
   if (rc) return rc;
+  if (plan_log_on()) log_plan(a.fwd ? "bsa_fwd" : "bsa_bwd", a, plan);
   const uint64_t need = plan.off[BSA_WS_TOTAL];
   if (workspace_size < need)
     return fail(BSA_ERR_PARAM_INVALID, "workspace of %llu bytes is smaller than the %llu needed",
@@ -743,8 +814,10 @@ int bsa_bwd_workspace_size(BSA_ARGS_DECL, uint64_t* workspace_size) {
   g_err.clear();
   if (workspace_size == nullptr) return fail(BSA_ERR_PARAM_NULLPTR, "workspaceSize is a null pointer");
   Plan plan;
-  int rc = make_plan(BSA_ARGS_PACK, &plan);
+  const Args a = BSA_ARGS_PACK;
+  int rc = make_plan(a, &plan);
   if (rc) return rc;
+  if (plan_log_on()) log_plan("bsa_bwd_workspace_size", a, plan);
   *workspace_size = plan.off[BSA_WS_TOTAL];
   return BSA_OK;
 }
@@ -770,8 +843,10 @@ int bsa_fwd_workspace_size(BSA_FWD_ARGS_DECL, uint64_t* workspace_size) {
   g_err.clear();
   if (workspace_size == nullptr) return fail(BSA_ERR_PARAM_NULLPTR, "workspaceSize is a null pointer");
   Plan plan;
-  int rc = make_plan(BSA_FWD_ARGS_PACK, &plan);
+  const Args a = BSA_FWD_ARGS_PACK;
+  int rc = make_plan(a, &plan);
   if (rc) return rc;
+  if (plan_log_on()) log_plan("bsa_fwd_workspace_size", a, plan);
   *workspace_size = plan.off[BSA_WS_TOTAL];
   return BSA_OK;
 }

@@ -40,6 +40,11 @@
  * Error behaviour: every entry point returns BSA_OK or one of the bsa_status
  * codes below; on a non-zero status nothing has been enqueued and
  * bsa_last_error() (thread-local) describes the first failed check.
+ *
+ * Diagnostics: with the environment variable BSA_LOG=1 (read on every call),
+ * each call that passes validation (workspace-size queries included) writes
+ * its plan to stderr: sizes, block grid, sequence table, work units and the
+ * workspace regions with their offsets and sizes.
  */
 #ifndef BSA_BWD_H
 #define BSA_BWD_H
@@ -117,7 +122,9 @@ typedef struct bsa_tensor {
  *                              any int64 otherwise (a window that leaves a row no
  *                              key gives that row LSE = -inf and zero outputs).
  *  dq, dk, dv                  outputs, same dtype/shape as query/key/value;
- *                              any outer strides, innermost stride 1.
+ *                              any outer strides, innermost stride 1, no two
+ *                              elements at one address (zero or overlapping
+ *                              strides are rejected with 161002).
  *  workspace_size              out: bytes of device workspace needed.
  *
  * Head dim D must be 64, 128 or 256 (the tile set built into this library;
@@ -169,8 +176,11 @@ int bsa_bwd(const bsa_tensor* dout, const bsa_tensor* query, const bsa_tensor* k
  *
  * Arguments are those of bsa_bwd_workspace_size without dout, dq, dk and dv, in
  * the same order and with the same rules, except:
- *  attention_out   output, dtype of query, shape of query; any outer strides,
- *                  innermost stride 1.  Every element is written.
+ *  attention_out   output, dtype of query, shape of query; outer strides
+ *                  multiples of 4 elements, innermost stride 1, no two elements
+ *                  at one address; data pointer 8-byte aligned (it is stored
+ *                  four elements at a time; 161002 otherwise).  Every element
+ *                  is written.
  *  softmax_lse     output, fp32, [B, N, S] / [B, N, S, 1] (BNSD) or
  *                  [T, N] / [T, N, 1] (TND), contiguous.  Every element is written.
  * Ownership, stream, workspace and error behaviour are as for bsa_bwd; the

@@ -67,3 +67,47 @@ def assert_close(name, got, ref, dtype, floor_ref=None):
             f"{name}: max abs err {err:.3e} > {bound:.3e} (max|ref| {ref_max:.3e}); worst at {idx}: "
             f"gpu {got[idx]:.6e} ref {ref[idx]:.6e}")
     return err, ref_max
+
+
+def oracle_backward_threaded(case, q, k, v, o, do, lse, workers=16):
+    """oracle.backward on the whole problem, run as independent (sequence, KV head)
+    pieces on a pool of threads (one BLAS thread each) and put back together.
+    Each piece is an unchanged oracle call; the pieces' outputs are disjoint."""
+    import os
+    from concurrent.futures import ThreadPoolExecutor
+
+    from threadpoolctl import threadpool_limits
+
+    from bench import _sub_problems
+    dq = np.zeros(q.shape, np.float64)
+    dk = np.zeros(k.shape, np.float64)
+    dv = np.zeros(v.shape, np.float64)
+    pieces = list(_sub_problems(case, q, k, v, o, do, lse))
+
+    def one(piece):
+        iq, ik, args, kw = piece
+        pq, pk, pv = oracle.backward(*args, **kw)
+        dq[iq], dk[ik], dv[ik] = pq, pk, pv
+
+    n = max(1, min(workers, len(os.sched_getaffinity(0)), len(pieces)))
+    with threadpool_limits(limits=1, user_api="blas"), ThreadPoolExecutor(max_workers=n) as pool:
+        list(pool.map(one, pieces))
+    return dq, dk, dv
+
+
+GUARD = 4096  # guard bytes on each side of every output and of the workspace
+
+
+def _guarded(shape, dtype):
+    """A tensor of `shape` in the middle of a larger buffer whose GUARD bytes on
+    each side hold a fixed pattern; returns (tensor, buffer, pattern)."""
+    import torch
+    n = int(np.prod(shape)) * torch.empty((), dtype=dtype).element_size()
+    buf = torch.randint(0, 256, (n + 2 * GUARD,), dtype=torch.uint8, device="cuda",
+                        generator=torch.Generator(device="cuda").manual_seed(n))
+    return buf[GUARD:GUARD + n].view(dtype).view(shape), buf, buf.clone()
+
+
+def _guards_intact(buf, pattern):
+    import torch
+    return torch.equal(buf[:GUARD], pattern[:GUARD]) and torch.equal(buf[-GUARD:], pattern[-GUARD:])

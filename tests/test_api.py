@@ -221,6 +221,14 @@ CASES = [
     ("non-contiguous query", lambda: _mut(_bnsd, query=_tr(torch.zeros(2, 4, 300, 128, dtype=torch.bfloat16))), INVALID),
     ("non-contiguous key", lambda: _mut(_bnsd, key=torch.zeros(2, 270, 2, 128, dtype=torch.bfloat16).transpose(1, 2)), INVALID),
     ("dq inner stride", lambda: _mut(_bnsd, dq=_tr(torch.zeros(2, 4, 300, 128, dtype=torch.bfloat16))), INVALID),
+    ("dq zero head stride", lambda: _mut(_bnsd, dq=torch.zeros(2, 1, 300, 128, dtype=torch.bfloat16).expand(2, 4, 300, 128)),
+     INVALID),
+    ("dk overlapping rows", lambda: _mut(_bnsd, dk=torch.zeros(2 * 2 * 270 * 64 + 64, dtype=torch.bfloat16).as_strided(
+        (2, 2, 270, 128), (2 * 270 * 64, 270 * 64, 64, 1))), INVALID),
+    ("dv with padded rows", lambda: _mut(_bnsd, dv=torch.zeros(2, 2, 270, 200, dtype=torch.bfloat16)[..., :128]),
+     bsa.BSA_OK),
+    ("dq heads interleaved (transposed outer dims)", lambda: _mut(
+        _bnsd, dq=torch.zeros(2, 300, 4, 128, dtype=torch.bfloat16).transpose(1, 2)), bsa.BSA_OK),
     # sequence lengths
     ("BNSD length > S", lambda: _mut(_bnsd, actual_seq_lengths=[301, 3]), INVALID),
     ("BNSD length count", lambda: _mut(_bnsd, actual_seq_lengths=[300]), INVALID),
@@ -358,6 +366,14 @@ FWD_CASES = [
     ("O dtype", lambda: _fwd(attention_out=torch.zeros(2, 4, 300, 128, dtype=torch.float16)), INVALID),
     ("O shape", lambda: _fwd(attention_out=torch.zeros(2, 4, 299, 128, dtype=torch.bfloat16)), INVALID),
     ("O inner stride", lambda: _fwd(attention_out=_tr(torch.zeros(2, 4, 300, 128, dtype=torch.bfloat16))), INVALID),
+    ("O row stride not a multiple of 4", lambda: _fwd(
+        attention_out=torch.zeros(2, 4, 300, 130, dtype=torch.bfloat16)[..., :128]), INVALID),
+    ("O row stride a multiple of 4", lambda: _fwd(
+        attention_out=torch.zeros(2, 4, 300, 132, dtype=torch.bfloat16)[..., :128]), bsa.BSA_OK),
+    ("O data pointer not 8-byte aligned", lambda: _fwd(
+        attention_out=torch.zeros(2 * 4 * 300 * 128 + 1, dtype=torch.bfloat16)[1:].view(2, 4, 300, 128)), INVALID),
+    ("O overlapping heads", lambda: _fwd(attention_out=torch.zeros(2, 1, 300, 128, dtype=torch.bfloat16).expand(
+        2, 4, 300, 128)), INVALID),
     ("LSE fp16", lambda: _fwd(softmax_lse=torch.zeros(2, 4, 300, dtype=torch.float16)), INVALID),
     ("LSE non-contiguous", lambda: _fwd(softmax_lse=torch.zeros(2, 300, 4).transpose(1, 2)), INVALID),
     ("LSE shape", lambda: _fwd(softmax_lse=torch.zeros(2, 4, 299)), INVALID),
@@ -384,3 +400,19 @@ def test_forward_binding_refuses_cpu_tensors():
     a = _fwd()
     with pytest.raises(ValueError):
         bsa.bsa_fwd(**a, workspace=None)
+
+
+def test_plan_dump_with_bsa_log():
+    """BSA_LOG=1 makes a validated call print its plan to stderr (read per call)."""
+    import subprocess
+    import sys
+    code = ("import sys; sys.path[:0] = [%r, %r]; import test_api as t, block_sparse_attention_bwd_amd as bsa; "
+            "bsa.bsa_bwd_workspace_size(**t._tnd())" % (ROOT, os.path.join(ROOT, "tests")))
+    env = dict(os.environ, BSA_LOG="1")
+    r = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, r.stderr
+    assert "[bsa] bsa_bwd_workspace_size: TND B=3 N=4 Nkv=1 G=4 D=64" in r.stderr
+    assert "ws row_list" in r.stderr and "workspace total" in r.stderr
+    r = subprocess.run([sys.executable, "-c", code], env=dict(os.environ, BSA_LOG="0"), capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 0 and "[bsa]" not in r.stderr

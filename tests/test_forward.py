@@ -76,7 +76,7 @@ def test_forward_small_case_parity(name):
     _check(name, c, o, lse)
 
 
-@pytest.mark.parametrize("k", [2, 3, 4])
+@pytest.mark.parametrize("k", [2, 3, 4, 5])
 def test_forward_full_config_parity(k):
     """The whole output of the full workloads (the oracle forward takes seconds)."""
     print(f"[forward] config {k}", flush=True)
@@ -113,6 +113,28 @@ def test_forward_noncontiguous_output():
     o2, l2 = _run_fwd(c, out=lambda q: torch.zeros(q.shape[0], q.shape[2], q.shape[1], q.shape[3],
                                                     dtype=q.dtype, device=q.device).transpose(1, 2))
     assert torch.equal(o_ref, o2) and torch.equal(l_ref, l2)
+
+
+@pytest.mark.parametrize("name", ["bnsd_fp16_d64_b64x128_padded", "tnd_fp16_d128_b64x128_gqa",
+                                  "bnsd_bf16_d256_window_attenmask"])
+def test_forward_guard_bytes(name):
+    """Nothing is written outside attention_out, softmax_lse and the workspace."""
+    import block_sparse_attention_bwd_amd as bsa
+    from bench import FwdRunner, to_device
+    from gpu_common import _guarded, _guards_intact
+    c = _case(name)
+    r = FwdRunner(c, to_device(c))
+    o_want, l_want = (t.clone() for t in r())
+    torch.cuda.synchronize()
+    go, gl = _guarded(r.o.shape, r.o.dtype), _guarded(r.lse.shape, r.lse.dtype)
+    ws = _guarded((r.ws_size,), torch.uint8)
+    kw = dict(r.kw, attention_out=go[0], softmax_lse=gl[0])
+    bsa.bsa_fwd(*r.args, **kw, workspace=ws[0], workspace_size=r.ws_size)
+    torch.cuda.synchronize()
+    for (t, buf, pat), w in ((go, o_want), (gl, l_want)):
+        assert _guards_intact(buf, pat)
+        assert torch.equal(t, w)
+    assert _guards_intact(ws[1], ws[2])
 
 
 def test_forward_bitwise_deterministic():
