@@ -25,6 +25,7 @@ from ._binding import (  # noqa: F401
     bsa_bwd,
     bsa_bwd_fp8,
     bsa_bwd_fp8_workspace_size,
+    bsa_bwd_noalloc,
     bsa_bwd_workspace_layout,
     bsa_bwd_workspace_size,
     bsa_fwd,

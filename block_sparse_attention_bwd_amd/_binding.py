@@ -87,6 +87,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.bsa_bwd.restype = ctypes.c_int
     lib.bsa_bwd_workspace_layout.argtypes = _COMMON + [ctypes.POINTER(ctypes.c_uint64), _PI64]
     lib.bsa_bwd_workspace_layout.restype = ctypes.c_int
+    lib.bsa_bwd_noalloc.argtypes = _COMMON + [ctypes.c_void_p]
+    lib.bsa_bwd_noalloc.restype = ctypes.c_int
     lib.bsa_fwd_workspace_size.argtypes = _FWD + [ctypes.POINTER(ctypes.c_uint64)]
     lib.bsa_fwd_workspace_size.restype = ctypes.c_int
     lib.bsa_fwd.argtypes = _FWD + [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p]
@@ -255,6 +257,22 @@ def bsa_bwd(dout, query, key, value, attention_out, softmax_lse, block_sparse_ma
     _check(lib.bsa_bwd(*args, ws_ptr, int(workspace_size), ctypes.c_void_p(handle)))
 
 
+def bsa_bwd_noalloc(dout, query, key, value, attention_out, softmax_lse, block_sparse_mask=None, atten_mask=None,
+                    block_shape=None, actual_seq_lengths=None, actual_seq_lengths_kv=None, q_input_layout="BNSD",
+                    kv_input_layout="BNSD", num_key_value_heads=1, mask_type=0, scale_value=1.0,
+                    pre_tokens=NO_WINDOW, next_tokens=NO_WINDOW, dq=None, dk=None, dv=None, stream=None) -> None:
+    """The backward on the library's own scratch array (no workspace argument, no
+    allocation): enqueued on ``stream`` (default: torch's current stream)."""
+    lib = load_library()
+    _need_gpu(dout=dout, query=query, key=key, value=value, attention_out=attention_out,
+              softmax_lse=softmax_lse, block_sparse_mask=block_sparse_mask, dq=dq, dk=dk, dv=dv)
+    args = _marshal(dout, query, key, value, attention_out, softmax_lse, block_sparse_mask, atten_mask,
+                    block_shape, actual_seq_lengths, actual_seq_lengths_kv, q_input_layout,
+                    kv_input_layout, num_key_value_heads, mask_type, scale_value, pre_tokens,
+                    next_tokens, dq, dk, dv)
+    _check(lib.bsa_bwd_noalloc(*args, _launch_args(None, 0, stream)[2]))
+
+
 def bsa_fwd_workspace_size(query, key, value, block_sparse_mask=None, atten_mask=None, block_shape=None,
                            actual_seq_lengths=None, actual_seq_lengths_kv=None, q_input_layout="BNSD",
                            kv_input_layout="BNSD", num_key_value_heads=1, mask_type=0, scale_value=1.0,
@@ -317,7 +335,7 @@ def _launch_args(workspace, workspace_size, stream):
 
 def _need_gpu(**tensors):
     for name, t in tensors.items():
-        if t is not None and not t.is_cuda:
+        if t is not None and not isinstance(t, bsa_tensor) and not t.is_cuda:
             raise ValueError(f"{name} must be a GPU tensor")
 
 

@@ -16,6 +16,8 @@
 #include "bsa_bwd.h"
 #include "bsa_internal.h"
 
+static_assert(bsa::kScratchBytes == BSA_NOALLOC_SCRATCH_BYTES, "scratch size in the header and the library");
+
 namespace {
 
 thread_local std::string g_err;
@@ -65,6 +67,9 @@ struct Args {
   bool fwd;  // forward: dout/dq/dk/dv absent; attention_out and softmax_lse are outputs
   bool fp8;                // fp8 entry points: fp8 data inputs, bf16 outputs
   const double* descale;   // fp8: {dout, query, key, value, attention_out} or {query, key, value}; NULL = 1
+  // partial-result slots for split dK/dV units: at most this many (fewer
+  // only load-balance heavy units less well; results are the same)
+  int64_t max_slots = bsa::kMaxSlots;
 };
 
 enum Fp8Role { kRoleDout = 0, kRoleQuery, kRoleKey, kRoleValue, kRoleOut };
@@ -537,7 +542,8 @@ int make_plan(const Args& a, Plan* plan) {
   take(BSA_WS_COL_LIST, bwd * 4ull * B * N * nkb * nqb);
   const int64_t n_units = B * Nkv * nkb * nsub_kv;
   const int64_t max_pieces = n_units * (N / Nkv) * nqb;  // a piece holds at least one Q block
-  const int64_t slots = max_pieces < bsa::kMaxSlots ? max_pieces : bsa::kMaxSlots;
+  const int64_t slots_lim = std::max<int64_t>(0, std::min<int64_t>(a.max_slots, bsa::kMaxSlots));
+  const int64_t slots = max_pieces < slots_lim ? max_pieces : slots_lim;
   take(BSA_WS_PLAN, bwd * 4ull * bsa::plan_words(n_units, slots));
   take(BSA_WS_PARTIAL, bwd * 4ull * slots * 2 * bsa::kTileRowsMax * D);
   // attenMask as bits: by query row (all) and by key (the backward's dK/dV kernel)
@@ -665,22 +671,9 @@ int check_device_pointer(const void* ptr, int device, const char* name) {
   return BSA_OK;
 }
 
-// Validate, carve the workspace and enqueue the kernels of one call.
-int run(const Args& a, void* workspace, uint64_t workspace_size, void* stream) {
-  Plan plan;
-  int rc = make_plan(a, &plan);
-  if (rc) return rc;
-  if (plan_log_on()) log_plan(a.fwd ? "bsa_fwd" : "bsa_bwd", a, plan);
-  const uint64_t need = plan.off[BSA_WS_TOTAL];
-  if (workspace_size < need)
-    return fail(BSA_ERR_PARAM_INVALID, "workspace of %llu bytes is smaller than the %llu needed",
-                static_cast<unsigned long long>(workspace_size), static_cast<unsigned long long>(need));
-  if (need > 0 && workspace == nullptr) return fail(BSA_ERR_PARAM_NULLPTR, "workspace is a null pointer");
-  if (reinterpret_cast<uintptr_t>(workspace) % kAlign != 0)
-    return fail(BSA_ERR_PARAM_INVALID, "workspace must be %llu-byte aligned", static_cast<unsigned long long>(kAlign));
-
-  int device = -1;
-  if (hipGetDevice(&device) != hipSuccess) {
+// The data tensors of a call live in device memory of the current device.
+int check_tensors_on_device(const Args& a, int* device) {
+  if (hipGetDevice(device) != hipSuccess) {
     (void)hipGetLastError();
     return fail(BSA_ERR_RUNTIME, "hipGetDevice failed (no usable GPU?)");
   }
@@ -695,13 +688,72 @@ int run(const Args& a, void* workspace, uint64_t workspace_size, void* stream) {
                       {a.dq, "dq"}, {a.dk, "dk"}, {a.dv, "dv"}};
   for (const Ptr& q : ptrs) {
     if (q.t == nullptr || q.t->data == nullptr) continue;
-    rc = check_device_pointer(q.t->data, device, q.name);
+    int rc = check_device_pointer(q.t->data, *device, q.name);
     if (rc) return rc;
   }
-  if (workspace != nullptr && (rc = check_device_pointer(workspace, device, "workspace"))) return rc;
+  return BSA_OK;
+}
 
+int enqueue(const Args& a, Plan& plan, char* ws, void* stream, bool allow_profile);
+
+// Validate, carve the caller's workspace and enqueue the kernels of one call.
+int run(const Args& a, void* workspace, uint64_t workspace_size, void* stream) {
+  Plan plan;
+  int rc = make_plan(a, &plan);
+  if (rc) return rc;
+  if (plan_log_on()) log_plan(a.fwd ? "bsa_fwd" : "bsa_bwd", a, plan);
+  const uint64_t need = plan.off[BSA_WS_TOTAL];
+  if (workspace_size < need)
+    return fail(BSA_ERR_PARAM_INVALID, "workspace of %llu bytes is smaller than the %llu needed",
+                static_cast<unsigned long long>(workspace_size), static_cast<unsigned long long>(need));
+  if (need > 0 && workspace == nullptr) return fail(BSA_ERR_PARAM_NULLPTR, "workspace is a null pointer");
+  if (reinterpret_cast<uintptr_t>(workspace) % kAlign != 0)
+    return fail(BSA_ERR_PARAM_INVALID, "workspace must be %llu-byte aligned", static_cast<unsigned long long>(kAlign));
+  int device = -1;
+  if ((rc = check_tensors_on_device(a, &device))) return rc;
+  if (workspace != nullptr && (rc = check_device_pointer(workspace, device, "workspace"))) return rc;
+  return enqueue(a, plan, static_cast<char*>(workspace), stream, true);
+}
+
+// The backward with the library's own scratch array as its workspace (see
+// bsa_bwd_noalloc): the plan takes as many partial-result slots as fit.
+int run_noalloc(const Args& a, void* stream) {
+  void* base = nullptr;
+  uint64_t cap = 0;
+  const int herr = bsa::scratch_region(&base, &cap);
+  if (herr) return fail(BSA_ERR_RUNTIME, "scratch lookup failed: %s", hipGetErrorString(static_cast<hipError_t>(herr)));
+  Plan plan;
+  Args b = a;
+  int rc = make_plan(b, &plan);
+  if (rc) return rc;
+  if (plan.off[BSA_WS_TOTAL] > cap && plan.p.slots_cap > 0) {
+    // the slots are the one region that may shrink: what is left after the
+    // other regions, one slot at a time (each also takes 8 plan bytes)
+    b.max_slots = 0;
+    if ((rc = make_plan(b, &plan))) return rc;
+    const uint64_t per_slot = 2ull * bsa::kTileRowsMax * static_cast<uint64_t>(plan.p.D) * 4 + 8;
+    b.max_slots = plan.off[BSA_WS_TOTAL] < cap ? static_cast<int64_t>((cap - plan.off[BSA_WS_TOTAL]) / per_slot) : 0;
+    for (;;) {
+      if ((rc = make_plan(b, &plan))) return rc;
+      if (plan.off[BSA_WS_TOTAL] <= cap || b.max_slots == 0) break;
+      b.max_slots = b.max_slots > 8 ? b.max_slots - 8 : 0;  // alignment padding of the regions
+    }
+  }
+  if (plan_log_on()) log_plan("bsa_bwd_noalloc", b, plan);
+  if (plan.off[BSA_WS_TOTAL] > cap)
+    return fail(BSA_ERR_PARAM_INVALID,
+                "this problem needs %llu bytes of workspace; the library's scratch array holds %llu "
+                "(use bsa_bwd with a caller workspace)",
+                static_cast<unsigned long long>(plan.off[BSA_WS_TOTAL]), static_cast<unsigned long long>(cap));
+  int device = -1;
+  if ((rc = check_tensors_on_device(b, &device))) return rc;
+  return enqueue(b, plan, static_cast<char*>(base), stream, false);
+}
+
+// Carve the workspace at `ws` by the plan and enqueue the stages.
+int enqueue(const Args& a, Plan& plan, char* ws, void* stream, bool allow_profile) {
+  int rc = BSA_OK;
   bsa::Params& p = plan.p;
-  char* ws = static_cast<char*>(workspace);
   p.seq = reinterpret_cast<bsa::SeqInfo*>(ws + plan.off[BSA_WS_SEQ]);
   float* consts = reinterpret_cast<float*>(ws + plan.off[BSA_WS_SEQ] + sizeof(bsa::SeqInfo) * plan.seq.size());
   p.consts = consts;
@@ -722,7 +774,7 @@ int run(const Args& a, void* workspace, uint64_t workspace_size, void* stream) {
 
   // Profiling: one event before the first stage and one after each stage run.
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const bool prof = g_prof.on && g_prof.max_calls > 0;
+  const bool prof = allow_profile && g_prof.on && g_prof.max_calls > 0;
   if (prof) --g_prof.max_calls;
   auto mark = [&](int tag) { return prof ? record_stage(s, tag) : static_cast<int>(BSA_OK); };
   auto launch_failed = [&](int herr, const char* what) {
@@ -837,6 +889,11 @@ int bsa_bwd_workspace_layout(BSA_ARGS_DECL, uint64_t* offsets, int64_t* dims) {
 int bsa_bwd(BSA_ARGS_DECL, void* workspace, uint64_t workspace_size, void* stream) {
   g_err.clear();
   return run(BSA_ARGS_PACK, workspace, workspace_size, stream);
+}
+
+int bsa_bwd_noalloc(BSA_ARGS_DECL, void* stream) {
+  g_err.clear();
+  return run_noalloc(BSA_ARGS_PACK, stream);
 }
 
 int bsa_fwd_workspace_size(BSA_FWD_ARGS_DECL, uint64_t* workspace_size) {

@@ -166,4 +166,10 @@ int launch_fwd(const Params& p, void* stream);
 int launch_dkdv(const Params& p, void* stream);
 int launch_dq(const Params& p, void* stream);  // also sums the pieces of split dK/dV units
 
+// The library's own device scratch array, used as the workspace of the entry
+// point that allocates nothing: its address on the current device (looked up
+// once per device) and its size in bytes.  Returns a hipError_t value.
+constexpr uint64_t kScratchBytes = uint64_t(64) << 20;  // BSA_NOALLOC_SCRATCH_BYTES
+int scratch_region(void** ptr, uint64_t* bytes);
+
 }  // namespace bsa

@@ -40,6 +40,8 @@
 // that order.
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+
 #include "bsa_internal.h"
 
 namespace bsa {
@@ -1509,6 +1511,37 @@ inline int waves_for(int rows) {
 }
 
 }  // namespace
+
+// ---------------------------------------------------------------------------
+// scratch array of the entry point that allocates nothing
+// ---------------------------------------------------------------------------
+// Every device the library runs on holds its own copy of this array from the
+// module's load to the end of the process.  Host code must not pass the name
+// itself to a kernel (on the host it is only a stand-in for the symbol): the
+// device address comes from hipGetSymbolAddress, looked up once per device with
+// that device current.
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+int scratch_region(void** ptr, uint64_t* bytes) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return static_cast<int>(e);
+  if (dev < 0 || dev >= kMaxDevices) return static_cast<int>(hipErrorInvalidDevice);
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* a = nullptr;
+    e = hipGetSymbolAddress(&a, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return static_cast<int>(e);
+    if (a == nullptr) return static_cast<int>(hipErrorInvalidSymbol);
+    addr[dev] = a;
+  }
+  *ptr = addr[dev];
+  *bytes = kScratchBytes;
+  return 0;
+}
 
 int launch_stage_fp8(const Fp8Stage& st, void* stream) {
   int64_t groups = 0;

@@ -163,6 +163,37 @@ int bsa_bwd(const bsa_tensor* dout, const bsa_tensor* query, const bsa_tensor* k
             void* stream);
 
 /*
+ * The backward without a caller workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation).  Same arguments and results as bsa_bwd without
+ * workspace / workspace_size; the stages run on the library's own static
+ * device scratch array of 64 MiB (BSA_NOALLOC_SCRATCH_BYTES), one copy per GPU,
+ * held from the library's first use on that GPU until the process ends.  The
+ * call allocates nothing (no hipMalloc or hipFree, no allocating library call).
+ *
+ * Limit: a problem whose workspace does not fit the scratch array is rejected
+ * with 161002 (bsa_last_error() gives both sizes) and nothing is enqueued; the
+ * partial-result slots of split dK/dV work are first reduced to what fits,
+ * which changes the load balance, not the results.  The sequence table, lists,
+ * softmax_grad, plan and partials are all rewritten by every call before they
+ * are read, so no scratch contents carry over from one call to the next.
+ * Every call on one GPU shares that GPU's array: calls that overlap in time on
+ * one GPU (different streams, or different host threads) race and give wrong
+ * results; serialise them.  Profiling (bsa_profile_start) does not record these
+ * calls.  fp16 / bf16 inputs only (no fp8 variant).
+ */
+#define BSA_NOALLOC_SCRATCH_BYTES (64ull << 20)
+int bsa_bwd_noalloc(const bsa_tensor* dout, const bsa_tensor* query, const bsa_tensor* key,
+                    const bsa_tensor* value, const bsa_tensor* attention_out, const bsa_tensor* softmax_lse,
+                    const bsa_tensor* block_sparse_mask, const bsa_tensor* atten_mask,
+                    const int64_t* block_shape, int64_t block_shape_len, const int64_t* actual_seq_lengths,
+                    int64_t actual_seq_lengths_len, const int64_t* actual_seq_lengths_kv,
+                    int64_t actual_seq_lengths_kv_len, const char* q_input_layout,
+                    const char* kv_input_layout, int64_t num_key_value_heads, int64_t mask_type,
+                    double scale_value, int64_t pre_tokens, int64_t next_tokens, const bsa_tensor* dq,
+                    const bsa_tensor* dk, const bsa_tensor* dv, void* stream);
+
+/*
  * Forward (the operation the backward differentiates; aclnnBlockSparseAttentionGrad
  * page, 计算公式: S = Mask(scale * Q * K^T), P = Softmax(S), Out = P * V, with the
  * softmax taken over the selected blocks only, as the FlashAttentionScore page's
