@@ -354,20 +354,33 @@ def synth_blocks(case):
 PEAK_CLOCK_MHZ = 2400.0  # the clock the published MFMA peak is quoted at
 
 
+def _driver_gfxclk(torch):
+    """The driver's current shader clock (MHz): the median over the XCDs of its
+    per-XCD readings where it gives them, else its single reading; None if none."""
+    try:
+        import amdsmi
+        h = torch.cuda._get_amdsmi_handler(torch.cuda.current_device())
+        m = amdsmi.amdsmi_get_gpu_metrics_info(h)
+        vals = [float(x) for x in (m.get("current_gfxclks") or []) if isinstance(x, (int, float)) and 0 < x < 10000]
+        if not vals and isinstance(m.get("current_gfxclk"), (int, float)) and 0 < m["current_gfxclk"] < 10000:
+            vals = [float(m["current_gfxclk"])]
+        return float(np.median(vals)) if vals else None
+    except Exception:  # no reading on this machine
+        return None
+
+
 def sustained_clock_mhz(run, torch, seconds=1.0, chunk=20):
-    """Median shader clock (MHz) sampled from the driver while the calls run back to
-    back for about ``seconds``; None where the driver gives no reading."""
+    """Median shader clock (MHz) the driver reports while the calls run back to
+    back for about ``seconds``; None where it gives no reading."""
     import threading
     samples, done = [], threading.Event()
 
     def poll():
         while not done.is_set():
-            try:
-                mhz = float(torch.cuda.clock_rate())
-            except Exception:  # no reading on this machine
+            mhz = _driver_gfxclk(torch)
+            if mhz is None:
                 return
-            if mhz > 0:
-                samples.append(mhz)
+            samples.append(mhz)
             done.wait(0.005)
 
     for _ in range(chunk):  # the GPU is busy before the first sample
@@ -384,13 +397,30 @@ def sustained_clock_mhz(run, torch, seconds=1.0, chunk=20):
     return float(np.median(samples)) if samples else None
 
 
-def clock_report(clock_mhz, tflops):
-    """The value as a fraction of the MFMA peak scaled to the sustained clock."""
-    if clock_mhz is None:
-        return {"sustained_mhz": None, "frac_of_peak_at_sustained_clock": None}
-    peak = MFMA_PEAK_BF16_TFLOPS * clock_mhz / PEAK_CLOCK_MHZ
-    return {"sustained_mhz": round(clock_mhz, 1), "peak_at_sustained_clock": round(peak, 1),
-            "frac_of_peak_at_sustained_clock": round(tflops / peak, 4)}
+def counter_clock_mhz(workload, kernel):
+    """Shader clock (MHz) over the dominant kernel from a committed rocprofv3 counter
+    summary: GRBM_GUI_ACTIVE (busy cycles, summed over the 8 XCDs) / 8 / the
+    kernel's duration in the same run; None if absent or taken on other source."""
+    vals = _profile_values(workload, kernel)
+    if not vals or "GRBM_GUI_ACTIVE" not in vals or "kernel_duration_ns" not in vals:
+        return None
+    return float(vals["GRBM_GUI_ACTIVE"]) / 8.0 / float(vals["kernel_duration_ns"]) * 1e3
+
+
+def clock_report(driver_mhz, counter_mhz, tflops):
+    """The value as a fraction of the MFMA peak scaled to the sustained clock (the
+    counter-derived clock where a current profile gives it, else the driver's)."""
+    mhz = counter_mhz if counter_mhz is not None else driver_mhz
+    out = {"driver_mhz": None if driver_mhz is None else round(driver_mhz, 1),
+           "counter_mhz": None if counter_mhz is None else round(counter_mhz, 1),
+           "sustained_mhz": None if mhz is None else round(mhz, 1),
+           "source": "counters" if counter_mhz is not None else ("driver" if driver_mhz is not None else None)}
+    if mhz is None:
+        out["frac_of_peak_at_sustained_clock"] = None
+        return out
+    peak = MFMA_PEAK_BF16_TFLOPS * mhz / PEAK_CLOCK_MHZ
+    out.update(peak_at_sustained_clock=round(peak, 1), frac_of_peak_at_sustained_clock=round(tflops / peak, 4))
+    return out
 
 
 def kernel_source_hash():
@@ -400,14 +430,9 @@ def kernel_source_hash():
         return hashlib.sha256(f.read()).hexdigest()
 
 
-def traffic_from_profile(workload, kernel, launches_per_step=1):
-    """HBM bytes per launch of `kernel` from a committed rocprofv3 counter summary.
-
-    The summary records FETCH_SIZE and WRITE_SIZE (KiB per dispatch), the scale
-    factors measured on a plain copy kernel, and the sha256 of the kernel source
-    it was taken on; if the source has changed since, the figure is stale and
-    None is returned.
-    """
+def _profile_values(workload, kernel):
+    """The `key: value` lines of a committed counter summary, or None if it is
+    missing or was taken on another version of the kernel source."""
     path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_hbm_counters.txt")
     if not os.path.exists(path):
         return None
@@ -418,6 +443,20 @@ def traffic_from_profile(workload, kernel, launches_per_step=1):
                 k, v = line.split(":", 1)
                 vals[k.strip()] = v.strip()
     if vals.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    return vals
+
+
+def traffic_from_profile(workload, kernel, launches_per_step=1):
+    """HBM bytes per launch of `kernel` from a committed rocprofv3 counter summary.
+
+    The summary records FETCH_SIZE and WRITE_SIZE (KiB per dispatch), the scale
+    factors measured on a plain copy kernel, and the sha256 of the kernel source
+    it was taken on; if the source has changed since, the figure is stale and
+    None is returned.
+    """
+    vals = _profile_values(workload, kernel)
+    if not vals:
         return None
     fetch = float(vals["FETCH_SIZE_KiB_per_dispatch"]) * float(vals["fetch_scale"])
     write = float(vals["WRITE_SIZE_KiB_per_dispatch"]) * float(vals["write_scale"])
@@ -584,7 +623,7 @@ def main(argv=None):
         "cpu_baseline": cpu,
         "call_ms": {"median": round(p50, 5), "p10": round(p10, 5), "p90": round(p90, 5), "calls": args.steps,
                     "tflops_at_median": round(flops / (p50 * 1e-3) / 1e12, 3)},
-        "clock": clock_report(clock_mhz, tflops),
+        "clock": clock_report(clock_mhz, counter_clock_mhz(case.name, kname), tflops),
     }
     print(json.dumps(out), flush=True)
     return 0
