@@ -72,7 +72,7 @@ struct Params {
   // workspace regions
   SeqInfo* seq;
   const float* consts;  // kConstFloats floats after the sequence table: zeros, then +inf, -inf
-  float* delta;
+  float* delta;         // -softmax_grad (negated: it seeds the dP accumulator of the dK/dV kernel)
   float* lse2;
   int32_t* row_cnt;
   int32_t* row_list;

@@ -8,7 +8,8 @@
 //   prologue    one launch, three block ranges:
 //                 - per-Q-block lists of selected in-range KV blocks
 //                 - per-KV-block lists of selected in-range Q blocks
-//                 - softmax_grad: delta = rowsum(dOut o Out) in fp32, and
+//                 - softmax_grad: delta = rowsum(dOut o Out) in fp32, stored
+//                   negated (it seeds dP's accumulator: dP - delta), and
 //                   lse2 = softmaxLse * log2(e), both [B, N, maxSq]
 //   plan        one workgroup: splits KV blocks that many Q blocks select
 //               into pieces and orders the dK/dV work longest first; picks
@@ -90,6 +91,23 @@ __device__ __forceinline__ u16x8 pack8(const float* x) {
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Four consecutive outputs rounded to the element type, as one 8-byte store
+// when the address allows it (outputs may have any outer strides; the row
+// start is 2-byte aligned only in general), else as four 2-byte stores.
+template <class E>
+__device__ __forceinline__ void store4(unsigned short* dst, const float (&x)[4]) {
+  unsigned short r[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) r[t] = E::from_f32(x[t]);
+  if ((reinterpret_cast<uintptr_t>(dst) & 7u) == 0) {
+    typedef unsigned short u16x4_t __attribute__((ext_vector_type(4)));
+    *reinterpret_cast<u16x4_t*>(dst) = u16x4_t{r[0], r[1], r[2], r[3]};
+  } else {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) dst[t] = r[t];
+  }
+}
 
 // The sliding window (preTokens / nextTokens): key position j takes part for
 // query position i only if i - pre <= j <= i + next.  Positions are below
@@ -266,7 +284,7 @@ __device__ void delta_part(const Params& p, int blk) {
 #pragma unroll
     for (int m = LPR / 2; m >= 1; m >>= 1) acc[k] += __shfl_xor(acc[k], m);
     if (sub == 0 && out[k] >= 0) {
-      p.delta[out[k]] = acc[k] * p.delta_scale;
+      p.delta[out[k]] = -(acc[k] * p.delta_scale);  // stored negated
       p.lse2[out[k]] = l2[k];
     }
   }
@@ -659,8 +677,16 @@ __device__ __forceinline__ unsigned lds_addr(const void* p) {
   return static_cast<unsigned>(reinterpret_cast<uintptr_t>((lds_void*)(p)));
 }
 __device__ __forceinline__ void dma16s(const void* base, unsigned voff, unsigned lds) {
-  const unsigned m = __builtin_amdgcn_readfirstlane(lds);  // wave-uniform by construction
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(voff), "s"(base), "s"(m)
+  // base and lds are wave-uniform by construction; readfirstlane states it to
+  // the compiler, which may not prove it and then could not place base in SGPRs
+  const unsigned m = __builtin_amdgcn_readfirstlane(lds);
+  // (readfirstlane yields an int: each half is widened through unsigned, so
+  // that the low half is zero-extended)
+  const uint64_t bp = reinterpret_cast<uintptr_t>(base);
+  const unsigned lo = static_cast<unsigned>(__builtin_amdgcn_readfirstlane(static_cast<unsigned>(bp)));
+  const unsigned hi = static_cast<unsigned>(__builtin_amdgcn_readfirstlane(static_cast<unsigned>(bp >> 32)));
+  const uint64_t sb = (static_cast<uint64_t>(hi) << 32) | lo;
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(voff), "s"(sb), "s"(m)
                : "memory", "m0");
 }
 __device__ __forceinline__ void dma4(const void* src, unsigned lds) {  // lane L's 4 bytes -> m0 + 4 L
@@ -817,6 +843,102 @@ __host__ __device__ constexpr int dkdv_tile_rows() {
 // as the tile need not start on a word boundary).
 template <int D, int W>
 __host__ __device__ constexpr int dkdv_mask_words() { return dkdv_tile_rows<D, W>() / 32 + 1; }
+
+// Epilogue of a dK/dV work item: the fp32 partial of a piece of a split unit,
+// or the scaled, rounded rows of a whole unit (every row up to w_end, zeros
+// where nothing contributed; rows from kv_end on are stored as zeros whatever
+// their accumulators hold).
+template <class E, int D, int W, int MODE>
+__device__ __forceinline__ void dkdv_store(const Params& p, int u, int piece, int pieces, int kv0, int kv_end, int w_end, int b,
+                                           int h, const SeqInfo& si, const f32x16 (&adv)[MODE != kDkdvOnlyK ? D / 32 : 1],
+                                           const f32x16 (&adk)[MODE != kDkdvOnlyV ? D / 32 : 1]) {
+  constexpr int NT = D / 32;
+  constexpr bool kDoV = MODE != kDkdvOnlyK, kDoK = MODE != kDkdvOnlyV;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, w = tid >> 6, l32 = lane & 31, g = lane >> 5;
+  const PlanView pv(p);
+  const int32_t* unit_base = pv.unit_base;
+  if (pieces > 1) {  // fp32 partial of this piece; the reduction applies the output factors
+    float* dst = p.partial + static_cast<int64_t>(unit_base[u] + piece) * 2 * kTileRowsMax * D;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int rl = 32 * w + 8 * (i >> 2) + 4 * g + (i & 3);
+        if (kv0 + rl < w_end) {
+          const bool live = kv0 + rl < kv_end;
+          if constexpr (kDoK) dst[rl * D + 32 * nt + l32] = live ? adk[nt][i] : 0.f;
+          if constexpr (kDoV) dst[(kTileRowsMax + rl) * D + 32 * nt + l32] = live ? adv[nt][i] : 0.f;
+        }
+      }
+    }
+    return;
+  }
+  unsigned short* dkp = static_cast<unsigned short*>(p.dk) + b * p.dk_sb + si.off_kv * p.dk_sr + h * p.dk_sh;
+  unsigned short* dvp = static_cast<unsigned short*>(p.dv) + b * p.dv_sb + si.off_kv * p.dv_sr + h * p.dv_sh;
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int r = kv0 + 32 * w + 8 * (i >> 2) + 4 * g + (i & 3);
+      if (r < w_end) {
+        const bool live = r < kv_end;
+        if constexpr (kDoK) dkp[r * p.dk_sr + 32 * nt + l32] = E::from_f32(live ? adk[nt][i] * p.dk_scale : 0.f);
+        if constexpr (kDoV) dvp[r * p.dv_sr + 32 * nt + l32] = E::from_f32(live ? adv[nt][i] * p.dv_scale : 0.f);
+      }
+    }
+  }
+}
+
+// The same epilogue for transposed accumulators (dV^T / dK^T tiles: lane l
+// holds key row 32 w + l % 32, register i of column tile nt holds element
+// 32 nt + 8 (i / 4) + 4 g + i % 4): four consecutive elements per store.
+template <class E, int D>
+__device__ __forceinline__ void dkdv_store_t(const Params& p, int u, int piece, int pieces, int kv0, int kv_end,
+                                             int w_end, int b, int h, const SeqInfo& si, const f32x16 (&adv)[D / 32],
+                                             const f32x16 (&adk)[D / 32]) {
+  constexpr int NT = D / 32;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, w = tid >> 6, l32 = lane & 31, g = lane >> 5;
+  const int rl = 32 * w + l32;  // this lane's key row within the part
+  if (kv0 + rl >= w_end) return;
+  const bool live = kv0 + rl < kv_end;
+  if (pieces > 1) {  // fp32 partial of this piece; the reduction applies the output factors
+    const PlanView pv(p);
+    float* dst = p.partial + static_cast<int64_t>(pv.unit_base[u] + piece) * 2 * kTileRowsMax * D;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        const int c = 32 * nt + 8 * a + 4 * g;
+        float4 vk, vv;
+        vk.x = live ? adk[nt][4 * a] : 0.f, vk.y = live ? adk[nt][4 * a + 1] : 0.f;
+        vk.z = live ? adk[nt][4 * a + 2] : 0.f, vk.w = live ? adk[nt][4 * a + 3] : 0.f;
+        vv.x = live ? adv[nt][4 * a] : 0.f, vv.y = live ? adv[nt][4 * a + 1] : 0.f;
+        vv.z = live ? adv[nt][4 * a + 2] : 0.f, vv.w = live ? adv[nt][4 * a + 3] : 0.f;
+        *reinterpret_cast<float4*>(dst + rl * D + c) = vk;
+        *reinterpret_cast<float4*>(dst + (kTileRowsMax + rl) * D + c) = vv;
+      }
+    return;
+  }
+  const int r = kv0 + rl;
+  unsigned short* dkp = static_cast<unsigned short*>(p.dk) + b * p.dk_sb + (si.off_kv + r) * p.dk_sr + h * p.dk_sh;
+  unsigned short* dvp = static_cast<unsigned short*>(p.dv) + b * p.dv_sb + (si.off_kv + r) * p.dv_sr + h * p.dv_sh;
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      const int c = 32 * nt + 8 * a + 4 * g;
+      float k4[4], v4[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        k4[t] = live ? adk[nt][4 * a + t] * p.dk_scale : 0.f;
+        v4[t] = live ? adv[nt][4 * a + t] * p.dv_scale : 0.f;
+      }
+      store4<E>(dkp + c, k4);
+      store4<E>(dvp + c, v4);
+    }
+}
 
 template <class E, int D, int W, int MODE, bool AM>
 __device__ __forceinline__ void dkdv_work(const Params& p, int item, unsigned short (*sQ)[dkdv_tile_rows<D, W>() * D],
@@ -992,7 +1114,7 @@ __device__ __forceinline__ void dkdv_work(const Params& p, int item, unsigned sh
           const float li = l4[i >> 2][i & 3], di = d4[i >> 2][i & 3];
           const float x = fast_exp2(s[i] * c2 - li);  // P = exp(scale*S - LSE)
           pv[i] = kv_ok ? x : 0.f;
-          dsv[i] = pv[i] * (dpv[i] - di);              // dS = P o (dP - softmax_grad)
+          dsv[i] = pv[i] * (dpv[i] + di);              // dS = P o (dP - softmax_grad); di = -softmax_grad
         }
       } else {
         // attenMask bits of this lane's 32 query rows (bit r: row cur.q0 + c0 + r excluded)
@@ -1014,7 +1136,7 @@ __device__ __forceinline__ void dkdv_work(const Params& p, int item, unsigned sh
           const float li = l4[i >> 2][i & 3], di = d4[i >> 2][i & 3];
           const float x = fast_exp2(s[i] * c2 - li);
           pv[i] = ((keep >> (8 * (i >> 2) + (i & 3))) & 1u) ? x : 0.f;  // a select: li may be -inf
-          dsv[i] = pv[i] * (dpv[i] - di);
+          dsv[i] = pv[i] * (dpv[i] + di);
         }
       }
       const u16x8 pa[2] = {pack8<E>(pv), pack8<E>(pv + 8)};
@@ -1040,34 +1162,353 @@ __device__ __forceinline__ void dkdv_work(const Params& p, int item, unsigned sh
     have = more;
   }
 
-  if (pieces > 1) {  // fp32 partial of this piece; the reduction applies the output factors
-    float* dst = p.partial + static_cast<int64_t>(unit_base[u] + piece) * 2 * kTileRowsMax * D;
+  dkdv_store<E, D, W, MODE>(p, u, piece, pieces, kv0, w_end, w_end, b, h, si, adv, adk);
+}
+
+// ---------------------------------------------------------------------------
+// dK / dV, scheduled build (fp16/bf16, head dim 64 or 128, no attenMask)
+// ---------------------------------------------------------------------------
+// The same work as dkdv_work in kDkdvBoth mode, laid out for one wave per
+// SIMD so that the matrix cores stay busy.  A wave keeps issuing VALU and LDS
+// instructions while its MFMAs execute, but issues in order: a VALU that waits
+// for an MFMA result also holds back every MFMA behind it.  So the slices of a
+// tile (NSL slices of 32 Q rows, unrolled) are software-pipelined: while the
+// softmax of slice i runs on the VALU, the matrix cores compute slice i + 1's
+// scores, and every VALU instruction reads results of the phase before:
+//   P    S(0) = Q_0 K^T, dP(0) = dO_0 V^T - softmax_grad             16 MFMA
+//   X(i) S(i+1), dP(i+1)                                              16 MFMA
+//        || P = exp2(S(i) c - lse2), dS = P o dP(i), rounded pairs     VALU
+//        || dO^T, Q^T fragments of slice i                             LDS
+//   Y(i) dV += P^T dO_i, dK += dS^T Q_i                                16 MFMA
+//        || Q, dO fragments of slice i + 2, LSE / softmax_grad rows    LDS
+// dP's accumulator starts at -softmax_grad (the prologue stores it negated).
+// Every LDS fragment comes from a per-lane byte address computed once per
+// work item plus an immediate offset (slice, half, tensor), so the tile does
+// no address arithmetic.  Rows past a tile's valid rows hold finite data with
+// LSE = +inf and softmax_grad = 0: their P and dS are exactly 0, so whole
+// tiles of NSL slices are computed without guards (NSL follows the block
+// height).  Keys past the sequence end hold zero K/V rows; their P and dS are
+// left unmasked, as they feed only that lane's own dK/dV rows, which the
+// epilogue stores as zeros.  With a sliding window the pairs outside it get
+// P = 0 by a bit mask (lse2 may be -inf there).
+template <int D, int W, int NSL>
+struct DkdvPipe {
+  static constexpr int KS = D / 16, NT = D / 32;
+  static constexpr int H = 32 * NSL;          // rows per tile
+  static constexpr int RW = H / W;            // rows each wave copies per tile
+  static constexpr unsigned TB = 2u * H * D;  // bytes of one tile tensor (Q or dO)
+  static constexpr unsigned BUF = 2u * TB;    // bytes of one buffer: Q tile, then dO tile
+  static_assert(D <= 128, "head dim 256 takes the two-pass build");
+  static_assert(TB + 2u * (H - 16) * D <= 65535u, "immediate LDS offsets");
+};
+// slices per tile for a block height of bx rows with W waves: up to 4 (the
+// whole 128-row part), and at most W so that 4 / W workgroups (one wave per
+// SIMD) fit the CU's LDS at head dim 128
+__host__ __device__ constexpr int dkdv_pipe_nsl(int bx, int W) {
+  const int want = bx <= 32 ? 1 : bx <= 64 ? 2 : 4;
+  return want < W ? want : W;
+}
+
+typedef __attribute__((address_space(3))) u16x8 lds_u16x8;
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
+__device__ __forceinline__ u16x8 lds_b128(unsigned addr) { return *(const lds_u16x8*)(static_cast<uintptr_t>(addr)); }
+__device__ __forceinline__ f32x4 lds_f4(unsigned addr) { return *(const lds_f32x4*)(static_cast<uintptr_t>(addr)); }
+__device__ __forceinline__ u16x4 lds_tr(unsigned addr) {
+  return __builtin_bit_cast(u16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(static_cast<uintptr_t>(addr))));
+}
+__device__ __forceinline__ u16x8 cat8(u16x4 a, u16x4 b) { return u16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]}; }
+
+// scheduling group masks (sched_group_barrier)
+constexpr int kSgMfma = 0x008, kSgValu = 0x002, kSgDsRead = 0x100;
+
+// Per-lane LDS byte addresses of a work item's fragments in buffer 0.
+template <int D, int W, int NSL>
+struct DkdvAddr {
+  using T = DkdvPipe<D, W, NSL>;
+  unsigned a[T::KS];      // along-row fragment ks of the Q tile (+TB: dO)
+  unsigned b[T::NT][2];   // down-rows fragment nt, upper/lower 8 rows, of the Q tile (+TB: dO)
+  unsigned l;             // this lane's LSE*log2e row quadruple (+4H: -softmax_grad)
+};
+
+// The fragments and row values one slice needs.
+template <int D>
+struct DkdvSliceIn {
+  u16x8 aq[D / 16], ao[D / 16];  // Q, dO along rows (MFMA A operands of S, dP)
+  f32x4 d4[4];                   // -softmax_grad of the lane's 16 rows (dP's initial accumulator)
+  f32x4 l4[4];                   // LSE*log2e of the lane's 16 rows
+};
+
+template <int D, int W, int NSL>
+__device__ __forceinline__ void dkdv_read_a(const DkdvAddr<D, W, NSL>& ad, int sl, DkdvSliceIn<D>& in) {
+  using T = DkdvPipe<D, W, NSL>;
+  const unsigned cb = 2u * 32 * sl * D;
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int rl = 32 * w + 8 * (i >> 2) + 4 * g + (i & 3);
-        if (kv0 + rl < w_end) {
-          if constexpr (kDoK) dst[rl * D + 32 * nt + l32] = adk[nt][i];
-          if constexpr (kDoV) dst[(kTileRowsMax + rl) * D + 32 * nt + l32] = adv[nt][i];
-        }
-      }
-    }
-    return;
+  for (int ks = 0; ks < T::KS; ++ks) {
+    in.aq[ks] = lds_b128(ad.a[ks] + cb);
+    in.ao[ks] = lds_b128(ad.a[ks] + T::TB + cb);
   }
-  unsigned short* dkp = static_cast<unsigned short*>(p.dk) + b * p.dk_sb + si.off_kv * p.dk_sr + h * p.dk_sh;
-  unsigned short* dvp = static_cast<unsigned short*>(p.dv) + b * p.dv_sb + si.off_kv * p.dv_sr + h * p.dv_sh;
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
+  for (int a = 0; a < 4; ++a) {
+    in.d4[a] = lds_f4(ad.l + 4u * T::H + 128u * sl + 32u * a);
+    in.l4[a] = lds_f4(ad.l + 128u * sl + 32u * a);
+  }
+}
+
+template <class E, int D>
+__device__ __forceinline__ void dkdv_sdp(const DkdvSliceIn<D>& in, const u16x8 (&kreg)[D / 16],
+                                         const u16x8 (&vreg)[D / 16], f32x16& s, f32x16& dp) {
+  s = f32x16{};
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int t = 0; t < 4; ++t) dp[4 * a + t] = in.d4[a][t];
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) {
+    s = E::mma(in.aq[ks], kreg[ks], s);    // S[q][kv] (unscaled); this lane's column is its key
+    dp = E::mma(in.ao[ks], vreg[ks], dp);  // dP[q][kv] - softmax_grad[q]
+  }
+}
+
+template <class E, int D, int W, int NSL, bool WIN>
+__device__ __forceinline__ void dkdv_pipe_tile(const DkdvAddr<D, W, NSL>& ad, const u16x8 (&kreg)[D / 16],
+                                               const u16x8 (&vreg)[D / 16], f32x16 (&adv)[D / 32],
+                                               f32x16 (&adk)[D / 32], float c2, const uint32_t (&keep)[NSL]) {
+  using T = DkdvPipe<D, W, NSL>;
+  constexpr int KS = T::KS, NT = T::NT;
+  constexpr unsigned TB = T::TB;
+  DkdvSliceIn<D> in[2];
+  f32x16 s[2], dp[2];
+  // P: slice 0's S and dP; loads slice 1's fragments
+  dkdv_read_a<D, W, NSL>(ad, 0, in[0]);
+  dkdv_sdp<E, D>(in[0], kreg, vreg, s[0], dp[0]);
+  if constexpr (NSL > 1) {
+    dkdv_read_a<D, W, NSL>(ad, 1, in[1]);
+    __builtin_amdgcn_sched_group_barrier(kSgDsRead, 2 * KS + 8, 0);  // slice 0's reads first
+#pragma unroll
+    for (int k = 0; k < 2 * KS; ++k) {
+      __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSgDsRead, (2 * KS + 8 + 2 * KS - 1) / (2 * KS), 0);
+    }
+  }
+#pragma unroll
+  for (int sl = 0; sl < NSL; ++sl) {
+    const int cur = sl & 1, nxt = cur ^ 1;
+    const unsigned cb = 2u * 32 * sl * D;
+    // ---- X(sl): slice sl + 1's S / dP on the matrix cores, slice sl's softmax on the VALU
+    const f32x4(&l4)[4] = in[cur].l4;
+    if (sl + 1 < NSL) dkdv_sdp<E, D>(in[nxt], kreg, vreg, s[nxt], dp[nxt]);
+    float pv[16], dsv[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const int r = kv0 + 32 * w + 8 * (i >> 2) + 4 * g + (i & 3);
-      if (r < w_end) {
-        if constexpr (kDoK) dkp[r * p.dk_sr + 32 * nt + l32] = E::from_f32(adk[nt][i] * p.dk_scale);
-        if constexpr (kDoV) dvp[r * p.dv_sr + 32 * nt + l32] = E::from_f32(adv[nt][i] * p.dv_scale);
+      const float x = fast_exp2(s[cur][i] * c2 - l4[i >> 2][i & 3]);  // P = exp(scale*S - LSE)
+      if constexpr (WIN)
+        pv[i] = __uint_as_float(__float_as_uint(x) & (0u - ((keep[sl] >> (8 * (i >> 2) + (i & 3))) & 1u)));
+      else pv[i] = x;
+      dsv[i] = pv[i] * dp[cur][i];  // dS = P o (dP - softmax_grad)
+    }
+    const u16x8 pa[2] = {pack8<E>(pv), pack8<E>(pv + 8)};
+    const u16x8 da[2] = {pack8<E>(dsv), pack8<E>(dsv + 8)};
+    u16x4 bo[2][NT][2], bq[2][NT][2];
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+          bo[hh][nt][h2] = lds_tr(ad.b[nt][h2] + TB + cb + 2u * 16 * hh * D);
+          bq[hh][nt][h2] = lds_tr(ad.b[nt][h2] + cb + 2u * 16 * hh * D);
+        }
+    if (sl + 1 < NSL) {
+#pragma unroll
+      for (int k = 0; k < 2 * KS; ++k) {
+        __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kSgDsRead, (8 * NT + 2 * KS - 1) / (2 * KS), 0);
+        __builtin_amdgcn_sched_group_barrier(kSgValu, (WIN ? 128 : 96) / (2 * KS), 0);
       }
     }
+    // ---- Y(sl): dV^T += dO^T P, dK^T += Q^T dS; loads slice sl + 2's fragments.
+    // The fragment read down dO's (Q's) rows is, as an A operand, dO^T with
+    // the same k order as P's (dS's) registers, which serve as the B operand:
+    // the accumulators hold dV^T / dK^T, one key row per lane, so the
+    // epilogue stores four consecutive elements at a time.
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) adv[nt] = E::mma(cat8(bo[hh][nt][0], bo[hh][nt][1]), pa[hh], adv[nt]);
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) adk[nt] = E::mma(cat8(bq[hh][nt][0], bq[hh][nt][1]), da[hh], adk[nt]);
+    if (sl + 2 < NSL) dkdv_read_a<D, W, NSL>(ad, sl + 2, in[cur]);
+#pragma unroll
+    for (int k = 0; k < 4 * NT; ++k) {
+      __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
+      if (sl + 2 < NSL) __builtin_amdgcn_sched_group_barrier(kSgDsRead, (2 * KS + 8 + 4 * NT - 1) / (4 * NT), 0);
+    }
   }
+}
+
+template <class E, int D, int W, int NSL, bool WIN>
+__global__ __launch_bounds__(64 * W) void dkdv_pipe_kernel(Params p) {
+  using T = DkdvPipe<D, W, NSL>;
+  constexpr int KS = T::KS, NT = T::NT, H = T::H, RW = T::RW;
+  constexpr unsigned TB = T::TB, BUF = T::BUF;
+  // Q / dO tiles of buffer b at byte 2 b TB (swizzled rows); per buffer the
+  // LSE*log2e rows, then the -softmax_grad rows
+  __shared__ __align__(1024) unsigned short sT[2 * 2 * H * D];
+  __shared__ __align__(16) float sLD[2 * 2 * H];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, w = tid >> 6, l32 = lane & 31, g = lane >> 5;
+
+  const PlanView pv(p);
+  const int item = blockIdx.x;
+  if (item >= p.plan[1]) return;
+  const int u = pv.order_unit[item];
+  const int piece = pv.order_piece[item];
+  const int pieces = pv.unit_k[u];
+  const int chunk = p.plan[0];
+
+  int wid = u;
+  const int nsub = (p.by + kTileRows - 1) / kTileRows;
+  const int sub = wid % nsub;
+  wid /= nsub;
+  const int jb = wid % p.nkb;
+  wid /= p.nkb;
+  const int h = wid % p.Nkv;
+  const int b = wid / p.Nkv;
+  const SeqInfo si = p.seq[b];
+  const int kv0 = jb * p.by + sub * kTileRows;
+  const int part_end = min(jb * p.by + p.by, kv0 + kTileRows);
+  const int kv_end = min(part_end, si.len_kv);
+  const int w_end = min(part_end, si.wlim_kv);
+  if (kv0 >= w_end) return;  // uniform over the workgroup
+
+  const int my_kv = kv0 + 32 * w + l32;
+  const bool kv_ok = my_kv < kv_end;
+  const int64_t kv_base = b * p.kv_sb + si.off_kv * p.kv_sr + h * p.kv_sh;
+  const unsigned short* kp = static_cast<const unsigned short*>(p.k) + kv_base;
+  const unsigned short* vp = static_cast<const unsigned short*>(p.v) + kv_base;
+
+  const float c2 = p.scale_log2e;
+  const int64_t bn0 = static_cast<int64_t>(b) * p.N;
+  const int n_end = (h + 1) * p.G;
+  const unsigned short* qbase = static_cast<const unsigned short*>(p.q) + b * p.q_sb + si.off_q * p.q_sr;
+  const unsigned short* obase = static_cast<const unsigned short*>(p.dout) + b * p.q_sb + si.off_q * p.q_sr;
+
+  // DMA of one tile into buffer `buf` (as in dkdv_work): Q rows, dO rows and
+  // their LSE*log2e / -softmax_grad values (+inf / 0 past the valid rows).
+  constexpr int RPI = 512 / D;  // rows per 1 KB wave instruction
+  constexpr int NCP = RW / RPI;
+  static_assert(NCP >= 1 && NCP * RPI == RW, "a tile splits evenly over the waves' copies");
+  const int lrow = lane / (D / 8);
+  const unsigned vz = 16u * static_cast<unsigned>(lane % (D / 8));
+  unsigned voff[NCP];
+#pragma unroll
+  for (int i = 0; i < NCP; ++i) {
+    const int r = (w * NCP + i) * RPI + lrow;
+    const int c = (lane % (D / 8)) ^ swz<D>(r);
+    voff[i] = static_cast<unsigned>(2 * (r * p.q_sr + 8 * c));
+  }
+  const unsigned t0 = lds_addr(sT), l0 = lds_addr(sLD);
+  auto issue = [&](const QTile& t, int buf) {
+    const int rows = min(H, t.qend - t.q0);
+    const int64_t first = static_cast<int64_t>(t.q0) * p.q_sr + t.n * p.q_sh;
+    const unsigned short* qa = qbase + first;
+    const unsigned short* oa = obase + first;
+    const unsigned qb = t0 + BUF * buf, ob = qb + TB;
+#pragma unroll
+    for (int i = 0; i < NCP; ++i) {
+      const int ins = w * NCP + i;
+      const unsigned v = ins * RPI + lrow < rows ? voff[i] : vz;
+      dma16s(qa, v, qb + 1024u * ins);
+      dma16s(oa, v, ob + 1024u * ins);
+    }
+#pragma unroll
+    for (int r0 = 0; r0 < RW; r0 += 64) {
+      if (lane < RW - r0) {
+        const int r = RW * w + r0 + lane;
+        const int64_t li = (bn0 + t.n) * p.sq_max + t.q0 + r;
+        const unsigned lb = l0 + 8u * H * buf + 4u * (RW * w + r0);
+        dma4(r < rows ? static_cast<const void*>(p.lse2 + li) : p.consts + kConstPosInf, lb);
+        dma4(r < rows ? static_cast<const void*>(p.delta + li) : p.consts, lb + 4u * H);
+      }
+    }
+  };
+  int left = pieces > 1 ? chunk : 0x7fffffff;
+  QTile cur{h * p.G, pieces > 1 ? piece * chunk : 0, 0, 0};
+  bool have = dkdv_seek(p, bn0, jb, n_end, si.len_q, cur);
+  if (have) issue(cur, 0);  // the first tile's copies fly while K and V load
+  u16x8 kreg[KS], vreg[KS];
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {
+    u16x8 zk = {0, 0, 0, 0, 0, 0, 0, 0};
+    u16x8 zv = zk;
+    if (kv_ok) {
+      zk = *reinterpret_cast<const u16x8*>(kp + my_kv * p.kv_sr + 16 * s + 8 * g);
+      zv = *reinterpret_cast<const u16x8*>(vp + my_kv * p.kv_sr + 16 * s + 8 * g);
+    }
+    kreg[s] = zk;
+    vreg[s] = zv;
+  }
+  f32x16 adv[NT], adk[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    adv[nt] = f32x16{};
+    adk[nt] = f32x16{};
+  }
+  wait_vmcnt<0>();
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {  // the K/V loads are complete: no waits for them in the tile loop
+    settle(kreg[s]);
+    settle(vreg[s]);
+  }
+
+  DkdvAddr<D, W, NSL> ad;
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) ad.a[ks] = t0 + 2u * tile_off<D>(l32, 16 * ks + 8 * g);
+  {
+    const int rr = 4 * g + ((lane & 15) >> 2);
+    const int col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      ad.b[nt][0] = t0 + 2u * tile_off<D>(rr, 32 * nt + col);
+      ad.b[nt][1] = t0 + 2u * tile_off<D>(rr + 8, 32 * nt + col);
+    }
+  }
+  ad.l = l0 + 16u * g;
+  __syncthreads();  // the first tile landed for every wave
+  for (int buf = 0; have; buf ^= 1) {
+    QTile nxt = cur;
+    nxt.q0 += H;
+    bool more = nxt.q0 < nxt.qend;
+    if (!more && --left > 0) {
+      ++nxt.e;
+      more = dkdv_seek(p, bn0, jb, n_end, si.len_q, nxt);
+    }
+    if (more) issue(nxt, buf ^ 1);  // the other buffer: everyone finished with it at the last barrier
+    // with a window, bit r of keep[sl]: row r of slice sl is in it for this
+    // lane's key, pre-shifted so that register i tests bit 8 (i / 4) + i % 4
+    uint32_t keep[NSL];
+#pragma unroll
+    for (int sl = 0; sl < NSL; ++sl) keep[sl] = WIN ? band_rows(p, cur.q0 + 32 * sl, my_kv) >> (4 * g) : 0u;
+    dkdv_pipe_tile<E, D, W, NSL, WIN>(ad, kreg, vreg, adv, adk, c2, keep);
+    wait_vmcnt<0>();  // this wave's copies of the next tile
+    __syncthreads();  // everyone's copies landed; everyone is done with this tile
+    const unsigned flip = buf ? 0u - BUF : BUF;  // the next tile sits in the other buffer
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) ad.a[ks] += flip;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      ad.b[nt][0] += flip;
+      ad.b[nt][1] += flip;
+    }
+    ad.l += buf ? 0u - 8u * H : 8u * H;
+    cur = nxt;
+    have = more;
+  }
+  dkdv_store_t<E, D>(p, u, piece, pieces, kv0, kv_end, w_end, b, h, si, adv, adk);
 }
 
 // AM: built for calls with an attenMask (its bits staged with the Q tiles);
@@ -1253,7 +1694,7 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(D >= 256
     float dsv[16];
     if (nrows == 32 && !AM && rect_in_band(p, q0 + 32 * w, 32, row0, 32)) {  // uniform: no mask needed
 #pragma unroll
-      for (int i = 0; i < 16; ++i) dsv[i] = fast_exp2(st[i] * c2 - l2) * (dpt[i] - dl);
+      for (int i = 0; i < 16; ++i) dsv[i] = fast_exp2(st[i] * c2 - l2) * (dpt[i] + dl);  // dl = -softmax_grad
     } else {
       const uint32_t ex = AM ? mask_word(sAB[slot][AM ? w : 0], row0, l32) : 0u;
       // bit kv of keep: slice key kv takes part (valid, in the window, not
@@ -1263,16 +1704,19 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(D >= 256
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const float x = ((keep >> (8 * (i >> 2) + (i & 3))) & 1u) ? fast_exp2(st[i] * c2 - l2) : 0.f;
-        dsv[i] = x * (dpt[i] - dl);
+        dsv[i] = x * (dpt[i] + dl);
       }
     }
     const u16x8 da[2] = {pack8<E>(dsv), pack8<E>(dsv + 8)};
     __builtin_amdgcn_s_setprio(1);
+    // dQ^T += K^T dS^T: the fragment read down K's rows is, as an A operand,
+    // K^T with the same k order as the dS^T registers (the B operand), so
+    // each lane accumulates its own query row of dQ
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh)
-        adq[nt] = E::mma(da[hh], frag_down_rows<D>(tk, 16 * hh, 32 * nt, lane), adq[nt]);  // dQ += dS K
+        adq[nt] = E::mma(frag_down_rows<D>(tk, 16 * hh, 32 * nt, lane), da[hh], adq[nt]);
     }
     __builtin_amdgcn_s_setprio(0);
   };
@@ -1296,14 +1740,18 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(D >= 256
   }
   wait_vmcnt<0>();  // copies of the empty slices past the end
 
-  unsigned short* dqp = static_cast<unsigned short*>(p.dq) + b * p.dq_sb + si.off_q * p.dq_sr + n * p.dq_sh;
+  // lane: query row my_q; register i of column tile nt: element 32 nt + 8 (i / 4) + 4 g + i % 4
+  if (my_q < w_end) {
+    unsigned short* dqp = static_cast<unsigned short*>(p.dq) + b * p.dq_sb + (si.off_q + my_q) * p.dq_sr + n * p.dq_sh;
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
+    for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int r = q0 + 32 * w + 8 * (i >> 2) + 4 * g + (i & 3);
-      if (r < w_end) dqp[r * p.dq_sr + 32 * nt + l32] = E::from_f32(adq[nt][i] * p.dq_scale);
-    }
+      for (int a = 0; a < 4; ++a) {
+        float x[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) x[t] = adq[nt][4 * a + t] * p.dq_scale;
+        store4<E>(dqp + 32 * nt + 8 * a + 4 * g, x);
+      }
   }
 }
 
@@ -1635,8 +2083,42 @@ int launch_plan(const Params& p, void* stream) {
   return static_cast<int>(hipGetLastError());
 }
 
+// The scheduled dK/dV build: fp16/bf16 at head dim 64 or 128 without an attenMask.
+template <class E, int D, int W, int NSL>
+void launch_dkdv_pipe(const Params& p, dim3 grid, hipStream_t s) {
+  if (p.win) hipLaunchKernelGGL((dkdv_pipe_kernel<E, D, W, NSL, true>), grid, dim3(64 * W), 0, s, p);
+  else hipLaunchKernelGGL((dkdv_pipe_kernel<E, D, W, NSL, false>), grid, dim3(64 * W), 0, s, p);
+}
+template <class E, int D>
+void launch_dkdv_pipe_w(const Params& p, int w, dim3 grid, hipStream_t s) {
+  const int nsl = dkdv_pipe_nsl(p.bx, w);
+  if (w == 4) {
+    if (nsl == 4) launch_dkdv_pipe<E, D, 4, 4>(p, grid, s);
+    else if (nsl == 2) launch_dkdv_pipe<E, D, 4, 2>(p, grid, s);
+    else launch_dkdv_pipe<E, D, 4, 1>(p, grid, s);
+  } else if (w == 2) {
+    if (nsl == 2) launch_dkdv_pipe<E, D, 2, 2>(p, grid, s);
+    else launch_dkdv_pipe<E, D, 2, 1>(p, grid, s);
+  } else {
+    launch_dkdv_pipe<E, D, 1, 1>(p, grid, s);
+  }
+}
+
 int launch_dkdv(const Params& p, void* stream) {
   const dim3 grid(static_cast<unsigned>(dkdv_passes(p.D) * (p.n_units + p.slots_cap)));
+  if (p.amask == nullptr && p.D <= 128) {
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    const int w = waves_for(p.by);
+    const bool bf = p.dtype == 2;
+    if (p.D == 128) {
+      if (bf) launch_dkdv_pipe_w<EBf16, 128>(p, w, grid, s);
+      else launch_dkdv_pipe_w<EF16, 128>(p, w, grid, s);
+    } else {
+      if (bf) launch_dkdv_pipe_w<EBf16, 64>(p, w, grid, s);
+      else launch_dkdv_pipe_w<EF16, 64>(p, w, grid, s);
+    }
+    return static_cast<int>(hipGetLastError());
+  }
   // head dim 256: the 1- and 2-wave builds spill registers, so KV blocks of
   // up to 64 rows also take the 4-wave one (its waves past the block's rows
   // compute on zero K/V rows and store nothing)

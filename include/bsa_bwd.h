@@ -311,7 +311,7 @@ int bsa_fwd_fp8(const bsa_tensor* query, const bsa_tensor* key, const bsa_tensor
 /* Workspace regions, as byte offsets filled in by bsa_bwd_workspace_layout. */
 enum bsa_ws_region {
   BSA_WS_SEQ = 0,      /* per-sequence table {int64 q_offset, kv_offset; int32 len_q, len_kv, wlim_q, wlim_kv} x B, then 128 fp32 constants */
-  BSA_WS_DELTA = 1,    /* fp32 [B, N, maxSq]: softmax_grad (row sums of dOut o Out); 0 past len_q */
+  BSA_WS_DELTA = 1,    /* fp32 [B, N, maxSq]: -softmax_grad (negated row sums of dOut o Out); 0 past len_q */
   BSA_WS_LSE2 = 2,     /* fp32 [B, N, maxSq]: softmaxLse * log2(e) */
   BSA_WS_ROW_CNT = 3,  /* int32 [B, N, nQB]: number of selected in-range KV blocks per Q block */
   BSA_WS_ROW_LIST = 4, /* int32 [B, N, nQB, nKB]: ascending KV-block lists, first ROW_CNT entries valid */

@@ -96,7 +96,7 @@ def test_delta_and_lse2(name):
     torch.cuda.synchronize()
     offs, _ = bsa.bsa_bwd_workspace_layout(*r.args, **r.kw)
     sq = c.Sq
-    delta = _read_ws(r, offs, "delta", c.B * c.N * sq, np.float32).reshape(c.B, c.N, sq)
+    delta = -_read_ws(r, offs, "delta", c.B * c.N * sq, np.float32).reshape(c.B, c.N, sq)  # stored negated
     lse2 = _read_ws(r, offs, "lse2", c.B * c.N * sq, np.float32).reshape(c.B, c.N, sq)
     offq = oracle.sequence_offsets(c.len_q)
     for b in range(c.B):
@@ -268,6 +268,56 @@ def test_guard_bytes_around_outputs_and_workspace(name):
         assert _guards_intact(buf, pat), f"{name}: bytes written next to {nm}"
         assert torch.equal(t.view(torch.int16), w.view(torch.int16)), nm
     assert _guards_intact(ws[1], ws[2]), f"{name}: bytes written next to the workspace"
+
+
+def _at_high_low_word(tensors):
+    """Copies of `tensors` inside one 4.1 GiB buffer, each at an address whose low
+    32 bits have bit 31 set (256-byte aligned, packed one after another)."""
+    big = torch.empty((1 << 32) + (1 << 26), dtype=torch.uint8, device="cuda")
+    base = big.data_ptr()
+    off = (((1 << 31) - base % (1 << 32)) % (1 << 32) + 255) // 256 * 256
+    out = []
+    for t in tensors:
+        n = t.numel() * t.element_size()
+        assert (base + off) % (1 << 32) >= 1 << 31 and (base + off + n) % (1 << 32) > (base + off) % (1 << 32)
+        v = big[off:off + n].view(t.dtype).view(t.shape)
+        v.copy_(t)
+        out.append(v)
+        off += (n + 255) // 256 * 256
+    return big, out
+
+
+@pytest.mark.parametrize("name", ["bnsd_bf16_d128_local_sink_split", "tnd_fp16_d64_window_ahead"])
+def test_inputs_at_addresses_with_bit31_of_the_low_word_set(name):
+    """The tile copies take their wave-uniform source address from scalar
+    registers, put together from two 32-bit halves; a sign-extended low half
+    once turned such addresses into invalid ones.  Every input and output here
+    sits at an address whose low word has bit 31 set; the results equal those
+    at ordinary addresses bitwise (backward and forward)."""
+    import block_sparse_attention_bwd_amd as bsa
+    from bench import FwdRunner
+    c, o, lse, _ = _prepared(name)
+    dev = upload(c, o, lse)
+    (dq, dk, dv), r = run_bsa(c, dev)
+    torch.cuda.synchronize()
+    want = [t.clone() for t in (dq, dk, dv)]
+    keys = ["do", "q", "k", "v", "o", "lse"]
+    big, moved = _at_high_low_word([dev[k] for k in keys] + [dq, dk, dv])
+    d2 = dict(dev, **dict(zip(keys, moved[:6])))
+    kw = dict(r.kw, dq=moved[6], dk=moved[7], dv=moved[8])
+    bsa.bsa_bwd(d2["do"], d2["q"], d2["k"], d2["v"], d2["o"], d2["lse"], **kw, workspace=r.ws,
+                workspace_size=r.ws_size)
+    torch.cuda.synchronize()
+    for got, w in zip(moved[6:], want):
+        assert torch.equal(got.view(torch.int16), w.view(torch.int16))
+    f = FwdRunner(c, dev)
+    o_want, l_want = (t.clone() for t in f())
+    torch.cuda.synchronize()
+    _, (q2, k2, v2, o2, l2) = _at_high_low_word([dev["q"], dev["k"], dev["v"], f.o, f.lse])
+    bsa.bsa_fwd(q2, k2, v2, **dict(f.kw, attention_out=o2, softmax_lse=l2), workspace=f.ws, workspace_size=f.ws_size)
+    torch.cuda.synchronize()
+    assert torch.equal(o2, o_want) and torch.equal(l2, l_want)
+    del big
 
 
 def test_too_small_workspace_launches_nothing():
