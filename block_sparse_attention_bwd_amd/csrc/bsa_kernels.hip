@@ -1349,6 +1349,37 @@ __device__ __forceinline__ void dkdv_pipe_tile(const DkdvAddr<D, W, NSL>& ad, co
   }
 }
 
+// A dK/dV work item's share of the merged list (the group's query heads in
+// order, each with its ascending list of Q blocks selecting the item's KV
+// block) is copied into LDS once, with every load in flight together, so that
+// finding the next tile is an LDS read.  Entry j holds (query head - first head
+// of the group, Q block).  Holds up to kDkdvListChunk entries at a time; longer
+// items refill it between tiles.
+constexpr int kDkdvListChunk = 1024;
+constexpr int kDkdvMaxGroup = 256;  // heads per KV head (the counts sit in LDS too)
+struct DkdvList {
+  int* ib;             // [kDkdvListChunk]
+  unsigned short* n;   // [kDkdvListChunk]
+  int* cnt;            // [kDkdvMaxGroup] list length of each head of the group
+  int first, count;    // the item's entries [first, first + count) of the merged list
+  int base;            // merged-list index of ib[0]
+};
+
+// Fill the LDS list from merged-list entry `from` (relative to the item's
+// first entry); every thread of the workgroup takes part.
+__device__ __forceinline__ void dkdv_list_fill(const Params& p, int64_t col0, int jb, DkdvList& l, int from) {
+  __syncthreads();  // everyone is done with the previous contents
+  const int nf = min(kDkdvListChunk, l.count - from);
+  for (int j = threadIdx.x; j < nf; j += blockDim.x) {
+    int e = l.first + from + j, n = 0;
+    while (e >= l.cnt[n]) e -= l.cnt[n++];
+    l.ib[j] = p.col_list[((col0 + n) * p.nkb + jb) * static_cast<int64_t>(p.nqb) + e];
+    l.n[j] = static_cast<unsigned short>(n);
+  }
+  l.base = from;
+  __syncthreads();
+}
+
 template <class E, int D, int W, int NSL, bool WIN>
 __global__ __launch_bounds__(64 * W) void dkdv_pipe_kernel(Params p) {
   using T = DkdvPipe<D, W, NSL>;
@@ -1358,6 +1389,8 @@ __global__ __launch_bounds__(64 * W) void dkdv_pipe_kernel(Params p) {
   // LSE*log2e rows, then the -softmax_grad rows
   __shared__ __align__(1024) unsigned short sT[2 * 2 * H * D];
   __shared__ __align__(16) float sLD[2 * 2 * H];
+  __shared__ int sListIb[kDkdvListChunk], sListCnt[kDkdvMaxGroup];
+  __shared__ unsigned short sListN[kDkdvListChunk];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6, l32 = lane & 31, g = lane >> 5;
@@ -1393,7 +1426,6 @@ __global__ __launch_bounds__(64 * W) void dkdv_pipe_kernel(Params p) {
 
   const float c2 = p.scale_log2e;
   const int64_t bn0 = static_cast<int64_t>(b) * p.N;
-  const int n_end = (h + 1) * p.G;
   const unsigned short* qbase = static_cast<const unsigned short*>(p.q) + b * p.q_sb + si.off_q * p.q_sr;
   const unsigned short* obase = static_cast<const unsigned short*>(p.dout) + b * p.q_sb + si.off_q * p.q_sr;
 
@@ -1436,10 +1468,32 @@ __global__ __launch_bounds__(64 * W) void dkdv_pipe_kernel(Params p) {
       }
     }
   };
-  int left = pieces > 1 ? chunk : 0x7fffffff;
-  QTile cur{h * p.G, pieces > 1 ? piece * chunk : 0, 0, 0};
-  bool have = dkdv_seek(p, bn0, jb, n_end, si.len_q, cur);
-  if (have) issue(cur, 0);  // the first tile's copies fly while K and V load
+  // the item's entries in LDS: counts of the group's heads, then the entries
+  const int64_t col0 = bn0 + static_cast<int64_t>(h) * p.G;  // (b, first head of the group)
+  DkdvList lst{sListIb, sListN, sListCnt, 0, 0, 0};
+  for (int t = tid; t < p.G; t += 64 * W) lst.cnt[t] = p.col_cnt[(col0 + t) * p.nkb + jb];
+  __syncthreads();
+  {
+    int tot = 0;
+    for (int t = 0; t < p.G; ++t) tot += lst.cnt[t];
+    lst.first = pieces > 1 ? piece * chunk : 0;
+    lst.count = pieces > 1 ? min(chunk, tot - lst.first) : tot;
+  }
+  dkdv_list_fill(p, col0, jb, lst, 0);
+  // tile of list entry e (relative to the item), first rows of its Q block
+  auto tile_of = [&](int e) {
+    if (e - lst.base >= kDkdvListChunk) dkdv_list_fill(p, col0, jb, lst, e);  // uniform
+    const int ib = lst.ib[e - lst.base];
+    QTile t{h * p.G + lst.n[e - lst.base], e, ib * p.bx, 0};
+    t.qend = min(t.q0 + p.bx, si.len_q);
+    return t;
+  };
+  bool have = lst.count > 0;
+  QTile cur{};
+  if (have) {
+    cur = tile_of(0);
+    issue(cur, 0);  // the first tile's copies fly while K and V load
+  }
   u16x8 kreg[KS], vreg[KS];
 #pragma unroll
   for (int s = 0; s < KS; ++s) {
@@ -1483,9 +1537,9 @@ __global__ __launch_bounds__(64 * W) void dkdv_pipe_kernel(Params p) {
     QTile nxt = cur;
     nxt.q0 += H;
     bool more = nxt.q0 < nxt.qend;
-    if (!more && --left > 0) {
-      ++nxt.e;
-      more = dkdv_seek(p, bn0, jb, n_end, si.len_q, nxt);
+    if (!more && cur.e + 1 < lst.count) {
+      nxt = tile_of(cur.e + 1);
+      more = true;
     }
     if (more) issue(nxt, buf ^ 1);  // the other buffer: everyone finished with it at the last barrier
     // with a window, bit r of keep[sl]: row r of slice sl is in it for this
@@ -2106,7 +2160,7 @@ void launch_dkdv_pipe_w(const Params& p, int w, dim3 grid, hipStream_t s) {
 
 int launch_dkdv(const Params& p, void* stream) {
   const dim3 grid(static_cast<unsigned>(dkdv_passes(p.D) * (p.n_units + p.slots_cap)));
-  if (p.amask == nullptr && p.D <= 128) {
+  if (p.amask == nullptr && p.D <= 128 && p.G <= kDkdvMaxGroup) {
     const hipStream_t s = static_cast<hipStream_t>(stream);
     const int w = waves_for(p.by);
     const bool bf = p.dtype == 2;
