@@ -544,7 +544,7 @@ int make_plan(const Args& a, Plan* plan) {
   const int64_t max_pieces = n_units * (N / Nkv) * nqb;  // a piece holds at least one Q block
   const int64_t slots_lim = std::max<int64_t>(0, std::min<int64_t>(a.max_slots, bsa::kMaxSlots));
   const int64_t slots = max_pieces < slots_lim ? max_pieces : slots_lim;
-  take(BSA_WS_PLAN, bwd * 4ull * bsa::plan_words(n_units, slots));
+  take(BSA_WS_PLAN, bwd * 4ull * bsa::plan_words(n_units, slots, B * N * nqb * nsub_q));
   take(BSA_WS_PARTIAL, bwd * 4ull * slots * 2 * bsa::kTileRowsMax * D);
   // attenMask as bits: by query row (all) and by key (the backward's dK/dV kernel)
   const bool am = a.atten_mask != nullptr;

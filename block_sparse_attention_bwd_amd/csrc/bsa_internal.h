@@ -85,7 +85,8 @@ struct Params {
   int32_t slots_cap;   // partial-result slots for units split over several workgroups
   int32_t* plan;       // [0] chunk size, [1] work items, [2] dQ order, [3] unused, unit_k[n_units],
                        // unit_base[n_units], slot_unit[slots_cap], slot_chunk[slots_cap],
-                       // order_unit[n_units + slots_cap], order_piece[n_units + slots_cap]
+                       // order_unit[n_units + slots_cap], order_piece[n_units + slots_cap],
+                       // dq_order[n_dq_units]
   float* partial;      // [slots_cap][2][kTileRowsMax][D] fp32 (dK unscaled, dV)
 };
 
@@ -96,9 +97,12 @@ struct Params {
 constexpr int kTileRowsMax = 128;
 
 // Words (int32) of the plan region: 4 header words, then per unit its piece
-// count and first slot, per slot its unit and piece, and the launch order as
-// two arrays (unit, piece) of n_units + slots entries.
-inline constexpr int64_t plan_words(int64_t n_units, int64_t slots) { return 4 + 4 * (n_units + slots); }
+// count and first slot, per slot its unit and piece, the launch order as
+// two arrays (unit, piece) of n_units + slots entries, and the dQ launch
+// order (n_dq entries).
+inline constexpr int64_t plan_words(int64_t n_units, int64_t slots, int64_t n_dq) {
+  return 4 + 4 * (n_units + slots) + n_dq;
+}
 constexpr int kBalanceGroups = 256;
 // Workgroups per dK/dV work item: 1, or 2 where dK and dV are accumulated by
 // separate workgroups (head dim 256: K, V and both accumulators do not fit

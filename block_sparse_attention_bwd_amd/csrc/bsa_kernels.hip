@@ -421,17 +421,14 @@ __device__ __forceinline__ int unit_entries(const Params& p, int u) {
   return t;
 }
 
-// dQ workgroup order.  Hardware hands workgroup i to XCD i % 8.  In XCD-range
-// order XCD x runs the x-th of eight contiguous ranges of units, so the Q
+// dQ workgroup order.  Hardware hands workgroup i to XCD i % 8.  With XCD
+// ranges, XCD x runs the x-th of eight contiguous ranges of dQ units (range x
+// starts at x * per + min(x, rem) for per = n / 8, rem = n % 8), so the Q
 // blocks of a head group, which read the same K/V rows, share one L2; the plan
 // kernel picks it only when the eight ranges hold nearly equal work, since one
 // heavy range (a long sequence among short ones) would leave seven XCDs idle.
-// Otherwise workgroup i runs unit i, spreading every range over all XCDs.
-__device__ __forceinline__ int xcd_range_id(int bid, int n) {
-  const int x = bid & 7, per = n >> 3, rem = n & 7;
-  return x * per + min(x, rem) + (bid >> 3);
-}
-// The XCD whose range holds unit u under xcd_range_id.
+// Either way the units are launched longest first (see plan_kernel).
+// The XCD whose range holds unit u.
 __device__ __forceinline__ int xcd_of_unit(int u, int n) {
   const int per = n >> 3, rem = n & 7;
   const int big = (per + 1) * rem;  // the first rem ranges hold per + 1 units
@@ -441,7 +438,8 @@ constexpr int kDqOrderPlain = 0, kDqOrderXcdRange = 1;
 
 // The plan region, in order: [0] chunk, [1] number of work items, [2] dQ order, [3]
 // unused, then per unit its piece count and first slot, per slot its unit
-// (-1 = unused) and piece, and the work items (unit, piece) in launch order.
+// (-1 = unused) and piece, the work items (unit, piece) in launch order, and
+// the dQ units in launch order.
 struct PlanView {
   int32_t* unit_k;
   int32_t* unit_base;
@@ -449,6 +447,7 @@ struct PlanView {
   int32_t* slot_chunk;
   int32_t* order_unit;
   int32_t* order_piece;
+  int32_t* dq_order;  // dQ workgroup k runs dQ unit dq_order[k]
   __device__ explicit PlanView(const Params& p) {
     unit_k = p.plan + 4;
     unit_base = unit_k + p.n_units;
@@ -456,6 +455,7 @@ struct PlanView {
     slot_chunk = slot_unit + p.slots_cap;
     order_unit = slot_chunk + p.slots_cap;
     order_piece = order_unit + p.n_units + p.slots_cap;
+    dq_order = order_piece + p.n_units + p.slots_cap;
   }
 };
 
@@ -479,12 +479,16 @@ __global__ __launch_bounds__(1024) void plan_kernel(Params p) {
   __shared__ int s_hist[kOrderBins], s_cursor[kOrderBins];
   __shared__ unsigned long long s_xcd[8];
   __shared__ int s_T[kPlanCachedUnits];
+  __shared__ int s_dq[8 * kOrderBins];  // dQ cost classes per XCD range: counts, then cursors
+  __shared__ int s_dqmax;
   const int tid = threadIdx.x;
   const PlanView pv(p);
   const int per = (p.n_units + 1023) / 1024;
   const int u0 = min(p.n_units, tid * per), u1 = min(p.n_units, u0 + per);
   if (tid < kOrderBins) s_hist[tid] = 0;
   if (tid < 8) s_xcd[tid] = 0;
+  if (tid < 8 * kOrderBins) s_dq[tid] = 0;
+  if (tid == 0) s_dqmax = 0;
   // T_u, read from the column counts once (each thread reads back only its own units)
   const bool cached = p.n_units <= kPlanCachedUnits;
   auto T = [&](int u) { return cached ? s_T[u] : unit_entries(p, u); };
@@ -553,18 +557,22 @@ __global__ __launch_bounds__(1024) void plan_kernel(Params p) {
     const int nd = p.n_dq_units, nsub_q = (p.bx + kTileRows - 1) / kTileRows;
     unsigned long long acc = 0;
     int cur = xcd_of_unit(min(tid, max(nd - 1, 0)), max(nd, 1));
+    int mx = 0;
 #pragma unroll 4
     for (int u = tid; u < nd; u += 1024) {
       const int x = xcd_of_unit(u, nd);
-      const unsigned c = 1u + static_cast<unsigned>(p.row_cnt[u / nsub_q]);
+      const int rc = p.row_cnt[u / nsub_q];
+      const unsigned c = 1u + static_cast<unsigned>(rc);
       if (x != cur) {
         atomicAdd(&s_xcd[cur], acc);
         acc = 0;
         cur = x;
       }
       acc += c;
+      mx = max(mx, rc);
     }
     if (acc) atomicAdd(&s_xcd[cur], acc);
+    atomicMax(&s_dqmax, mx);
   }
   __syncthreads();
   if (tid == 0) {
@@ -591,6 +599,33 @@ __global__ __launch_bounds__(1024) void plan_kernel(Params p) {
       const int at = atomicAdd(&s_cursor[order_bin(k > 1 ? min(chunk, t - c * chunk) : t, chunk)], 1);
       pv.order_unit[at] = u;
       pv.order_piece[at] = c;
+    }
+  }
+  // dQ launch order, longest first (cost classes of the selected KV-block
+  // count): with XCD ranges, within each range (workgroup 8 k + x runs the
+  // k-th unit of range x, as the hardware hands workgroup i to XCD i % 8);
+  // otherwise over all units, dealt round-robin to the XCDs.  Results do not
+  // depend on the order.
+  {
+    const int nd = p.n_dq_units, nsub_q = (p.bx + kTileRows - 1) / kTileRows;
+    const bool ranges = p.plan[2] == kDqOrderXcdRange;
+    const int mxc = max(s_dqmax, 1);
+    auto cls = [&](int u) { return order_bin(p.row_cnt[u / nsub_q], mxc); };
+    for (int u = tid; u < nd; u += 1024) atomicAdd(&s_dq[(ranges ? xcd_of_unit(u, nd) : 0) * kOrderBins + cls(u)], 1);
+    __syncthreads();
+    if (tid < (ranges ? 8 : 1)) {  // per range: cursors of the classes in descending order
+      int base = 0;
+      for (int c = kOrderBins - 1; c >= 0; --c) {
+        const int n = s_dq[tid * kOrderBins + c];
+        s_dq[tid * kOrderBins + c] = base;
+        base += n;
+      }
+    }
+    __syncthreads();
+    for (int u = tid; u < nd; u += 1024) {
+      const int x = ranges ? xcd_of_unit(u, nd) : 0;
+      const int k = atomicAdd(&s_dq[x * kOrderBins + cls(u)], 1);
+      pv.dq_order[ranges ? 8 * k + x : k] = u;
     }
   }
 }
@@ -1658,7 +1693,7 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(D >= 256
     reduce_pieces<E, D>(p, blockIdx.x - p.n_dq_units);
     return;
   }
-  int wid = p.plan[2] == kDqOrderXcdRange ? xcd_range_id(blockIdx.x, p.n_dq_units) : static_cast<int>(blockIdx.x);
+  int wid = PlanView(p).dq_order[blockIdx.x];
   const int nsub = (p.bx + kTileRows - 1) / kTileRows;
   const int sub = wid % nsub;
   wid /= nsub;

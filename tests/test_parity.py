@@ -168,7 +168,8 @@ def test_split_units_are_planned():
                                   "bnsd_fp16_d128_b256x256"])
 def test_dq_order_choice(name):
     """plan[2]: XCD-range order for dQ iff the eight contiguous ranges of dQ
-    units carry work within 1/32 of each other (unit cost = selected KV blocks + 1)."""
+    units carry work within 1/32 of each other (unit cost = selected KV blocks + 1);
+    the dQ launch order is longest first within each range (or overall)."""
     import block_sparse_attention_bwd_amd as bsa
     c, o, lse, _ = _prepared(name)
     dev = upload(c, o, lse)
@@ -184,6 +185,23 @@ def test_dq_order_choice(name):
     work = [sum(cost[bounds[x]:bounds[x + 1]]) for x in range(8)]
     want = 1 if 8 * max(work) * 32 <= sum(work) * 33 else 0
     assert int(_read_ws(r, offs, "plan", 4)[2]) == want
+    # the dQ launch order (the plan's last nd words): a permutation of the units;
+    # with ranges, workgroup 8k + x runs range x's units, else all units, longest
+    # first by cost class (selected KV blocks, 64 classes scaled to the largest)
+    n_units = c.B * c.Nkv * nkb * -(-by // 128)
+    slots = min(n_units * (c.N // c.Nkv) * nqb, 512)
+    words = 4 + 4 * (n_units + slots) + nd
+    order = _read_ws(r, offs, "plan", words)[4 + 4 * (n_units + slots):].tolist()
+    assert sorted(order) == list(range(nd))
+    sel = [x - 1 for x in cost]
+    mx = max(1, max(sel))
+    klass = [0 if v <= 0 else min(63, 1 + (v - 1) * 63 // mx) for v in sel]
+    groups = [[order[k] for k in range(x, nd, 8)] for x in range(8)] if want else [order]
+    for x, grp in enumerate(groups):
+        if want:
+            assert sorted(grp) == list(range(bounds[x], bounds[x + 1]))
+        cl = [klass[u] for u in grp]
+        assert cl == sorted(cl, reverse=True)
 
 
 def test_noncontiguous_outputs_match():
