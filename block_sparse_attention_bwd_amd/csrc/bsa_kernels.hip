@@ -41,6 +41,7 @@
 // that order.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <mutex>
 
 #include "bsa_internal.h"
@@ -437,7 +438,7 @@ __device__ __forceinline__ int xcd_of_unit(int u, int n) {
 constexpr int kDqOrderPlain = 0, kDqOrderXcdRange = 1;
 
 // The plan region, in order: [0] chunk, [1] number of work items, [2] dQ order, [3]
-// unused, then per unit its piece count and first slot, per slot its unit
+// the next work item to take (the persistent dK/dV kernel's counter), then per unit its piece count and first slot, per slot its unit
 // (-1 = unused) and piece, the work items (unit, piece) in launch order, and
 // the dQ units in launch order.
 struct PlanView {
@@ -590,6 +591,7 @@ __global__ __launch_bounds__(1024) void plan_kernel(Params p) {
     }
     p.plan[0] = chunk;
     p.plan[1] = p.n_units + s_scan[0];
+    p.plan[3] = 0;  // the persistent dK/dV kernel's item counter
   }
   __syncthreads();
   for (int u = u0; u < u1; ++u) {
@@ -1415,6 +1417,83 @@ __device__ __forceinline__ void dkdv_list_fill(const Params& p, int64_t col0, in
   __syncthreads();
 }
 
+// Persistent: a grid of as many workgroups as fit the GPU at once, each taking
+// work items from the plan's launch order (longest first) through a counter
+// in the plan region, which the plan kernel zeroes.  When an item's tiles are
+// done, the workgroup first starts the next item (its list, its first tile's
+// copies, its K and V rows) and only then issues the finished item's stores,
+// so those loads fly while the stores are issued.  Which workgroup runs an
+// item does not change the item's result.
+// Epilogue of a whole unit through LDS: every lane writes its key row's dK (then
+// dV) into `stage` (transposed accumulators: 4 consecutive elements per
+// 8-byte write; rows of D elements with their 16-byte chunks XOR-permuted by
+// the row's low bits (as many as index a row's chunks), so the rows of one
+// write spread over the banks),
+// then every 16-byte store of a wave covers 1 KB of consecutive rows.  STAGE
+// is the stage's size in bytes: both tensors at once when they fit, else one
+// after the other.  Rows from kv_end on are stored as zeros.  The caller syncs
+// the workgroup before the stage is reused.  Falls back to dkdv_store_t when an
+// output row is not 16-byte aligned, for a piece of a split unit, or when
+// one tensor's rows do not fit the stage.
+template <class E, int D, int W, unsigned STAGE>
+__device__ __forceinline__ void dkdv_store_staged(const Params& p, int u, int piece, int pieces, int kv0, int kv_end,
+                                                  int w_end, int b, int h, const SeqInfo& si,
+                                                  const f32x16 (&adv)[D / 32], const f32x16 (&adk)[D / 32],
+                                                  unsigned stage) {
+  constexpr int NT = D / 32, CPR = D / 8;  // 16-byte chunks per row (a power of two)
+  constexpr int RT = 32 * W;               // rows of one tensor
+  static_assert((CPR & (CPR - 1)) == 0, "chunk permutation");
+  constexpr unsigned TBYTES = 2u * RT * D;
+  unsigned short* dkp = static_cast<unsigned short*>(p.dk) + b * p.dk_sb + si.off_kv * p.dk_sr + h * p.dk_sh;
+  unsigned short* dvp = static_cast<unsigned short*>(p.dv) + b * p.dv_sb + si.off_kv * p.dv_sr + h * p.dv_sh;
+  const bool aligned = ((reinterpret_cast<uintptr_t>(dkp) | reinterpret_cast<uintptr_t>(dvp)) & 15u) == 0 &&
+                       ((p.dk_sr | p.dv_sr) & 7) == 0;
+  if (TBYTES > STAGE || pieces > 1 || !aligned) {  // uniform
+    dkdv_store_t<E, D>(p, u, piece, pieces, kv0, kv_end, w_end, b, h, si, adv, adk);
+    return;
+  }
+  constexpr int NPASS = 2 * TBYTES <= STAGE ? 1 : 2;  // tensors per pass: 2 / NPASS
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, w = tid >> 6, l32 = lane & 31, g = lane >> 5;
+  const int rl = 32 * w + l32;
+  const bool live = kv0 + rl < kv_end;
+  const int rows = min(w_end - kv0, RT);
+  typedef __attribute__((address_space(3))) u16x4 lds_u16x4;
+#pragma unroll
+  for (int pass = 0; pass < NPASS; ++pass) {
+    if (pass) __syncthreads();  // the first tensor's rows are read out
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        const int chunk = (4 * nt + a) ^ (rl & (CPR - 1));
+        const unsigned off = 2u * (rl * D + 8 * chunk + 4 * g);
+        u16x4 kv4, vv4;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          kv4[t] = E::from_f32(live ? adk[nt][4 * a + t] * p.dk_scale : 0.f);
+          vv4[t] = E::from_f32(live ? adv[nt][4 * a + t] * p.dv_scale : 0.f);
+        }
+        if (NPASS == 1) {
+          *(lds_u16x4*)(static_cast<uintptr_t>(stage + off)) = kv4;
+          *(lds_u16x4*)(static_cast<uintptr_t>(stage + TBYTES + off)) = vv4;
+        } else {
+          *(lds_u16x4*)(static_cast<uintptr_t>(stage + off)) = pass ? vv4 : kv4;
+        }
+      }
+    __syncthreads();
+    const int nten = 2 / NPASS;
+    for (int i = tid; i < nten * rows * CPR; i += 64 * W) {  // (tensor, row, chunk), chunks fastest
+      const int t = i / (rows * CPR), rem = i - t * rows * CPR;
+      const int r = rem / CPR, c = rem - r * CPR;
+      const u16x8 v = lds_b128(stage + t * TBYTES + 2u * (r * D + 8 * (c ^ (r & (CPR - 1)))));
+      const bool is_k = NPASS == 1 ? t == 0 : pass == 0;
+      unsigned short* dst = (is_k ? dkp + (kv0 + r) * p.dk_sr : dvp + (kv0 + r) * p.dv_sr) + 8 * c;
+      *reinterpret_cast<u16x8*>(dst) = v;
+    }
+  }
+}
+
 template <class E, int D, int W, int NSL, bool WIN>
 __global__ __launch_bounds__(64 * W) void dkdv_pipe_kernel(Params p) {
   using T = DkdvPipe<D, W, NSL>;
@@ -1426,43 +1505,47 @@ __global__ __launch_bounds__(64 * W) void dkdv_pipe_kernel(Params p) {
   __shared__ __align__(16) float sLD[2 * 2 * H];
   __shared__ int sListIb[kDkdvListChunk], sListCnt[kDkdvMaxGroup];
   __shared__ unsigned short sListN[kDkdvListChunk];
+  __shared__ int sItem;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6, l32 = lane & 31, g = lane >> 5;
-
   const PlanView pv(p);
-  const int item = blockIdx.x;
-  if (item >= p.plan[1]) return;
-  const int u = pv.order_unit[item];
-  const int piece = pv.order_piece[item];
-  const int pieces = pv.unit_k[u];
-  const int chunk = p.plan[0];
-
-  int wid = u;
+  const int chunk = p.plan[0], n_items = p.plan[1];
   const int nsub = (p.by + kTileRows - 1) / kTileRows;
-  const int sub = wid % nsub;
-  wid /= nsub;
-  const int jb = wid % p.nkb;
-  wid /= p.nkb;
-  const int h = wid % p.Nkv;
-  const int b = wid / p.Nkv;
-  const SeqInfo si = p.seq[b];
-  const int kv0 = jb * p.by + sub * kTileRows;
-  const int part_end = min(jb * p.by + p.by, kv0 + kTileRows);
-  const int kv_end = min(part_end, si.len_kv);
-  const int w_end = min(part_end, si.wlim_kv);
-  if (kv0 >= w_end) return;  // uniform over the workgroup
-
-  const int my_kv = kv0 + 32 * w + l32;
-  const bool kv_ok = my_kv < kv_end;
-  const int64_t kv_base = b * p.kv_sb + si.off_kv * p.kv_sr + h * p.kv_sh;
-  const unsigned short* kp = static_cast<const unsigned short*>(p.k) + kv_base;
-  const unsigned short* vp = static_cast<const unsigned short*>(p.v) + kv_base;
-
   const float c2 = p.scale_log2e;
-  const int64_t bn0 = static_cast<int64_t>(b) * p.N;
-  const unsigned short* qbase = static_cast<const unsigned short*>(p.q) + b * p.q_sb + si.off_q * p.q_sr;
-  const unsigned short* obase = static_cast<const unsigned short*>(p.dout) + b * p.q_sb + si.off_q * p.q_sr;
+
+  // one work item: piece `piece` of unit u (batch b, KV head h, KV rows [kv0, w_end))
+  struct Item {
+    int u, piece, pieces, kv0, kv_end, w_end, b, h, jb;
+    SeqInfo si;
+    int64_t bn0, col0;
+  };
+  auto grab = [&]() {  // the next item of the launch order, for the whole workgroup
+    __syncthreads();   // everyone read the previous one
+    if (tid == 0) sItem = atomicAdd(&p.plan[3], 1);
+    __syncthreads();
+    return sItem;
+  };
+  auto decode = [&](int item, Item& it) {  // false: the item writes nothing
+    it.u = pv.order_unit[item];
+    it.piece = pv.order_piece[item];
+    it.pieces = pv.unit_k[it.u];
+    int wid = it.u;
+    const int sub = wid % nsub;
+    wid /= nsub;
+    it.jb = wid % p.nkb;
+    wid /= p.nkb;
+    it.h = wid % p.Nkv;
+    it.b = wid / p.Nkv;
+    it.si = p.seq[it.b];
+    it.kv0 = it.jb * p.by + sub * kTileRows;
+    const int part_end = min(it.jb * p.by + p.by, it.kv0 + kTileRows);
+    it.kv_end = min(part_end, it.si.len_kv);
+    it.w_end = min(part_end, it.si.wlim_kv);
+    it.bn0 = static_cast<int64_t>(it.b) * p.N;
+    it.col0 = it.bn0 + static_cast<int64_t>(it.h) * p.G;  // (b, first head of the group)
+    return it.kv0 < it.w_end;
+  };
 
   // DMA of one tile into buffer `buf` (as in dkdv_work): Q rows, dO rows and
   // their LSE*log2e / -softmax_grad values (+inf / 0 past the valid rows).
@@ -1479,11 +1562,11 @@ __global__ __launch_bounds__(64 * W) void dkdv_pipe_kernel(Params p) {
     voff[i] = static_cast<unsigned>(2 * (r * p.q_sr + 8 * c));
   }
   const unsigned t0 = lds_addr(sT), l0 = lds_addr(sLD);
-  auto issue = [&](const QTile& t, int buf) {
+  auto issue = [&](const Item& it, const QTile& t, int buf) {
     const int rows = min(H, t.qend - t.q0);
-    const int64_t first = static_cast<int64_t>(t.q0) * p.q_sr + t.n * p.q_sh;
-    const unsigned short* qa = qbase + first;
-    const unsigned short* oa = obase + first;
+    const int64_t first = (it.b * p.q_sb + it.si.off_q * p.q_sr) + static_cast<int64_t>(t.q0) * p.q_sr + t.n * p.q_sh;
+    const unsigned short* qa = static_cast<const unsigned short*>(p.q) + first;
+    const unsigned short* oa = static_cast<const unsigned short*>(p.dout) + first;
     const unsigned qb = t0 + BUF * buf, ob = qb + TB;
 #pragma unroll
     for (int i = 0; i < NCP; ++i) {
@@ -1496,7 +1579,7 @@ __global__ __launch_bounds__(64 * W) void dkdv_pipe_kernel(Params p) {
     for (int r0 = 0; r0 < RW; r0 += 64) {
       if (lane < RW - r0) {
         const int r = RW * w + r0 + lane;
-        const int64_t li = (bn0 + t.n) * p.sq_max + t.q0 + r;
+        const int64_t li = (it.bn0 + t.n) * p.sq_max + t.q0 + r;
         const unsigned lb = l0 + 8u * H * buf + 4u * (RW * w + r0);
         dma4(r < rows ? static_cast<const void*>(p.lse2 + li) : p.consts + kConstPosInf, lb);
         dma4(r < rows ? static_cast<const void*>(p.delta + li) : p.consts, lb + 4u * H);
@@ -1504,100 +1587,133 @@ __global__ __launch_bounds__(64 * W) void dkdv_pipe_kernel(Params p) {
     }
   };
   // the item's entries in LDS: counts of the group's heads, then the entries
-  const int64_t col0 = bn0 + static_cast<int64_t>(h) * p.G;  // (b, first head of the group)
   DkdvList lst{sListIb, sListN, sListCnt, 0, 0, 0};
-  for (int t = tid; t < p.G; t += 64 * W) lst.cnt[t] = p.col_cnt[(col0 + t) * p.nkb + jb];
-  __syncthreads();
-  {
+  auto list_start = [&](const Item& it) {
+    __syncthreads();  // everyone is done with the previous item's list
+    for (int t = tid; t < p.G; t += 64 * W) lst.cnt[t] = p.col_cnt[(it.col0 + t) * p.nkb + it.jb];
+    __syncthreads();
     int tot = 0;
     for (int t = 0; t < p.G; ++t) tot += lst.cnt[t];
-    lst.first = pieces > 1 ? piece * chunk : 0;
-    lst.count = pieces > 1 ? min(chunk, tot - lst.first) : tot;
-  }
-  dkdv_list_fill(p, col0, jb, lst, 0);
+    lst.first = it.pieces > 1 ? it.piece * chunk : 0;
+    lst.count = it.pieces > 1 ? min(chunk, tot - lst.first) : tot;
+    dkdv_list_fill(p, it.col0, it.jb, lst, 0);
+  };
   // tile of list entry e (relative to the item), first rows of its Q block
-  auto tile_of = [&](int e) {
-    if (e - lst.base >= kDkdvListChunk) dkdv_list_fill(p, col0, jb, lst, e);  // uniform
+  auto tile_of = [&](const Item& it, int e) {
+    if (e - lst.base >= kDkdvListChunk) dkdv_list_fill(p, it.col0, it.jb, lst, e);  // uniform
     const int ib = lst.ib[e - lst.base];
-    QTile t{h * p.G + lst.n[e - lst.base], e, ib * p.bx, 0};
-    t.qend = min(t.q0 + p.bx, si.len_q);
+    QTile t{it.h * p.G + lst.n[e - lst.base], e, ib * p.bx, 0};
+    t.qend = min(t.q0 + p.bx, it.si.len_q);
     return t;
   };
-  bool have = lst.count > 0;
-  QTile cur{};
-  if (have) {
-    cur = tile_of(0);
-    issue(cur, 0);  // the first tile's copies fly while K and V load
-  }
+  // K and V rows of the item (zero rows for keys past the sequence end; their
+  // P and dS are not masked, as they feed only the lane's own dK/dV rows,
+  // which the epilogue stores as zeros)
   u16x8 kreg[KS], vreg[KS];
+  auto load_kv = [&](const Item& it) {
+    const int64_t kv_base = it.b * p.kv_sb + it.si.off_kv * p.kv_sr + it.h * p.kv_sh;
+    const unsigned short* kp = static_cast<const unsigned short*>(p.k) + kv_base;
+    const unsigned short* vp = static_cast<const unsigned short*>(p.v) + kv_base;
+    const int my_kv = it.kv0 + 32 * w + l32;
 #pragma unroll
-  for (int s = 0; s < KS; ++s) {
-    u16x8 zk = {0, 0, 0, 0, 0, 0, 0, 0};
-    u16x8 zv = zk;
-    if (kv_ok) {
-      zk = *reinterpret_cast<const u16x8*>(kp + my_kv * p.kv_sr + 16 * s + 8 * g);
-      zv = *reinterpret_cast<const u16x8*>(vp + my_kv * p.kv_sr + 16 * s + 8 * g);
+    for (int s = 0; s < KS; ++s) {
+      u16x8 zk = {0, 0, 0, 0, 0, 0, 0, 0};
+      u16x8 zv = zk;
+      if (my_kv < it.kv_end) {
+        zk = *reinterpret_cast<const u16x8*>(kp + my_kv * p.kv_sr + 16 * s + 8 * g);
+        zv = *reinterpret_cast<const u16x8*>(vp + my_kv * p.kv_sr + 16 * s + 8 * g);
+      }
+      kreg[s] = zk;
+      vreg[s] = zv;
     }
-    kreg[s] = zk;
-    vreg[s] = zv;
-  }
-  f32x16 adv[NT], adk[NT];
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    adv[nt] = f32x16{};
-    adk[nt] = f32x16{};
-  }
-  wait_vmcnt<0>();
-#pragma unroll
-  for (int s = 0; s < KS; ++s) {  // the K/V loads are complete: no waits for them in the tile loop
-    settle(kreg[s]);
-    settle(vreg[s]);
-  }
+  };
+  // start an item: its list, its first tile's copies into buffer 0, its K/V rows
+  auto start = [&](const Item& it, QTile& first) {
+    list_start(it);
+    if (lst.count > 0) {
+      first = tile_of(it, 0);
+      issue(it, first, 0);
+    }
+    load_kv(it);
+  };
 
-  DkdvAddr<D, W, NSL> ad;
-#pragma unroll
-  for (int ks = 0; ks < KS; ++ks) ad.a[ks] = t0 + 2u * tile_off<D>(l32, 16 * ks + 8 * g);
-  {
-    const int rr = 4 * g + ((lane & 15) >> 2);
-    const int col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      ad.b[nt][0] = t0 + 2u * tile_off<D>(rr, 32 * nt + col);
-      ad.b[nt][1] = t0 + 2u * tile_off<D>(rr + 8, 32 * nt + col);
-    }
-  }
-  ad.l = l0 + 16u * g;
-  __syncthreads();  // the first tile landed for every wave
-  for (int buf = 0; have; buf ^= 1) {
-    QTile nxt = cur;
-    nxt.q0 += H;
-    bool more = nxt.q0 < nxt.qend;
-    if (!more && cur.e + 1 < lst.count) {
-      nxt = tile_of(cur.e + 1);
-      more = true;
-    }
-    if (more) issue(nxt, buf ^ 1);  // the other buffer: everyone finished with it at the last barrier
-    // with a window, bit r of keep[sl]: row r of slice sl is in it for this
-    // lane's key, pre-shifted so that register i tests bit 8 (i / 4) + i % 4
-    uint32_t keep[NSL];
-#pragma unroll
-    for (int sl = 0; sl < NSL; ++sl) keep[sl] = WIN ? band_rows(p, cur.q0 + 32 * sl, my_kv) >> (4 * g) : 0u;
-    dkdv_pipe_tile<E, D, W, NSL, WIN>(ad, kreg, vreg, adv, adk, c2, keep);
-    wait_vmcnt<0>();  // this wave's copies of the next tile
-    __syncthreads();  // everyone's copies landed; everyone is done with this tile
-    const unsigned flip = buf ? 0u - BUF : BUF;  // the next tile sits in the other buffer
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) ad.a[ks] += flip;
+  Item cur_it{};
+  int item = grab();
+  while (item < n_items && !decode(item, cur_it)) item = grab();
+  if (item >= n_items) return;  // uniform
+  QTile cur{};
+  start(cur_it, cur);
+  f32x16 adv[NT], adk[NT];
+  for (;;) {
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-      ad.b[nt][0] += flip;
-      ad.b[nt][1] += flip;
+      adv[nt] = f32x16{};
+      adk[nt] = f32x16{};
     }
-    ad.l += buf ? 0u - 8u * H : 8u * H;
-    cur = nxt;
-    have = more;
+    wait_vmcnt<0>();
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {  // the K/V loads are complete: no waits for them in the tile loop
+      settle(kreg[s]);
+      settle(vreg[s]);
+    }
+    DkdvAddr<D, W, NSL> ad;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) ad.a[ks] = t0 + 2u * tile_off<D>(l32, 16 * ks + 8 * g);
+    {
+      const int rr = 4 * g + ((lane & 15) >> 2);
+      const int col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        ad.b[nt][0] = t0 + 2u * tile_off<D>(rr, 32 * nt + col);
+        ad.b[nt][1] = t0 + 2u * tile_off<D>(rr + 8, 32 * nt + col);
+      }
+    }
+    ad.l = l0 + 16u * g;
+    __syncthreads();  // the first tile landed for every wave
+    const int my_kv = cur_it.kv0 + 32 * w + l32;
+    bool have = lst.count > 0;
+    for (int buf = 0; have; buf ^= 1) {
+      QTile nxt = cur;
+      nxt.q0 += H;
+      bool more = nxt.q0 < nxt.qend;
+      if (!more && cur.e + 1 < lst.count) {
+        nxt = tile_of(cur_it, cur.e + 1);
+        more = true;
+      }
+      if (more) issue(cur_it, nxt, buf ^ 1);  // the other buffer: everyone finished with it at the last barrier
+      // with a window, bit r of keep[sl]: row r of slice sl is in it for this
+      // lane's key, pre-shifted so that register i tests bit 8 (i / 4) + i % 4
+      uint32_t keep[NSL];
+#pragma unroll
+      for (int sl = 0; sl < NSL; ++sl) keep[sl] = WIN ? band_rows(p, cur.q0 + 32 * sl, my_kv) >> (4 * g) : 0u;
+      dkdv_pipe_tile<E, D, W, NSL, WIN>(ad, kreg, vreg, adv, adk, c2, keep);
+      wait_vmcnt<0>();  // this wave's copies of the next tile
+      __syncthreads();  // everyone's copies landed; everyone is done with this tile
+      const unsigned flip = buf ? 0u - BUF : BUF;  // the next tile sits in the other buffer
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) ad.a[ks] += flip;
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        ad.b[nt][0] += flip;
+        ad.b[nt][1] += flip;
+      }
+      ad.l += buf ? 0u - 8u * H : 8u * H;
+      cur = nxt;
+      have = more;
+    }
+    // the next item starts before this one's stores are issued
+    Item nx_it{};
+    int nitem = grab();
+    bool next = false;
+    while (nitem < n_items && !(next = decode(nitem, nx_it))) nitem = grab();
+    QTile nx{};
+    if (next) start(nx_it, nx);  // the next item's first tile goes to buffer 0; buffer 1 stages the stores
+    dkdv_store_staged<E, D, W, BUF>(p, cur_it.u, cur_it.piece, cur_it.pieces, cur_it.kv0, cur_it.kv_end,
+                                    cur_it.w_end, cur_it.b, cur_it.h, cur_it.si, adv, adk, t0 + BUF);
+    if (!next) break;  // uniform
+    cur_it = nx_it;
+    cur = nx;
   }
-  dkdv_store_t<E, D>(p, u, piece, pieces, kv0, kv_end, w_end, b, h, si, adv, adk);
 }
 
 // AM: built for calls with an attenMask (its bits staged with the Q tiles);
@@ -2172,9 +2288,26 @@ int launch_plan(const Params& p, void* stream) {
   return static_cast<int>(hipGetLastError());
 }
 
-// The scheduled dK/dV build: fp16/bf16 at head dim 64 or 128 without an attenMask.
+// Compute units of the current device (looked up once per device).
+int device_cus() {
+  constexpr int kMaxDevices = 64;
+  static int cus[kMaxDevices] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
+  if (cus[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cus[dev] = n;
+  }
+  return cus[dev];
+}
+
+// The scheduled dK/dV build: fp16/bf16 at head dim 64 or 128 without an
+// attenMask; persistent, as many workgroups as run at once (one wave per SIMD:
+// 4 / W workgroups per compute unit), or fewer if there are fewer work items.
 template <class E, int D, int W, int NSL>
-void launch_dkdv_pipe(const Params& p, dim3 grid, hipStream_t s) {
+void launch_dkdv_pipe(const Params& p, dim3 items, hipStream_t s) {
+  const dim3 grid(static_cast<unsigned>(std::min<int64_t>(items.x, static_cast<int64_t>(device_cus()) * (4 / W))));
   if (p.win) hipLaunchKernelGGL((dkdv_pipe_kernel<E, D, W, NSL, true>), grid, dim3(64 * W), 0, s, p);
   else hipLaunchKernelGGL((dkdv_pipe_kernel<E, D, W, NSL, false>), grid, dim3(64 * W), 0, s, p);
 }
