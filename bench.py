@@ -424,10 +424,16 @@ def clock_report(driver_mhz, counter_mhz, tflops):
 
 
 def kernel_source_hash():
+    """sha256 over the device sources (csrc/*.hip and csrc/*.h, by name, each
+    name followed by its bytes)."""
     import hashlib
-    path = os.path.join(ROOT, "block_sparse_attention_bwd_amd", "csrc", "bsa_kernels.hip")
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    csrc = os.path.join(ROOT, "block_sparse_attention_bwd_amd", "csrc")
+    h = hashlib.sha256()
+    for name in sorted(n for n in os.listdir(csrc) if n.endswith((".hip", ".h"))):
+        h.update(name.encode() + b"\0")
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def _profile_values(workload, kernel):
