@@ -157,13 +157,14 @@ class Runner:
     bsa_bwd_fp8, with bf16 gradients.
     """
 
-    def __init__(self, case, dev, o, lse, descale=None):
+    def __init__(self, case, dev, o, lse, descale=None, dq_mode=0):
         torch = _torch()
         import block_sparse_attention_bwd_amd as bsa
         self.bsa = bsa
         self.dev = dev
         self.fp8 = descale is not None
         self.descale = descale
+        self.dq_mode = dq_mode
         odt = torch.bfloat16 if self.fp8 else dev["q"].dtype
         self.dq = torch.empty(dev["q"].shape, dtype=odt, device=dev["q"].device)
         self.dk = torch.empty(dev["k"].shape, dtype=odt, device=dev["k"].device)
@@ -181,6 +182,8 @@ class Runner:
         self.args = (dev["do"], dev["q"], dev["k"], dev["v"], o, lse)
         if self.fp8:
             self.ws_size = bsa.bsa_bwd_fp8_workspace_size(*self.args, **self.kw, descale=descale)
+        elif dq_mode:
+            self.ws_size = bsa.bsa_bwd_ex_workspace_size(*self.args, **self.kw, dq_mode=dq_mode)
         else:
             self.ws_size = bsa.bsa_bwd_workspace_size(*self.args, **self.kw)
         self.ws = torch.empty(max(1, self.ws_size), dtype=torch.uint8, device=dev["q"].device)
@@ -189,6 +192,9 @@ class Runner:
         if self.fp8:
             self.bsa.bsa_bwd_fp8(*self.args, **self.kw, descale=self.descale, workspace=self.ws,
                                  workspace_size=self.ws_size, stream=stream)
+        elif self.dq_mode:
+            self.bsa.bsa_bwd_ex(*self.args, **self.kw, dq_mode=self.dq_mode, workspace=self.ws,
+                                workspace_size=self.ws_size, stream=stream)
         else:
             self.bsa.bsa_bwd(*self.args, **self.kw, workspace=self.ws, workspace_size=self.ws_size,
                              stream=stream)
@@ -487,6 +493,9 @@ def main(argv=None):
                          "through the fp8 entry points; bf16 compute and outputs")
     ap.add_argument("--op", choices=["bwd", "fwd"], default="bwd",
                     help="bwd: the backward (default); fwd: the forward that produces O and LSE")
+    ap.add_argument("--dq-mode", choices=["recompute", "atomic"], default="recompute",
+                    help="backward dQ mode (bsa_bwd_ex): recompute (the default, deterministic) or atomic "
+                         "(dS K added into an fp32 accumulator by the dK/dV kernel)")
     args = ap.parse_args(argv)
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on exactly one GPU; --gpus must be 1",
@@ -516,6 +525,12 @@ def main(argv=None):
     dev = to_device(case)
     if args.fp8:
         case.name += "_fp8"
+    dq_mode = {"recompute": 0, "atomic": 1}[args.dq_mode]
+    if dq_mode and (fwd or args.fp8):
+        print(json.dumps({"error": "--dq-mode atomic applies to the bf16/fp16 backward only"}))
+        return 2
+    if dq_mode:
+        case.name += "_dqatomic"
     if fwd:
         o = lse = None
         if args.fp8:
@@ -531,7 +546,7 @@ def main(argv=None):
             dev8, fac = quantize_inputs(dev, ("do", "q", "k", "v", "o"))
             run = Runner(case, dev8, dev8["o"], lse, descale=[fac[k] for k in ("do", "q", "k", "v", "o")])
         else:
-            run = Runner(case, dev, o, lse)
+            run = Runner(case, dev, o, lse, dq_mode=dq_mode)
     stream = torch.cuda.current_stream()
 
     for _ in range(args.warmup):
@@ -576,7 +591,8 @@ def main(argv=None):
 
     # dominant kernel: dK/dV, credited with 4 of the 5 counted block GEMMs (S, dP, dV, dK);
     # the forward kernel for --op fwd, credited with both of its GEMMs (S, PV)
-    kname, kstage, kflop = ("fwd_kernel", "fwd", 4.0) if fwd else ("dkdv_kernel", "dkdv", 8.0)
+    # (with --dq-mode atomic the dK/dV kernel also forms dS K: all five)
+    kname, kstage, kflop = ("fwd_kernel", "fwd", 4.0) if fwd else ("dkdv_kernel", "dkdv", 10.0 if dq_mode else 8.0)
     dkdv_ms = stage_ms[kstage] / max(1, ncalls)
     dkdv_flops = kflop * case.bx * case.by * case.D * blocks
     achieved = dkdv_flops / (dkdv_ms * 1e-3) / 1e12

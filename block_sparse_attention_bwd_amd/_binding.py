@@ -33,7 +33,10 @@ BSA_DTYPE_FP8_E5M2 = 6
 
 NO_WINDOW = 2147483647
 WS_REGIONS = ("seq", "delta", "lse2", "row_cnt", "row_list", "col_cnt", "col_list", "plan", "partial",
-              "amask", "stage", "total")
+              "amask", "stage", "dq_acc", "total")
+# dq_mode of bsa_bwd_ex
+BSA_DQ_RECOMPUTE = 0
+BSA_DQ_ATOMIC = 1
 
 
 class bsa_tensor(ctypes.Structure):
@@ -89,6 +92,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.bsa_bwd_workspace_layout.restype = ctypes.c_int
     lib.bsa_bwd_noalloc.argtypes = _COMMON + [ctypes.c_void_p]
     lib.bsa_bwd_noalloc.restype = ctypes.c_int
+    lib.bsa_bwd_ex_workspace_size.argtypes = _COMMON + [ctypes.c_int32, ctypes.POINTER(ctypes.c_uint64)]
+    lib.bsa_bwd_ex_workspace_size.restype = ctypes.c_int
+    lib.bsa_bwd_ex.argtypes = _COMMON + [ctypes.c_int32, ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p]
+    lib.bsa_bwd_ex.restype = ctypes.c_int
     lib.bsa_fwd_workspace_size.argtypes = _FWD + [ctypes.POINTER(ctypes.c_uint64)]
     lib.bsa_fwd_workspace_size.restype = ctypes.c_int
     lib.bsa_fwd.argtypes = _FWD + [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p]
@@ -271,6 +278,39 @@ def bsa_bwd_noalloc(dout, query, key, value, attention_out, softmax_lse, block_s
                     kv_input_layout, num_key_value_heads, mask_type, scale_value, pre_tokens,
                     next_tokens, dq, dk, dv)
     _check(lib.bsa_bwd_noalloc(*args, _launch_args(None, 0, stream)[2]))
+
+
+def bsa_bwd_ex_workspace_size(dout, query, key, value, attention_out, softmax_lse, block_sparse_mask=None,
+                              atten_mask=None, block_shape=None, actual_seq_lengths=None,
+                              actual_seq_lengths_kv=None, q_input_layout="BNSD", kv_input_layout="BNSD",
+                              num_key_value_heads=1, mask_type=0, scale_value=1.0, pre_tokens=NO_WINDOW,
+                              next_tokens=NO_WINDOW, dq=None, dk=None, dv=None, dq_mode=BSA_DQ_RECOMPUTE) -> int:
+    """Phase 1 of the backward with a dQ mode (BSA_DQ_RECOMPUTE / BSA_DQ_ATOMIC)."""
+    lib = load_library()
+    args = _marshal(dout, query, key, value, attention_out, softmax_lse, block_sparse_mask, atten_mask,
+                    block_shape, actual_seq_lengths, actual_seq_lengths_kv, q_input_layout,
+                    kv_input_layout, num_key_value_heads, mask_type, scale_value, pre_tokens,
+                    next_tokens, dq, dk, dv)
+    size = ctypes.c_uint64(0)
+    _check(lib.bsa_bwd_ex_workspace_size(*args, int(dq_mode), ctypes.byref(size)))
+    return size.value
+
+
+def bsa_bwd_ex(dout, query, key, value, attention_out, softmax_lse, block_sparse_mask=None, atten_mask=None,
+               block_shape=None, actual_seq_lengths=None, actual_seq_lengths_kv=None, q_input_layout="BNSD",
+               kv_input_layout="BNSD", num_key_value_heads=1, mask_type=0, scale_value=1.0,
+               pre_tokens=NO_WINDOW, next_tokens=NO_WINDOW, dq=None, dk=None, dv=None, dq_mode=BSA_DQ_RECOMPUTE,
+               workspace=None, workspace_size=None, stream=None) -> None:
+    """Phase 2 of the backward with a dQ mode, enqueued on ``stream``."""
+    lib = load_library()
+    _need_gpu(dout=dout, query=query, key=key, value=value, attention_out=attention_out,
+              softmax_lse=softmax_lse, block_sparse_mask=block_sparse_mask, dq=dq, dk=dk, dv=dv,
+              workspace=workspace)
+    args = _marshal(dout, query, key, value, attention_out, softmax_lse, block_sparse_mask, atten_mask,
+                    block_shape, actual_seq_lengths, actual_seq_lengths_kv, q_input_layout,
+                    kv_input_layout, num_key_value_heads, mask_type, scale_value, pre_tokens,
+                    next_tokens, dq, dk, dv)
+    _check(lib.bsa_bwd_ex(*args, int(dq_mode), *_launch_args(workspace, workspace_size, stream)))
 
 
 def bsa_fwd_workspace_size(query, key, value, block_sparse_mask=None, atten_mask=None, block_shape=None,

@@ -70,6 +70,7 @@ struct Args {
   // partial-result slots for split dK/dV units: at most this many (fewer
   // only load-balance heavy units less well; results are the same)
   int64_t max_slots = bsa::kMaxSlots;
+  int32_t dq_mode = BSA_DQ_RECOMPUTE;  // bsa_bwd_ex
 };
 
 enum Fp8Role { kRoleDout = 0, kRoleQuery, kRoleKey, kRoleValue, kRoleOut };
@@ -581,6 +582,20 @@ int make_plan(const Args& a, Plan* plan) {
       return fail(BSA_ERR_PARAM_INVALID, "fp8 inputs too large for one decode launch");
   }
   take(BSA_WS_STAGE, stage_bytes);
+  // dQ by atomic adds: the fp32 accumulator, [B, N, maxSq, D]
+  const bool dq_atomic = !a.fwd && a.dq_mode == BSA_DQ_ATOMIC;
+  if (!a.fwd && a.dq_mode != BSA_DQ_RECOMPUTE && a.dq_mode != BSA_DQ_ATOMIC)
+    return fail(BSA_ERR_PARAM_INVALID, "dq_mode %d is not BSA_DQ_RECOMPUTE (0) or BSA_DQ_ATOMIC (1)", a.dq_mode);
+  if (dq_atomic) {
+    if (a.fp8) return fail(BSA_ERR_PARAM_INVALID, "BSA_DQ_ATOMIC takes fp16/bf16 inputs");
+    if (!bsa::dkdv_scheduled(static_cast<int>(D), am, static_cast<int>(N / Nkv)))
+      return fail(BSA_ERR_PARAM_INVALID,
+                  "BSA_DQ_ATOMIC needs head dim 64 or 128, no attenMask and at most %d query heads per KV head",
+                  bsa::kDkdvMaxGroup);
+    if (B * N * ceil_div(Sq, 64) + slots > bsa::kMaxGridGroups)
+      return fail(BSA_ERR_PARAM_INVALID, "problem too large for the dQ store launch");
+  }
+  take(BSA_WS_DQ_ACC, dq_atomic ? 4ull * rows * D : 0);
   plan->off[BSA_WS_TOTAL] = off;
   p.n_units = static_cast<int32_t>(n_units);
   p.n_dq_units = static_cast<int32_t>(B * N * nqb * nsub_q);
@@ -603,7 +618,8 @@ bool plan_log_on() {
 
 void log_plan(const char* entry, const Args& a, const Plan& plan) {
   static const char* const kRegion[BSA_WS_NUM] = {"seq", "delta", "lse2", "row_cnt", "row_list", "col_cnt",
-                                                  "col_list", "plan", "partial", "amask", "stage", "total"};
+                                                  "col_list", "plan", "partial", "amask", "stage", "dq_acc",
+                                                  "total"};
   const bsa::Params& p = plan.p;
   std::fprintf(stderr, "[bsa] %s: %s B=%d N=%d Nkv=%d G=%d D=%d dtype=%s maxSq=%d block=%dx%d nQB=%d nKB=%d\n",
                entry, p.tnd ? "TND" : "BNSD", p.B, p.N, p.Nkv, p.G, p.D, a.fp8 ? "fp8->bf16" : dtype_name(p.dtype),
@@ -619,8 +635,9 @@ void log_plan(const char* entry, const Args& a, const Plan& plan) {
                  plan.seq[b].wlim_kv);
   if (plan.seq.size() > 8) std::fprintf(stderr, "[bsa]   ... %zu sequences in all\n", plan.seq.size());
   if (!a.fwd)
-    std::fprintf(stderr, "[bsa]   dK/dV units=%d (+%d split slots, %d workgroup(s) per item)  dQ workgroups=%d\n",
-                 p.n_units, p.slots_cap, bsa::dkdv_passes(p.D), p.n_dq_units);
+    std::fprintf(stderr, "[bsa]   dK/dV units=%d (+%d split slots, %d workgroup(s) per item)  dQ workgroups=%d%s\n",
+                 p.n_units, p.slots_cap, bsa::dkdv_passes(p.D), p.n_dq_units,
+                 a.dq_mode == BSA_DQ_ATOMIC ? " (dQ by atomic adds in the dK/dV kernel instead)" : "");
   else
     std::fprintf(stderr, "[bsa]   forward workgroups=%d\n", p.n_dq_units);
   for (int r = 0; r < BSA_WS_TOTAL; ++r) {
@@ -766,6 +783,7 @@ int enqueue(const Args& a, Plan& plan, char* ws, void* stream, bool allow_profil
     p.col_list = reinterpret_cast<int32_t*>(ws + plan.off[BSA_WS_COL_LIST]);
     p.plan = reinterpret_cast<int32_t*>(ws + plan.off[BSA_WS_PLAN]);
     p.partial = reinterpret_cast<float*>(ws + plan.off[BSA_WS_PARTIAL]);
+    p.dq_acc = a.dq_mode == BSA_DQ_ATOMIC ? reinterpret_cast<float*>(ws + plan.off[BSA_WS_DQ_ACC]) : nullptr;
   }
   if (p.amask) {
     p.am_rows = reinterpret_cast<uint32_t*>(ws + plan.off[BSA_WS_AMASK]);
@@ -814,6 +832,7 @@ int enqueue(const Args& a, Plan& plan, char* ws, void* stream, bool allow_profil
   }
   if (herr == 0) herr = bsa::launch_prologue(p, stream);
   if (herr == 0) herr = bsa::launch_plan(p, stream);
+  if (herr == 0 && p.dq_acc) herr = bsa::launch_dq_acc_zero(p, stream);
   if (herr) return launch_failed(herr, "prologue");
   if ((rc = mark(kStagePrologue))) return rc;
   if ((herr = bsa::launch_dkdv(p, stream))) return launch_failed(herr, "dK/dV");
@@ -889,6 +908,26 @@ int bsa_bwd_workspace_layout(BSA_ARGS_DECL, uint64_t* offsets, int64_t* dims) {
 int bsa_bwd(BSA_ARGS_DECL, void* workspace, uint64_t workspace_size, void* stream) {
   g_err.clear();
   return run(BSA_ARGS_PACK, workspace, workspace_size, stream);
+}
+
+int bsa_bwd_ex_workspace_size(BSA_ARGS_DECL, int32_t dq_mode, uint64_t* workspace_size) {
+  g_err.clear();
+  if (workspace_size == nullptr) return fail(BSA_ERR_PARAM_NULLPTR, "workspaceSize is a null pointer");
+  Plan plan;
+  Args a = BSA_ARGS_PACK;
+  a.dq_mode = dq_mode;
+  int rc = make_plan(a, &plan);
+  if (rc) return rc;
+  if (plan_log_on()) log_plan("bsa_bwd_ex_workspace_size", a, plan);
+  *workspace_size = plan.off[BSA_WS_TOTAL];
+  return BSA_OK;
+}
+
+int bsa_bwd_ex(BSA_ARGS_DECL, int32_t dq_mode, void* workspace, uint64_t workspace_size, void* stream) {
+  g_err.clear();
+  Args a = BSA_ARGS_PACK;
+  a.dq_mode = dq_mode;
+  return run(a, workspace, workspace_size, stream);
 }
 
 int bsa_bwd_noalloc(BSA_ARGS_DECL, void* stream) {

@@ -484,10 +484,21 @@ __device__ __forceinline__ void dkdv_sdp(const DkdvSliceIn<D>& in, const u16x8 (
   }
 }
 
-template <class E, int D, int W, int NSL, bool WIN>
+// dQ by atomic adds: the dS tile of one 32-row slice in LDS, [key row][query]
+// with rows of kDsPitch elements (32 queries + 4, so that the rows of one
+// transposing read and of one write spread over the banks).
+constexpr int kDsPitch = 36;
+template <int W>
+__host__ __device__ constexpr unsigned ds_slice_bytes() { return 2u * kDsPitch * 32 * W; }
+
+// DQA: also write each slice's dS (as rounded for the dK product) to the dS
+// region at byte address ds_wr (this lane's key row and query quad; slice sl
+// at + sl * ds_slice_bytes), zero for keys past the sequence end.
+template <class E, int D, int W, int NSL, bool WIN, bool DQA>
 __device__ __forceinline__ void dkdv_pipe_tile(const DkdvAddr<D, W, NSL>& ad, const u16x8 (&kreg)[D / 16],
                                                const u16x8 (&vreg)[D / 16], f32x16 (&adv)[D / 32],
-                                               f32x16 (&adk)[D / 32], float c2, const uint32_t (&keep)[NSL]) {
+                                               f32x16 (&adk)[D / 32], float c2, const uint32_t (&keep)[NSL],
+                                               unsigned ds_wr, bool kv_ok) {
   using T = DkdvPipe<D, W, NSL>;
   constexpr int KS = T::KS, NT = T::NT;
   constexpr unsigned TB = T::TB;
@@ -523,6 +534,19 @@ __device__ __forceinline__ void dkdv_pipe_tile(const DkdvAddr<D, W, NSL>& ad, co
     }
     const u16x8 pa[2] = {pack8<E>(pv), pack8<E>(pv + 8)};
     const u16x8 da[2] = {pack8<E>(dsv), pack8<E>(dsv + 8)};
+    if constexpr (DQA) {
+      // registers 8hh..8hh+3 hold query rows 16hh + 4g + {0..3}, the next four
+      // rows 16hh + 8 + 4g + {0..3}: two 8-byte writes per half
+      typedef __attribute__((address_space(3))) u16x4 lds_u16x4;
+      const u16x8 z = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const u16x8 v = kv_ok ? da[hh] : z;
+        const unsigned a = ds_wr + sl * ds_slice_bytes<W>() + 32u * hh;
+        *(lds_u16x4*)(static_cast<uintptr_t>(a)) = u16x4{v[0], v[1], v[2], v[3]};
+        *(lds_u16x4*)(static_cast<uintptr_t>(a + 16u)) = u16x4{v[4], v[5], v[6], v[7]};
+      }
+    }
     u16x4 bo[2][NT][2], bq[2][NT][2];
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh)
@@ -563,6 +587,46 @@ __device__ __forceinline__ void dkdv_pipe_tile(const DkdvAddr<D, W, NSL>& ad, co
   }
 }
 
+// dQ by atomic adds, for one finished tile (its dS region written by every
+// wave, the barrier after the tile passed): wave w takes the head-dim stripes
+// nt = w, w + W, ... of 32 columns; per 32-row slice, dQ[q][d] = sum over the
+// item's 32 W keys of dS[q][key] K[key][d], with dS from the tile's region
+// and K from the item's K rows in LDS (tile layout), both read down their key
+// rows in the same order; each lane then adds its 16 results into dq_acc
+// (row base `row0` of (batch, query head)), a 128-byte run of one row per
+// half-wave and register.  Rows from qend on are not added.
+template <class E, int D, int W, int NSL>
+__device__ __forceinline__ void dkdv_dq_tile(const Params& p, unsigned kt, unsigned ds, int64_t row0, int q0,
+                                             int qend) {
+  constexpr int NT = D / 32;
+  constexpr unsigned DS_ROW = 2u * kDsPitch;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, l32 = lane & 31, g = lane >> 5;
+  const int rr = 4 * g + ((lane & 15) >> 2);
+  const int col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+#pragma unroll
+  for (int sl = 0; sl < NSL; ++sl) {
+    if (q0 + 32 * sl >= qend) break;  // uniform
+    const unsigned dsl = ds + sl * ds_slice_bytes<W>() + rr * DS_ROW + 2u * col;
+#pragma unroll
+    for (int nt = w; nt < NT; nt += W) {
+      f32x16 c = {};
+#pragma unroll
+      for (int kk = 0; kk < 2 * W; ++kk) {
+        const u16x8 a = cat8(lds_tr(dsl + 16u * kk * DS_ROW), lds_tr(dsl + (16u * kk + 8u) * DS_ROW));
+        const u16x8 b = cat8(lds_tr(kt + 2u * tile_off<D>(16 * kk + rr, 32 * nt + col)),
+                             lds_tr(kt + 2u * tile_off<D>(16 * kk + rr + 8, 32 * nt + col)));
+        c = E::mma(a, b, c);  // dQ[q][d] (unscaled): lane's column d = 32 nt + l32
+      }
+      float* dst = p.dq_acc + (row0 + q0 + 32 * sl) * D + 32 * nt + l32;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int q = 8 * (i >> 2) + 4 * g + (i & 3);
+        if (q0 + 32 * sl + q < qend) unsafeAtomicAdd(dst + static_cast<int64_t>(q) * D, c[i]);
+      }
+    }
+  }
+}
+
 // A dK/dV work item's share of the merged list (the group's query heads in
 // order, each with its ascending list of Q blocks selecting the item's KV
 // block) is copied into LDS once, with every load in flight together, so that
@@ -570,7 +634,6 @@ __device__ __forceinline__ void dkdv_pipe_tile(const DkdvAddr<D, W, NSL>& ad, co
 // of the group, Q block).  Holds up to kDkdvListChunk entries at a time; longer
 // items refill it between tiles.
 constexpr int kDkdvListChunk = 1024;
-constexpr int kDkdvMaxGroup = 256;  // heads per KV head (the counts sit in LDS too)
 struct DkdvList {
   int* ib;             // [kDkdvListChunk]
   unsigned short* n;   // [kDkdvListChunk]
@@ -671,11 +734,15 @@ __device__ __forceinline__ void dkdv_store_staged(const Params& p, int u, int pi
   }
 }
 
-template <class E, int D, int W, int NSL, bool WIN>
+// DQA: dQ by atomic adds (Params::dq_acc); the item's K rows are copied into
+// LDS too, and every finished tile's dQ is added into dq_acc (dkdv_dq_tile)
+// at the start of the next tile, after that tile's copies are issued.
+template <class E, int D, int W, int NSL, bool WIN, bool DQA>
 __global__ __launch_bounds__(64 * W) void dkdv_pipe_kernel(Params p) {
   using T = DkdvPipe<D, W, NSL>;
   constexpr int KS = T::KS, NT = T::NT, H = T::H, RW = T::RW;
   constexpr unsigned TB = T::TB, BUF = T::BUF;
+  static_assert(!DQA || NSL <= 2, "with dQ by atomics the LDS holds at most two slices per tile");
   // Q / dO tiles of buffer b at byte 2 b TB (swizzled rows); per buffer the
   // LSE*log2e rows, then the -softmax_grad rows
   __shared__ __align__(1024) unsigned short sT[2 * 2 * H * D];
@@ -683,6 +750,9 @@ __global__ __launch_bounds__(64 * W) void dkdv_pipe_kernel(Params p) {
   __shared__ int sListIb[kDkdvListChunk], sListCnt[kDkdvMaxGroup];
   __shared__ unsigned short sListN[kDkdvListChunk];
   __shared__ int sItem;
+  // DQA: the item's K rows (tile layout), and per buffer the tile's dS slices
+  __shared__ __align__(1024) unsigned short sKt[DQA ? 32 * W * D : 8];
+  __shared__ __align__(16) unsigned short sDS[DQA ? 2 * NSL * 32 * W * kDsPitch : 8];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6, l32 = lane & 31, g = lane >> 5;
@@ -804,6 +874,23 @@ __global__ __launch_bounds__(64 * W) void dkdv_pipe_kernel(Params p) {
       vreg[s] = zv;
     }
   };
+  // DQA: the item's 32 W K rows into sKt by DMA, each wave its own 32 rows;
+  // rows past the sequence end copy a chunk of the item's first row (finite;
+  // their dS is written as zero)
+  constexpr int NCK = 32 / RPI;  // copies per wave
+  const unsigned kt0 = lds_addr(sKt), ds0 = lds_addr(sDS);
+  auto load_kt = [&](const Item& it) {
+    const unsigned short* kp = static_cast<const unsigned short*>(p.k) + it.b * p.kv_sb +
+                               (it.si.off_kv + it.kv0) * p.kv_sr + it.h * p.kv_sh;
+#pragma unroll
+    for (int i = 0; i < NCK; ++i) {
+      const int ins = w * NCK + i;
+      const int r = ins * RPI + lrow;
+      const int c = (lane % (D / 8)) ^ swz<D>(r);
+      const unsigned v = static_cast<unsigned>(2 * (r * p.kv_sr + 8 * c));
+      dma16s(kp, it.kv0 + r < it.kv_end ? v : vz, kt0 + 1024u * ins);
+    }
+  };
   // start an item: its list, its first tile's copies into buffer 0, its K/V rows
   auto start = [&](const Item& it, QTile& first) {
     list_start(it);
@@ -811,6 +898,7 @@ __global__ __launch_bounds__(64 * W) void dkdv_pipe_kernel(Params p) {
       first = tile_of(it, 0);
       issue(it, first, 0);
     }
+    if constexpr (DQA) load_kt(it);
     load_kv(it);
   };
 
@@ -849,6 +937,11 @@ __global__ __launch_bounds__(64 * W) void dkdv_pipe_kernel(Params p) {
     __syncthreads();  // the first tile landed for every wave
     const int my_kv = cur_it.kv0 + 32 * w + l32;
     bool have = lst.count > 0;
+    // DQA: this lane's dS writes (its key row, its query quad) in buffer 0's region
+    const unsigned ds_wr = ds0 + (32u * w + l32) * 2u * kDsPitch + 8u * g;
+    constexpr unsigned DSB = NSL * ds_slice_bytes<W>();  // one buffer's dS region
+    QTile prev{};
+    bool have_prev = false;
     for (int buf = 0; have; buf ^= 1) {
       QTile nxt = cur;
       nxt.q0 += H;
@@ -863,7 +956,12 @@ __global__ __launch_bounds__(64 * W) void dkdv_pipe_kernel(Params p) {
       uint32_t keep[NSL];
 #pragma unroll
       for (int sl = 0; sl < NSL; ++sl) keep[sl] = WIN ? band_rows(p, cur.q0 + 32 * sl, my_kv) >> (4 * g) : 0u;
-      dkdv_pipe_tile<E, D, W, NSL, WIN>(ad, kreg, vreg, adv, adk, c2, keep);
+      if constexpr (DQA)  // the previous tile's dQ, its dS region complete since the last barrier
+        if (have_prev)
+          dkdv_dq_tile<E, D, W, NSL>(p, kt0, ds0 + (buf ^ 1) * DSB, (cur_it.bn0 + prev.n) * p.sq_max, prev.q0,
+                                     prev.qend);
+      dkdv_pipe_tile<E, D, W, NSL, WIN, DQA>(ad, kreg, vreg, adv, adk, c2, keep, ds_wr + buf * DSB,
+                                             my_kv < cur_it.kv_end);
       wait_vmcnt<0>();  // this wave's copies of the next tile
       __syncthreads();  // everyone's copies landed; everyone is done with this tile
       const unsigned flip = buf ? 0u - BUF : BUF;  // the next tile sits in the other buffer
@@ -875,8 +973,13 @@ __global__ __launch_bounds__(64 * W) void dkdv_pipe_kernel(Params p) {
         ad.b[nt][1] += flip;
       }
       ad.l += buf ? 0u - 8u * H : 8u * H;
+      prev = cur;
+      have_prev = true;
       cur = nxt;
       have = more;
+      if constexpr (DQA)  // the last tile's dQ (buffer buf ^ 1 after the flip below is this one's)
+        if (!have) dkdv_dq_tile<E, D, W, NSL>(p, kt0, ds0 + buf * DSB, (cur_it.bn0 + prev.n) * p.sq_max, prev.q0,
+                                              prev.qend);
     }
     // the next item starts before this one's stores are issued
     Item nx_it{};
@@ -915,25 +1018,46 @@ __global__ __launch_bounds__(256) void dkdv_kernel(Params p) {
 
 // The scheduled dK/dV build: fp16/bf16 at head dim 64 or 128 without an
 // attenMask; persistent, as many workgroups as run at once (one wave per SIMD:
-// 4 / W workgroups per compute unit), or fewer if there are fewer work items.
-template <class E, int D, int W, int NSL>
+// 4 / W workgroups per compute unit, fewer where the LDS of the dQ-by-atomics
+// build does not fit that many), or fewer if there are fewer work items.
+template <class E, int D, int W, int NSL, bool DQA>
 void launch_dkdv_pipe(const Params& p, dim3 items, hipStream_t s) {
-  const dim3 grid(static_cast<unsigned>(std::min<int64_t>(items.x, static_cast<int64_t>(device_cus()) * (4 / W))));
-  if (p.win) hipLaunchKernelGGL((dkdv_pipe_kernel<E, D, W, NSL, true>), grid, dim3(64 * W), 0, s, p);
-  else hipLaunchKernelGGL((dkdv_pipe_kernel<E, D, W, NSL, false>), grid, dim3(64 * W), 0, s, p);
+  int per_cu = 4 / W;
+  if constexpr (DQA) {
+    static int fit = 0;  // workgroups of this build per compute unit (looked up once)
+    if (fit == 0) {
+      int n = 0;
+      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, dkdv_pipe_kernel<E, D, W, NSL, false, true>, 64 * W, 0) !=
+              hipSuccess ||
+          n <= 0) {
+        (void)hipGetLastError();
+        n = 1;
+      }
+      fit = n;
+    }
+    per_cu = std::min(per_cu, fit);
+  }
+  const dim3 grid(static_cast<unsigned>(std::min<int64_t>(items.x, static_cast<int64_t>(device_cus()) * per_cu)));
+  if (p.win) hipLaunchKernelGGL((dkdv_pipe_kernel<E, D, W, NSL, true, DQA>), grid, dim3(64 * W), 0, s, p);
+  else hipLaunchKernelGGL((dkdv_pipe_kernel<E, D, W, NSL, false, DQA>), grid, dim3(64 * W), 0, s, p);
 }
-template <class E, int D>
+template <class E, int D, bool DQA>
 void launch_dkdv_pipe_w(const Params& p, int w, dim3 grid, hipStream_t s) {
-  const int nsl = dkdv_pipe_nsl(p.bx, w);
+  int nsl = dkdv_pipe_nsl(p.bx, w);
+  if (DQA && nsl > 2) nsl = 2;  // the dS and K regions take the LDS of two slices
   if (w == 4) {
-    if (nsl == 4) launch_dkdv_pipe<E, D, 4, 4>(p, grid, s);
-    else if (nsl == 2) launch_dkdv_pipe<E, D, 4, 2>(p, grid, s);
-    else launch_dkdv_pipe<E, D, 4, 1>(p, grid, s);
+    if (nsl == 4) {
+      if constexpr (!DQA) launch_dkdv_pipe<E, D, 4, 4, DQA>(p, grid, s);
+    } else if (nsl == 2) {
+      launch_dkdv_pipe<E, D, 4, 2, DQA>(p, grid, s);
+    } else {
+      launch_dkdv_pipe<E, D, 4, 1, DQA>(p, grid, s);
+    }
   } else if (w == 2) {
-    if (nsl == 2) launch_dkdv_pipe<E, D, 2, 2>(p, grid, s);
-    else launch_dkdv_pipe<E, D, 2, 1>(p, grid, s);
+    if (nsl == 2) launch_dkdv_pipe<E, D, 2, 2, DQA>(p, grid, s);
+    else launch_dkdv_pipe<E, D, 2, 1, DQA>(p, grid, s);
   } else {
-    launch_dkdv_pipe<E, D, 1, 1>(p, grid, s);
+    launch_dkdv_pipe<E, D, 1, 1, DQA>(p, grid, s);
   }
 }
 

@@ -19,7 +19,7 @@ int device_cus() {
 int launch_dkdv(const Params& p, void* stream) {
   const dim3 grid(static_cast<unsigned>(dkdv_passes(p.D) * (p.n_units + p.slots_cap)));
   const hipStream_t s = static_cast<hipStream_t>(stream);
-  if (p.amask == nullptr && p.D <= 128 && p.G <= kDkdvMaxGroup) {
+  if (dkdv_scheduled(p.D, p.amask != nullptr, p.G)) {
     if (p.dtype == 2) return p.D == 128 ? launch_dkdv_pipe_bf16_d128(p, grid, s) : launch_dkdv_pipe_bf16_d64(p, grid, s);
     return p.D == 128 ? launch_dkdv_pipe_f16_d128(p, grid, s) : launch_dkdv_pipe_f16_d64(p, grid, s);
   }

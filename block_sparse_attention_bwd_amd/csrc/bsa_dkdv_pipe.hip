@@ -20,7 +20,8 @@
 namespace bsa {
 
 int BSA_PIPE_FN(const Params& p, dim3 grid, hipStream_t s) {
-  launch_dkdv_pipe_w<BSA_PIPE_E, BSA_PIPE_D>(p, waves_for(p.by), grid, s);
+  if (p.dq_acc) launch_dkdv_pipe_w<BSA_PIPE_E, BSA_PIPE_D, true>(p, waves_for(p.by), grid, s);
+  else launch_dkdv_pipe_w<BSA_PIPE_E, BSA_PIPE_D, false>(p, waves_for(p.by), grid, s);
   return static_cast<int>(hipGetLastError());
 }
 

@@ -229,9 +229,73 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(D >= 256
   }
 }
 
+// ---------------------------------------------------------------------------
+// dQ by atomic adds (bsa_bwd_ex with BSA_DQ_ATOMIC)
+// ---------------------------------------------------------------------------
+// dq_acc = 0 before the dK/dV kernel adds into it (a fill kernel, so the call
+// records no memset).
+__global__ __launch_bounds__(256) void dq_acc_zero_kernel(float4* acc, int64_t n4) {
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < n4;
+       i += static_cast<int64_t>(gridDim.x) * 256)
+    acc[i] = float4{0.f, 0.f, 0.f, 0.f};
+}
+
+// dQ = dq_acc * dq_scale rounded to the element type, one workgroup per 64
+// positions of one (batch, query head), every row the call writes (rows past
+// the sequence end hold zeros in dq_acc); the workgroups after the first
+// n_runs sum the pieces of split dK/dV units, as in the recompute launch.
+template <class E, int D>
+__global__ __launch_bounds__(256) void dq_acc_store_kernel(Params p, int n_runs) {
+  if (static_cast<int>(blockIdx.x) >= n_runs) {
+    reduce_pieces<E, D>(p, blockIdx.x - n_runs);
+    return;
+  }
+  const int runs = (p.sq_max + 63) / 64;
+  const int bn = blockIdx.x / runs;
+  const int r0 = (blockIdx.x % runs) * 64;
+  const int b = bn / p.N, n = bn % p.N;
+  const SeqInfo si = p.seq[b];
+  const int r1 = min(r0 + 64, si.wlim_q);
+  constexpr int CH = D / 8;  // 8-element chunks per row
+  unsigned short* dq = static_cast<unsigned short*>(p.dq) + b * p.dq_sb + si.off_q * p.dq_sr + n * p.dq_sh;
+  const float* acc = p.dq_acc + static_cast<int64_t>(bn) * p.sq_max * D;
+  for (int i = threadIdx.x; i < (r1 - r0) * CH; i += 256) {
+    const int r = r0 + i / CH, c = 8 * (i % CH);
+    const float4 x = *reinterpret_cast<const float4*>(acc + static_cast<int64_t>(r) * D + c);
+    const float4 y = *reinterpret_cast<const float4*>(acc + static_cast<int64_t>(r) * D + c + 4);
+    const float lo[4] = {x.x * p.dq_scale, x.y * p.dq_scale, x.z * p.dq_scale, x.w * p.dq_scale};
+    const float hi[4] = {y.x * p.dq_scale, y.y * p.dq_scale, y.z * p.dq_scale, y.w * p.dq_scale};
+    store4<E>(dq + r * p.dq_sr + c, lo);
+    store4<E>(dq + r * p.dq_sr + c + 4, hi);
+  }
+}
+
 }  // namespace
 
+int launch_dq_acc_zero(const Params& p, void* stream) {
+  const int64_t n4 = static_cast<int64_t>(p.B) * p.N * p.sq_max * p.D / 4;
+  const int64_t blocks = std::min<int64_t>((n4 + 255) / 256, 8192);
+  if (blocks == 0) return 0;
+  hipLaunchKernelGGL(dq_acc_zero_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0,
+                     static_cast<hipStream_t>(stream), reinterpret_cast<float4*>(p.dq_acc), n4);
+  return static_cast<int>(hipGetLastError());
+}
+
 int launch_dq(const Params& p, void* stream) {
+  if (p.dq_acc) {  // dQ by atomic adds: scale and store the accumulator
+    const int n_runs = p.B * p.N * ((p.sq_max + 63) / 64);
+    const dim3 grid(static_cast<unsigned>(n_runs + p.slots_cap));
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    const bool bf = p.dtype == 2;
+    if (p.D == 128) {
+      if (bf) hipLaunchKernelGGL((dq_acc_store_kernel<EBf16, 128>), grid, dim3(256), 0, s, p, n_runs);
+      else hipLaunchKernelGGL((dq_acc_store_kernel<EF16, 128>), grid, dim3(256), 0, s, p, n_runs);
+    } else {
+      if (bf) hipLaunchKernelGGL((dq_acc_store_kernel<EBf16, 64>), grid, dim3(256), 0, s, p, n_runs);
+      else hipLaunchKernelGGL((dq_acc_store_kernel<EF16, 64>), grid, dim3(256), 0, s, p, n_runs);
+    }
+    return static_cast<int>(hipGetLastError());
+  }
   const dim3 grid(static_cast<unsigned>(p.n_dq_units + p.slots_cap));
   BSA_DISPATCH(dq_kernel, waves_for(p.bx), grid, static_cast<hipStream_t>(stream), p);
   return static_cast<int>(hipGetLastError());

@@ -88,6 +88,10 @@ struct Params {
                        // order_unit[n_units + slots_cap], order_piece[n_units + slots_cap],
                        // dq_order[n_dq_units]
   float* partial;      // [slots_cap][2][kTileRowsMax][D] fp32 (dK unscaled, dV)
+  // dQ by atomic adds (bsa_bwd_ex with BSA_DQ_ATOMIC; nullptr otherwise): fp32
+  // [B][N][sq_max][D] of unscaled dS K sums, zeroed before the dK/dV kernel
+  // adds into it and scaled, rounded and stored by the dQ launch
+  float* dq_acc;
 };
 
 // Work-split parameters: a unit with more than `chunk` selecting Q blocks is
@@ -109,6 +113,11 @@ constexpr int kBalanceGroups = 256;
 // in one wave's registers).
 inline constexpr int dkdv_passes(int D) { return D >= 256 ? 2 : 1; }
 constexpr int kMinChunk = 4;
+// The scheduled dK/dV build runs calls with head dim <= 128, no attenMask and
+// at most kDkdvMaxGroup query heads per KV head (the group's list counts sit
+// in LDS); the generic build runs the rest.
+constexpr int kDkdvMaxGroup = 256;
+inline constexpr bool dkdv_scheduled(int D, bool amask, int G) { return D <= 128 && !amask && G <= kDkdvMaxGroup; }
 constexpr int kMaxSlots = 2 * kBalanceGroups;
 
 // Launch-grid limits.  A dispatch counts work-items in 32 bits, so a grid of
@@ -169,6 +178,7 @@ int launch_prologue_rows(const Params& p, void* stream);  // row lists only (the
 int launch_fwd(const Params& p, void* stream);
 int launch_dkdv(const Params& p, void* stream);
 int launch_dq(const Params& p, void* stream);  // also sums the pieces of split dK/dV units
+int launch_dq_acc_zero(const Params& p, void* stream);  // dq_acc = 0 (atomic dQ mode)
 
 // The library's own device scratch array, used as the workspace of the entry
 // point that allocates nothing: its address on the current device (looked up

@@ -194,6 +194,50 @@ int bsa_bwd_noalloc(const bsa_tensor* dout, const bsa_tensor* query, const bsa_t
                     const bsa_tensor* dk, const bsa_tensor* dv, void* stream);
 
 /*
+ * The backward with a choice of how dQ is formed (dq_mode).  Arguments and
+ * results otherwise as bsa_bwd_workspace_size / bsa_bwd.
+ *
+ * BSA_DQ_RECOMPUTE  the dQ kernel recomputes S and dP for every selected block
+ *                   and forms dQ = (dS K) scale ([BSA] page, 功能说明 / 计算公式)
+ *                   with no atomics: the mode of bsa_bwd, bitwise reproducible.
+ * BSA_DQ_ATOMIC     opt-in: the dK/dV kernel, which already holds dS rounded to
+ *                   the input dtype, also multiplies it by its KV block's K and
+ *                   adds the product into an fp32 accumulator in the workspace
+ *                   with atomic adds; a last kernel applies scale, rounds and
+ *                   stores dQ.  No recompute, but the order of the fp32
+ *                   additions into a dQ element depends on scheduling, so dQ is
+ *                   not bitwise reproducible (dK and dV still are).  Head dim 64
+ *                   or 128, no attenMask, at most 256 query heads per KV head;
+ *                   other calls return 161002.  The workspace grows by
+ *                   4 * B * N * maxSq * D bytes (BSA_WS_DQ_ACC).
+ *
+ * Any other dq_mode returns 161002.
+ */
+#define BSA_DQ_RECOMPUTE 0
+#define BSA_DQ_ATOMIC 1
+int bsa_bwd_ex_workspace_size(const bsa_tensor* dout, const bsa_tensor* query, const bsa_tensor* key,
+                              const bsa_tensor* value, const bsa_tensor* attention_out,
+                              const bsa_tensor* softmax_lse, const bsa_tensor* block_sparse_mask,
+                              const bsa_tensor* atten_mask, const int64_t* block_shape, int64_t block_shape_len,
+                              const int64_t* actual_seq_lengths, int64_t actual_seq_lengths_len,
+                              const int64_t* actual_seq_lengths_kv, int64_t actual_seq_lengths_kv_len,
+                              const char* q_input_layout, const char* kv_input_layout,
+                              int64_t num_key_value_heads, int64_t mask_type, double scale_value,
+                              int64_t pre_tokens, int64_t next_tokens, const bsa_tensor* dq,
+                              const bsa_tensor* dk, const bsa_tensor* dv, int32_t dq_mode,
+                              uint64_t* workspace_size);
+int bsa_bwd_ex(const bsa_tensor* dout, const bsa_tensor* query, const bsa_tensor* key,
+               const bsa_tensor* value, const bsa_tensor* attention_out, const bsa_tensor* softmax_lse,
+               const bsa_tensor* block_sparse_mask, const bsa_tensor* atten_mask,
+               const int64_t* block_shape, int64_t block_shape_len, const int64_t* actual_seq_lengths,
+               int64_t actual_seq_lengths_len, const int64_t* actual_seq_lengths_kv,
+               int64_t actual_seq_lengths_kv_len, const char* q_input_layout,
+               const char* kv_input_layout, int64_t num_key_value_heads, int64_t mask_type,
+               double scale_value, int64_t pre_tokens, int64_t next_tokens, const bsa_tensor* dq,
+               const bsa_tensor* dk, const bsa_tensor* dv, int32_t dq_mode, void* workspace,
+               uint64_t workspace_size, void* stream);
+
+/*
  * Forward (the operation the backward differentiates; aclnnBlockSparseAttentionGrad
  * page, 计算公式: S = Mask(scale * Q * K^T), P = Softmax(S), Out = P * V, with the
  * softmax taken over the selected blocks only, as the FlashAttentionScore page's
@@ -322,8 +366,9 @@ enum bsa_ws_region {
   BSA_WS_AMASK = 9,    /* with an attenMask (else empty): uint32 [maxSq][ceil(maxSkv/32)] bits by query row,
                           then (backward) uint32 [maxSkv][ceil(maxSq/32)] bits by key; 1 = excluded */
   BSA_WS_STAGE = 10,   /* fp8 entry points only (else empty): bf16 copies of the fp8 inputs, each 256-byte aligned */
-  BSA_WS_TOTAL = 11,   /* total bytes (== the phase-1 size) */
-  BSA_WS_NUM = 12
+  BSA_WS_DQ_ACC = 11,  /* BSA_DQ_ATOMIC only (else empty): fp32 [B, N, maxSq, D] dQ accumulator (unscaled) */
+  BSA_WS_TOTAL = 12,   /* total bytes (== the phase-1 size) */
+  BSA_WS_NUM = 13
 };
 
 /*

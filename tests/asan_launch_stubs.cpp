@@ -15,5 +15,6 @@ int launch_prologue_rows(const Params&, void*) { return kNoKernels; }
 int launch_fwd(const Params&, void*) { return kNoKernels; }
 int launch_dkdv(const Params&, void*) { return kNoKernels; }
 int launch_dq(const Params&, void*) { return kNoKernels; }
+int launch_dq_acc_zero(const Params&, void*) { return kNoKernels; }
 int scratch_region(void**, uint64_t*) { return kNoKernels; }
 }  // namespace bsa

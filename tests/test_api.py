@@ -416,3 +416,46 @@ def test_plan_dump_with_bsa_log():
     r = subprocess.run([sys.executable, "-c", code], env=dict(os.environ, BSA_LOG="0"), capture_output=True,
                        text=True, timeout=120)
     assert r.returncode == 0 and "[bsa]" not in r.stderr
+
+
+# ---- dq_mode of bsa_bwd_ex ----------------------------------------------------
+
+def _ex_code(args, mode):
+    try:
+        bsa.bsa_bwd_ex_workspace_size(**args, dq_mode=mode)
+    except bsa.BsaError as e:
+        return e.code
+    return bsa.BSA_OK
+
+
+def test_dq_mode_recompute_is_the_plain_call():
+    for make in (_bnsd, _tnd):
+        a = make()
+        assert bsa.bsa_bwd_ex_workspace_size(**a, dq_mode=bsa.BSA_DQ_RECOMPUTE) == bsa.bsa_bwd_workspace_size(**a)
+
+
+def test_dq_mode_atomic_adds_the_accumulator():
+    """The accumulator is fp32 [B, N, maxSq, D]; nothing else changes."""
+    for make, (B, N, Sq, D) in ((_bnsd, (2, 4, 300, 128)), (_tnd, (3, 4, 250, 64))):
+        a = make()
+        plain = bsa.bsa_bwd_workspace_size(**a)
+        atomic = bsa.bsa_bwd_ex_workspace_size(**a, dq_mode=bsa.BSA_DQ_ATOMIC)
+        acc = 4 * B * N * Sq * D
+        assert atomic - plain == -(-acc // 256) * 256
+
+
+def test_dq_mode_rejections():
+    ok = _bnsd()
+    assert _ex_code(ok, bsa.BSA_DQ_ATOMIC) == bsa.BSA_OK
+    assert _ex_code(ok, 2) == bsa.BSA_ERR_PARAM_INVALID
+    assert _ex_code(ok, -1) == bsa.BSA_ERR_PARAM_INVALID
+    # head dim 256: the generic dK/dV build, which has no dQ product
+    assert _ex_code(_bnsd(D=256), bsa.BSA_DQ_ATOMIC) == bsa.BSA_ERR_PARAM_INVALID
+    assert _ex_code(_bnsd(D=256), bsa.BSA_DQ_RECOMPUTE) == bsa.BSA_OK
+    # an attenMask: likewise
+    am = _bnsd()
+    am["atten_mask"] = torch.zeros(300, 270, dtype=torch.bool)
+    assert _ex_code(am, bsa.BSA_DQ_ATOMIC) == bsa.BSA_ERR_PARAM_INVALID
+    assert _ex_code(am, bsa.BSA_DQ_RECOMPUTE) == bsa.BSA_OK
+    msg = bsa.bsa_last_error()
+    assert msg == ""
