@@ -523,6 +523,12 @@ int make_plan(const Args& a, Plan* plan) {
     oq += lq[b];
     ok += lk[b];
   }
+  // one record for every sequence: no table to stage
+  p.seq_uniform = !tnd && std::all_of(plan->seq.begin(), plan->seq.end(), [&](const bsa::SeqInfo& s) {
+    return s.len_q == Sq && s.len_kv == Skv;
+  });
+  p.seq0 = bsa::SeqInfo{0, 0, static_cast<int32_t>(Sq), static_cast<int32_t>(Skv), static_cast<int32_t>(Sq),
+                        static_cast<int32_t>(Skv)};
 
   // workspace regions (sizes from shapes, block shape and lengths only)
   uint64_t off = 0;
@@ -815,12 +821,13 @@ int enqueue(const Args& a, Plan& plan, char* ws, void* stream, bool allow_profil
     }
     if ((herr = bsa::launch_stage_fp8(st, stream))) return launch_failed(herr, "fp8 decode");
   }
-  for (size_t first = 0; first < plan.seq.size() && herr == 0; first += bsa::kMaxInlineSeq) {
+  // the sequence table (not needed when every sequence has the same record)
+  for (size_t first = 0; !p.seq_uniform && first < plan.seq.size() && herr == 0; first += bsa::kMaxInlineSeq) {
     bsa::SeqChunk chunk{};
     chunk.first = static_cast<int32_t>(first);
     chunk.count = static_cast<int32_t>(std::min<size_t>(bsa::kMaxInlineSeq, plan.seq.size() - first));
     for (int i = 0; i < chunk.count; ++i) chunk.s[i] = plan.seq[first + i];
-    herr = bsa::launch_stage_seq(chunk, p.seq, consts, stream);
+    herr = bsa::launch_stage_seq(chunk, p.seq, stream);
   }
   if (herr == 0 && p.amask) herr = bsa::launch_pack_amask(p, stream);
   if (a.fwd) {

@@ -116,6 +116,9 @@ __device__ __forceinline__ void store4(unsigned short* dst, const float (&x)[4])
   }
 }
 
+// The record of sequence b (offsets, lengths, rows written).
+__device__ __forceinline__ SeqInfo seq_of(const Params& p, int b) { return p.seq_uniform ? p.seq0 : p.seq[b]; }
+
 // The sliding window (preTokens / nextTokens): key position j takes part for
 // query position i only if i - pre <= j <= i + next.  Positions are below
 // 2^31, so j - i fits in 32 bits; pre and next are clamped on the host.
@@ -244,10 +247,17 @@ struct Slice {
   int nrows;  // valid rows, 0..32
 };
 
-// The LDS-DMA loads read m0 for their destination, and an SALU write of m0
-// needs one wait state before such a load reads it (a gfx9 hazard the
-// compiler observes for its own code but cannot see inside inline assembly):
-// hence the s_nop between the two.
+// Wait states inside the copy helpers (gfx9 hazards that the compiler observes
+// for its own code but cannot see inside inline assembly):
+//  - the LDS-DMA loads read m0 for their destination, and an SALU write of m0
+//    needs one wait state before such a load reads it;
+//  - a vector memory instruction that reads an SGPR written by a VALU
+//    instruction needs five wait states in between.  The wave-uniform base of
+//    dma16s often comes from v_readfirstlane (a VALU write of the SGPR pair)
+//    placed by the compiler right before the asm block, so the block waits
+//    five states (s_nop 4) after the m0 write before the load reads the base.
+//    Without them the load may address from a stale base (a copy of other
+//    rows); the compiled kernels are checked for this by tests/test_isa_hazards.py.
 //
 // Direct global -> LDS copy (global_load_lds_dwordx4): lane L's 16 bytes,
 // read from a wave-uniform base (held in an SGPR pair) plus a per-lane 32-bit
@@ -271,7 +281,7 @@ __device__ __forceinline__ void dma16s(const void* base, unsigned voff, unsigned
   const unsigned lo = static_cast<unsigned>(__builtin_amdgcn_readfirstlane(static_cast<unsigned>(bp)));
   const unsigned hi = static_cast<unsigned>(__builtin_amdgcn_readfirstlane(static_cast<unsigned>(bp >> 32)));
   const uint64_t sb = (static_cast<uint64_t>(hi) << 32) | lo;
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(voff), "s"(sb), "s"(m)
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 4\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(voff), "s"(sb), "s"(m)
                : "memory", "m0");
 }
 __device__ __forceinline__ void dma4(const void* src, unsigned lds) {  // lane L's 4 bytes -> m0 + 4 L

@@ -187,7 +187,7 @@ __device__ __forceinline__ void dkdv_work(const Params& p, int item, unsigned sh
   wid /= p.nkb;
   const int h = wid % p.Nkv;
   const int b = wid / p.Nkv;
-  const SeqInfo si = p.seq[b];
+  const SeqInfo si = seq_of(p, b);
   const int kv0 = jb * p.by + sub * kTileRows;
   const int part_end = min(jb * p.by + p.by, kv0 + kTileRows);
   const int kv_end = min(part_end, si.len_kv);  // rows that take part
@@ -784,7 +784,7 @@ __global__ __launch_bounds__(64 * W) void dkdv_pipe_kernel(Params p) {
     wid /= p.nkb;
     it.h = wid % p.Nkv;
     it.b = wid / p.Nkv;
-    it.si = p.seq[it.b];
+    it.si = seq_of(p, it.b);
     it.kv0 = it.jb * p.by + sub * kTileRows;
     const int part_end = min(it.jb * p.by + p.by, it.kv0 + kTileRows);
     it.kv_end = min(part_end, it.si.len_kv);

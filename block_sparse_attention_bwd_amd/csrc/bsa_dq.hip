@@ -23,7 +23,7 @@ __device__ void reduce_pieces(const Params& p, int s) {
   wid /= p.nkb;
   const int h = wid % p.Nkv;
   const int b = wid / p.Nkv;
-  const SeqInfo si = p.seq[b];
+  const SeqInfo si = seq_of(p, b);
   const int kv0 = jb * p.by + sub * kTileRows;
   const int w_end = min(min(jb * p.by + p.by, kv0 + kTileRows), si.wlim_kv);
   if (kv0 >= w_end) return;
@@ -86,7 +86,7 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(D >= 256
   wid /= p.nqb;
   const int n = wid % p.N;
   const int b = wid / p.N;
-  const SeqInfo si = p.seq[b];
+  const SeqInfo si = seq_of(p, b);
   const int q0 = ib * p.bx + sub * kTileRows;
   const int part_end = min(ib * p.bx + p.bx, q0 + kTileRows);
   const int q_end = min(part_end, si.len_q);
@@ -254,7 +254,7 @@ __global__ __launch_bounds__(256) void dq_acc_store_kernel(Params p, int n_runs)
   const int bn = blockIdx.x / runs;
   const int r0 = (blockIdx.x % runs) * 64;
   const int b = bn / p.N, n = bn % p.N;
-  const SeqInfo si = p.seq[b];
+  const SeqInfo si = seq_of(p, b);
   const int r1 = min(r0 + 64, si.wlim_q);
   constexpr int CH = D / 8;  // 8-element chunks per row
   unsigned short* dq = static_cast<unsigned short*>(p.dq) + b * p.dq_sb + si.off_q * p.dq_sr + n * p.dq_sh;

@@ -55,7 +55,7 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(D >= 256
   wid /= p.nqb;
   const int n = wid % p.N;
   const int b = wid / p.N;
-  const SeqInfo si = p.seq[b];
+  const SeqInfo si = seq_of(p, b);
   const int q0 = ib * p.bx + sub * kTileRows;
   const int part_end = min(ib * p.bx + p.bx, q0 + kTileRows);
   const int q_end = min(part_end, si.len_q);

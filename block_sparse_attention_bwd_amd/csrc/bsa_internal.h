@@ -69,9 +69,16 @@ struct Params {
   // the dequantised result (see the fp8 entry points).
   float dq_scale, dk_scale, dv_scale, delta_scale, o_scale;
 
+  // the per-sequence records: seq_uniform = 1 when every sequence has the same
+  // one (BNSD with all lengths equal to S), which is then seq0 and no table is
+  // staged; otherwise the table `seq` (see seq_of in the kernels)
+  int32_t seq_uniform;
+  SeqInfo seq0;
+
   // workspace regions
   SeqInfo* seq;
-  const float* consts;  // kConstFloats floats after the sequence table: zeros, then +inf, -inf
+  float* consts;        // kConstFloats floats after the sequence table: zeros, then +inf, -inf (written by
+                        // the prologue kernel)
   float* delta;         // -softmax_grad (negated: it seeds the dP accumulator of the dK/dV kernel)
   float* lse2;
   int32_t* row_cnt;
@@ -171,7 +178,7 @@ struct Fp8Stage {
 // Launch helpers (bsa_kernels.hip).  Return a hipError_t value (0 = success).
 int launch_stage_fp8(const Fp8Stage& st, void* stream);
 int launch_pack_amask(const Params& p, void* stream);  // attenMask -> am_rows / am_cols
-int launch_stage_seq(const SeqChunk& chunk, SeqInfo* dst, float* consts, void* stream);
+int launch_stage_seq(const SeqChunk& chunk, SeqInfo* dst, void* stream);
 int launch_prologue(const Params& p, void* stream);
 int launch_plan(const Params& p, void* stream);
 int launch_prologue_rows(const Params& p, void* stream);  // row lists only (the forward's)

@@ -11,13 +11,9 @@ namespace {
 // ---------------------------------------------------------------------------
 // per-sequence table
 // ---------------------------------------------------------------------------
-__global__ void stage_seq_kernel(SeqChunk c, SeqInfo* dst, float* consts) {
+__global__ void stage_seq_kernel(SeqChunk c, SeqInfo* dst) {
   const int t = threadIdx.x;
   if (t < c.count) dst[c.first + t] = c.s[t];
-  if (c.first == 0) {
-    for (int i = t; i < kConstFloats; i += blockDim.x)
-      consts[i] = i == kConstPosInf ? __builtin_inff() : i == kConstNegInf ? -__builtin_inff() : 0.f;
-  }
 }
 
 // ---------------------------------------------------------------------------
@@ -123,7 +119,7 @@ __device__ void delta_part(const Params& p, int blk) {
     const int i = f0 + k * RPP + rloc;  // position within the (b, n) run
     const int b = outer / p.N;
     const int n = outer - b * p.N;
-    const SeqInfo si = p.seq[b];
+    const SeqInfo si = seq_of(p, b);
     out[k] = i < p.sq_max ? (static_cast<int64_t>(b) * p.N + n) * p.sq_max + i : -1;
     valid[k] = i < si.len_q;
     acc[k] = 0.f;
@@ -155,7 +151,7 @@ __device__ void row_list_part(const Params& p, int blk) {
   if (R >= static_cast<int64_t>(p.B) * p.N * p.nqb) return;  // wave-uniform
   const int ib = static_cast<int>(R % p.nqb);
   const int b = static_cast<int>(R / p.nqb / p.N);
-  const SeqInfo si = p.seq[b];
+  const SeqInfo si = seq_of(p, b);
   const int nq_b = (si.len_q + p.bx - 1) / p.bx;
   const int nk_b = (si.len_kv + p.by - 1) / p.by;
   int base = 0;
@@ -201,7 +197,7 @@ __device__ void col_list_part(const Params& p, int blk) {
   const int cw = blk % ncw;
   const int64_t bn = blk / ncw;
   const int b = static_cast<int>(bn / p.N);
-  const SeqInfo si = p.seq[b];
+  const SeqInfo si = seq_of(p, b);
   const int nq_b = (si.len_q + p.bx - 1) / p.bx;
   const int nk_b = (si.len_kv + p.by - 1) / p.by;
   const int j0 = cw * 64;
@@ -249,6 +245,10 @@ __device__ void col_list_part(const Params& p, int blk) {
 template <class E, int D>
 __global__ __launch_bounds__(256) void prologue_kernel(Params p, int nb_rows, int nb_cols) {
   const int bid = blockIdx.x;
+  if (bid == 0 && threadIdx.x < kConstFloats) {  // the constant block (zeros, +inf, -inf)
+    const int i = threadIdx.x;
+    p.consts[i] = i == kConstPosInf ? __builtin_inff() : i == kConstNegInf ? -__builtin_inff() : 0.f;
+  }
   if (bid < nb_rows) row_list_part(p, bid);
   else if (bid < nb_rows + nb_cols) col_list_part(p, bid - nb_rows);
   else delta_part<E, D>(p, bid - nb_rows - nb_cols);
@@ -307,41 +307,115 @@ __device__ __forceinline__ int order_bin(int cost, int chunk) {
   return min(kOrderBins - 1, 1 + static_cast<int>((static_cast<long long>(cost - 1) * (kOrderBins - 1)) / chunk));
 }
 
+constexpr int kPlanThreads = 1024, kPlanWaves = kPlanThreads / 64;
 constexpr int kPlanCachedUnits = 8192;  // units whose T_u the plan kernel keeps in LDS
+constexpr int kPlanCachedDq = 32768;    // dQ units whose KV-block count it keeps in LDS (16 bits)
+// The dQ units are launched longest first only up to this many: with more,
+// each workgroup slot runs a long queue of units, the order changes little at
+// the end, and the sort's LDS atomics (one per unit, on a few class counters)
+// cost more than it saves.
+constexpr int kDqSortMaxUnits = 8192;
 
-__global__ __launch_bounds__(1024) void plan_kernel(Params p) {
-  __shared__ long long s_red[1024];
-  __shared__ int s_scan[1024];
-  __shared__ int s_hist[kOrderBins], s_cursor[kOrderBins];
+// Workgroup-wide sum, returned to every thread (s_w: one slot per wave).
+__device__ __forceinline__ long long plan_sum(long long v, long long* s_w) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+  __syncthreads();  // earlier readers of s_w are done
+  if ((threadIdx.x & 63) == 0) s_w[threadIdx.x >> 6] = v;
+  __syncthreads();
+  long long t = 0;
+#pragma unroll
+  for (int i = 0; i < kPlanWaves; ++i) t += s_w[i];
+  return t;
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave.
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int t = __shfl_up(v, off, 64);
+    if (lane >= off) v += t;
+  }
+  return v;
+}
+
+// Workgroup-wide exclusive prefix sum in thread order.
+__device__ __forceinline__ int plan_excl_scan(int v, long long* s_w) {
+  const int incl = wave_incl_scan(v);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 63) s_w[threadIdx.x >> 6] = incl;
+  __syncthreads();
+  int before = 0;
+  for (int i = 0; i < (static_cast<int>(threadIdx.x) >> 6); ++i) before += static_cast<int>(s_w[i]);
+  return before + incl - v;
+}
+
+// One wave: replace the kOrderBins counts in `bins` by the first position of
+// each class when the classes are laid out in descending order (the position
+// of class c is the count of every class above it).
+static_assert(kOrderBins == 64, "one class per lane");
+__device__ __forceinline__ void desc_class_cursors(int* bins) {
+  const int c = kOrderBins - 1 - (threadIdx.x & 63);
+  const int v = bins[c];
+  bins[c] = wave_incl_scan(v) - v;
+}
+
+__global__ __launch_bounds__(kPlanThreads) void plan_kernel(Params p) {
+  __shared__ long long s_w[kPlanWaves];
+  __shared__ int s_hist[kOrderBins];  // counts of the cost classes, then their cursors
   __shared__ unsigned long long s_xcd[8];
   __shared__ int s_T[kPlanCachedUnits];
+  __shared__ unsigned short s_rc[kPlanCachedDq];
   __shared__ int s_dq[8 * kOrderBins];  // dQ cost classes per XCD range: counts, then cursors
   __shared__ int s_dqmax;
   const int tid = threadIdx.x;
   const PlanView pv(p);
-  const int per = (p.n_units + 1023) / 1024;
+  const int per = (p.n_units + kPlanThreads - 1) / kPlanThreads;
   const int u0 = min(p.n_units, tid * per), u1 = min(p.n_units, u0 + per);
   if (tid < kOrderBins) s_hist[tid] = 0;
   if (tid < 8) s_xcd[tid] = 0;
   if (tid < 8 * kOrderBins) s_dq[tid] = 0;
   if (tid == 0) s_dqmax = 0;
-  // T_u, read from the column counts once (each thread reads back only its own units)
+  __syncthreads();
   const bool cached = p.n_units <= kPlanCachedUnits;
   auto T = [&](int u) { return cached ? s_T[u] : unit_entries(p, u); };
+  const int nd = p.n_dq_units, nsub_q = (p.bx + kTileRows - 1) / kTileRows;
+  const bool sort_dq = nd <= kDqSortMaxUnits;
+  const bool rc_cached = sort_dq && p.nkb <= 65535;
 
+  // T_u from the column counts, and the dQ units' KV-block counts, loaded
+  // together (each thread reads back only what it wrote, or all after a barrier)
   long long tot = 0;
   for (int u = u0; u < u1; ++u) {
     const int t = unit_entries(p, u);
     if (cached) s_T[u] = t;
     tot += t;
   }
-  s_red[tid] = tot;
-  __syncthreads();
-  for (int st = 512; st > 0; st >>= 1) {
-    if (tid < st) s_red[tid] += s_red[tid + st];
-    __syncthreads();
+  {
+    // work of each XCD range of dQ units, a unit costing its selected KV
+    // blocks + 1 (strided over the units: coalesced, several loads in flight;
+    // a thread's units change range only every nd / 8 units)
+    unsigned long long acc = 0;
+    int cur = xcd_of_unit(min(tid, max(nd - 1, 0)), max(nd, 1));
+    int mx = 0;
+#pragma unroll 4
+    for (int u = tid; u < nd; u += kPlanThreads) {
+      const int x = xcd_of_unit(u, nd);
+      const int rc = p.row_cnt[u / nsub_q];
+      if (rc_cached) s_rc[u] = static_cast<unsigned short>(rc);
+      if (x != cur) {
+        atomicAdd(&s_xcd[cur], acc);
+        acc = 0;
+        cur = x;
+      }
+      acc += 1u + static_cast<unsigned>(rc);
+      mx = max(mx, rc);
+    }
+    if (acc) atomicAdd(&s_xcd[cur], acc);
+    atomicMax(&s_dqmax, mx);
   }
-  const long long total = s_red[0];
+  const long long total = plan_sum(tot, s_w);
   const int chunk = static_cast<int>(max(static_cast<long long>(kMinChunk),
                                          (total + kBalanceGroups - 1) / kBalanceGroups));
 
@@ -350,17 +424,9 @@ __global__ __launch_bounds__(1024) void plan_kernel(Params p) {
     const int t = T(u);
     if (t > chunk) mine += (t + chunk - 1) / chunk;
   }
-  s_scan[tid] = mine;
-  for (int i = tid; i < p.slots_cap; i += 1024) pv.slot_unit[i] = -1;
-  __syncthreads();
-  for (int off = 1; off < 1024; off <<= 1) {  // inclusive scan
-    const int v = tid >= off ? s_scan[tid - off] : 0;
-    __syncthreads();
-    s_scan[tid] += v;
-    __syncthreads();
-  }
-  int run = s_scan[tid] - mine;  // exclusive prefix
-  int extra = 0;                 // pieces >= 1 this thread creates
+  for (int i = tid; i < p.slots_cap; i += kPlanThreads) pv.slot_unit[i] = -1;
+  int run = plan_excl_scan(mine, s_w);
+  int extra = 0;  // pieces >= 1 this thread creates
   for (int u = u0; u < u1; ++u) {
     const int t = T(u);
     const int k = t > chunk ? (t + chunk - 1) / chunk : 1;
@@ -380,52 +446,20 @@ __global__ __launch_bounds__(1024) void plan_kernel(Params p) {
       atomicAdd(&s_hist[order_bin(t, chunk)], 1);
     }
   }
-  s_scan[tid] = extra;
-  __syncthreads();
-  for (int st = 512; st > 0; st >>= 1) {
-    if (tid < st) s_scan[tid] += s_scan[tid + st];
-    __syncthreads();
+  const long long extra_total = plan_sum(extra, s_w);  // (its barriers also complete s_hist)
+  // dQ order: XCD ranges only if the heaviest holds at most 1/32 more than the mean
+  unsigned long long xtot = 0, xmx = 0;
+#pragma unroll
+  for (int x = 0; x < 8; ++x) {
+    xtot += s_xcd[x];
+    xmx = max(xmx, s_xcd[x]);
   }
-  // dQ order: work of each XCD range, a unit costing its selected KV blocks + 1
-  {
-    // strided over the units (coalesced, several loads in flight per thread);
-    // a thread's units change XCD range only every nd / 8 units
-    const int nd = p.n_dq_units, nsub_q = (p.bx + kTileRows - 1) / kTileRows;
-    unsigned long long acc = 0;
-    int cur = xcd_of_unit(min(tid, max(nd - 1, 0)), max(nd, 1));
-    int mx = 0;
-#pragma unroll 4
-    for (int u = tid; u < nd; u += 1024) {
-      const int x = xcd_of_unit(u, nd);
-      const int rc = p.row_cnt[u / nsub_q];
-      const unsigned c = 1u + static_cast<unsigned>(rc);
-      if (x != cur) {
-        atomicAdd(&s_xcd[cur], acc);
-        acc = 0;
-        cur = x;
-      }
-      acc += c;
-      mx = max(mx, rc);
-    }
-    if (acc) atomicAdd(&s_xcd[cur], acc);
-    atomicMax(&s_dqmax, mx);
-  }
-  __syncthreads();
+  const bool ranges = 8 * xmx * 32 <= xtot * 33;
+  if (tid < 64) desc_class_cursors(s_hist);
   if (tid == 0) {
-    unsigned long long tot = 0, mx = 0;
-    for (int x = 0; x < 8; ++x) {
-      tot += s_xcd[x];
-      mx = max(mx, s_xcd[x]);
-    }
-    // contiguous ranges only if the heaviest holds at most 1/32 more than the mean
-    p.plan[2] = 8 * mx * 32 <= tot * 33 ? kDqOrderXcdRange : kDqOrderPlain;
-    int base = 0;  // classes in descending order
-    for (int c = kOrderBins - 1; c >= 0; --c) {
-      s_cursor[c] = base;
-      base += s_hist[c];
-    }
     p.plan[0] = chunk;
-    p.plan[1] = p.n_units + s_scan[0];
+    p.plan[1] = p.n_units + static_cast<int>(extra_total);
+    p.plan[2] = ranges ? kDqOrderXcdRange : kDqOrderPlain;
     p.plan[3] = 0;  // the persistent dK/dV kernel's item counter
   }
   __syncthreads();
@@ -433,37 +467,36 @@ __global__ __launch_bounds__(1024) void plan_kernel(Params p) {
     const int t = T(u);
     const int k = pv.unit_k[u];
     for (int c = 0; c < k; ++c) {
-      const int at = atomicAdd(&s_cursor[order_bin(k > 1 ? min(chunk, t - c * chunk) : t, chunk)], 1);
+      const int at = atomicAdd(&s_hist[order_bin(k > 1 ? min(chunk, t - c * chunk) : t, chunk)], 1);
       pv.order_unit[at] = u;
       pv.order_piece[at] = c;
     }
   }
-  // dQ launch order, longest first (cost classes of the selected KV-block
-  // count): with XCD ranges, within each range (workgroup 8 k + x runs the
-  // k-th unit of range x, as the hardware hands workgroup i to XCD i % 8);
-  // otherwise over all units, dealt round-robin to the XCDs.  Results do not
-  // depend on the order.
-  {
-    const int nd = p.n_dq_units, nsub_q = (p.bx + kTileRows - 1) / kTileRows;
-    const bool ranges = p.plan[2] == kDqOrderXcdRange;
-    const int mxc = max(s_dqmax, 1);
-    auto cls = [&](int u) { return order_bin(p.row_cnt[u / nsub_q], mxc); };
-    for (int u = tid; u < nd; u += 1024) atomicAdd(&s_dq[(ranges ? xcd_of_unit(u, nd) : 0) * kOrderBins + cls(u)], 1);
-    __syncthreads();
-    if (tid < (ranges ? 8 : 1)) {  // per range: cursors of the classes in descending order
-      int base = 0;
-      for (int c = kOrderBins - 1; c >= 0; --c) {
-        const int n = s_dq[tid * kOrderBins + c];
-        s_dq[tid * kOrderBins + c] = base;
-        base += n;
-      }
-    }
-    __syncthreads();
-    for (int u = tid; u < nd; u += 1024) {
+  // dQ launch order: with XCD ranges, workgroup 8 k + x runs the k-th unit of
+  // range x (the hardware hands workgroup i to XCD i % 8); otherwise the units
+  // are dealt round-robin to the XCDs.  With few units, longest first (cost
+  // classes of the selected KV-block count) within each range or overall;
+  // else in unit order.  Results do not depend on the order.
+  if (!sort_dq) {
+    const int per_x = nd >> 3, rem_x = nd & 7;
+    for (int u = tid; u < nd; u += kPlanThreads) {
       const int x = ranges ? xcd_of_unit(u, nd) : 0;
-      const int k = atomicAdd(&s_dq[x * kOrderBins + cls(u)], 1);
+      const int k = ranges ? u - (x * per_x + min(x, rem_x)) : u;
       pv.dq_order[ranges ? 8 * k + x : k] = u;
     }
+    return;
+  }
+  const int mxc = max(s_dqmax, 1);
+  auto cls = [&](int u) { return order_bin(rc_cached ? static_cast<int>(s_rc[u]) : p.row_cnt[u / nsub_q], mxc); };
+  for (int u = tid; u < nd; u += kPlanThreads)
+    atomicAdd(&s_dq[(ranges ? xcd_of_unit(u, nd) : 0) * kOrderBins + cls(u)], 1);
+  __syncthreads();
+  if (tid < (ranges ? 8 : 1) * 64) desc_class_cursors(s_dq + (tid >> 6) * kOrderBins);
+  __syncthreads();
+  for (int u = tid; u < nd; u += kPlanThreads) {
+    const int x = ranges ? xcd_of_unit(u, nd) : 0;
+    const int k = atomicAdd(&s_dq[x * kOrderBins + cls(u)], 1);
+    pv.dq_order[ranges ? 8 * k + x : k] = u;
   }
 }
 
@@ -518,9 +551,9 @@ int launch_pack_amask(const Params& p, void* stream) {
   return static_cast<int>(hipGetLastError());
 }
 
-int launch_stage_seq(const SeqChunk& chunk, SeqInfo* dst, float* consts, void* stream) {
+int launch_stage_seq(const SeqChunk& chunk, SeqInfo* dst, void* stream) {
   hipLaunchKernelGGL(stage_seq_kernel, dim3(1), dim3(kMaxInlineSeq), 0,
-                     static_cast<hipStream_t>(stream), chunk, dst, consts);
+                     static_cast<hipStream_t>(stream), chunk, dst);
   return static_cast<int>(hipGetLastError());
 }
 

@@ -8,7 +8,7 @@ namespace bsa {
 constexpr int kNoKernels = 98;  // hipErrorInvalidDeviceFunction: no kernel in this build
 int launch_stage_fp8(const Fp8Stage&, void*) { return kNoKernels; }
 int launch_pack_amask(const Params&, void*) { return kNoKernels; }
-int launch_stage_seq(const SeqChunk&, SeqInfo*, float*, void*) { return kNoKernels; }
+int launch_stage_seq(const SeqChunk&, SeqInfo*, void*) { return kNoKernels; }
 int launch_prologue(const Params&, void*) { return kNoKernels; }
 int launch_plan(const Params&, void*) { return kNoKernels; }
 int launch_prologue_rows(const Params&, void*) { return kNoKernels; }

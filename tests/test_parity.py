@@ -204,6 +204,46 @@ def test_dq_order_choice(name):
         assert cl == sorted(cl, reverse=True)
 
 
+# dQ units are sorted longest first only up to this many (the plan kernel's threshold)
+DQ_SORT_MAX_UNITS = 8192
+
+
+@pytest.mark.parametrize("k", [2, 4])
+def test_full_config_dq_order(k):
+    """The dQ launch order at full size: workload 2 (1024 dQ units) longest first
+    by cost class; workload 4 (32768 units, above the sort threshold) in unit
+    order, dealt to the XCD ranges when the plan chose them."""
+    import block_sparse_attention_bwd_amd as bsa
+    c, r, _, _, _ = _full_run(k)
+    offs, (bx, by, nqb, nkb) = bsa.bsa_bwd_workspace_layout(*r.args, **r.kw)
+    rc = _read_ws(r, offs, "row_cnt", c.B * c.N * nqb).astype(np.int64)
+    nsub = -(-bx // 128)
+    cost = np.repeat(rc, nsub)
+    nd = cost.size
+    n_units = c.B * c.Nkv * nkb * -(-by // 128)
+    slots = min(n_units * (c.N // c.Nkv) * nqb, 512)
+    head = _read_ws(r, offs, "plan", 4)
+    words = 4 + 4 * (n_units + slots) + nd
+    order = _read_ws(r, offs, "plan", words)[4 + 4 * (n_units + slots):]
+    assert np.array_equal(np.sort(order), np.arange(nd))
+    ranges = int(head[2]) == 1
+    per, rem = nd // 8, nd % 8
+    bounds = [x * per + min(x, rem) for x in range(9)]
+    groups = [order[x::8] for x in range(8)] if ranges else [order]
+    if ranges:
+        for x in range(8):
+            assert np.array_equal(np.sort(groups[x]), np.arange(bounds[x], bounds[x + 1]))
+    if nd <= DQ_SORT_MAX_UNITS:
+        mx = max(1, int(cost.max()))
+        klass = np.where(cost <= 0, 0, np.minimum(63, 1 + (cost - 1) * 63 // mx))
+        for grp in groups:
+            cl = klass[grp]
+            assert np.all(cl[:-1] >= cl[1:]), "not longest first"
+    else:
+        for grp in groups:
+            assert np.all(np.diff(grp) == 1), "not in unit order"
+
+
 def test_noncontiguous_outputs_match():
     c, o, lse, ref = _prepared("bnsd_bf16_d128_b128x128_ragged")
     dev = upload(c, o, lse)
