@@ -361,8 +361,9 @@ PEAK_CLOCK_MHZ = 2400.0  # the clock the published MFMA peak is quoted at
 
 
 def _driver_gfxclk(torch):
-    """The driver's current shader clock (MHz): the median over the XCDs of its
-    per-XCD readings where it gives them, else its single reading; None if none."""
+    """(activity %, shader clock MHz) from the driver's metrics table: the clock
+    is the median over the XCDs of its per-XCD readings where it gives them,
+    else its single reading; None if there is no reading."""
     try:
         import amdsmi
         h = torch.cuda._get_amdsmi_handler(torch.cuda.current_device())
@@ -370,23 +371,30 @@ def _driver_gfxclk(torch):
         vals = [float(x) for x in (m.get("current_gfxclks") or []) if isinstance(x, (int, float)) and 0 < x < 10000]
         if not vals and isinstance(m.get("current_gfxclk"), (int, float)) and 0 < m["current_gfxclk"] < 10000:
             vals = [float(m["current_gfxclk"])]
-        return float(np.median(vals)) if vals else None
+        act = m.get("average_gfx_activity")
+        if not vals or not isinstance(act, (int, float)):
+            return None
+        return float(act), float(np.median(vals))
     except Exception:  # no reading on this machine
         return None
 
 
-def sustained_clock_mhz(run, torch, seconds=1.0, chunk=20):
+def sustained_clock_mhz(run, torch, seconds=2.5, chunk=20):
     """Median shader clock (MHz) the driver reports while the calls run back to
-    back for about ``seconds``; None where it gives no reading."""
+    back: the driver refreshes its table about once a second, so the run lasts
+    a few refreshes and only readings taken with the GPU at least 90% busy
+    count (the first ones after the start still show the idle clock); None
+    where it gives no such reading."""
     import threading
     samples, done = [], threading.Event()
 
     def poll():
         while not done.is_set():
-            mhz = _driver_gfxclk(torch)
-            if mhz is None:
+            r = _driver_gfxclk(torch)
+            if r is None:
                 return
-            samples.append(mhz)
+            if r[0] >= 90:
+                samples.append(r[1])
             done.wait(0.005)
 
     for _ in range(chunk):  # the GPU is busy before the first sample
@@ -493,6 +501,8 @@ def main(argv=None):
                          "through the fp8 entry points; bf16 compute and outputs")
     ap.add_argument("--op", choices=["bwd", "fwd"], default="bwd",
                     help="bwd: the backward (default); fwd: the forward that produces O and LSE")
+    ap.add_argument("--clock-seconds", type=float, default=2.5,
+                    help="how long to sample the driver's shader clock while calls run (0: skip)")
     ap.add_argument("--dq-mode", choices=["recompute", "atomic"], default="recompute",
                     help="backward dQ mode (bsa_bwd_ex): recompute (the default, deterministic) or atomic "
                          "(dS K added into an fp32 accumulator by the dK/dV kernel)")
@@ -573,7 +583,7 @@ def main(argv=None):
     torch.cuda.synchronize()
     per_call = np.array([a.elapsed_time(b) for a, b in evs])
     p10, p50, p90 = (float(x) for x in np.percentile(per_call, [10, 50, 90]))
-    clock_mhz = sustained_clock_mhz(run, torch)
+    clock_mhz = sustained_clock_mhz(run, torch, seconds=args.clock_seconds) if args.clock_seconds > 0 else None
     # per-kernel durations: K more calls with the library's HIP events between
     # its stages, on the launch stream (kept out of the timed region above,
     # since each event adds a few microseconds to the stream)
@@ -591,8 +601,11 @@ def main(argv=None):
 
     # dominant kernel: dK/dV, credited with 4 of the 5 counted block GEMMs (S, dP, dV, dK);
     # the forward kernel for --op fwd, credited with both of its GEMMs (S, PV)
-    # (with --dq-mode atomic the dK/dV kernel also forms dS K: all five)
-    kname, kstage, kflop = ("fwd_kernel", "fwd", 4.0) if fwd else ("dkdv_kernel", "dkdv", 10.0 if dq_mode else 8.0)
+    # (with --dq-mode atomic the dK/dV kernel also forms dS K: all five); the
+    # scheduled dK/dV build runs head dims up to 128 without an attenMask
+    scheduled = case.D <= 128 and case.atten_mask is None and case.N // case.Nkv <= 256
+    dk_name = "dkdv_pipe_kernel" if scheduled else "dkdv_kernel"
+    kname, kstage, kflop = ("fwd_kernel", "fwd", 4.0) if fwd else (dk_name, "dkdv", 10.0 if dq_mode else 8.0)
     dkdv_ms = stage_ms[kstage] / max(1, ncalls)
     dkdv_flops = kflop * case.bx * case.by * case.D * blocks
     achieved = dkdv_flops / (dkdv_ms * 1e-3) / 1e12
