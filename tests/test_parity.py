@@ -499,6 +499,9 @@ def test_full_variant_whole_tensors(name):
     torch.cuda.synchronize()
     got = (to_np(dq), to_np(dk), to_np(dv))
     del dq, dk, dv, r
+    t0 = time.perf_counter()
     ref = oracle_backward_threaded(c, vals["q"], vals["k"], vals["v"], vals["o"], vals["do"], lse_h)
+    print(f"[full variant] {name}: oracle backward {time.perf_counter() - t0:.1f} s", flush=True)
     for nm, g, want in zip(("dq", "dk", "dv"), got, ref):
-        assert_close(f"{name}/{nm}", g, want, tol_dtype)
+        err, ref_max = assert_close(f"{name}/{nm}", g, want, tol_dtype)
+        print(f"[full variant] {name} {nm}: max err {err:.3e} = {err / ref_max:.2e} x max|ref|", flush=True)
