@@ -657,13 +657,6 @@ __device__ __forceinline__ void dkdv_list_fill(const Params& p, int64_t col0, in
   __syncthreads();
 }
 
-// Persistent: a grid of as many workgroups as fit the GPU at once, each taking
-// work items from the plan's launch order (longest first) through a counter
-// in the plan region, which the plan kernel zeroes.  When an item's tiles are
-// done, the workgroup first starts the next item (its list, its first tile's
-// copies, its K and V rows) and only then issues the finished item's stores,
-// so those loads fly while the stores are issued.  Which workgroup runs an
-// item does not change the item's result.
 // Epilogue of a whole unit through LDS: every lane writes its key row's dK (then
 // dV) into `stage` (transposed accumulators: 4 consecutive elements per
 // 8-byte write; rows of D elements with their 16-byte chunks XOR-permuted by
@@ -722,18 +715,37 @@ __device__ __forceinline__ void dkdv_store_staged(const Params& p, int u, int pi
         }
       }
     __syncthreads();
-    const int nten = 2 / NPASS;
-    for (int i = tid; i < nten * rows * CPR; i += 64 * W) {  // (tensor, row, chunk), chunks fastest
-      const int t = i / (rows * CPR), rem = i - t * rows * CPR;
-      const int r = rem / CPR, c = rem - r * CPR;
-      const u16x8 v = lds_b128(stage + t * TBYTES + 2u * (r * D + 8 * (c ^ (r & (CPR - 1)))));
+    // read-out: lane tid takes chunk c = tid % CPR of rows tid / CPR + RPP k,
+    // all of a tensor's reads issued before its stores
+    constexpr int RPP = 64 * W / CPR;  // rows one sweep of the workgroup covers
+    constexpr int KPT = RT / RPP;      // sweeps per tensor
+    static_assert(KPT * RPP == RT, "rows split evenly over the sweeps");
+    const int c = tid % CPR, r0 = tid / CPR;
+#pragma unroll
+    for (int t = 0; t < 2 / NPASS; ++t) {
       const bool is_k = NPASS == 1 ? t == 0 : pass == 0;
-      unsigned short* dst = (is_k ? dkp + (kv0 + r) * p.dk_sr : dvp + (kv0 + r) * p.dv_sr) + 8 * c;
-      *reinterpret_cast<u16x8*>(dst) = v;
+      const int64_t sr = is_k ? p.dk_sr : p.dv_sr;
+      unsigned short* dst = (is_k ? dkp : dvp) + (kv0 + r0) * sr + 8 * c;
+      u16x8 v[KPT];
+#pragma unroll
+      for (int k = 0; k < KPT; ++k) {
+        const int r = r0 + RPP * k;
+        v[k] = lds_b128(stage + t * TBYTES + 2u * (r * D + 8 * (c ^ (r & (CPR - 1)))));
+      }
+#pragma unroll
+      for (int k = 0; k < KPT; ++k)
+        if (r0 + RPP * k < rows) *reinterpret_cast<u16x8*>(dst + RPP * k * sr) = v[k];
     }
   }
 }
 
+// Persistent: a grid of as many workgroups as fit the GPU at once, each taking
+// work items from the plan's launch order (longest first) through a counter
+// in the plan region, which the plan kernel zeroes.  When an item's tiles are
+// done, the workgroup first starts the next item (its list, its first tile's
+// copies, its K and V rows) and only then issues the finished item's stores,
+// so those loads fly while the stores are issued.  Which workgroup runs an
+// item does not change the item's result.
 // DQA: dQ by atomic adds (Params::dq_acc); the item's K rows are copied into
 // LDS too, and every finished tile's dQ is added into dq_acc (dkdv_dq_tile)
 // at the start of the next tile, after that tile's copies are issued.
