@@ -602,6 +602,9 @@ int make_plan(const Args& a, Plan* plan) {
       return fail(BSA_ERR_PARAM_INVALID, "problem too large for the dQ store launch");
   }
   take(BSA_WS_DQ_ACC, dq_atomic ? 4ull * rows * D : 0);
+  // the dQ kernel computes softmax_grad (and runs before dK/dV) unless dQ is
+  // formed by atomic adds in the dK/dV kernel
+  p.fused_delta = !a.fwd && !dq_atomic;
   plan->off[BSA_WS_TOTAL] = off;
   p.n_units = static_cast<int32_t>(n_units);
   p.n_dq_units = static_cast<int32_t>(B * N * nqb * nsub_q);
@@ -842,6 +845,12 @@ int enqueue(const Args& a, Plan& plan, char* ws, void* stream, bool allow_profil
   if (herr == 0 && p.dq_acc) herr = bsa::launch_dq_acc_zero(p, stream);
   if (herr) return launch_failed(herr, "prologue");
   if ((rc = mark(kStagePrologue))) return rc;
+  if (p.fused_delta) {  // dQ first: it writes the softmax_grad rows the dK/dV kernel reads
+    if ((herr = bsa::launch_dq(p, stream))) return launch_failed(herr, "dQ");
+    if ((rc = mark(kStageDq))) return rc;
+    if ((herr = bsa::launch_dkdv(p, stream))) return launch_failed(herr, "dK/dV");
+    return mark(kStageDkdv);
+  }
   if ((herr = bsa::launch_dkdv(p, stream))) return launch_failed(herr, "dK/dV");
   if ((rc = mark(kStageDkdv))) return rc;
   if ((herr = bsa::launch_dq(p, stream))) return launch_failed(herr, "dQ");

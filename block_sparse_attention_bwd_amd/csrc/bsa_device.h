@@ -160,10 +160,11 @@ __device__ __forceinline__ bool rect_meets_band(const Params& p, int r0, int nr,
                     static_cast<int64_t>(p.win_pre) + p.win_next >= 0);
 }
 
-// The plan region, in order: [0] chunk, [1] number of work items, [2] dQ order, [3]
-// the next work item to take (the persistent dK/dV kernel's counter), then per unit its piece count and first slot, per slot its unit
-// (-1 = unused) and piece, the work items (unit, piece) in launch order, and
-// the dQ units in launch order.
+// The plan region, in order: [0] entries per piece, [1] number of work items, [2] dQ order,
+// [3] the next work item to take (the persistent dK/dV kernel's counter), then
+// per unit its piece count and first slot, per slot its unit (-1 = unused) and
+// piece, the work items (unit, piece) in launch order, the dQ units in launch
+// order, and per unit the count of its finished pieces.
 struct PlanView {
   int32_t* unit_k;
   int32_t* unit_base;
@@ -172,6 +173,7 @@ struct PlanView {
   int32_t* order_unit;
   int32_t* order_piece;
   int32_t* dq_order;  // dQ workgroup k runs dQ unit dq_order[k]
+  int32_t* piece_done;  // finished pieces (and passes) of each split unit
   __device__ explicit PlanView(const Params& p) {
     unit_k = p.plan + 4;
     unit_base = unit_k + p.n_units;
@@ -180,6 +182,7 @@ struct PlanView {
     order_unit = slot_chunk + p.slots_cap;
     order_piece = order_unit + p.n_units + p.slots_cap;
     dq_order = order_piece + p.n_units + p.slots_cap;
+    piece_done = dq_order + p.n_dq_units;
   }
 };
 

@@ -106,6 +106,104 @@ __device__ __forceinline__ void dkdv_store(const Params& p, int u, int piece, in
   }
 }
 
+// Sum the pieces of split unit u in piece order, scale dK, round and store
+// both (every thread of the workgroup takes part).
+template <class E, int D>
+__device__ void reduce_unit(const Params& p, int u) {
+  const PlanView pv(p);
+  const int pieces = pv.unit_k[u];
+  const float* src = p.partial + static_cast<int64_t>(pv.unit_base[u]) * 2 * kTileRowsMax * D;
+  int wid = u;
+  const int nsub = (p.by + kTileRows - 1) / kTileRows;
+  const int sub = wid % nsub;
+  wid /= nsub;
+  const int jb = wid % p.nkb;
+  wid /= p.nkb;
+  const int h = wid % p.Nkv;
+  const int b = wid / p.Nkv;
+  const SeqInfo si = seq_of(p, b);
+  const int kv0 = jb * p.by + sub * kTileRows;
+  const int w_end = min(min(jb * p.by + p.by, kv0 + kTileRows), si.wlim_kv);
+  if (kv0 >= w_end) return;
+  unsigned short* dkp = static_cast<unsigned short*>(p.dk) + b * p.dk_sb + si.off_kv * p.dk_sr + h * p.dk_sh;
+  unsigned short* dvp = static_cast<unsigned short*>(p.dv) + b * p.dv_sb + si.off_kv * p.dv_sr + h * p.dv_sh;
+  const int per_t = (w_end - kv0) * D / 4;  // float4 groups of one tensor
+  const int nthr = blockDim.x;
+  // GB groups per thread at a time and up to PB pieces' loads in flight
+  // together, summed in piece order
+  constexpr int GB = 4, PB = 4;
+  constexpr int64_t PSTRIDE = 2 * kTileRowsMax * D;  // floats between pieces
+  for (int q0 = threadIdx.x; q0 < 2 * per_t; q0 += GB * nthr) {
+    float4 acc[GB];
+    const float* at[GB];
+    bool ok[GB];
+#pragma unroll
+    for (int i = 0; i < GB; ++i) {
+      const int q = q0 + i * nthr;
+      ok[i] = q < 2 * per_t;
+      const int t = ok[i] ? q / per_t : 0;  // 0: dK, 1: dV
+      const int rem = ok[i] ? q - t * per_t : 0;
+      at[i] = src + (t * kTileRowsMax + rem / (D / 4)) * D + 4 * (rem % (D / 4));
+      acc[i] = ok[i] ? *reinterpret_cast<const float4*>(at[i]) : float4{0.f, 0.f, 0.f, 0.f};
+    }
+    for (int c0 = 1; c0 < pieces; c0 += PB) {
+      float4 x[PB][GB];
+#pragma unroll
+      for (int j = 0; j < PB; ++j)
+#pragma unroll
+        for (int i = 0; i < GB; ++i)
+          x[j][i] = ok[i] && c0 + j < pieces ? *reinterpret_cast<const float4*>(at[i] + (c0 + j) * PSTRIDE)
+                                              : float4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < PB; ++j)
+#pragma unroll
+        for (int i = 0; i < GB; ++i)
+          if (c0 + j < pieces) {
+            acc[i].x += x[j][i].x;
+            acc[i].y += x[j][i].y;
+            acc[i].z += x[j][i].z;
+            acc[i].w += x[j][i].w;
+          }
+    }
+#pragma unroll
+    for (int i = 0; i < GB; ++i) {
+      if (!ok[i]) continue;
+      const int q = q0 + i * nthr;
+      const int t = q / per_t, rem = q - t * per_t;
+      const int rl = rem / (D / 4), d = 4 * (rem % (D / 4));
+      const float sc = t == 0 ? p.dk_scale : p.dv_scale;
+      const float v[4] = {acc[i].x * sc, acc[i].y * sc, acc[i].z * sc, acc[i].w * sc};
+      store4<E>((t == 0 ? dkp + (kv0 + rl) * p.dk_sr : dvp + (kv0 + rl) * p.dv_sr) + d, v);
+    }
+  }
+}
+
+// After a workgroup has stored its piece of split unit u: count the piece
+// (each of the dkdv_passes workgroups of a piece counts once), and the
+// workgroup that completes the count sums the unit (no workgroup waits for
+// another).  The barrier orders the workgroup's partial stores before one
+// thread's release fence (agent scope: it writes the XCD's L2 back, so the
+// stores are visible on every XCD) and count; only the last workgroup takes
+// the acquire fence (it invalidates its XCD's L2, which costs every other
+// workgroup there its cached tiles), again in one thread, with the barrier
+// ordering the sum after it.  The sum is the same whichever workgroup does
+// it.  `flag` is an LDS word.
+template <class E, int D>
+__device__ void piece_finished(const Params& p, int u, int* flag) {
+  __syncthreads();  // every thread's partial stores, before the fence below
+  if (threadIdx.x == 0) {
+    const PlanView pv(p);
+    const int total = pv.unit_k[u] * dkdv_passes(D);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    const bool last = atomicAdd(&pv.piece_done[u], 1) == total - 1;
+    if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");  // the other pieces' stores, before the sum
+    *flag = last;
+  }
+  __syncthreads();
+  if (*flag) reduce_unit<E, D>(p, u);  // uniform
+  __syncthreads();  // everyone read the flag before it is written again
+}
+
 // The same epilogue for transposed accumulators (dV^T / dK^T tiles: lane l
 // holds key row 32 w + l % 32, register i of column tile nt holds element
 // 32 nt + 8 (i / 4) + 4 g + i % 4): four consecutive elements per store.
@@ -160,7 +258,7 @@ template <class E, int D, int W, int MODE, bool AM>
 __device__ __forceinline__ void dkdv_work(const Params& p, int item, unsigned short (*sQ)[dkdv_tile_rows<D, W>() * D],
                                           unsigned short (*sO)[dkdv_tile_rows<D, W>() * D],
                                           float (*sL)[dkdv_tile_rows<D, W>()], float (*sDl)[dkdv_tile_rows<D, W>()],
-                                          uint32_t (*sB)[AM ? dkdv_mask_words<D, W>() : 1][32 * W]) {
+                                          uint32_t (*sB)[AM ? dkdv_mask_words<D, W>() : 1][32 * W], int* sFlag) {
   constexpr int KS = D / 16;  // K=16 steps over the head dim
   constexpr int NT = D / 32;  // 32-wide column tiles of the head dim
   constexpr int H = dkdv_tile_rows<D, W>();
@@ -377,6 +475,7 @@ __device__ __forceinline__ void dkdv_work(const Params& p, int item, unsigned sh
   }
 
   dkdv_store<E, D, W, MODE>(p, u, piece, pieces, kv0, w_end, w_end, b, h, si, adv, adk);
+  if (pieces > 1) piece_finished<E, D>(p, u, sFlag);  // uniform
 }
 
 // ---------------------------------------------------------------------------
@@ -761,7 +860,7 @@ __global__ __launch_bounds__(64 * W) void dkdv_pipe_kernel(Params p) {
   __shared__ __align__(16) float sLD[2 * 2 * H];
   __shared__ int sListIb[kDkdvListChunk], sListCnt[kDkdvMaxGroup];
   __shared__ unsigned short sListN[kDkdvListChunk];
-  __shared__ int sItem;
+  __shared__ int sItem, sFlag;
   // DQA: the item's K rows (tile layout), and per buffer the tile's dS slices
   __shared__ __align__(1024) unsigned short sKt[DQA ? 32 * W * D : 8];
   __shared__ __align__(16) unsigned short sDS[DQA ? 2 * NSL * 32 * W * kDsPitch : 8];
@@ -1002,6 +1101,7 @@ __global__ __launch_bounds__(64 * W) void dkdv_pipe_kernel(Params p) {
     if (next) start(nx_it, nx);  // the next item's first tile goes to buffer 0; buffer 1 stages the stores
     dkdv_store_staged<E, D, W, BUF>(p, cur_it.u, cur_it.piece, cur_it.pieces, cur_it.kv0, cur_it.kv_end,
                                     cur_it.w_end, cur_it.b, cur_it.h, cur_it.si, adv, adk, t0 + BUF);
+    if (cur_it.pieces > 1) piece_finished<E, D>(p, cur_it.u, &sFlag);  // uniform
     if (!next) break;  // uniform
     cur_it = nx_it;
     cur = nx;
@@ -1020,11 +1120,12 @@ __global__ __launch_bounds__(256) void dkdv_kernel(Params p) {
   __shared__ __align__(16) float sL[2][H];
   __shared__ __align__(16) float sDl[2][H];
   __shared__ __align__(16) uint32_t sB[2][AM ? dkdv_mask_words<D, W>() : 1][32 * W];  // attenMask bits
+  __shared__ int sFlag;
   if constexpr (dkdv_passes(D) == 1) {
-    dkdv_work<E, D, W, kDkdvBoth, AM>(p, blockIdx.x, sQ, sO, sL, sDl, sB);
+    dkdv_work<E, D, W, kDkdvBoth, AM>(p, blockIdx.x, sQ, sO, sL, sDl, sB, &sFlag);
   } else {  // workgroups 2i and 2i + 1 run the dV and the dK pass of work item i
-    if (blockIdx.x & 1) dkdv_work<E, D, W, kDkdvOnlyK, AM>(p, blockIdx.x >> 1, sQ, sO, sL, sDl, sB);
-    else dkdv_work<E, D, W, kDkdvOnlyV, AM>(p, blockIdx.x >> 1, sQ, sO, sL, sDl, sB);
+    if (blockIdx.x & 1) dkdv_work<E, D, W, kDkdvOnlyK, AM>(p, blockIdx.x >> 1, sQ, sO, sL, sDl, sB, &sFlag);
+    else dkdv_work<E, D, W, kDkdvOnlyV, AM>(p, blockIdx.x >> 1, sQ, sO, sL, sDl, sB, &sFlag);
   }
 }
 

@@ -1,55 +1,10 @@
-// The dQ kernel (Q-block outer) and the sum of split dK/dV pieces.
+// The dQ kernel (Q-block outer; it also computes softmax_grad) and the store of
+// the atomic mode's dQ accumulator.
 #include "bsa_device.h"
 
 namespace bsa {
 namespace {
 
-
-// Sum the pieces of split dK/dV unit slot_unit[s] (for the slot holding its
-// piece 0) in piece order, scale dK, round and store both.  Runs as extra
-// workgroups of the dQ launch, which starts after the dK/dV kernel finished.
-template <class E, int D>
-__device__ void reduce_pieces(const Params& p, int s) {
-  const PlanView pv(p);
-  const int u = pv.slot_unit[s];
-  if (u < 0 || pv.slot_chunk[s] != 0) return;
-  const int pieces = pv.unit_k[u];
-  const float* src = p.partial + static_cast<int64_t>(pv.unit_base[u]) * 2 * kTileRowsMax * D;
-  int wid = u;
-  const int nsub = (p.by + kTileRows - 1) / kTileRows;
-  const int sub = wid % nsub;
-  wid /= nsub;
-  const int jb = wid % p.nkb;
-  wid /= p.nkb;
-  const int h = wid % p.Nkv;
-  const int b = wid / p.Nkv;
-  const SeqInfo si = seq_of(p, b);
-  const int kv0 = jb * p.by + sub * kTileRows;
-  const int w_end = min(min(jb * p.by + p.by, kv0 + kTileRows), si.wlim_kv);
-  if (kv0 >= w_end) return;
-  unsigned short* dkp = static_cast<unsigned short*>(p.dk) + b * p.dk_sb + si.off_kv * p.dk_sr + h * p.dk_sh;
-  unsigned short* dvp = static_cast<unsigned short*>(p.dv) + b * p.dv_sb + si.off_kv * p.dv_sr + h * p.dv_sh;
-  const int n4 = 2 * (w_end - kv0) * D / 4;  // float4 groups over [dK rows, dV rows]
-  for (int q = threadIdx.x; q < n4; q += blockDim.x) {
-    const int t = q / ((w_end - kv0) * D / 4);  // 0: dK, 1: dV
-    const int rem = q % ((w_end - kv0) * D / 4);
-    const int rl = rem / (D / 4), d = 4 * (rem % (D / 4));
-    float4 acc = *reinterpret_cast<const float4*>(src + (t * kTileRowsMax + rl) * D + d);
-    for (int c = 1; c < pieces; ++c) {
-      const float4 x = *reinterpret_cast<const float4*>(src + (static_cast<int64_t>(c) * 2 * kTileRowsMax + t * kTileRowsMax + rl) * D + d);
-      acc.x += x.x;
-      acc.y += x.y;
-      acc.z += x.z;
-      acc.w += x.w;
-    }
-    const float sc = t == 0 ? p.dk_scale : p.dv_scale;
-    unsigned short* dst = (t == 0 ? dkp + (kv0 + rl) * p.dk_sr : dvp + (kv0 + rl) * p.dv_sr) + d;
-    dst[0] = E::from_f32(acc.x * sc);
-    dst[1] = E::from_f32(acc.y * sc);
-    dst[2] = E::from_f32(acc.z * sc);
-    dst[3] = E::from_f32(acc.w * sc);
-  }
-}
 
 // ---------------------------------------------------------------------------
 // dQ: Q-block-outer
@@ -74,10 +29,6 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(D >= 256
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6, l32 = lane & 31, g = lane >> 5;
 
-  if (static_cast<int>(blockIdx.x) >= p.n_dq_units) {  // the workgroups after the dQ ones reduce split dK/dV units
-    reduce_pieces<E, D>(p, blockIdx.x - p.n_dq_units);
-    return;
-  }
   int wid = PlanView(p).dq_order[blockIdx.x];
   const int nsub = (p.bx + kTileRows - 1) / kTileRows;
   const int sub = wid % nsub;
@@ -91,11 +42,20 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(D >= 256
   const int part_end = min(ib * p.bx + p.bx, q0 + kTileRows);
   const int q_end = min(part_end, si.len_q);
   const int w_end = min(part_end, si.wlim_q);
-  if (q0 >= w_end) return;
-
-  const int h = n / p.G;
   const int64_t bn = static_cast<int64_t>(b) * p.N + n;
   const int my_q = q0 + 32 * w + l32;  // B-operand column == score column of this lane
+  // this lane writes row my_q of the softmax_grad / lse2 arrays (zeros past
+  // the sequence's length, as for every position below maxSq)
+  const bool row_out = g == 0 && my_q < min(part_end, p.sq_max);
+  if (q0 >= w_end) {  // no row of the sequence here (a TND block past its end)
+    if (row_out) {
+      p.delta[bn * p.sq_max + my_q] = 0.f;
+      p.lse2[bn * p.sq_max + my_q] = 0.f;
+    }
+    return;
+  }
+
+  const int h = n / p.G;
   const bool q_ok = my_q < q_end;
   const int64_t q_base = b * p.q_sb + si.off_q * p.q_sr + n * p.q_sh;
   const unsigned short* qp = static_cast<const unsigned short*>(p.q) + q_base;
@@ -115,8 +75,42 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(D >= 256
     qreg[s] = zq;
     oreg[s] = zo;
   }
-  const float l2 = q_ok ? p.lse2[bn * p.sq_max + my_q] : 0.f;
-  const float dl = q_ok ? p.delta[bn * p.sq_max + my_q] : 0.f;
+  // softmax_grad (aclnnBlockSparseAttentionGrad page, 功能说明: softmaxGrad of
+  // dOut and attentionOut, the row sums of dOut o Out).  This lane holds the
+  // row's 8-element chunks 2s + g of dOut (s < KS); it sums each chunk in
+  // order, folds the KS chunk sums in halves (chunk 2s with 2s + KS, then
+  // with 2s + KS / 2, ...), and adds the partner lane's (+-32) result: the
+  // order of the prologue's pass (chunk sums combined by lane shuffles at
+  // distances D/16, D/32, ..., 1), so both give the same bits.  Written
+  // negated for the dK/dV kernel, which runs after this one and seeds dP's
+  // accumulator with it; lse2 = LSE * log2(e) too.
+  float part = 0.f, lse = 0.f;
+  if (q_ok) {
+    const unsigned short* orow = static_cast<const unsigned short*>(p.o) + q_base + my_q * p.q_sr;
+    u16x8 ov[KS];
+#pragma unroll
+    for (int s = 0; s < KS; ++s) ov[s] = *reinterpret_cast<const u16x8*>(orow + 16 * s + 8 * g);
+    lse = p.lse[b * p.lse_sb + (si.off_q + my_q) * p.lse_sr + n * p.lse_sh];
+    float cs[KS];
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      cs[s] = 0.f;
+#pragma unroll
+      for (int t = 0; t < 8; ++t) cs[s] += E::to_f32(oreg[s][t]) * E::to_f32(ov[s][t]);
+    }
+#pragma unroll
+    for (int half = KS / 2; half >= 1; half >>= 1)
+#pragma unroll
+      for (int s = 0; s < half; ++s) cs[s] += cs[s + half];
+    part = cs[0];
+  }
+  part += __shfl_xor(part, 32);
+  const float dl = q_ok ? -(part * p.delta_scale) : 0.f;  // -softmax_grad
+  const float l2 = q_ok ? lse * kLog2e : 0.f;
+  if (row_out) {
+    p.delta[bn * p.sq_max + my_q] = dl;
+    p.lse2[bn * p.sq_max + my_q] = l2;
+  }
 #pragma unroll
   for (int s = 0; s < KS; ++s) {
     settle(qreg[s]);
@@ -242,14 +236,9 @@ __global__ __launch_bounds__(256) void dq_acc_zero_kernel(float4* acc, int64_t n
 
 // dQ = dq_acc * dq_scale rounded to the element type, one workgroup per 64
 // positions of one (batch, query head), every row the call writes (rows past
-// the sequence end hold zeros in dq_acc); the workgroups after the first
-// n_runs sum the pieces of split dK/dV units, as in the recompute launch.
+// the sequence end hold zeros in dq_acc).
 template <class E, int D>
 __global__ __launch_bounds__(256) void dq_acc_store_kernel(Params p, int n_runs) {
-  if (static_cast<int>(blockIdx.x) >= n_runs) {
-    reduce_pieces<E, D>(p, blockIdx.x - n_runs);
-    return;
-  }
   const int runs = (p.sq_max + 63) / 64;
   const int bn = blockIdx.x / runs;
   const int r0 = (blockIdx.x % runs) * 64;
@@ -284,7 +273,7 @@ int launch_dq_acc_zero(const Params& p, void* stream) {
 int launch_dq(const Params& p, void* stream) {
   if (p.dq_acc) {  // dQ by atomic adds: scale and store the accumulator
     const int n_runs = p.B * p.N * ((p.sq_max + 63) / 64);
-    const dim3 grid(static_cast<unsigned>(n_runs + p.slots_cap));
+    const dim3 grid(static_cast<unsigned>(n_runs));
     const hipStream_t s = static_cast<hipStream_t>(stream);
     const bool bf = p.dtype == 2;
     if (p.D == 128) {
@@ -296,7 +285,8 @@ int launch_dq(const Params& p, void* stream) {
     }
     return static_cast<int>(hipGetLastError());
   }
-  const dim3 grid(static_cast<unsigned>(p.n_dq_units + p.slots_cap));
+  if (p.n_dq_units == 0) return 0;
+  const dim3 grid(static_cast<unsigned>(p.n_dq_units));
   BSA_DISPATCH(dq_kernel, waves_for(p.bx), grid, static_cast<hipStream_t>(stream), p);
   return static_cast<int>(hipGetLastError());
 }

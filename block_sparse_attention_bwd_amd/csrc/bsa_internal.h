@@ -90,11 +90,16 @@ struct Params {
   int32_t n_units;     // dK/dV work units: B * Nkv * nKB * ceil(by / 128)
   int32_t n_dq_units;  // dQ workgroups: B * N * nQB * ceil(bx / 128)
   int32_t slots_cap;   // partial-result slots for units split over several workgroups
-  int32_t* plan;       // [0] chunk size, [1] work items, [2] dQ order, [3] unused, unit_k[n_units],
-                       // unit_base[n_units], slot_unit[slots_cap], slot_chunk[slots_cap],
-                       // order_unit[n_units + slots_cap], order_piece[n_units + slots_cap],
-                       // dq_order[n_dq_units]
+  int32_t* plan;       // [0] entries per piece, [1] work items, [2] dQ order, [3] the persistent dK/dV
+                       // kernel's item counter, unit_k[n_units], unit_base[n_units],
+                       // slot_unit[slots_cap], slot_chunk[slots_cap], order_unit[n_units + slots_cap],
+                       // order_piece[n_units + slots_cap], dq_order[n_dq_units],
+                       // piece_done[n_units] (finished pieces of each split unit)
   float* partial;      // [slots_cap][2][kTileRowsMax][D] fp32 (dK unscaled, dV)
+  // 1: the dQ kernel computes softmax_grad and lse2 (and writes them for the
+  // dK/dV kernel, which then runs after it) and the prologue skips them;
+  // 0 (the forward, and dQ by atomic adds): the prologue computes them
+  int32_t fused_delta;
   // dQ by atomic adds (bsa_bwd_ex with BSA_DQ_ATOMIC; nullptr otherwise): fp32
   // [B][N][sq_max][D] of unscaled dS K sums, zeroed before the dK/dV kernel
   // adds into it and scaled, rounded and stored by the dQ launch
@@ -102,17 +107,18 @@ struct Params {
 };
 
 // Work-split parameters: a unit with more than `chunk` selecting Q blocks is
-// split into ceil(T / chunk) pieces, chunk = max(kMinChunk, ceil(total /
-// kBalanceGroups)); at most kMaxSlots pieces exist in total, which that
-// choice of chunk guarantees (pieces <= total / chunk + split units <= 2 x kBalanceGroups).
+// split into ceil(T / piece) pieces, chunk = max(kMinChunk, ceil(total /
+// kBalanceGroups)), piece = ceil(chunk / 2); at most kMaxSlots pieces exist
+// in total, which that choice guarantees (pieces <= total / piece + split
+// units <= 2 x kBalanceGroups + kBalanceGroups).
 constexpr int kTileRowsMax = 128;
 
 // Words (int32) of the plan region: 4 header words, then per unit its piece
 // count and first slot, per slot its unit and piece, the launch order as
-// two arrays (unit, piece) of n_units + slots entries, and the dQ launch
-// order (n_dq entries).
+// two arrays (unit, piece) of n_units + slots entries, the dQ launch order
+// (n_dq entries), and per unit a count of its finished pieces.
 inline constexpr int64_t plan_words(int64_t n_units, int64_t slots, int64_t n_dq) {
-  return 4 + 4 * (n_units + slots) + n_dq;
+  return 4 + 4 * (n_units + slots) + n_dq + n_units;
 }
 constexpr int kBalanceGroups = 256;
 // Workgroups per dK/dV work item: 1, or 2 where dK and dV are accumulated by
@@ -125,7 +131,7 @@ constexpr int kMinChunk = 4;
 // in LDS); the generic build runs the rest.
 constexpr int kDkdvMaxGroup = 256;
 inline constexpr bool dkdv_scheduled(int D, bool amask, int G) { return D <= 128 && !amask && G <= kDkdvMaxGroup; }
-constexpr int kMaxSlots = 2 * kBalanceGroups;
+constexpr int kMaxSlots = 3 * kBalanceGroups;
 
 // Launch-grid limits.  A dispatch counts work-items in 32 bits, so a grid of
 // 256-thread workgroups holds at most kMaxGridGroups of them.
@@ -184,7 +190,7 @@ int launch_plan(const Params& p, void* stream);
 int launch_prologue_rows(const Params& p, void* stream);  // row lists only (the forward's)
 int launch_fwd(const Params& p, void* stream);
 int launch_dkdv(const Params& p, void* stream);
-int launch_dq(const Params& p, void* stream);  // also sums the pieces of split dK/dV units
+int launch_dq(const Params& p, void* stream);
 int launch_dq_acc_zero(const Params& p, void* stream);  // dq_acc = 0 (atomic dQ mode)
 
 // The library's own device scratch array, used as the workspace of the entry

@@ -262,9 +262,12 @@ __global__ __launch_bounds__(256) void prologue_kernel(Params p, int nb_rows, in
 // that selects it, for every query head of its group: T_u entries.  Units with
 // far more entries than the rest (a KV block every Q block selects) would keep
 // one workgroup busy long after the others finish, so a unit with
-// T_u > chunk is cut into ceil(T_u / chunk) pieces of consecutive entries;
-// each piece writes an fp32 partial dK/dV and the pieces are summed in order
-// afterwards, so the result is the same on every run.  Pieces get slots by an
+// T_u > chunk is cut into ceil(T_u / piece) pieces of consecutive entries,
+// piece = ceil(chunk / 2): half the balanced share, so that the pieces end
+// well before the kernel does and the sum that follows the last of them
+// (which waits for every piece) stays off the end of the schedule.  Each
+// piece writes an fp32 partial dK/dV and the pieces are summed in order, so
+// the result is the same on every run.  Pieces get slots by an
 // exclusive scan over units in unit order; units that would overflow the slot
 // capacity stay whole.  One workgroup of 1024 threads.
 __device__ __forceinline__ int unit_entries(const Params& p, int u) {
@@ -297,7 +300,7 @@ constexpr int kDqOrderPlain = 0, kDqOrderXcdRange = 1;
 
 // Launch order of the work items: longest first, so that the last workgroups
 // to start are short ones.  Costs (Q-block entries of the piece) are binned
-// into kOrderBins classes, class kOrderBins-1 holding pieces of about `chunk`
+// into kOrderBins classes, class kOrderBins-1 holding units of about `chunk`
 // entries and class 0 the units with nothing to do (they only write zeros).
 // The order inside a class depends on scheduling; the results do not, since
 // every piece sums its entries in list order and pieces are reduced in order.
@@ -419,24 +422,26 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Params p) {
   const int chunk = static_cast<int>(max(static_cast<long long>(kMinChunk),
                                          (total + kBalanceGroups - 1) / kBalanceGroups));
 
+  const int pc = (chunk + 1) / 2;  // entries per piece of a split unit
   int mine = 0;
   for (int u = u0; u < u1; ++u) {
     const int t = T(u);
-    if (t > chunk) mine += (t + chunk - 1) / chunk;
+    if (t > chunk) mine += (t + pc - 1) / pc;
   }
   for (int i = tid; i < p.slots_cap; i += kPlanThreads) pv.slot_unit[i] = -1;
+  for (int i = tid; i < p.n_units; i += kPlanThreads) pv.piece_done[i] = 0;
   int run = plan_excl_scan(mine, s_w);
   int extra = 0;  // pieces >= 1 this thread creates
   for (int u = u0; u < u1; ++u) {
     const int t = T(u);
-    const int k = t > chunk ? (t + chunk - 1) / chunk : 1;
+    const int k = t > chunk ? (t + pc - 1) / pc : 1;
     if (k > 1 && run + k <= p.slots_cap) {
       pv.unit_k[u] = k;
       pv.unit_base[u] = run;
       for (int c = 0; c < k; ++c) {
         pv.slot_unit[run + c] = u;
         pv.slot_chunk[run + c] = c;
-        atomicAdd(&s_hist[order_bin(min(chunk, t - c * chunk), chunk)], 1);
+        atomicAdd(&s_hist[order_bin(min(pc, t - c * pc), chunk)], 1);
       }
       run += k;
       extra += k - 1;
@@ -457,7 +462,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Params p) {
   const bool ranges = 8 * xmx * 32 <= xtot * 33;
   if (tid < 64) desc_class_cursors(s_hist);
   if (tid == 0) {
-    p.plan[0] = chunk;
+    p.plan[0] = pc;
     p.plan[1] = p.n_units + static_cast<int>(extra_total);
     p.plan[2] = ranges ? kDqOrderXcdRange : kDqOrderPlain;
     p.plan[3] = 0;  // the persistent dK/dV kernel's item counter
@@ -467,7 +472,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Params p) {
     const int t = T(u);
     const int k = pv.unit_k[u];
     for (int c = 0; c < k; ++c) {
-      const int at = atomicAdd(&s_hist[order_bin(k > 1 ? min(chunk, t - c * chunk) : t, chunk)], 1);
+      const int at = atomicAdd(&s_hist[order_bin(k > 1 ? min(pc, t - c * pc) : t, chunk)], 1);
       pv.order_unit[at] = u;
       pv.order_piece[at] = c;
     }
@@ -575,7 +580,9 @@ void launch_prologue_kernel(const Params& p, dim3 grid, hipStream_t s, A... a) {
 
 int launch_prologue(const Params& p, void* stream) {
   const PrologueGrid pg = prologue_grid(p.B, p.N, p.sq_max, p.nqb, p.nkb, p.tnd != 0);
-  launch_prologue_kernel(p, dim3(static_cast<unsigned>(pg.total())), static_cast<hipStream_t>(stream),
+  const int64_t blocks = pg.rows + pg.cols + (p.fused_delta ? 0 : pg.delta);  // softmax_grad blocks last
+  if (blocks == 0) return 0;
+  launch_prologue_kernel(p, dim3(static_cast<unsigned>(blocks)), static_cast<hipStream_t>(stream),
                          static_cast<int>(pg.rows), static_cast<int>(pg.cols));
   return static_cast<int>(hipGetLastError());
 }

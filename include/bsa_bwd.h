@@ -398,10 +398,12 @@ const char* bsa_last_error(void);
  * next max_calls bsa_bwd / bsa_fwd calls on this process record HIP events
  * between their kernel stages (on the call's stream).  bsa_profile_stop waits
  * for the recorded events, writes the summed milliseconds of each stage into
- * stage_ms[0..n_stages) (stage order: 0 = sequence table + softmax_grad + mask
- * compaction + work plan (+ the attenMask packing, + the fp8 decode of the
- * fp8 entry points),
- * 1 = dK/dV, 2 = dQ + the sum of split dK/dV units,
+ * stage_ms[0..n_stages) (stage order: 0 = sequence table + mask compaction +
+ * work plan (+ the attenMask packing, + the fp8 decode of the fp8 entry
+ * points, + softmax_grad in the forward and with BSA_DQ_ATOMIC),
+ * 1 = dK/dV, including the sums of split dK/dV units, 2 = dQ (by default it
+ * runs before dK/dV and also computes softmax_grad; with BSA_DQ_ATOMIC it
+ * runs after dK/dV and stores the accumulated dQ),
  * 3 = forward; a stage a call does not run adds 0), writes the number of
  * profiled calls to *n_calls, frees the events and turns recording off.
  * Not thread-safe.

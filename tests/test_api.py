@@ -111,7 +111,7 @@ def test_layout_region_sizes():
     128-row part, 72 possible pieces)."""
     offs, dims = bsa.bsa_bwd_workspace_layout(**_bnsd())
     B, N, Nkv, Sq, D, nqb, nkb = 2, 4, 2, 300, 128, 3, 3
-    n_units, slots = B * Nkv * nkb, min(B * Nkv * nkb * (N // Nkv) * nqb, 512)
+    n_units, slots = B * Nkv * nkb, min(B * Nkv * nkb * (N // Nkv) * nqb, 768)
     size = {k: offs[b] - offs[a] for k, a, b in zip(bsa.WS_REGIONS, bsa.WS_REGIONS, bsa.WS_REGIONS[1:])}
     assert size["seq"] >= B * 32 + 128 * 4
     assert size["delta"] >= B * N * Sq * 4 and size["lse2"] >= B * N * Sq * 4
@@ -138,7 +138,7 @@ def test_layout_partial_region_scales_with_head_dim():
         offs, _ = bsa.bsa_bwd_workspace_layout(**_bnsd(D=D))
         i = bsa.WS_REGIONS.index("partial")
         sizes[D] = offs[bsa.WS_REGIONS[i + 1]] - offs["partial"]
-    slots = min(2 * 2 * 3 * 2 * 3, 512)
+    slots = min(2 * 2 * 3 * 2 * 3, 768)
     for D in (64, 128, 256):
         assert sizes[D] >= slots * 2 * 128 * D * 4
     assert sizes[256] > sizes[128] > sizes[64]

@@ -142,15 +142,16 @@ def test_split_units_are_planned():
     offs, (bx, by, nqb, nkb) = bsa.bsa_bwd_workspace_layout(*r.args, **r.kw)
     n_units = c.B * c.Nkv * nkb
     G = c.N // c.Nkv
-    slots = min(n_units * G * nqb, 512)
+    slots = min(n_units * G * nqb, 768)
     assert offs["partial"] - offs["plan"] >= 4 * (4 + 4 * (n_units + slots))
     plan = _read_ws(r, offs, "plan", 4 + 4 * (n_units + slots))
-    chunk, n_items = int(plan[0]), int(plan[1])
+    pc, n_items = int(plan[0]), int(plan[1])
     pieces = [int(k) for k in plan[4:4 + n_units]]
     _, cols = oracle.block_lists(c.mask, c.B, c.N, nqb, nkb, bx, by, c.len_q, c.len_kv)
     totals = [sum(len(cols[0][n][j]) for n in range(c.N)) for j in range(nkb)]
-    assert chunk == max(4, -(-sum(totals) // 256))
-    assert pieces == [(-(-t // chunk) if t > chunk else 1) for t in totals]
+    chunk = max(4, -(-sum(totals) // 256))  # a unit with more entries is split
+    assert pc == (chunk + 1) // 2  # entries per piece
+    assert pieces == [(-(-t // pc) if t > chunk else 1) for t in totals]
     assert max(pieces) > 1
     assert n_items == sum(pieces)
     ou = plan[4 + 2 * (n_units + slots):][:n_items]
@@ -158,7 +159,7 @@ def test_split_units_are_planned():
     assert sorted(zip(ou.tolist(), op.tolist())) == [(u, k) for u in range(n_units) for k in range(pieces[u])]
 
     def cls(u, k):
-        cost = min(chunk, totals[u] - k * chunk) if pieces[u] > 1 else totals[u]
+        cost = min(pc, totals[u] - k * pc) if pieces[u] > 1 else totals[u]
         return 0 if cost <= 0 else min(63, 1 + (cost - 1) * 63 // chunk)
     classes = [cls(u, k) for u, k in zip(ou.tolist(), op.tolist())]
     assert classes == sorted(classes, reverse=True)
@@ -189,7 +190,7 @@ def test_dq_order_choice(name):
     # with ranges, workgroup 8k + x runs range x's units, else all units, longest
     # first by cost class (selected KV blocks, 64 classes scaled to the largest)
     n_units = c.B * c.Nkv * nkb * -(-by // 128)
-    slots = min(n_units * (c.N // c.Nkv) * nqb, 512)
+    slots = min(n_units * (c.N // c.Nkv) * nqb, 768)
     words = 4 + 4 * (n_units + slots) + nd
     order = _read_ws(r, offs, "plan", words)[4 + 4 * (n_units + slots):].tolist()
     assert sorted(order) == list(range(nd))
@@ -221,7 +222,7 @@ def test_full_config_dq_order(k):
     cost = np.repeat(rc, nsub)
     nd = cost.size
     n_units = c.B * c.Nkv * nkb * -(-by // 128)
-    slots = min(n_units * (c.N // c.Nkv) * nqb, 512)
+    slots = min(n_units * (c.N // c.Nkv) * nqb, 768)
     head = _read_ws(r, offs, "plan", 4)
     words = 4 + 4 * (n_units + slots) + nd
     order = _read_ws(r, offs, "plan", words)[4 + 4 * (n_units + slots):]
