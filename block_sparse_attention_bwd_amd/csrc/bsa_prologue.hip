@@ -271,14 +271,15 @@ __global__ __launch_bounds__(256) void prologue_kernel(Params p, int nb_rows, in
 // exclusive scan over units in unit order; units that would overflow the slot
 // capacity stay whole.  One workgroup of 1024 threads.
 __device__ __forceinline__ int unit_entries(const Params& p, int u) {
+  // u = ((b Nkv + h) nkb + jb) nsub + sub, and head n = h G + i of batch b
+  // has column counts at ((b Nkv + h) G + i) nkb + jb: two divisions
   const int nsub = (p.by + kTileRows - 1) / kTileRows;
-  int w = u / nsub;
-  const int jb = w % p.nkb;
-  w /= p.nkb;
-  const int h = w % p.Nkv;
-  const int b = w / p.Nkv;
+  const int w = nsub == 1 ? u : u / nsub;
+  const int bh = w / p.nkb;
+  const int jb = w - bh * p.nkb;
+  const int32_t* c = p.col_cnt + static_cast<int64_t>(bh) * p.G * p.nkb + jb;
   int t = 0;
-  for (int n = h * p.G; n < (h + 1) * p.G; ++n) t += p.col_cnt[(static_cast<int64_t>(b) * p.N + n) * p.nkb + jb];
+  for (int i = 0; i < p.G; ++i) t += c[static_cast<int64_t>(i) * p.nkb];
   return t;
 }
 
@@ -307,7 +308,10 @@ constexpr int kDqOrderPlain = 0, kDqOrderXcdRange = 1;
 constexpr int kOrderBins = 64;
 __device__ __forceinline__ int order_bin(int cost, int chunk) {
   if (cost <= 0) return 0;
-  return min(kOrderBins - 1, 1 + static_cast<int>((static_cast<long long>(cost - 1) * (kOrderBins - 1)) / chunk));
+  const unsigned long long num = static_cast<unsigned long long>(cost - 1) * (kOrderBins - 1);
+  const unsigned long long q = num >> 32 ? num / static_cast<unsigned>(chunk)  // (cost above 2^32 / 63)
+                                         : static_cast<unsigned>(num) / static_cast<unsigned>(chunk);
+  return min(static_cast<unsigned long long>(kOrderBins - 1), 1 + q);
 }
 
 constexpr int kPlanThreads = 1024, kPlanWaves = kPlanThreads / 64;
@@ -387,36 +391,52 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Params p) {
   const bool sort_dq = nd <= kDqSortMaxUnits;
   const bool rc_cached = sort_dq && p.nkb <= 65535;
 
-  // T_u from the column counts, and the dQ units' KV-block counts, loaded
-  // together (each thread reads back only what it wrote, or all after a barrier)
+  // T_u from the column counts, and the dQ units' KV-block counts, loaded in
+  // one loop strided over the units (coalesced; both loads of an iteration,
+  // and of the next, in flight together); the per-thread unit ranges below
+  // read s_T after plan_sum's barriers.  Per XCD range of dQ units its work,
+  // a unit costing its selected KV blocks + 1 (a thread's units change range
+  // only every nd / 8 units).
   long long tot = 0;
-  for (int u = u0; u < u1; ++u) {
-    const int t = unit_entries(p, u);
-    if (cached) s_T[u] = t;
-    tot += t;
-  }
   {
-    // work of each XCD range of dQ units, a unit costing its selected KV
-    // blocks + 1 (strided over the units: coalesced, several loads in flight;
-    // a thread's units change range only every nd / 8 units)
     unsigned long long acc = 0;
     int cur = xcd_of_unit(min(tid, max(nd - 1, 0)), max(nd, 1));
     int mx = 0;
-#pragma unroll 4
-    for (int u = tid; u < nd; u += kPlanThreads) {
-      const int x = xcd_of_unit(u, nd);
-      const int rc = p.row_cnt[u / nsub_q];
-      if (rc_cached) s_rc[u] = static_cast<unsigned short>(rc);
-      if (x != cur) {
-        atomicAdd(&s_xcd[cur], acc);
-        acc = 0;
-        cur = x;
+    const int n_all = max(p.n_units, nd);
+#pragma unroll 2
+    for (int u = tid; u < n_all; u += kPlanThreads) {
+      const int t = u < p.n_units ? unit_entries(p, u) : 0;
+      const int rc = u < nd ? p.row_cnt[nsub_q == 1 ? u : u / nsub_q] : 0;
+      if (u < p.n_units) {
+        if (cached) s_T[u] = t;
+        tot += t;
       }
-      acc += 1u + static_cast<unsigned>(rc);
-      mx = max(mx, rc);
+      if (u < nd) {
+        const int x = xcd_of_unit(u, nd);
+        if (rc_cached) s_rc[u] = static_cast<unsigned short>(rc);
+        if (x != cur) {
+          atomicAdd(&s_xcd[cur], acc);
+          acc = 0;
+          cur = x;
+        }
+        acc += 1u + static_cast<unsigned>(rc);
+        mx = max(mx, rc);
+      }
     }
-    if (acc) atomicAdd(&s_xcd[cur], acc);
-    atomicMax(&s_dqmax, mx);
+    // one LDS atomic per wave where its lanes end in the same range (the
+    // common case: 64 consecutive units), else one per lane
+    const int cur0 = __shfl(cur, 0, 64);
+    if (__all(cur == cur0)) {
+      unsigned long long w = acc;
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) w += __shfl_xor(w, off, 64);
+      if ((tid & 63) == 0 && w) atomicAdd(&s_xcd[cur0], w);
+    } else if (acc) {
+      atomicAdd(&s_xcd[cur], acc);
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) mx = max(mx, __shfl_xor(mx, off, 64));
+    if ((tid & 63) == 0) atomicMax(&s_dqmax, mx);
   }
   const long long total = plan_sum(tot, s_w);
   const int chunk = static_cast<int>(max(static_cast<long long>(kMinChunk),
@@ -431,6 +451,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Params p) {
   for (int i = tid; i < p.slots_cap; i += kPlanThreads) pv.slot_unit[i] = -1;
   for (int i = tid; i < p.n_units; i += kPlanThreads) pv.piece_done[i] = 0;
   int run = plan_excl_scan(mine, s_w);
+  const int run0 = run;  // the order loop below replays the piece counts from here
   int extra = 0;  // pieces >= 1 this thread creates
   for (int u = u0; u < u1; ++u) {
     const int t = T(u);
@@ -468,9 +489,12 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Params p) {
     p.plan[3] = 0;  // the persistent dK/dV kernel's item counter
   }
   __syncthreads();
+  run = run0;
   for (int u = u0; u < u1; ++u) {
     const int t = T(u);
-    const int k = pv.unit_k[u];
+    int k = t > chunk ? (t + pc - 1) / pc : 1;  // as above, without reading unit_k back
+    if (k > 1 && run + k <= p.slots_cap) run += k;
+    else k = 1;
     for (int c = 0; c < k; ++c) {
       const int at = atomicAdd(&s_hist[order_bin(k > 1 ? min(pc, t - c * pc) : t, chunk)], 1);
       pv.order_unit[at] = u;
