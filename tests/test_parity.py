@@ -87,8 +87,11 @@ def test_block_lists_bit_exact(name):
 
 
 @pytest.mark.parametrize("name", ["config1", "tnd_fp16_d128_b64x128_gqa", "bnsd_fp16_d64_b64x128_padded",
-                                  "tnd_fp16_d256_b64x64_gqa"])
+                                  "tnd_fp16_d256_b64x64_gqa", "tnd_bf16_d64_empty_seqs", "bnsd_fp16_d128_b256x256"])
 def test_delta_and_lse2(name):
+    """softmax_grad (stored negated) and lse2 as the dQ kernel writes them for
+    the dK/dV kernel: every row of [B, N, maxSq], zeros past a sequence's end
+    (a sequence with no queries; Q blocks of two 128-row parts)."""
     import block_sparse_attention_bwd_amd as bsa
     c, o, lse, _ = _prepared(name)
     dev = upload(c, o, lse)
