@@ -56,6 +56,23 @@ def test_small_case_parity(name):
         assert_close(f"{name}/{nm}", to_np(got), want, c.dtype, floor_ref=floor)
 
 
+@pytest.mark.parametrize("scale", [0.0, 1e-32, 1e-20, -0.09])
+def test_scale_edges(scale):
+    """The scheduled dK/dV kernel starts its score accumulator at -lse2 / c
+    (c = scale * log2 e): a scale of 0, one below 2^-100 (scores taken as 0),
+    a tiny one (-lse2 / c near 1e20) and a negative one against the oracle."""
+    c = synth.make_case(layout="BNSD", dtype="bf16", B=1, N=2, Nkv=1, D=128, Sq=256, Skv=288, bx=128, by=128,
+                        p=0.6, scale=scale, seed=131)
+    o, lse = oracle_fwd_inputs(c)
+    ref = oracle.backward(c.q, c.k, c.v, o, c.do, lse, c.mask, **oracle_kw(c))
+    dev = upload(c, o, lse)
+    (dq, dk, dv), _ = run_bsa(c, dev)
+    torch.cuda.synchronize()
+    floor = float(np.abs(ref[2]).max())
+    for nm, got, want in (("dq", dq, ref[0]), ("dk", dk, ref[1]), ("dv", dv, ref[2])):
+        assert_close(f"scale {scale}/{nm}", to_np(got), want, c.dtype, floor_ref=floor)
+
+
 def _read_ws(runner, offs, name, count, dtype=np.int32):
     import block_sparse_attention_bwd_amd  # noqa: F401
     start = offs[name]
