@@ -375,7 +375,8 @@ enum bsa_ws_region {
  * Test and tooling hook: the same validation as phase 1, then the byte offset
  * of every workspace region (offsets[BSA_WS_NUM]) and the plan's block grid
  * (dims[4] = {bx, by, nQB, nKB}; may be NULL).  After a bsa_bwd call has
- * completed, these regions hold the delta pre-pass and the mask compaction.
+ * completed, these regions hold softmax_grad and lse2 (written by the dQ
+ * kernel) and the mask compaction.
  */
 int bsa_bwd_workspace_layout(const bsa_tensor* dout, const bsa_tensor* query,
                              const bsa_tensor* key, const bsa_tensor* value,
