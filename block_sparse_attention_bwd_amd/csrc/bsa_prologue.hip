@@ -237,11 +237,12 @@ __device__ void col_list_part(const Params& p, int blk) {
   }
 }
 
-// Row lists, then column lists, then softmax_grad workgroups (the forward
-// launches the row lists only).  The list workgroups are latency-bound (a
-// row-list wave walks its mask row 64 blocks per dependent load); dispatched
-// first, they overlap the bandwidth-bound softmax_grad pass instead of
-// trailing it.
+// Row lists, then column lists, then softmax_grad workgroups: those only
+// where the dQ kernel does not compute softmax_grad itself (dQ by atomic
+// adds); the forward launches the row lists only.  The list workgroups are
+// latency-bound (a row-list wave walks its mask row 64 blocks per dependent
+// load); dispatched first, they overlap the bandwidth-bound softmax_grad pass
+// instead of trailing it.
 template <class E, int D>
 __global__ __launch_bounds__(256) void prologue_kernel(Params p, int nb_rows, int nb_cols) {
   const int bid = blockIdx.x;
