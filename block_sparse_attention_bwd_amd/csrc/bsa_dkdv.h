@@ -615,6 +615,14 @@ __device__ __forceinline__ void dkdv_pipe_tile(const DkdvAddr<D, W, NSL>& ad, co
       __builtin_amdgcn_sched_group_barrier(kSgDsRead, (2 * KS + 8 + 2 * KS - 1) / (2 * KS), 0);
     }
   }
+  // DV: slice NSL-2's dV products wait for X(NSL-1), which has no S / dP of
+  // its own to hide slice NSL-1's softmax under (the accumulation order
+  // stays slice order).  For two-slice tiles only: that softmax is a quarter
+  // of their VALU work (3% off the kernel at 64-row blocks), while with four
+  // slices the longer-lived operands cost more than they hide (+1.5%).
+  constexpr bool DV = NSL == 2;
+  u16x8 pa_d[2];
+  u16x4 bo_d[2][NT][2];
 #pragma unroll
   for (int sl = 0; sl < NSL; ++sl) {
     const int cur = sl & 1, nxt = cur ^ 1;
@@ -622,6 +630,12 @@ __device__ __forceinline__ void dkdv_pipe_tile(const DkdvAddr<D, W, NSL>& ad, co
     // ---- X(sl): slice sl + 1's S / dP on the matrix cores, slice sl's softmax on the VALU
     const f32x4(&l4)[4] = in[cur].l4;
     if (sl + 1 < NSL) dkdv_sdp<E, D>(in[nxt], kreg, vreg, s[nxt], dp[nxt]);
+    if (DV && sl + 1 == NSL) {
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) adv[nt] = E::mma(cat8(bo_d[hh][nt][0], bo_d[hh][nt][1]), pa_d[hh], adv[nt]);
+    }
     float pv[16], dsv[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
@@ -663,23 +677,42 @@ __device__ __forceinline__ void dkdv_pipe_tile(const DkdvAddr<D, W, NSL>& ad, co
         __builtin_amdgcn_sched_group_barrier(kSgDsRead, (8 * NT + 2 * KS - 1) / (2 * KS), 0);
         __builtin_amdgcn_sched_group_barrier(kSgValu, (WIN ? 128 : 96) / (2 * KS), 0);
       }
+    } else if (DV) {
+#pragma unroll
+      for (int k = 0; k < 2 * NT; ++k) {
+        __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kSgDsRead, (8 * NT + 2 * NT - 1) / (2 * NT), 0);
+        __builtin_amdgcn_sched_group_barrier(kSgValu, (WIN ? 128 : 96) / (2 * NT), 0);
+      }
     }
     // ---- Y(sl): dV^T += dO^T P, dK^T += Q^T dS; loads slice sl + 2's fragments.
     // The fragment read down dO's (Q's) rows is, as an A operand, dO^T with
     // the same k order as P's (dS's) registers, which serve as the B operand:
     // the accumulators hold dV^T / dK^T, one key row per lane, so the
     // epilogue stores four consecutive elements at a time.
+    if (DV && sl + 2 == NSL) {  // to X(NSL-1)
 #pragma unroll
-    for (int hh = 0; hh < 2; ++hh)
+      for (int hh = 0; hh < 2; ++hh) {
+        pa_d[hh] = pa[hh];
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) adv[nt] = E::mma(cat8(bo[hh][nt][0], bo[hh][nt][1]), pa[hh], adv[nt]);
+        for (int nt = 0; nt < NT; ++nt) {
+          bo_d[hh][nt][0] = bo[hh][nt][0];
+          bo_d[hh][nt][1] = bo[hh][nt][1];
+        }
+      }
+    } else {
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) adv[nt] = E::mma(cat8(bo[hh][nt][0], bo[hh][nt][1]), pa[hh], adv[nt]);
+    }
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) adk[nt] = E::mma(cat8(bq[hh][nt][0], bq[hh][nt][1]), da[hh], adk[nt]);
     if (sl + 2 < NSL) dkdv_read_a<D, W, NSL>(ad, sl + 2, in[cur]);
 #pragma unroll
-    for (int k = 0; k < 4 * NT; ++k) {
+    for (int k = 0; k < (DV && sl + 2 == NSL ? 2 : 4) * NT; ++k) {
       __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
       if (sl + 2 < NSL) __builtin_amdgcn_sched_group_barrier(kSgDsRead, (2 * KS + 8 + 4 * NT - 1) / (4 * NT), 0);
     }
