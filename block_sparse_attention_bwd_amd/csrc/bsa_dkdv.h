@@ -181,16 +181,19 @@ __device__ void reduce_unit(const Params& p, int u) {
 // After a workgroup has stored its piece of split unit u: count the piece
 // (each of the dkdv_passes workgroups of a piece counts once), and the
 // workgroup that completes the count sums the unit (no workgroup waits for
-// another).  The barrier orders the workgroup's partial stores before one
-// thread's release fence (agent scope: it writes the XCD's L2 back, so the
-// stores are visible on every XCD) and count; only the last workgroup takes
+// another).  Every wave first waits for its own partial stores to complete
+// (the barrier alone waits for LDS operations only), so that after the
+// barrier one thread's release fence (agent scope: it writes the XCD's L2
+// back, so the stores are visible on every XCD) covers all of them before
+// the count; only the last workgroup takes
 // the acquire fence (it invalidates its XCD's L2, which costs every other
 // workgroup there its cached tiles), again in one thread, with the barrier
 // ordering the sum after it.  The sum is the same whichever workgroup does
 // it.  `flag` is an LDS word.
 template <class E, int D>
 __device__ void piece_finished(const Params& p, int u, int* flag) {
-  __syncthreads();  // every thread's partial stores, before the fence below
+  wait_vmcnt<0>();  // this wave's partial stores have reached its XCD's L2
+  __syncthreads();  // ... for every wave, before the fence below
   if (threadIdx.x == 0) {
     const PlanView pv(p);
     const int total = pv.unit_k[u] * dkdv_passes(D);

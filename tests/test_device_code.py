@@ -8,6 +8,11 @@
   v_readfirstlane right before the asm block).
 - No kernel indexes the sequence table directly: calls whose sequences all
   share one record stage no table, so every read goes through seq_of.
+- The count of a split dK/dV unit's pieces publishes the workgroup's fp32
+  partial with one thread's agent-scope release fence after a barrier; every
+  wave must first wait for its own stores (vmcnt 0): a barrier by itself
+  waits for LDS operations only, so another wave's partial could still be in
+  flight when the L2 is written back.
 """
 import os
 import re
@@ -131,3 +136,17 @@ def test_sequence_table_is_read_through_seq_of():
                 code = line.split("//")[0]
                 if re.search(r"\.seq\[", code) and "seq_of" not in code:
                     pytest.fail(f"{name}:{k} indexes the sequence table directly: {line.strip()}")
+
+
+
+def test_split_unit_release_waits_for_every_wave():
+    """piece_finished (the count of a split unit's pieces) waits for the wave's
+    own stores (vmcnt 0) before the barrier that precedes the release fence."""
+    with open(os.path.join(B.CSRC, "bsa_dkdv.h")) as f:
+        src = f.read()
+    m = re.search(r"__device__ void piece_finished\([^)]*\) \{(.*?)\n\}", src, re.S)
+    assert m, "piece_finished not found"
+    body = "\n".join(line.split("//")[0] for line in m.group(1).split("\n"))
+    wait, barrier = body.find("wait_vmcnt<0>()"), body.find("__syncthreads()")
+    fence = body.find('__builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent")')
+    assert 0 <= wait < barrier < fence, "the partial stores are not waited for before the barrier and the release"
